@@ -1,0 +1,47 @@
+"""Float64 CPU oracle for the E(3)-equivariant tensor-product graph convolution.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  The
+GPU product path (``tensor_product_convolution_amd``) never imports, links or
+runs it, and this package imports nothing from the product path: the two share
+no code, tables, constants or pre/post-processing.
+
+What it computes is the operator the pages describe in prose only:
+
+* the NequIP equivariant convolution whose tensor product dominates the
+  interaction layer ("Accelerating Tensor Products in E(3)-Equivariant Graph
+  Neural Networks", NeurIPS 2026, Abstract);
+* the full Clebsch-Gordan product, not a cheaper substitute, since different
+  tensor products are different operations ("The Price of Freedom: Exploring
+  Expressivity and Runtime Tradeoffs in Equivariant Tensor Products", ICML
+  2025, Abstract);
+* edge-conditioned, scatter-summed into receivers; edge-sized messages are a
+  property of the schedule, not of the operator ("Sobek: Streaming Equivariant
+  Tensor Product Convolutions", Abstract) -- so this oracle materialises
+  per-edge messages freely, which the GPU path must not.
+
+Every convention the pages leave open (real basis, CG phase and sign, path and
+output order, normalisation, edge-vector direction, radial basis) is a stated
+reading; each function's docstring names the reading it implements.
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+things other than itself (sympy's exact CG, scipy's spherical harmonics,
+closed forms, Wigner-D equivariance, trilinearity, finite differences and
+brute-force loops).  No function here is "parity unpinned".
+"""
+from .irreps import parse_irreps, build_plan, OraclePlan
+from .cg import cg_complex, real_basis_matrix, cg_real
+from .sh import sh_complex, sh_real
+from .wigner import wigner_D_real
+from .csr import csr_build
+from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, radial_mlp_fwd,
+                   radial_mlp_bwd, uvw_mix_fwd, uvw_mix_bwd,
+                   tp_conv_radial_fwd, tp_conv_radial_bwd)
+
+__all__ = [
+    "parse_irreps", "build_plan", "OraclePlan", "cg_complex",
+    "real_basis_matrix", "cg_real", "sh_complex", "sh_real", "wigner_D_real",
+    "csr_build", "tp_conv_fwd", "tp_conv_bwd", "bessel_basis",
+    "radial_mlp_fwd", "radial_mlp_bwd", "uvw_mix_fwd", "uvw_mix_bwd",
+    "tp_conv_radial_fwd", "tp_conv_radial_bwd",
+]
