@@ -1,0 +1,193 @@
+/*
+ * tpconv.h -- C ABI of the MI355X (gfx950) E(3)-equivariant tensor-product
+ * graph convolution.
+ *
+ * The operation (the NequIP equivariant convolution of "Accelerating Tensor
+ * Products in E(3)-Equivariant Graph Neural Networks", NeurIPS 2026, Abstract;
+ * the edge-conditioned product streamed into receivers of "Sobek: Streaming
+ * Equivariant Tensor Product Convolutions", Abstract; the full sparse CG
+ * product of "FlashTP: Fused, Sparsity-Aware Tensor Product for MLIPs",
+ * Abstract).  For every directed edge e = (j -> i):
+ *
+ *   out[i, k, u, c] += sum_{p : k(p) = k} w[e, p, u]
+ *                      * sum_{a, b} C_p[a, b, c] x[j, l1(p), u, a] Y[e, l2(p), b]
+ *
+ * with p running over every path (l1, l2 -> l3) allowed by the triangle rule,
+ * C_p the real-basis Clebsch-Gordan tensor, u the channel ("uvu": channel u
+ * of the input feeds channel u of the output) and k(p) the output irrep
+ * (l3, parity).  The pages never write this formula; it is the plain reading
+ * of their prose.  Conventions (all fixed by this library):
+ *   - real components m = -l..l; for l = 1 the order is (y, z, x);
+ *   - harmonics are component-normalised: sum_m Y_lm^2 = 2l + 1;
+ *   - real CG: Racah closed form, Condon-Shortley phase, orthonormal in the
+ *     output index, sign making the first nonzero (a, b, c) positive;
+ *   - paths: input irreps in string order, then l2 = 0..lmax_sh, then l3
+ *     ascending; output irreps: distinct (l3, parity), l3 ascending, even
+ *     before odd; paths on the same output irrep are summed;
+ *   - edge vectors point from receiver to sender: r_e = pos[src] - pos[dst].
+ *
+ * Layouts (row-major, float32 unless stated):
+ *   x     [N][xdim]   node rows; irrep blocks in string order, each [U][2l+1]
+ *   out   [N][outdim] same, over the output irreps
+ *   Y     [E][ysh]    ysh = (lmax_sh+1)^2; l-blocks, m = -l..l
+ *   w     [E][P][U]   per-edge, per-path, per-channel weights
+ *   Every edge-sized array (Y, w, r_len, grad_Y, grad_w) is in
+ *   RECEIVER-SORTED order: position q holds original edge perm[q], where perm
+ *   comes from tp_conv_graph_build.  tp_conv_gather_rows applies perm.
+ *
+ * Ownership: the caller allocates and owns every device buffer, workspace and
+ * stream.  A plan owns a small host table and is freed by
+ * tp_conv_plan_destroy.  No entry point allocates device memory.
+ *
+ * Errors: every entry point validates its arguments on the host before any
+ * launch and returns a negative tp_status on failure, launching nothing.
+ * Launches are asynchronous on the given stream; device faults surface at
+ * the caller's next synchronisation.  tp_conv_last_error() describes the
+ * last failure on the calling thread.  Outputs are overwritten, never
+ * accumulated.  Device pointers must be 4-byte aligned.
+ */
+#ifndef TPCONV_H
+#define TPCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tp_status;
+#define TP_OK 0
+#define TP_ERR_ARG (-1)         /* null pointer, negative or inconsistent size */
+#define TP_ERR_IRREPS (-2)      /* irreps string does not parse, mixed
+                                   multiplicities, or non-natural parity */
+#define TP_ERR_UNSUPPORTED (-3) /* no compiled kernel for this signature */
+#define TP_ERR_OVERFLOW (-4)    /* a count does not fit the int32 indices */
+#define TP_ERR_WORKSPACE (-5)   /* workspace missing or too small */
+#define TP_ERR_HIP (-6)         /* a HIP call failed; text in last_error */
+#define TP_ERR_INDEX (-7)       /* checked graph build found src/dst outside [0, N) */
+
+#define TP_MODE_UVU 0
+
+typedef struct tp_plan_s* tp_plan_t;
+
+/* Receiver- and sender-grouped edge indices, all int32 device pointers owned
+ * by the caller, filled by tp_conv_graph_build:
+ *   row_ptr[N+1]   receiver offsets into the receiver-sorted edge order
+ *   col[E]         sender of each receiver-sorted edge
+ *   perm[E]        original edge id of each receiver-sorted position
+ *   t_row_ptr[N+1] sender offsets into t_perm
+ *   t_perm[E]      receiver-sorted positions grouped by sender (ascending)
+ *   t_col[E]       receiver of each sender-grouped edge */
+typedef struct {
+  int32_t n_nodes;
+  int32_t n_edges;
+  const int32_t* row_ptr;
+  const int32_t* col;
+  const int32_t* perm;
+  const int32_t* t_row_ptr;
+  const int32_t* t_perm;
+  const int32_t* t_col;
+} tp_graph;
+
+/* Options of a plan.  Zero-initialised means "none".
+ *   radial_basis, radial_hidden, r_cut: edge weights come from a radial
+ *     network of the edge length (Bessel basis -> SiLU hidden layer ->
+ *     P*U weights), used by the *_radial entry points;
+ *   uvw: a U x U channel mix per output irrep follows the aggregation. */
+typedef struct {
+  int32_t radial_basis;
+  int32_t radial_hidden;
+  float r_cut;
+  int32_t uvw;
+} tp_plan_opts;
+
+/* ---- plan (host only; no HIP calls) ---------------------------------------
+ * Builds the path list, output irreps and real CG tables of a channel-wise
+ * ("uvu") tensor product of `irreps_in` (e.g. "32x0e+32x1o+32x2e": one shared
+ * multiplicity, natural parity) with harmonics up to lmax_sh, keeping output
+ * degrees up to lmax_out, and selects the compiled kernel specialisation.
+ * Source: path-aggregated sparse CG product ("FlashTP", Abstract).
+ * Returns TP_ERR_IRREPS / TP_ERR_UNSUPPORTED / TP_ERR_ARG on failure, in which
+ * case *out is set to NULL. */
+tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lmax_sh,
+                              int32_t lmax_out, int32_t mode, const tp_plan_opts* opts);
+
+/* Sizes of a plan.  Any output pointer may be NULL.  out_irreps receives the
+ * output irreps string (NUL-terminated; TP_ERR_ARG if cap is too small). */
+tp_status tp_conv_plan_info(tp_plan_t plan, int32_t* n_paths, int32_t* mul, int32_t* xdim,
+                            int32_t* ysh, int32_t* outdim, int32_t* nnz, char* out_irreps,
+                            size_t out_irreps_cap);
+
+/* Path list: for path p, l1l2l3k[4p..4p+3] = (l1, l2, l3, output irrep index). */
+tp_status tp_conv_plan_paths(tp_plan_t plan, int32_t* l1l2l3k);
+
+/* CG nonzeros of the plan, path by path, (a, b, c) lexicographic within a
+ * path: pabc[4n..4n+3] = (p, a, b, c), val[n] = coefficient (float64). */
+tp_status tp_conv_plan_cg(tp_plan_t plan, int16_t* pabc, double* val);
+
+void tp_conv_plan_destroy(tp_plan_t plan);
+
+/* Dense real CG tensor of one path, out[(a*(2l2+1) + b)*(2l3+1) + c], for
+ * degrees up to 6 (host only).  TP_ERR_ARG if a degree is out of range; the
+ * tensor is all zeros when the triangle rule fails. */
+tp_status tp_cg_real(int32_t l1, int32_t l2, int32_t l3, double* out);
+
+/* ---- graph (device) --------------------------------------------------------
+ * Workspace bytes tp_conv_graph_build needs for (n_nodes, n_edges). */
+tp_status tp_conv_graph_workspace(int32_t n_nodes, int32_t n_edges, size_t* bytes);
+
+#define TP_GRAPH_CHECK 1   /* verify every src/dst is in [0, N); synchronises */
+
+/* Groups the edge list (src[e] -> dst[e], device int32) by receiver and by
+ * sender with a stable order (ties keep the original edge order, and the
+ * sender grouping keeps receiver-sorted order), filling every array of
+ * tp_graph (see above).  Streaming edges grouped by receiver replaces scatter
+ * atomics with receiver-side accumulation ("Sobek", Abstract; "The GPU
+ * Workload That Rewrites Molecular Physics", section "What Makes MLFF
+ * Workloads Structurally Different").  ws must hold
+ * tp_conv_graph_workspace bytes.  Without TP_GRAPH_CHECK, indices outside
+ * [0, N) give an unspecified grouping (never an out-of-bounds write). */
+tp_status tp_conv_graph_build(const int32_t* src, const int32_t* dst, int32_t n_edges,
+                              int32_t n_nodes, int32_t* row_ptr, int32_t* col, int32_t* perm,
+                              int32_t* t_row_ptr, int32_t* t_perm, int32_t* t_col, void* ws,
+                              size_t ws_bytes, int32_t flags, hipStream_t stream);
+
+/* out[q, :] = in[perm[q], :] for q < n_rows, rows of row_words 32-bit words
+ * (device pointers).  Puts edge-sized inputs into receiver-sorted order. */
+tp_status tp_conv_gather_rows(const void* in, const int32_t* perm, int64_t n_rows,
+                              int64_t row_words, void* out, hipStream_t stream);
+
+/* Real component-normalised harmonics of the directions of r[E][3] (device
+ * float32), Y[E][(lmax+1)^2], lmax <= 3.  A zero vector yields the
+ * harmonics' polynomials evaluated at the origin (the direction is
+ * undefined).  Harmonics of the edge direction are the second operand of the
+ * product ("The GPU Workload That Rewrites Molecular Physics", section "What
+ * Makes MLFF Workloads Structurally Different"). */
+tp_status tp_conv_sph_harm(int32_t lmax, const float* r, int32_t n_edges, float* Y,
+                           hipStream_t stream);
+
+/* ---- convolution (device) ---------------------------------------------------
+ * Forward: out = conv(x, Y, w) for the edges of `graph` (formula above).
+ * One pass streams each receiver's edges, keeps the receiver's outputs in
+ * registers and LDS and stores each output row once; no edge-sized
+ * intermediate is written ("Sobek", Abstract; "FlashTP", Abstract). */
+tp_status tp_conv_forward(tp_plan_t plan, const tp_graph* graph, const float* x,
+                          const float* Y, const float* w, float* out, hipStream_t stream);
+
+/* Backward: gradients of <grad_out, out> with respect to x, Y and w (exact
+ * adjoint of the forward; "Sobek", Abstract, backward pass).  grad_x, grad_Y
+ * or grad_w may be NULL to skip that output.  grad_x [N][xdim]; grad_Y
+ * [E][ysh] and grad_w [E][P][U] in receiver-sorted order. */
+tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x,
+                           const float* Y, const float* w, const float* grad_out,
+                           float* grad_x, float* grad_Y, float* grad_w, hipStream_t stream);
+
+/* Thread-local description of the last failure on this thread. */
+const char* tp_conv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPCONV_H */

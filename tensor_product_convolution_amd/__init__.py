@@ -1,0 +1,275 @@
+"""Python binding of libtpconv (MI355X / gfx950 tensor-product convolution).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream; results are torch
+tensors on the same device.  There is no fallback: if ``libtpconv.so`` is
+missing or no GPU is present the calls raise.
+
+Conventions, layouts and error codes are those of ``include/tpconv.h``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libtpconv.so")
+
+TP_OK = 0
+STATUS_NAMES = {-1: "TP_ERR_ARG", -2: "TP_ERR_IRREPS", -3: "TP_ERR_UNSUPPORTED",
+                -4: "TP_ERR_OVERFLOW", -5: "TP_ERR_WORKSPACE", -6: "TP_ERR_HIP",
+                -7: "TP_ERR_INDEX"}
+TP_GRAPH_CHECK = 1
+
+# every exported symbol of include/tpconv.h
+EXPORTS = (
+    "tp_conv_plan_create", "tp_conv_plan_info", "tp_conv_plan_paths", "tp_conv_plan_cg",
+    "tp_conv_plan_destroy", "tp_cg_real", "tp_conv_graph_workspace", "tp_conv_graph_build",
+    "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
+    "tp_conv_last_error",
+)
+
+
+class TPError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Graph(ctypes.Structure):
+    _fields_ = [("n_nodes", ctypes.c_int32), ("n_edges", ctypes.c_int32),
+                ("row_ptr", ctypes.c_void_p), ("col", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("t_row_ptr", ctypes.c_void_p),
+                ("t_perm", ctypes.c_void_p), ("t_col", ctypes.c_void_p)]
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("radial_basis", ctypes.c_int32), ("radial_hidden", ctypes.c_int32),
+                ("r_cut", ctypes.c_float), ("uvw", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ctypes library (loads on first use; raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python tensor_product_convolution_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, VP = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                           ctypes.c_size_t, ctypes.c_void_p)
+    pI32 = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "tp_conv_plan_create": (I32, [ctypes.POINTER(P), ctypes.c_char_p, I32, I32, I32,
+                                      ctypes.POINTER(_Opts)]),
+        "tp_conv_plan_info": (I32, [P, pI32, pI32, pI32, pI32, pI32, pI32, ctypes.c_char_p, SZ]),
+        "tp_conv_plan_paths": (I32, [P, VP]),
+        "tp_conv_plan_cg": (I32, [P, VP, VP]),
+        "tp_conv_plan_destroy": (None, [P]),
+        "tp_cg_real": (I32, [I32, I32, I32, VP]),
+        "tp_conv_graph_workspace": (I32, [I32, I32, ctypes.POINTER(SZ)]),
+        "tp_conv_graph_build": (I32, [VP, VP, I32, I32, VP, VP, VP, VP, VP, VP, VP, SZ, I32, VP]),
+        "tp_conv_gather_rows": (I32, [VP, VP, I64, I64, VP, VP]),
+        "tp_conv_sph_harm": (I32, [I32, VP, I32, VP, VP]),
+        "tp_conv_forward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
+        "tp_conv_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
+        "tp_conv_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != TP_OK:
+        raise TPError(status, lib().tp_conv_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def cg_real(l1, l2, l3):
+    """Dense real CG tensor [2l1+1, 2l2+1, 2l3+1] from the library's builder (host)."""
+    out = np.zeros((2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1), dtype=np.float64)
+    _check(lib().tp_cg_real(l1, l2, l3, out.ctypes.data_as(ctypes.c_void_p)))
+    return out.reshape(2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1)
+
+
+class Plan:
+    """Paths, output irreps and CG tables of a channel-wise product (host only)."""
+
+    def __init__(self, irreps_in, lmax_sh, lmax_out, mode=0):
+        h = ctypes.c_void_p()
+        _check(lib().tp_conv_plan_create(ctypes.byref(h), irreps_in.encode(), lmax_sh, lmax_out,
+                                         mode, None))
+        self._h = h
+        self.irreps_in = irreps_in
+        self.lmax_sh, self.lmax_out = lmax_sh, lmax_out
+        v = [ctypes.c_int32() for _ in range(6)]
+        buf = ctypes.create_string_buffer(256)
+        _check(lib().tp_conv_plan_info(h, *[ctypes.byref(x) for x in v], buf, 256))
+        (self.n_paths, self.mul, self.xdim, self.ysh, self.outdim, self.nnz) = [x.value for x in v]
+        self.out_irreps = buf.value.decode()
+
+    @property
+    def handle(self):
+        return self._h
+
+    def paths(self):
+        a = np.zeros(4 * self.n_paths, dtype=np.int32)
+        _check(lib().tp_conv_plan_paths(self._h, a.ctypes.data_as(ctypes.c_void_p)))
+        return [tuple(int(v) for v in r) for r in a.reshape(-1, 4)]
+
+    def cg(self):
+        idx = np.zeros(4 * self.nnz, dtype=np.int16)
+        val = np.zeros(self.nnz, dtype=np.float64)
+        _check(lib().tp_conv_plan_cg(self._h, idx.ctypes.data_as(ctypes.c_void_p),
+                                     val.ctypes.data_as(ctypes.c_void_p)))
+        return idx.reshape(-1, 4), val
+
+    def dims(self):
+        return dict(xdim=self.xdim, n_paths=self.n_paths, U=self.mul, outdim=self.outdim,
+                    n_out_irreps=len(self.out_irreps.split("+")))
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().tp_conv_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Graph:
+    """Receiver/sender grouping of an edge list (int32 device tensors)."""
+
+    def __init__(self, n_nodes, n_edges, row_ptr, col, perm, t_row_ptr, t_perm, t_col):
+        self.n_nodes, self.n_edges = n_nodes, n_edges
+        self.row_ptr, self.col, self.perm = row_ptr, col, perm
+        self.t_row_ptr, self.t_perm, self.t_col = t_row_ptr, t_perm, t_col
+
+    def cstruct(self):
+        return _Graph(self.n_nodes, self.n_edges, self.row_ptr.data_ptr(),
+                      self.col.data_ptr(), self.perm.data_ptr(), self.t_row_ptr.data_ptr(),
+                      self.t_perm.data_ptr(), self.t_col.data_ptr())
+
+
+def graph_build(src, dst, n_nodes, check=True):
+    """Group edges src -> dst (int32 cuda tensors) by receiver and by sender."""
+    torch = _torch()
+    _need(src, "src", torch.int32)
+    E = src.shape[0]
+    _need(dst, "dst", torch.int32, (E,))
+    dev = src.device
+    need = ctypes.c_size_t()
+    _check(lib().tp_conv_graph_workspace(n_nodes, E, ctypes.byref(need)))
+    ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    g = Graph(n_nodes, E, torch.empty(n_nodes + 1, **i32), torch.empty(E, **i32),
+              torch.empty(E, **i32), torch.empty(n_nodes + 1, **i32),
+              torch.empty(E, **i32), torch.empty(E, **i32))
+    _check(lib().tp_conv_graph_build(_ptr(src), _ptr(dst), E, n_nodes, _ptr(g.row_ptr),
+                                     _ptr(g.col), _ptr(g.perm), _ptr(g.t_row_ptr),
+                                     _ptr(g.t_perm), _ptr(g.t_col), _ptr(ws), need.value,
+                                     TP_GRAPH_CHECK if check else 0, _stream(dev)))
+    g._ws = ws
+    return g
+
+
+def gather_rows(t, perm, out=None):
+    """out[q] = t[perm[q]] for a contiguous 4-byte-element tensor t (rows = dim 0)."""
+    torch = _torch()
+    _need(perm, "perm", torch.int32)
+    if t.element_size() != 4 or not t.is_contiguous():
+        raise TypeError("gather_rows needs a contiguous tensor of 4-byte elements")
+    n = perm.shape[0]
+    words = int(t[0].numel()) if t.shape[0] else 0
+    if out is None:
+        out = torch.empty((n,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+    _check(lib().tp_conv_gather_rows(_ptr(t), _ptr(perm), n, words, _ptr(out), _stream(t.device)))
+    return out
+
+
+def sph_harm(lmax, r, out=None):
+    """Real component-normalised harmonics of the rows of r [E, 3] (float32 cuda)."""
+    torch = _torch()
+    _need(r, "r", torch.float32)
+    E = r.shape[0]
+    if out is None:
+        out = torch.empty((E, (lmax + 1) ** 2), dtype=torch.float32, device=r.device)
+    _check(lib().tp_conv_sph_harm(lmax, _ptr(r), E, _ptr(out), _stream(r.device)))
+    return out
+
+
+def forward(plan, graph, x, Y, w, out=None):
+    """out [N, outdim] of the convolution (edge arrays in receiver-sorted order)."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(w, "w", torch.float32, (E, plan.n_paths, plan.mul))
+    if out is None:
+        out = torch.empty((N, plan.outdim), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (N, plan.outdim))
+    g = graph.cstruct()
+    _check(lib().tp_conv_forward(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
+                                 _ptr(out), _stream(x.device)))
+    return out
+
+
+def backward(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=None):
+    """(grad_x, grad_Y, grad_w); entries not in ``want`` come back as None."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(w, "w", torch.float32, (E, plan.n_paths, plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    f32 = dict(dtype=torch.float32, device=x.device)
+    if outs is None:
+        gx = torch.empty((N, plan.xdim), **f32) if "x" in want else None
+        gY = torch.empty((E, plan.ysh), **f32) if "Y" in want else None
+        gw = torch.empty((E, plan.n_paths, plan.mul), **f32) if "w" in want else None
+    else:
+        gx, gY, gw = outs
+    g = graph.cstruct()
+    _check(lib().tp_conv_backward(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
+                                  _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw),
+                                  _stream(x.device)))
+    return gx, gY, gw

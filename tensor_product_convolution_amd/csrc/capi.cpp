@@ -1,0 +1,351 @@
+// C ABI: plan building (host only), argument validation and kernel dispatch.
+// The plan enumerates the paths of a channel-wise product and its output
+// irreps (path aggregation over every (l1, l2 -> l3): "FlashTP: Fused,
+// Sparsity-Aware Tensor Product for MLIPs", Abstract), computes the real CG
+// nonzeros with the same constexpr routines the kernels were specialised
+// with, and picks the compiled kernel set for the signature.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cctype>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "cg_table.hpp"
+#include "internal.hpp"
+
+struct tp_plan_s {
+  int mul = 0;
+  std::vector<int> ls;                 // input degrees, string order
+  int lmax_sh = 0, lmax_out = 0;
+  struct Path {
+    int in, l1, l2, l3, k;
+  };
+  std::vector<Path> paths;
+  std::vector<std::pair<int, int>> outs;  // (l, parity)
+  int xdim = 0, ysh = 0, outdim = 0, nnz = 0;
+  std::vector<int16_t> cg_pabc;
+  std::vector<double> cg_val;
+  std::string out_irreps;
+  tp_plan_opts opts{};
+  const tpc::KernelSet* ks = nullptr;
+};
+
+namespace tpc {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+tp_status set_error(tp_status code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+tp_status hip_error(hipError_t e, const char* where) {
+  return set_error(TP_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+const KernelSet* find_kernels(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul) {
+  if (ls == std::vector<int>{0, 1} && lmax_sh == 2 && lmax_out == 2) return kernels_l01_s2(mul);
+  if (ls == std::vector<int>{0, 1, 2} && lmax_sh == 2 && lmax_out == 2) return kernels_l012_s2(mul);
+  if (ls == std::vector<int>{0, 1, 2, 3} && lmax_sh == 3 && lmax_out == 3)
+    return kernels_l0123_s3(mul);
+  return nullptr;
+}
+
+namespace {
+
+// "MxLp" terms joined by '+'; whitespace around terms is ignored.
+bool parse_irreps(const char* s, std::vector<int>* muls, std::vector<int>* ls, std::vector<int>* ps,
+                  std::string* err) {
+  std::string str(s);
+  size_t pos = 0;
+  if (str.find_first_not_of(" \t") == std::string::npos) {
+    *err = "empty irreps string";
+    return false;
+  }
+  while (true) {
+    size_t plus = str.find('+', pos);
+    std::string term = str.substr(pos, plus == std::string::npos ? std::string::npos : plus - pos);
+    size_t b = term.find_first_not_of(" \t"), e = term.find_last_not_of(" \t");
+    term = b == std::string::npos ? std::string() : term.substr(b, e - b + 1);
+    size_t x = term.find('x');
+    if (term.empty() || x == std::string::npos || x == 0 || x + 2 > term.size()) {
+      *err = "bad irreps term '" + term + "'";
+      return false;
+    }
+    std::string m = term.substr(0, x), l = term.substr(x + 1, term.size() - x - 2);
+    char p = term.back();
+    auto digits = [](const std::string& t) {
+      return !t.empty() && t.size() < 7 &&
+             std::all_of(t.begin(), t.end(), [](char c) { return std::isdigit((unsigned char)c); });
+    };
+    if (!digits(m) || !digits(l) || (p != 'e' && p != 'o')) {
+      *err = "bad irreps term '" + term + "'";
+      return false;
+    }
+    int mv = std::stoi(m), lv = std::stoi(l);
+    if (mv <= 0) {
+      *err = "multiplicity must be positive in '" + term + "'";
+      return false;
+    }
+    muls->push_back(mv);
+    ls->push_back(lv);
+    ps->push_back(p == 'e' ? 1 : -1);
+    if (plus == std::string::npos) break;
+    pos = plus + 1;
+  }
+  return true;
+}
+
+}  // namespace
+}  // namespace tpc
+
+using tpc::set_error;
+
+extern "C" {
+
+const char* tp_conv_last_error(void) { return tpc::g_last_error.c_str(); }
+
+tp_status tp_cg_real(int32_t l1, int32_t l2, int32_t l3, double* out) {
+  if (!out) return set_error(TP_ERR_ARG, "tp_cg_real: out is NULL");
+  if (l1 < 0 || l2 < 0 || l3 < 0 || l1 > tpc::kMaxL || l2 > tpc::kMaxL || l3 > tpc::kMaxL)
+    return set_error(TP_ERR_ARG, "tp_cg_real: degrees must be in 0..6");
+  const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+  const bool ok = tpc::triangle(l1, l2, l3);
+  const double s = ok ? tpc::real_cg_sign(l1, l2, l3) : 1.0;
+  for (int a = 0; a < n1; ++a)
+    for (int b = 0; b < n2; ++b)
+      for (int c = 0; c < n3; ++c)
+        out[(a * n2 + b) * n3 + c] = ok ? tpc::real_cg(l1, l2, l3, a, b, c, s) : 0.0;
+  return TP_OK;
+}
+
+tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lmax_sh,
+                              int32_t lmax_out, int32_t mode, const tp_plan_opts* opts) {
+  if (!out) return set_error(TP_ERR_ARG, "tp_conv_plan_create: out is NULL");
+  *out = nullptr;
+  if (!irreps_in) return set_error(TP_ERR_ARG, "tp_conv_plan_create: irreps_in is NULL");
+  if (mode != TP_MODE_UVU) return set_error(TP_ERR_UNSUPPORTED, "only mode TP_MODE_UVU (0) exists");
+  if (lmax_sh < 0 || lmax_out < 0 || lmax_sh > tpc::kMaxL || lmax_out > tpc::kMaxL)
+    return set_error(TP_ERR_ARG, "lmax_sh and lmax_out must be in 0..6");
+  std::vector<int> muls, ls, ps;
+  std::string err;
+  if (!tpc::parse_irreps(irreps_in, &muls, &ls, &ps, &err)) return set_error(TP_ERR_IRREPS, err);
+  for (size_t i = 0; i < ls.size(); ++i) {
+    if (muls[i] != muls[0])
+      return set_error(TP_ERR_IRREPS, "channel-wise product needs one multiplicity for all irreps");
+    if (ps[i] != ((ls[i] & 1) ? -1 : 1))
+      return set_error(TP_ERR_IRREPS, "input irreps must have natural parity (-1)^l");
+    if (ls[i] > tpc::kMaxL) return set_error(TP_ERR_UNSUPPORTED, "input degree above 6");
+  }
+  if (opts && (opts->radial_basis || opts->radial_hidden || opts->uvw))
+    return set_error(TP_ERR_UNSUPPORTED, "radial / uvw plan options are not available in this build");
+
+  auto* p = new tp_plan_s();
+  p->mul = muls[0];
+  p->ls = ls;
+  p->lmax_sh = lmax_sh;
+  p->lmax_out = lmax_out;
+  if (opts) p->opts = *opts;
+  // paths
+  std::vector<std::pair<int, int>> raw_out;
+  for (size_t i = 0; i < ls.size(); ++i)
+    for (int l2 = 0; l2 <= lmax_sh; ++l2)
+      for (int l3 = std::abs(ls[i] - l2); l3 <= std::min(ls[i] + l2, (int)lmax_out); ++l3) {
+        p->paths.push_back({(int)i, ls[i], l2, l3, -1});
+        raw_out.push_back({l3, ps[i] * ((l2 & 1) ? -1 : 1)});
+      }
+  if (p->paths.empty()) {
+    delete p;
+    return set_error(TP_ERR_ARG, "no path satisfies the triangle rule with these lmax");
+  }
+  for (int l = 0; l <= lmax_out; ++l)
+    for (int par : {1, -1})
+      if (std::find(raw_out.begin(), raw_out.end(), std::make_pair(l, par)) != raw_out.end())
+        p->outs.push_back({l, par});
+  for (size_t q = 0; q < p->paths.size(); ++q)
+    p->paths[q].k = (int)(std::find(p->outs.begin(), p->outs.end(), raw_out[q]) - p->outs.begin());
+  for (int l : ls) p->xdim += p->mul * (2 * l + 1);
+  for (auto& o : p->outs) p->outdim += p->mul * (2 * o.first + 1);
+  p->ysh = (lmax_sh + 1) * (lmax_sh + 1);
+  for (size_t q = 0; q < p->paths.size(); ++q) {
+    const auto& pa = p->paths[q];
+    const double s = tpc::real_cg_sign(pa.l1, pa.l2, pa.l3);
+    for (int a = 0; a <= 2 * pa.l1; ++a)
+      for (int b = 0; b <= 2 * pa.l2; ++b)
+        for (int c = 0; c <= 2 * pa.l3; ++c) {
+          double v = tpc::real_cg(pa.l1, pa.l2, pa.l3, a, b, c, s);
+          if (v != 0.0) {
+            p->cg_pabc.insert(p->cg_pabc.end(), {(int16_t)q, (int16_t)a, (int16_t)b, (int16_t)c});
+            p->cg_val.push_back(v);
+          }
+        }
+  }
+  p->nnz = (int)p->cg_val.size();
+  for (size_t k = 0; k < p->outs.size(); ++k) {
+    if (k) p->out_irreps += "+";
+    p->out_irreps += std::to_string(p->mul) + "x" + std::to_string(p->outs[k].first) +
+                     (p->outs[k].second == 1 ? "e" : "o");
+  }
+  p->ks = tpc::find_kernels(ls, lmax_sh, lmax_out, p->mul);
+  if (!p->ks) {
+    delete p;
+    return set_error(TP_ERR_UNSUPPORTED,
+                     "no compiled kernel for this signature (supported: 0e+1o / lmax 2, "
+                     "0e+1o+2e / lmax 2, 0e+1o+2e+3o / lmax 3; multiplicity 8, 16, 32, 64 or 128)");
+  }
+  *out = p;
+  return TP_OK;
+}
+
+tp_status tp_conv_plan_info(tp_plan_t plan, int32_t* n_paths, int32_t* mul, int32_t* xdim,
+                            int32_t* ysh, int32_t* outdim, int32_t* nnz, char* out_irreps,
+                            size_t cap) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_plan_info: plan is NULL");
+  if (n_paths) *n_paths = (int32_t)plan->paths.size();
+  if (mul) *mul = plan->mul;
+  if (xdim) *xdim = plan->xdim;
+  if (ysh) *ysh = plan->ysh;
+  if (outdim) *outdim = plan->outdim;
+  if (nnz) *nnz = plan->nnz;
+  if (out_irreps) {
+    if (cap < plan->out_irreps.size() + 1)
+      return set_error(TP_ERR_ARG, "tp_conv_plan_info: out_irreps buffer too small");
+    std::memcpy(out_irreps, plan->out_irreps.c_str(), plan->out_irreps.size() + 1);
+  }
+  return TP_OK;
+}
+
+tp_status tp_conv_plan_paths(tp_plan_t plan, int32_t* l1l2l3k) {
+  if (!plan || !l1l2l3k) return set_error(TP_ERR_ARG, "tp_conv_plan_paths: NULL argument");
+  for (size_t q = 0; q < plan->paths.size(); ++q) {
+    l1l2l3k[4 * q] = plan->paths[q].l1;
+    l1l2l3k[4 * q + 1] = plan->paths[q].l2;
+    l1l2l3k[4 * q + 2] = plan->paths[q].l3;
+    l1l2l3k[4 * q + 3] = plan->paths[q].k;
+  }
+  return TP_OK;
+}
+
+tp_status tp_conv_plan_cg(tp_plan_t plan, int16_t* pabc, double* val) {
+  if (!plan || !pabc || !val) return set_error(TP_ERR_ARG, "tp_conv_plan_cg: NULL argument");
+  std::memcpy(pabc, plan->cg_pabc.data(), plan->cg_pabc.size() * sizeof(int16_t));
+  std::memcpy(val, plan->cg_val.data(), plan->cg_val.size() * sizeof(double));
+  return TP_OK;
+}
+
+void tp_conv_plan_destroy(tp_plan_t plan) { delete plan; }
+
+tp_status tp_conv_graph_workspace(int32_t n_nodes, int32_t n_edges, size_t* bytes) {
+  if (!bytes) return set_error(TP_ERR_ARG, "tp_conv_graph_workspace: bytes is NULL");
+  if (n_nodes < 0 || n_edges < 0) return set_error(TP_ERR_ARG, "negative size");
+  *bytes = tpc::graph_workspace_bytes(n_nodes, n_edges);
+  return TP_OK;
+}
+
+tp_status tp_conv_graph_build(const int32_t* src, const int32_t* dst, int32_t n_edges,
+                              int32_t n_nodes, int32_t* row_ptr, int32_t* col, int32_t* perm,
+                              int32_t* t_row_ptr, int32_t* t_perm, int32_t* t_col, void* ws,
+                              size_t ws_bytes, int32_t flags, hipStream_t stream) {
+  if (n_nodes < 0 || n_edges < 0) return set_error(TP_ERR_ARG, "tp_conv_graph_build: negative size");
+  if (n_edges > 0 && n_nodes == 0)
+    return set_error(TP_ERR_ARG, "tp_conv_graph_build: edges need at least one node");
+  if (!row_ptr || !t_row_ptr) return set_error(TP_ERR_ARG, "tp_conv_graph_build: NULL row pointer");
+  if (n_edges > 0 && (!src || !dst || !col || !perm || !t_perm || !t_col))
+    return set_error(TP_ERR_ARG, "tp_conv_graph_build: NULL edge array");
+  const size_t need = tpc::graph_workspace_bytes(n_nodes, n_edges);
+  if (!ws || ws_bytes < need)
+    return set_error(TP_ERR_WORKSPACE, "tp_conv_graph_build: workspace needs " +
+                                           std::to_string(need) + " bytes");
+  return tpc::graph_build(src, dst, n_edges, n_nodes, row_ptr, col, perm, t_row_ptr, t_perm, t_col,
+                          ws, flags, stream);
+}
+
+tp_status tp_conv_gather_rows(const void* in, const int32_t* perm, int64_t n_rows,
+                              int64_t row_words, void* out, hipStream_t stream) {
+  if (n_rows < 0 || row_words < 0) return set_error(TP_ERR_ARG, "tp_conv_gather_rows: negative size");
+  if (n_rows > 0 && row_words > 0 && (!in || !perm || !out))
+    return set_error(TP_ERR_ARG, "tp_conv_gather_rows: NULL pointer");
+  if (n_rows > INT32_MAX) return set_error(TP_ERR_OVERFLOW, "tp_conv_gather_rows: too many rows");
+  return tpc::gather_rows(in, perm, n_rows, row_words, out, stream);
+}
+
+tp_status tp_conv_sph_harm(int32_t lmax, const float* r, int32_t n_edges, float* Y,
+                           hipStream_t stream) {
+  if (n_edges < 0) return set_error(TP_ERR_ARG, "tp_conv_sph_harm: negative size");
+  if (n_edges > 0 && (!r || !Y)) return set_error(TP_ERR_ARG, "tp_conv_sph_harm: NULL pointer");
+  return tpc::sph_harm(lmax, r, n_edges, Y, stream);
+}
+
+static tp_status check_graph(const tp_graph* g, bool need_sender) {
+  if (!g) return set_error(TP_ERR_ARG, "graph is NULL");
+  if (g->n_nodes < 0 || g->n_edges < 0) return set_error(TP_ERR_ARG, "graph has a negative size");
+  if (g->n_nodes > 0 && !g->row_ptr) return set_error(TP_ERR_ARG, "graph.row_ptr is NULL");
+  if (g->n_edges > 0 && !g->col) return set_error(TP_ERR_ARG, "graph.col is NULL");
+  if (need_sender && g->n_nodes > 0 && !g->t_row_ptr)
+    return set_error(TP_ERR_ARG, "graph.t_row_ptr is NULL");
+  if (need_sender && g->n_edges > 0 && (!g->t_perm || !g->t_col))
+    return set_error(TP_ERR_ARG, "graph.t_perm / t_col is NULL");
+  return TP_OK;
+}
+
+tp_status tp_conv_forward(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                          const float* w, float* out, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward: plan is NULL");
+  tp_status s = check_graph(graph, false);
+  if (s != TP_OK) return s;
+  if (graph->n_nodes > 0 && (!x || !out)) return set_error(TP_ERR_ARG, "tp_conv_forward: x/out NULL");
+  if (graph->n_edges > 0 && (!Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_forward: Y/w NULL");
+  tpc::ConvArgs a;
+  a.n_nodes = graph->n_nodes;
+  a.n_edges = graph->n_edges;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.x = x;
+  a.Y = Y;
+  a.w = w;
+  a.out = out;
+  a.stream = stream;
+  hipError_t e = plan->ks->fwd(a);
+  return e == hipSuccess ? TP_OK : tpc::hip_error(e, "tp_conv_forward launch");
+}
+
+tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                           const float* w, const float* grad_out, float* grad_x, float* grad_Y,
+                           float* grad_w, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward: plan is NULL");
+  tp_status s = check_graph(graph, grad_x != nullptr);
+  if (s != TP_OK) return s;
+  const bool any_edge_grad = grad_Y || grad_w;
+  if (graph->n_nodes > 0 && !grad_out) return set_error(TP_ERR_ARG, "tp_conv_backward: grad_out NULL");
+  if (graph->n_edges > 0 && (!Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_backward: Y/w NULL");
+  if (graph->n_edges > 0 && any_edge_grad && !x)
+    return set_error(TP_ERR_ARG, "tp_conv_backward: x NULL");
+  tpc::ConvArgs a;
+  a.n_nodes = graph->n_nodes;
+  a.n_edges = graph->n_edges;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_perm = graph->t_perm;
+  a.t_col = graph->t_col;
+  a.x = x;
+  a.Y = Y;
+  a.w = w;
+  a.grad_out = grad_out;
+  a.grad_x = grad_x;
+  a.grad_Y = grad_Y;
+  a.grad_w = grad_w;
+  a.stream = stream;
+  hipError_t e = plan->ks->bwd_recv(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward receiver pass");
+  e = plan->ks->bwd_send(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward sender pass");
+  return TP_OK;
+}
+
+}  // extern "C"

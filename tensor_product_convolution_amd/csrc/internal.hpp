@@ -1,0 +1,53 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/tpconv.h"
+
+namespace tpc {
+
+// ---- error reporting --------------------------------------------------------
+tp_status set_error(tp_status code, const std::string& msg);
+tp_status hip_error(hipError_t e, const char* where);
+
+// ---- kernel dispatch --------------------------------------------------------
+struct ConvArgs {
+  int32_t n_nodes = 0, n_edges = 0;
+  const int32_t *row_ptr = nullptr, *col = nullptr;
+  const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
+  const float *x = nullptr, *Y = nullptr, *w = nullptr, *grad_out = nullptr;
+  float *out = nullptr, *grad_x = nullptr, *grad_Y = nullptr, *grad_w = nullptr;
+  hipStream_t stream = nullptr;
+};
+
+using LaunchFn = hipError_t (*)(const ConvArgs&);
+
+struct KernelSet {
+  LaunchFn fwd = nullptr;       // receiver pass: out
+  LaunchFn bwd_recv = nullptr;  // receiver pass: grad_w, grad_Y
+  LaunchFn bwd_send = nullptr;  // sender pass: grad_x
+};
+
+// Lookup of the compiled specialisation for (input degrees, lmax_sh,
+// lmax_out, multiplicity); nullptr if none.
+const KernelSet* find_kernels(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul);
+
+// Per-signature registries (one translation unit each).
+const KernelSet* kernels_l01_s2(int mul);
+const KernelSet* kernels_l012_s2(int mul);
+const KernelSet* kernels_l0123_s3(int mul);
+
+// ---- device helpers implemented in graph.hip / sh.hip ------------------------
+size_t graph_workspace_bytes(int n_nodes, int n_edges);
+tp_status graph_build(const int32_t* src, const int32_t* dst, int n_edges, int n_nodes,
+                      int32_t* row_ptr, int32_t* col, int32_t* perm, int32_t* t_row_ptr,
+                      int32_t* t_perm, int32_t* t_col, void* ws, int32_t flags, hipStream_t st);
+tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64_t words, void* out,
+                      hipStream_t st);
+tp_status sph_harm(int lmax, const float* r, int n, float* Y, hipStream_t st);
+
+}  // namespace tpc

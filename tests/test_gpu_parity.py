@@ -1,0 +1,308 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bar: CSR arrays bit-identical; every float output within 1e-4 * max|ref|
+per irrep block (output irreps for out, input irreps for grad_x, paths for
+grad_w, degrees for grad_Y).  Each side computes its own harmonics from the
+same float32 edge vectors (the GPU in float32, the oracle in float64).
+Full-size workloads the oracle cannot finish in seconds are checked on
+sampled receivers/senders/edges, which the oracle computes exactly from the
+edges that touch them.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests._common import dims_of
+from workloads import make_workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+CFG = {"tiny": ("8x0e+8x1o", 2, 2), "mid": ("32x0e+32x1o+32x2e", 2, 2),
+       "lmax3": ("64x0e+64x1o+64x2e+64x3o", 3, 3), "zipf": ("64x0e+64x1o+64x2e+64x3o", 3, 3),
+       "stream": ("128x0e+128x1o+128x2e", 2, 2)}
+
+
+@pytest.fixture(scope="module")
+def tpc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_product_convolution_amd as m
+    m.lib()
+    return m
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def T(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def block_err(got, ref, blocks):
+    worst = 0.0
+    for s in blocks:
+        r, g = ref[:, s], got[:, s]
+        if r.size == 0:
+            continue
+        scale = float(np.max(np.abs(r)))
+        err = float(np.max(np.abs(g - r)))
+        worst = max(worst, err / scale if scale > 0 else err)
+    return worst
+
+
+def out_blocks(op):
+    return [slice(o, o + op.U * (2 * l + 1)) for (l, _), o in zip(op.out_irreps, op.out_offsets)]
+
+
+def in_blocks(op):
+    return [slice(o, o + op.U * (2 * l + 1)) for (_, l, _), o in zip(op.irreps_in, op.in_offsets)]
+
+
+def y_blocks(op):
+    return [slice(l * l, (l + 1) ** 2) for l in range(op.lmax_sh + 1)]
+
+
+def w_err(got, ref):
+    return max(block_err(got[:, p, :], ref[:, p, :], [slice(None)]) for p in range(ref.shape[1]))
+
+
+def run_gpu(tpc, plan, wl, bwd=True, w=None):
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(plan.lmax_sh, tpc.gather_rows(T(wl.r), g.perm))
+    wv = tpc.gather_rows(T(wl.w if w is None else w), g.perm)
+    x = T(wl.x)
+    out = tpc.forward(plan, g, x, Y, wv)
+    res = dict(graph=g, out=out)
+    if bwd:
+        gx, gY, gw = tpc.backward(plan, g, x, Y, wv, T(wl.g))
+        res.update(gx=gx, gY=gY, gw=gw)
+    torch.cuda.synchronize()
+    res = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in res.items()}
+    res["perm"] = g.perm.cpu().numpy()[:wl.n_edges]
+    return res
+
+
+def plans(name, mul=None):
+    irr, ls, lo = CFG[name]
+    if mul is not None:
+        irr = "+".join(f"{mul}x{t.split('x')[1]}" for t in irr.split("+"))
+    import tensor_product_convolution_amd as m
+    return m.Plan(irr, ls, lo), oracle.build_plan(irr, ls, lo)
+
+
+# ---------------------------------------------------------------------------
+# CSR
+
+def _csr_check(tpc, src, dst, n):
+    g = tpc.graph_build(T(np.asarray(src, np.int32)), T(np.asarray(dst, np.int32)), n)
+    torch.cuda.synchronize()
+    ref = oracle.csr_build(src, dst, n)
+    E = len(src)
+    got = dict(perm=g.perm, row_ptr=g.row_ptr, col=g.col, t_perm=g.t_perm,
+               t_row_ptr=g.t_row_ptr, t_col=g.t_col)
+    for k, v in got.items():
+        v = v.cpu().numpy().astype(np.int64)
+        if k in ("perm", "col", "t_perm", "t_col"):
+            v = v[:E]
+        assert np.array_equal(v, ref[k]), k
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "lmax3", "zipf", "stream"])
+def test_csr_bit_exact_full_size(tpc, name):
+    say(f"csr {name}")
+    wl = make_workload(name, dict(xdim=0, n_paths=0, U=0, outdim=0, n_out_irreps=0),
+                       graph_only=True)
+    _csr_check(tpc, wl.src, wl.dst, wl.n_nodes)
+
+
+def test_csr_edge_cases(tpc):
+    rng = np.random.default_rng(0)
+    say("csr edge cases")
+    _csr_check(tpc, np.zeros(0, np.int32), np.zeros(0, np.int32), 5)       # no edges
+    _csr_check(tpc, [0, 0, 0], [0, 0, 0], 1)                               # one node, self loops
+    _csr_check(tpc, rng.integers(0, 50, 7000), np.zeros(7000, np.int64), 50)   # one hub, many tiles
+    _csr_check(tpc, rng.integers(0, 300000, 5000), rng.integers(0, 300000, 5000), 300000)  # 3 passes
+    s = rng.integers(0, 40, 20000)
+    _csr_check(tpc, s, rng.integers(0, 40, 20000), 40)                     # many duplicates
+    _csr_check(tpc, np.arange(2049), np.arange(2049)[::-1].copy(), 2049)   # tile boundary
+
+
+def test_csr_checked_mode_rejects_bad_index(tpc):
+    say("csr checked mode")
+    with pytest.raises(tpc.TPError) as e:
+        tpc.graph_build(T(np.array([0, 5], np.int32)), T(np.array([1, 1], np.int32)), 4)
+    assert e.value.status == -7
+    with pytest.raises(tpc.TPError):
+        tpc.graph_build(T(np.array([0, 1], np.int32)), T(np.array([-1, 1], np.int32)), 4)
+
+
+# ---------------------------------------------------------------------------
+# harmonics
+
+def test_sph_harm_parity(tpc):
+    say("sph_harm")
+    rng = np.random.default_rng(1)
+    r = rng.normal(size=(5000, 3)) * rng.uniform(0.5, 6, size=(5000, 1))
+    r[:6] = [[1, 0, 0], [0, 1, 0], [0, 0, 1], [0, 0, -2], [-1, 0, 0], [0, -3, 0]]
+    r = r.astype(np.float32)
+    for lmax in range(4):
+        got = tpc.sph_harm(lmax, T(r)).cpu().numpy()
+        ref = oracle.sh_real(lmax, r)
+        assert np.max(np.abs(got - ref)) <= 2e-6 * max(1.0, np.max(np.abs(ref)))
+
+
+# ---------------------------------------------------------------------------
+# forward / backward, full element-wise
+
+@pytest.mark.parametrize("name,n_nodes,mul,bwd", [
+    ("tiny", None, None, True),
+    ("mid", None, None, True),
+    ("lmax3", 512, None, True),
+    ("zipf", 600, None, True),
+    ("stream", 300, None, True),
+    ("mid", 200, 8, True),
+    ("mid", 200, 16, True),
+    ("mid", 200, 64, True),
+    ("lmax3", 200, 32, True),
+    ("lmax3", 120, 128, True),
+    ("tiny", None, 16, True),
+])
+def test_conv_parity(tpc, name, n_nodes, mul, bwd):
+    say(f"conv parity {name} n={n_nodes} mul={mul}")
+    plan, op = plans(name, mul)
+    wname = "mid" if name == "stream" else name   # direct weights on the stream shapes
+    wl = make_workload(wname, dims_of(op), n_nodes=n_nodes or (300 if name == "stream" else None))
+    res = run_gpu(tpc, plan, wl, bwd)
+    Y = oracle.sh_real(op.lmax_sh, wl.r)
+    ref = oracle.tp_conv_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w)
+    assert block_err(res["out"], ref, out_blocks(op)) <= TOL
+    if bwd:
+        gx, gY, gw = oracle.tp_conv_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w, wl.g)
+        p = res["perm"]
+        assert block_err(res["gx"], gx, in_blocks(op)) <= TOL
+        assert block_err(res["gY"], gY[p], y_blocks(op)) <= TOL
+        assert w_err(res["gw"], gw[p]) <= TOL
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows
+
+def _sample(deg, k, rng):
+    order = np.argsort(-deg, kind="stable")
+    hubs = list(order[:4])
+    zero = list(np.nonzero(deg == 0)[0][:2])
+    rest = list(rng.choice(len(deg), size=k, replace=False))
+    return np.unique(np.array(hubs + zero + rest, dtype=np.int64))
+
+
+@pytest.mark.parametrize("name,bwd", [("lmax3", False), ("zipf", True)])
+def test_conv_parity_full_size_sampled(tpc, name, bwd):
+    say(f"conv full-size sampled {name}")
+    plan, op = plans(name)
+    wl = make_workload(name, dims_of(op))
+    res = run_gpu(tpc, plan, wl, bwd)
+    rng = np.random.default_rng(5)
+    N = wl.n_nodes
+    recv = _sample(np.bincount(wl.dst, minlength=N), 40, rng)
+    m = np.isin(wl.dst, recv)
+    e = np.nonzero(m)[0]
+    Y = oracle.sh_real(op.lmax_sh, wl.r[e])
+    ref = oracle.tp_conv_fwd(op, wl.src[e], wl.dst[e], N, wl.x, Y, wl.w[e])
+    assert block_err(res["out"][recv], ref[recv], out_blocks(op)) <= TOL
+    if not bwd:
+        return
+    # per-edge gradients of the edges into the sampled receivers
+    _, gY, gw = oracle.tp_conv_bwd(op, wl.src[e], wl.dst[e], N, wl.x, Y, wl.w[e], wl.g)
+    inv = np.empty(wl.n_edges, np.int64)
+    inv[res["perm"]] = np.arange(wl.n_edges)
+    q = inv[e]
+    assert block_err(res["gY"][q], gY, y_blocks(op)) <= TOL
+    assert w_err(res["gw"][q], gw) <= TOL
+    # grad_x of sampled senders
+    send = _sample(np.bincount(wl.src, minlength=N), 40, rng)
+    e2 = np.nonzero(np.isin(wl.src, send))[0]
+    Y2 = oracle.sh_real(op.lmax_sh, wl.r[e2])
+    gx, _, _ = oracle.tp_conv_bwd(op, wl.src[e2], wl.dst[e2], N, wl.x, Y2, wl.w[e2], wl.g)
+    assert block_err(res["gx"][send], gx[send], in_blocks(op)) <= TOL
+
+
+# ---------------------------------------------------------------------------
+# degenerate cases, determinism, memory
+
+def test_empty_and_isolated(tpc):
+    say("empty graph")
+    plan, op = plans("mid")
+    N = 7
+    x = torch.randn(N, op.xdim, device=dev())
+    g = tpc.graph_build(T(np.zeros(0, np.int32)), T(np.zeros(0, np.int32)), N)
+    Y = torch.zeros(0, op.ysh, device=dev())
+    w = torch.zeros(0, op.n_paths, op.U, device=dev())
+    out = torch.full((N, op.outdim), 7.0, device=dev())
+    tpc.forward(plan, g, x, Y, w, out=out)
+    gx, gY, gw = tpc.backward(plan, g, x, Y, w, torch.randn(N, op.outdim, device=dev()))
+    torch.cuda.synchronize()
+    assert float(out.abs().max()) == 0.0 and float(gx.abs().max()) == 0.0
+    # one hub receiver with 3000 edges and isolated nodes elsewhere
+    say("hub receiver")
+    rng = np.random.default_rng(3)
+    src = rng.integers(1, 50, 3000).astype(np.int32)
+    dst = np.zeros(3000, np.int32)
+    r = rng.normal(size=(3000, 3)).astype(np.float32)
+    xs = rng.normal(size=(50, op.xdim)).astype(np.float32)
+    ws = (rng.normal(size=(3000, op.n_paths, op.U)) / 4).astype(np.float32)
+    gs = rng.normal(size=(50, op.outdim)).astype(np.float32)
+
+    class W:
+        pass
+    wl = W()
+    wl.src, wl.dst, wl.r, wl.x, wl.w, wl.g, wl.n_nodes, wl.n_edges = src, dst, r, xs, ws, gs, 50, 3000
+    res = run_gpu(tpc, plan, wl, True)
+    Yo = oracle.sh_real(2, r)
+    ref = oracle.tp_conv_fwd(op, src, dst, 50, xs, Yo, ws)
+    assert block_err(res["out"], ref, out_blocks(op)) <= TOL
+    assert np.all(res["out"][1:] == 0)
+    gx, gY, gw = oracle.tp_conv_bwd(op, src, dst, 50, xs, Yo, ws, gs)
+    assert block_err(res["gx"], gx, in_blocks(op)) <= TOL
+    assert block_err(res["gY"], gY[res["perm"]], y_blocks(op)) <= TOL
+
+
+def test_bitwise_deterministic(tpc):
+    say("determinism")
+    plan, op = plans("mid")
+    wl = make_workload("zipf", dims_of(op), n_nodes=2000)
+    a = run_gpu(tpc, plan, wl, True)
+    b = run_gpu(tpc, plan, wl, True)
+    for k in ("out", "gx", "gY", "gw", "perm"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_forward_allocates_nothing(tpc):
+    say("no allocations")
+    plan, op = plans("mid")
+    wl = make_workload("mid", dims_of(op), n_nodes=400)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+    w = tpc.gather_rows(T(wl.w), g.perm)
+    x = T(wl.x)
+    out = torch.empty(wl.n_nodes, op.outdim, device=dev())
+    gx = torch.empty_like(x)
+    gY = torch.empty_like(Y)
+    gw = torch.empty_like(w)
+    go = T(wl.g)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    tpc.forward(plan, g, x, Y, w, out=out)
+    tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == base
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0

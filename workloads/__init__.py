@@ -123,12 +123,14 @@ def _directions(rng, n):
     return v * rng.uniform(LEN_LO, LEN_HI, size=(n, 1))
 
 
-def make_workload(name, dims, seed=0, n_nodes=None):
+def make_workload(name, dims, seed=0, n_nodes=None, graph_only=False):
     """Draw one workload.
 
     ``dims`` gives the sizes the plan fixes: xdim, n_paths, U, outdim and
     n_out_irreps (the generator does not enumerate paths itself).  ``n_nodes``
     overrides the configuration's atom count for reduced-size parity runs.
+    ``graph_only`` stops after the edge vectors (the same graph and vectors
+    as a full draw, since those are drawn first).
     """
     cfg = CONFIGS[name]
     n = int(n_nodes or cfg["n_nodes"])
@@ -137,6 +139,10 @@ def make_workload(name, dims, seed=0, n_nodes=None):
     shuffle = rng.permutation(len(src))
     src, dst = src[shuffle], dst[shuffle]
     r = r[shuffle] if r is not None else _directions(rng, len(src))
+    if graph_only:
+        return Workload(name=name, irreps=cfg["irreps"], lmax_sh=cfg["lmax_sh"],
+                        lmax_out=cfg["lmax_out"], n_nodes=n, src=src.astype(np.int32),
+                        dst=dst.astype(np.int32), r=_f32(r), x=None)
     x = rng.normal(size=(n, dims["xdim"]))
     wl = Workload(name=name, irreps=cfg["irreps"], lmax_sh=cfg["lmax_sh"],
                   lmax_out=cfg["lmax_out"], n_nodes=n,
