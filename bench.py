@@ -11,7 +11,7 @@ Timing: W untimed warm-up steps, then K timed steps.  Every kernel is timed
 with HIP events on the stream it is launched on (torch's current stream).
 Before each step a 1 GiB buffer is overwritten so that L2 and the 256 MB
 Infinity Cache hold none of the step's inputs: they come from HBM.  The same
-steps are also timed back to back without the flush ("warm").
+steps can also be timed back to back without the flush (``--warm``).
 
 Output: one JSON line (rank 0, N = 1).  ``value`` is edges per second of
 forward + backward; ``roofline`` reports the slowest of the three kernels
@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mid", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time the steps back to back without the cache flush")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 counter passes: a few steps plus a 512 MiB copy")
     args = ap.parse_args()
@@ -197,7 +199,7 @@ def main():
     t = timed(args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    warm = timed(args.steps, False)
+    warm = timed(args.steps, False) if args.warm else None
 
     kt = t.mean(axis=0)                      # ms per kernel: fwd, bwd_recv, bwd_send
     step_ms = float(t.sum(axis=1).mean())
@@ -230,8 +232,8 @@ def main():
                               for j, n in enumerate(names)},
         "step_hbm_frac": ab["step"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "fwd_hbm_frac": ab["fwd"] / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "warm_edges_per_s": E / (float(warm.sum(axis=1).mean()) * 1e-3),
-        "warm_kernel_ms": {n: float(v) for n, v in zip(names, warm.mean(axis=0))},
+        "warm_edges_per_s": None if warm is None else E / (float(warm.sum(axis=1).mean()) * 1e-3),
+        "warm_kernel_ms": None if warm is None else {n: float(v) for n, v in zip(names, warm.mean(axis=0))},
         "graph_build_ms": float(np.median(gb)),
         "wall_s_timed_region": wall,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
