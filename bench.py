@@ -7,11 +7,12 @@ harmonics to l = 2, every path with l3 <= 2, channel-wise weights) by
 default.  The graph grouping (CSR build) is timed separately: it runs once per
 neighbour list, not per layer.
 
-Timing: W untimed warm-up steps, then K timed steps.  Every kernel is timed
-with HIP events on the stream it is launched on (torch's current stream).
-Before each step a 1 GiB buffer is overwritten so that L2 and the 256 MB
-Infinity Cache hold none of the step's inputs: they come from HBM.  The same
-steps can also be timed back to back without the flush (``--warm``).
+Timing: W untimed warm-up steps, then K timed steps, each bracketed by a pair
+of HIP events on the stream the kernels run on (torch's current stream).
+Before each step a 1 GiB buffer is read so that L2 and the 256 MB Infinity
+Cache hold none of the step's inputs: they come from HBM.  Per-kernel launch
+durations (for the roofline) are event-timed over 10 back-to-back launches of
+that kernel after a flush.  ``--warm`` also times steps without the flush.
 
 Output: one JSON line (rank 0, N = 1).  ``value`` is edges per second of
 forward + backward; ``roofline`` reports the slowest of the three kernels
@@ -154,58 +155,85 @@ def main():
         tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None))
 
     if args.counters:
+        flush.fill_(1.0)
         for _ in range(3):
-            flush.fill_(1.0)
+            flush.sum()
             step()
         a = torch.empty(1 << 27, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         a.fill_(2.0)
+        flush.sum()
         b.copy_(a)                      # plain copy: 512 MiB read + 512 MiB written
         torch.cuda.synchronize()
         print(json.dumps({"counters_run": args.config, "copy_bytes": a.numel() * 4}))
         return
 
-    def timed(k, do_flush):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(k)]
-        for i in range(k):
-            if do_flush:
-                flush.fill_(float(i))
-            e = ev[i]
-            e[0].record()
-            tpc.forward(plan, g, x, Y, w, out=out)
-            e[1].record()
-            tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw))
-            e[2].record()
-            tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None))
-            e[3].record()
-        torch.cuda.synchronize()
-        t = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
-        return t
+    def do_flush():
+        # read 1 GiB: L2 and the Infinity Cache end up holding clean lines of
+        # an unrelated buffer (a write would leave dirty lines whose write-back
+        # competes with the next kernel's reads)
+        flush.sum()
 
+    def timed_steps(k, cold):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(k)]
+        for e0, e1 in ev:
+            if cold:
+                do_flush()
+            e0.record()
+            step()
+            e1.record()
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) for e0, e1 in ev])   # ms
+
+    kernels = {
+        "fwd": lambda: tpc.forward(plan, g, x, Y, w, out=out),
+        "bwd_recv": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw)),
+        "bwd_send": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None)),
+    }
+
+    def timed_kernel(fn, reps, rounds):
+        # launch duration amortised over back-to-back launches (an event pair
+        # around a single short launch mostly measures the event overhead)
+        res = []
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            do_flush()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / reps)
+        return np.array(res)
+
+    flush.fill_(1.0)
     # graph grouping, timed separately
     gb = []
     for _ in range(3):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        flush.fill_(0.0)
+        do_flush()
         e0.record()
         tpc.graph_build(src, dst, N, check=False)
         e1.record()
         torch.cuda.synchronize()
         gb.append(e0.elapsed_time(e1))
 
-    timed(args.warmup, True)
+    timed_steps(args.warmup, True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    t = timed(args.steps, True)
+    t = timed_steps(args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    warm = timed(args.steps, False) if args.warm else None
+    warm = timed_steps(args.steps, False) if args.warm else None
+    reps, rounds = 10, max(2, args.steps // 5)
+    kt_all = {n: timed_kernel(fn, reps, rounds) for n, fn in kernels.items()}
 
-    kt = t.mean(axis=0)                      # ms per kernel: fwd, bwd_recv, bwd_send
-    step_ms = float(t.sum(axis=1).mean())
+    names = ["fwd", "bwd_recv", "bwd_send"]
+    kt = np.array([kt_all[n].mean() for n in names])     # ms per launch
+    step_ms = float(t.mean())
     fwd_ms = float(kt[0])
     ab = algorithmic_bytes(N, E, P, U, ysh, plan.xdim, plan.outdim)
-    names = ["fwd", "bwd_recv", "bwd_send"]
     dom = names[int(np.argmax(kt))]
     dom_ms = float(kt[names.index(dom)])
     achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
@@ -227,13 +255,13 @@ def main():
                    "irreps": irreps, "lmax_sh": lsh, "lmax_out": lout, "paths": P,
                    "mode": "fwd+bwd", "cache": "L2+MALL flushed before each step"},
         "fwd_edges_per_s": E / (fwd_ms * 1e-3),
+        "fwd_edges_per_s_note": "forward kernel alone (launch duration); value is the whole step",
+        "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
         "kernel_ms": {n: float(v) for n, v in zip(names, kt)},
-        "kernel_ms_p10_p90": {n: [float(np.percentile(t[:, j], 10)), float(np.percentile(t[:, j], 90))]
-                              for j, n in enumerate(names)},
+        "kernel_ms_note": f"per launch, {reps} back-to-back launches after a cache flush, mean of {rounds}",
+        "kernel_hbm_frac": {n: ab[n] / (float(v) * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in zip(names, kt)},
         "step_hbm_frac": ab["step"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "fwd_hbm_frac": ab["fwd"] / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "warm_edges_per_s": None if warm is None else E / (float(warm.sum(axis=1).mean()) * 1e-3),
-        "warm_kernel_ms": None if warm is None else {n: float(v) for n, v in zip(names, warm.mean(axis=0))},
+        "warm_edges_per_s": None if warm is None else E / (float(warm.mean()) * 1e-3),
         "graph_build_ms": float(np.median(gb)),
         "wall_s_timed_region": wall,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,

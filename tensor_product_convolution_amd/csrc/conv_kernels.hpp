@@ -56,7 +56,8 @@ __device__ __forceinline__ void edge_fwd(const float (&xr)[S::XC], const float (
   });
 }
 
-// grad_w_p = sum_c g_c t_c ; grad_Y_b += sum_p w_p sum_nz C x_a g_c
+// Z_p[b] = sum_{a,c} C x_a g_c ; grad_w_p = sum_b Y_b Z_p[b] ; grad_Y_b += w_p Z_p[b]
+// (the products x_a g_c are shared by every path with the same (l1, output irrep))
 template <class S>
 __device__ __forceinline__ void edge_bwd_recv(const float (&xr)[S::XC], const float (&yr)[S::YC],
                                               const float (&wr)[S::NP], const float (&gr)[S::OC],
@@ -64,22 +65,17 @@ __device__ __forceinline__ void edge_bwd_recv(const float (&xr)[S::XC], const fl
   static_for<S::NP>([&](auto P) {
     constexpr PathInfo pi = S::paths.p[P];
     using T = CgPath<pi.l1, pi.l2, pi.l3>;
-    constexpr int D3 = 2 * pi.l3 + 1;
-    float t[D3];
-    static_for<D3>([&](auto C) { t[C] = 0.f; });
+    constexpr int D2 = 2 * pi.l2 + 1;
+    float z[D2];
+    static_for<D2>([&](auto B) { z[B] = 0.f; });
     static_for<T::nnz>([&](auto N) {
-      constexpr Nz z = T::table.e[N];
-      t[z.c] = fmaf(z.v, xr[pi.xo + z.a] * yr[pi.yo + z.b], t[z.c]);
+      constexpr Nz e = T::table.e[N];
+      z[e.b] = fmaf(e.v, xr[pi.xo + e.a] * gr[pi.ko + e.c], z[e.b]);
     });
     float s = 0.f;
-    static_for<D3>([&](auto C) { s = fmaf(gr[pi.ko + C], t[C], s); });
+    static_for<D2>([&](auto B) { s = fmaf(yr[pi.yo + B], z[B], s); });
     gw[P] = s;
-    float wg[D3];
-    static_for<D3>([&](auto C) { wg[C] = wr[P] * gr[pi.ko + C]; });
-    static_for<T::nnz>([&](auto N) {
-      constexpr Nz z = T::table.e[N];
-      gy[pi.yo + z.b] = fmaf(z.v, xr[pi.xo + z.a] * wg[z.c], gy[pi.yo + z.b]);
-    });
+    static_for<D2>([&](auto B) { gy[pi.yo + B] = fmaf(wr[P], z[B], gy[pi.yo + B]); });
   });
 }
 
@@ -183,168 +179,542 @@ struct InBlocks {
 };
 
 // ---------------------------------------------------------------------------
-// kernels
+// LDS staging of edge operands
+//
+// Each wave streams its edges through a private double buffer in LDS filled by
+// gfx950's direct global->LDS loads (global_load_lds_dwordx4: every lane moves
+// 16 bytes, one instruction moves 1 KB, no VGPRs involved).  While the wave
+// computes step k from buffer k&1, the loads of step k+1 fill the other
+// buffer; a wait on the vector-memory counter with the number of loads just
+// issued ensures step k's data has landed.  The edges of one wave step are
+// consecutive in the receiver-sorted order, so their weight and Y rows are one
+// contiguous run; x (or grad_out) rows are gathered row by row.  Indices past
+// the segment are clamped to its last edge so every load is in bounds.
 
-template <class S, int U, int WPB>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+// s_waitcnt vmcnt(n) (expcnt / lgkmcnt left at their maxima), n < 64
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+constexpr int ceil16(int bytes) { return (bytes + 15) / 16 * 16; }
+
+// Copy NR rows of RB bytes (RB % 16 == 0) to LDS at dst, rows back to back.
+// row(r) returns the global address of row r.  Issues ceil(NR*RB/1024) loads.
+// cache policy of a staging load: streams read once are non-temporal so they do
+// not evict data that is re-read (x rows, grad_out rows) from L2
+constexpr int kTemporal = 0;
+constexpr int kStream = 2;   // nt
+
+template <int NR, int RB, int POL = kTemporal, class RowFn>
+__device__ __forceinline__ void dma_rows16(char* dst, RowFn row, int lane) {
+  static_assert(RB % 16 == 0, "row bytes must be a multiple of 16");
+  constexpr int CH = RB / 16, N = NR * CH, INSTR = (N + 63) / 64;
+  static_for<INSTR>([&](auto K) {
+    const int c = K * 64 + lane;
+    if (K * 64 + 64 <= N || c < N) {
+      const int r = c / CH;
+      const char* src = row(r) + (c - r * CH) * 16;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(dst + K * 1024), 16, 0, POL);
+    }
+  });
+}
+template <int NR, int RB>
+constexpr int dma16_count() { return (NR * (RB / 16) + 63) / 64; }
+
+// Same with 4-byte granules (rows of any multiple of 4 bytes).
+template <int NR, int RB, int POL = kTemporal, class RowFn>
+__device__ __forceinline__ void dma_rows4(char* dst, RowFn row, int lane) {
+  static_assert(RB % 4 == 0, "row bytes must be a multiple of 4");
+  constexpr int CH = RB / 4, N = NR * CH, INSTR = (N + 63) / 64;
+  static_for<INSTR>([&](auto K) {
+    const int c = K * 64 + lane;
+    if (K * 64 + 64 <= N || c < N) {
+      const int r = c / CH;
+      const char* src = row(r) + (c - r * CH) * 4;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(dst + K * 256), 4, 0, POL);
+    }
+  });
+}
+template <int NR, int RB>
+constexpr int dma4_count() { return (NR * (RB / 4) + 63) / 64; }
+
+// select v[r] from a small wave-uniform array with a constant-index chain
+template <int N>
+__device__ __forceinline__ int pick(const int (&v)[N], int r) {
+  int o = v[0];
+#pragma unroll
+  for (int t = 1; t < N; ++t) o = r == t ? v[t] : o;
+  return o;
+}
+
+// Per-wave staging layout for receiver-grouped passes: [W | Y | X] per buffer.
+template <class S, int U>
+struct RecvStage {
+  static constexpr int EPW = LaneMap<U>::EPW;
+  static constexpr int WB = S::NP * U * 4;       // weight row bytes
+  static constexpr int YB = S::YC * 4;           // Y row bytes
+  static constexpr int XB = S::XC * U * 4;       // x row bytes
+  static constexpr int W_OFF = 0;
+  static constexpr int Y_OFF = ceil16(EPW * WB);
+  static constexpr int X_OFF = Y_OFF + ceil16(EPW * YB);
+  static constexpr int BUF = X_OFF + EPW * XB;   // bytes per buffer
+  static constexpr int NLOADS = dma16_count<EPW, WB>() + dma4_count<EPW, YB>() + dma16_count<EPW, XB>();
+};
+
+// issue the loads of the wave step starting at segment position q0
+template <class S, int U>
+__device__ __forceinline__ void stage_recv(char* buf, const float* __restrict__ x,
+                                           const float* __restrict__ Y, const float* __restrict__ w,
+                                           const int (&j)[LaneMap<U>::EPW], int q0, int last,
+                                           int lane) {
+  using T = RecvStage<S, U>;
+  dma_rows16<T::EPW, T::WB, kStream>(buf + T::W_OFF, [&](int r) {
+    return (const char*)(w + (size_t)min(q0 + r, last) * (S::NP * U));
+  }, lane);
+  dma_rows4<T::EPW, T::YB, kStream>(buf + T::Y_OFF, [&](int r) {
+    return (const char*)(Y + (size_t)min(q0 + r, last) * S::YC);
+  }, lane);
+  dma_rows16<T::EPW, T::XB>(buf + T::X_OFF, [&](int r) {
+    return (const char*)(x + (size_t)pick(j, r) * (S::XC * U));
+  }, lane);
+}
+
+// read this lane's operands of its edge slot from a staged buffer
+template <class S, int U>
+__device__ __forceinline__ void read_recv(const char* buf, int slot, int uu,
+                                          float (&xr)[LaneMap<U>::CPL][S::XC], float (&yr)[S::YC],
+                                          float (&wr)[LaneMap<U>::CPL][S::NP]) {
+  using T = RecvStage<S, U>;
+  const float* W = (const float*)(buf + T::W_OFF) + slot * (S::NP * U);
+  const float* Yv = (const float*)(buf + T::Y_OFF) + slot * S::YC;
+  const float* X = (const float*)(buf + T::X_OFF) + slot * (S::XC * U);
+#pragma unroll
+  for (int b = 0; b < S::YC; ++b) yr[b] = Yv[b];
+#pragma unroll
+  for (int p = 0; p < S::NP; ++p)
+#pragma unroll
+    for (int cc = 0; cc < LaneMap<U>::CPL; ++cc) wr[cc][p] = W[p * U + uu + 64 * cc];
+  static_for<S::NIN>([&](auto I) {
+    constexpr int d = 2 * S::ls.v[I] + 1;
+    constexpr int xo = S::xoff(I);
+#pragma unroll
+    for (int cc = 0; cc < LaneMap<U>::CPL; ++cc) {
+      const float* p = X + U * xo + (uu + 64 * cc) * d;
+      static_for<d>([&](auto A) { xr[cc][xo + A] = p[A]; });
+    }
+  });
+}
+
+// sender-grouped pass: [W | Y | G] per buffer, all rows gathered
+template <class S, int U>
+struct SendStage {
+  static constexpr int EPW = LaneMap<U>::EPW;
+  static constexpr int WB = S::NP * U * 4;
+  static constexpr int YB = S::YC * 4;
+  static constexpr int GB = S::OC * U * 4;
+  static constexpr int W_OFF = 0;
+  static constexpr int Y_OFF = ceil16(EPW * WB);
+  static constexpr int G_OFF = Y_OFF + ceil16(EPW * YB);
+  static constexpr int BUF = G_OFF + EPW * GB;
+  static constexpr int NLOADS = dma16_count<EPW, WB>() + dma4_count<EPW, YB>() + dma16_count<EPW, GB>();
+};
+
+template <class S, int U>
+__device__ __forceinline__ void stage_send(char* buf, const float* __restrict__ Y,
+                                           const float* __restrict__ w, const float* __restrict__ g,
+                                           const int (&q)[LaneMap<U>::EPW],
+                                           const int (&i)[LaneMap<U>::EPW], int lane) {
+  using T = SendStage<S, U>;
+  dma_rows16<T::EPW, T::WB, kStream>(buf + T::W_OFF, [&](int r) {
+    return (const char*)(w + (size_t)pick(q, r) * (S::NP * U));
+  }, lane);
+  dma_rows4<T::EPW, T::YB, kStream>(buf + T::Y_OFF, [&](int r) {
+    return (const char*)(Y + (size_t)pick(q, r) * S::YC);
+  }, lane);
+  dma_rows16<T::EPW, T::GB>(buf + T::G_OFF, [&](int r) {
+    return (const char*)(g + (size_t)pick(i, r) * (S::OC * U));
+  }, lane);
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+//
+// Slot s of wave v owns segment positions beg + v*EPW + s + k*SLOTS.  Every
+// wave runs the trip count of its first slot; a slot past the segment works on
+// the clamped last edge and its contribution is masked (forward, sender pass)
+// or it rewrites exactly the values of that edge (receiver pass).
+//
+// Pipeline: NBUF staging buffers per wave; step k is computed from buffer
+// k % NBUF while the loads of steps k+1 .. k+NBUF-1 are in flight.  Before
+// computing step k the wave waits until at most "ops issued after step k's
+// loads" vector-memory operations are outstanding; that count is exact
+// (DMA loads per step, plus the receiver pass's per-step stores), so the wait
+// never drains the loads of later steps.
+
+template <int U, int WPB>
+__device__ __forceinline__ int wave_trips(int beg, int end, int wv) {
+  using M = LaneMap<U>;
+  constexpr int SLOTS = WPB * M::EPW;
+  const int first = beg + wv * M::EPW;
+  const int n = first < end ? (end - first + SLOTS - 1) / SLOTS : 0;
+  return __builtin_amdgcn_readfirstlane(n);
+}
+
+// wait for vmcnt <= ahead*NL + sg*NS with ahead, sg in [0, NA) x [0, NSG)
+template <int NA, int NSG, int NL, int NS>
+__device__ __forceinline__ void wait_steps(int ahead, int sg) {
+  static_for<NA>([&](auto A) {
+    static_for<NSG>([&](auto G) {
+      if (ahead == A && sg == G) wait_vmcnt<A * NL + G * NS>();
+    });
+  });
+}
+
+// Launch configuration of a signature / multiplicity: waves per block and
+// staging depth, bounded by the 63 outstanding vector-memory operations a wave
+// can count and by 64 KB of LDS per workgroup.
+template <class S, int U>
+struct Cfg {
+  using M = LaneMap<U>;
+  using R = RecvStage<S, U>;
+  using Sd = SendStage<S, U>;
+  // receiver pass stores per step and lane: one word per path and channel set
+  // (grad_w), one word per LPE harmonic components (grad_Y)
+  static constexpr int ST_W = S::NP * M::CPL;
+  static constexpr int ST_Y = (S::YC + M::LPE - 1) / M::LPE;
+  static constexpr int NST = ST_W + ST_Y;
+  // Staging depth: double buffering (deeper pipelines measured slower on the
+  // 1,536-atom workload), single buffering when a step has too many memory
+  // operations to count or the buffers would exceed the LDS budget.
+  static constexpr int depth(int nl, int buf, int waves) {
+    return (nl <= 63 && 2 * buf * waves <= 64 * 1024) ? 2 : 1;
+  }
+  static constexpr bool fits(int buf, int nbuf, int waves) { return buf * nbuf * waves <= 64 * 1024;
+  }
+  // waves per workgroup of each pass (one if a single buffer per wave for two
+  // waves would not fit)
+  static constexpr int LDS = 64 * 1024;
+  static constexpr int WPB_F = 2 * R::BUF <= LDS ? 2 : 1;
+  static constexpr int WPB_R = 2 * R::BUF <= LDS ? 2 : 1;
+  static constexpr int WPB_S = (U <= 32 || 2 * Sd::BUF > LDS) ? 1 : 2;
+  static constexpr int NBUF_F = depth(R::NLOADS, R::BUF, WPB_F);
+  static constexpr int NBUF_R = depth(R::NLOADS + NST, R::BUF, WPB_R);
+  static constexpr int NBUF_S = depth(Sd::NLOADS, Sd::BUF, WPB_S);
+  static_assert(fits(R::BUF, NBUF_F, WPB_F) && fits(R::BUF, NBUF_R, WPB_R) &&
+                    fits(Sd::BUF, NBUF_S, WPB_S), "staging exceeds 64 KB of LDS");
+};
+
+template <class S, int U, int WPB, int NBUF>
+struct FwdSmem {
+  static constexpr int STAGE = NBUF * WPB * RecvStage<S, U>::BUF;
+  static constexpr int RED = WPB * LaneMap<U>::CPL * S::OC * 65 * 4;
+  static constexpr int BYTES = STAGE > RED ? STAGE : RED;
+};
+
+template <class S, int U, int WPB, int NBUF>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                const float* __restrict__ x, const float* __restrict__ Y,
                const float* __restrict__ w, float* __restrict__ out) {
   using M = LaneMap<U>;
-  constexpr int XD = U * S::XC, OD = U * S::OC, SLOTS = WPB * M::EPW;
-  __shared__ float red[WPB * M::CPL * S::OC * 65];
+  using T = RecvStage<S, U>;
+  constexpr int OD = U * S::OC, SLOTS = WPB * M::EPW, EPW = M::EPW;
+  static_assert((NBUF - 1) * T::NLOADS < 64, "pipeline too deep for vmcnt");
+  __shared__ __attribute__((aligned(16))) char smem[FwdSmem<S, U, WPB, NBUF>::BYTES];
   const int i = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
+  const int last = end - 1;
   float acc[M::CPL][S::OC];
 #pragma unroll
   for (int cc = 0; cc < M::CPL; ++cc)
 #pragma unroll
     for (int o = 0; o < S::OC; ++o) acc[cc][o] = 0.f;
-  for (int q = beg + wv * M::EPW + slot; q < end; q += SLOTS) {
-    const int j = col[q];
-    float xr[M::CPL][S::XC];
-    load_xrow<S, U>(x + (size_t)j * XD, uu, xr);
-    float yr[S::YC];
+  const int trips = wave_trips<U, WPB>(beg, end, wv);
+  char* mybuf = smem + wv * NBUF * T::BUF;
+  // first position of this wave (wave-uniform, so the index loads are scalar)
+  const int q00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
+  if (trips > 0) {
+    int jn[EPW];
+    // prologue: stage steps 0 .. NBUF-2
 #pragma unroll
-    for (int b = 0; b < S::YC; ++b) yr[b] = Y[(size_t)q * S::YC + b];
-    float wr[M::CPL][S::NP];
+    for (int b = 0; b < NBUF - 1; ++b) {
+      if (b < trips) {
 #pragma unroll
-    for (int p = 0; p < S::NP; ++p)
+        for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + b * SLOTS + r, last)];
+        stage_recv<S, U>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
+      }
+    }
 #pragma unroll
-      for (int cc = 0; cc < M::CPL; ++cc) wr[cc][p] = w[((size_t)q * S::NP + p) * U + uu + 64 * cc];
+    for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + (NBUF - 1) * SLOTS + r, last)];
+    for (int k = 0; k < trips; ++k) {
+      const int q0 = q00 + k * SLOTS;
+      const char* cur = mybuf + (k % NBUF) * T::BUF;
+      int ahead = trips - 1 - k;
+      if (ahead >= NBUF - 1) {
+        ahead = NBUF - 1;
+        stage_recv<S, U>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, x, Y, w, jn,
+                         q0 + (NBUF - 1) * SLOTS, last, lane);
+      }
+      wait_steps<NBUF, 1, T::NLOADS, 0>(ahead, 0);
+      float xr[M::CPL][S::XC], yr[S::YC], wr[M::CPL][S::NP];
+      read_recv<S, U>(cur, slot, uu, xr, yr, wr);
+      __builtin_amdgcn_sched_barrier(0);
+      // senders of the next step to stage, loaded while this step computes
 #pragma unroll
-    for (int cc = 0; cc < M::CPL; ++cc) edge_fwd<S>(xr[cc], yr, wr[cc], acc[cc]);
+      for (int r = 0; r < EPW; ++r) jn[r] = col[min(q0 + NBUF * SLOTS + r, last)];
+      const float m = q0 + slot < end ? 1.f : 0.f;
+#pragma unroll
+      for (int cc = 0; cc < M::CPL; ++cc) {
+#pragma unroll
+        for (int p = 0; p < S::NP; ++p) wr[cc][p] *= m;
+        edge_fwd<S>(xr[cc], yr, wr[cc], acc[cc]);
+      }
+    }
   }
-  block_reduce_store<U, WPB, S::OC, S::NO>(acc, red, out + (size_t)i * OD, OutBlocks<S>{});
+  __syncthreads();   // staging buffers become the reduction buffer
+  block_reduce_store<U, WPB, S::OC, S::NO>(acc, (float*)smem, out + (size_t)i * OD, OutBlocks<S>{});
 }
 
-template <class S, int U, int WPB>
+// MODE bit 0: write grad_w; bit 1: write grad_Y
+template <class S, int U, int WPB, int NBUF, int MODE>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_bwd_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                     const float* __restrict__ x, const float* __restrict__ Y,
                     const float* __restrict__ w, const float* __restrict__ g,
                     float* __restrict__ grad_w, float* __restrict__ grad_Y) {
   using M = LaneMap<U>;
-  constexpr int XD = U * S::XC, OD = U * S::OC, SLOTS = WPB * M::EPW;
+  using T = RecvStage<S, U>;
+  using C = Cfg<S, U>;
+  constexpr int OD = U * S::OC, SLOTS = WPB * M::EPW, EPW = M::EPW;
+  constexpr int NST = ((MODE & 1) ? C::ST_W : 0) + ((MODE & 2) ? C::ST_Y : 0);
+  static_assert((NBUF - 1) * (T::NLOADS + NST) < 64, "pipeline too deep for vmcnt");
+  constexpr int WAVE_LDS = NBUF * T::BUF;
+  __shared__ __attribute__((aligned(16))) char smem[WPB * WAVE_LDS];
   const int i = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
-  if (beg >= end) return;
+  const int last = end - 1;
+  const int trips = wave_trips<U, WPB>(beg, end, wv);
+  if (trips == 0) return;
   float gr[M::CPL][S::OC];
   load_orow<S, U>(g + (size_t)i * OD, uu, gr);
-  for (int q = beg + wv * M::EPW + slot; q < end; q += SLOTS) {
-    const int j = col[q];
-    float xr[M::CPL][S::XC];
-    load_xrow<S, U>(x + (size_t)j * XD, uu, xr);
-    float yr[S::YC];
+  // grad_out must have landed before the pipelined loop starts: a wait for it
+  // inside the loop would also wait for the staging loads in flight
+  wait_vmcnt<0>();
+  char* mybuf = smem + wv * WAVE_LDS;
+  const int q00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
+  int jn[EPW];
 #pragma unroll
-    for (int b = 0; b < S::YC; ++b) yr[b] = Y[(size_t)q * S::YC + b];
-    float wr[M::CPL][S::NP];
+  for (int b = 0; b < NBUF - 1; ++b) {
+    if (b < trips) {
 #pragma unroll
-    for (int p = 0; p < S::NP; ++p)
+      for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + b * SLOTS + r, last)];
+      stage_recv<S, U>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
+    }
+  }
 #pragma unroll
-      for (int cc = 0; cc < M::CPL; ++cc) wr[cc][p] = w[((size_t)q * S::NP + p) * U + uu + 64 * cc];
+  for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + (NBUF - 1) * SLOTS + r, last)];
+  // Results of step k are stored during step k+1, after its wait, straight
+  // from registers; the number of store instructions per step is fixed (NST).
+  float pgw[M::CPL][S::NP], pgy[(S::YC + M::LPE - 1) / M::LPE];
+  size_t pq = 0;
+  auto flush = [&]() {
+    if constexpr (MODE & 1) {
+#pragma unroll
+      for (int cc = 0; cc < M::CPL; ++cc)
+#pragma unroll
+        for (int p = 0; p < S::NP; ++p)
+          __builtin_nontemporal_store(pgw[cc][p], grad_w + (pq * S::NP + p) * U + uu + 64 * cc);
+    }
+    if constexpr (MODE & 2) {
+#pragma unroll
+      for (int r = 0; r < (S::YC + M::LPE - 1) / M::LPE; ++r) {
+        const int b = uu + r * M::LPE;
+        if (b < S::YC) __builtin_nontemporal_store(pgy[r], grad_Y + pq * S::YC + b);
+      }
+    }
+  };
+  for (int k = 0; k < trips; ++k) {
+    const int q0 = q00 + k * SLOTS;
+    const char* cur = mybuf + (k % NBUF) * T::BUF;
+    int ahead = trips - 1 - k;
+    if (ahead >= NBUF - 1) {
+      ahead = NBUF - 1;
+      stage_recv<S, U>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, x, Y, w, jn,
+                       q0 + (NBUF - 1) * SLOTS, last, lane);
+    }
+    // store groups issued after this step's loads: steps max(1, k-NBUF+1) .. k-1
+    const int sg = k - 1 < NBUF - 1 ? (k - 1 > 0 ? k - 1 : 0) : NBUF - 1;
+    wait_steps<NBUF, NBUF, T::NLOADS, NST>(ahead, sg);
+    if (k > 0) flush();
+    float xr[M::CPL][S::XC], yr[S::YC], wr[M::CPL][S::NP];
+    read_recv<S, U>(cur, slot, uu, xr, yr, wr);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < EPW; ++r) jn[r] = col[min(q0 + NBUF * SLOTS + r, last)];
     float gy[S::YC];
 #pragma unroll
     for (int b = 0; b < S::YC; ++b) gy[b] = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < M::CPL; ++cc) {
-      float gw[S::NP];
-      edge_bwd_recv<S>(xr[cc], yr, wr[cc], gr[cc], gw, gy);
-      if (grad_w) {
-#pragma unroll
-        for (int p = 0; p < S::NP; ++p) grad_w[((size_t)q * S::NP + p) * U + uu + 64 * cc] = gw[p];
-      }
-    }
-    if (grad_Y) {
-      // sum over the edge's channel lanes (partners stay inside the slot)
+    for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_recv<S>(xr[cc], yr, wr[cc], gr[cc], pgw[cc], gy);
+    if constexpr (MODE & 2) {
+      // sum over the edge's channel lanes (partners stay inside the slot);
+      // lane uu then keeps components uu, uu + LPE, ...
 #pragma unroll
       for (int b = 0; b < S::YC; ++b)
 #pragma unroll
         for (int off = 1; off < M::LPE; off <<= 1) gy[b] += __shfl_xor(gy[b], off, 64);
-      for (int b = uu; b < S::YC; b += M::LPE) {
+#pragma unroll
+      for (int r = 0; r < (S::YC + M::LPE - 1) / M::LPE; ++r) {
+        const int b = uu + r * M::LPE;
         float v = 0.f;
 #pragma unroll
-        for (int bb = 0; bb < S::YC; ++bb)
-          if (bb == b) v = gy[bb];
-        grad_Y[(size_t)q * S::YC + b] = v;
+        for (int bb = 0; bb < S::YC; ++bb) v = (bb == b) ? gy[bb] : v;
+        pgy[r] = v;
       }
     }
+    pq = (size_t)min(q0 + slot, last);
   }
+  flush();
 }
 
-template <class S, int U, int WPB>
+template <class S, int U, int WPB, int NBUF>
+struct SendSmem {
+  static constexpr int STAGE = NBUF * WPB * SendStage<S, U>::BUF;
+  static constexpr int RED = WPB * LaneMap<U>::CPL * S::XC * 65 * 4;
+  static constexpr int BYTES = STAGE > RED ? STAGE : RED;
+};
+
+template <class S, int U, int WPB, int NBUF>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_bwd_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                     const int32_t* __restrict__ t_col, const float* __restrict__ Y,
                     const float* __restrict__ w, const float* __restrict__ g,
                     float* __restrict__ grad_x) {
   using M = LaneMap<U>;
-  constexpr int XD = U * S::XC, OD = U * S::OC, SLOTS = WPB * M::EPW;
-  __shared__ float red[WPB * M::CPL * S::XC * 65];
+  using T = SendStage<S, U>;
+  constexpr int XD = U * S::XC, SLOTS = WPB * M::EPW, EPW = M::EPW;
+  static_assert((NBUF - 1) * T::NLOADS < 64, "pipeline too deep for vmcnt");
+  __shared__ __attribute__((aligned(16))) char smem[SendSmem<S, U, WPB, NBUF>::BYTES];
   const int j = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
+  const int last = end - 1;
   float gx[M::CPL][S::XC];
 #pragma unroll
   for (int cc = 0; cc < M::CPL; ++cc)
 #pragma unroll
     for (int a = 0; a < S::XC; ++a) gx[cc][a] = 0.f;
-  for (int k = beg + wv * M::EPW + slot; k < end; k += SLOTS) {
-    const int q = t_perm[k];
-    const int i = t_col[k];
-    float gr[M::CPL][S::OC];
-    load_orow<S, U>(g + (size_t)i * OD, uu, gr);
-    float yr[S::YC];
+  const int trips = wave_trips<U, WPB>(beg, end, wv);
+  char* mybuf = smem + wv * NBUF * T::BUF;
+  const int k00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
+  if (trips > 0) {
+    int qn[EPW], in[EPW];
 #pragma unroll
-    for (int b = 0; b < S::YC; ++b) yr[b] = Y[(size_t)q * S::YC + b];
-    float wr[M::CPL][S::NP];
+    for (int b = 0; b < NBUF - 1; ++b) {
+      if (b < trips) {
 #pragma unroll
-    for (int p = 0; p < S::NP; ++p)
+        for (int r = 0; r < EPW; ++r) {
+          qn[r] = t_perm[min(k00 + b * SLOTS + r, last)];
+          in[r] = t_col[min(k00 + b * SLOTS + r, last)];
+        }
+        stage_send<S, U>(mybuf + b * T::BUF, Y, w, g, qn, in, lane);
+      }
+    }
 #pragma unroll
-      for (int cc = 0; cc < M::CPL; ++cc) wr[cc][p] = w[((size_t)q * S::NP + p) * U + uu + 64 * cc];
+    for (int r = 0; r < EPW; ++r) {
+      qn[r] = t_perm[min(k00 + (NBUF - 1) * SLOTS + r, last)];
+      in[r] = t_col[min(k00 + (NBUF - 1) * SLOTS + r, last)];
+    }
+    for (int k = 0; k < trips; ++k) {
+      const int k0 = k00 + k * SLOTS;
+      const char* cur = mybuf + (k % NBUF) * T::BUF;
+      int ahead = trips - 1 - k;
+      if (ahead >= NBUF - 1) {
+        ahead = NBUF - 1;
+        stage_send<S, U>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, Y, w, g, qn, in, lane);
+      }
+      wait_steps<NBUF, 1, T::NLOADS, 0>(ahead, 0);
+      const float* W = (const float*)(cur + T::W_OFF) + slot * (S::NP * U);
+      const float* Yv = (const float*)(cur + T::Y_OFF) + slot * S::YC;
+      const float* G = (const float*)(cur + T::G_OFF) + slot * (S::OC * U);
+      float yr[S::YC], wr[M::CPL][S::NP], gr[M::CPL][S::OC];
 #pragma unroll
-    for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_send<S>(yr, wr[cc], gr[cc], gx[cc]);
+      for (int b = 0; b < S::YC; ++b) yr[b] = Yv[b];
+      const float m = k0 + slot < end ? 1.f : 0.f;
+#pragma unroll
+      for (int cc = 0; cc < M::CPL; ++cc) {
+#pragma unroll
+        for (int p = 0; p < S::NP; ++p) wr[cc][p] = W[p * U + uu + 64 * cc];
+        static_for<S::NO>([&](auto K) {
+          constexpr OutInfo oi = S::outs.o[K];
+          constexpr int d = 2 * oi.l + 1;
+          const float* pg = G + U * oi.ko + (uu + 64 * cc) * d;
+          static_for<d>([&](auto C) { gr[cc][oi.ko + C] = pg[C]; });
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < EPW; ++r) {
+        qn[r] = t_perm[min(k0 + NBUF * SLOTS + r, last)];
+        in[r] = t_col[min(k0 + NBUF * SLOTS + r, last)];
+      }
+#pragma unroll
+      for (int cc = 0; cc < M::CPL; ++cc) {
+#pragma unroll
+        for (int p = 0; p < S::NP; ++p) wr[cc][p] *= m;
+        edge_bwd_send<S>(yr, wr[cc], gr[cc], gx[cc]);
+      }
+    }
   }
-  block_reduce_store<U, WPB, S::XC, S::NIN>(gx, red, grad_x + (size_t)j * XD, InBlocks<S>{});
+  __syncthreads();
+  block_reduce_store<U, WPB, S::XC, S::NIN>(gx, (float*)smem, grad_x + (size_t)j * XD, InBlocks<S>{});
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 
-template <int U>
-struct Wpb {
-  static constexpr int value = 4;
-};
-
 template <class S, int U>
 hipError_t launch_fwd(const ConvArgs& a) {
-  constexpr int WPB = Wpb<U>::value;
+  using C = Cfg<S, U>;
   if (a.n_nodes == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_conv_fwd<S, U, WPB>), dim3(a.n_nodes), dim3(WPB * 64), 0, a.stream,
-                     a.row_ptr, a.col, a.x, a.Y, a.w, a.out);
+  hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F, C::NBUF_F>), dim3(a.n_nodes), dim3(C::WPB_F * 64), 0,
+                     a.stream, a.row_ptr, a.col, a.x, a.Y, a.w, a.out);
   return hipGetLastError();
 }
 
 template <class S, int U>
 hipError_t launch_bwd_recv(const ConvArgs& a) {
-  constexpr int WPB = Wpb<U>::value;
+  using C = Cfg<S, U>;
   if (a.n_nodes == 0 || a.n_edges == 0 || (!a.grad_w && !a.grad_Y)) return hipSuccess;
-  hipLaunchKernelGGL((k_conv_bwd_recv<S, U, WPB>), dim3(a.n_nodes), dim3(WPB * 64), 0, a.stream,
-                     a.row_ptr, a.col, a.x, a.Y, a.w, a.grad_out, a.grad_w, a.grad_Y);
+  const dim3 grid(a.n_nodes), block(C::WPB_R * 64);
+  if (a.grad_w && a.grad_Y)
+    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 3>), grid, block, 0, a.stream,
+                       a.row_ptr, a.col, a.x, a.Y, a.w, a.grad_out, a.grad_w, a.grad_Y);
+  else if (a.grad_w)
+    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 1>), grid, block, 0, a.stream,
+                       a.row_ptr, a.col, a.x, a.Y, a.w, a.grad_out, a.grad_w, a.grad_Y);
+  else
+    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 2>), grid, block, 0, a.stream,
+                       a.row_ptr, a.col, a.x, a.Y, a.w, a.grad_out, a.grad_w, a.grad_Y);
   return hipGetLastError();
 }
 
 template <class S, int U>
 hipError_t launch_bwd_send(const ConvArgs& a) {
-  constexpr int WPB = Wpb<U>::value;
+  using C = Cfg<S, U>;
   if (a.n_nodes == 0 || !a.grad_x) return hipSuccess;
-  hipLaunchKernelGGL((k_conv_bwd_send<S, U, WPB>), dim3(a.n_nodes), dim3(WPB * 64), 0, a.stream,
-                     a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.w, a.grad_out, a.grad_x);
+  hipLaunchKernelGGL((k_conv_bwd_send<S, U, C::WPB_S, C::NBUF_S>), dim3(a.n_nodes), dim3(C::WPB_S * 64), 0,
+                     a.stream, a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.w, a.grad_out, a.grad_x);
   return hipGetLastError();
 }
 
