@@ -184,6 +184,39 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
                            const float* Y, const float* w, const float* grad_out,
                            float* grad_x, float* grad_Y, float* grad_w, hipStream_t stream);
 
+/* ---- channel mix ("uvw", dense; fp32 MFMA) ----------------------------------
+ * One U x U matrix per output irrep k (Wmix [K][U][U], K = number of output
+ * irreps, U = 16, 32, 64 or 128; 1e and 1o never mix):
+ *   out[i, k, v, c] = sum_u Wmix[k][u][v] in[i, k, u, c]       (in, out: [N][outdim])
+ * The post-aggregation channel mixing of the radial-weight layer ("Sobek",
+ * Abstract, on preserving multiplicity mixing).  in and out must not alias. */
+tp_status tp_conv_uvw_forward(tp_plan_t plan, int32_t n_nodes, const float* Wmix, const float* in,
+                              float* out, hipStream_t stream);
+
+/* Adjoint of tp_conv_uvw_forward for grad_out = d<.,out>:
+ *   grad_in[i, k, u, c] = sum_v Wmix[k][u][v] grad_out[i, k, v, c]   (NULL: skip)
+ *   grad_Wmix[k][u][v]  = sum_{i,c} in[i, k, u, c] grad_out[i, k, v, c]  (NULL: skip)
+ * grad_Wmix is reduced deterministically through ws (tp_conv_uvw_workspace
+ * bytes). */
+tp_status tp_conv_uvw_backward(tp_plan_t plan, int32_t n_nodes, const float* Wmix, const float* in,
+                               const float* grad_out, float* grad_in, float* grad_Wmix, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+tp_status tp_conv_uvw_workspace(tp_plan_t plan, size_t* bytes);
+
+/* ---- radial-weight convolution (plan with radial_basis / radial_hidden) ----
+ * Edge weights come from a radial network of the edge length r_len[E]
+ * (receiver-sorted), computed on chip and never stored ("Sobek", Abstract and
+ * AI Summary: radial projection reassociated with coupling and aggregation):
+ *   B_n(r) = sqrt(2/r_cut) sin(n pi r / r_cut) / r, n = 1..radial_basis
+ *   w[e, p, u] = (SiLU(B(r_e) W1) W2)[p*U + u]
+ * W1 [radial_basis][radial_hidden], W2 [radial_hidden][P*U] (device float32).
+ * With Wmix (NULL: no mix) the aggregated output is written to out_pre and
+ * the mixed output to out (tp_conv_uvw_forward); without it, to out. */
+tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                 const float* Y, const float* r_len, const float* W1,
+                                 const float* W2, const float* Wmix, float* out_pre, float* out,
+                                 hipStream_t stream);
+
 /* Thread-local description of the last failure on this thread. */
 const char* tp_conv_last_error(void);
 

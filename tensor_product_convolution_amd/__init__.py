@@ -26,7 +26,8 @@ EXPORTS = (
     "tp_conv_plan_create", "tp_conv_plan_info", "tp_conv_plan_paths", "tp_conv_plan_cg",
     "tp_conv_plan_destroy", "tp_cg_real", "tp_conv_graph_workspace", "tp_conv_graph_build",
     "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
-    "tp_conv_last_error",
+    "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
+    "tp_conv_forward_radial", "tp_conv_last_error",
 )
 
 
@@ -77,6 +78,11 @@ def lib():
         "tp_conv_sph_harm": (I32, [I32, VP, I32, VP, VP]),
         "tp_conv_forward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
+        "tp_conv_uvw_forward": (I32, [P, I32, VP, VP, VP, VP]),
+        "tp_conv_uvw_backward": (I32, [P, I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
+        "tp_conv_uvw_workspace": (I32, [P, ctypes.POINTER(SZ)]),
+        "tp_conv_forward_radial": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
+                                         VP]),
         "tp_conv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -131,10 +137,17 @@ def cg_real(l1, l2, l3):
 class Plan:
     """Paths, output irreps and CG tables of a channel-wise product (host only)."""
 
-    def __init__(self, irreps_in, lmax_sh, lmax_out, mode=0):
+    def __init__(self, irreps_in, lmax_sh, lmax_out, mode=0, radial=None, uvw=False):
+        """radial: (n_basis, hidden, r_cut) for radial-network edge weights."""
         h = ctypes.c_void_p()
+        opts = None
+        if radial is not None or uvw:
+            nb, nh, rc = radial if radial is not None else (0, 0, 0.0)
+            opts = ctypes.byref(_Opts(nb, nh, rc, 1 if uvw else 0))
         _check(lib().tp_conv_plan_create(ctypes.byref(h), irreps_in.encode(), lmax_sh, lmax_out,
-                                         mode, None))
+                                         mode, opts))
+        self.radial = radial
+        self.uvw = uvw
         self._h = h
         self.irreps_in = irreps_in
         self.lmax_sh, self.lmax_out = lmax_sh, lmax_out
@@ -273,3 +286,62 @@ def backward(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=None):
                                   _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw),
                                   _stream(x.device)))
     return gx, gY, gw
+
+
+def uvw_forward(plan, Wmix, x_in, out=None):
+    """Per-output-irrep U x U channel mix of node rows x_in [N, outdim]."""
+    torch = _torch()
+    N = x_in.shape[0]
+    _need(x_in, "in", torch.float32, (N, plan.outdim))
+    K = len(plan.out_irreps.split("+"))
+    _need(Wmix, "Wmix", torch.float32, (K, plan.mul, plan.mul))
+    if out is None:
+        out = torch.empty_like(x_in)
+    _check(lib().tp_conv_uvw_forward(plan.handle, N, _ptr(Wmix), _ptr(x_in), _ptr(out),
+                                     _stream(x_in.device)))
+    return out
+
+
+def uvw_backward(plan, Wmix, x_in, grad_out, want=("in", "W")):
+    """(grad_in, grad_Wmix) of the channel mix; entries not in ``want`` are None."""
+    torch = _torch()
+    N = grad_out.shape[0]
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    K = len(plan.out_irreps.split("+"))
+    _need(Wmix, "Wmix", torch.float32, (K, plan.mul, plan.mul))
+    gi = torch.empty_like(grad_out) if "in" in want else None
+    gW = torch.empty_like(Wmix) if "W" in want else None
+    ws, nbytes = None, 0
+    if gW is not None:
+        _need(x_in, "in", torch.float32, (N, plan.outdim))
+        b = ctypes.c_size_t()
+        _check(lib().tp_conv_uvw_workspace(plan.handle, ctypes.byref(b)))
+        nbytes = b.value
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=grad_out.device)
+    _check(lib().tp_conv_uvw_backward(plan.handle, N, _ptr(Wmix), _ptr(x_in), _ptr(grad_out),
+                                      _ptr(gi), _ptr(gW), _ptr(ws), nbytes,
+                                      _stream(grad_out.device)))
+    return gi, gW
+
+
+def forward_radial(plan, graph, x, Y, r_len, W1, W2, Wmix=None, out=None, out_pre=None):
+    """(out, out_pre) of the radial-weight convolution; out_pre is None without a mix."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    nb, nh, _ = plan.radial
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(r_len, "r_len", torch.float32, (E,))
+    _need(W1, "W1", torch.float32, (nb, nh))
+    _need(W2, "W2", torch.float32, (nh, plan.n_paths * plan.mul))
+    f32 = dict(dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((N, plan.outdim), **f32)
+    if Wmix is not None and out_pre is None:
+        out_pre = torch.empty((N, plan.outdim), **f32)
+    g = graph.cstruct()
+    _check(lib().tp_conv_forward_radial(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y),
+                                        _ptr(r_len), _ptr(W1), _ptr(W2), _ptr(Wmix),
+                                        _ptr(out_pre) if Wmix is not None else None, _ptr(out),
+                                        _stream(x.device)))
+    return out, (out_pre if Wmix is not None else None)

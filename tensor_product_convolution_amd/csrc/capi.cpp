@@ -31,6 +31,8 @@ struct tp_plan_s {
   std::string out_irreps;
   tp_plan_opts opts{};
   const tpc::KernelSet* ks = nullptr;
+  const tpc::RadialSet* rs = nullptr;   // radial-weight kernels (opts.radial_basis > 0)
+  tpc::UvwIrreps uvw{};
 };
 
 namespace tpc {
@@ -46,6 +48,13 @@ tp_status set_error(tp_status code, const std::string& msg) {
 
 tp_status hip_error(hipError_t e, const char* where) {
   return set_error(TP_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul, int nb,
+                             int nh) {
+  if (ls == std::vector<int>{0, 1, 2} && lmax_sh == 2 && lmax_out == 2)
+    return radial_l012_s2(mul, nb, nh);
+  return nullptr;
 }
 
 const KernelSet* find_kernels(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul) {
@@ -142,8 +151,14 @@ tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lma
       return set_error(TP_ERR_IRREPS, "input irreps must have natural parity (-1)^l");
     if (ls[i] > tpc::kMaxL) return set_error(TP_ERR_UNSUPPORTED, "input degree above 6");
   }
-  if (opts && (opts->radial_basis || opts->radial_hidden || opts->uvw))
-    return set_error(TP_ERR_UNSUPPORTED, "radial / uvw plan options are not available in this build");
+  if (opts) {
+    if (opts->radial_basis < 0 || opts->radial_hidden < 0 || opts->uvw < 0)
+      return set_error(TP_ERR_ARG, "negative plan option");
+    if ((opts->radial_basis > 0) != (opts->radial_hidden > 0))
+      return set_error(TP_ERR_ARG, "radial_basis and radial_hidden must both be set");
+    if (opts->radial_basis > 0 && !(opts->r_cut > 0.f))
+      return set_error(TP_ERR_ARG, "r_cut must be positive");
+  }
 
   auto* p = new tp_plan_s();
   p->mul = muls[0];
@@ -190,6 +205,28 @@ tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lma
     if (k) p->out_irreps += "+";
     p->out_irreps += std::to_string(p->mul) + "x" + std::to_string(p->outs[k].first) +
                      (p->outs[k].second == 1 ? "e" : "o");
+  }
+  p->uvw.n = (int)p->outs.size();
+  for (size_t k = 0, ko = 0; k < p->outs.size(); ++k) {
+    p->uvw.dim[k] = 2 * p->outs[k].first + 1;
+    p->uvw.ko[k] = (int)ko;
+    ko += 2 * p->outs[k].first + 1;
+  }
+  if (opts && opts->uvw) {
+    const int m = p->mul;
+    if (m > 128 || (m & (m - 1)) || m < 16 || p->outs.size() > 8) {
+      delete p;
+      return set_error(TP_ERR_UNSUPPORTED, "uvw mix needs a multiplicity of 16, 32, 64 or 128");
+    }
+  }
+  if (opts && opts->radial_basis > 0) {
+    p->rs = tpc::find_radial(ls, lmax_sh, lmax_out, p->mul, opts->radial_basis, opts->radial_hidden);
+    if (!p->rs) {
+      delete p;
+      return set_error(TP_ERR_UNSUPPORTED,
+                       "no compiled radial-weight kernel for this signature (supported: 0e+1o+2e / "
+                       "lmax 2, multiplicity 16 or 128, 8 basis functions, 64 hidden units)");
+    }
   }
   p->ks = tpc::find_kernels(ls, lmax_sh, lmax_out, p->mul);
   if (!p->ks) {
@@ -345,6 +382,93 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward receiver pass");
   e = plan->ks->bwd_send(a);
   if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward sender pass");
+  return TP_OK;
+}
+
+static tp_status need_uvw(tp_plan_t plan) {
+  const int m = plan->mul;
+  if (m > 128 || (m & (m - 1)) || m < 16 || plan->outs.size() > 8)
+    return set_error(TP_ERR_UNSUPPORTED, "uvw mix needs a multiplicity of 16, 32, 64 or 128");
+  return TP_OK;
+}
+
+tp_status tp_conv_uvw_workspace(tp_plan_t plan, size_t* bytes) {
+  if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_uvw_workspace: NULL argument");
+  tp_status s = need_uvw(plan);
+  if (s != TP_OK) return s;
+  *bytes = tpc::uvw_workspace_bytes(plan->uvw.n, plan->mul);
+  return TP_OK;
+}
+
+tp_status tp_conv_uvw_forward(tp_plan_t plan, int32_t n_nodes, const float* Wmix, const float* in,
+                              float* out, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_uvw_forward: plan is NULL");
+  tp_status s = need_uvw(plan);
+  if (s != TP_OK) return s;
+  if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_uvw_forward: negative size");
+  if (n_nodes > 0 && (!Wmix || !in || !out))
+    return set_error(TP_ERR_ARG, "tp_conv_uvw_forward: NULL pointer");
+  if (in == out) return set_error(TP_ERR_ARG, "tp_conv_uvw_forward: in and out must differ");
+  return tpc::uvw_forward(n_nodes, plan->mul, plan->outdim, plan->uvw, Wmix, in, out, false, stream);
+}
+
+tp_status tp_conv_uvw_backward(tp_plan_t plan, int32_t n_nodes, const float* Wmix, const float* in,
+                               const float* grad_out, float* grad_in, float* grad_Wmix, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_uvw_backward: plan is NULL");
+  tp_status s = need_uvw(plan);
+  if (s != TP_OK) return s;
+  if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_uvw_backward: negative size");
+  if (n_nodes > 0 && (!Wmix || !grad_out)) return set_error(TP_ERR_ARG, "tp_conv_uvw_backward: NULL pointer");
+  if (grad_Wmix) {
+    if (n_nodes > 0 && !in) return set_error(TP_ERR_ARG, "tp_conv_uvw_backward: in is NULL");
+    if (!ws || ws_bytes < tpc::uvw_workspace_bytes(plan->uvw.n, plan->mul))
+      return set_error(TP_ERR_WORKSPACE, "tp_conv_uvw_backward: workspace too small");
+  }
+  if (grad_in) {
+    s = tpc::uvw_forward(n_nodes, plan->mul, plan->outdim, plan->uvw, Wmix, grad_out, grad_in, true,
+                         stream);
+    if (s != TP_OK) return s;
+  }
+  if (grad_Wmix) return tpc::uvw_grad_w(n_nodes, plan->mul, plan->outdim, plan->uvw, in, grad_out,
+                                        grad_Wmix, ws, stream);
+  return TP_OK;
+}
+
+tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                 const float* Y, const float* r_len, const float* W1,
+                                 const float* W2, const float* Wmix, float* out_pre, float* out,
+                                 hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward_radial: plan is NULL");
+  if (!plan->rs) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  tp_status s = check_graph(graph, false);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && (!x || !out)) return set_error(TP_ERR_ARG, "tp_conv_forward_radial: x/out NULL");
+  if (E > 0 && (!Y || !r_len || !W1 || !W2))
+    return set_error(TP_ERR_ARG, "tp_conv_forward_radial: Y/r_len/W1/W2 NULL");
+  if (Wmix && N > 0 && (!out_pre || out_pre == out))
+    return set_error(TP_ERR_ARG, "tp_conv_forward_radial: a mix needs a separate out_pre buffer");
+  tpc::RadialArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.x = x;
+  a.Y = Y;
+  a.r_len = r_len;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.r_cut = plan->opts.r_cut;
+  a.out = Wmix ? out_pre : out;
+  a.stream = stream;
+  hipError_t e = plan->rs->fwd(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_forward_radial launch");
+  if (Wmix) {
+    s = need_uvw(plan);
+    if (s != TP_OK) return s;
+    return tpc::uvw_forward(N, plan->mul, plan->outdim, plan->uvw, Wmix, out_pre, out, false, stream);
+  }
   return TP_OK;
 }
 

@@ -32,6 +32,28 @@ struct KernelSet {
   LaunchFn bwd_send = nullptr;  // sender pass: grad_x
 };
 
+// radial-weight variant (edge weights from a radial network of the length)
+struct RadialArgs {
+  int32_t n_nodes = 0, n_edges = 0;
+  const int32_t *row_ptr = nullptr, *col = nullptr;
+  const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
+  const float *x = nullptr, *Y = nullptr, *r_len = nullptr, *W1 = nullptr, *W2 = nullptr;
+  const float* grad_out = nullptr;   // gradient w.r.t. the unmixed output
+  float *out = nullptr, *grad_x = nullptr, *grad_Y = nullptr, *grad_W1 = nullptr, *grad_W2 = nullptr;
+  float r_cut = 0.f;
+  void* ws = nullptr;
+  hipStream_t stream = nullptr;
+};
+using RadialFn = hipError_t (*)(const RadialArgs&);
+struct RadialSet {
+  RadialFn fwd = nullptr;
+  RadialFn bwd = nullptr;                        // grad_x, grad_Y, grad_W1, grad_W2
+  size_t (*bwd_workspace)(int n_nodes, int n_edges) = nullptr;
+};
+const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul, int nb,
+                             int nh);
+const RadialSet* radial_l012_s2(int mul, int nb, int nh);
+
 // Lookup of the compiled specialisation for (input degrees, lmax_sh,
 // lmax_out, multiplicity); nullptr if none.
 const KernelSet* find_kernels(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul);
@@ -41,7 +63,15 @@ const KernelSet* kernels_l01_s2(int mul);
 const KernelSet* kernels_l012_s2(int mul);
 const KernelSet* kernels_l0123_s3(int mul);
 
-// ---- device helpers implemented in graph.hip / sh.hip ------------------------
+// output-irrep description for the channel mix: degree-block sizes (2l+1) and
+// per-channel offsets of each output irrep
+struct UvwIrreps {
+  int n;
+  int dim[8];
+  int ko[8];
+};
+
+// ---- device helpers implemented in graph.hip / sh.hip / uvw.hip --------------
 size_t graph_workspace_bytes(int n_nodes, int n_edges);
 tp_status graph_build(const int32_t* src, const int32_t* dst, int n_edges, int n_nodes,
                       int32_t* row_ptr, int32_t* col, int32_t* perm, int32_t* t_row_ptr,
@@ -49,5 +79,10 @@ tp_status graph_build(const int32_t* src, const int32_t* dst, int n_edges, int n
 tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64_t words, void* out,
                       hipStream_t st);
 tp_status sph_harm(int lmax, const float* r, int n, float* Y, hipStream_t st);
+size_t uvw_workspace_bytes(int n_irreps, int U);
+tp_status uvw_forward(int n_nodes, int U, int outdim, const UvwIrreps& irr, const float* W,
+                      const float* X, float* Z, bool trans_w, hipStream_t st);
+tp_status uvw_grad_w(int n_nodes, int U, int outdim, const UvwIrreps& irr, const float* X,
+                     const float* G, float* gradW, void* ws, hipStream_t st);
 
 }  // namespace tpc
