@@ -217,6 +217,28 @@ tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const fl
                                  const float* W2, const float* Wmix, float* out_pre, float* out,
                                  hipStream_t stream);
 
+/* Backward of tp_conv_forward_radial for the upstream gradient grad_out of its
+ * final output ("Sobek", Abstract: the streaming schedule covers the backward
+ * pass).  With Wmix, out_pre is the forward's unmixed output and grad_Wmix
+ * [K][U][U] is produced; the gradient reaching the aggregation is
+ * Wmix-applied grad_out.  Outputs (each may be NULL to skip it):
+ *   grad_x [N][xdim], grad_Y [E][ysh] (receiver-sorted), grad_W1 and grad_W2
+ *   (shapes of W1, W2), grad_Wmix.
+ * The per-edge weights, their gradients and the hidden activations are
+ * recomputed on chip, never stored.  x, grad_out and W2 must be 16-byte
+ * aligned (vector loads of four channels).  Parameter gradients are reduced in a fixed
+ * order through ws (tp_conv_radial_workspace bytes for the same sizes), so the
+ * results are bitwise reproducible. */
+tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                  const float* Y, const float* r_len, const float* W1,
+                                  const float* W2, const float* Wmix, const float* out_pre,
+                                  const float* grad_out, float* grad_x, float* grad_Y,
+                                  float* grad_W1, float* grad_W2, float* grad_Wmix, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+/* Workspace bytes of tp_conv_backward_radial for n_nodes nodes (with_mix != 0:
+ * a channel mix is differentiated too). */
+tp_status tp_conv_radial_workspace(tp_plan_t plan, int32_t n_nodes, int32_t with_mix, size_t* bytes);
+
 /* Thread-local description of the last failure on this thread. */
 const char* tp_conv_last_error(void);
 

@@ -27,7 +27,8 @@ EXPORTS = (
     "tp_conv_plan_destroy", "tp_cg_real", "tp_conv_graph_workspace", "tp_conv_graph_build",
     "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
-    "tp_conv_forward_radial", "tp_conv_last_error",
+    "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
+    "tp_conv_last_error",
 )
 
 
@@ -83,6 +84,9 @@ def lib():
         "tp_conv_uvw_workspace": (I32, [P, ctypes.POINTER(SZ)]),
         "tp_conv_forward_radial": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
                                          VP]),
+        "tp_conv_backward_radial": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP,
+                                          VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
+        "tp_conv_radial_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -345,3 +349,39 @@ def forward_radial(plan, graph, x, Y, r_len, W1, W2, Wmix=None, out=None, out_pr
                                         _ptr(out_pre) if Wmix is not None else None, _ptr(out),
                                         _stream(x.device)))
     return out, (out_pre if Wmix is not None else None)
+
+
+def backward_radial(plan, graph, x, Y, r_len, W1, W2, grad_out, Wmix=None, out_pre=None,
+                    want=("x", "Y", "W1", "W2", "Wmix")):
+    """(grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix) of the radial-weight convolution
+    (grad_Y receiver-sorted); entries not in ``want`` (and grad_Wmix without a mix)
+    are None."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    nb, nh, _ = plan.radial
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(r_len, "r_len", torch.float32, (E,))
+    _need(W1, "W1", torch.float32, (nb, nh))
+    _need(W2, "W2", torch.float32, (nh, plan.n_paths * plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    if Wmix is not None:
+        K = len(plan.out_irreps.split("+"))
+        _need(Wmix, "Wmix", torch.float32, (K, plan.mul, plan.mul))
+        if "Wmix" in want:
+            _need(out_pre, "out_pre", torch.float32, (N, plan.outdim))
+    gx = torch.empty_like(x) if "x" in want else None
+    gY = torch.empty_like(Y) if "Y" in want else None
+    gW1 = torch.empty_like(W1) if "W1" in want else None
+    gW2 = torch.empty_like(W2) if "W2" in want else None
+    gWm = torch.empty_like(Wmix) if (Wmix is not None and "Wmix" in want) else None
+    b = ctypes.c_size_t()
+    _check(lib().tp_conv_radial_workspace(plan.handle, N, int(Wmix is not None), ctypes.byref(b)))
+    ws = torch.empty(max(b.value, 1), dtype=torch.uint8, device=x.device)
+    g = graph.cstruct()
+    _check(lib().tp_conv_backward_radial(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(r_len),
+                                         _ptr(W1), _ptr(W2), _ptr(Wmix),
+                                         _ptr(out_pre) if gWm is not None else None, _ptr(grad_out),
+                                         _ptr(gx), _ptr(gY), _ptr(gW1), _ptr(gW2), _ptr(gWm),
+                                         _ptr(ws), b.value, _stream(x.device)))
+    return gx, gY, gW1, gW2, gWm

@@ -472,4 +472,88 @@ tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const fl
   return TP_OK;
 }
 
+static size_t align_up(size_t b) { return (b + 255) & ~size_t(255); }
+
+tp_status tp_conv_radial_workspace(tp_plan_t plan, int32_t n_nodes, int32_t with_mix, size_t* bytes) {
+  if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_radial_workspace: NULL argument");
+  if (!plan->rs || !plan->rs->bwd_workspace)
+    return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_radial_workspace: negative size");
+  size_t b = plan->rs->bwd_workspace(n_nodes, 0);
+  if (with_mix) {
+    tp_status s = need_uvw(plan);
+    if (s != TP_OK) return s;
+    const size_t u = tpc::uvw_workspace_bytes(plan->uvw.n, plan->mul);
+    b = align_up((size_t)n_nodes * plan->outdim * sizeof(float)) + (u > b ? u : b);
+  }
+  *bytes = b;
+  return TP_OK;
+}
+
+tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                  const float* Y, const float* r_len, const float* W1,
+                                  const float* W2, const float* Wmix, const float* out_pre,
+                                  const float* grad_out, float* grad_x, float* grad_Y,
+                                  float* grad_W1, float* grad_W2, float* grad_Wmix, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: plan is NULL");
+  if (!plan->rs || !plan->rs->bwd) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  tp_status s = check_graph(graph, grad_x != nullptr);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && !grad_out) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: grad_out NULL");
+  if (!W1 || !W2) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: W1/W2 NULL");
+  if (E > 0 && (!x || !Y || !r_len)) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: x/Y/r_len NULL");
+  if (grad_Wmix && !Wmix) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: grad_Wmix without Wmix");
+  if (Wmix && grad_Wmix && N > 0 && !out_pre)
+    return set_error(TP_ERR_ARG, "tp_conv_backward_radial: grad_Wmix needs out_pre");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(grad_out) |
+       reinterpret_cast<uintptr_t>(W2)) & 15)
+    return set_error(TP_ERR_ARG, "tp_conv_backward_radial: x, grad_out and W2 must be 16-byte aligned");
+  size_t need = 0;
+  s = tp_conv_radial_workspace(plan, N, Wmix != nullptr, &need);
+  if (s != TP_OK) return s;
+  if (ws_bytes < need || (need > 0 && !ws))
+    return set_error(TP_ERR_WORKSPACE, "tp_conv_backward_radial: workspace too small");
+  char* w = static_cast<char*>(ws);
+  const float* g = grad_out;
+  if (Wmix) {
+    float* gmix = reinterpret_cast<float*>(w);
+    w += align_up((size_t)N * plan->outdim * sizeof(float));
+    if (N > 0) {
+      s = tpc::uvw_forward(N, plan->mul, plan->outdim, plan->uvw, Wmix, grad_out, gmix, true, stream);
+      if (s != TP_OK) return s;
+    }
+    if (grad_Wmix) {
+      s = tpc::uvw_grad_w(N, plan->mul, plan->outdim, plan->uvw, out_pre, grad_out, grad_Wmix, w, stream);
+      if (s != TP_OK) return s;
+    }
+    g = gmix;
+  }
+  tpc::RadialArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_perm = graph->t_perm;
+  a.t_col = graph->t_col;
+  a.x = x;
+  a.Y = Y;
+  a.r_len = r_len;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.grad_out = g;
+  a.grad_x = grad_x;
+  a.grad_Y = grad_Y;
+  a.grad_W1 = grad_W1;
+  a.grad_W2 = grad_W2;
+  a.r_cut = plan->opts.r_cut;
+  a.ws = w;
+  a.stream = stream;
+  hipError_t e = plan->rs->bwd(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward_radial launch");
+  return TP_OK;
+}
+
 }  // extern "C"

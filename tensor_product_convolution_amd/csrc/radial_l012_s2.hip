@@ -4,24 +4,89 @@
 namespace tpc {
 
 using SigR = Sig<2, 2, 0, 1, 2>;
+constexpr int kNB = 8, kNH = 64;
+constexpr int kPGS = 4;                                   // paths per wave, grad_W2 pass
+constexpr int kNPG = (SigR::NP + kPGS - 1) / kPGS;
+
+namespace {
+
+// out[e] = sum_b part[b][e], fixed order over b
+__global__ void __launch_bounds__(256)
+    k_radial_sum(const float* __restrict__ part, int nparts, long long n, float* __restrict__ out) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.f;
+  for (int b = 0; b < nparts; ++b) s += part[(size_t)b * n + e];
+  out[e] = s;
+}
+
+// persistent grid sizes (fixed functions of the node count, so the partial
+// sums and hence the results do not depend on the device)
+int recv_blocks(int n_nodes) { return n_nodes < 2048 ? (n_nodes > 0 ? n_nodes : 1) : 2048; }
+template <int U>
+int w2_blocks(int n_nodes) {
+  const int cap = 2048 / (U / 16);
+  return n_nodes < cap ? (n_nodes > 0 ? n_nodes : 1) : cap;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+}  // namespace
 
 template <int U>
 static hipError_t launch_radial_fwd(const RadialArgs& a) {
   if (a.n_nodes == 0) return hipSuccess;
   RadialParams rp{a.r_cut, a.W1, a.W2};
-  hipLaunchKernelGGL((k_radial_fwd<SigR, U, 8, 64>), dim3(a.n_nodes), dim3(64), 0, a.stream,
+  hipLaunchKernelGGL((k_radial_fwd<SigR, U, kNB, kNH>), dim3(a.n_nodes), dim3(64), 0, a.stream,
                      a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.out);
   return hipGetLastError();
 }
 
 template <int U>
+static size_t radial_bwd_ws(int n_nodes, int /*n_edges*/) {
+  return align256((size_t)recv_blocks(n_nodes) * kNB * kNH * sizeof(float)) +
+         (size_t)w2_blocks<U>(n_nodes) * kNH * SigR::NP * U * sizeof(float);
+}
+
+// grad_Y and grad_W1 (receiver pass), grad_W2, grad_x (sender pass); a.ws holds
+// radial_bwd_ws bytes.  grad_W1/grad_W2/grad_x may be null (skipped).
+template <int U>
+static hipError_t launch_radial_bwd(const RadialArgs& a) {
+  RadialParams rp{a.r_cut, a.W1, a.W2};
+  const int nb1 = recv_blocks(a.n_nodes), nb2 = w2_blocks<U>(a.n_nodes);
+  float* part1 = static_cast<float*>(a.ws);
+  float* part2 = reinterpret_cast<float*>(static_cast<char*>(a.ws) +
+                                          align256((size_t)nb1 * kNB * kNH * sizeof(float)));
+  if (a.grad_Y || a.grad_W1) {
+    hipLaunchKernelGGL((k_radial_bwd_recv<SigR, U, kNB, kNH>), dim3(nb1), dim3(64), 0, a.stream,
+                       a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.grad_out, a.grad_Y, part1);
+    if (a.grad_W1) {
+      const long long n = (long long)kNB * kNH;
+      hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream, part1,
+                         nb1, n, a.grad_W1);
+    }
+  }
+  if (a.grad_W2) {
+    hipLaunchKernelGGL((k_radial_bwd_w2<SigR, U, kNB, kNH, kPGS>), dim3(nb2, U / 16), dim3(64 * kNPG), 0,
+                       a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.grad_out, part2);
+    const long long n = (long long)kNH * SigR::NP * U;
+    hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream, part2, nb2,
+                       n, a.grad_W2);
+  }
+  if (a.grad_x && a.n_nodes > 0)
+    hipLaunchKernelGGL((k_radial_bwd_send<SigR, U, kNB, kNH>), dim3(a.n_nodes), dim3(64), 0, a.stream,
+                       a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.r_len, rp, a.grad_out, a.grad_x);
+  return hipGetLastError();
+}
+
+template <int U>
 static const RadialSet* radial_set() {
-  static const RadialSet s{&launch_radial_fwd<U>, nullptr};
+  static const RadialSet s{&launch_radial_fwd<U>, &launch_radial_bwd<U>, &radial_bwd_ws<U>};
   return &s;
 }
 
 const RadialSet* radial_l012_s2(int mul, int nb, int nh) {
-  if (nb != 8 || nh != 64) return nullptr;
+  if (nb != kNB || nh != kNH) return nullptr;
   switch (mul) {
     case 16: return radial_set<16>();
     case 128: return radial_set<128>();

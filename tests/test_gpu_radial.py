@@ -91,3 +91,105 @@ def test_radial_forward_parity(tpc, U, name, n):
     # without a mix the aggregated output goes straight to out
     _, _, _, out2, _ = _gpu_radial_fwd(tpc, plan, wl, mix=False)
     assert block_err(out2, ref_pre, out_blocks(op)) <= TOL
+
+
+def _gpu_radial(tpc, plan, wl, mix, g2):
+    """forward + backward on the GPU; everything returned as numpy."""
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+    rl = tpc.gather_rows(T(wl.r_len), g.perm)
+    Wm = T(wl.Wmix) if mix else None
+    out, pre = tpc.forward_radial(plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), Wm)
+    grads = tpc.backward_radial(plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), T(g2), Wmix=Wm,
+                                out_pre=pre)
+    torch.cuda.synchronize()
+    cpu = lambda t: None if t is None else t.cpu().numpy()
+    return dict(perm=cpu(g.perm)[:wl.n_edges], out=cpu(out), pre=cpu(pre),
+                gx=cpu(grads[0]), gY=cpu(grads[1]), gW1=cpu(grads[2]), gW2=cpu(grads[3]),
+                gWm=cpu(grads[4]))
+
+
+def _param_err(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def _check_params(op, res, ref, U):
+    _, _, gW1, gW2, gWm = ref
+    assert _param_err(res["gW1"], gW1) <= TOL
+    # grad_W2 per path block
+    P = op.n_paths
+    a, b = res["gW2"].reshape(-1, P, U), gW2.reshape(-1, P, U)
+    for p in range(P):
+        assert _param_err(a[:, p], b[:, p]) <= TOL, f"grad_W2 path {p}"
+    if gWm is not None:
+        for k in range(gWm.shape[0]):
+            assert _param_err(res["gWm"][k], gWm[k]) <= TOL, f"grad_Wmix irrep {k}"
+
+
+@pytest.mark.parametrize("U,name,n,mix", [(16, "stream", 300, True), (128, "stream", 120, True),
+                                          (16, "zipf", 400, False), (128, "uniform", 100, True)])
+def test_radial_backward_parity(tpc, U, name, n, mix):
+    say(f"radial bwd U={U} graph={name} n={n} mix={mix}")
+    gname = "lmax3" if name == "uniform" else name
+    op, wl = _radial_inputs(U, gname, n)
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    res = _gpu_radial(tpc, plan, wl, mix, wl.g)
+    Yo = oracle.sh_real(2, wl.r)
+    Wm = wl.Wmix if mix else None
+    ref = oracle.tp_conv_radial_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Yo, wl.r_len, wl.W1, wl.W2,
+                                    Wm, wl.g, 8, RC)
+    assert block_err(res["gx"], ref[0], in_blocks(op)) <= TOL
+    assert block_err(res["gY"], ref[1][res["perm"]], y_blocks(op)) <= TOL
+    _check_params(op, res, ref, U)
+    if not mix:
+        assert res["gWm"] is None
+
+
+def _subgraph(wl, e, recv):
+    """edges e over the compacted node set (their senders and the receivers recv):
+    (nodes, src', dst', position of each receiver of recv in nodes)."""
+    nodes = np.unique(np.concatenate([wl.src[e], recv]))
+    src = np.searchsorted(nodes, wl.src[e]).astype(np.int64)
+    dst = np.searchsorted(nodes, wl.dst[e]).astype(np.int64)
+    return nodes, src, dst, np.searchsorted(nodes, recv)
+
+
+def test_radial_full_size_sampled(tpc):
+    """The 100,000-atom / 3,000,000-edge streaming layer with its mix, forward and
+    backward at full size in the launch configuration the benchmark times.  Forward:
+    sampled receivers.  Backward: the upstream gradient is zero outside the sampled
+    receivers, so every gradient (including the parameter sums over all edges) is
+    exactly that of the sampled receivers' edges, which the oracle computes."""
+    say("radial full-size sampled: stream 100000 nodes")
+    U = 128
+    op = oracle.build_plan(_irreps(U), 2, 2)
+    wl = make_workload("stream", dims_of(op))
+    N = wl.n_nodes
+    rng = np.random.default_rng(11)
+    recv = np.sort(rng.choice(N, size=24, replace=False))
+    g2 = np.zeros_like(wl.g)
+    g2[recv] = wl.g[recv]
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    res = _gpu_radial(tpc, plan, wl, True, g2)
+    e = np.nonzero(np.isin(wl.dst, recv))[0]
+    nodes, src, dst, rpos = _subgraph(wl, e, recv)
+    n = len(nodes)
+    Yo = oracle.sh_real(2, wl.r[e])
+    rl = wl.r_len[e]
+    ref_out, ref_pre = oracle.tp_conv_radial_fwd(op, src, dst, n, wl.x[nodes], Yo, rl, wl.W1, wl.W2,
+                                                 wl.Wmix, 8, RC, return_pre_mix=True)
+    assert block_err(res["pre"][recv], ref_pre[rpos], out_blocks(op)) <= TOL
+    assert block_err(res["out"][recv], ref_out[rpos], out_blocks(op)) <= TOL
+    # backward on the subgraph: the upstream gradient is zero off the sampled receivers
+    ref = oracle.tp_conv_radial_bwd(op, src, dst, n, wl.x[nodes], Yo, rl, wl.W1, wl.W2, wl.Wmix,
+                                    g2[nodes], 8, RC)
+    assert block_err(res["gx"][nodes], ref[0], in_blocks(op)) <= TOL
+    others = np.setdiff1d(rng.choice(N, size=200, replace=False), nodes)
+    assert np.all(res["gx"][others] == 0)
+    inv = np.empty(wl.n_edges, np.int64)
+    inv[res["perm"]] = np.arange(wl.n_edges)
+    assert block_err(res["gY"][inv[e]], ref[1], y_blocks(op)) <= TOL
+    mask = np.ones(wl.n_edges, bool)
+    mask[inv[e]] = False
+    assert np.all(res["gY"][mask][:100000] == 0)
+    _check_params(op, res, ref, U)
