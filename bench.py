@@ -14,6 +14,14 @@ Cache hold none of the step's inputs: they come from HBM.  Per-kernel launch
 durations (for the roofline) are event-timed over 10 back-to-back launches of
 that kernel after a flush.  ``--warm`` also times steps without the flush.
 
+``--config stream`` times the 100,000-atom / 3,000,000-edge streaming layer
+instead: edge weights from the radial network (8 Bessel functions, 64 SiLU
+units, 15 x 128 weights per edge) recomputed on chip in every pass, then the
+128 x 128 channel mix per output irrep; a step is its forward (radial pass +
+mix) and backward (mix adjoint, receiver pass, grad_W2 pass, sender pass).
+Its kernels are bound by the fp32 MFMA work of the radial network, so its
+roofline is reported against the 157.3 TFLOP/s fp32 matrix peak.
+
 Output: one JSON line (rank 0, N = 1).  ``value`` is edges per second of
 forward + backward; ``roofline`` reports the slowest of the three kernels
 against the 8 TB/s HBM peak with its algorithmic bytes; ``cpu_baseline`` is
@@ -42,14 +50,23 @@ WORKLOADS = {
     "zipf": ("64x0e+64x1o+64x2e+64x3o", 3, 3,
              "32768 atoms, Zipf(1.5) degrees capped at 256, lmax 3, 64 channels"),
 }
+RADIAL_WORKLOADS = {
+    "stream": ("128x0e+128x1o+128x2e", 2, 2, (8, 64, 5.0),
+               "100000 atoms, 3000000 directed edges (30 distinct random senders each, length "
+               "U[0.8,5] A), 128x0e+128x1o+128x2e, real SH lmax 2, all paths l3<=2 (15), edge "
+               "weights from a radial MLP (8 Bessel -> 64 SiLU -> 15x128) computed on chip, "
+               "128x128 uvw mix per output irrep, fwd+bwd"),
+}
+FP32_MFMA_PEAK_TFLOPS = 157.3
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_{}.txt")
 KERNEL_SOURCES = ("conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
+RADIAL_SOURCES = ("radial_kernels.hpp", "conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tensor_product_convolution_amd", "csrc")
-    for f in KERNEL_SOURCES:
+    for f in sources:
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -66,7 +83,13 @@ def algorithmic_bytes(N, E, P, U, ysh, xdim, outdim):
     }
 
 
-def read_traffic(config):
+def radial_flops(E, P, U, NH):
+    """MFMA flops per launch: each pass forms [E x NH] x [NH x P*U] products."""
+    mlp = 2.0 * NH * P * U * E
+    return {"fwd": mlp, "bwd_recv": 2 * mlp, "bwd_w2": mlp, "bwd_send": mlp}
+
+
+def read_traffic(config, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None."""
     path = PROFILE_SUMMARY.format(config)
     if not os.path.exists(path):
@@ -78,7 +101,7 @@ def read_traffic(config):
             continue
         k, v = line.split("=", 1)
         vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_hash") != kernel_source_hash():
+    if vals.get("kernel_source_hash") != kernel_source_hash(sources):
         return None          # kernels changed since the counters were taken
     out = {}
     for k, v in vals.items():
@@ -105,12 +128,65 @@ def cpu_baseline(op, wl):
                       f"{dt:.2f} s; host affinity {len(os.sched_getaffinity(0))} cores"}
 
 
+def make_timers(torch, flush):
+    """(do_flush, timed_steps, timed_kernel) on torch's current stream."""
+    def do_flush():
+        # read 1 GiB: L2 and the Infinity Cache end up holding clean lines of
+        # an unrelated buffer (a write would leave dirty lines whose write-back
+        # competes with the next kernel's reads)
+        flush.sum()
+
+    def timed_steps(step, k, cold):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(k)]
+        for e0, e1 in ev:
+            if cold:
+                do_flush()
+            e0.record()
+            step()
+            e1.record()
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) for e0, e1 in ev])   # ms
+
+    def timed_kernel(fn, reps, rounds):
+        # launch duration amortised over back-to-back launches (an event pair
+        # around a single short launch mostly measures the event overhead)
+        res = []
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            do_flush()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / reps)
+        return np.array(res)
+
+    return do_flush, timed_steps, timed_kernel
+
+
+def counters_run(torch, dev, flush, step, config):
+    """a few steps plus a plain 512 MiB copy (the calibration of the counters)"""
+    flush.fill_(1.0)
+    for _ in range(3):
+        flush.sum()
+        step()
+    a = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(2.0)
+    flush.sum()
+    b.copy_(a)                      # plain copy: 512 MiB read + 512 MiB written
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_run": config, "copy_bytes": a.numel() * 4}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mid", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="mid", choices=sorted(WORKLOADS) + sorted(RADIAL_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time the steps back to back without the cache flush")
@@ -131,6 +207,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.config in RADIAL_WORKLOADS:
+        return bench_radial(args, torch, tpc, make_workload, dev)
     irreps, lsh, lout, desc = WORKLOADS[args.config]
     plan = tpc.Plan(irreps, lsh, lout)
     wl = make_workload(args.config, plan.dims(), seed=0)
@@ -155,57 +233,16 @@ def main():
         tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None))
 
     if args.counters:
-        flush.fill_(1.0)
-        for _ in range(3):
-            flush.sum()
-            step()
-        a = torch.empty(1 << 27, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        a.fill_(2.0)
-        flush.sum()
-        b.copy_(a)                      # plain copy: 512 MiB read + 512 MiB written
-        torch.cuda.synchronize()
-        print(json.dumps({"counters_run": args.config, "copy_bytes": a.numel() * 4}))
+        counters_run(torch, dev, flush, step, args.config)
         return
-
-    def do_flush():
-        # read 1 GiB: L2 and the Infinity Cache end up holding clean lines of
-        # an unrelated buffer (a write would leave dirty lines whose write-back
-        # competes with the next kernel's reads)
-        flush.sum()
-
-    def timed_steps(k, cold):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(k)]
-        for e0, e1 in ev:
-            if cold:
-                do_flush()
-            e0.record()
-            step()
-            e1.record()
-        torch.cuda.synchronize()
-        return np.array([e0.elapsed_time(e1) for e0, e1 in ev])   # ms
+    do_flush, timed_steps_of, timed_kernel = make_timers(torch, flush)
+    timed_steps = lambda k, cold: timed_steps_of(step, k, cold)
 
     kernels = {
         "fwd": lambda: tpc.forward(plan, g, x, Y, w, out=out),
         "bwd_recv": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw)),
         "bwd_send": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None)),
     }
-
-    def timed_kernel(fn, reps, rounds):
-        # launch duration amortised over back-to-back launches (an event pair
-        # around a single short launch mostly measures the event overhead)
-        res = []
-        for _ in range(rounds):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            do_flush()
-            e0.record()
-            for _ in range(reps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            res.append(e0.elapsed_time(e1) / reps)
-        return np.array(res)
 
     flush.fill_(1.0)
     # graph grouping, timed separately
@@ -273,6 +310,125 @@ def main():
         import oracle
         op = oracle.build_plan(irreps, lsh, lout)
         res["cpu_baseline"] = cpu_baseline(op, wl)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+def cpu_baseline_radial(op, wl, radial, n_recv=200):
+    """The float64 oracle on this host, fwd + bwd (with the mix) over the edges
+    into the first n_recv receivers (a bounded sample of the layer)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    nb, _, rc = radial
+    recv = np.arange(n_recv)
+    e = np.nonzero(np.isin(wl.dst, recv))[0]
+    nodes = np.unique(np.concatenate([wl.src[e], recv]))
+    src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
+    x, g, rl = wl.x[nodes], wl.g[nodes], wl.r_len[e]
+    t0 = time.perf_counter()
+    Y = oracle.sh_real(op.lmax_sh, wl.r[e])
+    oracle.tp_conv_radial_fwd(op, src, dst, len(nodes), x, Y, rl, wl.W1, wl.W2, wl.Wmix, nb, rc)
+    oracle.tp_conv_radial_bwd(op, src, dst, len(nodes), x, Y, rl, wl.W1, wl.W2, wl.Wmix, g, nb, rc)
+    dt = time.perf_counter() - t0
+    return {"value": len(e) / dt, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"edges into receivers 0..{n_recv - 1} ({len(e)} of {wl.n_edges} edges, "
+                      f"{len(nodes)} nodes): harmonics + radial fwd + bwd with the mix once, "
+                      f"float64, {dt:.2f} s; host affinity {len(os.sched_getaffinity(0))} cores"}
+
+
+def bench_radial(args, torch, tpc, make_workload, dev):
+    irreps, lsh, lout, radial, desc = RADIAL_WORKLOADS[args.config]
+    plan = tpc.Plan(irreps, lsh, lout, radial=radial, uvw=True)
+    wl = make_workload(args.config, plan.dims(), seed=0)
+    N, E = wl.n_nodes, wl.n_edges
+    P, U = plan.n_paths, plan.mul
+    NH = radial[1]
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    src, dst = T(wl.src), T(wl.dst)
+    g = tpc.graph_build(src, dst, N)
+    Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
+    rl = tpc.gather_rows(T(wl.r_len), g.perm)
+    x, W1, W2, Wm, go = T(wl.x), T(wl.W1), T(wl.W2), T(wl.Wmix), T(wl.g)
+    out = torch.empty(N, plan.outdim, device=dev)
+    pre = torch.empty_like(out)
+    outs = {"x": torch.empty_like(x), "Y": torch.empty_like(Y), "W1": torch.empty_like(W1),
+            "W2": torch.empty_like(W2), "Wmix": torch.empty_like(Wm)}
+    ws = torch.empty(tpc.radial_workspace(plan, N, True), dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+
+    def step():
+        tpc.forward_radial(plan, g, x, Y, rl, W1, W2, Wm, out=out, out_pre=pre)
+        tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, Wmix=Wm, out_pre=pre, outs=outs, ws=ws)
+
+    if args.counters:
+        counters_run(torch, dev, flush, step, args.config)
+        return
+    do_flush, timed_steps, timed_kernel = make_timers(torch, flush)
+    bwd = lambda want: (lambda: tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, want=want,
+                                                    outs=outs, ws=ws))
+    kernels = {
+        "fwd": lambda: tpc.forward_radial(plan, g, x, Y, rl, W1, W2, None, out=pre),
+        "bwd_recv": bwd(("Y", "W1")),
+        "bwd_w2": bwd(("W2",)),
+        "bwd_send": bwd(("x",)),
+        "fwd_with_mix": lambda: tpc.forward_radial(plan, g, x, Y, rl, W1, W2, Wm, out=out,
+                                                   out_pre=pre),
+    }
+    flush.fill_(1.0)
+    timed_steps(step, args.warmup, True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    t = timed_steps(step, args.steps, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    reps, rounds = 3, 2
+    kt = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in kernels.items()}
+    fl = radial_flops(E, P, U, NH)
+    names = ["fwd", "bwd_recv", "bwd_w2", "bwd_send"]
+    dom = max(names, key=lambda n: kt[n])
+    achieved = fl[dom] / (kt[dom] * 1e-3) / 1e12
+    step_ms = float(t.mean())
+    traffic = read_traffic(args.config, RADIAL_SOURCES)
+    res = {
+        "metric": METRIC,
+        "value": E / (step_ms * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; random-init radial MLP and mix weights)",
+        "config": {"workload": f"{args.config}: {desc}", "n_nodes": N, "n_edges": E,
+                   "irreps": irreps, "lmax_sh": lsh, "lmax_out": lout, "paths": P,
+                   "radial": {"basis": radial[0], "hidden": radial[1], "r_cut": radial[2]},
+                   "mode": "fwd+bwd", "cache": "L2+MALL flushed before each step"},
+        "fwd_edges_per_s": E / (kt["fwd_with_mix"] * 1e-3),
+        "fwd_edges_per_s_note": "forward alone (radial pass + mix, launch durations)",
+        "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
+        "kernel_ms": kt,
+        "kernel_ms_note": f"per call, {reps} back-to-back calls after a cache flush, mean of "
+                          f"{rounds}; bwd_recv and bwd_w2 include their partial-sum kernels",
+        "kernel_mfma_frac": {n: fl[n] / (kt[n] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS
+                             for n in names},
+        "wall_s_timed_region": wall,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": fl[dom],
+                     "traffic": (traffic or {}).get(dom)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        op = oracle.build_plan(irreps, lsh, lout)
+        res["cpu_baseline"] = cpu_baseline_radial(op, wl, radial)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res))

@@ -352,10 +352,11 @@ def forward_radial(plan, graph, x, Y, r_len, W1, W2, Wmix=None, out=None, out_pr
 
 
 def backward_radial(plan, graph, x, Y, r_len, W1, W2, grad_out, Wmix=None, out_pre=None,
-                    want=("x", "Y", "W1", "W2", "Wmix")):
+                    want=("x", "Y", "W1", "W2", "Wmix"), outs=None, ws=None):
     """(grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix) of the radial-weight convolution
     (grad_Y receiver-sorted); entries not in ``want`` (and grad_Wmix without a mix)
-    are None."""
+    are None.  ``outs`` (a dict name -> tensor) and ``ws`` (uint8, at least
+    radial_workspace bytes) supply preallocated buffers."""
     torch = _torch()
     N, E = graph.n_nodes, graph.n_edges
     nb, nh, _ = plan.radial
@@ -370,18 +371,34 @@ def backward_radial(plan, graph, x, Y, r_len, W1, W2, grad_out, Wmix=None, out_p
         _need(Wmix, "Wmix", torch.float32, (K, plan.mul, plan.mul))
         if "Wmix" in want:
             _need(out_pre, "out_pre", torch.float32, (N, plan.outdim))
-    gx = torch.empty_like(x) if "x" in want else None
-    gY = torch.empty_like(Y) if "Y" in want else None
-    gW1 = torch.empty_like(W1) if "W1" in want else None
-    gW2 = torch.empty_like(W2) if "W2" in want else None
-    gWm = torch.empty_like(Wmix) if (Wmix is not None and "Wmix" in want) else None
-    b = ctypes.c_size_t()
-    _check(lib().tp_conv_radial_workspace(plan.handle, N, int(Wmix is not None), ctypes.byref(b)))
-    ws = torch.empty(max(b.value, 1), dtype=torch.uint8, device=x.device)
+    outs = outs or {}
+
+    def buf(name, like):
+        if name not in want or like is None:
+            return None
+        t = outs.get(name)
+        if t is None:
+            return torch.empty_like(like)
+        _need(t, "grad_" + name, torch.float32, tuple(like.shape))
+        return t
+    gx, gY, gW1, gW2 = buf("x", x), buf("Y", Y), buf("W1", W1), buf("W2", W2)
+    gWm = buf("Wmix", Wmix)
+    nbytes = radial_workspace(plan, N, Wmix is not None)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    elif ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
     g = graph.cstruct()
     _check(lib().tp_conv_backward_radial(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(r_len),
                                          _ptr(W1), _ptr(W2), _ptr(Wmix),
                                          _ptr(out_pre) if gWm is not None else None, _ptr(grad_out),
                                          _ptr(gx), _ptr(gY), _ptr(gW1), _ptr(gW2), _ptr(gWm),
-                                         _ptr(ws), b.value, _stream(x.device)))
+                                         _ptr(ws), ws.numel(), _stream(x.device)))
     return gx, gY, gW1, gW2, gWm
+
+
+def radial_workspace(plan, n_nodes, with_mix):
+    """bytes of workspace backward_radial needs"""
+    b = ctypes.c_size_t()
+    _check(lib().tp_conv_radial_workspace(plan.handle, n_nodes, int(bool(with_mix)), ctypes.byref(b)))
+    return b.value

@@ -179,6 +179,12 @@ struct CgPath {
     return t;
   }
   static constexpr Table table = make();
+  // does some nonzero couple Y component b to output component c?
+  static constexpr bool has_bc(int b, int c) {
+    for (int n = 0; n < nnz; ++n)
+      if (table.e[n].b == b && table.e[n].c == c) return true;
+    return false;
+  }
 };
 
 }  // namespace tpc

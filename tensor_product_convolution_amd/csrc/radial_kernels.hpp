@@ -33,61 +33,7 @@ struct RadialParams {
   const float* W2;   // [NH][P*U]
 };
 
-// Bessel basis of one length (n = 1..NB)
-template <int NB>
-__device__ __forceinline__ void bessel(float r, float r_cut, float (&b)[NB]) {
-  const float pre = sqrtf(2.0f / r_cut) / r;
-  const float k = 3.14159265358979323846f / r_cut;
-#pragma unroll
-  for (int n = 0; n < NB; ++n) b[n] = pre * sinf((float)(n + 1) * k * r);
-}
-
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// pre-activation of hidden unit hid for basis values b
-template <int NB, int NH>
-__device__ __forceinline__ float hidden_pre(const float (&b)[NB], const float* __restrict__ W1, int hid) {
-  float s = 0.f;
-#pragma unroll
-  for (int n = 0; n < NB; ++n) s = fmaf(b[n], W1[n * NH + hid], s);
-  return s;
-}
-
-// Per-lane A operands of the M-tile whose edge l%16 has length r (valid):
-// a[k] = h[edge][4k + l/16], k = 0..NH/4-1; zero for an invalid edge.
-template <int NB, int NH>
-__device__ __forceinline__ void hidden_A(float r, bool valid, const RadialParams& rp, int lane,
-                                         float (&a)[NH / 4]) {
-  float b[NB];
-  bessel<NB>(valid ? r : 1.0f, rp.r_cut, b);
-#pragma unroll
-  for (int k = 0; k < NH / 4; ++k) {
-    const float h = silu(hidden_pre<NB, NH>(b, rp.W1, 4 * k + (lane >> 4)));
-    a[k] = valid ? h : 0.f;
-  }
-}
-
-// w of MT M-tiles for the 16 channels of chunk c: C[mt][p] (4 edges each)
-template <class S, int U, int NH, int MT>
-__device__ __forceinline__ void radial_weights(const float (&a)[MT][NH / 4], const float* __restrict__ W2,
-                                               int chunk, int lane, f32x4 (&C)[MT][S::NP]) {
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int p = 0; p < S::NP; ++p) C[mt][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* w2 = W2 + 16 * chunk + (lane & 15);
-#pragma unroll 2
-  for (int k = 0; k < NH / 4; ++k) {
-    const float* row = w2 + (size_t)(4 * k + (lane >> 4)) * (S::NP * U);
-    float b[S::NP];
-#pragma unroll
-    for (int p = 0; p < S::NP; ++p) b[p] = row[p * U];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int p = 0; p < S::NP; ++p) C[mt][p] = mfma_16x16x4(a[mt][k], b[p], C[mt][p]);
-  }
-}
 
 // x components of channel u of node row j
 template <class S, int U>
@@ -121,69 +67,6 @@ __device__ __forceinline__ void reduce_quads(float (&v)[N]) {
   }
 }
 
-constexpr int kRadialMT = 2;   // M-tiles (of 16 edges) per group
-
-// ---------------------------------------------------------------------------
-// forward: one wave per receiver; for each chunk of 16 channels, the weights
-// of up to 32 edges at a time come from MFMA and feed the tensor product.
-template <class S, int U, int NB, int NH>
-__global__ void __launch_bounds__(64)
-    k_radial_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-                 const float* __restrict__ x, const float* __restrict__ Y,
-                 const float* __restrict__ r_len, RadialParams rp, float* __restrict__ out) {
-  static_assert(U % 16 == 0 && NH % 4 == 0, "radial tiling");
-  constexpr int MT = kRadialMT, G = 16 * MT;
-  const int i = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int beg = row_ptr[i], end = row_ptr[i + 1];
-  const int ngroups = (end - beg + G - 1) / G;
-  float a[MT][NH / 4];
-  auto hidden = [&](int g) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int q = beg + g * G + 16 * mt + (lane & 15);
-      const bool v = q < end;
-      hidden_A<NB, NH>(r_len[v ? q : end - 1], v, rp, lane, a[mt]);   // end > beg here
-    }
-  };
-  if (ngroups == 1) hidden(0);
-  for (int c = 0; c < U / 16; ++c) {
-    const int u = 16 * c + (lane & 15);
-    float acc[S::OC];
-#pragma unroll
-    for (int o = 0; o < S::OC; ++o) acc[o] = 0.f;
-    for (int g = 0; g < ngroups; ++g) {
-      if (ngroups > 1) hidden(g);
-      f32x4 C[MT][S::NP];
-      radial_weights<S, U, NH, MT>(a, rp.W2, c, lane, C);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = beg + g * G + 16 * mt + 4 * (lane >> 4) + r;
-          const int qc = q < end ? q : end - 1;   // weights of a padded edge are zero
-          float xr[S::XC], yr[S::YC], wr[S::NP];
-          load_x_channel<S, U>(x, col[qc], u, xr);
-#pragma unroll
-          for (int b = 0; b < S::YC; ++b) yr[b] = Y[(size_t)qc * S::YC + b];
-#pragma unroll
-          for (int p = 0; p < S::NP; ++p) wr[p] = C[mt][p][r];
-          edge_fwd<S>(xr, yr, wr, acc);
-        }
-    }
-    reduce_quads<S::OC>(acc);
-    if (lane < 16) {
-      float* row = out + (size_t)i * (U * S::OC);
-      static_for<S::NO>([&](auto K) {
-        constexpr OutInfo oi = S::outs.o[K];
-        constexpr int d = 2 * oi.l + 1;
-        static_for<d>([&](auto C2) { row[U * oi.ko + u * d + C2] = acc[oi.ko + C2]; });
-      });
-    }
-  }
-}
-
-
 // ---------------------------------------------------------------------------
 // backward
 //
@@ -198,18 +81,32 @@ __global__ void __launch_bounds__(64)
 
 __device__ __forceinline__ int hid_T(int k, int g) { return 16 * (k >> 2) + 4 * g + (k & 3); }
 
-// hidden values (B operands of the transposed tile) and SiLU derivatives of the
-// lane's edge; both zero for an invalid edge
+// Hidden values and SiLU derivatives of the edge of lane l (edge l%16 of a
+// 16-edge tile) in K-slot order: hB[k] = h[hid_T(k, l/16)].  The
+// pre-activations come from a small MFMA, pre^T = W1^T B^T (K = NB), whose D
+// layout is exactly that order.  bq[s] = B_{4s + l/16 + 1}(r) is kept for the
+// grad_W1 reduction.  Everything is zero for an invalid edge.
 template <int NB, int NH>
-__device__ __forceinline__ void hidden_T(float r, bool valid, const RadialParams& rp, int g,
-                                         float (&b)[NB], float (&hB)[NH / 4], float (&ds)[NH / 4]) {
-  bessel<NB>(valid ? r : 1.0f, rp.r_cut, b);
+__device__ __forceinline__ void hidden_T(float r, bool valid, const RadialParams& rp, int e16, int g,
+                                         float (&bq)[NB / 4], float (&hB)[NH / 4], float (&ds)[NH / 4]) {
+  static_assert(NB % 4 == 0 && NH % 16 == 0, "hidden tiling");
+  const float rr = valid ? r : 1.0f;
+  const float pre_b = sqrtf(2.0f / rp.r_cut) / rr;
+  const float kk = 3.14159265358979323846f / rp.r_cut;
 #pragma unroll
-  for (int k = 0; k < NH / 4; ++k) {
-    const float z = hidden_pre<NB, NH>(b, rp.W1, hid_T(k, g));
-    const float s = 1.0f / (1.0f + expf(-z));
-    hB[k] = valid ? z * s : 0.f;
-    ds[k] = valid ? s * (1.0f + z * (1.0f - s)) : 0.f;
+  for (int s = 0; s < NB / 4; ++s) bq[s] = valid ? pre_b * sinf((float)(4 * s + g + 1) * kk * rr) : 0.f;
+#pragma unroll
+  for (int t = 0; t < NH / 16; ++t) {
+    f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NB / 4; ++s) z = mfma_16x16x4(rp.W1[(4 * s + g) * NH + 16 * t + e16], bq[s], z);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pre = z[i];
+      const float sg = 1.0f / (1.0f + expf(-pre));
+      hB[4 * t + i] = valid ? pre * sg : 0.f;
+      ds[4 * t + i] = valid ? sg * (1.0f + pre * (1.0f - sg)) : 0.f;
+    }
   }
 }
 
@@ -231,131 +128,226 @@ __device__ __forceinline__ void load_x4(const float* __restrict__ x, int j, int 
   });
 }
 
-template <class S, int U>
-__device__ __forceinline__ void load_o4(const float* __restrict__ g, int i, int u0, float (&gr)[4][S::OC]) {
-  const float* row = g + (size_t)i * (U * S::OC);
-  static_for<S::NO>([&](auto K) {
-    constexpr OutInfo oi = S::outs.o[K];
-    constexpr int d = 2 * oi.l + 1;
-    const float4* p = reinterpret_cast<const float4*>(row + U * oi.ko + u0 * d);
-    float v[4 * d];
-    static_for<d>([&](auto Q) {
-      const float4 t = p[Q];
-      v[4 * Q + 0] = t.x; v[4 * Q + 1] = t.y; v[4 * Q + 2] = t.z; v[4 * Q + 3] = t.w;
-    });
-    static_for<4>([&](auto I2) { static_for<d>([&](auto C) { gr[I2][oi.ko + C] = v[I2 * d + C]; }); });
+// W2 slice of one chunk of 16 channels in LDS: row hid holds, for every path p,
+// the 16 floats W2[hid][p*U + 16c .. +15], then 4 floats of padding.  With the
+// row stride of NP*16 + 4 floats both operand patterns read conflict-free:
+// 16 consecutive floats from four rows 4 apart (A of the w-MFMA), and 16 bytes
+// from sixteen consecutive rows (A of the grad_h-MFMA).
+template <class S, int NH>
+struct W2Slice {
+  static constexpr int WS = S::NP * 16 + 4;          // row stride, floats
+  static constexpr int FLOATS = NH * WS;
+  static constexpr int QUADS = FLOATS / 4;
+  static constexpr int BYTES = FLOATS * 4;
+};
+
+// cooperative global->LDS copy of chunk c's slice by the NW waves of a workgroup
+template <class S, int U, int NH, int NW>
+__device__ __forceinline__ void stage_w2(float* w2s, const float* __restrict__ W2, int c, int wv, int lane) {
+  using L = W2Slice<S, NH>;
+  constexpr int INSTR = (L::QUADS + 64 * NW - 1) / (64 * NW);
+  // opaque copy of the lane index: the per-lane source offsets are recomputed
+  // per chunk instead of being hoisted into INSTR live 64-bit registers
+  asm volatile("" : "+v"(lane));
+  static_for<INSTR>([&](auto K) {
+    const int blk = K * NW + wv;                    // 64-quad block of this instruction
+    const int q = blk * 64 + lane;
+    if (blk * 64 < L::QUADS && q < L::QUADS) {
+      const int f = 4 * q;
+      const int hid = f / L::WS, rem = f - hid * L::WS;
+      const int p = rem >> 4;
+      const float* src = rem < S::NP * 16 ? W2 + (size_t)hid * (S::NP * U) + p * U + 16 * c + (rem & 15) : W2;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(w2s + blk * 256), 16, 0, 0);
+    }
   });
 }
 
-// Receiver pass: one wave walks receivers i = blockIdx.x, +gridDim.x, ...; per
-// 16-edge tile and chunk of 16 channels, each path p gives w (MFMA), the Z-form
-// adjoint (grad_w_p, grad_Y += w_p Z_p) and grad_h += W2_p grad_w_p (MFMA).
+// the chunk's 16 channels of grad_out row i into LDS (output blocks back to
+// back, each [16][2l+1]); two load instructions per wave
+template <class S, int U>
+__device__ __forceinline__ void stage_g(float* gs, const float* __restrict__ g, int i, int c, int lane) {
+  constexpr int QUADS = 4 * S::OC;                  // 16 * OC floats
+  const float* row = g + (size_t)i * (U * S::OC);
+  static_for<(QUADS + 63) / 64>([&](auto K) {
+    const int q = K * 64 + lane;
+    if (q < QUADS) {
+      // block of quad q: blocks hold 4(2l+1) quads each, in output order
+      int k = 0;
+      static_for<S::NO>([&](auto K2) {
+        if (q >= 4 * S::outs.o[K2].ko) k = K2;
+      });
+      int ko = 0, d = 1;
+      static_for<S::NO>([&](auto K2) {
+        if (k == K2) { ko = S::outs.o[K2].ko; d = 2 * S::outs.o[K2].l + 1; }
+      });
+      const float* src = row + U * ko + 16 * c * d + (4 * q - 16 * ko);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)(gs + K * 256), 16, 0, 0);
+    }
+  });
+}
+
+// Receiver pass.  A workgroup of NW waves walks its receivers tile by tile
+// (16 edges of one receiver per wave and round); within a round the waves go
+// through the chunks together: the chunk's W2 slice is copied once into LDS
+// for all of them, and grad_out of each wave's receiver is staged beside it.
+// Per chunk and path: w (MFMA, A from LDS), the Z-form adjoint on VALU
+// (grad_w_p, grad_Y += w_p Z_p) and grad_h += W2_p grad_w_p (MFMA).  After the
+// chunks: grad_Y is summed over the edge's channel lanes and stored, and
 // grad_W1 = B^T (grad_h * SiLU') is reduced through LDS into one partial per
-// workgroup (part[blockIdx.x][n][hid]), summed later in a fixed order.
-template <class S, int U, int NB, int NH>
-__global__ void __launch_bounds__(64)
+// wave (part[wave][n][hid]), summed later in a fixed order.
+template <class S, int U, int NB, int NH, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
     k_radial_bwd_recv(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                       const float* __restrict__ x, const float* __restrict__ Y,
                       const float* __restrict__ r_len, RadialParams rp, const float* __restrict__ gout,
                       float* __restrict__ grad_Y, float* __restrict__ part) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NH <= 64, "radial tiling");
-  constexpr int LD = S::NP * U;      // row length of W2
-  __shared__ float s_gp[16][NH + 1];
-  __shared__ float s_b[16][NB];
-  const int lane = threadIdx.x, e16 = lane & 15, g = lane >> 4;
+  using L = W2Slice<S, NH>;
+  constexpr int GF = 16 * S::OC;                    // staged grad_out floats per wave
+  constexpr int RED = 16 * (NH + 1) + 16 * NB;      // grad_W1 scratch floats per wave
+  static_assert(NW * RED <= L::FLOATS, "grad_W1 scratch reuses the W2 slice");
+  __shared__ __attribute__((aligned(16))) float smem[L::FLOATS + NW * GF];
+  float* w2s = smem;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e16 = lane & 15, g = lane >> 4;
+  float* gs = smem + L::FLOATS + wv * GF;
+  float* red = smem + wv * RED;                     // s_gp [16][NH+1], s_b [16][NB]
   float w1[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) w1[n] = 0.f;
-  for (int i = blockIdx.x; i < n_nodes; i += gridDim.x) {
-    const int beg = row_ptr[i], end = row_ptr[i + 1];
-    for (int t0 = beg; t0 < end; t0 += 16) {
-      const int q = t0 + e16;
-      const bool valid = q < end;
-      const int qc = valid ? q : end - 1;
-      const int j = col[qc];
-      float b[NB], hB[NH / 4], ds[NH / 4], yr[S::YC], gy[S::YC];
-      hidden_T<NB, NH>(r_len[qc], valid, rp, g, b, hB, ds);
+  // tile cursor of this wave: receiver i, first edge t0
+  const int stride = gridDim.x * NW;
+  int i = blockIdx.x * NW + wv, t0 = 0, end = 0;
+  auto seek = [&]() {   // first receiver >= i with edges
+    while (i < n_nodes) {
+      t0 = row_ptr[i];
+      end = row_ptr[i + 1];
+      if (t0 < end) break;
+      i += stride;
+    }
+  };
+  seek();
+  while (__syncthreads_or(i < n_nodes)) {
+    const bool has = i < n_nodes;
+    const int q = t0 + e16;
+    const bool valid = has && q < end;
+    const int qc = has ? (q < end ? q : end - 1) : 0;
+    const int j = has ? col[qc] : 0;
+    float bq[NB / 4], hB[NH / 4], ds[NH / 4], yr[S::YC], gy[S::YC];
+    hidden_T<NB, NH>(has ? r_len[qc] : 1.f, valid, rp, e16, g, bq, hB, ds);
 #pragma unroll
-      for (int t = 0; t < S::YC; ++t) {
-        yr[t] = Y[(size_t)qc * S::YC + t];
-        gy[t] = 0.f;
-      }
-      f32x4 gh[NH / 16];
+    for (int t = 0; t < S::YC; ++t) {
+      yr[t] = has ? Y[(size_t)qc * S::YC + t] : 0.f;
+      gy[t] = 0.f;
+    }
+    f32x4 gh[NH / 16];
 #pragma unroll
-      for (int t = 0; t < NH / 16; ++t) gh[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NH / 16; ++t) gh[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-      for (int c = 0; c < U / 16; ++c) {
-        const int u0 = 16 * c + 4 * g;
-        float xr[4][S::XC], gr[4][S::OC];
-        load_x4<S, U>(x, j, u0, xr);
-        load_o4<S, U>(gout, i, u0, gr);
+    for (int c = 0; c < U / 16; ++c) {
+      const int u0 = 16 * c + 4 * g;
+      __syncthreads();                              // previous chunk's LDS reads done
+      stage_w2<S, U, NH, NW>(w2s, rp.W2, c, wv, lane);
+      if (has) stage_g<S, U>(gs, gout, i, c, lane);
+      float xr[4][S::XC];
+      load_x4<S, U>(x, j, u0, xr);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (has) {
         static_for<S::NP>([&](auto P) {
           constexpr PathInfo pi = S::paths.p[P];
           using T = CgPath<pi.l1, pi.l2, pi.l3>;
-          constexpr int D2 = 2 * pi.l2 + 1;
-          // w[channel 16c + 4g + r][edge e16], r = 0..3
-          const float* wa = rp.W2 + P * U + 16 * c + e16;
+          constexpr int D2 = 2 * pi.l2 + 1, D3 = 2 * pi.l3 + 1;
+          // w[channel 16c + 4g + r][edge e16]
+          const float* wa = w2s + P * 16 + e16;
           f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int k = 0; k < NH / 4; ++k) w = mfma_16x16x4(wa[(size_t)hid_T(k, g) * LD], hB[k], w);
+          for (int k = 0; k < NH / 4; ++k) w = mfma_16x16x4(wa[hid_T(k, g) * L::WS], hB[k], w);
+          // grad_out block of the path's output irrep, the lane's four channels
+          float gb[4 * D3];
+          const float4* gp = reinterpret_cast<const float4*>(gs + 16 * pi.ko + 4 * g * D3);
+          static_for<D3>([&](auto Q) {
+            const float4 t = gp[Q];
+            gb[4 * Q + 0] = t.x; gb[4 * Q + 1] = t.y; gb[4 * Q + 2] = t.z; gb[4 * Q + 3] = t.w;
+          });
           float gw[4];
           static_for<4>([&](auto R) {
-            float z[D2];
-            static_for<D2>([&](auto B2) { z[B2] = 0.f; });
+            // z[b] = sum_c g_c sum_a C_abc x_a (contracting x first keeps the
+            // temporaries local to the path)
+            float t[D2][D3];
+            static_for<D2>([&](auto B2) {
+              static_for<D3>([&](auto C3) {
+                if constexpr (T::has_bc(B2, C3)) t[B2][C3] = 0.f;
+              });
+            });
             static_for<T::nnz>([&](auto N) {
               constexpr Nz e = T::table.e[N];
-              z[e.b] = fmaf(e.v, xr[R][pi.xo + e.a] * gr[R][pi.ko + e.c], z[e.b]);
+              t[e.b][e.c] = fmaf(e.v, xr[R][pi.xo + e.a], t[e.b][e.c]);
             });
             float s = 0.f;
             static_for<D2>([&](auto B2) {
-              s = fmaf(yr[pi.yo + B2], z[B2], s);
-              gy[pi.yo + B2] = fmaf(w[int(R)], z[B2], gy[pi.yo + B2]);
+              float z = 0.f;
+              static_for<D3>([&](auto C3) {
+                if constexpr (T::has_bc(B2, C3)) z = fmaf(t[B2][C3], gb[R * D3 + C3], z);
+              });
+              s = fmaf(yr[pi.yo + B2], z, s);
+              gy[pi.yo + B2] = fmaf(w[int(R)], z, gy[pi.yo + B2]);
             });
             gw[R] = s;
           });
           // grad_h[hid 16t + 4g + r][edge e16] += sum over the chunk's channels
-          const float* wb = rp.W2 + (size_t)e16 * LD + P * U + u0;
+          const float* wb = w2s + e16 * L::WS + P * 16 + 4 * g;
 #pragma unroll
           for (int t = 0; t < NH / 16; ++t) {
-            const float4 a4 = *reinterpret_cast<const float4*>(wb + (size_t)16 * t * LD);
+            const float4 a4 = *reinterpret_cast<const float4*>(wb + 16 * t * L::WS);
             gh[t] = mfma_16x16x4(a4.x, gw[0], gh[t]);
             gh[t] = mfma_16x16x4(a4.y, gw[1], gh[t]);
             gh[t] = mfma_16x16x4(a4.z, gw[2], gh[t]);
             gh[t] = mfma_16x16x4(a4.w, gw[3], gh[t]);
           }
+          __builtin_amdgcn_sched_barrier(0);        // keep each path's temporaries local
         });
       }
-      // grad_Y: sum over the four channel groups of the edge
+    }
+    // grad_Y: sum over the four channel groups of the edge
 #pragma unroll
-      for (int t = 0; t < S::YC; ++t) {
-        gy[t] += __shfl_xor(gy[t], 16, 64);
-        gy[t] += __shfl_xor(gy[t], 32, 64);
-      }
-      if (grad_Y && g == 0 && valid) {
+    for (int t = 0; t < S::YC; ++t) {
+      gy[t] += __shfl_xor(gy[t], 16, 64);
+      gy[t] += __shfl_xor(gy[t], 32, 64);
+    }
+    if (grad_Y && g == 0 && valid) {
 #pragma unroll
-        for (int t = 0; t < S::YC; ++t) grad_Y[(size_t)q * S::YC + t] = gy[t];
-      }
-      // grad_W1[n][hid] += sum over the tile's edges of B_n * grad_pre[hid]
+      for (int t = 0; t < S::YC; ++t) grad_Y[(size_t)q * S::YC + t] = gy[t];
+    }
+    // grad_W1[n][hid] += sum over the tile's edges of B_n * grad_pre[hid]
+    __syncthreads();                                // W2 slice no longer read
+    if (has) {
+      float* s_gp = red;
+      float* s_b = red + 16 * (NH + 1);
 #pragma unroll
-      for (int k = 0; k < NH / 4; ++k) s_gp[e16][hid_T(k, g)] = gh[k >> 2][k & 3] * ds[k];
-      if (g == 0) {
+      for (int k = 0; k < NH / 4; ++k) s_gp[e16 * (NH + 1) + hid_T(k, g)] = gh[k >> 2][k & 3] * ds[k];
 #pragma unroll
-        for (int n = 0; n < NB; ++n) s_b[e16][n] = b[n];
-      }
-      __syncthreads();
+      for (int t = 0; t < NB / 4; ++t) s_b[e16 * NB + 4 * t + g] = bq[t];
+      __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): own LDS writes done (one wave)
+      __builtin_amdgcn_wave_barrier();
       if (lane < NH) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float gp = s_gp[e][lane];
+          const float gp = s_gp[e * (NH + 1) + lane];
 #pragma unroll
-          for (int n = 0; n < NB; ++n) w1[n] = fmaf(s_b[e][n], gp, w1[n]);
+          for (int n = 0; n < NB; ++n) w1[n] = fmaf(s_b[e * NB + n], gp, w1[n]);
         }
       }
-      __syncthreads();
+      // advance the cursor
+      t0 += 16;
+      if (t0 >= end) {
+        i += stride;
+        seek();
+      }
     }
   }
   if (lane < NH) {
-    float* p = part + (size_t)blockIdx.x * (NB * NH);
+    float* p = part + (size_t)(blockIdx.x * NW + wv) * (NB * NH);
 #pragma unroll
     for (int n = 0; n < NB; ++n) p[n * NH + lane] = w1[n];
   }
@@ -457,63 +449,94 @@ __global__ void __launch_bounds__(64 * ((S::NP + PGS - 1) / PGS))
   });
 }
 
-// Sender pass (grad_x): the forward's structure over the sender grouping; w is
-// recomputed per chunk by MFMA, grad_out of each edge's receiver is gathered.
-template <class S, int U, int NB, int NH>
-__global__ void __launch_bounds__(64)
-    k_radial_bwd_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
-                      const int32_t* __restrict__ t_col, const float* __restrict__ Y,
-                      const float* __restrict__ r_len, RadialParams rp, const float* __restrict__ gout,
-                      float* __restrict__ grad_x) {
-  static_assert(U % 16 == 0 && NH % 4 == 0, "radial tiling");
-  constexpr int MT = kRadialMT, G = 16 * MT;
-  const int j = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
-  const int ngroups = (end - beg + G - 1) / G;
-  float a[MT][NH / 4];
-  auto hidden = [&](int gi) {
+// Forward (SEND = false) and sender pass (SEND = true), chunk-major: workgroup
+// (block, chunk c) keeps chunk c's W2 slice in LDS for its whole life and its
+// NW waves walk nodes i = block*NW + wave, + gridDim.x*NW, ...  Per 16-edge
+// tile the hidden values come from the small MFMA, the weights of every path
+// from the w-MFMA (A = hidden rows of the tile's edges, B = the slice), so lane
+// l holds w[edge 4(l/16) + r][channel 16c + l%16]; the per-lane products then
+// run over the lane's four edges.  Forward: out[i] of receiver i (edges
+// grouped by receiver, x of each sender gathered).  Sender pass: grad_x[j] of
+// sender j (edges grouped by sender through t_perm, grad_out of each receiver
+// gathered).  Each output row chunk is written once; no atomics.
+template <class S, int U, int NB, int NH, int NW, bool SEND>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+    k_radial_node(int n_nodes, const int32_t* __restrict__ ptr, const int32_t* __restrict__ perm,
+                  const int32_t* __restrict__ other, const float* __restrict__ feat,
+                  const float* __restrict__ Y, const float* __restrict__ r_len, RadialParams rp,
+                  float* __restrict__ outp) {
+  static_assert(U % 16 == 0 && NH % 16 == 0 && NH <= 64, "radial tiling");
+  using L = W2Slice<S, NH>;
+  constexpr int NA = SEND ? S::XC : S::OC;          // accumulated components per channel
+  __shared__ __attribute__((aligned(16))) float w2s[L::FLOATS];
+  const int c = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e16 = lane & 15, g = lane >> 4;
+  const int u = 16 * c + e16;
+  stage_w2<S, U, NH, NW>(w2s, rp.W2, c, wv, lane);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int i = blockIdx.x * NW + wv; i < n_nodes; i += gridDim.x * NW) {
+    const int beg = ptr[i], end = ptr[i + 1];
+    float acc[NA];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int q = beg + gi * G + 16 * mt + (lane & 15);
-      const bool v = q < end;
-      hidden_A<NB, NH>(r_len[t_perm[v ? q : end - 1]], v, rp, lane, a[mt]);   // end > beg here
-    }
-  };
-  if (ngroups == 1) hidden(0);
-  for (int c = 0; c < U / 16; ++c) {
-    const int u = 16 * c + (lane & 15);
-    float acc[S::XC];
+    for (int o = 0; o < NA; ++o) acc[o] = 0.f;
+    for (int t0 = beg; t0 < end; t0 += 16) {
+      const int qa = t0 + e16;
+      const bool va = qa < end;
+      const int qac = va ? qa : end - 1;
+      float bq[NB / 4], hB[NH / 4], ds[NH / 4];
+      hidden_T<NB, NH>(r_len[SEND ? perm[qac] : qac], va, rp, e16, g, bq, hB, ds);
+      f32x4 C[S::NP];
 #pragma unroll
-    for (int o = 0; o < S::XC; ++o) acc[o] = 0.f;
-    for (int gi = 0; gi < ngroups; ++gi) {
-      if (ngroups > 1) hidden(gi);
-      f32x4 C[MT][S::NP];
-      radial_weights<S, U, NH, MT>(a, rp.W2, c, lane, C);
+      for (int p = 0; p < S::NP; ++p) {
+        C[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const float* wb = w2s + p * 16 + e16;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int k = 0; k < NH / 4; ++k) C[p] = mfma_16x16x4(hB[k], wb[hid_T(k, g) * L::WS], C[p]);
+      }
+      // the lane's four edges; the operands of edge r+1 are requested before
+      // edge r is computed
+      constexpr int NF = SEND ? S::OC : S::XC;
+      float fr[2][NF], yr[2][S::YC];
+      auto fetch = [&](int r, float (&f)[NF], float (&y)[S::YC]) {
+        const int q = t0 + 4 * g + r;
+        const int qc = q < end ? q : end - 1;       // weights of a padded edge are zero
+        const int e = SEND ? perm[qc] : qc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = beg + gi * G + 16 * mt + 4 * (lane >> 4) + r;
-          const int qc = q < end ? q : end - 1;   // weights of a padded edge are zero
-          const int e = t_perm[qc];
-          float gr[S::OC], yr[S::YC], wr[S::NP];
-          load_o_channel<S, U>(gout, t_col[qc], u, gr);
+        for (int b = 0; b < S::YC; ++b) y[b] = Y[(size_t)e * S::YC + b];
+        if constexpr (SEND) load_o_channel<S, U>(feat, other[qc], u, f);
+        else load_x_channel<S, U>(feat, other[qc], u, f);
+      };
+      fetch(0, fr[0], yr[0]);
+      static_for<4>([&](auto R) {
+        if constexpr (R < 3) fetch(R + 1, fr[(R + 1) & 1], yr[(R + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        float wr[S::NP];
 #pragma unroll
-          for (int b = 0; b < S::YC; ++b) yr[b] = Y[(size_t)e * S::YC + b];
-#pragma unroll
-          for (int p = 0; p < S::NP; ++p) wr[p] = C[mt][p][r];
-          edge_bwd_send<S>(yr, wr, gr, acc);
-        }
-    }
-    reduce_quads<S::XC>(acc);
-    if (lane < 16) {
-      float* row = grad_x + (size_t)j * (U * S::XC);
-      static_for<S::NIN>([&](auto I) {
-        constexpr int d = 2 * S::ls.v[I] + 1;
-        constexpr int xo = S::xoff(I);
-        static_for<d>([&](auto A) { row[U * xo + u * d + A] = acc[xo + A]; });
+        for (int p = 0; p < S::NP; ++p) wr[p] = C[p][int(R)];
+        if constexpr (SEND) edge_bwd_send<S>(yr[R & 1], wr, fr[R & 1], acc);
+        else edge_fwd<S>(fr[R & 1], yr[R & 1], wr, acc);
+        __builtin_amdgcn_sched_barrier(0);          // one edge's operands in flight at a time
       });
+    }
+    reduce_quads<NA>(acc);
+    if (lane < 16) {
+      if constexpr (SEND) {
+        float* row = outp + (size_t)i * (U * S::XC);
+        static_for<S::NIN>([&](auto I) {
+          constexpr int d = 2 * S::ls.v[I] + 1;
+          constexpr int xo = S::xoff(I);
+          static_for<d>([&](auto A) { row[U * xo + u * d + A] = acc[xo + A]; });
+        });
+      } else {
+        float* row = outp + (size_t)i * (U * S::OC);
+        static_for<S::NO>([&](auto K) {
+          constexpr OutInfo oi = S::outs.o[K];
+          constexpr int d = 2 * oi.l + 1;
+          static_for<d>([&](auto C2) { row[U * oi.ko + u * d + C2] = acc[oi.ko + C2]; });
+        });
+      }
     }
   }
 }

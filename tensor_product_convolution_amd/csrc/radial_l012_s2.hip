@@ -22,7 +22,12 @@ __global__ void __launch_bounds__(256)
 
 // persistent grid sizes (fixed functions of the node count, so the partial
 // sums and hence the results do not depend on the device)
-int recv_blocks(int n_nodes) { return n_nodes < 2048 ? (n_nodes > 0 ? n_nodes : 1) : 2048; }
+constexpr int kRecvWaves = 4;                             // waves per receiver-pass workgroup
+int recv_blocks(int n_nodes) {
+  const int b = (n_nodes + kRecvWaves - 1) / kRecvWaves;
+  return b < 512 ? (b > 0 ? b : 1) : 512;                 // two workgroups per CU
+}
+int recv_parts(int n_nodes) { return recv_blocks(n_nodes) * kRecvWaves; }
 template <int U>
 int w2_blocks(int n_nodes) {
   const int cap = 2048 / (U / 16);
@@ -33,18 +38,27 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 }  // namespace
 
+constexpr int kNodeWaves = 4;                             // waves per forward / sender workgroup
+// chunk-major grid: (node blocks, chunks); about two workgroups per CU in all
+template <int U>
+dim3 node_grid(int n_nodes) {
+  const int want = (n_nodes + kNodeWaves - 1) / kNodeWaves, cap = 512 / (U / 16);
+  return dim3(want < cap ? (want > 0 ? want : 1) : cap, U / 16);
+}
+
 template <int U>
 static hipError_t launch_radial_fwd(const RadialArgs& a) {
   if (a.n_nodes == 0) return hipSuccess;
   RadialParams rp{a.r_cut, a.W1, a.W2};
-  hipLaunchKernelGGL((k_radial_fwd<SigR, U, kNB, kNH>), dim3(a.n_nodes), dim3(64), 0, a.stream,
-                     a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.out);
+  hipLaunchKernelGGL((k_radial_node<SigR, U, kNB, kNH, kNodeWaves, false>), node_grid<U>(a.n_nodes),
+                     dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.row_ptr, nullptr, a.col, a.x, a.Y,
+                     a.r_len, rp, a.out);
   return hipGetLastError();
 }
 
 template <int U>
 static size_t radial_bwd_ws(int n_nodes, int /*n_edges*/) {
-  return align256((size_t)recv_blocks(n_nodes) * kNB * kNH * sizeof(float)) +
+  return align256((size_t)recv_parts(n_nodes) * kNB * kNH * sizeof(float)) +
          (size_t)w2_blocks<U>(n_nodes) * kNH * SigR::NP * U * sizeof(float);
 }
 
@@ -53,13 +67,14 @@ static size_t radial_bwd_ws(int n_nodes, int /*n_edges*/) {
 template <int U>
 static hipError_t launch_radial_bwd(const RadialArgs& a) {
   RadialParams rp{a.r_cut, a.W1, a.W2};
-  const int nb1 = recv_blocks(a.n_nodes), nb2 = w2_blocks<U>(a.n_nodes);
+  const int nb1 = recv_parts(a.n_nodes), nb2 = w2_blocks<U>(a.n_nodes);
   float* part1 = static_cast<float*>(a.ws);
   float* part2 = reinterpret_cast<float*>(static_cast<char*>(a.ws) +
                                           align256((size_t)nb1 * kNB * kNH * sizeof(float)));
   if (a.grad_Y || a.grad_W1) {
-    hipLaunchKernelGGL((k_radial_bwd_recv<SigR, U, kNB, kNH>), dim3(nb1), dim3(64), 0, a.stream,
-                       a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.grad_out, a.grad_Y, part1);
+    hipLaunchKernelGGL((k_radial_bwd_recv<SigR, U, kNB, kNH, kRecvWaves>), dim3(recv_blocks(a.n_nodes)),
+                       dim3(64 * kRecvWaves), 0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len,
+                       rp, a.grad_out, a.grad_Y, part1);
     if (a.grad_W1) {
       const long long n = (long long)kNB * kNH;
       hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream, part1,
@@ -74,8 +89,9 @@ static hipError_t launch_radial_bwd(const RadialArgs& a) {
                        n, a.grad_W2);
   }
   if (a.grad_x && a.n_nodes > 0)
-    hipLaunchKernelGGL((k_radial_bwd_send<SigR, U, kNB, kNH>), dim3(a.n_nodes), dim3(64), 0, a.stream,
-                       a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.r_len, rp, a.grad_out, a.grad_x);
+    hipLaunchKernelGGL((k_radial_node<SigR, U, kNB, kNH, kNodeWaves, true>), node_grid<U>(a.n_nodes),
+                       dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.t_row_ptr, a.t_perm, a.t_col,
+                       a.grad_out, a.Y, a.r_len, rp, a.grad_x);
   return hipGetLastError();
 }
 
