@@ -353,100 +353,142 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
-// grad_W2 pass: workgroup (block, chunk c) with one wave per group of PGS
-// paths; the waves walk the same receivers' edges.  Tile: M = 16 hidden units,
-// N = 16 channels, K = edges; lane l owns channel 16c + l%16 and edges
-// 4(l/16)..+3 of a 16-edge tile.  The hidden values come from a small MFMA
-// (pre = B W1, K = NB) whose D layout is exactly the A operand needed here.
-template <class S, int U, int NB, int NH, int PGS>
-__global__ void __launch_bounds__(64 * ((S::NP + PGS - 1) / PGS))
+// grad_W2 pass, chunk-major: workgroup (block, chunk c) of NH/16 waves.  Per
+// round every wave takes one 16-edge tile of its receivers and computes the
+// Z-form adjoint grad_w of all paths for it (lane l: edges 4(l/16) + r, channel
+// 16c + l%16), written to LDS; after a barrier wave w contracts the four
+// tiles' grad_w with the hidden values of its own 16 hidden units:
+//   grad_W2[hid 16w + .][p*U + 16c + .] += sum over edges of h * grad_w_p
+// (MFMA: M = hidden units, N = channels, K = edges).  The hidden values come
+// from the small MFMA pre = B W1 (K = NB) whose D layout is the A operand
+// needed here, so each wave computes only its own 16 hidden units.  The
+// accumulators (one 16x16 tile per path) stay in registers; one partial per
+// workgroup is written and summed later in a fixed order.
+template <class S, int U, int NB, int NH>
+__global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_per_eu(2)))
     k_radial_bwd_w2(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                     const float* __restrict__ x, const float* __restrict__ Y,
                     const float* __restrict__ r_len, RadialParams rp, const float* __restrict__ gout,
                     float* __restrict__ part) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NB % 4 == 0, "radial tiling");
-  constexpr int NPG = (S::NP + PGS - 1) / PGS;
+  constexpr int NW = NH / 16;
   constexpr int LD = S::NP * U;
+  // grad_w of one tile in LDS: [p][edge 16][ch 16 + 4 pad]; the edge-row stride
+  // of 20 floats puts the four lane groups (edges 4g + k) on distinct banks
+  constexpr int RS = 20, PS = 16 * RS;
+  constexpr int TILE = S::NP * PS;
+  __shared__ __attribute__((aligned(16))) float s_gw[NW * TILE];
+  __shared__ float s_r[NW * 16];                    // edge lengths of the tiles (-1: no edge)
   const int c = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e16 = lane & 15, g = lane >> 4;
   const int u = 16 * c + e16;
-  static_for<NPG>([&](auto G) {
-    if (wv != G) return;
-    constexpr int P0 = G * PGS;
-    constexpr int NPP = S::NP - P0 < PGS ? S::NP - P0 : PGS;
-    f32x4 acc[NPP][NH / 16];
-    static_for<NPP>([&](auto PP) {
+  f32x4 acc[S::NP];
 #pragma unroll
-      for (int t = 0; t < NH / 16; ++t) acc[PP][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    });
-    for (int i = blockIdx.x; i < n_nodes; i += gridDim.x) {
-      const int beg = row_ptr[i], end = row_ptr[i + 1];
-      if (beg == end) continue;
+  for (int p = 0; p < S::NP; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // W1 operands of this wave's hidden units (B[n][hid 16w + e16], n = 4s + g)
+  float w1b[NB / 4];
+#pragma unroll
+  for (int s = 0; s < NB / 4; ++s) w1b[s] = rp.W1[(4 * s + g) * NH + 16 * wv + e16];
+  const float pre_b = sqrtf(2.0f / rp.r_cut);
+  const float kk = 3.14159265358979323846f / rp.r_cut;
+  const int stride = gridDim.x * NW;
+  int i = blockIdx.x * NW + wv, t0 = 0, end = 0;
+  auto seek = [&]() {
+    while (i < n_nodes) {
+      t0 = row_ptr[i];
+      end = row_ptr[i + 1];
+      if (t0 < end) break;
+      i += stride;
+    }
+  };
+  seek();
+  float* gw_own = s_gw + wv * TILE;
+  while (__syncthreads_or(i < n_nodes)) {
+    if (i < n_nodes) {
+      if (g == 0) {
+        const int q = t0 + e16;
+        s_r[wv * 16 + e16] = q < end ? r_len[q] : -1.f;
+      }
       float gr[S::OC];
       load_o_channel<S, U>(gout, i, u, gr);
-      for (int t0 = beg; t0 < end; t0 += 16) {
-        // pre[edge 4g + r][hid 16t + e16] via MFMA: A = B_n(edge e16), B = W1
-        const int qa = t0 + e16;
-        const bool va = qa < end;
-        const float ra = va ? r_len[qa < end ? qa : end - 1] : 1.0f;
-        const float pre_b = sqrtf(2.0f / rp.r_cut) / ra;
-        const float kk = 3.14159265358979323846f / rp.r_cut;
-        float bn[NB / 4];
+      // grad_w of the lane's four edges, all paths
 #pragma unroll
-        for (int s = 0; s < NB / 4; ++s)
-          bn[s] = va ? pre_b * sinf((float)(4 * s + g + 1) * kk * ra) : 0.f;
-        float hA[NH / 16][4];
+      for (int r = 0; r < 4; ++r) {
+        const int q = t0 + 4 * g + r;
+        const int qc = q < end ? q : end - 1;       // its hidden values are zero
+        float xr[S::XC], yr[S::YC];
+        load_x_channel<S, U>(x, col[qc], u, xr);
 #pragma unroll
-        for (int t = 0; t < NH / 16; ++t) {
-          f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < NB / 4; ++s) z = mfma_16x16x4(bn[s], rp.W1[(4 * s + g) * NH + 16 * t + e16], z);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) hA[t][r] = silu(z[r]);
-        }
-        // grad_w of this wave's paths for the lane's four edges
-        float gw[NPP][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = t0 + 4 * g + r;
-          const int qc = q < end ? q : end - 1;   // its hidden values are zero
-          float xr[S::XC], yr[S::YC];
-          load_x_channel<S, U>(x, col[qc], u, xr);
-#pragma unroll
-          for (int t = 0; t < S::YC; ++t) yr[t] = Y[(size_t)qc * S::YC + t];
-          static_for<NPP>([&](auto PP) {
-            constexpr PathInfo pi = S::paths.p[P0 + PP];
-            using T = CgPath<pi.l1, pi.l2, pi.l3>;
-            constexpr int D2 = 2 * pi.l2 + 1;
-            float z[D2];
-            static_for<D2>([&](auto B2) { z[B2] = 0.f; });
-            static_for<T::nnz>([&](auto N) {
-              constexpr Nz e = T::table.e[N];
-              z[e.b] = fmaf(e.v, xr[pi.xo + e.a] * gr[pi.ko + e.c], z[e.b]);
+        for (int t = 0; t < S::YC; ++t) yr[t] = Y[(size_t)qc * S::YC + t];
+        static_for<S::NP>([&](auto P) {
+          constexpr PathInfo pi = S::paths.p[P];
+          using T = CgPath<pi.l1, pi.l2, pi.l3>;
+          constexpr int D2 = 2 * pi.l2 + 1, D3 = 2 * pi.l3 + 1;
+          float tt[D2][D3];
+          static_for<D2>([&](auto B2) {
+            static_for<D3>([&](auto C3) {
+              if constexpr (T::has_bc(B2, C3)) tt[B2][C3] = 0.f;
             });
-            float s = 0.f;
-            static_for<D2>([&](auto B2) { s = fmaf(yr[pi.yo + B2], z[B2], s); });
-            gw[PP][r] = s;
           });
-        }
-        static_for<NPP>([&](auto PP) {
-#pragma unroll
-          for (int t = 0; t < NH / 16; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[PP][t] = mfma_16x16x4(hA[t][r], gw[PP][r], acc[PP][t]);
+          static_for<T::nnz>([&](auto N) {
+            constexpr Nz e = T::table.e[N];
+            tt[e.b][e.c] = fmaf(e.v, xr[pi.xo + e.a], tt[e.b][e.c]);
+          });
+          float s = 0.f;
+          static_for<D2>([&](auto B2) {
+            float z = 0.f;
+            static_for<D3>([&](auto C3) {
+              if constexpr (T::has_bc(B2, C3)) z = fmaf(tt[B2][C3], gr[pi.ko + C3], z);
+            });
+            s = fmaf(yr[pi.yo + B2], z, s);
+          });
+          gw_own[P * PS + (4 * g + r) * RS + e16] = s;
         });
+        __builtin_amdgcn_sched_barrier(0);
       }
+      t0 += 16;
+      if (t0 >= end) {
+        i += stride;
+        seek();
+      }
+    } else {
+      // no tile this round: zero lengths and weights-gradients (the latter so
+      // that no stale or uninitialised LDS value meets a zero hidden value)
+      if (g == 0) s_r[wv * 16 + e16] = -1.f;
+      for (int t = lane; t < TILE; t += 64) gw_own[t] = 0.f;
     }
-    // part[block][hid][p*U + u] (each chunk writes its own columns)
-    float* pb = part + (size_t)blockIdx.x * NH * LD;
-    static_for<NPP>([&](auto PP) {
+    __syncthreads();
+    // contract the tiles of all waves with this wave's hidden units
+#pragma unroll 1
+    for (int tw = 0; tw < NW; ++tw) {
+      const float r = s_r[tw * 16 + e16];
+      const bool v = r >= 0.f;
+      const float rr = v ? r : 1.0f;
+      f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < NH / 16; ++t)
+      for (int s = 0; s < NB / 4; ++s) {
+        const float bn = v ? pre_b / rr * sinf((float)(4 * s + g + 1) * kk * rr) : 0.f;
+        z = mfma_16x16x4(bn, w1b[s], z);
+      }
+      // z[i] = pre[edge 4g + i][hid 16w + e16]; h = 0 for an invalid edge
+      float hA[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pb[(size_t)(16 * t + 4 * g + r) * LD + (P0 + PP) * U + u] = acc[PP][t][r];
-    });
-  });
+      for (int t = 0; t < 4; ++t) hA[t] = silu(z[t]);
+      const float* gt = s_gw + tw * TILE + 4 * g * RS + e16;
+#pragma unroll
+      for (int p = 0; p < S::NP; ++p)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[p] = mfma_16x16x4(hA[k], gt[p * PS + k * RS], acc[p]);
+    }
+    __syncthreads();
+  }
+  // part[block][hid][p*U + u]; each chunk writes its own columns
+  float* pb = part + (size_t)blockIdx.x * NH * LD;
+#pragma unroll
+  for (int p = 0; p < S::NP; ++p)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pb[(size_t)(16 * wv + 4 * g + t) * LD + p * U + u] = acc[p][t];
 }
 
 // Forward (SEND = false) and sender pass (SEND = true), chunk-major: workgroup

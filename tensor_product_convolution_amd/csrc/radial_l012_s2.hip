@@ -5,8 +5,6 @@ namespace tpc {
 
 using SigR = Sig<2, 2, 0, 1, 2>;
 constexpr int kNB = 8, kNH = 64;
-constexpr int kPGS = 4;                                   // paths per wave, grad_W2 pass
-constexpr int kNPG = (SigR::NP + kPGS - 1) / kPGS;
 
 namespace {
 
@@ -30,8 +28,8 @@ int recv_blocks(int n_nodes) {
 int recv_parts(int n_nodes) { return recv_blocks(n_nodes) * kRecvWaves; }
 template <int U>
 int w2_blocks(int n_nodes) {
-  const int cap = 2048 / (U / 16);
-  return n_nodes < cap ? (n_nodes > 0 ? n_nodes : 1) : cap;
+  const int want = (n_nodes + kNH / 16 - 1) / (kNH / 16), cap = 512 / (U / 16);
+  return want < cap ? (want > 0 ? want : 1) : cap;
 }
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -82,7 +80,7 @@ static hipError_t launch_radial_bwd(const RadialArgs& a) {
     }
   }
   if (a.grad_W2) {
-    hipLaunchKernelGGL((k_radial_bwd_w2<SigR, U, kNB, kNH, kPGS>), dim3(nb2, U / 16), dim3(64 * kNPG), 0,
+    hipLaunchKernelGGL((k_radial_bwd_w2<SigR, U, kNB, kNH>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)), 0,
                        a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.grad_out, part2);
     const long long n = (long long)kNH * SigR::NP * U;
     hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream, part2, nb2,
