@@ -33,7 +33,11 @@ struct RadialParams {
   const float* W2;   // [NH][P*U]
 };
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// logistic function with the hardware exponential and reciprocal (about 1e-6
+// relative error, far inside the float32 parity bound); exp overflow gives
+// inf and a result of 0, as it should
+__device__ __forceinline__ float sigmoid_fast(float z) { return __frcp_rn(1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu(float z) { return z * sigmoid_fast(z); }
 
 // x components of channel u of node row j
 template <class S, int U>
@@ -86,8 +90,18 @@ __device__ __forceinline__ int hid_T(int k, int g) { return 16 * (k >> 2) + 4 * 
 // pre-activations come from a small MFMA, pre^T = W1^T B^T (K = NB), whose D
 // layout is exactly that order.  bq[s] = B_{4s + l/16 + 1}(r) is kept for the
 // grad_W1 reduction.  Everything is zero for an invalid edge.
+// A operands W1[4s + l/16][16t + l%16] of the small MFMA, loaded once per kernel
 template <int NB, int NH>
-__device__ __forceinline__ void hidden_T(float r, bool valid, const RadialParams& rp, int e16, int g,
+__device__ __forceinline__ void load_w1a(const RadialParams& rp, int e16, int g, float (&w1a)[NH / 16][NB / 4]) {
+#pragma unroll
+  for (int t = 0; t < NH / 16; ++t)
+#pragma unroll
+    for (int s = 0; s < NB / 4; ++s) w1a[t][s] = rp.W1[(4 * s + g) * NH + 16 * t + e16];
+}
+
+template <int NB, int NH>
+__device__ __forceinline__ void hidden_T(float r, bool valid, const RadialParams& rp,
+                                         const float (&w1a)[NH / 16][NB / 4], int g,
                                          float (&bq)[NB / 4], float (&hB)[NH / 4], float (&ds)[NH / 4]) {
   static_assert(NB % 4 == 0 && NH % 16 == 0, "hidden tiling");
   const float rr = valid ? r : 1.0f;
@@ -99,11 +113,11 @@ __device__ __forceinline__ void hidden_T(float r, bool valid, const RadialParams
   for (int t = 0; t < NH / 16; ++t) {
     f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < NB / 4; ++s) z = mfma_16x16x4(rp.W1[(4 * s + g) * NH + 16 * t + e16], bq[s], z);
+    for (int s = 0; s < NB / 4; ++s) z = mfma_16x16x4(w1a[t][s], bq[s], z);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float pre = z[i];
-      const float sg = 1.0f / (1.0f + expf(-pre));
+      const float sg = sigmoid_fast(pre);
       hB[4 * t + i] = valid ? pre * sg : 0.f;
       ds[4 * t + i] = valid ? sg * (1.0f + pre * (1.0f - sg)) : 0.f;
     }
@@ -212,6 +226,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   const int e16 = lane & 15, g = lane >> 4;
   float* gs = smem + L::FLOATS + wv * GF;
   float* red = smem + wv * RED;                     // s_gp [16][NH+1], s_b [16][NB]
+  float w1a[NH / 16][NB / 4];
+  load_w1a<NB, NH>(rp, e16, g, w1a);
   float w1[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) w1[n] = 0.f;
@@ -234,7 +250,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     const int qc = has ? (q < end ? q : end - 1) : 0;
     const int j = has ? col[qc] : 0;
     float bq[NB / 4], hB[NH / 4], ds[NH / 4], yr[S::YC], gy[S::YC];
-    hidden_T<NB, NH>(has ? r_len[qc] : 1.f, valid, rp, e16, g, bq, hB, ds);
+    hidden_T<NB, NH>(has ? r_len[qc] : 1.f, valid, rp, w1a, g, bq, hB, ds);
 #pragma unroll
     for (int t = 0; t < S::YC; ++t) {
       yr[t] = has ? Y[(size_t)qc * S::YC + t] : 0.f;
@@ -515,6 +531,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e16 = lane & 15, g = lane >> 4;
   const int u = 16 * c + e16;
+  float w1a[NH / 16][NB / 4];
+  load_w1a<NB, NH>(rp, e16, g, w1a);
   stage_w2<S, U, NH, NW>(w2s, rp.W2, c, wv, lane);
   wait_vmcnt<0>();
   __syncthreads();
@@ -524,11 +542,26 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int o = 0; o < NA; ++o) acc[o] = 0.f;
     for (int t0 = beg; t0 < end; t0 += 16) {
+      // gathered operands of the lane's four edges, requested first so that
+      // they arrive while the hidden layer and the weights are computed
+      constexpr int NF = SEND ? S::OC : S::XC;
+      float fr[4][NF], yr[4][S::YC];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = t0 + 4 * g + r;
+        const int qc = q < end ? q : end - 1;       // weights of a padded edge are zero
+        const int e = SEND ? perm[qc] : qc;
+#pragma unroll
+        for (int b = 0; b < S::YC; ++b) yr[r][b] = Y[(size_t)e * S::YC + b];
+        if constexpr (SEND) load_o_channel<S, U>(feat, other[qc], u, fr[r]);
+        else load_x_channel<S, U>(feat, other[qc], u, fr[r]);
+      }
+      __builtin_amdgcn_sched_barrier(0);            // keep the loads ahead of the MFMAs
       const int qa = t0 + e16;
       const bool va = qa < end;
       const int qac = va ? qa : end - 1;
       float bq[NB / 4], hB[NH / 4], ds[NH / 4];
-      hidden_T<NB, NH>(r_len[SEND ? perm[qac] : qac], va, rp, e16, g, bq, hB, ds);
+      hidden_T<NB, NH>(r_len[SEND ? perm[qac] : qac], va, rp, w1a, g, bq, hB, ds);
       f32x4 C[S::NP];
 #pragma unroll
       for (int p = 0; p < S::NP; ++p) {
@@ -537,29 +570,13 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
         for (int k = 0; k < NH / 4; ++k) C[p] = mfma_16x16x4(hB[k], wb[hid_T(k, g) * L::WS], C[p]);
       }
-      // the lane's four edges; the operands of edge r+1 are requested before
-      // edge r is computed
-      constexpr int NF = SEND ? S::OC : S::XC;
-      float fr[2][NF], yr[2][S::YC];
-      auto fetch = [&](int r, float (&f)[NF], float (&y)[S::YC]) {
-        const int q = t0 + 4 * g + r;
-        const int qc = q < end ? q : end - 1;       // weights of a padded edge are zero
-        const int e = SEND ? perm[qc] : qc;
-#pragma unroll
-        for (int b = 0; b < S::YC; ++b) y[b] = Y[(size_t)e * S::YC + b];
-        if constexpr (SEND) load_o_channel<S, U>(feat, other[qc], u, f);
-        else load_x_channel<S, U>(feat, other[qc], u, f);
-      };
-      fetch(0, fr[0], yr[0]);
       static_for<4>([&](auto R) {
-        if constexpr (R < 3) fetch(R + 1, fr[(R + 1) & 1], yr[(R + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
         float wr[S::NP];
 #pragma unroll
         for (int p = 0; p < S::NP; ++p) wr[p] = C[p][int(R)];
-        if constexpr (SEND) edge_bwd_send<S>(yr[R & 1], wr, fr[R & 1], acc);
-        else edge_fwd<S>(fr[R & 1], yr[R & 1], wr, acc);
-        __builtin_amdgcn_sched_barrier(0);          // one edge's operands in flight at a time
+        if constexpr (SEND) edge_bwd_send<S>(yr[R], wr, fr[R], acc);
+        else edge_fwd<S>(fr[R], yr[R], wr, acc);
+        __builtin_amdgcn_sched_barrier(0);          // one edge's products live at a time
       });
     }
     reduce_quads<NA>(acc);
