@@ -189,7 +189,8 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
  * irreps, U = 16, 32, 64 or 128; 1e and 1o never mix):
  *   out[i, k, v, c] = sum_u Wmix[k][u][v] in[i, k, u, c]       (in, out: [N][outdim])
  * The post-aggregation channel mixing of the radial-weight layer ("Sobek",
- * Abstract, on preserving multiplicity mixing).  in and out must not alias. */
+ * Abstract, on preserving multiplicity mixing).  in and out must not alias
+ * and must be 16-byte aligned (whole node blocks move as 16-byte granules). */
 tp_status tp_conv_uvw_forward(tp_plan_t plan, int32_t n_nodes, const float* Wmix, const float* in,
                               float* out, hipStream_t stream);
 
