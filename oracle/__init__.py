@@ -31,17 +31,18 @@ brute-force loops).  No function here is "parity unpinned".
 """
 from .irreps import parse_irreps, build_plan, OraclePlan
 from .cg import cg_complex, real_basis_matrix, cg_real
-from .sh import sh_complex, sh_real
+from .sh import sh_complex, sh_real, sh_real_jacobian, sh_real_vjp
 from .wigner import wigner_D_real
 from .csr import csr_build
-from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, radial_mlp_fwd,
+from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, bessel_basis_deriv, radial_mlp_fwd,
                    radial_mlp_bwd, uvw_mix_fwd, uvw_mix_bwd,
                    tp_conv_radial_fwd, tp_conv_radial_bwd)
 
 __all__ = [
     "parse_irreps", "build_plan", "OraclePlan", "cg_complex",
-    "real_basis_matrix", "cg_real", "sh_complex", "sh_real", "wigner_D_real",
-    "csr_build", "tp_conv_fwd", "tp_conv_bwd", "bessel_basis",
+    "real_basis_matrix", "cg_real", "sh_complex", "sh_real", "sh_real_jacobian",
+    "sh_real_vjp", "wigner_D_real", "csr_build", "tp_conv_fwd", "tp_conv_bwd",
+    "bessel_basis", "bessel_basis_deriv",
     "radial_mlp_fwd", "radial_mlp_bwd", "uvw_mix_fwd", "uvw_mix_bwd",
     "tp_conv_radial_fwd", "tp_conv_radial_bwd",
 ]

@@ -125,6 +125,13 @@ def bessel_basis(r_len, n_basis, r_cut):
     return np.sqrt(2.0 / r_cut) * np.sin(n * np.pi * r / r_cut) / r
 
 
+def bessel_basis_deriv(r_len, n_basis, r_cut):
+    """dB_n/dr: sqrt(2/r_c) (k_n cos(k_n r) / r - sin(k_n r) / r^2), k_n = n pi / r_c."""
+    r = np.asarray(r_len, dtype=np.float64).reshape(-1, 1)
+    k = np.arange(1, n_basis + 1, dtype=np.float64).reshape(1, -1) * np.pi / r_cut
+    return np.sqrt(2.0 / r_cut) * (k * np.cos(k * r) / r - np.sin(k * r) / r ** 2)
+
+
 def _sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
@@ -138,8 +145,9 @@ def radial_mlp_fwd(r_len, W1, W2, n_basis, r_cut):
     return w, (B, pre, h)
 
 
-def radial_mlp_bwd(grad_w, cache, W2):
-    """(grad_W1, grad_W2) from grad_w [E, P*U]."""
+def radial_mlp_bwd(grad_w, cache, W2, W1=None):
+    """(grad_W1, grad_W2) from grad_w [E, P*U]; with W1 also grad_B [E, n_basis],
+    the gradient with respect to the basis values."""
     B, pre, h = cache
     grad_w = np.asarray(grad_w, dtype=np.float64)
     grad_W2 = h.T @ grad_w
@@ -147,7 +155,9 @@ def radial_mlp_bwd(grad_w, cache, W2):
     s = _sigmoid(pre)
     grad_pre = grad_h * (s * (1.0 + pre * (1.0 - s)))
     grad_W1 = B.T @ grad_pre
-    return grad_W1, grad_W2
+    if W1 is None:
+        return grad_W1, grad_W2
+    return grad_W1, grad_W2, grad_pre @ np.asarray(W1, dtype=np.float64).T
 
 
 # ---------------------------------------------------------------------------
@@ -205,8 +215,10 @@ def tp_conv_radial_fwd(plan, src, dst, n_nodes, x, Y, r_len, W1, W2, Wmix,
 
 
 def tp_conv_radial_bwd(plan, src, dst, n_nodes, x, Y, r_len, W1, W2, Wmix, g2,
-                       n_basis, r_cut):
-    """(grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix); grad_Wmix is None without a mix."""
+                       n_basis, r_cut, with_grad_rlen=False):
+    """(grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix); grad_Wmix is None without a mix.
+    with_grad_rlen: a sixth entry, the gradient with respect to the edge lengths
+    (through the radial basis), grad_rlen[e] = sum_n grad_B[e, n] dB_n/dr."""
     src, dst, x, Y = _check(plan, src, dst, n_nodes, x, Y)
     r_len = np.asarray(r_len, dtype=np.float64)
     g2 = np.asarray(g2, dtype=np.float64)
@@ -221,6 +233,7 @@ def tp_conv_radial_bwd(plan, src, dst, n_nodes, x, Y, r_len, W1, W2, Wmix, g2,
     grad_Y = np.zeros_like(Y)
     grad_W1 = np.zeros_like(np.asarray(W1, dtype=np.float64))
     grad_W2 = np.zeros_like(np.asarray(W2, dtype=np.float64))
+    grad_rlen = np.zeros(len(src))
     for s in range(0, len(src), CHUNK):
         e = slice(s, s + CHUNK)
         w, cache = radial_mlp_fwd(r_len[e], W1, W2, n_basis, r_cut)
@@ -228,7 +241,10 @@ def tp_conv_radial_bwd(plan, src, dst, n_nodes, x, Y, r_len, W1, W2, Wmix, g2,
         gx, gY, gw = _adjoint_chunk(plan, x[src[e]], Y[e], w, g[dst[e]])
         np.add.at(grad_x, src[e], gx)
         grad_Y[e] = gY
-        a, b = radial_mlp_bwd(gw.reshape(gw.shape[0], -1), cache, W2)
+        a, b, gB = radial_mlp_bwd(gw.reshape(gw.shape[0], -1), cache, W2, W1)
         grad_W1 += a
         grad_W2 += b
+        grad_rlen[e] = np.sum(gB * bessel_basis_deriv(r_len[e], n_basis, r_cut), axis=1)
+    if with_grad_rlen:
+        return grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix, grad_rlen
     return grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix

@@ -72,3 +72,73 @@ def sh_real(lmax, r):
             raise AssertionError("real harmonics came out complex")
         blocks.append(Z.real)
     return np.concatenate(blocks, axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Gradient with respect to the edge vector (forces flow through Y).
+#
+# R_lm(r) = |r|^l Y_lm(r_hat) is a homogeneous polynomial of degree l (a solid
+# harmonic).  Its monomial coefficients are obtained here by interpolating
+# sh_real at more points than there are monomials of degree l (an exact
+# interpolation of a polynomial of known degree, up to rounding); then
+#   dY/dr = grad R(r) / |r|^l - l R(r) r / |r|^(l+2),
+# which is zero along r, as it must be for a function of the direction only.
+# ---------------------------------------------------------------------------
+
+def _monomial_exponents(l):
+    return [(a, b, l - a - b) for a in range(l, -1, -1) for b in range(l - a, -1, -1)]
+
+
+def _monomials(exps, r):
+    x, y, z = r[:, 0:1], r[:, 1:2], r[:, 2:3]
+    return np.concatenate([x ** a * y ** b * z ** c for a, b, c in exps], axis=1)
+
+
+_SOLID = {}
+
+
+def solid_harmonic_coefficients(l):
+    """[2l+1, n_monomials] coefficients of R_lm in the monomials of degree l."""
+    if l not in _SOLID:
+        exps = _monomial_exponents(l)
+        rng = np.random.default_rng(12345)
+        u = rng.normal(size=(4 * len(exps) + 8, 3))
+        u /= np.linalg.norm(u, axis=1, keepdims=True)
+        Y = sh_real(l, u)[:, l * l:]                 # on the unit sphere R = Y
+        M = _monomials(exps, u)
+        C, *_ = np.linalg.lstsq(M, Y, rcond=None)
+        if np.max(np.abs(M @ C - Y)) > 1e-12:
+            raise AssertionError("solid harmonic is not a polynomial of degree l")
+        _SOLID[l] = (exps, C.T.copy())
+    return _SOLID[l]
+
+
+def sh_real_jacobian(lmax, r):
+    """dY/dr, shape [n, (lmax+1)^2, 3], for the harmonics of sh_real."""
+    r = np.asarray(r, dtype=np.float64).reshape(-1, 3)
+    nr = np.linalg.norm(r, axis=1)
+    if np.any(nr == 0.0):
+        raise ValueError("zero-length edge vector has no direction")
+    J = np.zeros((r.shape[0], (lmax + 1) ** 2, 3))
+    for l in range(1, lmax + 1):
+        exps, C = solid_harmonic_coefficients(l)
+        R = _monomials(exps, r) @ C.T                                  # [n, 2l+1]
+        grad = np.zeros((r.shape[0], 2 * l + 1, 3))
+        for axis in range(3):
+            dexps, scale = [], []
+            for e in exps:
+                k = e[axis]
+                d = list(e)
+                d[axis] = max(k - 1, 0)
+                dexps.append(tuple(d))
+                scale.append(float(k))
+            dm = _monomials(dexps, r) * np.array(scale)[None, :]
+            grad[:, :, axis] = dm @ C.T
+        s = nr[:, None, None]
+        J[:, l * l:(l + 1) ** 2, :] = grad / s ** l - l * R[:, :, None] * r[:, None, :] / s ** (l + 2)
+    return J
+
+
+def sh_real_vjp(lmax, r, grad_Y):
+    """grad_r[e] = sum_b grad_Y[e, b] dY_b/dr[e]."""
+    return np.einsum("nb,nbk->nk", np.asarray(grad_Y, dtype=np.float64), sh_real_jacobian(lmax, r))

@@ -302,3 +302,66 @@ def test_workload_shapes():
     plan, wl = _wl("tiny")
     assert np.all(np.linalg.norm(wl.r, axis=1) < 4.0)
     assert 300 < wl.n_edges < 800
+
+
+def test_bessel_basis_derivative_against_scipy():
+    r = np.linspace(0.8, 5.0, 50)
+    dB = oracle.bessel_basis_deriv(r, 8, 5.0)
+    for n in range(1, 9):
+        k = n * np.pi / 5.0
+        want = np.sqrt(2.0 / 5.0) * k * k * spherical_jn(0, k * r, derivative=True)
+        assert np.max(np.abs(dB[:, n - 1] - want)) <= 1e-13
+
+
+def _energy(fn, g):
+    return float(np.sum(np.asarray(g, dtype=np.float64) * fn()))
+
+
+def test_edge_vector_gradients_by_differences():
+    """Forces: d<g, out>/dr through the harmonics (direct weights) and through
+    the harmonics and the radial network (radial weights), by central
+    differences of the forward in r."""
+    rng = np.random.default_rng(9)
+    h = 1e-6
+    # direct weights: grad_r = J_Y^T grad_Y
+    plan, wl = _wl("tiny")
+    x = wl.x.astype(np.float64)
+    w = wl.w.astype(np.float64)
+    r = wl.r.astype(np.float64)
+    g = wl.g.astype(np.float64)
+    _, gY, _ = oracle.tp_conv_bwd(plan, wl.src, wl.dst, wl.n_nodes, x, oracle.sh_real(2, r), w, g)
+    grad_r = oracle.sh_real_vjp(2, r, gY)
+    for _ in range(3):
+        d = rng.normal(size=r.shape)
+        F = [_energy(lambda: oracle.tp_conv_fwd(plan, wl.src, wl.dst, wl.n_nodes, x,
+                                                oracle.sh_real(2, r + s * d), w), g) for s in (h, -h)]
+        an = float(np.sum(grad_r * d))
+        assert abs((F[0] - F[1]) / (2 * h) - an) <= 1e-6 * max(1.0, abs(an))
+    # radial weights with the mix: grad_r = J_Y^T grad_Y + grad_rlen r_hat
+    plan = oracle.build_plan("4x0e+4x1o+4x2e", 2, 2)
+    wl = make_workload("stream", dims_of(plan), seed=2, n_nodes=10)
+    x, r, g = wl.x.astype(np.float64), wl.r.astype(np.float64), wl.g.astype(np.float64)
+    kw = dict(n_basis=wl.n_basis, r_cut=wl.r_cut)
+    args = (plan, wl.src, wl.dst, wl.n_nodes)
+    rl = np.linalg.norm(r, axis=1)
+    out = oracle.tp_conv_radial_bwd(*args, x, oracle.sh_real(2, r), rl, wl.W1, wl.W2, wl.Wmix, g,
+                                    with_grad_rlen=True, **kw)
+    gY, grl = out[1], out[5]
+    grad_r = oracle.sh_real_vjp(2, r, gY) + grl[:, None] * r / rl[:, None]
+    for _ in range(3):
+        d = rng.normal(size=r.shape)
+        F = []
+        for s in (h, -h):
+            rs = r + s * d
+            F.append(_energy(lambda: oracle.tp_conv_radial_fwd(
+                *args, x, oracle.sh_real(2, rs), np.linalg.norm(rs, axis=1), wl.W1, wl.W2,
+                wl.Wmix, **kw), g))
+        an = float(np.sum(grad_r * d))
+        assert abs((F[0] - F[1]) / (2 * h) - an) <= 1e-6 * max(1.0, abs(an))
+    # the length gradient alone, by differences in r_len at fixed directions
+    Y = oracle.sh_real(2, r)
+    d = rng.normal(size=rl.shape)
+    F = [_energy(lambda: oracle.tp_conv_radial_fwd(*args, x, Y, rl + s * d, wl.W1, wl.W2, wl.Wmix,
+                                                   **kw), g) for s in (h, -h)]
+    an = float(np.sum(grl * d))
+    assert abs((F[0] - F[1]) / (2 * h) - an) <= 1e-6 * max(1.0, abs(an))

@@ -111,3 +111,33 @@ def test_wigner_D_matches_sympy_euler_route():
         Dr = U @ Dc.conj() @ U.conj().T
         assert np.max(np.abs(Dr.imag)) <= 1e-12
         assert np.max(np.abs(Dr.real - oracle.wigner_D_real(l, R))) <= 1e-12
+
+
+def test_sh_jacobian_against_differences_rotation_and_closed_form():
+    """dY/dr: central differences of sh_real, zero along r (a function of the
+    direction only), rotation covariance J(Rr) = D J(r) R^T, and the l = 1
+    closed form sqrt3 (P - (P u) u^T) / |r| with P the (y, z, x) permutation."""
+    rng = np.random.default_rng(8)
+    r = rng.normal(size=(40, 3)) * rng.uniform(0.5, 3.0, size=(40, 1))
+    J = oracle.sh_real_jacobian(3, r)
+    h = 1e-6
+    for k in range(3):
+        d = np.zeros(3)
+        d[k] = h
+        fd = (oracle.sh_real(3, r + d) - oracle.sh_real(3, r - d)) / (2 * h)
+        assert np.max(np.abs(J[:, :, k] - fd)) <= 1e-7
+    assert np.max(np.abs(np.einsum("nbk,nk->nb", J, r))) <= 1e-12
+    R = _haar(4)
+    JR = oracle.sh_real_jacobian(3, r @ R.T)
+    for l in range(4):
+        D = oracle.wigner_D_real(l, R)
+        s = slice(l * l, (l + 1) ** 2)
+        assert np.max(np.abs(JR[:, s, :] - np.einsum("ab,nbk,jk->naj", D, J[:, s, :], R))) <= 1e-11
+    P = np.array([[0, 1, 0], [0, 0, 1], [1, 0, 0]], dtype=float)
+    nr = np.linalg.norm(r, axis=1)
+    u = r / nr[:, None]
+    want = np.sqrt(3.0) * (P[None] - np.einsum("ab,nb,nk->nak", P, u, u)) / nr[:, None, None]
+    assert np.max(np.abs(J[:, 1:4, :] - want)) <= 1e-13
+    # vector-Jacobian product
+    gY = rng.normal(size=(40, 16))
+    assert np.max(np.abs(oracle.sh_real_vjp(3, r, gY) - np.einsum("nb,nbk->nk", gY, J))) <= 1e-13
