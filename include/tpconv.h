@@ -223,8 +223,11 @@ tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const fl
  * pass).  With Wmix, out_pre is the forward's unmixed output and grad_Wmix
  * [K][U][U] is produced; the gradient reaching the aggregation is
  * Wmix-applied grad_out.  Outputs (each may be NULL to skip it):
- *   grad_x [N][xdim], grad_Y [E][ysh] (receiver-sorted), grad_W1 and grad_W2
- *   (shapes of W1, W2), grad_Wmix.
+ *   grad_x [N][xdim], grad_Y [E][ysh] and grad_rlen [E] (receiver-sorted),
+ *   grad_W1 and grad_W2 (shapes of W1, W2), grad_Wmix.
+ * grad_rlen is the gradient with respect to the edge lengths through the
+ * radial basis: sum_n grad_B[e][n] dB_n/dr with grad_B = grad_pre W1^T; with
+ * grad_Y it gives the forces on the edge vectors (tp_conv_sph_harm_backward).
  * The per-edge weights, their gradients and the hidden activations are
  * recomputed on chip, never stored.  x, grad_out and W2 must be 16-byte
  * aligned (vector loads of four channels).  Parameter gradients are reduced in a fixed
@@ -234,11 +237,26 @@ tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const f
                                   const float* Y, const float* r_len, const float* W1,
                                   const float* W2, const float* Wmix, const float* out_pre,
                                   const float* grad_out, float* grad_x, float* grad_Y,
-                                  float* grad_W1, float* grad_W2, float* grad_Wmix, void* ws,
-                                  size_t ws_bytes, hipStream_t stream);
+                                  float* grad_rlen, float* grad_W1, float* grad_W2,
+                                  float* grad_Wmix, void* ws, size_t ws_bytes, hipStream_t stream);
 /* Workspace bytes of tp_conv_backward_radial for n_nodes nodes (with_mix != 0:
  * a channel mix is differentiated too). */
 tp_status tp_conv_radial_workspace(tp_plan_t plan, int32_t n_nodes, int32_t with_mix, size_t* bytes);
+
+/* Gradient with respect to the edge vectors r[E][3] of a loss that depends on
+ * them through Y = tp_conv_sph_harm(lmax, r) (upstream grad_Y[E][(lmax+1)^2])
+ * and, optionally, through the edge lengths |r| (upstream grad_rlen[E], NULL:
+ * none):  grad_r = sum_b grad_Y[b] dY_b/dr + grad_rlen r/|r|.  The forces on
+ * atoms follow by summing -grad_r into the sender and +grad_r into the
+ * receiver of each edge (r = pos[src] - pos[dst]).  Forces are what a force
+ * field predicts ("The GPU Workload That Rewrites Molecular Physics", opening
+ * sections), obtained by differentiating through the layer and the harmonics
+ * of the edge direction ("Sobek", Abstract: the schedule extends through the
+ * backward pass).  lmax <= 3; all arrays device float32, edge order as given;
+ * grad_r is overwritten. */
+tp_status tp_conv_sph_harm_backward(int32_t lmax, const float* r, int32_t n_edges,
+                                    const float* grad_Y, const float* grad_rlen, float* grad_r,
+                                    hipStream_t stream);
 
 /* Thread-local description of the last failure on this thread. */
 const char* tp_conv_last_error(void);

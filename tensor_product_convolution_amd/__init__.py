@@ -28,7 +28,7 @@ EXPORTS = (
     "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
-    "tp_conv_last_error",
+    "tp_conv_sph_harm_backward", "tp_conv_last_error",
 )
 
 
@@ -85,7 +85,8 @@ def lib():
         "tp_conv_forward_radial": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
                                          VP]),
         "tp_conv_backward_radial": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP,
-                                          VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
+                                          VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
+        "tp_conv_sph_harm_backward": (I32, [I32, VP, I32, VP, VP, VP, VP]),
         "tp_conv_radial_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_last_error": (ctypes.c_char_p, []),
     }
@@ -254,6 +255,21 @@ def sph_harm(lmax, r, out=None):
     return out
 
 
+def sph_harm_backward(lmax, r, grad_Y, grad_rlen=None, out=None):
+    """grad_r [E, 3] = grad_Y . dY/dr (+ grad_rlen * r/|r|) for Y = sph_harm(lmax, r)."""
+    torch = _torch()
+    _need(r, "r", torch.float32)
+    E = r.shape[0]
+    _need(grad_Y, "grad_Y", torch.float32, (E, (lmax + 1) ** 2))
+    if grad_rlen is not None:
+        _need(grad_rlen, "grad_rlen", torch.float32, (E,))
+    if out is None:
+        out = torch.empty((E, 3), dtype=torch.float32, device=r.device)
+    _check(lib().tp_conv_sph_harm_backward(lmax, _ptr(r), E, _ptr(grad_Y), _ptr(grad_rlen), _ptr(out),
+                                           _stream(r.device)))
+    return out
+
+
 def forward(plan, graph, x, Y, w, out=None):
     """out [N, outdim] of the convolution (edge arrays in receiver-sorted order)."""
     torch = _torch()
@@ -353,10 +369,11 @@ def forward_radial(plan, graph, x, Y, r_len, W1, W2, Wmix=None, out=None, out_pr
 
 def backward_radial(plan, graph, x, Y, r_len, W1, W2, grad_out, Wmix=None, out_pre=None,
                     want=("x", "Y", "W1", "W2", "Wmix"), outs=None, ws=None):
-    """(grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix) of the radial-weight convolution
-    (grad_Y receiver-sorted); entries not in ``want`` (and grad_Wmix without a mix)
-    are None.  ``outs`` (a dict name -> tensor) and ``ws`` (uint8, at least
-    radial_workspace bytes) supply preallocated buffers."""
+    """(grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix, grad_rlen) of the radial-weight
+    convolution (grad_Y, grad_rlen receiver-sorted); entries not in ``want`` (names
+    x, Y, W1, W2, Wmix, rlen) and grad_Wmix without a mix are None.  ``outs`` (a
+    dict name -> tensor) and ``ws`` (uint8, at least radial_workspace bytes)
+    supply preallocated buffers."""
     torch = _torch()
     N, E = graph.n_nodes, graph.n_edges
     nb, nh, _ = plan.radial
@@ -383,6 +400,7 @@ def backward_radial(plan, graph, x, Y, r_len, W1, W2, grad_out, Wmix=None, out_p
         return t
     gx, gY, gW1, gW2 = buf("x", x), buf("Y", Y), buf("W1", W1), buf("W2", W2)
     gWm = buf("Wmix", Wmix)
+    grl = buf("rlen", r_len)
     nbytes = radial_workspace(plan, N, Wmix is not None)
     if ws is None:
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
@@ -392,9 +410,9 @@ def backward_radial(plan, graph, x, Y, r_len, W1, W2, grad_out, Wmix=None, out_p
     _check(lib().tp_conv_backward_radial(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(r_len),
                                          _ptr(W1), _ptr(W2), _ptr(Wmix),
                                          _ptr(out_pre) if gWm is not None else None, _ptr(grad_out),
-                                         _ptr(gx), _ptr(gY), _ptr(gW1), _ptr(gW2), _ptr(gWm),
-                                         _ptr(ws), ws.numel(), _stream(x.device)))
-    return gx, gY, gW1, gW2, gWm
+                                         _ptr(gx), _ptr(gY), _ptr(grl), _ptr(gW1), _ptr(gW2),
+                                         _ptr(gWm), _ptr(ws), ws.numel(), _stream(x.device)))
+    return gx, gY, gW1, gW2, gWm, grl
 
 
 def radial_workspace(plan, n_nodes, with_mix):

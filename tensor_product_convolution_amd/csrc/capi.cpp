@@ -311,6 +311,14 @@ tp_status tp_conv_gather_rows(const void* in, const int32_t* perm, int64_t n_row
   return tpc::gather_rows(in, perm, n_rows, row_words, out, stream);
 }
 
+tp_status tp_conv_sph_harm_backward(int32_t lmax, const float* r, int32_t n_edges, const float* grad_Y,
+                                    const float* grad_rlen, float* grad_r, hipStream_t stream) {
+  if (n_edges < 0) return set_error(TP_ERR_ARG, "tp_conv_sph_harm_backward: negative size");
+  if (n_edges > 0 && (!r || !grad_Y || !grad_r))
+    return set_error(TP_ERR_ARG, "tp_conv_sph_harm_backward: NULL pointer");
+  return tpc::sph_harm_bwd(lmax, r, n_edges, grad_Y, grad_rlen, grad_r, stream);
+}
+
 tp_status tp_conv_sph_harm(int32_t lmax, const float* r, int32_t n_edges, float* Y,
                            hipStream_t stream) {
   if (n_edges < 0) return set_error(TP_ERR_ARG, "tp_conv_sph_harm: negative size");
@@ -494,8 +502,8 @@ tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const f
                                   const float* Y, const float* r_len, const float* W1,
                                   const float* W2, const float* Wmix, const float* out_pre,
                                   const float* grad_out, float* grad_x, float* grad_Y,
-                                  float* grad_W1, float* grad_W2, float* grad_Wmix, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+                                  float* grad_rlen, float* grad_W1, float* grad_W2,
+                                  float* grad_Wmix, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: plan is NULL");
   if (!plan->rs || !plan->rs->bwd) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
   tp_status s = check_graph(graph, grad_x != nullptr);
@@ -546,6 +554,7 @@ tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const f
   a.grad_out = g;
   a.grad_x = grad_x;
   a.grad_Y = grad_Y;
+  a.grad_rlen = grad_rlen;
   a.grad_W1 = grad_W1;
   a.grad_W2 = grad_W2;
   a.r_cut = plan->opts.r_cut;

@@ -40,6 +40,7 @@ struct RadialArgs {
   const float *x = nullptr, *Y = nullptr, *r_len = nullptr, *W1 = nullptr, *W2 = nullptr;
   const float* grad_out = nullptr;   // gradient w.r.t. the unmixed output
   float *out = nullptr, *grad_x = nullptr, *grad_Y = nullptr, *grad_W1 = nullptr, *grad_W2 = nullptr;
+  float* grad_rlen = nullptr;        // gradient w.r.t. the edge lengths (through the basis)
   float r_cut = 0.f;
   void* ws = nullptr;
   hipStream_t stream = nullptr;
@@ -47,7 +48,7 @@ struct RadialArgs {
 using RadialFn = hipError_t (*)(const RadialArgs&);
 struct RadialSet {
   RadialFn fwd = nullptr;
-  RadialFn bwd = nullptr;                        // grad_x, grad_Y, grad_W1, grad_W2
+  RadialFn bwd = nullptr;                        // grad_x, grad_Y, grad_rlen, grad_W1, grad_W2
   size_t (*bwd_workspace)(int n_nodes, int n_edges) = nullptr;
 };
 const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul, int nb,
@@ -79,6 +80,8 @@ tp_status graph_build(const int32_t* src, const int32_t* dst, int n_edges, int n
 tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64_t words, void* out,
                       hipStream_t st);
 tp_status sph_harm(int lmax, const float* r, int n, float* Y, hipStream_t st);
+tp_status sph_harm_bwd(int lmax, const float* r, int n, const float* gY, const float* grl, float* gr,
+                       hipStream_t st);
 size_t uvw_workspace_bytes(int n_irreps, int U);
 tp_status uvw_forward(int n_nodes, int U, int outdim, const UvwIrreps& irr, const float* W,
                       const float* X, float* Z, bool trans_w, hipStream_t st);

@@ -214,8 +214,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     k_radial_bwd_recv(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                       const float* __restrict__ x, const float* __restrict__ Y,
                       const float* __restrict__ r_len, RadialParams rp, const float* __restrict__ gout,
-                      float* __restrict__ grad_Y, float* __restrict__ part) {
-  static_assert(U % 16 == 0 && NH % 16 == 0 && NH <= 64, "radial tiling");
+                      float* __restrict__ grad_Y, float* __restrict__ grad_rlen, float* __restrict__ part) {
+  static_assert(U % 16 == 0 && NH % 16 == 0 && NH <= 64 && NB <= 16, "radial tiling");
   using L = W2Slice<S, NH>;
   constexpr int GF = 16 * S::OC;                    // staged grad_out floats per wave
   constexpr int RED = 16 * (NH + 1) + 16 * NB;      // grad_W1 scratch floats per wave
@@ -250,7 +250,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     const int qc = has ? (q < end ? q : end - 1) : 0;
     const int j = has ? col[qc] : 0;
     float bq[NB / 4], hB[NH / 4], ds[NH / 4], yr[S::YC], gy[S::YC];
-    hidden_T<NB, NH>(has ? r_len[qc] : 1.f, valid, rp, w1a, g, bq, hB, ds);
+    const float rl = has ? r_len[qc] : 1.f;
+    hidden_T<NB, NH>(rl, valid, rp, w1a, g, bq, hB, ds);
 #pragma unroll
     for (int t = 0; t < S::YC; ++t) {
       yr[t] = has ? Y[(size_t)qc * S::YC + t] : 0.f;
@@ -335,13 +336,39 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
       for (int t = 0; t < S::YC; ++t) grad_Y[(size_t)q * S::YC + t] = gy[t];
     }
+    // grad_pre (zero for an invalid edge) in the K-slot order of the hidden values
+    float gp[NH / 4];
+#pragma unroll
+    for (int k = 0; k < NH / 4; ++k) gp[k] = gh[k >> 2][k & 3] * ds[k];
+    if (grad_rlen && has) {
+      // grad_B[n][edge] = sum_h W1[n][h] grad_pre[h][edge] on the MFMA (rows
+      // n >= NB zero); lane l gets n = 4(l/16) + i of edge l%16, then
+      // grad_rlen = sum_n grad_B[n] dB_n/dr, summed over the lane groups
+      f32x4 gbn = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NH / 4; ++k)
+        gbn = mfma_16x16x4(e16 < NB ? rp.W1[e16 * NH + hid_T(k, g)] : 0.f, gp[k], gbn);
+      const float pre_b = sqrtf(2.0f / rp.r_cut), kk = 3.14159265358979323846f / rp.r_cut;
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 4 * g + i;
+        if (n < NB) {
+          const float kn = (float)(n + 1) * kk;
+          acc += gbn[i] * pre_b * (kn * cosf(kn * rl) / rl - sinf(kn * rl) / (rl * rl));
+        }
+      }
+      acc += __shfl_xor(acc, 16, 64);
+      acc += __shfl_xor(acc, 32, 64);
+      if (g == 0 && valid) grad_rlen[q] = acc;
+    }
     // grad_W1[n][hid] += sum over the tile's edges of B_n * grad_pre[hid]
     __syncthreads();                                // W2 slice no longer read
     if (has) {
       float* s_gp = red;
       float* s_b = red + 16 * (NH + 1);
 #pragma unroll
-      for (int k = 0; k < NH / 4; ++k) s_gp[e16 * (NH + 1) + hid_T(k, g)] = gh[k >> 2][k & 3] * ds[k];
+      for (int k = 0; k < NH / 4; ++k) s_gp[e16 * (NH + 1) + hid_T(k, g)] = gp[k];
 #pragma unroll
       for (int t = 0; t < NB / 4; ++t) s_b[e16 * NB + 4 * t + g] = bq[t];
       __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): own LDS writes done (one wave)

@@ -69,10 +69,10 @@ static hipError_t launch_radial_bwd(const RadialArgs& a) {
   float* part1 = static_cast<float*>(a.ws);
   float* part2 = reinterpret_cast<float*>(static_cast<char*>(a.ws) +
                                           align256((size_t)nb1 * kNB * kNH * sizeof(float)));
-  if (a.grad_Y || a.grad_W1) {
+  if (a.grad_Y || a.grad_W1 || a.grad_rlen) {
     hipLaunchKernelGGL((k_radial_bwd_recv<SigR, U, kNB, kNH, kRecvWaves>), dim3(recv_blocks(a.n_nodes)),
                        dim3(64 * kRecvWaves), 0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len,
-                       rp, a.grad_out, a.grad_Y, part1);
+                       rp, a.grad_out, a.grad_Y, a.grad_rlen, part1);
     if (a.grad_W1) {
       const long long n = (long long)kNB * kNH;
       hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream, part1,

@@ -57,7 +57,87 @@ __global__ void __launch_bounds__(256)
   for (int t = 0; t < YC; ++t) Y[(size_t)e * YC + t] = v[t];
 }
 
+// Gradient with respect to the edge vector.  On the unit sphere each Y_lm is a
+// homogeneous polynomial P_lm of degree l (the forms above with 1 replaced by
+// x^2 + y^2 + z^2), and for Y(r) = P(r / |r|)
+//   dY/dr = (grad P(u) - l P(u) u) / |r|,   u = r / |r|
+// (Euler's identity u . grad P = l P makes it orthogonal to u).  grad_r =
+// sum_b grad_Y[b] dY_b/dr, plus grad_rlen * u when the edge length also feeds
+// the layer (radial weights).
+template <int LMAX>
+__global__ void __launch_bounds__(256)
+    k_sph_harm_bwd(const float* __restrict__ r, int n, const float* __restrict__ gY,
+                   const float* __restrict__ grl, float* __restrict__ gr) {
+  constexpr int YC = (LMAX + 1) * (LMAX + 1);
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float x = r[3 * (size_t)e], y = r[3 * (size_t)e + 1], z = r[3 * (size_t)e + 2];
+  const float n2 = x * x + y * y + z * z;
+  const float inv = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.f;
+  x *= inv;
+  y *= inv;
+  z *= inv;
+  float g[YC];
+#pragma unroll
+  for (int t = 0; t < YC; ++t) g[t] = gY[(size_t)e * YC + t];
+  float gx = 0.f, gy = 0.f, gz = 0.f, lp = 0.f;   // sum g grad P, sum g l P
+  if constexpr (LMAX >= 1) {
+    const float s3 = 1.7320508075688772f;
+    gx += s3 * g[3];
+    gy += s3 * g[1];
+    gz += s3 * g[2];
+    lp += s3 * (g[1] * y + g[2] * z + g[3] * x);
+  }
+  if constexpr (LMAX >= 2) {
+    const float s15 = 3.8729833462074170f, s5h = 1.1180339887498949f;
+    const float P4 = s15 * x * y, P5 = s15 * y * z, P6 = s5h * (2.f * z * z - x * x - y * y);
+    const float P7 = s15 * x * z, P8 = 0.5f * s15 * (x * x - y * y);
+    gx += g[4] * s15 * y + g[6] * (-2.f * s5h * x) + g[7] * s15 * z + g[8] * s15 * x;
+    gy += g[4] * s15 * x + g[5] * s15 * z + g[6] * (-2.f * s5h * y) + g[8] * (-s15 * y);
+    gz += g[5] * s15 * y + g[6] * (4.f * s5h * z) + g[7] * s15 * x;
+    lp += 2.f * (g[4] * P4 + g[5] * P5 + g[6] * P6 + g[7] * P7 + g[8] * P8);
+  }
+  if constexpr (LMAX >= 3) {
+    const float c70 = 2.0916500663351889f, c105 = 10.246950765959598f;
+    const float c42 = 1.6201851746019651f, c7 = 1.3228756555322954f;
+    const float xx = x * x, yy = y * y, zz = z * z;
+    const float P9 = c70 * y * (3.f * xx - yy), P10 = c105 * x * y * z;
+    const float P11 = c42 * y * (4.f * zz - xx - yy), P12 = c7 * z * (2.f * zz - 3.f * xx - 3.f * yy);
+    const float P13 = c42 * x * (4.f * zz - xx - yy), P14 = 0.5f * c105 * z * (xx - yy);
+    const float P15 = c70 * x * (xx - 3.f * yy);
+    gx += g[9] * c70 * 6.f * x * y + g[10] * c105 * y * z + g[11] * c42 * (-2.f * x * y) +
+          g[12] * c7 * (-6.f * x * z) + g[13] * c42 * (4.f * zz - 3.f * xx - yy) +
+          g[14] * c105 * x * z + g[15] * c70 * (3.f * xx - 3.f * yy);
+    gy += g[9] * c70 * (3.f * xx - 3.f * yy) + g[10] * c105 * x * z +
+          g[11] * c42 * (4.f * zz - xx - 3.f * yy) + g[12] * c7 * (-6.f * y * z) +
+          g[13] * c42 * (-2.f * x * y) + g[14] * (-c105 * y * z) + g[15] * c70 * (-6.f * x * y);
+    gz += g[10] * c105 * x * y + g[11] * c42 * 8.f * y * z + g[12] * c7 * (6.f * zz - 3.f * xx - 3.f * yy) +
+          g[13] * c42 * 8.f * x * z + g[14] * 0.5f * c105 * (xx - yy);
+    lp += 3.f * (g[9] * P9 + g[10] * P10 + g[11] * P11 + g[12] * P12 + g[13] * P13 + g[14] * P14 +
+                 g[15] * P15);
+  }
+  const float gl = grl ? grl[e] : 0.f;
+  gr[3 * (size_t)e + 0] = (gx - lp * x) * inv + gl * x;
+  gr[3 * (size_t)e + 1] = (gy - lp * y) * inv + gl * y;
+  gr[3 * (size_t)e + 2] = (gz - lp * z) * inv + gl * z;
+}
+
 }  // namespace
+
+tp_status sph_harm_bwd(int lmax, const float* r, int n, const float* gY, const float* grl, float* gr,
+                       hipStream_t st) {
+  if (n == 0) return TP_OK;
+  const dim3 grid((n + 255) / 256), block(256);
+  switch (lmax) {
+    case 0: hipLaunchKernelGGL(k_sph_harm_bwd<0>, grid, block, 0, st, r, n, gY, grl, gr); break;
+    case 1: hipLaunchKernelGGL(k_sph_harm_bwd<1>, grid, block, 0, st, r, n, gY, grl, gr); break;
+    case 2: hipLaunchKernelGGL(k_sph_harm_bwd<2>, grid, block, 0, st, r, n, gY, grl, gr); break;
+    case 3: hipLaunchKernelGGL(k_sph_harm_bwd<3>, grid, block, 0, st, r, n, gY, grl, gr); break;
+    default: return set_error(TP_ERR_UNSUPPORTED, "tp_conv_sph_harm_backward: lmax must be 0..3");
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TP_OK : hip_error(e, "sph_harm_bwd launch");
+}
 
 tp_status sph_harm(int lmax, const float* r, int n, float* Y, hipStream_t st) {
   if (n == 0) return TP_OK;

@@ -82,7 +82,9 @@ def run_gpu(tpc, plan, wl, bwd=True, w=None):
     res = dict(graph=g, out=out)
     if bwd:
         gx, gY, gw = tpc.backward(plan, g, x, Y, wv, T(wl.g))
-        res.update(gx=gx, gY=gY, gw=gw)
+        # forces on the receiver-sorted edge vectors through the harmonics
+        gr = tpc.sph_harm_backward(plan.lmax_sh, tpc.gather_rows(T(wl.r), g.perm), gY)
+        res.update(gx=gx, gY=gY, gw=gw, gr=gr)
     torch.cuda.synchronize()
     res = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in res.items()}
     res["perm"] = g.perm.cpu().numpy()[:wl.n_edges]
@@ -189,6 +191,8 @@ def test_conv_parity(tpc, name, n_nodes, mul, bwd):
         assert block_err(res["gx"], gx, in_blocks(op)) <= TOL
         assert block_err(res["gY"], gY[p], y_blocks(op)) <= TOL
         assert w_err(res["gw"], gw[p]) <= TOL
+        gr = oracle.sh_real_vjp(op.lmax_sh, wl.r.astype(np.float64), gY)[p]
+        assert np.max(np.abs(res["gr"] - gr)) <= TOL * np.max(np.abs(gr))
 
 
 # ---------------------------------------------------------------------------

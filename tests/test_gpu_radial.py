@@ -101,12 +101,25 @@ def _gpu_radial(tpc, plan, wl, mix, g2):
     Wm = T(wl.Wmix) if mix else None
     out, pre = tpc.forward_radial(plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), Wm)
     grads = tpc.backward_radial(plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), T(g2), Wmix=Wm,
-                                out_pre=pre)
+                                out_pre=pre, want=("x", "Y", "W1", "W2", "Wmix", "rlen"))
+    # forces on the (receiver-sorted) edge vectors through Y and the lengths
+    rs = tpc.gather_rows(T(wl.r), g.perm)
+    gr = tpc.sph_harm_backward(2, rs, grads[1], grads[5])
     torch.cuda.synchronize()
     cpu = lambda t: None if t is None else t.cpu().numpy()
     return dict(perm=cpu(g.perm)[:wl.n_edges], out=cpu(out), pre=cpu(pre),
                 gx=cpu(grads[0]), gY=cpu(grads[1]), gW1=cpu(grads[2]), gW2=cpu(grads[3]),
-                gWm=cpu(grads[4]))
+                gWm=cpu(grads[4]), grl=cpu(grads[5]), gr=cpu(gr))
+
+
+def _forces_ref(r, gY, grl):
+    """oracle forces on edge vectors: J_Y^T grad_Y + grad_rlen r_hat"""
+    r = r.astype(np.float64)
+    return oracle.sh_real_vjp(2, r, gY) + grl[:, None] * r / np.linalg.norm(r, axis=1)[:, None]
+
+
+def _vec_err(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
 def _param_err(got, ref):
@@ -114,7 +127,7 @@ def _param_err(got, ref):
 
 
 def _check_params(op, res, ref, U):
-    _, _, gW1, gW2, gWm = ref
+    gW1, gW2, gWm = ref[2], ref[3], ref[4]
     assert _param_err(res["gW1"], gW1) <= TOL
     # grad_W2 per path block
     P = op.n_paths
@@ -137,9 +150,12 @@ def test_radial_backward_parity(tpc, U, name, n, mix):
     Yo = oracle.sh_real(2, wl.r)
     Wm = wl.Wmix if mix else None
     ref = oracle.tp_conv_radial_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Yo, wl.r_len, wl.W1, wl.W2,
-                                    Wm, wl.g, 8, RC)
+                                    Wm, wl.g, 8, RC, with_grad_rlen=True)
+    p = res["perm"]
     assert block_err(res["gx"], ref[0], in_blocks(op)) <= TOL
-    assert block_err(res["gY"], ref[1][res["perm"]], y_blocks(op)) <= TOL
+    assert block_err(res["gY"], ref[1][p], y_blocks(op)) <= TOL
+    assert _vec_err(res["grl"], ref[5][p]) <= TOL
+    assert _vec_err(res["gr"], _forces_ref(wl.r, ref[1], ref[5])[p]) <= TOL
     _check_params(op, res, ref, U)
     if not mix:
         assert res["gWm"] is None
@@ -182,14 +198,36 @@ def test_radial_full_size_sampled(tpc):
     assert block_err(res["out"][recv], ref_out[rpos], out_blocks(op)) <= TOL
     # backward on the subgraph: the upstream gradient is zero off the sampled receivers
     ref = oracle.tp_conv_radial_bwd(op, src, dst, n, wl.x[nodes], Yo, rl, wl.W1, wl.W2, wl.Wmix,
-                                    g2[nodes], 8, RC)
+                                    g2[nodes], 8, RC, with_grad_rlen=True)
     assert block_err(res["gx"][nodes], ref[0], in_blocks(op)) <= TOL
     others = np.setdiff1d(rng.choice(N, size=200, replace=False), nodes)
     assert np.all(res["gx"][others] == 0)
     inv = np.empty(wl.n_edges, np.int64)
     inv[res["perm"]] = np.arange(wl.n_edges)
     assert block_err(res["gY"][inv[e]], ref[1], y_blocks(op)) <= TOL
+    assert _vec_err(res["grl"][inv[e]], ref[5]) <= TOL
+    assert _vec_err(res["gr"][inv[e]], _forces_ref(wl.r[e], ref[1], ref[5])) <= TOL
     mask = np.ones(wl.n_edges, bool)
     mask[inv[e]] = False
     assert np.all(res["gY"][mask][:100000] == 0)
     _check_params(op, res, ref, U)
+
+
+@pytest.mark.parametrize("lmax", [0, 1, 2, 3])
+def test_sph_harm_backward_parity(tpc, lmax):
+    say(f"sph_harm_backward lmax={lmax}")
+    rng = np.random.default_rng(40 + lmax)
+    E = 3001
+    r = (rng.normal(size=(E, 3)) * rng.uniform(0.5, 5.0, size=(E, 1))).astype(np.float32)
+    gY = rng.normal(size=(E, (lmax + 1) ** 2)).astype(np.float32)
+    grl = rng.normal(size=E).astype(np.float32)
+    got = tpc.sph_harm_backward(lmax, T(r), T(gY)).cpu().numpy()
+    ref = oracle.sh_real_vjp(lmax, r.astype(np.float64), gY) if lmax > 0 else np.zeros((E, 3))
+    if lmax > 0:
+        assert _vec_err(got, ref) <= TOL
+    else:
+        assert np.all(got == 0)
+    got2 = tpc.sph_harm_backward(lmax, T(r), T(gY), T(grl)).cpu().numpy()
+    r64 = r.astype(np.float64)
+    ref2 = ref + grl[:, None] * r64 / np.linalg.norm(r64, axis=1)[:, None]
+    assert _vec_err(got2, ref2) <= TOL
