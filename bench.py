@@ -243,6 +243,9 @@ def main():
         "bwd_recv": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw)),
         "bwd_send": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None)),
     }
+    r_sorted = tpc.gather_rows(T(wl.r), g.perm)
+    grad_r = torch.empty_like(r_sorted)
+    extras = {"forces": lambda: tpc.sph_harm_backward(lsh, r_sorted, gY, out=grad_r)}
 
     flush.fill_(1.0)
     # graph grouping, timed separately
@@ -265,6 +268,7 @@ def main():
     warm = timed_steps(args.steps, False) if args.warm else None
     reps, rounds = 10, max(2, args.steps // 5)
     kt_all = {n: timed_kernel(fn, reps, rounds) for n, fn in kernels.items()}
+    extra_ms = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in extras.items()}
 
     names = ["fwd", "bwd_recv", "bwd_send"]
     kt = np.array([kt_all[n].mean() for n in names])     # ms per launch
@@ -297,6 +301,9 @@ def main():
         "kernel_ms": {n: float(v) for n, v in zip(names, kt)},
         "kernel_ms_note": f"per launch, {reps} back-to-back launches after a cache flush, mean of {rounds}",
         "kernel_hbm_frac": {n: ab[n] / (float(v) * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in zip(names, kt)},
+        "forces_ms": extra_ms["forces"],
+        "forces_note": "edge-vector gradient from grad_Y (tp_conv_sph_harm_backward), per launch; "
+                       "not part of the step",
         "step_hbm_frac": ab["step"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "warm_edges_per_s": None if warm is None else E / (float(warm.mean()) * 1e-3),
         "graph_build_ms": float(np.median(gb)),
@@ -379,6 +386,18 @@ def bench_radial(args, torch, tpc, make_workload, dev):
         "fwd_with_mix": lambda: tpc.forward_radial(plan, g, x, Y, rl, W1, W2, Wm, out=out,
                                                    out_pre=pre),
     }
+    r_sorted = tpc.gather_rows(T(wl.r), g.perm)
+    grl = torch.empty_like(rl)
+    grad_r = torch.empty_like(r_sorted)
+    outs_f = dict(outs, rlen=grl)
+    extras = {
+        # receiver pass that also returns the edge-length gradient, then the
+        # edge-vector gradient
+        "bwd_recv_with_rlen": lambda: tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go,
+                                                          want=("Y", "W1", "rlen"), outs=outs_f,
+                                                          ws=ws),
+        "forces": lambda: tpc.sph_harm_backward(lsh, r_sorted, outs["Y"], grl, out=grad_r),
+    }
     flush.fill_(1.0)
     timed_steps(step, args.warmup, True)
     torch.cuda.synchronize()
@@ -388,6 +407,7 @@ def bench_radial(args, torch, tpc, make_workload, dev):
     wall = time.perf_counter() - t_wall0
     reps, rounds = 3, 2
     kt = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in kernels.items()}
+    extra_ms = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in extras.items()}
     fl = radial_flops(E, P, U, NH)
     names = ["fwd", "bwd_recv", "bwd_w2", "bwd_send"]
     dom = max(names, key=lambda n: kt[n])
@@ -419,6 +439,9 @@ def bench_radial(args, torch, tpc, make_workload, dev):
                           f"{rounds}; bwd_recv and bwd_w2 include their partial-sum kernels",
         "kernel_mfma_frac": {n: fl[n] / (kt[n] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS
                              for n in names},
+        "forces_ms": extra_ms,
+        "forces_note": "receiver pass that also returns the edge-length gradient, and the "
+                       "edge-vector gradient kernel; not part of the step",
         "wall_s_timed_region": wall,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
