@@ -229,8 +229,7 @@ def main():
 
     def step():
         tpc.forward(plan, g, x, Y, w, out=out)
-        tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw))
-        tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None))
+        tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))   # receiver, then sender pass
 
     if args.counters:
         counters_run(torch, dev, flush, step, args.config)
@@ -243,6 +242,7 @@ def main():
         "bwd_recv": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw)),
         "bwd_send": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None)),
     }
+    bwd_both = lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))
     r_sorted = tpc.gather_rows(T(wl.r), g.perm)
     grad_r = torch.empty_like(r_sorted)
     extras = {"forces": lambda: tpc.sph_harm_backward(lsh, r_sorted, gY, out=grad_r)}
@@ -269,6 +269,7 @@ def main():
     reps, rounds = 10, max(2, args.steps // 5)
     kt_all = {n: timed_kernel(fn, reps, rounds) for n, fn in kernels.items()}
     extra_ms = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in extras.items()}
+    bwd_ms = float(timed_kernel(bwd_both, reps, rounds).mean())
 
     names = ["fwd", "bwd_recv", "bwd_send"]
     kt = np.array([kt_all[n].mean() for n in names])     # ms per launch
@@ -301,6 +302,8 @@ def main():
         "kernel_ms": {n: float(v) for n, v in zip(names, kt)},
         "kernel_ms_note": f"per launch, {reps} back-to-back launches after a cache flush, mean of {rounds}",
         "kernel_hbm_frac": {n: ab[n] / (float(v) * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in zip(names, kt)},
+        "bwd_ms": bwd_ms,
+        "bwd_note": "one backward call (receiver then sender pass), per call",
         "forces_ms": extra_ms["forces"],
         "forces_note": "edge-vector gradient from grad_Y (tp_conv_sph_harm_backward), per launch; "
                        "not part of the step",
