@@ -36,7 +36,7 @@ from .wigner import wigner_D_real
 from .csr import csr_build
 from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, bessel_basis_deriv, radial_mlp_fwd,
                    radial_mlp_bwd, uvw_mix_fwd, uvw_mix_bwd,
-                   tp_conv_radial_fwd, tp_conv_radial_bwd)
+                   tp_conv_radial_fwd, tp_conv_radial_bwd, tp_conv_double_bwd)
 
 __all__ = [
     "parse_irreps", "build_plan", "OraclePlan", "cg_complex",
@@ -44,5 +44,5 @@ __all__ = [
     "sh_real_vjp", "wigner_D_real", "csr_build", "tp_conv_fwd", "tp_conv_bwd",
     "bessel_basis", "bessel_basis_deriv",
     "radial_mlp_fwd", "radial_mlp_bwd", "uvw_mix_fwd", "uvw_mix_bwd",
-    "tp_conv_radial_fwd", "tp_conv_radial_bwd",
+    "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd",
 ]

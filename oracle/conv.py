@@ -109,6 +109,36 @@ def tp_conv_bwd(plan, src, dst, n_nodes, x, Y, w, g):
     return grad_x, grad_Y, grad_w
 
 
+def tp_conv_double_bwd(plan, src, dst, n_nodes, x, Y, w, g, ggx=None, ggY=None, ggw=None):
+    """Second-order backward ("Sobek", Abstract: forward, backward and double
+    backward).  With F(g, x, Y, w) = <g, out(x, Y, w)> (linear in each
+    argument) the first backward returns (gx, gY, gw) = grad F; given
+    cotangents (ggx, ggY, ggw) of those (None: zero), the loss
+    L = <ggx, gx> + <ggY, gY> + <ggw, gw> equals
+        F(g, ggx, Y, w) + F(g, x, ggY, w) + F(g, x, Y, ggw),
+    so its gradients are
+        dg = out(ggx, Y, w) + out(x, ggY, w) + out(x, Y, ggw)
+        dx = gx(ggY, w, g) + gx(Y, ggw, g)     (sender-side adjoint)
+        dY = gY(ggx, w, g) + gY(x, ggw, g)     (receiver-side adjoint)
+        dw = gw(ggx, Y, g) + gw(x, ggY, g)
+    where gx(Y', w', g) is the first backward's grad_x with Y, w replaced, etc.
+    Returns (dx, dY, dw, dg)."""
+    src, dst, x, Y = _check(plan, src, dst, n_nodes, x, Y)
+    w = np.asarray(w, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    z = lambda a, like: np.zeros_like(like) if a is None else np.asarray(a, dtype=np.float64)
+    ggx, ggY, ggw = z(ggx, x), z(ggY, Y), z(ggw, w)
+    dg = (tp_conv_fwd(plan, src, dst, n_nodes, ggx, Y, w) + tp_conv_fwd(plan, src, dst, n_nodes, x, ggY, w)
+          + tp_conv_fwd(plan, src, dst, n_nodes, x, Y, ggw))
+    gx_a, gY_a, gw_a = tp_conv_bwd(plan, src, dst, n_nodes, ggx, Y, w, g)      # x -> ggx
+    gx_b, gY_b, gw_b = tp_conv_bwd(plan, src, dst, n_nodes, x, ggY, w, g)      # Y -> ggY
+    gx_c, gY_c, gw_c = tp_conv_bwd(plan, src, dst, n_nodes, x, Y, ggw, g)      # w -> ggw
+    dx = gx_b + gx_c
+    dY = gY_a + gY_c
+    dw = gw_a + gw_b
+    return dx, dY, dw, dg
+
+
 # ---------------------------------------------------------------------------
 # Radial weights (edge-conditioned weights computed from the edge length).
 #

@@ -365,3 +365,42 @@ def test_edge_vector_gradients_by_differences():
                                                    **kw), g) for s in (h, -h)]
     an = float(np.sum(grl * d))
     assert abs((F[0] - F[1]) / (2 * h) - an) <= 1e-6 * max(1.0, abs(an))
+
+
+def test_double_backward_by_differences_and_multilinearity():
+    """The second-order backward: central differences of the first backward
+    (exact up to rounding, every term being multilinear) in each of g, x, Y, w,
+    and the scaling identities of a loss linear in g and affine in x, Y, w."""
+    plan, wl = _wl("tiny")
+    rng = np.random.default_rng(11)
+    x, w, g = wl.x.astype(np.float64), wl.w.astype(np.float64), wl.g.astype(np.float64)
+    Y = oracle.sh_real(2, wl.r)
+    args = (plan, wl.src, wl.dst, wl.n_nodes)
+    ggx, ggY, ggw = rng.normal(size=x.shape), rng.normal(size=Y.shape), rng.normal(size=w.shape)
+
+    def L(x_, Y_, w_, g_):
+        gx, gY, gw = oracle.tp_conv_bwd(*args, x_, Y_, w_, g_)
+        return float(np.sum(ggx * gx) + np.sum(ggY * gY) + np.sum(ggw * gw))
+
+    dx, dY, dw, dg = oracle.tp_conv_double_bwd(*args, x, Y, w, g, ggx, ggY, ggw)
+    h = 1e-3
+    for grad, name in ((dx, 0), (dY, 1), (dw, 2), (dg, 3)):
+        base = [x, Y, w, g]
+        d = rng.normal(size=base[name].shape)
+        up = list(base)
+        dn = list(base)
+        up[name] = base[name] + h * d
+        dn[name] = base[name] - h * d
+        fd = (L(*up) - L(*dn)) / (2 * h)
+        an = float(np.sum(grad * d))
+        assert abs(fd - an) <= 1e-10 * max(1.0, abs(an))
+    Lv = L(x, Y, w, g)
+    assert abs(float(np.sum(dg * g)) - Lv) <= 1e-10 * max(1.0, abs(Lv))
+    # L = F(g, ggx, Y, w) + F(g, x, ggY, w) + F(g, x, Y, ggw): the terms with x
+    Fx = L(np.zeros_like(x), Y, w, g)
+    assert abs(float(np.sum(dx * x)) - (Lv - Fx)) <= 1e-10 * max(1.0, abs(Lv))
+    # missing cotangents are zeros
+    a = oracle.tp_conv_double_bwd(*args, x, Y, w, g, ggx, None, None)
+    b = oracle.tp_conv_double_bwd(*args, x, Y, w, g, ggx, np.zeros_like(Y), np.zeros_like(w))
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
