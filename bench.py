@@ -246,6 +246,8 @@ def main():
     r_sorted = tpc.gather_rows(T(wl.r), g.perm)
     grad_r = torch.empty_like(r_sorted)
     extras = {"forces": lambda: tpc.sph_harm_backward(lsh, r_sorted, gY, out=grad_r)}
+    # second-order backward with all three cotangents (here: the first backward's outputs)
+    extras["double_bwd"] = lambda: tpc.double_backward(plan, g, x, Y, w, go, gx, gY, gw)
 
     flush.fill_(1.0)
     # graph grouping, timed separately
@@ -304,6 +306,9 @@ def main():
         "kernel_hbm_frac": {n: ab[n] / (float(v) * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in zip(names, kt)},
         "bwd_ms": bwd_ms,
         "bwd_note": "one backward call (receiver then sender pass), per call",
+        "double_bwd_ms": extra_ms["double_bwd"],
+        "double_bwd_note": "second-order backward (dx, dY, dw, d grad_out for cotangents of all "
+                           "three first-order outputs), per call; not part of the step",
         "forces_ms": extra_ms["forces"],
         "forces_note": "edge-vector gradient from grad_Y (tp_conv_sph_harm_backward), per launch; "
                        "not part of the step",

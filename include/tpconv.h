@@ -184,6 +184,24 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
                            const float* Y, const float* w, const float* grad_out,
                            float* grad_x, float* grad_Y, float* grad_w, hipStream_t stream);
 
+/* Second-order backward ("Sobek", Abstract: the streaming schedule extends
+ * through forward, backward and double backward), e.g. for training on
+ * forces.  Given the inputs of tp_conv_backward and cotangents gg_x [N][xdim],
+ * gg_Y [E][ysh], gg_w [E][P][U] of its outputs (any may be NULL: zero), returns
+ * the gradients of  L = <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_w, grad_w>:
+ *   d_grad_out = out(gg_x, Y, w) + out(x, gg_Y, w) + out(x, Y, gg_w)   [N][outdim]
+ *   d_x = grad_x(gg_Y, w) + grad_x(Y, gg_w)                            [N][xdim]
+ *   d_Y = grad_Y(gg_x, w) + grad_Y(x, gg_w)                            [E][ysh]
+ *   d_w = grad_w(gg_x, Y) + grad_w(x, gg_Y)                            [E][P][U]
+ * (each term a first-order pass with one operand replaced; the layer is
+ * linear in each of g, x, Y, w).  Outputs may be NULL to skip them; edge
+ * arrays in receiver-sorted order; no atomics, deterministic. */
+tp_status tp_conv_double_backward(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                  const float* Y, const float* w, const float* grad_out,
+                                  const float* gg_x, const float* gg_Y, const float* gg_w,
+                                  float* d_x, float* d_Y, float* d_w, float* d_grad_out,
+                                  hipStream_t stream);
+
 /* ---- channel mix ("uvw", dense; fp32 MFMA) ----------------------------------
  * One U x U matrix per output irrep k (Wmix [K][U][U], K = number of output
  * irreps, U = 16, 32, 64 or 128; 1e and 1o never mix):

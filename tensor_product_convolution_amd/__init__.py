@@ -28,7 +28,7 @@ EXPORTS = (
     "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
-    "tp_conv_sph_harm_backward", "tp_conv_last_error",
+    "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_last_error",
 )
 
 
@@ -87,6 +87,8 @@ def lib():
         "tp_conv_backward_radial": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP,
                                           VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
         "tp_conv_sph_harm_backward": (I32, [I32, VP, I32, VP, VP, VP, VP]),
+        "tp_conv_double_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
+                                          VP, VP, VP, VP]),
         "tp_conv_radial_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_last_error": (ctypes.c_char_p, []),
     }
@@ -306,6 +308,31 @@ def backward(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=None):
                                   _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw),
                                   _stream(x.device)))
     return gx, gY, gw
+
+
+def double_backward(plan, graph, x, Y, w, grad_out, gg_x=None, gg_Y=None, gg_w=None,
+                    want=("x", "Y", "w", "g")):
+    """(d_x, d_Y, d_w, d_grad_out): gradients of <gg_x, grad_x> + <gg_Y, grad_Y> +
+    <gg_w, grad_w> with respect to the inputs of backward(); missing cotangents are
+    zero, outputs not in ``want`` are None."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(w, "w", torch.float32, (E, plan.n_paths, plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    for t, n, like in ((gg_x, "gg_x", x), (gg_Y, "gg_Y", Y), (gg_w, "gg_w", w)):
+        if t is not None:
+            _need(t, n, torch.float32, tuple(like.shape))
+    dx = torch.empty_like(x) if "x" in want else None
+    dY = torch.empty_like(Y) if "Y" in want else None
+    dw = torch.empty_like(w) if "w" in want else None
+    dg = torch.empty_like(grad_out) if "g" in want else None
+    gs = graph.cstruct()
+    _check(lib().tp_conv_double_backward(plan.handle, ctypes.byref(gs), _ptr(x), _ptr(Y), _ptr(w),
+                                         _ptr(grad_out), _ptr(gg_x), _ptr(gg_Y), _ptr(gg_w),
+                                         _ptr(dx), _ptr(dY), _ptr(dw), _ptr(dg), _stream(x.device)))
+    return dx, dY, dw, dg
 
 
 def uvw_forward(plan, Wmix, x_in, out=None):

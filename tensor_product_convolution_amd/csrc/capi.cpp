@@ -393,6 +393,46 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   return TP_OK;
 }
 
+tp_status tp_conv_double_backward(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                  const float* Y, const float* w, const float* grad_out,
+                                  const float* gg_x, const float* gg_Y, const float* gg_w,
+                                  float* d_x, float* d_Y, float* d_w, float* d_grad_out,
+                                  hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_double_backward: plan is NULL");
+  if (!plan->ks || !plan->ks->dbl_recv) return set_error(TP_ERR_UNSUPPORTED, "no compiled kernels");
+  tp_status s = check_graph(graph, d_x != nullptr);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && !grad_out && (d_x || d_Y || d_w))
+    return set_error(TP_ERR_ARG, "tp_conv_double_backward: grad_out NULL");
+  if (E > 0 && (!x || !Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_double_backward: x/Y/w NULL");
+  tpc::ConvArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_perm = graph->t_perm;
+  a.t_col = graph->t_col;
+  a.x = x;
+  a.Y = Y;
+  a.w = w;
+  a.grad_out = grad_out;
+  a.gg_x = gg_x;
+  a.gg_Y = gg_Y;
+  a.gg_w = gg_w;
+  a.d_x = d_x;
+  a.d_Y = d_Y;
+  a.d_w = d_w;
+  a.d_g = d_grad_out;
+  a.stream = stream;
+  hipError_t e = plan->ks->dbl_recv(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_double_backward receiver pass");
+  e = plan->ks->dbl_send(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_double_backward sender pass");
+  return TP_OK;
+}
+
 static tp_status need_uvw(tp_plan_t plan) {
   const int m = plan->mul;
   if (m > 128 || (m & (m - 1)) || m < 16 || plan->outs.size() > 8)

@@ -718,9 +718,16 @@ hipError_t launch_bwd_send(const ConvArgs& a) {
   return hipGetLastError();
 }
 
+}  // namespace tpc
+
+#include "dbl_kernels.hpp"
+
+namespace tpc {
+
 template <class S, int U>
 const KernelSet* kernel_set() {
-  static const KernelSet k{&launch_fwd<S, U>, &launch_bwd_recv<S, U>, &launch_bwd_send<S, U>};
+  static const KernelSet k{&launch_fwd<S, U>, &launch_bwd_recv<S, U>, &launch_bwd_send<S, U>,
+                           &launch_dbl_recv<S, U>, &launch_dbl_send<S, U>};
   return &k;
 }
 

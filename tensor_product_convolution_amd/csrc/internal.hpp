@@ -21,6 +21,9 @@ struct ConvArgs {
   const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
   const float *x = nullptr, *Y = nullptr, *w = nullptr, *grad_out = nullptr;
   float *out = nullptr, *grad_x = nullptr, *grad_Y = nullptr, *grad_w = nullptr;
+  // second-order backward: cotangents of (grad_x, grad_Y, grad_w), outputs
+  const float *gg_x = nullptr, *gg_Y = nullptr, *gg_w = nullptr;
+  float *d_x = nullptr, *d_Y = nullptr, *d_w = nullptr, *d_g = nullptr;
   hipStream_t stream = nullptr;
 };
 
@@ -30,6 +33,8 @@ struct KernelSet {
   LaunchFn fwd = nullptr;       // receiver pass: out
   LaunchFn bwd_recv = nullptr;  // receiver pass: grad_w, grad_Y
   LaunchFn bwd_send = nullptr;  // sender pass: grad_x
+  LaunchFn dbl_recv = nullptr;  // second order, receiver pass: d_grad_out, d_Y, d_w
+  LaunchFn dbl_send = nullptr;  // second order, sender pass: d_x
 };
 
 // radial-weight variant (edge weights from a radial network of the length)
