@@ -110,21 +110,37 @@ def read_traffic(config, sources=KERNEL_SOURCES):
     return out or None
 
 
-def cpu_baseline(op, wl):
-    """The float64 oracle on this host, fwd + bwd over the whole workload."""
+def cpu_baseline(op, wl, fwd_only=False, max_edges=60000):
+    """The float64 oracle on this host: harmonics + fwd (+ bwd) over the whole
+    workload, or over the edges into the first receivers when it has more than
+    max_edges edges (a bounded sample of the same graph)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
+    src, dst, r, n, x, g = wl.src, wl.dst, wl.r, wl.n_nodes, wl.x, wl.g
+    w = wl.w
+    what = f"whole workload ({wl.n_edges} edges)"
+    if wl.n_edges > max_edges:
+        order = np.argsort(dst, kind="stable")
+        e = np.sort(order[:max_edges])
+        e = e[np.isin(dst[e], np.unique(dst[order[:max_edges]])[:-1])]   # whole receivers only
+        nodes = np.unique(np.concatenate([src[e], dst[e]]))
+        src, dst = np.searchsorted(nodes, src[e]), np.searchsorted(nodes, dst[e])
+        r, w, x, n = r[e], w[e], x[nodes], len(nodes)
+        g = None if g is None else g[nodes]
+        what = (f"edges into the first receivers ({len(e)} of {wl.n_edges} edges, "
+                f"{n} nodes)")
     t0 = time.perf_counter()
-    Y = oracle.sh_real(op.lmax_sh, wl.r)
-    oracle.tp_conv_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w)
-    oracle.tp_conv_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w, wl.g)
+    Y = oracle.sh_real(op.lmax_sh, r)
+    oracle.tp_conv_fwd(op, src, dst, n, x, Y, w)
+    if not fwd_only:
+        oracle.tp_conv_bwd(op, src, dst, n, x, Y, w, g)
     dt = time.perf_counter() - t0
-    return {"value": wl.n_edges / dt, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"whole workload ({wl.n_edges} edges), harmonics + fwd + bwd once, float64, "
+    return {"value": len(src) / dt, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{what}, harmonics + fwd{'' if fwd_only else ' + bwd'} once, float64, "
                       f"{dt:.2f} s; host affinity {len(os.sched_getaffinity(0))} cores"}
 
 
@@ -210,6 +226,8 @@ def main():
     if args.config in RADIAL_WORKLOADS:
         return bench_radial(args, torch, tpc, make_workload, dev)
     irreps, lsh, lout, desc = WORKLOADS[args.config]
+    from workloads import CONFIGS
+    fwd_only = "fwd+bwd" not in CONFIGS[args.config]["modes"]   # the lmax-3 layer is forward only
     plan = tpc.Plan(irreps, lsh, lout)
     wl = make_workload(args.config, plan.dims(), seed=0)
     N, E = wl.n_nodes, wl.n_edges
@@ -220,7 +238,8 @@ def main():
     g = tpc.graph_build(src, dst, N)
     Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
     w = tpc.gather_rows(T(wl.w), g.perm)
-    x, go = T(wl.x), T(wl.g)
+    x = T(wl.x)
+    go = None if fwd_only else T(wl.g)
     out = torch.empty(N, plan.outdim, device=dev)
     gx = torch.empty_like(x)
     gY = torch.empty_like(Y)
@@ -229,7 +248,8 @@ def main():
 
     def step():
         tpc.forward(plan, g, x, Y, w, out=out)
-        tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))   # receiver, then sender pass
+        if not fwd_only:
+            tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))   # receiver, then sender pass
 
     if args.counters:
         counters_run(torch, dev, flush, step, args.config)
@@ -237,17 +257,17 @@ def main():
     do_flush, timed_steps_of, timed_kernel = make_timers(torch, flush)
     timed_steps = lambda k, cold: timed_steps_of(step, k, cold)
 
-    kernels = {
-        "fwd": lambda: tpc.forward(plan, g, x, Y, w, out=out),
-        "bwd_recv": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw)),
-        "bwd_send": lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None)),
-    }
-    bwd_both = lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))
-    r_sorted = tpc.gather_rows(T(wl.r), g.perm)
-    grad_r = torch.empty_like(r_sorted)
-    extras = {"forces": lambda: tpc.sph_harm_backward(lsh, r_sorted, gY, out=grad_r)}
-    # second-order backward with all three cotangents (here: the first backward's outputs)
-    extras["double_bwd"] = lambda: tpc.double_backward(plan, g, x, Y, w, go, gx, gY, gw)
+    kernels = {"fwd": lambda: tpc.forward(plan, g, x, Y, w, out=out)}
+    extras = {}
+    if not fwd_only:
+        kernels["bwd_recv"] = lambda: tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw))
+        kernels["bwd_send"] = lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None))
+        extras["bwd"] = lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))
+        r_sorted = tpc.gather_rows(T(wl.r), g.perm)
+        grad_r = torch.empty_like(r_sorted)
+        extras["forces"] = lambda: tpc.sph_harm_backward(lsh, r_sorted, gY, out=grad_r)
+        # second-order backward with all three cotangents (here: the first backward's outputs)
+        extras["double_bwd"] = lambda: tpc.double_backward(plan, g, x, Y, w, go, gx, gY, gw)
 
     flush.fill_(1.0)
     # graph grouping, timed separately
@@ -271,9 +291,8 @@ def main():
     reps, rounds = 10, max(2, args.steps // 5)
     kt_all = {n: timed_kernel(fn, reps, rounds) for n, fn in kernels.items()}
     extra_ms = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in extras.items()}
-    bwd_ms = float(timed_kernel(bwd_both, reps, rounds).mean())
 
-    names = ["fwd", "bwd_recv", "bwd_send"]
+    names = list(kernels)
     kt = np.array([kt_all[n].mean() for n in names])     # ms per launch
     step_ms = float(t.mean())
     fwd_ms = float(kt[0])
@@ -297,22 +316,23 @@ def main():
         "data": "synthetic (seeded; stands in for the pages' molecular graph)",
         "config": {"workload": f"{args.config}: {desc}", "n_nodes": N, "n_edges": E,
                    "irreps": irreps, "lmax_sh": lsh, "lmax_out": lout, "paths": P,
-                   "mode": "fwd+bwd", "cache": "L2+MALL flushed before each step"},
+                   "mode": "fwd" if fwd_only else "fwd+bwd",
+                   "cache": "L2+MALL flushed before each step"},
         "fwd_edges_per_s": E / (fwd_ms * 1e-3),
         "fwd_edges_per_s_note": "forward kernel alone (launch duration); value is the whole step",
         "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
         "kernel_ms": {n: float(v) for n, v in zip(names, kt)},
         "kernel_ms_note": f"per launch, {reps} back-to-back launches after a cache flush, mean of {rounds}",
         "kernel_hbm_frac": {n: ab[n] / (float(v) * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in zip(names, kt)},
-        "bwd_ms": bwd_ms,
+        "bwd_ms": extra_ms.get("bwd"),
         "bwd_note": "one backward call (receiver then sender pass), per call",
-        "double_bwd_ms": extra_ms["double_bwd"],
+        "double_bwd_ms": extra_ms.get("double_bwd"),
         "double_bwd_note": "second-order backward (dx, dY, dw, d grad_out for cotangents of all "
                            "three first-order outputs), per call; not part of the step",
-        "forces_ms": extra_ms["forces"],
+        "forces_ms": extra_ms.get("forces"),
         "forces_note": "edge-vector gradient from grad_Y (tp_conv_sph_harm_backward), per launch; "
                        "not part of the step",
-        "step_hbm_frac": ab["step"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_hbm_frac": ab["fwd" if fwd_only else "step"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "warm_edges_per_s": None if warm is None else E / (float(warm.mean()) * 1e-3),
         "graph_build_ms": float(np.median(gb)),
         "wall_s_timed_region": wall,
@@ -324,7 +344,8 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         op = oracle.build_plan(irreps, lsh, lout)
-        res["cpu_baseline"] = cpu_baseline(op, wl)
+        # about 10-30 s of oracle work: the lmax-3 product costs ~10x the lmax-2 one per edge
+        res["cpu_baseline"] = cpu_baseline(op, wl, fwd_only, max_edges=60000 if lsh <= 2 else 12000)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res))
