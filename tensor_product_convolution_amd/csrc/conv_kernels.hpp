@@ -37,11 +37,43 @@ struct LaneMap {
 
 // ---------------------------------------------------------------------------
 // per-edge arithmetic of one channel
+//
+// For large signatures the arithmetic is cut into phases at every change of
+// (input irrep, l2): the accumulators and the inputs pass through an empty asm
+// statement there, so every product of one group is formed after the previous
+// group has been folded into the accumulators.  Without it the code generator
+// forms the partial sums of all paths first (the instruction-selection DAG
+// orders pure arithmetic freely) and holds hundreds of them live, which cuts
+// occupancy to one wave per SIMD and adds register spills.  Small signatures
+// are left to the scheduler.
+
+template <class S>
+constexpr bool kPhased = S::nnz_total() > 256;
+
+template <class S, int P>
+constexpr bool group_end() {
+  if constexpr (P + 1 < S::NP) {
+    constexpr PathInfo a = S::paths.p[P], b = S::paths.p[P + 1];
+    return a.in != b.in || a.l2 != b.l2;
+  }
+  return false;
+}
+
+template <int N>
+__device__ __forceinline__ void launder(float (&v)[N]) {
+#pragma unroll
+  for (int t = 0; t < N; ++t) asm volatile("" : "+v"(v[t]));
+}
 
 // out accumulators += sum_p w_p * sum_nz C x_a Y_b
 template <class S>
-__device__ __forceinline__ void edge_fwd(const float (&xr)[S::XC], const float (&yr)[S::YC],
+__device__ __forceinline__ void edge_fwd(const float (&xin)[S::XC], const float (&yin)[S::YC],
                                          const float (&wr)[S::NP], float (&acc)[S::OC]) {
+  float xr[S::XC], yr[S::YC];
+#pragma unroll
+  for (int a = 0; a < S::XC; ++a) xr[a] = xin[a];
+#pragma unroll
+  for (int b = 0; b < S::YC; ++b) yr[b] = yin[b];
   static_for<S::NP>([&](auto P) {
     constexpr PathInfo pi = S::paths.p[P];
     using T = CgPath<pi.l1, pi.l2, pi.l3>;
@@ -53,15 +85,25 @@ __device__ __forceinline__ void edge_fwd(const float (&xr)[S::XC], const float (
       t[z.c] = fmaf(z.v, xr[pi.xo + z.a] * yr[pi.yo + z.b], t[z.c]);
     });
     static_for<D3>([&](auto C) { acc[pi.ko + C] = fmaf(wr[P], t[C], acc[pi.ko + C]); });
+    if constexpr (kPhased<S> && group_end<S, P>()) {
+      launder(acc);
+      launder(xr);
+      launder(yr);
+    }
   });
 }
 
 // Z_p[b] = sum_{a,c} C x_a g_c ; grad_w_p = sum_b Y_b Z_p[b] ; grad_Y_b += w_p Z_p[b]
 // (the products x_a g_c are shared by every path with the same (l1, output irrep))
 template <class S>
-__device__ __forceinline__ void edge_bwd_recv(const float (&xr)[S::XC], const float (&yr)[S::YC],
-                                              const float (&wr)[S::NP], const float (&gr)[S::OC],
+__device__ __forceinline__ void edge_bwd_recv(const float (&xin)[S::XC], const float (&yr)[S::YC],
+                                              const float (&wr)[S::NP], const float (&gin)[S::OC],
                                               float (&gw)[S::NP], float (&gy)[S::YC]) {
+  float xr[S::XC], gr[S::OC];
+#pragma unroll
+  for (int a = 0; a < S::XC; ++a) xr[a] = xin[a];
+#pragma unroll
+  for (int c = 0; c < S::OC; ++c) gr[c] = gin[c];
   static_for<S::NP>([&](auto P) {
     constexpr PathInfo pi = S::paths.p[P];
     using T = CgPath<pi.l1, pi.l2, pi.l3>;
@@ -76,13 +118,24 @@ __device__ __forceinline__ void edge_bwd_recv(const float (&xr)[S::XC], const fl
     static_for<D2>([&](auto B) { s = fmaf(yr[pi.yo + B], z[B], s); });
     gw[P] = s;
     static_for<D2>([&](auto B) { gy[pi.yo + B] = fmaf(wr[P], z[B], gy[pi.yo + B]); });
+    if constexpr (kPhased<S> && group_end<S, P>()) {
+      launder(gy);
+      launder(gw);
+      launder(xr);
+      launder(gr);
+    }
   });
 }
 
 // grad_x_a += sum_p w_p sum_nz C Y_b g_c
 template <class S>
-__device__ __forceinline__ void edge_bwd_send(const float (&yr)[S::YC], const float (&wr)[S::NP],
-                                              const float (&gr)[S::OC], float (&gx)[S::XC]) {
+__device__ __forceinline__ void edge_bwd_send(const float (&yin)[S::YC], const float (&wr)[S::NP],
+                                              const float (&gin)[S::OC], float (&gx)[S::XC]) {
+  float yr[S::YC], gr[S::OC];
+#pragma unroll
+  for (int b = 0; b < S::YC; ++b) yr[b] = yin[b];
+#pragma unroll
+  for (int c = 0; c < S::OC; ++c) gr[c] = gin[c];
   static_for<S::NP>([&](auto P) {
     constexpr PathInfo pi = S::paths.p[P];
     using T = CgPath<pi.l1, pi.l2, pi.l3>;
@@ -93,6 +146,11 @@ __device__ __forceinline__ void edge_bwd_send(const float (&yr)[S::YC], const fl
       constexpr Nz z = T::table.e[N];
       gx[pi.xo + z.a] = fmaf(z.v, yr[pi.yo + z.b] * wg[z.c], gx[pi.xo + z.a]);
     });
+    if constexpr (kPhased<S> && group_end<S, P>()) {
+      launder(gx);
+      launder(yr);
+      launder(gr);
+    }
   });
 }
 
