@@ -460,8 +460,11 @@ struct Cfg {
   static constexpr int WPB_F = 2 * R::BUF <= LDS ? 2 : 1;
   static constexpr int WPB_R = 2 * R::BUF <= LDS ? 2 : 1;
   static constexpr int WPB_S = (U <= 32 || 2 * Sd::BUF > LDS) ? 1 : 2;
-  static constexpr int NBUF_F = depth(R::NLOADS, R::BUF, WPB_F);
-  static constexpr int NBUF_R = depth(R::NLOADS + NST, R::BUF, WPB_R);
+  // large signatures are arithmetic-heavy: one buffer per wave doubles the
+  // workgroups (waves) that fit in LDS, which hides more latency than a
+  // second buffer would
+  static constexpr int NBUF_F = kPhased<S> ? 1 : depth(R::NLOADS, R::BUF, WPB_F);
+  static constexpr int NBUF_R = kPhased<S> ? 1 : depth(R::NLOADS + NST, R::BUF, WPB_R);
   static constexpr int NBUF_S = depth(Sd::NLOADS, Sd::BUF, WPB_S);
   static_assert(fits(R::BUF, NBUF_F, WPB_F) && fits(R::BUF, NBUF_R, WPB_R) &&
                     fits(Sd::BUF, NBUF_S, WPB_S), "staging exceeds 64 KB of LDS");
