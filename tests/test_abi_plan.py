@@ -109,3 +109,60 @@ def test_graph_and_conv_argument_errors_without_launch():
     assert L.tp_conv_gather_rows(fake, fake, -1, 3, fake, None) == -1
     msg = L.tp_conv_last_error().decode()
     assert "negative" in msg
+
+
+def test_radial_uvw_forces_double_argument_errors_without_launch():
+    """Host validation of the radial, mix, forces and second-order entry points:
+    every case returns its status before any HIP call."""
+    L = tpc.lib()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)                  # not 16-byte aligned
+    plain = tpc.Plan("16x0e+16x1o+16x2e", 2, 2)
+    rad = tpc.Plan("16x0e+16x1o+16x2e", 2, 2, radial=(8, 64, 5.0), uvw=True)
+    g = tpc._Graph(4, 10, fake, fake, fake, fake, fake, fake)
+    sz = ctypes.c_size_t()
+    # radial workspace: only for radial plans; a mix adds to it
+    assert L.tp_conv_radial_workspace(plain.handle, 4, 0, ctypes.byref(sz)) == -3
+    assert L.tp_conv_radial_workspace(rad.handle, -1, 0, ctypes.byref(sz)) == -1
+    assert L.tp_conv_radial_workspace(rad.handle, 4, 0, ctypes.byref(sz)) == 0 and sz.value > 0
+    base = sz.value
+    assert L.tp_conv_radial_workspace(rad.handle, 4, 1, ctypes.byref(sz)) == 0 and sz.value > base
+    # radial forward / backward
+    assert L.tp_conv_forward_radial(plain.handle, ctypes.byref(g), fake, fake, fake, fake, fake, None,
+                                    None, fake, None) == -3
+    assert L.tp_conv_forward_radial(rad.handle, ctypes.byref(g), fake, fake, fake, fake, fake, fake,
+                                    fake, fake, None) == -1          # out_pre aliases out
+    # x, Y, r_len, W1, W2 | Wmix, out_pre | grad_out | grad_x, grad_Y, grad_rlen, grad_W1, grad_W2 | grad_Wmix
+    args = [fake] * 5 + [None, None] + [fake] + [fake] * 5 + [None]
+    assert L.tp_conv_backward_radial(None, ctypes.byref(g), *args, fake, 1 << 30, None) == -1
+    assert L.tp_conv_backward_radial(plain.handle, ctypes.byref(g), *args, fake, 1 << 30, None) == -3
+    assert L.tp_conv_backward_radial(rad.handle, ctypes.byref(g), *args, fake, 16, None) == -5
+    bad = [odd] + [fake] * 4 + [None, None] + [fake] + [fake] * 5 + [None]
+    assert L.tp_conv_backward_radial(rad.handle, ctypes.byref(g), *bad, fake, 1 << 30, None) == -1
+    assert "aligned" in L.tp_conv_last_error().decode()
+    nomix = [fake] * 5 + [None, None] + [fake] + [fake] * 5 + [fake]   # grad_Wmix without Wmix
+    assert L.tp_conv_backward_radial(rad.handle, ctypes.byref(g), *nomix, fake, 1 << 30, None) == -1
+    # mix
+    assert L.tp_conv_uvw_forward(rad.handle, 4, fake, fake, fake, None) == -1      # in == out
+    assert L.tp_conv_uvw_forward(rad.handle, -1, fake, fake, ctypes.c_void_p(0x2000), None) == -1
+    assert L.tp_conv_uvw_forward(rad.handle, 4, fake, odd, ctypes.c_void_p(0x2000), None) == -1
+    assert L.tp_conv_uvw_backward(rad.handle, 4, fake, fake, fake, None, fake, fake, 16, None) == -5
+    # forces
+    assert L.tp_conv_sph_harm_backward(2, None, 5, fake, None, fake, None) == -1
+    assert L.tp_conv_sph_harm_backward(2, fake, -1, fake, None, fake, None) == -1
+    assert L.tp_conv_sph_harm_backward(4, fake, 5, fake, None, fake, None) == -3
+    # second order
+    assert L.tp_conv_double_backward(None, ctypes.byref(g), *([fake] * 4), None, None, None,
+                                     fake, fake, fake, fake, None) == -1
+    assert L.tp_conv_double_backward(plain.handle, None, *([fake] * 4), None, None, None,
+                                     fake, fake, fake, fake, None) == -1
+    assert L.tp_conv_double_backward(plain.handle, ctypes.byref(g), None, fake, fake, fake, None, None,
+                                     None, fake, fake, fake, fake, None) == -1
+    # plan options
+    h = ctypes.c_void_p()
+    o = tpc._Opts(8, 0, 5.0, 0)
+    assert L.tp_conv_plan_create(ctypes.byref(h), b"16x0e+16x1o+16x2e", 2, 2, 0, ctypes.byref(o)) == -1
+    o = tpc._Opts(8, 64, 5.0, 0)
+    assert L.tp_conv_plan_create(ctypes.byref(h), b"16x0e+16x1o", 2, 2, 0, ctypes.byref(o)) == -3
+    o = tpc._Opts(0, 0, 0.0, 1)
+    assert L.tp_conv_plan_create(ctypes.byref(h), b"24x0e+24x1o", 2, 2, 0, ctypes.byref(o)) == -3

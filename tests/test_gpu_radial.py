@@ -231,3 +231,35 @@ def test_sph_harm_backward_parity(tpc, lmax):
     r64 = r.astype(np.float64)
     ref2 = ref + grl[:, None] * r64 / np.linalg.norm(r64, axis=1)[:, None]
     assert _vec_err(got2, ref2) <= TOL
+
+
+def test_radial_isolated_nodes_empty_graph_and_determinism(tpc):
+    """Nodes without edges, a graph without edges, and bitwise-identical repeats
+    (every parameter gradient is a fixed-order sum of per-workgroup partials)."""
+    say("radial degenerate graphs and determinism")
+    U = 16
+    op = oracle.build_plan(_irreps(U), 2, 2)
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    wl = make_workload("stream", dims_of(op), seed=3, n_nodes=60)
+    keep = (wl.src >= 10) & (wl.dst >= 10)          # nodes 0..9 lose every edge
+    wl.src, wl.dst, wl.r = wl.src[keep], wl.dst[keep], wl.r[keep]
+    a = _gpu_radial(tpc, plan, wl, True, wl.g)
+    b = _gpu_radial(tpc, plan, wl, True, wl.g)
+    for k, v in a.items():
+        if isinstance(v, np.ndarray):
+            assert np.array_equal(v, b[k]), k
+    Yo = oracle.sh_real(2, wl.r)
+    ref = oracle.tp_conv_radial_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Yo, wl.r_len, wl.W1, wl.W2,
+                                    wl.Wmix, wl.g, 8, RC, with_grad_rlen=True)
+    assert block_err(a["gx"], ref[0], in_blocks(op)) <= TOL
+    assert np.all(a["gx"][:10] == 0) and np.all(a["pre"][:10] == 0)
+    assert block_err(a["gY"], ref[1][a["perm"]], y_blocks(op)) <= TOL
+    _check_params(op, a, ref, U)
+    # no edges at all
+    wl.src = wl.src[:0]
+    wl.dst = wl.dst[:0]
+    wl.r = wl.r[:0]
+    c = _gpu_radial(tpc, plan, wl, True, wl.g)
+    for k in ("out", "pre", "gx", "gW1", "gW2", "gWm"):
+        assert np.all(c[k] == 0), k
+    assert c["gY"].shape == (0, 9) and c["grl"].shape == (0,) and c["gr"].shape == (0, 3)
