@@ -182,6 +182,37 @@ def make_timers(torch, flush):
     return do_flush, timed_steps, timed_kernel
 
 
+def copy_bandwidth(torch, dev, flush, nbytes=1 << 29):
+    """GB/s of a plain device copy (read + write of nbytes each) after a flush: the
+    practical ceiling of a kernel that writes as much as it reads."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    best = None
+    for _ in range(3):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del a, b
+    return 2 * nbytes / (best * 1e-3) / 1e9
+
+
+def read_profile_value(config, key, sources):
+    """one value of the committed counter summary (None if absent or stale)"""
+    path = PROFILE_SUMMARY.format(config)
+    if not os.path.exists(path):
+        return None
+    vals = dict(l.split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
+    vals = {k.strip(): v.strip() for k, v in vals.items()}
+    if vals.get("kernel_source_hash") != kernel_source_hash(sources):
+        return None
+    return float(vals[key]) if key in vals else None
+
+
 def counters_run(torch, dev, flush, step, config):
     """a few steps plus a plain 512 MiB copy (the calibration of the counters)"""
     flush.fill_(1.0)
@@ -294,6 +325,9 @@ def main():
 
     names = list(kernels)
     kt = np.array([kt_all[n].mean() for n in names])     # ms per launch
+    copy_gbs = copy_bandwidth(torch, dev, flush)
+    wk = read_profile_value(args.config, "write_kib.fwd", KERNEL_SOURCES)
+    fwd_write_ratio = None if wk is None else wk * 1024 / (4.0 * N * plan.outdim)
     step_ms = float(t.mean())
     fwd_ms = float(kt[0])
     ab = algorithmic_bytes(N, E, P, U, ysh, plan.xdim, plan.outdim)
@@ -333,6 +367,12 @@ def main():
         "forces_note": "edge-vector gradient from grad_Y (tp_conv_sph_harm_backward), per launch; "
                        "not part of the step",
         "step_hbm_frac": ab["fwd" if fwd_only else "step"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "copy_GBs": copy_gbs,
+        "copy_note": "plain device copy of 512 MiB (read + write) after a flush: the practical "
+                     "ceiling of a kernel that writes as much as it reads",
+        "fwd_write_ratio": fwd_write_ratio,
+        "fwd_write_note": "forward HBM writes (rocprofv3 WRITE_SIZE, committed summary) over "
+                          "N*outdim*4: 1.0 means nothing but the output is written",
         "warm_edges_per_s": None if warm is None else E / (float(warm.mean()) * 1e-3),
         "graph_build_ms": float(np.median(gb)),
         "wall_s_timed_region": wall,
@@ -438,6 +478,9 @@ def bench_radial(args, torch, tpc, make_workload, dev):
     kt = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in kernels.items()}
     extra_ms = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in extras.items()}
     fl = radial_flops(E, P, U, NH)
+    copy_gbs = copy_bandwidth(torch, dev, flush)
+    wk = read_profile_value(args.config, "write_kib.fwd", RADIAL_SOURCES)
+    fwd_write_ratio = None if wk is None else wk * 1024 / (4.0 * N * plan.outdim)
     names = ["fwd", "bwd_recv", "bwd_w2", "bwd_send"]
     dom = max(names, key=lambda n: kt[n])
     achieved = fl[dom] / (kt[dom] * 1e-3) / 1e12
@@ -471,6 +514,10 @@ def bench_radial(args, torch, tpc, make_workload, dev):
         "forces_ms": extra_ms,
         "forces_note": "receiver pass that also returns the edge-length gradient, and the "
                        "edge-vector gradient kernel; not part of the step",
+        "copy_GBs": copy_gbs,
+        "fwd_write_ratio": fwd_write_ratio,
+        "fwd_write_note": "radial pass HBM writes (WRITE_SIZE, committed summary) over "
+                          "N*outdim*4: no per-edge weight or message is written",
         "wall_s_timed_region": wall,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
