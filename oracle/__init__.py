@@ -37,6 +37,7 @@ from .csr import csr_build
 from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, bessel_basis_deriv, radial_mlp_fwd,
                    radial_mlp_bwd, uvw_mix_fwd, uvw_mix_bwd,
                    tp_conv_radial_fwd, tp_conv_radial_bwd, tp_conv_double_bwd)
+from .fc import fc_conv_fwd, fc_conv_bwd
 
 __all__ = [
     "parse_irreps", "build_plan", "OraclePlan", "cg_complex",
@@ -44,5 +45,6 @@ __all__ = [
     "sh_real_vjp", "wigner_D_real", "csr_build", "tp_conv_fwd", "tp_conv_bwd",
     "bessel_basis", "bessel_basis_deriv",
     "radial_mlp_fwd", "radial_mlp_bwd", "uvw_mix_fwd", "uvw_mix_bwd",
-    "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd",
+    "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd", "fc_conv_fwd",
+    "fc_conv_bwd",
 ]
