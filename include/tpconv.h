@@ -202,6 +202,22 @@ tp_status tp_conv_double_backward(tp_plan_t plan, const tp_graph* graph, const f
                                   float* d_x, float* d_Y, float* d_w, float* d_grad_out,
                                   hipStream_t stream);
 
+/* ---- fully connected per-edge weights (second operator family) -------------
+ * Per-edge weights that mix channels, W_e[p][u][v] = sum_h R[e][h] Theta[h][p][u][v]
+ * (R [E][n_radial] radial features, receiver-sorted; Theta [n_radial][P][U][U]):
+ *   out[i, k, v, c] = sum_{e into i} sum_{p->k} sum_u W_e[p,u,v] T_p(x_j[u], Y_e)[c]
+ * computed by reassociation ("Sobek", Abstract: radial projection, coupling and
+ * aggregation reassociated into bounded receiver-side state; fully connected
+ * multiplicity mixing preserved): S_i[h,p,u,c] = sum_e R[e][h] T_p(x_j[u], Y_e)[c]
+ * is streamed per receiver into the node-sized workspace (tp_conv_fc_workspace
+ * bytes), then out_i = Theta^T S_i per output irrep on the matrix cores.  No
+ * per-edge weight or message is formed.  Compiled for 0e+1o+2e / lmax 2 with 16
+ * or 32 channels and 8 radial features (other shapes: TP_ERR_UNSUPPORTED). */
+tp_status tp_conv_fc_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial, size_t* bytes);
+tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                             const float* R, int32_t n_radial, const float* Theta, float* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- channel mix ("uvw", dense; fp32 MFMA) ----------------------------------
  * One U x U matrix per output irrep k (Wmix [K][U][U], K = number of output
  * irreps, U = 16, 32, 64 or 128; 1e and 1o never mix):

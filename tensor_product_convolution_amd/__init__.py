@@ -28,7 +28,8 @@ EXPORTS = (
     "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
-    "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_last_error",
+    "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
+    "tp_conv_forward_fc", "tp_conv_last_error",
 )
 
 
@@ -87,6 +88,8 @@ def lib():
         "tp_conv_backward_radial": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP,
                                           VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
         "tp_conv_sph_harm_backward": (I32, [I32, VP, I32, VP, VP, VP, VP]),
+        "tp_conv_fc_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
+        "tp_conv_forward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, SZ, VP]),
         "tp_conv_double_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
                                           VP, VP, VP, VP]),
         "tp_conv_radial_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
@@ -333,6 +336,28 @@ def double_backward(plan, graph, x, Y, w, grad_out, gg_x=None, gg_Y=None, gg_w=N
                                          _ptr(grad_out), _ptr(gg_x), _ptr(gg_Y), _ptr(gg_w),
                                          _ptr(dx), _ptr(dY), _ptr(dw), _ptr(dg), _stream(x.device)))
     return dx, dY, dw, dg
+
+
+def forward_fc(plan, graph, x, Y, R, Theta, out=None, ws=None):
+    """out [N, outdim] of the convolution with fully connected per-edge weights
+    W_e = sum_h R[e, h] Theta[h] (R receiver-sorted [E, H], Theta [H, P, U, U])."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    H = R.shape[1]
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(R, "R", torch.float32, (E, H))
+    _need(Theta, "Theta", torch.float32, (H, plan.n_paths, plan.mul, plan.mul))
+    if out is None:
+        out = torch.empty((N, plan.outdim), dtype=torch.float32, device=x.device)
+    b = ctypes.c_size_t()
+    _check(lib().tp_conv_fc_workspace(plan.handle, N, H, ctypes.byref(b)))
+    if ws is None:
+        ws = torch.empty(max(b.value, 1), dtype=torch.uint8, device=x.device)
+    g = graph.cstruct()
+    _check(lib().tp_conv_forward_fc(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(R), H,
+                                    _ptr(Theta), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
 
 
 def uvw_forward(plan, Wmix, x_in, out=None):

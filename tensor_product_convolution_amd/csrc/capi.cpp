@@ -433,6 +433,55 @@ tp_status tp_conv_double_backward(tp_plan_t plan, const tp_graph* graph, const f
   return TP_OK;
 }
 
+static const tpc::FcSet* find_fc(tp_plan_t plan, int n_radial) {
+  if (plan->ls == std::vector<int>{0, 1, 2} && plan->lmax_sh == 2 && plan->lmax_out == 2)
+    return tpc::fc_l012_s2(plan->mul, n_radial);
+  return nullptr;
+}
+
+tp_status tp_conv_fc_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial, size_t* bytes) {
+  if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_fc_workspace: NULL argument");
+  if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_fc_workspace: negative size");
+  const tpc::FcSet* fs = find_fc(plan, n_radial);
+  if (!fs)
+    return set_error(TP_ERR_UNSUPPORTED, "no compiled fully connected kernel (supported: 0e+1o+2e / "
+                                         "lmax 2 with 16 or 32 channels and 8 radial features)");
+  *bytes = fs->workspace(n_nodes);
+  return TP_OK;
+}
+
+tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                             const float* R, int32_t n_radial, const float* Theta, float* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward_fc: plan is NULL");
+  size_t need = 0;
+  tp_status s = tp_conv_fc_workspace(plan, graph ? graph->n_nodes : 0, n_radial, &need);
+  if (s != TP_OK) return s;
+  s = check_graph(graph, false);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && (!out || !Theta)) return set_error(TP_ERR_ARG, "tp_conv_forward_fc: out/Theta NULL");
+  if (E > 0 && (!x || !Y || !R)) return set_error(TP_ERR_ARG, "tp_conv_forward_fc: x/Y/R NULL");
+  if (ws_bytes < need || (need > 0 && !ws))
+    return set_error(TP_ERR_WORKSPACE, "tp_conv_forward_fc: workspace too small");
+  tpc::FcArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.outdim = plan->outdim;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.x = x;
+  a.Y = Y;
+  a.R = R;
+  a.Theta = Theta;
+  a.out = out;
+  a.ws = ws;
+  a.stream = stream;
+  hipError_t e = find_fc(plan, n_radial)->fwd(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_forward_fc launch");
+  return TP_OK;
+}
+
 static tp_status need_uvw(tp_plan_t plan) {
   const int m = plan->mul;
   if (m > 128 || (m & (m - 1)) || m < 16 || plan->outs.size() > 8)

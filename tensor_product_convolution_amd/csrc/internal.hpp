@@ -56,6 +56,22 @@ struct RadialSet {
   RadialFn bwd = nullptr;                        // grad_x, grad_Y, grad_rlen, grad_W1, grad_W2
   size_t (*bwd_workspace)(int n_nodes, int n_edges) = nullptr;
 };
+// fully connected per-edge weights (W_e = sum_h R_e[h] Theta[h]), reassociated
+struct FcArgs {
+  int32_t n_nodes = 0, n_edges = 0, outdim = 0;
+  const int32_t *row_ptr = nullptr, *col = nullptr;
+  const float *x = nullptr, *Y = nullptr, *R = nullptr, *Theta = nullptr;
+  float* out = nullptr;
+  void* ws = nullptr;
+  hipStream_t stream = nullptr;
+};
+struct FcSet {
+  hipError_t (*fwd)(const FcArgs&) = nullptr;
+  size_t (*workspace)(int n_nodes) = nullptr;
+  int n_radial = 0;
+};
+const FcSet* fc_l012_s2(int mul, int n_radial);
+
 const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul, int nb,
                              int nh);
 const RadialSet* radial_l012_s2(int mul, int nb, int nh);

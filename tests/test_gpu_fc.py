@@ -1,0 +1,73 @@
+"""GPU parity of the convolution with fully connected per-edge weights (computed
+by reassociation into receiver state and a dense contraction) against the
+float64 oracle, which forms the per-edge weights and messages by definition.
+Every output irrep block within 1e-4 of max|ref| of that block."""
+import numpy as np
+import pytest
+
+import oracle
+from tests._common import dims_of
+from tests.test_gpu_parity import T, block_err, out_blocks, say
+from workloads import make_workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+H = 8
+
+
+@pytest.fixture(scope="module")
+def tpc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_product_convolution_amd as m
+    m.lib()
+    return m
+
+
+def _case(U, graph, n, seed=0):
+    irr = f"{U}x0e+{U}x1o+{U}x2e"
+    op = oracle.build_plan(irr, 2, 2)
+    wl = make_workload("mid", dims_of(op), seed=seed, n_nodes=n)
+    if graph != "mid":
+        gw = make_workload(graph, dims_of(op), seed=seed, n_nodes=n, graph_only=True)
+        wl.src, wl.dst, wl.r = gw.src, gw.dst, gw.r
+    rng = np.random.default_rng(seed + 17)
+    R = rng.normal(size=(wl.n_edges, H)).astype(np.float32)
+    Th = (rng.normal(size=(H, op.n_paths, U, U)) / np.sqrt(H * U)).astype(np.float32)
+    return irr, op, wl, R, Th
+
+
+def _gpu(tpc, irr, wl, R, Th):
+    plan = tpc.Plan(irr, 2, 2)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+    Rs = tpc.gather_rows(T(R), g.perm)
+    out = tpc.forward_fc(plan, g, T(wl.x), Y, Rs, T(Th))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("U,graph,n", [(16, "mid", 200), (32, "mid", 300), (32, "zipf", 400),
+                                       (16, "lmax3", 250), (32, "mid", 1536)])
+def test_fc_forward_parity(tpc, U, graph, n):
+    say(f"fc forward U={U} graph={graph} n={n}")
+    irr, op, wl, R, Th = _case(U, graph, n)
+    got = _gpu(tpc, irr, wl, R, Th)
+    ref = oracle.fc_conv_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, oracle.sh_real(2, wl.r), R, Th)
+    assert block_err(got, ref, out_blocks(op)) <= TOL
+
+
+def test_fc_isolated_and_empty(tpc):
+    say("fc forward isolated nodes, empty graph")
+    irr, op, wl, R, Th = _case(32, "mid", 80, seed=3)
+    keep = wl.dst >= 10
+    wl.src, wl.dst, wl.r = wl.src[keep], wl.dst[keep], wl.r[keep]
+    R = R[keep]
+    got = _gpu(tpc, irr, wl, R, Th)
+    ref = oracle.fc_conv_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, oracle.sh_real(2, wl.r), R, Th)
+    assert np.all(got[:10] == 0)
+    assert block_err(got, ref, out_blocks(op)) <= TOL
+    wl.src, wl.dst, wl.r = wl.src[:0], wl.dst[:0], wl.r[:0]
+    assert np.all(_gpu(tpc, irr, wl, R[:0], Th) == 0)
