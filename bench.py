@@ -57,10 +57,17 @@ RADIAL_WORKLOADS = {
                "weights from a radial MLP (8 Bessel -> 64 SiLU -> 15x128) computed on chip, "
                "128x128 uvw mix per output irrep, fwd+bwd"),
 }
+FC_WORKLOADS = {
+    "fc": ("32x0e+32x1o+32x2e", 2, 2, 8,
+           "1536 atoms, 46080 directed edges (the mid graph), 32x0e+32x1o+32x2e, real SH lmax 2, "
+           "15 paths, fully connected per-edge weights W_e = sum_h R_e[h] Theta[h] (8 radial "
+           "features, 32x32 per path) by reassociation into receiver state, fwd"),
+}
 FP32_MFMA_PEAK_TFLOPS = 157.3
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_{}.txt")
 KERNEL_SOURCES = ("conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
 RADIAL_SOURCES = ("radial_kernels.hpp", "conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
+FC_SOURCES = ("fc_kernels.hip", "radial_kernels.hpp", "conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES):
@@ -233,7 +240,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mid", choices=sorted(WORKLOADS) + sorted(RADIAL_WORKLOADS))
+    ap.add_argument("--config", default="mid",
+                    choices=sorted(WORKLOADS) + sorted(RADIAL_WORKLOADS) + sorted(FC_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time the steps back to back without the cache flush")
@@ -256,6 +264,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.config in RADIAL_WORKLOADS:
         return bench_radial(args, torch, tpc, make_workload, dev)
+    if args.config in FC_WORKLOADS:
+        return bench_fc(args, torch, tpc, make_workload, dev)
     irreps, lsh, lout, desc = WORKLOADS[args.config]
     from workloads import CONFIGS
     fwd_only = "fwd+bwd" not in CONFIGS[args.config]["modes"]   # the lmax-3 layer is forward only
@@ -530,6 +540,101 @@ def bench_radial(args, torch, tpc, make_workload, dev):
         res["cpu_baseline"] = cpu_baseline_radial(op, wl, radial)
     else:
         res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+def fc_algorithmic(N, E, P, U, H, d3_paths):
+    """compulsory bytes (inputs and output once) and the reassociated schedule's
+    MFMA flops: state accumulation 2 H Q per edge, contraction 2 H Q U per node,
+    Q = U * sum_p (2 l3 + 1)"""
+    Q = U * sum(d3_paths)
+    return {"bytes": 4.0 * (E * (9 + H + 2) + N * (9 * U + 17 * U + 1)) + 4.0 * H * P * U * U,
+            "state_flops": 2.0 * H * Q * E, "contract_flops": 2.0 * H * Q * U * N}
+
+
+def bench_fc(args, torch, tpc, make_workload, dev):
+    from workloads import make_fc_inputs
+    irreps, lsh, lout, H, desc = FC_WORKLOADS[args.config]
+    plan = tpc.Plan(irreps, lsh, lout)
+    wl = make_workload("mid", plan.dims(), seed=0)
+    N, E = wl.n_nodes, wl.n_edges
+    P, U = plan.n_paths, plan.mul
+    R, Th = make_fc_inputs(E, P, U, H, seed=0)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), N)
+    Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
+    Rs = tpc.gather_rows(T(R), g.perm)
+    x, Tht = T(wl.x), T(Th)
+    out = torch.empty(N, plan.outdim, device=dev)
+    ws = torch.empty(tpc.fc_workspace(plan, N, H), dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def step():
+        tpc.forward_fc(plan, g, x, Y, Rs, Tht, out=out, ws=ws)
+
+    if args.counters:
+        counters_run(torch, dev, flush, step, args.config)
+        return
+    do_flush, timed_steps, timed_kernel = make_timers(torch, flush)
+    flush.fill_(1.0)
+    timed_steps(step, args.warmup, True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    t = timed_steps(step, args.steps, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    step_ms = float(t.mean())
+    d3s = [2 * l3 + 1 for (_, _, l3, _) in plan.paths()]
+    alg = fc_algorithmic(N, E, P, U, H, d3s)
+    traffic = read_traffic(args.config, FC_SOURCES)
+    if traffic is not None and {"fc_state", "fc_contract"} <= set(traffic):
+        traffic = traffic["fc_state"] + traffic["fc_contract"]
+    else:
+        traffic = None
+    flops = alg["state_flops"] + alg["contract_flops"]
+    res = {
+        "metric": METRIC, "value": E / (step_ms * 1e-3), "unit": "edges/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; random radial features and mixing parameters)",
+        "config": {"workload": f"{args.config}: {desc}", "n_nodes": N, "n_edges": E,
+                   "irreps": irreps, "paths": P, "radial_features": H, "mode": "fwd",
+                   "cache": "L2+MALL flushed before each step"},
+        "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
+        "compulsory_bytes": alg["bytes"],
+        "state_bytes": ws.numel(),
+        "mfma_flops": flops,
+        "step_mfma_frac": flops / (step_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+        "wall_s_timed_region": wall,
+        "roofline": {"bound": "hbm", "kernel": "forward_fc (both phases)",
+                     "achieved": (alg["bytes"] + 2 * ws.numel()) / (step_ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (alg["bytes"] + 2 * ws.numel()) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes": alg["bytes"] + 2 * ws.numel(),
+                     "note": "inputs and output once plus one write and one read of the "
+                             "node-sized receiver state", "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        op = oracle.build_plan(irreps, lsh, lout)
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            threads = 1
+        n_s = min(E, 46080)
+        order = np.argsort(wl.dst, kind="stable")[:n_s]
+        e = np.sort(order)
+        nodes = np.unique(np.concatenate([wl.src[e], wl.dst[e]]))
+        src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
+        t0 = time.perf_counter()
+        oracle.fc_conv_fwd(op, src, dst, len(nodes), wl.x[nodes], oracle.sh_real(lsh, wl.r[e]), R[e], Th)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(e) / dt, "unit": "edges/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"{len(e)} of {E} edges (receiver order), harmonics + "
+                                         f"fwd once, float64 (per-edge weights formed), {dt:.2f} s"}
     print(json.dumps(res))
 
 

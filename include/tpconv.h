@@ -212,7 +212,10 @@ tp_status tp_conv_double_backward(tp_plan_t plan, const tp_graph* graph, const f
  * is streamed per receiver into the node-sized workspace (tp_conv_fc_workspace
  * bytes), then out_i = Theta^T S_i per output irrep on the matrix cores.  No
  * per-edge weight or message is formed.  Compiled for 0e+1o+2e / lmax 2 with 16
- * or 32 channels and 8 radial features (other shapes: TP_ERR_UNSUPPORTED). */
+ * or 32 channels and 8 radial features (other shapes: TP_ERR_UNSUPPORTED).
+ * Errors: TP_ERR_WORKSPACE if ws is smaller than tp_conv_fc_workspace; TP_ERR_ARG
+ * if ws is not 16-byte aligned or a needed pointer is NULL.  out is overwritten
+ * (isolated receivers get zeros). */
 tp_status tp_conv_fc_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial, size_t* bytes);
 tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
                              const float* R, int32_t n_radial, const float* Theta, float* out,

@@ -338,6 +338,13 @@ def double_backward(plan, graph, x, Y, w, grad_out, gg_x=None, gg_Y=None, gg_w=N
     return dx, dY, dw, dg
 
 
+def fc_workspace(plan, n_nodes, n_radial):
+    """bytes of the node-sized receiver state forward_fc needs"""
+    b = ctypes.c_size_t()
+    _check(lib().tp_conv_fc_workspace(plan.handle, n_nodes, n_radial, ctypes.byref(b)))
+    return b.value
+
+
 def forward_fc(plan, graph, x, Y, R, Theta, out=None, ws=None):
     """out [N, outdim] of the convolution with fully connected per-edge weights
     W_e = sum_h R[e, h] Theta[h] (R receiver-sorted [E, H], Theta [H, P, U, U])."""
@@ -350,10 +357,11 @@ def forward_fc(plan, graph, x, Y, R, Theta, out=None, ws=None):
     _need(Theta, "Theta", torch.float32, (H, plan.n_paths, plan.mul, plan.mul))
     if out is None:
         out = torch.empty((N, plan.outdim), dtype=torch.float32, device=x.device)
-    b = ctypes.c_size_t()
-    _check(lib().tp_conv_fc_workspace(plan.handle, N, H, ctypes.byref(b)))
+    nbytes = fc_workspace(plan, N, H)
     if ws is None:
-        ws = torch.empty(max(b.value, 1), dtype=torch.uint8, device=x.device)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    elif ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
     g = graph.cstruct()
     _check(lib().tp_conv_forward_fc(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(R), H,
                                     _ptr(Theta), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)))

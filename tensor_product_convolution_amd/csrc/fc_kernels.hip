@@ -130,45 +130,67 @@ __global__ void __launch_bounds__(256)
   });
 }
 
-// Phase 2.  Workgroup of 4 waves; each wave computes a tile of 16 rows (i, c)
-// of one output irrep against all U output channels.  Rows of all irreps are
-// enumerated irrep by irrep.
+// Phase 2.  One workgroup (4 waves) per tile of 16 rows (i, c) of one output
+// irrep; the waves split the contraction length K_k in four and meet in LDS.
+// Within a wave, lane group l/16 takes four consecutive K per four MFMA steps
+// (the order of a sum over K is free), so each lane reads its row with one
+// 16-byte load per four steps.  Rows of all irreps are enumerated irrep by
+// irrep (blockIdx.x).
 template <int U, int H>
 __global__ void __launch_bounds__(256)
     k_fc_contract(int n_nodes, const float* __restrict__ Sbuf, const float* __restrict__ Theta, int P,
                   int outdim, float* __restrict__ out, FcLayout lay) {
   constexpr int NV = U / 16;
+  __shared__ float red[3][NV][4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e16 = lane & 15, g = lane >> 4;
-  // total row tiles over irreps
-  int tiles_before[9];
-  tiles_before[0] = 0;
-  for (int k = 0; k < lay.n_out; ++k)
-    tiles_before[k + 1] = tiles_before[k] + (n_nodes * lay.d3[k] + 15) / 16;
-  const int total = tiles_before[lay.n_out];
-  for (int tile = blockIdx.x * 4 + wv; tile < total; tile += gridDim.x * 4) {
-    int k = 0;
-    while (tile >= tiles_before[k + 1]) ++k;
-    const int d3 = lay.d3[k], npk = lay.npk[k];
-    const int KK = H * npk * U;
-    const int rows = n_nodes * d3;
-    const int row0 = (tile - tiles_before[k]) * 16;
-    const int ra = row0 + e16;                     // this lane's A row
-    const bool va = ra < rows;
-    const float* arow = Sbuf + lay.base[k] + (size_t)(va ? ra : rows - 1) * KK;
-    f32x4 acc[NV];
+  int k = 0, first = 0;
+  while (k + 1 < lay.n_out && (int)blockIdx.x >= first + (n_nodes * lay.d3[k] + 15) / 16) {
+    first += (n_nodes * lay.d3[k] + 15) / 16;
+    ++k;
+  }
+  const int d3 = lay.d3[k], npk = lay.npk[k];
+  const int KK = H * npk * U;                       // a multiple of 256
+  const int rows = n_nodes * d3;
+  const int row0 = ((int)blockIdx.x - first) * 16;
+  const int ra = row0 + e16;                         // this lane's A row
+  const bool va = ra < rows;
+  const float* arow = Sbuf + lay.base[k] + (size_t)(va ? ra : rows - 1) * KK;
+  const int kq = KK / 4;                             // this wave's share of K
+  const int K0 = wv * kq;
+  f32x4 acc[NV];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int kk = 0; kk < KK / 4; ++kk) {
-      const int K = 4 * kk + g;
-      const float a = va ? arow[K] : 0.f;
-      const int uu = K % U, t = K / U;
-      const int pl = t % npk, h = t / npk;
-      const float* th = Theta + (((size_t)h * P + lay.pg[k][pl]) * U + uu) * U + e16;
+  for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // K = (h * npk + pl) * U + uu; a 16-aligned block of K shares (h, pl), so
+  // t = K / U is uniform over the wave and Theta's row block is a scalar base.
+  for (int t = K0 / U; t < (K0 + kq) / U; ++t) {
+    const int pl = t % npk, h = t / npk;
+    const float* thb = Theta + ((size_t)h * P + lay.pg[k][pl]) * U * U + e16;
+    const float* ab = arow + (size_t)t * U + 4 * g;
 #pragma unroll
-      for (int n = 0; n < NV; ++n) acc[n] = mfma_16x16x4(a, th[16 * n], acc[n]);
+    for (int ub = 0; ub < U; ub += 16) {
+      const float4 a4 = va ? *reinterpret_cast<const float4*>(ab + ub) : float4{0.f, 0.f, 0.f, 0.f};
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float* th = thb + (size_t)(ub + 4 * g + st) * U;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) acc[n] = mfma_16x16x4(av[st], th[16 * n], acc[n]);
+      }
     }
+  }
+  if (wv > 0) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wv - 1][n][r][lane] = acc[n][r];
+  }
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[n][r] += red[0][n][r][lane] + red[1][n][r][lane] + red[2][n][r][lane];
     // D[row 4g + r][v = 16n + l%16]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -221,8 +243,7 @@ hipError_t launch_fc_fwd(const FcArgs& a) {
                      a.col, a.x, a.Y, a.R, Sbuf, L);
   int tiles = 0;
   for (int k = 0; k < L.n_out; ++k) tiles += (a.n_nodes * L.d3[k] + 15) / 16;
-  const int blocks = (tiles + 3) / 4 < 1024 ? (tiles + 3) / 4 : 1024;
-  hipLaunchKernelGGL((k_fc_contract<U, kH>), dim3(blocks), dim3(256), 0, a.stream, a.n_nodes, Sbuf, a.Theta,
+  hipLaunchKernelGGL((k_fc_contract<U, kH>), dim3(tiles), dim3(256), 0, a.stream, a.n_nodes, Sbuf, a.Theta,
                      SigF::NP, a.outdim, a.out, L);
   return hipGetLastError();
 }

@@ -8,7 +8,7 @@ import pytest
 import oracle
 from tests._common import dims_of
 from tests.test_gpu_parity import T, block_err, out_blocks, say
-from workloads import make_workload
+from workloads import make_fc_inputs, make_workload
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -33,9 +33,7 @@ def _case(U, graph, n, seed=0):
     if graph != "mid":
         gw = make_workload(graph, dims_of(op), seed=seed, n_nodes=n, graph_only=True)
         wl.src, wl.dst, wl.r = gw.src, gw.dst, gw.r
-    rng = np.random.default_rng(seed + 17)
-    R = rng.normal(size=(wl.n_edges, H)).astype(np.float32)
-    Th = (rng.normal(size=(H, op.n_paths, U, U)) / np.sqrt(H * U)).astype(np.float32)
+    R, Th = make_fc_inputs(wl.n_edges, op.n_paths, U, H, seed)
     return irr, op, wl, R, Th
 
 

@@ -160,3 +160,13 @@ def make_workload(name, dims, seed=0, n_nodes=None, graph_only=False):
         wl.w = _f32(rng.normal(size=(len(src), P, U)) * std)
     wl.g = _f32(rng.normal(size=(n, dims["outdim"])))
     return wl
+
+
+def make_fc_inputs(n_edges, n_paths, U, H=8, seed=0):
+    """Radial features R [E, H] (edge order of the workload) and channel-mixing
+    parameters Theta [H, P, U, U] of the fully connected per-edge-weight layer:
+    R ~ N(0, 1), Theta ~ N(0, 1/(H U)), float64 draws rounded to float32."""
+    rng = np.random.default_rng(seed + 17)
+    R = _f32(rng.normal(size=(n_edges, H)))
+    Th = _f32(rng.normal(size=(H, n_paths, U, U)) / np.sqrt(H * U))
+    return R, Th
