@@ -15,6 +15,9 @@ What it computes is the operator the pages describe in prose only:
   tensor products are different operations ("The Price of Freedom: Exploring
   Expressivity and Runtime Tradeoffs in Equivariant Tensor Products", ICML
   2025, Abstract);
+* separately, the Gaunt product (the pointwise product of spherical signals,
+  evaluated on a grid), which the same page sets apart as a cheaper and less
+  expressive operation (``gaunt.py``);
 * edge-conditioned, scatter-summed into receivers; edge-sized messages are a
   property of the schedule, not of the operator ("Sobek: Streaming Equivariant
   Tensor Product Convolutions", Abstract) -- so this oracle materialises
@@ -38,6 +41,7 @@ from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, bessel_basis_deriv, r
                    radial_mlp_bwd, uvw_mix_fwd, uvw_mix_bwd,
                    tp_conv_radial_fwd, tp_conv_radial_bwd, tp_conv_double_bwd)
 from .fc import fc_conv_fwd, fc_conv_bwd
+from .gaunt import sphere_quadrature, gaunt_coefficients, gaunt_plan, gaunt_conv_fwd
 
 __all__ = [
     "parse_irreps", "build_plan", "OraclePlan", "cg_complex",
@@ -46,5 +50,5 @@ __all__ = [
     "bessel_basis", "bessel_basis_deriv",
     "radial_mlp_fwd", "radial_mlp_bwd", "uvw_mix_fwd", "uvw_mix_bwd",
     "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd", "fc_conv_fwd",
-    "fc_conv_bwd",
+    "fc_conv_bwd", "sphere_quadrature", "gaunt_coefficients", "gaunt_plan", "gaunt_conv_fwd",
 ]

@@ -170,3 +170,11 @@ def make_fc_inputs(n_edges, n_paths, U, H=8, seed=0):
     R = _f32(rng.normal(size=(n_edges, H)))
     Th = _f32(rng.normal(size=(H, n_paths, U, U)) / np.sqrt(H * U))
     return R, Th
+
+
+def make_gaunt_weights(n_edges, lmax_sh, U, seed=0):
+    """Per-edge filter weights of the Gaunt (spherical-grid) convolution,
+    w [E, lmax_sh+1, U] (one weight per edge, filter degree and channel),
+    w ~ N(0, 1/(lmax_sh+1)) drawn in float64 and rounded to float32."""
+    rng = np.random.default_rng(seed + 29)
+    return _f32(rng.normal(size=(n_edges, lmax_sh + 1, U)) / np.sqrt(lmax_sh + 1))
