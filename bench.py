@@ -63,6 +63,14 @@ FC_WORKLOADS = {
            "15 paths, fully connected per-edge weights W_e = sum_h R_e[h] Theta[h] (8 radial "
            "features, 32x32 per path) by reassociation into receiver state, fwd"),
 }
+GAUNT_WORKLOADS = {
+    "gaunt": ("32x0e+32x1o+32x2e", 2, 2,
+              "1536 atoms, 46080 directed edges (the mid graph), 32x0e+32x1o+32x2e, real SH lmax 2, "
+              "Gaunt product (even couplings, outputs 0e+1o+2e) evaluated on a 32-point spherical "
+              "grid, filter weights per edge, degree and channel, fwd"),
+}
+GAUNT_SOURCES = ("gaunt.hip",)
+GAUNT_MFMA_PER_EDGE = 7          # 32x32x2 fp32 products per edge and 32-channel tile
 FP32_MFMA_PEAK_TFLOPS = 157.3
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_{}.txt")
 KERNEL_SOURCES = ("conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
@@ -241,7 +249,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mid",
-                    choices=sorted(WORKLOADS) + sorted(RADIAL_WORKLOADS) + sorted(FC_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(RADIAL_WORKLOADS) + sorted(FC_WORKLOADS)
+                    + sorted(GAUNT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time the steps back to back without the cache flush")
@@ -266,6 +275,8 @@ def main():
         return bench_radial(args, torch, tpc, make_workload, dev)
     if args.config in FC_WORKLOADS:
         return bench_fc(args, torch, tpc, make_workload, dev)
+    if args.config in GAUNT_WORKLOADS:
+        return bench_gaunt(args, torch, tpc, make_workload, dev)
     irreps, lsh, lout, desc = WORKLOADS[args.config]
     from workloads import CONFIGS
     fwd_only = "fwd+bwd" not in CONFIGS[args.config]["modes"]   # the lmax-3 layer is forward only
@@ -635,6 +646,96 @@ def bench_fc(args, torch, tpc, make_workload, dev):
                                "kind": "oracle",
                                "sample": f"{len(e)} of {E} edges (receiver order), harmonics + "
                                          f"fwd once, float64 (per-edge weights formed), {dt:.2f} s"}
+    print(json.dumps(res))
+
+
+def gaunt_algorithmic(N, E, U, xdim, ysh, wdim, outdim, Q):
+    """bytes each array moves once (row pointers, col, Y and w per edge; x and out
+    per node) and the matrix-core flops the grid schedule issues: per edge and
+    32-channel tile, f = x Yq (K 9 padded to 10) and g = w Z (K padded to 4) as
+    seven 32x32x2 products of 4,096 flops each."""
+    byts = 4.0 * (E * (1 + ysh + wdim) + (N + 1) + N * (xdim + outdim))
+    tiles = max(1, U // 32)
+    mfma = 2.0 * 32 * 32 * 2 * GAUNT_MFMA_PER_EDGE * E * tiles
+    return {"step": byts, "mfma_flops": mfma}
+
+
+def bench_gaunt(args, torch, tpc, make_workload, dev):
+    from workloads import make_gaunt_weights
+    irreps, lsh, lout, desc = GAUNT_WORKLOADS[args.config]
+    plan = tpc.Plan(irreps, lsh, lout, mode=tpc.TP_MODE_GAUNT)
+    outdim, wdim, Q = tpc.gaunt_dims(plan)
+    U = plan.mul
+    dims = dict(xdim=plan.xdim, n_paths=1, U=U, outdim=outdim, n_out_irreps=lout + 1)
+    wl = make_workload("mid", dims, seed=0)
+    N, E = wl.n_nodes, wl.n_edges
+    w = make_gaunt_weights(E, lsh, U, seed=0)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), N)
+    Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
+    ws_ = tpc.gather_rows(T(w.reshape(E, -1)), g.perm)
+    x = T(wl.x)
+    out = torch.empty(N, outdim, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def step():
+        tpc.forward_gaunt(plan, g, x, Y, ws_, out=out)
+
+    if args.counters:
+        counters_run(torch, dev, flush, step, args.config)
+        return
+    do_flush, timed_steps, timed_kernel = make_timers(torch, flush)
+    flush.fill_(1.0)
+    timed_steps(step, args.warmup, True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    t = timed_steps(step, args.steps, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    step_ms = float(np.median(t))
+    alg = gaunt_algorithmic(N, E, U, plan.xdim, plan.ysh, wdim, outdim, Q)
+    traffic = (read_traffic(args.config, GAUNT_SOURCES) or {}).get("gaunt_conv")
+    gbs = alg["step"] / (step_ms * 1e-3) / 1e9
+    tfs = alg["mfma_flops"] / (step_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": E / (step_ms * 1e-3), "unit": "edges/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; mid graph, random filter weights)",
+        "config": {"workload": f"{args.config}: {desc}", "n_nodes": N, "n_edges": E,
+                   "irreps": irreps, "out_irreps": plan.out_irreps, "grid_points": Q,
+                   "weights_per_edge": wdim, "mode": "fwd",
+                   "cache": "L2+MALL flushed before each step"},
+        "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
+        "compulsory_bytes": alg["step"],
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "wall_s_timed_region": wall,
+        "roofline": {"bound": "mfma", "kernel": "k_gaunt_conv (the one launch of the step)",
+                     "achieved": tfs, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tfs / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": alg["mfma_flops"],
+                     "note": "fp32 matrix-core flops issued per edge (signals on the grid); the "
+                             "compulsory bytes are in compulsory_bytes / hbm_frac",
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            threads = 1
+        gp = oracle.gaunt_plan(irreps, lsh, lout)
+        dts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.gaunt_conv_fwd(gp, wl.src, wl.dst, N, wl.x, oracle.sh_real(lsh, wl.r), w)
+            dts.append(time.perf_counter() - t0)
+        dt = float(np.median(dts))
+        res["cpu_baseline"] = {"value": E / dt, "unit": "edges/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"the whole workload ({E} edges), harmonics + Gaunt fwd, "
+                                         f"float64, median of 3 runs ({dt:.2f} s each)"}
     print(json.dumps(res))
 
 

@@ -68,7 +68,8 @@ typedef int32_t tp_status;
 #define TP_ERR_HIP (-6)         /* a HIP call failed; text in last_error */
 #define TP_ERR_INDEX (-7)       /* checked graph build found src/dst outside [0, N) */
 
-#define TP_MODE_UVU 0
+#define TP_MODE_UVU 0   /* channel-wise Clebsch-Gordan product over every path */
+#define TP_MODE_GAUNT 1 /* Gaunt (spherical-grid) product: tp_conv_forward_gaunt only */
 
 typedef struct tp_plan_s* tp_plan_t;
 
@@ -109,6 +110,8 @@ typedef struct {
  * multiplicity, natural parity) with harmonics up to lmax_sh, keeping output
  * degrees up to lmax_out, and selects the compiled kernel specialisation.
  * Source: path-aggregated sparse CG product ("FlashTP", Abstract).
+ * mode TP_MODE_GAUNT builds the plan of the Gaunt product instead (see
+ * tp_conv_forward_gaunt: even couplings only, no CG table, nnz = 0).
  * Returns TP_ERR_IRREPS / TP_ERR_UNSUPPORTED / TP_ERR_ARG on failure, in which
  * case *out is set to NULL. */
 tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lmax_sh,
@@ -220,6 +223,35 @@ tp_status tp_conv_fc_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial
 tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
                              const float* R, int32_t n_radial, const float* Theta, float* out,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Gaunt (spherical-grid) product: a different, cheaper operator ----------
+ * The Gaunt tensor product is not the CG product: it lacks the couplings with
+ * l1 + l2 + l3 odd (such as the cross product) and so is less expressive, and
+ * it can be evaluated on a spherical grid ("The Price of Freedom: Exploring
+ * Expressivity and Runtime Tradeoffs in Equivariant Tensor Products",
+ * Abstract).  It needs a plan created with mode TP_MODE_GAUNT (whose paths
+ * are the even couplings and whose output irreps are l = 0..lmax_out of
+ * parity (-1)^l); the CG entry points reject such a plan and the Gaunt ones
+ * reject a TP_MODE_UVU plan, so neither replaces the other silently.  Per channel u the sender's row is the signal
+ * f(s) = sum_{l,m} x[j,l,u,m] Y_lm(s), the edge the filter
+ * g(s) = sum_{l2} w[e][l2][u] sum_m Y[e][l2,m] Y_{l2 m}(s), and
+ *   out[i, l3, u, m3] = sum_{e into i} (1/4pi) int f g Y_{l3 m3} dOmega
+ *                     = sum_e sum_{l1,l2} w[e][l2][u] sum_{a,b} G[a,b,c] x[j,l1,u,a] Y[e][l2,b],
+ * G[a,b,c] = (1/4pi) int Y_a Y_b Y_c (component-normalised real harmonics).
+ * Output irreps: 0e, 1o, 2e, ... up to lmax_out, block l3 = [U][2l3+1] at
+ * column U*l3^2 (outdim = U (lmax_out+1)^2).  w is [E][lmax_sh+1][U] in
+ * receiver order.  Evaluated on a 32-point product grid (4 Gauss-Legendre
+ * nodes x 8 azimuths) that is exact for the degrees involved; per edge the
+ * two signals on the grid are formed on the matrix cores and multiplied
+ * pointwise into the receiver's grid values, which are projected once.
+ * Compiled for distinct input degrees <= 2 (natural parity, any order),
+ * lmax_sh <= 2, lmax_out <= 2 and U = 16, 32, 64 or 128; otherwise
+ * TP_ERR_UNSUPPORTED.  out is overwritten; isolated receivers get zeros.
+ * Deterministic (no atomics).  tp_conv_gaunt_dims reports outdim, the weights
+ * per edge ((lmax_sh+1) U) and the number of grid points. */
+tp_status tp_conv_gaunt_dims(tp_plan_t plan, int32_t* outdim, int32_t* wdim, int32_t* grid_points);
+tp_status tp_conv_forward_gaunt(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                const float* w, float* out, hipStream_t stream);
 
 /* ---- channel mix ("uvw", dense; fp32 MFMA) ----------------------------------
  * One U x U matrix per output irrep k (Wmix [K][U][U], K = number of output

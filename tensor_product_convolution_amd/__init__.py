@@ -20,6 +20,7 @@ STATUS_NAMES = {-1: "TP_ERR_ARG", -2: "TP_ERR_IRREPS", -3: "TP_ERR_UNSUPPORTED",
                 -4: "TP_ERR_OVERFLOW", -5: "TP_ERR_WORKSPACE", -6: "TP_ERR_HIP",
                 -7: "TP_ERR_INDEX"}
 TP_GRAPH_CHECK = 1
+TP_MODE_UVU, TP_MODE_GAUNT = 0, 1
 
 # every exported symbol of include/tpconv.h
 EXPORTS = (
@@ -29,7 +30,7 @@ EXPORTS = (
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
     "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
-    "tp_conv_forward_fc", "tp_conv_last_error",
+    "tp_conv_forward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_last_error",
 )
 
 
@@ -90,6 +91,8 @@ def lib():
         "tp_conv_sph_harm_backward": (I32, [I32, VP, I32, VP, VP, VP, VP]),
         "tp_conv_fc_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_forward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, SZ, VP]),
+        "tp_conv_gaunt_dims": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "tp_conv_forward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_double_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
                                           VP, VP, VP, VP]),
         "tp_conv_radial_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
@@ -365,6 +368,34 @@ def forward_fc(plan, graph, x, Y, R, Theta, out=None, ws=None):
     g = graph.cstruct()
     _check(lib().tp_conv_forward_fc(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(R), H,
                                     _ptr(Theta), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def gaunt_dims(plan):
+    """(outdim, weights per edge, grid points) of the Gaunt product of this plan"""
+    o, w, q = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().tp_conv_gaunt_dims(plan.handle, ctypes.byref(o), ctypes.byref(w), ctypes.byref(q)))
+    return o.value, w.value, q.value
+
+
+def forward_gaunt(plan, graph, x, Y, w, out=None):
+    """out [N, U (lmax_out+1)^2] of the Gaunt (spherical-grid) convolution:
+    receiver-sorted Y [E, ysh] and filter weights w [E, lmax_sh+1, U] (or [E, wdim])."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    outdim, wdim, _ = gaunt_dims(plan)
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    if w.dim() == 3:
+        _need(w, "w", torch.float32, (E, plan.lmax_sh + 1, plan.mul))
+    else:
+        _need(w, "w", torch.float32, (E, wdim))
+    if out is None:
+        out = torch.empty((N, outdim), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (N, outdim))
+    g = graph.cstruct()
+    _check(lib().tp_conv_forward_gaunt(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
+                                       _ptr(out), _stream(x.device)))
     return out
 
 

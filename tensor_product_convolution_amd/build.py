@@ -27,6 +27,11 @@ CFLAGS = [
 ]
 
 
+# per-source device flags: the Gaunt kernel multiplies matrix-core results
+# elementwise on the vector units, so they are kept in VGPRs (no AGPR copies)
+EXTRA = {"gaunt.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -34,7 +39,7 @@ def sources():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; harmless
     noise = "is not a recognized feature for this target"

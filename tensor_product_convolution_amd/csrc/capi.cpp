@@ -17,6 +17,7 @@
 #include "internal.hpp"
 
 struct tp_plan_s {
+  int mode = TP_MODE_UVU;
   int mul = 0;
   std::vector<int> ls;                 // input degrees, string order
   int lmax_sh = 0, lmax_out = 0;
@@ -133,12 +134,58 @@ tp_status tp_cg_real(int32_t l1, int32_t l2, int32_t l3, double* out) {
   return TP_OK;
 }
 
+static tp_status gaunt_supported(tp_plan_t plan, const char* who);
+
+// Gaunt-mode plan: the (l1, l2, l3) couplings with l1 + l2 + l3 even inside
+// the triangle (all others vanish), output irreps l = 0..lmax_out of parity
+// (-1)^l; no CG table and no CG kernels.
+static tp_status gaunt_plan_create(tp_plan_t* out, int mul, const std::vector<int>& ls, int lmax_sh,
+                                   int lmax_out, const tp_plan_opts* opts) {
+  if (opts && (opts->radial_basis || opts->radial_hidden || opts->uvw))
+    return set_error(TP_ERR_UNSUPPORTED, "Gaunt plans take no radial network or mix options");
+  auto* p = new tp_plan_s();
+  p->mode = TP_MODE_GAUNT;
+  p->mul = mul;
+  p->ls = ls;
+  p->lmax_sh = lmax_sh;
+  p->lmax_out = lmax_out;
+  tp_status s = gaunt_supported(p, "tp_conv_plan_create");
+  if (s != TP_OK) {
+    delete p;
+    return s;
+  }
+  for (size_t i = 0; i < ls.size(); ++i)
+    for (int l2 = 0; l2 <= lmax_sh; ++l2)
+      for (int l3 = std::abs(ls[i] - l2); l3 <= std::min(ls[i] + l2, lmax_out); ++l3)
+        if (((ls[i] + l2 + l3) & 1) == 0) p->paths.push_back({(int)i, ls[i], l2, l3, l3});
+  if (p->paths.empty()) {
+    delete p;
+    return set_error(TP_ERR_ARG, "no even coupling satisfies the triangle rule with these lmax");
+  }
+  for (int l = 0; l <= lmax_out; ++l) p->outs.push_back({l, (l & 1) ? -1 : 1});
+  for (int l : ls) p->xdim += mul * (2 * l + 1);
+  p->outdim = mul * (lmax_out + 1) * (lmax_out + 1);
+  p->ysh = (lmax_sh + 1) * (lmax_sh + 1);
+  p->nnz = 0;
+  p->uvw.n = (int)p->outs.size();
+  for (size_t k = 0; k < p->outs.size(); ++k) {
+    if (k) p->out_irreps += "+";
+    p->out_irreps += std::to_string(mul) + "x" + std::to_string(p->outs[k].first) +
+                     (p->outs[k].second == 1 ? "e" : "o");
+    p->uvw.dim[k] = 2 * p->outs[k].first + 1;
+    p->uvw.ko[k] = (int)(k * k);
+  }
+  *out = p;
+  return TP_OK;
+}
+
 tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lmax_sh,
                               int32_t lmax_out, int32_t mode, const tp_plan_opts* opts) {
   if (!out) return set_error(TP_ERR_ARG, "tp_conv_plan_create: out is NULL");
   *out = nullptr;
   if (!irreps_in) return set_error(TP_ERR_ARG, "tp_conv_plan_create: irreps_in is NULL");
-  if (mode != TP_MODE_UVU) return set_error(TP_ERR_UNSUPPORTED, "only mode TP_MODE_UVU (0) exists");
+  if (mode != TP_MODE_UVU && mode != TP_MODE_GAUNT)
+    return set_error(TP_ERR_UNSUPPORTED, "mode must be TP_MODE_UVU (0) or TP_MODE_GAUNT (1)");
   if (lmax_sh < 0 || lmax_out < 0 || lmax_sh > tpc::kMaxL || lmax_out > tpc::kMaxL)
     return set_error(TP_ERR_ARG, "lmax_sh and lmax_out must be in 0..6");
   std::vector<int> muls, ls, ps;
@@ -159,6 +206,8 @@ tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lma
     if (opts->radial_basis > 0 && !(opts->r_cut > 0.f))
       return set_error(TP_ERR_ARG, "r_cut must be positive");
   }
+
+  if (mode == TP_MODE_GAUNT) return gaunt_plan_create(out, muls[0], ls, lmax_sh, lmax_out, opts);
 
   auto* p = new tp_plan_s();
   p->mul = muls[0];
@@ -355,6 +404,7 @@ tp_status tp_conv_forward(tp_plan_t plan, const tp_graph* graph, const float* x,
   a.w = w;
   a.out = out;
   a.stream = stream;
+  if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_forward: not a channel-wise CG plan");
   hipError_t e = plan->ks->fwd(a);
   return e == hipSuccess ? TP_OK : tpc::hip_error(e, "tp_conv_forward launch");
 }
@@ -386,6 +436,7 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   a.grad_Y = grad_Y;
   a.grad_w = grad_w;
   a.stream = stream;
+  if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_backward: not a channel-wise CG plan");
   hipError_t e = plan->ks->bwd_recv(a);
   if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward receiver pass");
   e = plan->ks->bwd_send(a);
@@ -434,7 +485,7 @@ tp_status tp_conv_double_backward(tp_plan_t plan, const tp_graph* graph, const f
 }
 
 static const tpc::FcSet* find_fc(tp_plan_t plan, int n_radial) {
-  if (plan->ls == std::vector<int>{0, 1, 2} && plan->lmax_sh == 2 && plan->lmax_out == 2)
+  if (plan->mode == TP_MODE_UVU && plan->ls == std::vector<int>{0, 1, 2} && plan->lmax_sh == 2 && plan->lmax_out == 2)
     return tpc::fc_l012_s2(plan->mul, n_radial);
   return nullptr;
 }
@@ -481,6 +532,65 @@ tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float*
   a.stream = stream;
   hipError_t e = find_fc(plan, n_radial)->fwd(a);
   if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_forward_fc launch");
+  return TP_OK;
+}
+
+// ---- Gaunt (spherical-grid) product -----------------------------------------
+static tp_status gaunt_supported(tp_plan_t plan, const char* who) {
+  const int m = plan->mul;
+  if (std::string(who) != "tp_conv_plan_create" && plan->mode != TP_MODE_GAUNT)
+    return set_error(TP_ERR_UNSUPPORTED, std::string(who) + ": plan was not created with TP_MODE_GAUNT");
+  bool ok = (m == 16 || m == 32 || m == 64 || m == 128) && plan->lmax_sh <= 2 && plan->lmax_out <= 2 &&
+            !plan->ls.empty() && plan->ls.size() <= 3;
+  for (size_t a = 0; ok && a < plan->ls.size(); ++a) {
+    if (plan->ls[a] > 2) ok = false;
+    for (size_t b = 0; b < a; ++b)
+      if (plan->ls[a] == plan->ls[b]) ok = false;
+  }
+  if (!ok)
+    return set_error(TP_ERR_UNSUPPORTED, std::string(who) +
+                                             ": the Gaunt product is compiled for distinct input degrees <= 2, "
+                                             "lmax_sh and lmax_out <= 2, and 16, 32, 64 or 128 channels");
+  return TP_OK;
+}
+
+tp_status tp_conv_gaunt_dims(tp_plan_t plan, int32_t* outdim, int32_t* wdim, int32_t* grid_points) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_gaunt_dims: plan is NULL");
+  tp_status s = gaunt_supported(plan, "tp_conv_gaunt_dims");
+  if (s != TP_OK) return s;
+  if (outdim) *outdim = plan->mul * (plan->lmax_out + 1) * (plan->lmax_out + 1);
+  if (wdim) *wdim = plan->mul * (plan->lmax_sh + 1);
+  if (grid_points) *grid_points = tpc::gaunt_grid_points();
+  return TP_OK;
+}
+
+tp_status tp_conv_forward_gaunt(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                const float* w, float* out, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward_gaunt: plan is NULL");
+  tp_status s = gaunt_supported(plan, "tp_conv_forward_gaunt");
+  if (s != TP_OK) return s;
+  s = check_graph(graph, false);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && !out) return set_error(TP_ERR_ARG, "tp_conv_forward_gaunt: out NULL");
+  if (E > 0 && (!x || !Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_forward_gaunt: x/Y/w NULL");
+  tpc::GauntArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.U = plan->mul;
+  a.n_in = (int)plan->ls.size();
+  for (int b = 0; b < a.n_in; ++b) a.deg[b] = plan->ls[b];
+  a.lmax_sh = plan->lmax_sh;
+  a.lmax_out = plan->lmax_out;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.x = x;
+  a.Y = Y;
+  a.w = w;
+  a.out = out;
+  a.stream = stream;
+  hipError_t e = tpc::gaunt_forward(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_forward_gaunt launch");
   return TP_OK;
 }
 

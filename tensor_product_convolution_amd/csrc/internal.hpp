@@ -72,6 +72,19 @@ struct FcSet {
 };
 const FcSet* fc_l012_s2(int mul, int n_radial);
 
+// Gaunt (spherical-grid) product: input degrees deg[0..n_in) (distinct, <= 2),
+// filter degrees 0..lmax_sh (<= 2), output degrees 0..lmax_out (<= 2)
+struct GauntArgs {
+  int32_t n_nodes = 0, n_edges = 0, U = 0, n_in = 0, deg[3] = {0, 0, 0};
+  int32_t lmax_sh = 0, lmax_out = 0;
+  const int32_t *row_ptr = nullptr, *col = nullptr;
+  const float *x = nullptr, *Y = nullptr, *w = nullptr;
+  float* out = nullptr;
+  hipStream_t stream = nullptr;
+};
+hipError_t gaunt_forward(const GauntArgs& a);
+int gaunt_grid_points();
+
 const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul, int nb,
                              int nh);
 const RadialSet* radial_l012_s2(int mul, int nb, int nh);

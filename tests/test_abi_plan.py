@@ -166,3 +166,46 @@ def test_radial_uvw_forces_double_argument_errors_without_launch():
     assert L.tp_conv_plan_create(ctypes.byref(h), b"16x0e+16x1o", 2, 2, 0, ctypes.byref(o)) == -3
     o = tpc._Opts(0, 0, 0.0, 1)
     assert L.tp_conv_plan_create(ctypes.byref(h), b"24x0e+24x1o", 2, 2, 0, ctypes.byref(o)) == -3
+
+
+def test_fc_and_gaunt_host_validation_without_launch():
+    """Sizes and host validation of the fully connected and Gaunt entry points;
+    every error case returns before any HIP call."""
+    L = tpc.lib()
+    G = tpc.TP_MODE_GAUNT
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    g = tpc._Graph(4, 10, fake, fake, fake, fake, fake, fake)
+    sz = ctypes.c_size_t()
+    p = tpc.Plan("32x0e+32x1o+32x2e", 2, 2, mode=G)
+    # Gaunt plan: even couplings only, outputs 0e+1o+2e, no CG table
+    o = oracle.gaunt_plan("32x0e+32x1o+32x2e", 2, 2)
+    assert sorted(t[0:3] for t in p.paths()) == sorted(o.G)
+    assert p.out_irreps == o.out_irreps_str() and p.outdim == o.outdim and p.nnz == 0
+    # sizes: outdim U (lmax_out+1)^2, weights U (lmax_sh+1), a 32-point grid
+    assert tpc.gaunt_dims(p) == (32 * 9, 32 * 3, 32)
+    assert tpc.gaunt_dims(tpc.Plan("16x1o+16x0e", 1, 2, mode=G)) == (16 * 9, 16 * 2, 32)
+    assert tpc.gaunt_dims(tpc.Plan("64x2e", 1, 1, mode=G)) == (64 * 4, 64 * 2, 32)
+    h = ctypes.c_void_p()
+    for irr, lsh, lout in (("8x0e+8x1o", 2, 2), ("64x0e+64x1o+64x2e+64x3o", 3, 3),
+                           ("16x0e+16x1o", 3, 2), ("16x1o+16x1o", 2, 2)):
+        assert L.tp_conv_plan_create(ctypes.byref(h), irr.encode(), lsh, lout, G, None) == -3
+        assert not h.value
+    assert L.tp_conv_plan_create(ctypes.byref(h), b"16x2e", 0, 1, G, None) == -1   # no even coupling
+    # the CG entry points reject a Gaunt plan; the Gaunt ones reject a CG plan
+    cg = tpc.Plan("32x0e+32x1o+32x2e", 2, 2)
+    assert L.tp_conv_forward(p.handle, ctypes.byref(g), fake, fake, fake, fake, None) == -3
+    assert L.tp_conv_forward_gaunt(cg.handle, ctypes.byref(g), fake, fake, fake, fake, None) == -3
+    dims = [ctypes.c_int32() for _ in range(3)]
+    assert L.tp_conv_gaunt_dims(cg.handle, *[ctypes.byref(d) for d in dims]) == -3
+    assert L.tp_conv_fc_workspace(p.handle, 10, 8, ctypes.byref(sz)) == -3
+    assert L.tp_conv_forward_gaunt(p.handle, ctypes.byref(g), fake, None, fake, fake, None) == -1
+    assert L.tp_conv_forward_gaunt(p.handle, ctypes.byref(g), fake, fake, fake, None, None) == -1
+    assert L.tp_conv_forward_gaunt(p.handle, None, fake, fake, fake, fake, None) == -1
+    # fully connected: sizes, unsupported shapes, workspace and alignment
+    assert L.tp_conv_fc_workspace(cg.handle, 10, 8, ctypes.byref(sz)) == 0 and sz.value > 0
+    assert L.tp_conv_fc_workspace(cg.handle, 10, 4, ctypes.byref(sz)) == -3
+    assert L.tp_conv_forward_fc(cg.handle, ctypes.byref(g), fake, fake, fake, 8, fake, fake, fake,
+                                16, None) == -5
+    assert L.tp_conv_forward_fc(cg.handle, ctypes.byref(g), fake, fake, fake, 8, fake, fake, odd,
+                                1 << 30, None) == -1
