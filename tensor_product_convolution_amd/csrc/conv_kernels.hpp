@@ -530,13 +530,17 @@ __global__ void __launch_bounds__(WPB * 64)
       // senders of the next step to stage, loaded while this step computes
 #pragma unroll
       for (int r = 0; r < EPW; ++r) jn[r] = col[min(q0 + NBUF * SLOTS + r, last)];
-      const float m = q0 + slot < end ? 1.f : 0.f;
+      // only the receiver's last step can hold slots past its edges (they
+      // re-read its last edge); their weights are zeroed there alone
+      if (q0 + EPW > end) {
+        const float m = q0 + slot < end ? 1.f : 0.f;
 #pragma unroll
-      for (int cc = 0; cc < M::CPL; ++cc) {
+        for (int cc = 0; cc < M::CPL; ++cc)
 #pragma unroll
-        for (int p = 0; p < S::NP; ++p) wr[cc][p] *= m;
-        edge_fwd<S>(xr[cc], yr, wr[cc], acc[cc]);
+          for (int p = 0; p < S::NP; ++p) wr[cc][p] *= m;
       }
+#pragma unroll
+      for (int cc = 0; cc < M::CPL; ++cc) edge_fwd<S>(xr[cc], yr, wr[cc], acc[cc]);
     }
   }
   __syncthreads();   // staging buffers become the reduction buffer
@@ -711,7 +715,6 @@ __global__ void __launch_bounds__(WPB * 64)
       float yr[S::YC], wr[M::CPL][S::NP], gr[M::CPL][S::OC];
 #pragma unroll
       for (int b = 0; b < S::YC; ++b) yr[b] = Yv[b];
-      const float m = k0 + slot < end ? 1.f : 0.f;
 #pragma unroll
       for (int cc = 0; cc < M::CPL; ++cc) {
 #pragma unroll
@@ -729,12 +732,16 @@ __global__ void __launch_bounds__(WPB * 64)
         qn[r] = t_perm[min(k0 + NBUF * SLOTS + r, last)];
         in[r] = t_col[min(k0 + NBUF * SLOTS + r, last)];
       }
+      // only the sender's last step can hold slots past its edges
+      if (k0 + EPW > end) {
+        const float m = k0 + slot < end ? 1.f : 0.f;
 #pragma unroll
-      for (int cc = 0; cc < M::CPL; ++cc) {
+        for (int cc = 0; cc < M::CPL; ++cc)
 #pragma unroll
-        for (int p = 0; p < S::NP; ++p) wr[cc][p] *= m;
-        edge_bwd_send<S>(yr, wr[cc], gr[cc], gx[cc]);
+          for (int p = 0; p < S::NP; ++p) wr[cc][p] *= m;
       }
+#pragma unroll
+      for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_send<S>(yr, wr[cc], gr[cc], gx[cc]);
     }
   }
   __syncthreads();
