@@ -27,9 +27,11 @@ CFLAGS = [
 ]
 
 
-# per-source device flags: the Gaunt kernel multiplies matrix-core results
-# elementwise on the vector units, so they are kept in VGPRs (no AGPR copies)
-EXTRA = {"gaunt.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source device flags: these kernels use matrix-core results on the
+# vector units (elementwise products, cross-lane sums), so the accumulators
+# are kept in VGPRs (no AGPR copies)
+EXTRA = {"gaunt.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "fc_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

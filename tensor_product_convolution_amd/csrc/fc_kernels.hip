@@ -57,60 +57,119 @@ constexpr int comps(int p0, int n) {
 template <class S>
 constexpr int comp_off(int p0, int p) { return comps<S>(p0, p - p0); }
 
-// Phase 1.  One workgroup (4 waves) per receiver; wave w takes channel chunk
-// w % NCH and path group w / NCH.
+// contiguous path groups of about equal output-component counts (one group
+// per wave of the state kernel)
+template <class S, int NG>
+struct PathGroups {
+  int start[NG + 1];
+};
+template <class S, int NG>
+constexpr PathGroups<S, NG> make_groups() {
+  PathGroups<S, NG> g{};
+  const int total = comps<S>(0, S::NP);
+  int p = 0;
+  for (int k = 0; k < NG; ++k) {
+    g.start[k] = p;
+    const int target = (total * (k + 1) + NG - 1) / NG;
+    while (p < S::NP && (k == NG - 1 || comps<S>(0, p + 1) <= target)) ++p;
+  }
+  g.start[NG] = S::NP;
+  return g;
+}
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Phase 1.  One workgroup (4 waves) per receiver; wave w owns path group w.
+// v_mfma_f32_4x4x1_16b_f32 (16 independent 4 x 4 blocks, K = 1): block b =
+// lane / 4 takes A[i] from lane 4b + i, B[j] from lane 4b + j and keeps
+// D[i][j] in lane 4b + j, register i.  Lane l = (edge class l / U, channel
+// l % U); its block's rows are four of the H = 8 radial features (two
+// instructions per term: features 0-3 and 4-7), its columns four channels of
+// the same edge.  So each instruction adds R_e[h] T_e[u] for 64 / U edges x
+// U channels x 4 features with no idle rows, and the edge classes are summed
+// across lanes once at the end.  The receiver's sender indices, Y rows and R
+// rows are staged in LDS; x channels are gathered per step (BATCH steps at a
+// time; one measured best, since the accumulators already take most of the
+// registers).
 template <class S, int U, int H>
 __global__ void __launch_bounds__(256)
     k_fc_state(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ R,
                float* __restrict__ Sbuf, FcLayout lay) {
-  constexpr int NCH = U / 16, NGRP = 4 / NCH, PPG = (S::NP + NGRP - 1) / NGRP;
-  static_assert(NCH * NGRP == 4 && H <= 16, "fc tiling");
-  const int i = blockIdx.x;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int e16 = lane & 15, g = lane >> 4;
-  const int ch = wv % NCH, grp = wv / NCH;
-  const int u = 16 * ch + e16;
+  constexpr int EPI = 64 / U;                      // edges per instruction (edge classes)
+  constexpr int NG = 4;
+  constexpr int CH = 128;                          // edges staged in LDS at a time
+  constexpr int BATCH = 1;                         // steps whose gathers are in flight together
+  static_assert(H == 8 && (U == 16 || U == 32 || U == 64), "fc state tiling");
+  constexpr PathGroups<S, NG> PG = make_groups<S, NG>();
+  __shared__ int cs[CH];
+  __shared__ float ys[CH * S::YC];
+  __shared__ float rs[CH * H];
+  const int i = blockIdx.x, t = threadIdx.x;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
-  static_for<NGRP>([&](auto G) {
+  const int grp = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
+  const int ec = lane / U, u = lane % U, p4 = lane % 4;
+  static_for<NG>([&](auto G) {
     if (grp != G) return;
-    constexpr int P0 = G * PPG;
-    constexpr int NPP = S::NP - P0 < PPG ? S::NP - P0 : PPG;
-    constexpr int NT = comps<S>(P0, NPP);          // (path, component) tiles of this wave
-    f32x4 acc[NT];
+    constexpr int P0 = PG.start[G], NPP = PG.start[G + 1] - P0;
+    constexpr int NT = comps<S>(P0, NPP);
+    v4f acc[NT][2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int t0 = beg; t0 < end; t0 += 16) {
+    for (int k = 0; k < NT; ++k) acc[k][0] = acc[k][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = beg; c0 < end; c0 += CH) {
+      const int cn = end - c0 < CH ? end - c0 : CH;
+      __syncthreads();
+      for (int k = t; k < cn; k += 256) cs[k] = col[c0 + k];
+      for (int k = t; k < cn * S::YC; k += 256) ys[k] = Y[(size_t)c0 * S::YC + k];
+      for (int k = t; k < cn * H; k += 256) rs[k] = R[(size_t)c0 * H + k];
+      __syncthreads();
+      for (int s0 = 0; s0 * EPI < cn; s0 += BATCH) {
+        float xr[BATCH][S::XC];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int q = t0 + 4 * g + r;
-        const bool v = q < end;
-        const int qc = v ? q : end - 1;
-        // A: R[edge 4g + r][h = l%16] (zero rows past H and for a padded edge)
-        const float a = (v && e16 < H) ? R[(size_t)qc * H + e16] : 0.f;
-        float xr[S::XC], yr[S::YC];
-        load_x_channel<S, U>(x, col[qc], u, xr);
-#pragma unroll
-        for (int b = 0; b < S::YC; ++b) yr[b] = Y[(size_t)qc * S::YC + b];
-        // B: the CG terms of this edge and channel, one per (path, component)
-        float tv[NT];
-        static_for<NPP>([&](auto PP) {
-          constexpr PathInfo pi = S::paths.p[P0 + PP];
-          using T = CgPath<pi.l1, pi.l2, pi.l3>;
-          constexpr int D3 = 2 * pi.l3 + 1, OFF = comp_off<S>(P0, P0 + PP);
-          static_for<D3>([&](auto C) { tv[OFF + C] = 0.f; });
-          static_for<T::nnz>([&](auto N) {
-            constexpr Nz z = T::table.e[N];
-            tv[OFF + z.c] = fmaf(z.v, xr[pi.xo + z.a] * yr[pi.yo + z.b], tv[OFF + z.c]);
-          });
-        });
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = mfma_16x16x4(a, tv[t], acc[t]);
+        for (int bb = 0; bb < BATCH; ++bb) {
+          const int e = (s0 + bb) * EPI + ec;
+          load_x_channel<S, U>(x, cs[e < cn ? e : cn - 1], u, xr[bb]);
+        }
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bb = 0; bb < BATCH; ++bb) {
+          const int e = (s0 + bb) * EPI + ec;
+          const bool ok = e < cn;
+          const int ee = ok ? e : cn - 1;
+          float yr[S::YC];
+#pragma unroll
+          for (int b = 0; b < S::YC; ++b) yr[b] = ys[ee * S::YC + b];
+          const float a0 = ok ? rs[ee * H + p4] : 0.f, a1 = ok ? rs[ee * H + 4 + p4] : 0.f;
+          float tv[NT];
+          static_for<NPP>([&](auto PP) {
+            constexpr PathInfo pi = S::paths.p[P0 + PP];
+            using T = CgPath<pi.l1, pi.l2, pi.l3>;
+            constexpr int D3 = 2 * pi.l3 + 1, OFF = comp_off<S>(P0, P0 + PP);
+            static_for<D3>([&](auto C) { tv[OFF + C] = 0.f; });
+            static_for<T::nnz>([&](auto N) {
+              constexpr Nz z = T::table.e[N];
+              tv[OFF + z.c] = fmaf(z.v, xr[bb][pi.xo + z.a] * yr[pi.yo + z.b], tv[OFF + z.c]);
+            });
+          });
+#pragma unroll
+          for (int k = 0; k < NT; ++k) {
+            acc[k][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, tv[k], acc[k][0], 0, 0, 0);
+            acc[k][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, tv[k], acc[k][1], 0, 0, 0);
+          }
+        }
       }
     }
-    // S_k[(i, c)][(h, path of k, u)]: lane holds rows h = 4(l/16) + r of column u
-    if (g * 4 < H) {
+    // sum the edge classes (lanes u, u + U, ...), then lanes of class 0 store
+    // S_k[(i, c)][(h, path of k, u)] for h = 4 half + row
+#pragma unroll
+    for (int k = 0; k < NT; ++k)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int off = U; off < 64; off <<= 1) acc[k][hf][r] += __shfl_xor(acc[k][hf][r], off, 64);
+    if (ec == 0) {
       static_for<NPP>([&](auto PP) {
         constexpr int P = P0 + PP;
         constexpr PathInfo pi = S::paths.p[P];
@@ -120,10 +179,10 @@ __global__ void __launch_bounds__(256)
         float* Sk = Sbuf + lay.base[pi.k] + (size_t)i * D3 * KK;
         static_for<D3>([&](auto C) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int h = 4 * g + r;
-            if (h < H) Sk[(size_t)C * KK + (size_t)(h * NPK + PL) * U + u] = acc[OFF + C][r];
-          }
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              Sk[(size_t)C * KK + (size_t)((4 * hf + r) * NPK + PL) * U + u] = acc[OFF + C][hf][r];
         });
       });
     }
