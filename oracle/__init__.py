@@ -41,7 +41,8 @@ from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, bessel_basis_deriv, r
                    radial_mlp_bwd, uvw_mix_fwd, uvw_mix_bwd,
                    tp_conv_radial_fwd, tp_conv_radial_bwd, tp_conv_double_bwd)
 from .fc import fc_conv_fwd, fc_conv_bwd
-from .gaunt import sphere_quadrature, gaunt_coefficients, gaunt_plan, gaunt_conv_fwd
+from .gaunt import (sphere_quadrature, gaunt_coefficients, gaunt_plan, gaunt_conv_fwd,
+                    gaunt_conv_bwd)
 
 __all__ = [
     "parse_irreps", "build_plan", "OraclePlan", "cg_complex",
@@ -51,4 +52,5 @@ __all__ = [
     "radial_mlp_fwd", "radial_mlp_bwd", "uvw_mix_fwd", "uvw_mix_bwd",
     "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd", "fc_conv_fwd",
     "fc_conv_bwd", "sphere_quadrature", "gaunt_coefficients", "gaunt_plan", "gaunt_conv_fwd",
+    "gaunt_conv_bwd",
 ]

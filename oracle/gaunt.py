@@ -154,3 +154,41 @@ def gaunt_conv_fwd(gp, src, dst, n_nodes, x, Y, w):
             msg[:, o:o + U * (2 * l3 + 1)] += t.reshape(n, U * (2 * l3 + 1))
         np.add.at(out, dst[e], msg)
     return out
+
+
+def gaunt_conv_bwd(gp, src, dst, n_nodes, x, Y, w, g):
+    """Exact adjoint of ``gaunt_conv_fwd`` for the upstream gradient g [n_nodes,
+    outdim]: (grad_x [n_nodes, xdim], grad_Y [E, ysh], grad_w [E, lmax_sh+1, U]).
+    The forward is linear in each of x, Y and w, so each gradient is the
+    forward's coefficient sum with that operand left out."""
+    src = np.asarray(src, dtype=np.int64)
+    dst = np.asarray(dst, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float64)
+    Y = np.asarray(Y, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    E, U = len(src), gp.U
+    w = np.asarray(w, dtype=np.float64).reshape(E, gp.lmax_sh + 1, U)
+    if x.shape != (n_nodes, gp.xdim) or Y.shape != (E, gp.ysh) or g.shape != (n_nodes, gp.outdim):
+        raise ValueError("shape mismatch")
+    gx = np.zeros_like(x)
+    gY = np.zeros_like(Y)
+    gw = np.zeros_like(w)
+    for s in range(0, E, CHUNK):
+        e = slice(s, min(E, s + CHUNK))
+        n = e.stop - e.start
+        xe, Ye, we, ge = x[src[e]], Y[e], w[e], g[dst[e]]
+        gxe = np.zeros((n, gp.xdim))
+        for (l1, l2, l3), G in gp.G.items():
+            i = gp.degrees.index(l1)
+            xs = slice(gp.in_offsets[i], gp.in_offsets[i] + U * (2 * l1 + 1))
+            xa = xe[:, xs].reshape(n, U, 2 * l1 + 1)
+            yb = Ye[:, l2 * l2:(l2 + 1) ** 2]
+            o = gp.out_offsets[l3]
+            gc = ge[:, o:o + U * (2 * l3 + 1)].reshape(n, U, 2 * l3 + 1)
+            wl = we[:, l2, :]
+            # d/dw: sum over a, b, c;  d/dY: sum over u, a, c;  d/dx: sum over b, c
+            gw[e, l2, :] += np.einsum("abc,eua,eb,euc->eu", G, xa, yb, gc, optimize=True)
+            gY[e, l2 * l2:(l2 + 1) ** 2] += np.einsum("abc,eua,euc,eu->eb", G, xa, gc, wl, optimize=True)
+            gxe[:, xs] += np.einsum("abc,eb,euc,eu->eua", G, yb, gc, wl, optimize=True).reshape(n, -1)
+        np.add.at(gx, src[e], gxe)
+    return gx, gY, gw

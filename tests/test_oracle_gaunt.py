@@ -14,7 +14,7 @@ import pytest
 import scipy.sparse
 
 import oracle
-from oracle.gaunt import gaunt_coefficients, gaunt_conv_fwd, gaunt_plan, sphere_quadrature
+from oracle.gaunt import gaunt_coefficients, gaunt_conv_bwd, gaunt_conv_fwd, gaunt_plan, sphere_quadrature
 from tests._common import haar
 from workloads import make_gaunt_weights, make_workload
 
@@ -210,3 +210,38 @@ def test_plan_rejects_bad_irreps():
         gaunt_plan("4x0e+8x1o", 2, 2)
     with pytest.raises(ValueError):
         gaunt_plan("4x1o+4x1o", 2, 2)
+
+
+def test_backward_trilinearity():
+    # out is linear in each of x, Y, w: <g, out> = <grad_x, x> = <grad_Y, Y> = <grad_w, w>
+    gp, wl, Y, w = _case(n=20, seed=2)
+    rng = np.random.default_rng(9)
+    g = rng.normal(size=(wl.n_nodes, gp.outdim))
+    out = gaunt_conv_fwd(gp, wl.src, wl.dst, wl.n_nodes, wl.x, Y, w)
+    gx, gY, gw = gaunt_conv_bwd(gp, wl.src, wl.dst, wl.n_nodes, wl.x, Y, w, g)
+    ref = float(np.sum(g * out))
+    for got in (np.sum(gx * wl.x), np.sum(gY * Y), np.sum(gw * np.asarray(w, dtype=np.float64))):
+        assert abs(float(got) - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_backward_central_differences():
+    gp, wl, Y, w = _case(n=6, U=2, seed=3)
+    w = np.asarray(w, dtype=np.float64)
+    rng = np.random.default_rng(4)
+    g = rng.normal(size=(wl.n_nodes, gp.outdim))
+    x = wl.x.astype(np.float64)
+    gx, gY, gw = gaunt_conv_bwd(gp, wl.src, wl.dst, wl.n_nodes, x, Y, w, g)
+    f = lambda x_, Y_, w_: float(np.sum(g * gaunt_conv_fwd(gp, wl.src, wl.dst, wl.n_nodes, x_, Y_, w_)))
+    h = 1e-6
+    for arr, grad, name in ((x, gx, "x"), (Y, gY, "Y"), (w, gw, "w")):
+        flat = arr.reshape(-1)
+        for k in rng.choice(flat.size, size=min(12, flat.size), replace=False):
+            d = np.zeros_like(flat)
+            d[k] = h
+            args = {"x": x, "Y": Y, "w": w}
+            args[name] = (flat + d).reshape(arr.shape)
+            fp = f(args["x"], args["Y"], args["w"])
+            args[name] = (flat - d).reshape(arr.shape)
+            fm = f(args["x"], args["Y"], args["w"])
+            num = (fp - fm) / (2 * h)
+            assert abs(num - grad.reshape(-1)[k]) <= 1e-7 * max(1.0, abs(num)), (name, k)
