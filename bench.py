@@ -67,10 +67,9 @@ GAUNT_WORKLOADS = {
     "gaunt": ("32x0e+32x1o+32x2e", 2, 2,
               "1536 atoms, 46080 directed edges (the mid graph), 32x0e+32x1o+32x2e, real SH lmax 2, "
               "Gaunt product (even couplings, outputs 0e+1o+2e) evaluated on a 32-point spherical "
-              "grid, filter weights per edge, degree and channel, fwd"),
+              "grid, filter weights per edge, degree and channel, fwd+bwd"),
 }
 GAUNT_SOURCES = ("gaunt.hip",)
-GAUNT_MFMA_PER_EDGE = 7          # 32x32x2 fp32 products per edge and 32-channel tile
 FP32_MFMA_PEAK_TFLOPS = 157.3
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_{}.txt")
 KERNEL_SOURCES = ("conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
@@ -649,15 +648,23 @@ def bench_fc(args, torch, tpc, make_workload, dev):
     print(json.dumps(res))
 
 
-def gaunt_algorithmic(N, E, U, xdim, ysh, wdim, outdim, Q):
-    """bytes each array moves once (row pointers, col, Y and w per edge; x and out
-    per node) and the matrix-core flops the grid schedule issues: per edge and
-    32-channel tile, f = x Yq (K 9 padded to 10) and g = w Z (K padded to 4) as
-    seven 32x32x2 products of 4,096 flops each."""
-    byts = 4.0 * (E * (1 + ysh + wdim) + (N + 1) + N * (xdim + outdim))
+def gaunt_algorithmic(N, E, U, xdim, ysh, wdim, outdim):
+    """Per kernel of the Gaunt step: compulsory bytes (each array it must touch
+    once) and the fp32 matrix-core flops it issues (32x32x2 products of 4,096
+    flops per 32-channel tile): forward f = x Yq (5) and g = w Z (2) per edge;
+    receiver backward f (5) per edge plus gH (5) per receiver; sender backward
+    gH (5) and g (2) per edge."""
     tiles = max(1, U // 32)
-    mfma = 2.0 * 32 * 32 * 2 * GAUNT_MFMA_PER_EDGE * E * tiles
-    return {"step": byts, "mfma_flops": mfma}
+    fl = 2.0 * 32 * 32 * 2 * tiles
+    edge_in = 4.0 * E * (1 + ysh + wdim)            # col (or t_perm / t_col), Y, w
+    return {
+        "fwd": {"bytes": edge_in + 4.0 * (N + 1 + N * (xdim + outdim)), "flops": fl * 7 * E},
+        "bwd_recv": {"bytes": edge_in + 4.0 * E * (ysh + wdim) + 4.0 * (N + 1 + N * (xdim + outdim)),
+                     "flops": fl * (5 * E + 5 * N)},
+        "bwd_send": {"bytes": 4.0 * E * (2 + ysh + wdim) + 4.0 * (N + 1 + N * (xdim + outdim)),
+                     "flops": fl * 7 * E},
+        "step_bytes": 4.0 * E * (1 + 2 * ysh + 2 * wdim) + 4.0 * (N + 1 + 2 * N * (xdim + outdim)),
+    }
 
 
 def bench_gaunt(args, torch, tpc, make_workload, dev):
@@ -670,17 +677,25 @@ def bench_gaunt(args, torch, tpc, make_workload, dev):
     wl = make_workload("mid", dims, seed=0)
     N, E = wl.n_nodes, wl.n_edges
     w = make_gaunt_weights(E, lsh, U, seed=0)
+    go_h = np.random.default_rng(1).normal(size=(N, outdim)).astype(np.float32)
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     g = tpc.graph_build(T(wl.src), T(wl.dst), N)
     Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
     ws_ = tpc.gather_rows(T(w.reshape(E, -1)), g.perm)
-    x = T(wl.x)
+    x, go = T(wl.x), T(go_h)
     out = torch.empty(N, outdim, device=dev)
+    gx, gY, gw = torch.empty_like(x), torch.empty_like(Y), torch.empty_like(ws_)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
     def step():
         tpc.forward_gaunt(plan, g, x, Y, ws_, out=out)
+        tpc.backward_gaunt(plan, g, x, Y, ws_, go, outs=(gx, gY, gw))
 
+    kernels = {
+        "fwd": lambda: tpc.forward_gaunt(plan, g, x, Y, ws_, out=out),
+        "bwd_recv": lambda: tpc.backward_gaunt(plan, g, x, Y, ws_, go, outs=(None, gY, gw)),
+        "bwd_send": lambda: tpc.backward_gaunt(plan, g, x, Y, ws_, go, outs=(gx, None, None)),
+    }
     if args.counters:
         counters_run(torch, dev, flush, step, args.config)
         return
@@ -693,28 +708,33 @@ def bench_gaunt(args, torch, tpc, make_workload, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
     step_ms = float(np.median(t))
-    alg = gaunt_algorithmic(N, E, U, plan.xdim, plan.ysh, wdim, outdim, Q)
-    traffic = (read_traffic(args.config, GAUNT_SOURCES) or {}).get("gaunt_conv")
-    gbs = alg["step"] / (step_ms * 1e-3) / 1e9
-    tfs = alg["mfma_flops"] / (step_ms * 1e-3) / 1e12
+    reps, rounds = 10, max(2, args.steps // 5)
+    kt = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in kernels.items()}
+    alg = gaunt_algorithmic(N, E, U, plan.xdim, plan.ysh, wdim, outdim)
+    dom = max(kt, key=kt.get)
+    tfs = alg[dom]["flops"] / (kt[dom] * 1e-3) / 1e12
+    traffic = (read_traffic(args.config, GAUNT_SOURCES) or {}).get("gaunt_" + dom)
     res = {
         "metric": METRIC, "value": E / (step_ms * 1e-3), "unit": "edges/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded; mid graph, random filter weights)",
+        "data": "synthetic (seeded; mid graph, random filter weights and upstream gradient)",
         "config": {"workload": f"{args.config}: {desc}", "n_nodes": N, "n_edges": E,
                    "irreps": irreps, "out_irreps": plan.out_irreps, "grid_points": Q,
-                   "weights_per_edge": wdim, "mode": "fwd",
+                   "weights_per_edge": wdim, "mode": "fwd+bwd",
                    "cache": "L2+MALL flushed before each step"},
         "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
-        "compulsory_bytes": alg["step"],
-        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "kernel_ms": kt,
+        "fwd_edges_per_s": E / (kt["fwd"] * 1e-3),
+        "compulsory_bytes": alg["step_bytes"],
+        "hbm_frac_step": alg["step_bytes"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "hbm_frac_per_kernel": {n: alg[n]["bytes"] / (kt[n] * 1e-3) / 1e9 / HBM_PEAK_GBS for n in kt},
         "wall_s_timed_region": wall,
-        "roofline": {"bound": "mfma", "kernel": "k_gaunt_conv (the one launch of the step)",
+        "roofline": {"bound": "mfma", "kernel": dom,
                      "achieved": tfs, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tfs / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": alg["mfma_flops"],
-                     "note": "fp32 matrix-core flops issued per edge (signals on the grid); the "
-                             "compulsory bytes are in compulsory_bytes / hbm_frac",
+                     "frac": tfs / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": alg[dom]["flops"],
+                     "note": "fp32 matrix-core flops the kernel issues (signals on the grid); its "
+                             "compulsory bytes are in hbm_frac_per_kernel",
                      "traffic": traffic},
         "cpu_baseline": None,
     }
@@ -729,12 +749,14 @@ def bench_gaunt(args, torch, tpc, make_workload, dev):
         dts = []
         for _ in range(3):
             t0 = time.perf_counter()
-            oracle.gaunt_conv_fwd(gp, wl.src, wl.dst, N, wl.x, oracle.sh_real(lsh, wl.r), w)
+            Yo = oracle.sh_real(lsh, wl.r)
+            oracle.gaunt_conv_fwd(gp, wl.src, wl.dst, N, wl.x, Yo, w)
+            oracle.gaunt_conv_bwd(gp, wl.src, wl.dst, N, wl.x, Yo, w, go_h)
             dts.append(time.perf_counter() - t0)
         dt = float(np.median(dts))
         res["cpu_baseline"] = {"value": E / dt, "unit": "edges/s", "cores": int(threads),
                                "kind": "oracle",
-                               "sample": f"the whole workload ({E} edges), harmonics + Gaunt fwd, "
+                               "sample": f"the whole workload ({E} edges), harmonics + Gaunt fwd + bwd, "
                                          f"float64, median of 3 runs ({dt:.2f} s each)"}
     print(json.dumps(res))
 

@@ -253,6 +253,20 @@ tp_status tp_conv_gaunt_dims(tp_plan_t plan, int32_t* outdim, int32_t* wdim, int
 tp_status tp_conv_forward_gaunt(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
                                 const float* w, float* out, hipStream_t stream);
 
+/* Adjoint of tp_conv_forward_gaunt for grad_out = d<., out> [N][outdim]
+ * (NULL output: skip):
+ *   grad_x[j, l1, u, a] = sum_{e = (j -> i)} sum_{l2} w[e][l2][u] sum_{b,c} G[a,b,c] Y[e][l2,b] grad_out[i, l3, u, c]
+ *   grad_w[e][l2][u]    = sum_{l1,l3} sum_{a,b,c} G[a,b,c] x[j, l1, u, a] Y[e][l2,b] grad_out[i, l3, u, c]
+ *   grad_Y[e][l2, b]    = sum_u w[e][l2][u] sum_{l1,l3} sum_{a,c} G[a,b,c] x[j, l1, u, a] grad_out[i, l3, u, c]
+ * evaluated on the same grid (the adjoint of the projection puts grad_out on
+ * the grid): a receiver pass for grad_w and grad_Y (edge arrays in receiver
+ * order) and a sender pass for grad_x, which needs the graph's sender grouping
+ * (t_row_ptr, t_perm, t_col).  Outputs are overwritten; deterministic.  w must
+ * be 16-byte aligned (TP_ERR_ARG); other errors as tp_conv_forward_gaunt. */
+tp_status tp_conv_backward_gaunt(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                 const float* w, const float* grad_out, float* grad_x, float* grad_Y,
+                                 float* grad_w, hipStream_t stream);
+
 /* ---- channel mix ("uvw", dense; fp32 MFMA) ----------------------------------
  * One U x U matrix per output irrep k (Wmix [K][U][U], K = number of output
  * irreps, U = 16, 32, 64 or 128; 1e and 1o never mix):

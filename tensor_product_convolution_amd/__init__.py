@@ -30,7 +30,8 @@ EXPORTS = (
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
     "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
-    "tp_conv_forward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_last_error",
+    "tp_conv_forward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_backward_gaunt",
+    "tp_conv_last_error",
 )
 
 
@@ -93,6 +94,7 @@ def lib():
         "tp_conv_forward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, SZ, VP]),
         "tp_conv_gaunt_dims": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "tp_conv_forward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
+        "tp_conv_backward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
         "tp_conv_double_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
                                           VP, VP, VP, VP]),
         "tp_conv_radial_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
@@ -397,6 +399,29 @@ def forward_gaunt(plan, graph, x, Y, w, out=None):
     _check(lib().tp_conv_forward_gaunt(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
                                        _ptr(out), _stream(x.device)))
     return out
+
+
+def backward_gaunt(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=None):
+    """(grad_x, grad_Y, grad_w) of the Gaunt convolution for grad_out [N, outdim];
+    entries not in ``want`` are None (skipped on the device).  grad_w has w's shape."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    outdim, wdim, _ = gaunt_dims(plan)
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(w, "w", torch.float32, tuple(w.shape))
+    if w.numel() != E * wdim:
+        raise ValueError(f"w has {w.numel()} elements, expected {E * wdim}")
+    _need(grad_out, "grad_out", torch.float32, (N, outdim))
+    if outs is None:
+        outs = (torch.empty_like(x) if "x" in want else None,
+                torch.empty_like(Y) if "Y" in want else None,
+                torch.empty_like(w) if "w" in want else None)
+    gx, gY, gw = outs
+    g = graph.cstruct()
+    _check(lib().tp_conv_backward_gaunt(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
+                                        _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw), _stream(x.device)))
+    return gx, gY, gw
 
 
 def uvw_forward(plan, Wmix, x_in, out=None):

@@ -594,6 +594,45 @@ tp_status tp_conv_forward_gaunt(tp_plan_t plan, const tp_graph* graph, const flo
   return TP_OK;
 }
 
+tp_status tp_conv_backward_gaunt(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                 const float* w, const float* grad_out, float* grad_x, float* grad_Y,
+                                 float* grad_w, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward_gaunt: plan is NULL");
+  tp_status s = gaunt_supported(plan, "tp_conv_backward_gaunt");
+  if (s != TP_OK) return s;
+  s = check_graph(graph, grad_x != nullptr);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && !grad_out) return set_error(TP_ERR_ARG, "tp_conv_backward_gaunt: grad_out NULL");
+  if (E > 0 && (!x || !Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_backward_gaunt: x/Y/w NULL");
+  if (reinterpret_cast<uintptr_t>(w) & 15)
+    return set_error(TP_ERR_ARG, "tp_conv_backward_gaunt: w must be 16-byte aligned");
+  tpc::GauntArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.U = plan->mul;
+  a.n_in = (int)plan->ls.size();
+  for (int b = 0; b < a.n_in; ++b) a.deg[b] = plan->ls[b];
+  a.lmax_sh = plan->lmax_sh;
+  a.lmax_out = plan->lmax_out;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_perm = graph->t_perm;
+  a.t_col = graph->t_col;
+  a.x = x;
+  a.Y = Y;
+  a.w = w;
+  a.gout = grad_out;
+  a.grad_x = grad_x;
+  a.grad_Y = grad_Y;
+  a.grad_w = grad_w;
+  a.stream = stream;
+  hipError_t e = tpc::gaunt_backward(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward_gaunt launch");
+  return TP_OK;
+}
+
 static tp_status need_uvw(tp_plan_t plan) {
   const int m = plan->mul;
   if (m > 128 || (m & (m - 1)) || m < 16 || plan->outs.size() > 8)

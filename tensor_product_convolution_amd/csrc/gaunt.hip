@@ -46,6 +46,7 @@ constexpr int kBatch = 8;     // edges whose gathers one wave has in flight toge
 constexpr int kChunk = 256;   // edges whose sender index and Y row are staged in LDS at a time
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 struct GauntLayout {
   int n_in;         // input irreps (distinct degrees <= 2)
@@ -263,6 +264,314 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// ---- backward --------------------------------------------------------------
+// With gH_i[u][q] = sum_c P[c][q] gout_i[u][c] (the adjoint of the projection)
+// and the forward's signals f (sender) and g (filter) on the grid:
+//   grad_x[j][u][a]  = sum_q Yq[a][q] sum_{e = (j -> i)} gH_i[u][q] g_e[u][q]      (sender pass)
+//   grad_w[e][l2][u] = sum_q gH_i[u][q] f_j[u][q] Z_e[l2][q]                      (receiver pass)
+//   grad_Y[e][l2,m]  = sum_q Yq[l2m][q] sum_u gH_i[u][q] f_j[u][q] w_e[l2][u]     (receiver pass)
+// gH is one more 32x32x2 product per 32-channel tile (K = output harmonics).
+
+// A operand of a product over an output row (K index c = 2 ks + hk, padded to
+// 10): this lane's column offsets and the matching B values of a table
+__device__ __forceinline__ void out_operand(const GauntLayout& L, int U, int uc, int hk, int n,
+                                            const float (&tab)[9][kQ], int (&oo)[5], float (&bt)[5]) {
+  const int nc = (L.lout + 1) * (L.lout + 1);
+#pragma unroll
+  for (int ks = 0; ks < 5; ++ks) {
+    const int c = 2 * ks + hk;
+    const int l3 = c == 0 ? 0 : (c < 4 ? 1 : 2), m = c - l3 * l3;
+    const bool ok = c < nc;
+    oo[ks] = ok ? U * l3 * l3 + uc * (2 * l3 + 1) + m : 0;
+    bt[ks] = ok ? tab[c < 9 ? c : 8][n] : 0.f;
+  }
+}
+
+// Receiver pass: grad_w and grad_Y (either may be skipped).  One workgroup per
+// receiver; its four waves split the edges and every wave covers all channel
+// tiles.  Per edge and tile: f (five products), gg = gH f (elementwise); the
+// sum over channels for grad_Y is in-lane (the lane's 16 channels) plus one
+// cross-half exchange, then a butterfly over the 32 points; the sum over
+// points for grad_w goes through a per-wave LDS transpose of gg.
+template <int U, int NL2>
+__global__ void __launch_bounds__(256)
+    k_gaunt_bwd_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
+                     const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ w,
+                     const float* __restrict__ gout, float* __restrict__ grad_Y, float* __restrict__ grad_w,
+                     GauntLayout L) {
+  constexpr int NUT = U >= 32 ? U / 32 : 1;
+  constexpr int WD = NL2 * U;
+  constexpr int YS = NL2 * NL2;
+  constexpr int CR = WD <= 128 ? 32 : (WD <= 256 ? 16 : 8);   // edges staged per chunk
+  constexpr int NB = 4 / NUT;                                 // edges per wave batch
+  __shared__ int cs[CR];
+  __shared__ float ysm[CR * 9];
+  __shared__ __align__(16) float wsm[CR * WD];
+  __shared__ __align__(16) float tr[4][32][kHS];     // per-wave transpose of gg
+  __shared__ __align__(16) float zt[4][3][kQ];       // per-wave Z at the 32 points
+  __shared__ __align__(16) float yr[4][9][kHS];      // per-wave grad_Y terms at the 32 points
+  const int i = blockIdx.x, t = threadIdx.x;
+  const int beg = row_ptr[i], end = row_ptr[i + 1];
+  const int wave = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
+  const int n = lane % 32, hk = lane / 32;
+  float yv[9];
+#pragma unroll
+  for (int c = 0; c < 9; ++c) yv[c] = c_grid.y[c][n];
+  v16f zero;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+  // per tile: gH (this receiver's output gradient on the grid) and the
+  // operands of f
+  v16f gH[NUT];
+  int xo[NUT][5];
+  float bf[5];
+#pragma unroll
+  for (int ut = 0; ut < NUT; ++ut) {
+    const int u = 32 * ut + n, uc = u < U ? u : U - 1;
+    int oo[5];
+    float bp[5];
+    out_operand(L, U, uc, hk, n, c_grid.p, oo, bp);
+    gH[ut] = zero;
+#pragma unroll
+    for (int ks = 0; ks < 5; ++ks) gH[ut] = mfma32(gout[(size_t)i * L.outdim + oo[ks]], bp[ks], gH[ut]);
+#pragma unroll
+    for (int ks = 0; ks < 5; ++ks) {
+      const int a = 2 * ks + hk;
+      const int l = a == 0 ? 0 : (a < 4 ? 1 : 2), m = a - l * l;
+      int o = -1;
+      for (int b = 0; b < L.n_in; ++b)
+        if (L.deg[b] == l && a < 9) o = L.off[b] + uc * (2 * l + 1) + m;
+      if (ut == 0) bf[ks] = o >= 0 ? c_grid.y[a][n] : 0.f;
+      xo[ut][ks] = o >= 0 ? o : 0;
+    }
+  }
+  // one edge (k in the chunk, its sender row gathered in xa) for every tile
+  auto edge = [&](int c0, int k, const float (&xa)[NUT][5]) {
+    const size_t e = (size_t)(c0 + k);
+    float z[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int l2 = 0; l2 < NL2; ++l2)
+#pragma unroll
+      for (int m = 0; m < 2 * l2 + 1; ++m) z[l2] = fmaf(ysm[k * L.ysh + l2 * l2 + m], yv[l2 * l2 + m], z[l2]);
+    if (grad_w && hk == 0) {
+#pragma unroll
+      for (int l2 = 0; l2 < NL2; ++l2) zt[wave][l2][n] = z[l2];
+    }
+    float gz[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ut = 0; ut < NUT; ++ut) {
+      v16f f = mfma32(xa[ut][0], bf[0], zero);
+#pragma unroll
+      for (int ks = 1; ks < 5; ++ks) f = mfma32(xa[ut][ks], bf[ks], f);
+      v16f gg;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gg[r] = gH[ut][r] * f[r];
+      // rows of register r: channel 32 ut + 8 (r / 4) + 4 hk + r % 4
+      if (grad_Y) {
+#pragma unroll
+        for (int l2 = 0; l2 < NL2; ++l2)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int u0 = 32 * ut + 8 * q4 + 4 * hk;
+            if (u0 < U) {
+              const float4 w4 = *reinterpret_cast<const float4*>(&wsm[k * WD + l2 * U + u0]);
+              gz[l2] = fmaf(gg[4 * q4], w4.x, gz[l2]);
+              gz[l2] = fmaf(gg[4 * q4 + 1], w4.y, gz[l2]);
+              gz[l2] = fmaf(gg[4 * q4 + 2], w4.z, gz[l2]);
+              gz[l2] = fmaf(gg[4 * q4 + 3], w4.w, gz[l2]);
+            }
+          }
+      }
+      if (grad_w) {
+        // transpose gg through LDS: lane (point n, half hk) writes its 16
+        // channels; lane (channel n, half hk) then reads points 16 hk .. +15
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tr[wave][8 * (r / 4) + 4 * hk + r % 4][n] = gg[r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float gw[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const float4 v = reinterpret_cast<const float4*>(&tr[wave][n][16 * hk])[s4];
+#pragma unroll
+          for (int l2 = 0; l2 < NL2; ++l2) {
+            const float4 zz = reinterpret_cast<const float4*>(&zt[wave][l2][16 * hk])[s4];
+            gw[l2] = fmaf(v.x, zz.x, fmaf(v.y, zz.y, fmaf(v.z, zz.z, fmaf(v.w, zz.w, gw[l2]))));
+          }
+        }
+#pragma unroll
+        for (int l2 = 0; l2 < NL2; ++l2) gw[l2] += __shfl_xor(gw[l2], 32, 64);
+        if (hk == 0 && 32 * ut + n < U) {
+#pragma unroll
+          for (int l2 = 0; l2 < NL2; ++l2) grad_w[e * WD + l2 * U + 32 * ut + n] = gw[l2];
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    if (grad_Y) {
+      // channels of the other half; then the terms Yq[c][q] gZ[l2(c)][q] go
+      // through LDS and lane c < ysh adds its row over the 32 points
+#pragma unroll
+      for (int l2 = 0; l2 < NL2; ++l2) gz[l2] += __shfl_xor(gz[l2], 32, 64);
+      if (hk == 0) {
+#pragma unroll
+        for (int c = 0; c < YS; ++c) yr[wave][c][n] = yv[c] * gz[c == 0 ? 0 : (c < 4 ? 1 : 2)];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int c = n < YS ? n : 0;
+      float acc = 0.f;
+#pragma unroll
+      for (int s4 = 0; s4 < kQ / 4; ++s4) {
+        const float4 v = reinterpret_cast<const float4*>(yr[wave][c])[s4];
+        acc += (v.x + v.y) + (v.z + v.w);
+      }
+      if (hk == 0 && n < YS) grad_Y[e * L.ysh + n] = acc;
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+  for (int c0 = beg; c0 < end; c0 += CR) {
+    const int cn = end - c0 < CR ? end - c0 : CR;
+    __syncthreads();   // previous chunk consumed
+    for (int k = t; k < cn; k += 256) cs[k] = col[c0 + k];
+    for (int k = t; k < cn * L.ysh; k += 256) ysm[k] = Y[(size_t)c0 * L.ysh + k];
+    {
+      const float4* src = reinterpret_cast<const float4*>(w + (size_t)c0 * WD);
+      for (int k = t; k < cn * WD / 4; k += 256) reinterpret_cast<float4*>(wsm)[k] = src[k];
+    }
+    __syncthreads();
+    // batches of NB edges per wave: the sender rows of a batch are gathered
+    // before its products (slots past the chunk re-read its last edge, unused)
+    for (int k0 = wave; k0 < cn; k0 += 4 * NB) {
+      float xa[NB][NUT][5];
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        const int k = k0 + 4 * r < cn ? k0 + 4 * r : cn - 1;
+        const float* xj = x + (size_t)cs[k] * L.xdim;
+#pragma unroll
+        for (int ut = 0; ut < NUT; ++ut)
+#pragma unroll
+          for (int ks = 0; ks < 5; ++ks) xa[r][ut][ks] = xj[xo[ut][ks]];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < NB; ++r)
+        if (k0 + 4 * r < cn) edge(c0, k0 + 4 * r, xa[r]);
+    }
+  }
+}
+
+// Sender pass: grad_x.  The mirror of the forward: one workgroup per sender,
+// edges from the sender grouping (receiver-order position t_perm, receiver
+// t_col); per edge and tile gH of the receiver (five products on its output
+// gradient row) times the filter g (two products), summed on the grid and
+// projected once onto the sender's harmonics (no quadrature weights: the
+// adjoint of evaluating x on the grid).
+template <int U, int NL2>
+__global__ void __launch_bounds__(256)
+    k_gaunt_bwd_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
+                     const int32_t* __restrict__ t_col, const float* __restrict__ Y,
+                     const float* __restrict__ w, const float* __restrict__ gout, float* __restrict__ grad_x,
+                     GauntLayout L) {
+  constexpr int NUT = U >= 32 ? U / 32 : 1;
+  constexpr int WPT = 4 / NUT;
+  constexpr int WD = NL2 * U;
+  __shared__ __align__(16) float yt[10][kHS];
+  __shared__ __align__(16) float hs[4][32][kHS];
+  __shared__ int rs[kChunk], ps_[kChunk];
+  __shared__ float ysm[kChunk * 9];
+  const int j = blockIdx.x, t = threadIdx.x;
+  const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
+  const int wave = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
+  const int ut = wave / WPT, sub = wave % WPT;
+  const int n = lane % 32, hk = lane / 32;
+  float yv[9];
+#pragma unroll
+  for (int c = 0; c < 9; ++c) yv[c] = c_grid.y[c][n];
+  for (int k = t; k < 9 * kQ; k += 256) yt[k / kQ][k % kQ] = c_grid.y[k / kQ][k % kQ];
+  const int u = 32 * ut + n, uc = u < U ? u : U - 1;
+  int oo[5];
+  float bp[5];
+  out_operand(L, U, uc, hk, n, c_grid.p, oo, bp);
+  int wo[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) wo[ks] = (2 * ks + hk < NL2 ? (2 * ks + hk) * U : 0) + uc;
+  v16f h, zero;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    h[r] = 0.f;
+    zero[r] = 0.f;
+  }
+  for (int c0 = beg; c0 < end; c0 += kChunk) {
+    const int cn = end - c0 < kChunk ? end - c0 : kChunk;
+    __syncthreads();
+    for (int k = t; k < cn; k += 256) {
+      rs[k] = t_col[c0 + k];
+      ps_[k] = t_perm[c0 + k];
+    }
+    __syncthreads();
+    for (int k = t; k < cn * L.ysh; k += 256)
+      ysm[k] = Y[(size_t)ps_[k / L.ysh] * L.ysh + k % L.ysh];
+    __syncthreads();
+    for (int k = sub; k < cn; k += WPT) {
+      const float* gi = gout + (size_t)rs[k] * L.outdim;
+      const float* we = w + (size_t)ps_[k] * WD;
+      float ga[5], wa[2];
+#pragma unroll
+      for (int ks = 0; ks < 5; ++ks) ga[ks] = gi[oo[ks]];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) wa[ks] = __builtin_nontemporal_load(we + wo[ks]);
+      float z[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int l2 = 0; l2 < NL2; ++l2)
+#pragma unroll
+        for (int m = 0; m < 2 * l2 + 1; ++m) z[l2] = fmaf(ysm[k * L.ysh + l2 * l2 + m], yv[l2 * l2 + m], z[l2]);
+      const float zb0 = hk ? z[1] : z[0], zb1 = hk ? 0.f : z[2];
+      v16f gh = mfma32(ga[0], bp[0], zero);
+#pragma unroll
+      for (int ks = 1; ks < 5; ++ks) gh = mfma32(ga[ks], bp[ks], gh);
+      v16f g = mfma32(wa[0], zb0, zero);
+      g = mfma32(wa[1], zb1, g);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) h[r] = fmaf(gh[r], g[r], h[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) hs[wave][8 * (r / 4) + 4 * hk + r % 4][n] = h[r];
+  __syncthreads();
+  if (WPT > 1) {
+    for (int k = t; k < NUT * 32 * 32; k += 256) {
+      const int tw = (k / 1024) * WPT, row = (k / 32) % 32, q = k % 32;
+      float a = hs[tw][row][q];
+#pragma unroll
+      for (int s2 = 1; s2 < WPT; ++s2) a += hs[tw + s2][row][q];
+      hs[tw][row][q] = a;
+    }
+    __syncthreads();
+  }
+  // grad_x[j][block b][uu][m] = sum_q Yq[l_b^2 + m][q] H[uu][q]
+  for (int o = t; o < L.xdim; o += 256) {
+    int b = 0;
+    while (b + 1 < L.n_in && o >= L.off[b + 1]) ++b;
+    const int l = L.deg[b], d = 2 * l + 1, r = o - L.off[b];
+    const int uu = r / d, a = l * l + (r - uu * d);
+    const float4* hr = reinterpret_cast<const float4*>(hs[(uu / 32) * WPT][uu % 32]);
+    const float4* yr = reinterpret_cast<const float4*>(yt[a]);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kQ / 4; ++k) {
+      const float4 hv = hr[k], yq = yr[k];
+      acc = fmaf(hv.x, yq.x, acc);
+      acc = fmaf(hv.y, yq.y, acc);
+      acc = fmaf(hv.z, yq.z, acc);
+      acc = fmaf(hv.w, yq.w, acc);
+    }
+    grad_x[(size_t)j * L.xdim + o] = acc;
+  }
+}
+
 template <int U>
 hipError_t launch(const GauntArgs& a, const GauntLayout& L) {
   const dim3 blocks(a.n_nodes), threads(256);
@@ -283,12 +592,33 @@ hipError_t launch(const GauntArgs& a, const GauntLayout& L) {
   return hipGetLastError();
 }
 
+template <int U, int NL2>
+hipError_t launch_bwd_nl(const GauntArgs& a, const GauntLayout& L) {
+  const dim3 blocks(a.n_nodes), threads(256);
+  if (a.n_edges > 0 && (a.grad_w || a.grad_Y))
+    hipLaunchKernelGGL((k_gaunt_bwd_recv<U, NL2>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
+                       a.w, a.gout, a.grad_Y, a.grad_w, L);
+  if (a.grad_x)
+    hipLaunchKernelGGL((k_gaunt_bwd_send<U, NL2>), blocks, threads, 0, a.stream, a.t_row_ptr, a.t_perm,
+                       a.t_col, a.Y, a.w, a.gout, a.grad_x, L);
+  return hipGetLastError();
+}
+
+template <int U>
+hipError_t launch_bwd(const GauntArgs& a, const GauntLayout& L) {
+  switch (a.lmax_sh) {
+    case 0: return launch_bwd_nl<U, 1>(a, L);
+    case 1: return launch_bwd_nl<U, 2>(a, L);
+    default: return launch_bwd_nl<U, 3>(a, L);
+  }
+}
+
 }  // namespace
 
 int gaunt_grid_points() { return kQ; }
 
-hipError_t gaunt_forward(const GauntArgs& a) {
-  if (a.n_nodes == 0) return hipSuccess;
+namespace {
+GauntLayout make_layout(const GauntArgs& a) {
   GauntLayout L{};
   L.n_in = a.n_in;
   int off = 0;
@@ -301,11 +631,30 @@ hipError_t gaunt_forward(const GauntArgs& a) {
   L.ysh = (a.lmax_sh + 1) * (a.lmax_sh + 1);
   L.lout = a.lmax_out;
   L.outdim = a.U * (a.lmax_out + 1) * (a.lmax_out + 1);
+  return L;
+}
+}  // namespace
+
+hipError_t gaunt_forward(const GauntArgs& a) {
+  if (a.n_nodes == 0) return hipSuccess;
+  const GauntLayout L = make_layout(a);
   switch (a.U) {
     case 16: return launch<16>(a, L);
     case 32: return launch<32>(a, L);
     case 64: return launch<64>(a, L);
     case 128: return launch<128>(a, L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t gaunt_backward(const GauntArgs& a) {
+  if (a.n_nodes == 0) return hipSuccess;
+  const GauntLayout L = make_layout(a);
+  switch (a.U) {
+    case 16: return launch_bwd<16>(a, L);
+    case 32: return launch_bwd<32>(a, L);
+    case 64: return launch_bwd<64>(a, L);
+    case 128: return launch_bwd<128>(a, L);
     default: return hipErrorInvalidValue;
   }
 }

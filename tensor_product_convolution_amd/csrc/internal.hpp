@@ -80,9 +80,14 @@ struct GauntArgs {
   const int32_t *row_ptr = nullptr, *col = nullptr;
   const float *x = nullptr, *Y = nullptr, *w = nullptr;
   float* out = nullptr;
+  // backward: the upstream gradient, the sender grouping and the outputs (NULL: skip)
+  const float* gout = nullptr;
+  const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
+  float *grad_x = nullptr, *grad_Y = nullptr, *grad_w = nullptr;
   hipStream_t stream = nullptr;
 };
 hipError_t gaunt_forward(const GauntArgs& a);
+hipError_t gaunt_backward(const GauntArgs& a);
 int gaunt_grid_points();
 
 const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul, int nb,

@@ -202,6 +202,17 @@ def test_fc_and_gaunt_host_validation_without_launch():
     assert L.tp_conv_forward_gaunt(p.handle, ctypes.byref(g), fake, None, fake, fake, None) == -1
     assert L.tp_conv_forward_gaunt(p.handle, ctypes.byref(g), fake, fake, fake, None, None) == -1
     assert L.tp_conv_forward_gaunt(p.handle, None, fake, fake, fake, fake, None) == -1
+    # Gaunt backward: plan mode, the sender grouping for grad_x, grad_out, w alignment
+    gg = tpc._Graph(4, 10, fake, fake, fake, None, None, None)
+    assert L.tp_conv_backward_gaunt(cg.handle, ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake,
+                                    None) == -3
+    assert L.tp_conv_backward_gaunt(p.handle, ctypes.byref(gg), fake, fake, fake, fake, fake, None, None,
+                                    None) == -1                                      # no t_row_ptr
+    assert L.tp_conv_backward_gaunt(p.handle, ctypes.byref(g), fake, fake, fake, None, None, fake, fake,
+                                    None) == -1                                      # no grad_out
+    assert L.tp_conv_backward_gaunt(p.handle, ctypes.byref(g), fake, fake, odd, fake, None, fake, fake,
+                                    None) == -1
+    assert "aligned" in L.tp_conv_last_error().decode()
     # fully connected: sizes, unsupported shapes, workspace and alignment
     assert L.tp_conv_fc_workspace(cg.handle, 10, 8, ctypes.byref(sz)) == 0 and sz.value > 0
     assert L.tp_conv_fc_workspace(cg.handle, 10, 4, ctypes.byref(sz)) == -3

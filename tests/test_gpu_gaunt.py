@@ -87,3 +87,67 @@ def test_gaunt_deterministic_isolated_and_empty(tpc):
     assert block_err(a, _ref(gp, wl, w), _blocks(gp)) <= TOL
     wl.src, wl.dst, wl.r = wl.src[:0], wl.dst[:0], wl.r[:0]
     assert np.all(_gpu(tpc, irr, 2, 2, wl, w[:0]) == 0)
+
+
+def _gpu_bwd(tpc, irr, lsh, lout, wl, w, go, want=("x", "Y", "w")):
+    plan = tpc.Plan(irr, lsh, lout, mode=tpc.TP_MODE_GAUNT)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
+    ws = tpc.gather_rows(T(w.reshape(w.shape[0], w.shape[1] * w.shape[2])), g.perm)
+    res = tpc.backward_gaunt(plan, g, T(wl.x), Y, ws, T(go), want=want)
+    torch.cuda.synchronize()
+    return [None if r is None else r.cpu().numpy() for r in res], g.perm.cpu().numpy()
+
+
+def _bwd_blocks(gp, E):
+    xb = [slice(o, o + gp.U * (2 * l + 1)) for l, o in zip(gp.degrees, gp.in_offsets)]
+    yb = [slice(l * l, (l + 1) ** 2) for l in range(gp.lmax_sh + 1)]
+    wb = [slice(l * gp.U, (l + 1) * gp.U) for l in range(gp.lmax_sh + 1)]
+    return xb, yb, wb
+
+
+@pytest.mark.parametrize("U,irr_t,lsh,lout,graph,n", [
+    (16, "{U}x0e+{U}x1o+{U}x2e", 2, 2, "tiny", 32),
+    (32, "{U}x0e+{U}x1o+{U}x2e", 2, 2, "mid", 300),
+    (32, "{U}x0e+{U}x1o+{U}x2e", 2, 2, "zipf", 400),
+    (64, "{U}x0e+{U}x1o+{U}x2e", 2, 2, "lmax3", 200),
+    (128, "{U}x0e+{U}x1o+{U}x2e", 2, 2, "mid", 120),
+    (32, "{U}x1o+{U}x0e", 1, 2, "mid", 150),
+    (16, "{U}x2e", 1, 1, "mid", 150),
+    (32, "{U}x0e+{U}x1o+{U}x2e", 2, 2, "mid", 1536),
+])
+def test_gaunt_backward_parity(tpc, U, irr_t, lsh, lout, graph, n):
+    irr = irr_t.format(U=U)
+    say(f"gaunt backward {irr} lsh={lsh} lout={lout} graph={graph} n={n}")
+    gp, wl, w = _case(irr, lsh, lout, graph, n)
+    go = np.random.default_rng(11).normal(size=(wl.n_nodes, gp.outdim)).astype(np.float32)
+    (gx, gY, gw), perm = _gpu_bwd(tpc, irr, lsh, lout, wl, w, go)
+    rx, rY, rw = oracle.gaunt_conv_bwd(gp, wl.src, wl.dst, wl.n_nodes, wl.x,
+                                       oracle.sh_real(lsh, wl.r), w, go)
+    xb, yb, wb = _bwd_blocks(gp, wl.n_edges)
+    assert block_err(gx, rx, xb) <= TOL
+    assert block_err(gY, rY[perm], yb) <= TOL
+    assert block_err(gw, rw.reshape(len(rw), -1)[perm], wb) <= TOL
+
+
+def test_gaunt_backward_subsets_isolated_empty_deterministic(tpc):
+    say("gaunt backward output subsets, isolated nodes, empty graph, determinism")
+    irr = "32x0e+32x1o+32x2e"
+    gp, wl, w = _case(irr, 2, 2, "mid", 90, seed=5)
+    keep = (wl.dst >= 10) & (wl.src >= 5)     # receivers 0..9 and senders 0..4 isolated
+    wl.src, wl.dst, wl.r, w = wl.src[keep], wl.dst[keep], wl.r[keep], w[keep]
+    go = np.random.default_rng(12).normal(size=(wl.n_nodes, gp.outdim)).astype(np.float32)
+    (gx, gY, gw), perm = _gpu_bwd(tpc, irr, 2, 2, wl, w, go)
+    (gx2, gY2, gw2), _ = _gpu_bwd(tpc, irr, 2, 2, wl, w, go)
+    assert np.array_equal(gx, gx2) and np.array_equal(gY, gY2) and np.array_equal(gw, gw2)
+    assert np.all(gx[:5] == 0)
+    rx, rY, rw = oracle.gaunt_conv_bwd(gp, wl.src, wl.dst, wl.n_nodes, wl.x, oracle.sh_real(2, wl.r), w, go)
+    xb, yb, wb = _bwd_blocks(gp, wl.n_edges)
+    (sx, sY, sw), _ = _gpu_bwd(tpc, irr, 2, 2, wl, w, go, want=("w",))
+    assert sx is None and sY is None and np.array_equal(sw, gw)
+    (sx, sY, sw), _ = _gpu_bwd(tpc, irr, 2, 2, wl, w, go, want=("x", "Y"))
+    assert sw is None and np.array_equal(sx, gx) and np.array_equal(sY, gY)
+    assert block_err(gx, rx, xb) <= TOL
+    wl.src, wl.dst, wl.r = wl.src[:0], wl.dst[:0], wl.r[:0]
+    (gx, gY, gw), _ = _gpu_bwd(tpc, irr, 2, 2, wl, w[:0], go)
+    assert np.all(gx == 0) and gY.size == 0 and gw.size == 0
