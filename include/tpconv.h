@@ -224,6 +224,24 @@ tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float*
                              const float* R, int32_t n_radial, const float* Theta, float* out,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Adjoint of tp_conv_forward_fc for grad_out = d<., out> [N][outdim] (NULL
+ * output: skip): grad_x [N][xdim], grad_Y [E][ysh] and grad_R [E][n_radial]
+ * (receiver order), grad_Theta [n_radial][P][U][U].  Reassociated like the
+ * forward (Sobek, Abstract: the streaming schedule covers the backward too):
+ * the state's gradient gS_i = Theta gout_i is a dense product per receiver; a
+ * receiver pass forms grad_R = <gS_i, T_e> and the CG adjoint for grad_Y; a
+ * sender pass accumulates the sender-side state Q_j = sum_e R_e (x) G_e
+ * (G_e: the CG adjoint terms of gout_i and Y_e), and grad_x = Theta^T Q_j; the
+ * forward's state S is recomputed for grad_Theta = sum S^T gout.  No per-edge
+ * weight matrix or message is formed.  ws: tp_conv_fc_backward_workspace
+ * bytes, 16-byte aligned; grad_x needs the graph's sender grouping.  Errors as
+ * tp_conv_forward_fc.  Deterministic. */
+tp_status tp_conv_fc_backward_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial, size_t* bytes);
+tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                              const float* R, int32_t n_radial, const float* Theta, const float* grad_out,
+                              float* grad_x, float* grad_Y, float* grad_R, float* grad_Theta, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
 /* ---- Gaunt (spherical-grid) product: a different, cheaper operator ----------
  * The Gaunt tensor product is not the CG product: it lacks the couplings with
  * l1 + l2 + l3 odd (such as the cross product) and so is less expressive, and

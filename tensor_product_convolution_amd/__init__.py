@@ -30,7 +30,7 @@ EXPORTS = (
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
     "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
-    "tp_conv_forward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_backward_gaunt",
+    "tp_conv_forward_fc", "tp_conv_fc_backward_workspace", "tp_conv_backward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_backward_gaunt",
     "tp_conv_last_error",
 )
 
@@ -92,6 +92,9 @@ def lib():
         "tp_conv_sph_harm_backward": (I32, [I32, VP, I32, VP, VP, VP, VP]),
         "tp_conv_fc_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_forward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, SZ, VP]),
+        "tp_conv_fc_backward_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
+        "tp_conv_backward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, VP, VP, VP, VP,
+                                      SZ, VP]),
         "tp_conv_gaunt_dims": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "tp_conv_forward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_backward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
@@ -422,6 +425,40 @@ def backward_gaunt(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=No
     _check(lib().tp_conv_backward_gaunt(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
                                         _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw), _stream(x.device)))
     return gx, gY, gw
+
+
+def fc_backward_workspace(plan, n_nodes, n_radial):
+    """bytes of the node-sized states backward_fc needs"""
+    b = ctypes.c_size_t()
+    _check(lib().tp_conv_fc_backward_workspace(plan.handle, n_nodes, n_radial, ctypes.byref(b)))
+    return b.value
+
+
+def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "Theta"), ws=None):
+    """(grad_x, grad_Y, grad_R, grad_Theta) of the fully connected convolution;
+    entries not in ``want`` are None (skipped on the device)."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    H = R.shape[1]
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(R, "R", torch.float32, (E, H))
+    _need(Theta, "Theta", torch.float32, (H, plan.n_paths, plan.mul, plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    nbytes = fc_backward_workspace(plan, N, H)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    elif ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
+    gx = torch.empty_like(x) if "x" in want else None
+    gY = torch.empty_like(Y) if "Y" in want else None
+    gR = torch.empty_like(R) if "R" in want else None
+    gT = torch.empty_like(Theta) if "Theta" in want else None
+    g = graph.cstruct()
+    _check(lib().tp_conv_backward_fc(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(R), H, _ptr(Theta),
+                                     _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gR), _ptr(gT), _ptr(ws),
+                                     ws.numel(), _stream(x.device)))
+    return gx, gY, gR, gT
 
 
 def uvw_forward(plan, Wmix, x_in, out=None):

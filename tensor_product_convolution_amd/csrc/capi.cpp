@@ -535,6 +535,59 @@ tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float*
   return TP_OK;
 }
 
+tp_status tp_conv_fc_backward_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial, size_t* bytes) {
+  if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_fc_backward_workspace: NULL argument");
+  if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_fc_backward_workspace: negative size");
+  const tpc::FcSet* fs = find_fc(plan, n_radial);
+  if (!fs || !fs->bwd_workspace)
+    return set_error(TP_ERR_UNSUPPORTED, "no compiled fully connected kernel (supported: 0e+1o+2e / "
+                                         "lmax 2 with 16 or 32 channels and 8 radial features)");
+  *bytes = fs->bwd_workspace(n_nodes);
+  return TP_OK;
+}
+
+tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                              const float* R, int32_t n_radial, const float* Theta, const float* grad_out,
+                              float* grad_x, float* grad_Y, float* grad_R, float* grad_Theta, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward_fc: plan is NULL");
+  size_t need = 0;
+  tp_status s = tp_conv_fc_backward_workspace(plan, graph ? graph->n_nodes : 0, n_radial, &need);
+  if (s != TP_OK) return s;
+  s = check_graph(graph, grad_x != nullptr);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && (!grad_out || !Theta)) return set_error(TP_ERR_ARG, "tp_conv_backward_fc: grad_out/Theta NULL");
+  if (E > 0 && (!x || !Y || !R)) return set_error(TP_ERR_ARG, "tp_conv_backward_fc: x/Y/R NULL");
+  if (ws_bytes < need || (need > 0 && !ws))
+    return set_error(TP_ERR_WORKSPACE, "tp_conv_backward_fc: workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 15)
+    return set_error(TP_ERR_ARG, "tp_conv_backward_fc: ws must be 16-byte aligned");
+  tpc::FcArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.outdim = plan->outdim;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_perm = graph->t_perm;
+  a.t_col = graph->t_col;
+  a.x = x;
+  a.Y = Y;
+  a.R = R;
+  a.Theta = Theta;
+  a.gout = grad_out;
+  a.grad_x = grad_x;
+  a.grad_Y = grad_Y;
+  a.grad_R = grad_R;
+  a.grad_Theta = grad_Theta;
+  a.ws = ws;
+  a.stream = stream;
+  hipError_t e = find_fc(plan, n_radial)->bwd(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward_fc launch");
+  return TP_OK;
+}
+
 // ---- Gaunt (spherical-grid) product -----------------------------------------
 static tp_status gaunt_supported(tp_plan_t plan, const char* who) {
   const int m = plan->mul;

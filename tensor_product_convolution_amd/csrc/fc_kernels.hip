@@ -195,7 +195,10 @@ __global__ void __launch_bounds__(256)
 // (the order of a sum over K is free), so each lane reads its row with one
 // 16-byte load per four steps.  Rows of all irreps are enumerated irrep by
 // irrep (blockIdx.x).
-template <int U, int H>
+// TRANS: the product with Theta transposed in its two channel indices (the
+// backward's grad_x, whose state rows carry output channels v and whose
+// columns are input channels u).
+template <int U, int H, bool TRANS>
 __global__ void __launch_bounds__(256)
     k_fc_contract(int n_nodes, const float* __restrict__ Sbuf, const float* __restrict__ Theta, int P,
                   int outdim, float* __restrict__ out, FcLayout lay) {
@@ -224,7 +227,9 @@ __global__ void __launch_bounds__(256)
   // t = K / U is uniform over the wave and Theta's row block is a scalar base.
   for (int t = K0 / U; t < (K0 + kq) / U; ++t) {
     const int pl = t % npk, h = t / npk;
-    const float* thb = Theta + ((size_t)h * P + lay.pg[k][pl]) * U * U + e16;
+    // element (row uu, column col) of this (h, path) block of Theta
+    constexpr int RS = TRANS ? 1 : U, CS = TRANS ? U : 1;
+    const float* thb = Theta + ((size_t)h * P + lay.pg[k][pl]) * U * U + e16 * CS;
     const float* ab = arow + (size_t)t * U + 4 * g;
 #pragma unroll
     for (int ub = 0; ub < U; ub += 16) {
@@ -232,9 +237,9 @@ __global__ void __launch_bounds__(256)
       const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const float* th = thb + (size_t)(ub + 4 * g + st) * U;
+        const float* th = thb + (size_t)(ub + 4 * g + st) * RS;
 #pragma unroll
-        for (int n = 0; n < NV; ++n) acc[n] = mfma_16x16x4(av[st], th[16 * n], acc[n]);
+        for (int n = 0; n < NV; ++n) acc[n] = mfma_16x16x4(av[st], th[16 * n * CS], acc[n]);
       }
     }
   }
@@ -262,6 +267,364 @@ __global__ void __launch_bounds__(256)
       }
     }
   }
+}
+
+// ---- backward ----------------------------------------------------------------
+// With gS_i[h,p,u,c] = sum_v Theta[h,p,u,v] gout_i[k(p),v,c] (the state's
+// gradient) and T_e the forward's CG terms:
+//   grad_Theta[h,p,u,v] = sum_{i,c} S_i[h,p,u,c] gout_i[k,v,c]            (k_fc_gradtheta)
+//   grad_R[e][h]        = sum_{p,u,c} gS_i[h,p,u,c] T_e[p,u,c]             (k_fc_bwd_recv)
+//   grad_Y[e]           = CG adjoint of T with gT_e = sum_h R_e[h] gS_i     (k_fc_bwd_recv)
+//   grad_x[j][u][a]     = sum_{h,p,v} Theta[h,p,u,v] Q_j[h,p,v,a],
+//   Q_j[h,p,v,a]        = sum_{e = (j -> i)} R_e[h] sum_{b,c} C_p[a,b,c] Y_e[b] gout_i[k,v,c]
+// The last is the forward's reassociation mirrored onto the sender side: Q is
+// a sender-side state (k_fc_bwd_send, on the same 4x4x1 products) followed by
+// the dense contraction with Theta transposed (k_fc_contract<TRANS>).  No
+// per-edge weight matrix or message is formed.
+
+// gS_k[(i,c)][(h,pl,u)] = sum_v gout[i][k][v][c] Theta[h,pg,u,v]: one
+// workgroup per 16-row tile of one output irrep, its waves taking column
+// tiles in turn; A = the tile's gout rows (K = v), B = Theta.
+template <int U, int H>
+__global__ void __launch_bounds__(256)
+    k_fc_expand(int n_nodes, const float* __restrict__ gout, const float* __restrict__ Theta, int P,
+                int outdim, float* __restrict__ gS, FcLayout lay) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e16 = lane & 15, g = lane >> 4;
+  int k = 0, first = 0;
+  while (k + 1 < lay.n_out && (int)blockIdx.x >= first + (n_nodes * lay.d3[k] + 15) / 16) {
+    first += (n_nodes * lay.d3[k] + 15) / 16;
+    ++k;
+  }
+  const int d3 = lay.d3[k], npk = lay.npk[k];
+  const int KK = H * npk * U, rows = n_nodes * d3;
+  const int row0 = ((int)blockIdx.x - first) * 16;
+  const int ra = row0 + e16;
+  const bool va = ra < rows;
+  const int node = (va ? ra : rows - 1) / d3, c = (va ? ra : rows - 1) % d3;
+  // A[row e16][v = 4 ks + g]
+  float av[U / 4];
+#pragma unroll
+  for (int ks = 0; ks < U / 4; ++ks)
+    av[ks] = va ? gout[(size_t)node * outdim + (size_t)U * lay.ko[k] + (4 * ks + g) * d3 + c] : 0.f;
+  for (int ct = wv; ct < KK / 16; ct += 4) {
+    // columns K = 16 ct + e16 = (h npk + pl) U + uu; a 16-block shares (h, pl)
+    const int t = (16 * ct) / U, uu = (16 * ct) % U + e16;
+    const int pl = t % npk, h = t / npk;
+    const float* th = Theta + (((size_t)h * P + lay.pg[k][pl]) * U + uu) * U + g;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < U / 4; ++ks) acc = mfma_16x16x4(av[ks], th[4 * ks], acc);
+    // D[row 4g + r][column e16]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 4 * g + r;
+      if (row < rows) gS[lay.base[k] + (size_t)row * KK + 16 * ct + e16] = acc[r];
+    }
+  }
+}
+
+// Partial sums of grad_Theta_k[K][v] = sum_rows S_k[row][K] gout_k[row][v]
+// over a block of kRowBlock rows: one wave per 16-column K tile (M = K, N = v,
+// the sum over rows as K = 4 per product).  part_k[block][K][v].
+constexpr int kRowBlock = 256;
+template <int U, int H>
+__global__ void __launch_bounds__(256)
+    k_fc_gradtheta(int n_nodes, const float* __restrict__ Sbuf, const float* __restrict__ gout, int outdim,
+                   float* __restrict__ part, FcLayout lay, FcLayout plan_part) {
+  constexpr int NV = U / 16;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e16 = lane & 15, g = lane >> 4;
+  // blocks: irrep by irrep, then (row block, group of four K tiles)
+  int k = 0, first = 0;
+  auto nblk = [&](int kk) {
+    const int rows = n_nodes * lay.d3[kk];
+    return ((rows + kRowBlock - 1) / kRowBlock) * ((H * lay.npk[kk] * U / 16 + 3) / 4);
+  };
+  while (k + 1 < lay.n_out && (int)blockIdx.x >= first + nblk(k)) {
+    first += nblk(k);
+    ++k;
+  }
+  const int d3 = lay.d3[k], npk = lay.npk[k];
+  const int KK = H * npk * U, rows = n_nodes * d3;
+  const int nkq = (KK / 16 + 3) / 4;
+  const int b = (int)blockIdx.x - first;
+  const int rb = b / nkq, kt = (b % nkq) * 4 + wv;
+  if (kt >= KK / 16) return;
+  const int K0 = 16 * kt;
+  f32x4 acc[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r_end = min(rows, (rb + 1) * kRowBlock);
+  for (int r0 = rb * kRowBlock; r0 < r_end; r0 += 4) {
+    const int r = r0 + g;
+    const bool ok = r < r_end;
+    const int rr = ok ? r : r_end - 1;
+    const int node = rr / d3, c = rr % d3;
+    const float a = ok ? Sbuf[lay.base[k] + (size_t)rr * KK + K0 + e16] : 0.f;
+    const float* gr = gout + (size_t)node * outdim + (size_t)U * lay.ko[k] + c;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) acc[n] = mfma_16x16x4(a, ok ? gr[(16 * n + e16) * d3] : 0.f, acc[n]);
+  }
+  // D[K = K0 + 4g + r][v = 16 n + e16]
+  float* pk = part + plan_part.base[k] + (size_t)rb * KK * U;
+#pragma unroll
+  for (int n = 0; n < NV; ++n)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pk[(size_t)(K0 + 4 * g + r) * U + 16 * n + e16] = acc[n][r];
+}
+
+// output irrep and position among that irrep's paths, per path
+struct PathMap {
+  int k[16], pl[16];
+};
+
+// grad_Theta[h][p][u][v] = sum over row blocks of part_k[block][(h npk + pl) U + u][v]
+template <int U, int H>
+__global__ void __launch_bounds__(256)
+    k_fc_gradtheta_sum(int n_nodes, const float* __restrict__ part, int P, float* __restrict__ gTheta,
+                       FcLayout lay, FcLayout plan_part, PathMap pm) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= H * P * U * U) return;
+  const int v = idx % U, u = (idx / U) % U, p = (idx / (U * U)) % P, h = idx / (U * U * P);
+  const int k = pm.k[p], pl = pm.pl[p];
+  const int KK = H * lay.npk[k] * U;
+  const int nrb = (n_nodes * lay.d3[k] + kRowBlock - 1) / kRowBlock;
+  const float* pk = part + plan_part.base[k] + (size_t)((h * lay.npk[k] + pl) * U + u) * U + v;
+  float a = 0.f;
+  for (int rb = 0; rb < nrb; ++rb) a += pk[(size_t)rb * KK * U];
+  gTheta[idx] = a;
+}
+
+// Receiver pass: grad_R and grad_Y.  One workgroup per receiver, one wave per
+// path group (as the state kernel); the receiver's gS for the group sits in
+// registers (8 features x the group's output components per lane).  Per edge
+// and lane: the CG terms T, gT = R gS, the partial of grad_R (sum over the
+// group's components) and of grad_Y (CG adjoint with gT); both are summed over
+// the edge's channel lanes, then over the groups through LDS.
+template <class S, int U, int H>
+__global__ void __launch_bounds__(256)
+    k_fc_bwd_recv(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
+                  const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ R,
+                  const float* __restrict__ gS, float* __restrict__ grad_Y, float* __restrict__ grad_R,
+                  FcLayout lay) {
+  constexpr int EPI = 64 / U, NG = 4, CH = 64, NR = H + S::YC;
+  constexpr PathGroups<S, NG> PG = make_groups<S, NG>();
+  __shared__ int cs[CH];
+  __shared__ float ys[CH * S::YC];
+  __shared__ float rs[CH * H];
+  __shared__ float red[NG][CH][NR];
+  const int i = blockIdx.x, t = threadIdx.x;
+  const int beg = row_ptr[i], end = row_ptr[i + 1];
+  const int grp = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
+  const int ec = lane / U, u = lane % U;
+  static_for<NG>([&](auto G) {
+    if (grp != G) return;
+    constexpr int P0 = PG.start[G], NPP = PG.start[G + 1] - P0;
+    constexpr int NT = comps<S>(P0, NPP);
+    float gs[NT][H];
+    static_for<NPP>([&](auto PP) {
+      constexpr int P = P0 + PP;
+      constexpr PathInfo pi = S::paths.p[P];
+      constexpr int D3 = 2 * pi.l3 + 1, OFF = comp_off<S>(P0, P);
+      constexpr int NPK = paths_into<S>(pi.k), PL = path_local<S>(P);
+      constexpr int KK = H * NPK * U;
+      const float* gk = gS + lay.base[pi.k] + (size_t)i * D3 * KK;
+      static_for<D3>([&](auto C) {
+#pragma unroll
+        for (int h = 0; h < H; ++h) gs[OFF + C][h] = gk[(size_t)C * KK + (size_t)(h * NPK + PL) * U + u];
+      });
+    });
+    for (int c0 = beg; c0 < end; c0 += CH) {
+      const int cn = end - c0 < CH ? end - c0 : CH;
+      __syncthreads();
+      for (int k = t; k < cn; k += 256) cs[k] = col[c0 + k];
+      for (int k = t; k < cn * S::YC; k += 256) ys[k] = Y[(size_t)c0 * S::YC + k];
+      for (int k = t; k < cn * H; k += 256) rs[k] = R[(size_t)c0 * H + k];
+      __syncthreads();
+      for (int s0 = 0; s0 * EPI < cn; ++s0) {
+        const int e = s0 * EPI + ec;
+        const bool ok = e < cn;
+        const int ee = ok ? e : cn - 1;
+        float xr[S::XC], yr[S::YC], rr[H];
+        load_x_channel<S, U>(x, cs[ee], u, xr);
+#pragma unroll
+        for (int b = 0; b < S::YC; ++b) yr[b] = ys[ee * S::YC + b];
+#pragma unroll
+        for (int h = 0; h < H; ++h) rr[h] = rs[ee * H + h];
+        float acc[NR];
+#pragma unroll
+        for (int q = 0; q < NR; ++q) acc[q] = 0.f;
+        static_for<NPP>([&](auto PP) {
+          constexpr PathInfo pi = S::paths.p[P0 + PP];
+          using T = CgPath<pi.l1, pi.l2, pi.l3>;
+          constexpr int D3 = 2 * pi.l3 + 1, OFF = comp_off<S>(P0, P0 + PP);
+          float tv[D3], gt[D3];
+          static_for<D3>([&](auto C) {
+            tv[C] = 0.f;
+            float a = 0.f;
+#pragma unroll
+            for (int h = 0; h < H; ++h) a = fmaf(rr[h], gs[OFF + C][h], a);
+            gt[C] = a;
+          });
+          static_for<T::nnz>([&](auto N) {
+            constexpr Nz z = T::table.e[N];
+            tv[z.c] = fmaf(z.v, xr[pi.xo + z.a] * yr[pi.yo + z.b], tv[z.c]);
+            acc[H + pi.yo + z.b] = fmaf(z.v, xr[pi.xo + z.a] * gt[z.c], acc[H + pi.yo + z.b]);
+          });
+          static_for<D3>([&](auto C) {
+#pragma unroll
+            for (int h = 0; h < H; ++h) acc[h] = fmaf(gs[OFF + C][h], tv[C], acc[h]);
+          });
+        });
+        // sum over the edge's U channel lanes
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
+#pragma unroll
+          for (int off = 1; off < U; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
+        if (ok && u == 0) {
+#pragma unroll
+          for (int q = 0; q < NR; ++q) red[G][e][q] = acc[q];
+        }
+      }
+      __syncthreads();
+      for (int k = t; k < cn * NR; k += 256) {
+        const int e = k / NR, q = k % NR;
+        const float v = (red[0][e][q] + red[1][e][q]) + (red[2][e][q] + red[3][e][q]);
+        if (q < H) {
+          if (grad_R) grad_R[(size_t)(c0 + e) * H + q] = v;
+        } else if (grad_Y) {
+          grad_Y[(size_t)(c0 + e) * S::YC + (q - H)] = v;
+        }
+      }
+    }
+  });
+}
+
+// sender-side path groups: balanced input components (Q's accumulators)
+template <class S>
+constexpr int comps_in(int p0, int n) {
+  int t = 0;
+  for (int q = p0; q < p0 + n; ++q) t += 2 * S::paths.p[q].l1 + 1;
+  return t;
+}
+template <class S>
+constexpr int paths_from(int b) {
+  int n = 0;
+  for (int q = 0; q < S::NP; ++q)
+    if (S::paths.p[q].in == b) ++n;
+  return n;
+}
+template <class S>
+constexpr int path_local_in(int p) {
+  int n = 0;
+  for (int q = 0; q < p; ++q)
+    if (S::paths.p[q].in == S::paths.p[p].in) ++n;
+  return n;
+}
+template <class S, int NG>
+constexpr PathGroups<S, NG> make_groups_in() {
+  PathGroups<S, NG> g{};
+  const int total = comps_in<S>(0, S::NP);
+  int p = 0;
+  for (int k = 0; k < NG; ++k) {
+    g.start[k] = p;
+    const int target = (total * (k + 1) + NG - 1) / NG;
+    while (p < S::NP && (k == NG - 1 || comps_in<S>(0, p + 1) <= target)) ++p;
+  }
+  g.start[NG] = S::NP;
+  return g;
+}
+
+// Sender pass: Q_j[h][p][v][a] = sum_{e out of j} R_e[h] G_e[p][v][a],
+// G_e[p][v][a] = sum_{b,c} C_p[a,b,c] Y_e[b] gout_i[k(p)][v][c].  The state
+// kernel's layout with the sender grouping: one workgroup per sender, one
+// wave per path group, lane = (edge class, output channel v), 4x4x1 products
+// of R (rows) and G (columns); Q is written once per sender in the layout of
+// the input irreps: Q_b[(j, a)][(h, path of b, v)].
+template <class S, int U, int H>
+__global__ void __launch_bounds__(256)
+    k_fc_bwd_send(int n_nodes, const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
+                  const int32_t* __restrict__ t_col, const float* __restrict__ Y, const float* __restrict__ R,
+                  const float* __restrict__ gout, float* __restrict__ Qbuf, FcLayout lin) {
+  constexpr int EPI = 64 / U, NG = 4, CH = 128;
+  constexpr PathGroups<S, NG> PG = make_groups_in<S, NG>();
+  __shared__ int rc[CH];
+  __shared__ float ys[CH * S::YC];
+  __shared__ float rs[CH * H];
+  const int j = blockIdx.x, t = threadIdx.x;
+  const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
+  const int grp = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
+  const int ec = lane / U, v = lane % U, p4 = lane % 4;
+  static_for<NG>([&](auto G) {
+    if (grp != G) return;
+    constexpr int P0 = PG.start[G], NPP = PG.start[G + 1] - P0;
+    constexpr int NT = comps_in<S>(P0, NPP);
+    v4f acc[NT][2];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) acc[k][0] = acc[k][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = beg; c0 < end; c0 += CH) {
+      const int cn = end - c0 < CH ? end - c0 : CH;
+      __syncthreads();
+      for (int k = t; k < cn; k += 256) rc[k] = t_col[c0 + k];
+      for (int k = t; k < cn * S::YC; k += 256)
+        ys[k] = Y[(size_t)t_perm[c0 + k / S::YC] * S::YC + k % S::YC];
+      for (int k = t; k < cn * H; k += 256) rs[k] = R[(size_t)t_perm[c0 + k / H] * H + k % H];
+      __syncthreads();
+      for (int s0 = 0; s0 * EPI < cn; ++s0) {
+        const int e = s0 * EPI + ec;
+        const bool ok = e < cn;
+        const int ee = ok ? e : cn - 1;
+        float gr[S::OC], yr[S::YC];
+        load_o_channel<S, U>(gout, rc[ee], v, gr);
+#pragma unroll
+        for (int b = 0; b < S::YC; ++b) yr[b] = ys[ee * S::YC + b];
+        const float a0 = ok ? rs[ee * H + p4] : 0.f, a1 = ok ? rs[ee * H + 4 + p4] : 0.f;
+        float gt[NT];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) gt[q] = 0.f;
+        static_for<NPP>([&](auto PP) {
+          constexpr PathInfo pi = S::paths.p[P0 + PP];
+          using T = CgPath<pi.l1, pi.l2, pi.l3>;
+          constexpr int OFF = comps_in<S>(P0, PP);
+          static_for<T::nnz>([&](auto N) {
+            constexpr Nz z = T::table.e[N];
+            gt[OFF + z.a] = fmaf(z.v, yr[pi.yo + z.b] * gr[pi.ko + z.c], gt[OFF + z.a]);
+          });
+        });
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+          acc[q][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, gt[q], acc[q][0], 0, 0, 0);
+          acc[q][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, gt[q], acc[q][1], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int off = U; off < 64; off <<= 1) acc[q][hf][r] += __shfl_xor(acc[q][hf][r], off, 64);
+    if (ec == 0) {
+      static_for<NPP>([&](auto PP) {
+        constexpr int P = P0 + PP;
+        constexpr PathInfo pi = S::paths.p[P];
+        constexpr int D1 = 2 * pi.l1 + 1, OFF = comps_in<S>(P0, PP);
+        constexpr int NPB = paths_from<S>(pi.in), PL = path_local_in<S>(P);
+        constexpr int KK = H * NPB * U;
+        float* Qb = Qbuf + lin.base[pi.in] + (size_t)j * D1 * KK;
+        static_for<D1>([&](auto A) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              Qb[(size_t)A * KK + (size_t)((4 * hf + r) * NPB + PL) * U + v] = acc[OFF + A][hf][r];
+        });
+      });
+    }
+  });
 }
 
 using SigF = Sig<2, 2, 0, 1, 2>;
@@ -293,6 +656,50 @@ size_t fc_ws(int n_nodes) {
   return (size_t)tot * sizeof(float);
 }
 
+// the input-irrep layout of the sender-side state Q (and of grad_x)
+template <int U>
+FcLayout make_layout_in(int n_nodes) {
+  FcLayout L{};
+  L.n_out = SigF::NIN;
+  long long off = 0;
+  for (int b = 0; b < SigF::NIN; ++b) {
+    L.d3[b] = 2 * SigF::ls.v[b] + 1;
+    L.ko[b] = SigF::xoff(b);
+    int n = 0;
+    for (int p = 0; p < SigF::NP; ++p)
+      if (SigF::paths.p[p].in == b) L.pg[b][n++] = p;
+    L.npk[b] = n;
+    L.base[b] = off;
+    off += (long long)n_nodes * L.d3[b] * kH * n * U;
+  }
+  return L;
+}
+
+// offsets of the grad_Theta partial sums per output irrep
+template <int U>
+FcLayout make_layout_part(int n_nodes) {
+  const FcLayout L = make_layout<U>(n_nodes);
+  FcLayout P{};
+  P.n_out = L.n_out;
+  long long off = 0;
+  for (int k = 0; k < L.n_out; ++k) {
+    P.base[k] = off;
+    const long long nrb = ((long long)n_nodes * L.d3[k] + kRowBlock - 1) / kRowBlock;
+    off += nrb * kH * L.npk[k] * U * U;
+  }
+  P.base[L.n_out] = off;   // total (the layout has room for 8 irreps; this signature has 5)
+  return P;
+}
+
+template <int U>
+size_t fc_bwd_ws(int n_nodes) {
+  const FcLayout Li = make_layout_in<U>(n_nodes);
+  const FcLayout Lp = make_layout_part<U>(n_nodes);
+  long long q = 0;
+  for (int b = 0; b < Li.n_out; ++b) q += (long long)n_nodes * Li.d3[b] * kH * Li.npk[b] * U;
+  return 2 * fc_ws<U>(n_nodes) + (size_t)(q + Lp.base[Lp.n_out]) * sizeof(float);
+}
+
 template <int U>
 hipError_t launch_fc_fwd(const FcArgs& a) {
   if (a.n_nodes == 0) return hipSuccess;
@@ -302,14 +709,64 @@ hipError_t launch_fc_fwd(const FcArgs& a) {
                      a.col, a.x, a.Y, a.R, Sbuf, L);
   int tiles = 0;
   for (int k = 0; k < L.n_out; ++k) tiles += (a.n_nodes * L.d3[k] + 15) / 16;
-  hipLaunchKernelGGL((k_fc_contract<U, kH>), dim3(tiles), dim3(256), 0, a.stream, a.n_nodes, Sbuf, a.Theta,
+  hipLaunchKernelGGL((k_fc_contract<U, kH, false>), dim3(tiles), dim3(256), 0, a.stream, a.n_nodes, Sbuf, a.Theta,
                      SigF::NP, a.outdim, a.out, L);
   return hipGetLastError();
 }
 
 template <int U>
+hipError_t launch_fc_bwd(const FcArgs& a) {
+  if (a.n_nodes == 0) return hipSuccess;
+  const FcLayout L = make_layout<U>(a.n_nodes);
+  const FcLayout Li = make_layout_in<U>(a.n_nodes);
+  const FcLayout Lp = make_layout_part<U>(a.n_nodes);
+  float* Sbuf = static_cast<float*>(a.ws);
+  float* gS = Sbuf + fc_ws<U>(a.n_nodes) / sizeof(float);
+  float* Q = gS + fc_ws<U>(a.n_nodes) / sizeof(float);
+  long long qn = 0;
+  for (int b = 0; b < Li.n_out; ++b) qn += (long long)a.n_nodes * Li.d3[b] * kH * Li.npk[b] * U;
+  float* part = Q + qn;
+  int tiles = 0;
+  for (int k = 0; k < L.n_out; ++k) tiles += (a.n_nodes * L.d3[k] + 15) / 16;
+  if (a.grad_Theta) {
+    hipLaunchKernelGGL((k_fc_state<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes, a.row_ptr,
+                       a.col, a.x, a.Y, a.R, Sbuf, L);
+    int nb = 0;
+    for (int k = 0; k < L.n_out; ++k)
+      nb += ((a.n_nodes * L.d3[k] + kRowBlock - 1) / kRowBlock) * ((kH * L.npk[k] * U / 16 + 3) / 4);
+    hipLaunchKernelGGL((k_fc_gradtheta<U, kH>), dim3(nb), dim3(256), 0, a.stream, a.n_nodes, Sbuf, a.gout,
+                       a.outdim, part, L, Lp);
+    PathMap pm{};
+    for (int p = 0; p < SigF::NP; ++p) {
+      pm.k[p] = SigF::paths.p[p].k;
+      int n = 0;
+      for (int q = 0; q < p; ++q) n += SigF::paths.p[q].k == pm.k[p];
+      pm.pl[p] = n;
+    }
+    const int tot = kH * SigF::NP * U * U;
+    hipLaunchKernelGGL((k_fc_gradtheta_sum<U, kH>), dim3((tot + 255) / 256), dim3(256), 0, a.stream, a.n_nodes,
+                       part, SigF::NP, a.grad_Theta, L, Lp, pm);
+  }
+  if ((a.grad_R || a.grad_Y) && a.n_edges > 0) {
+    hipLaunchKernelGGL((k_fc_expand<U, kH>), dim3(tiles), dim3(256), 0, a.stream, a.n_nodes, a.gout, a.Theta,
+                       SigF::NP, a.outdim, gS, L);
+    hipLaunchKernelGGL((k_fc_bwd_recv<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes,
+                       a.row_ptr, a.col, a.x, a.Y, a.R, gS, a.grad_Y, a.grad_R, L);
+  }
+  if (a.grad_x) {
+    hipLaunchKernelGGL((k_fc_bwd_send<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes,
+                       a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.R, a.gout, Q, Li);
+    int tin = 0;
+    for (int b = 0; b < Li.n_out; ++b) tin += (a.n_nodes * Li.d3[b] + 15) / 16;
+    hipLaunchKernelGGL((k_fc_contract<U, kH, true>), dim3(tin), dim3(256), 0, a.stream, a.n_nodes, Q, a.Theta,
+                       SigF::NP, SigF::XC * U, a.grad_x, Li);
+  }
+  return hipGetLastError();
+}
+
+template <int U>
 const FcSet* fc_set() {
-  static const FcSet s{&launch_fc_fwd<U>, &fc_ws<U>, kH};
+  static const FcSet s{&launch_fc_fwd<U>, &fc_ws<U>, kH, &launch_fc_bwd<U>, &fc_bwd_ws<U>};
   return &s;
 }
 

@@ -60,8 +60,12 @@ struct RadialSet {
 struct FcArgs {
   int32_t n_nodes = 0, n_edges = 0, outdim = 0;
   const int32_t *row_ptr = nullptr, *col = nullptr;
+  const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
   const float *x = nullptr, *Y = nullptr, *R = nullptr, *Theta = nullptr;
   float* out = nullptr;
+  // backward: upstream gradient and outputs (NULL: skip)
+  const float* gout = nullptr;
+  float *grad_x = nullptr, *grad_Y = nullptr, *grad_R = nullptr, *grad_Theta = nullptr;
   void* ws = nullptr;
   hipStream_t stream = nullptr;
 };
@@ -69,6 +73,8 @@ struct FcSet {
   hipError_t (*fwd)(const FcArgs&) = nullptr;
   size_t (*workspace)(int n_nodes) = nullptr;
   int n_radial = 0;
+  hipError_t (*bwd)(const FcArgs&) = nullptr;
+  size_t (*bwd_workspace)(int n_nodes) = nullptr;
 };
 const FcSet* fc_l012_s2(int mul, int n_radial);
 

@@ -69,3 +69,55 @@ def test_fc_isolated_and_empty(tpc):
     assert block_err(got, ref, out_blocks(op)) <= TOL
     wl.src, wl.dst, wl.r = wl.src[:0], wl.dst[:0], wl.r[:0]
     assert np.all(_gpu(tpc, irr, wl, R[:0], Th) == 0)
+
+
+def _gpu_bwd(tpc, irr, wl, R, Th, go, want=("x", "Y", "R", "Theta")):
+    plan = tpc.Plan(irr, 2, 2)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+    Rs = tpc.gather_rows(T(R), g.perm)
+    res = tpc.backward_fc(plan, g, T(wl.x), Y, Rs, T(Th), T(go), want=want)
+    torch.cuda.synchronize()
+    return [None if r is None else r.cpu().numpy() for r in res], g.perm.cpu().numpy()
+
+
+def _check_bwd(op, wl, R, Th, go, got, perm):
+    gx, gY, gR, gT = got
+    rx, rY, rR, rT = oracle.fc_conv_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, oracle.sh_real(2, wl.r), R, Th, go)
+    xb = [slice(o, o + op.U * (2 * l + 1)) for (_, l, _), o in zip(op.irreps_in, op.in_offsets)]
+    yb = [slice(l * l, (l + 1) ** 2) for l in range(3)]
+    assert block_err(gx, rx, xb) <= TOL
+    assert block_err(gY, rY[perm], yb) <= TOL
+    assert block_err(gR, rR[perm], [slice(0, R.shape[1])]) <= TOL
+    P, U = op.n_paths, op.U
+    assert block_err(gT.reshape(-1, P * U * U), rT.reshape(-1, P * U * U),
+                     [slice(p * U * U, (p + 1) * U * U) for p in range(P)]) <= TOL
+
+
+@pytest.mark.parametrize("U,graph,n", [(16, "mid", 200), (32, "mid", 300), (32, "zipf", 400),
+                                       (16, "lmax3", 250), (32, "mid", 1536)])
+def test_fc_backward_parity(tpc, U, graph, n):
+    say(f"fc backward U={U} graph={graph} n={n}")
+    irr, op, wl, R, Th = _case(U, graph, n)
+    go = np.random.default_rng(7).normal(size=(wl.n_nodes, op.outdim)).astype(np.float32)
+    got, perm = _gpu_bwd(tpc, irr, wl, R, Th, go)
+    _check_bwd(op, wl, R, Th, go, got, perm)
+
+
+def test_fc_backward_subsets_isolated_empty(tpc):
+    say("fc backward output subsets, isolated nodes, empty graph")
+    irr, op, wl, R, Th = _case(32, "mid", 80, seed=3)
+    keep = (wl.dst >= 10) & (wl.src >= 5)
+    wl.src, wl.dst, wl.r = wl.src[keep], wl.dst[keep], wl.r[keep]
+    R = R[keep]
+    go = np.random.default_rng(8).normal(size=(wl.n_nodes, op.outdim)).astype(np.float32)
+    got, perm = _gpu_bwd(tpc, irr, wl, R, Th, go)
+    _check_bwd(op, wl, R, Th, go, got, perm)
+    assert np.all(got[0][:5] == 0)
+    again, _ = _gpu_bwd(tpc, irr, wl, R, Th, go)
+    assert all(np.array_equal(a, b) for a, b in zip(got, again))
+    part, _ = _gpu_bwd(tpc, irr, wl, R, Th, go, want=("R",))
+    assert part[0] is None and part[1] is None and part[3] is None and np.array_equal(part[2], got[2])
+    wl.src, wl.dst, wl.r = wl.src[:0], wl.dst[:0], wl.r[:0]
+    empty, _ = _gpu_bwd(tpc, irr, wl, R[:0], Th, go)
+    assert np.all(empty[0] == 0) and np.all(empty[3] == 0) and empty[1].size == 0 and empty[2].size == 0
