@@ -61,7 +61,7 @@ FC_WORKLOADS = {
     "fc": ("32x0e+32x1o+32x2e", 2, 2, 8,
            "1536 atoms, 46080 directed edges (the mid graph), 32x0e+32x1o+32x2e, real SH lmax 2, "
            "15 paths, fully connected per-edge weights W_e = sum_h R_e[h] Theta[h] (8 radial "
-           "features, 32x32 per path) by reassociation into receiver state, fwd"),
+           "features, 32x32 per path) by reassociation into receiver state, fwd+bwd"),
 }
 GAUNT_WORKLOADS = {
     "gaunt": ("32x0e+32x1o+32x2e", 2, 2,
@@ -553,13 +553,23 @@ def bench_radial(args, torch, tpc, make_workload, dev):
     print(json.dumps(res))
 
 
-def fc_algorithmic(N, E, P, U, H, d3_paths):
-    """compulsory bytes (inputs and output once) and the reassociated schedule's
-    MFMA flops: state accumulation 2 H Q per edge, contraction 2 H Q U per node,
-    Q = U * sum_p (2 l3 + 1)"""
-    Q = U * sum(d3_paths)
-    return {"bytes": 4.0 * (E * (9 + H + 2) + N * (9 * U + 17 * U + 1)) + 4.0 * H * P * U * U,
-            "state_flops": 2.0 * H * Q * E, "contract_flops": 2.0 * H * Q * U * N}
+def fc_algorithmic(N, E, P, U, H, d3_paths, d1_paths, xdim, outdim, ysh):
+    """Bytes each phase of the fully connected layer must move once, counting
+    the node-sized states it writes and reads back (the reassociated schedule's
+    own traffic): S and gS have H U sum_p (2l3+1) floats per node, Q has
+    H U sum_p (2l1+1)."""
+    s_state = 4.0 * N * H * U * sum(d3_paths)
+    q_state = 4.0 * N * H * U * sum(d1_paths)
+    edge_in = 4.0 * E * (1 + ysh + H)                  # col (or t_perm / t_col), Y, R
+    theta = 4.0 * H * P * U * U
+    node = 4.0 * N * (xdim + outdim)
+    return {
+        "fwd": edge_in + node + theta + 2 * s_state,
+        "bwd_theta": edge_in + 4.0 * N * (xdim + outdim) + theta + 2 * s_state,
+        "bwd_RY": edge_in + 4.0 * N * (xdim + outdim) + theta + 2 * s_state + 4.0 * E * (ysh + H),
+        "bwd_x": edge_in + 4.0 * E + 4.0 * N * (outdim + xdim) + theta + 2 * q_state,
+        "compulsory": 4.0 * E * (1 + 2 * ysh + 2 * H) + 4.0 * N * 2 * (xdim + outdim) + 2 * theta,
+    }
 
 
 def bench_fc(args, torch, tpc, make_workload, dev):
@@ -570,18 +580,28 @@ def bench_fc(args, torch, tpc, make_workload, dev):
     N, E = wl.n_nodes, wl.n_edges
     P, U = plan.n_paths, plan.mul
     R, Th = make_fc_inputs(E, P, U, H, seed=0)
+    go_h = np.random.default_rng(1).normal(size=(N, plan.outdim)).astype(np.float32)
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     g = tpc.graph_build(T(wl.src), T(wl.dst), N)
     Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
     Rs = tpc.gather_rows(T(R), g.perm)
-    x, Tht = T(wl.x), T(Th)
+    x, Tht, go = T(wl.x), T(Th), T(go_h)
     out = torch.empty(N, plan.outdim, device=dev)
     ws = torch.empty(tpc.fc_workspace(plan, N, H), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(tpc.fc_backward_workspace(plan, N, H), dtype=torch.uint8, device=dev)
+    gx, gY, gR, gT = torch.empty_like(x), torch.empty_like(Y), torch.empty_like(Rs), torch.empty_like(Tht)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
     def step():
         tpc.forward_fc(plan, g, x, Y, Rs, Tht, out=out, ws=ws)
+        tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(gx, gY, gR, gT))
 
+    phases = {
+        "fwd": lambda: tpc.forward_fc(plan, g, x, Y, Rs, Tht, out=out, ws=ws),
+        "bwd_theta": lambda: tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(None, None, None, gT)),
+        "bwd_RY": lambda: tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(None, gY, gR, None)),
+        "bwd_x": lambda: tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(gx, None, None, None)),
+    }
     if args.counters:
         counters_run(torch, dev, flush, step, args.config)
         return
@@ -593,36 +613,33 @@ def bench_fc(args, torch, tpc, make_workload, dev):
     t = timed_steps(step, args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    step_ms = float(t.mean())
+    step_ms = float(np.median(t))
+    reps, rounds = 5, max(2, args.steps // 5)
+    kt = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in phases.items()}
     d3s = [2 * l3 + 1 for (_, _, l3, _) in plan.paths()]
-    alg = fc_algorithmic(N, E, P, U, H, d3s)
-    traffic = read_traffic(args.config, FC_SOURCES)
-    if traffic is not None and {"fc_state", "fc_contract"} <= set(traffic):
-        traffic = traffic["fc_state"] + traffic["fc_contract"]
-    else:
-        traffic = None
-    flops = alg["state_flops"] + alg["contract_flops"]
+    d1s = [2 * l1 + 1 for (l1, _, _, _) in plan.paths()]
+    alg = fc_algorithmic(N, E, P, U, H, d3s, d1s, plan.xdim, plan.outdim, plan.ysh)
+    dom = max(kt, key=kt.get)
+    gbs = alg[dom] / (kt[dom] * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": E / (step_ms * 1e-3), "unit": "edges/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded; random radial features and mixing parameters)",
+        "data": "synthetic (seeded; random radial features, mixing parameters and upstream gradient)",
         "config": {"workload": f"{args.config}: {desc}", "n_nodes": N, "n_edges": E,
-                   "irreps": irreps, "paths": P, "radial_features": H, "mode": "fwd",
+                   "irreps": irreps, "paths": P, "radial_features": H, "mode": "fwd+bwd",
                    "cache": "L2+MALL flushed before each step"},
         "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
-        "compulsory_bytes": alg["bytes"],
+        "phase_ms": kt,
+        "fwd_edges_per_s": E / (kt["fwd"] * 1e-3),
+        "compulsory_bytes": alg["compulsory"],
         "state_bytes": ws.numel(),
-        "mfma_flops": flops,
-        "step_mfma_frac": flops / (step_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
         "wall_s_timed_region": wall,
-        "roofline": {"bound": "hbm", "kernel": "forward_fc (both phases)",
-                     "achieved": (alg["bytes"] + 2 * ws.numel()) / (step_ms * 1e-3) / 1e9,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (alg["bytes"] + 2 * ws.numel()) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "algorithmic_bytes": alg["bytes"] + 2 * ws.numel(),
-                     "note": "inputs and output once plus one write and one read of the "
-                             "node-sized receiver state", "traffic": traffic},
+        "roofline": {"bound": "hbm", "kernel": f"{dom} (one entry-point call)",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": alg[dom],
+                     "note": "inputs and outputs once plus one write and one read of each "
+                             "node-sized state the phase uses", "traffic": None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -633,18 +650,20 @@ def bench_fc(args, torch, tpc, make_workload, dev):
             threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         except Exception:
             threads = 1
-        n_s = min(E, 46080)
+        n_s = 12000
         order = np.argsort(wl.dst, kind="stable")[:n_s]
         e = np.sort(order)
         nodes = np.unique(np.concatenate([wl.src[e], wl.dst[e]]))
         src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
         t0 = time.perf_counter()
-        oracle.fc_conv_fwd(op, src, dst, len(nodes), wl.x[nodes], oracle.sh_real(lsh, wl.r[e]), R[e], Th)
+        Yo = oracle.sh_real(lsh, wl.r[e])
+        oracle.fc_conv_fwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th)
+        oracle.fc_conv_bwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th, go_h[nodes])
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": len(e) / dt, "unit": "edges/s", "cores": int(threads),
                                "kind": "oracle",
-                               "sample": f"{len(e)} of {E} edges (receiver order), harmonics + "
-                                         f"fwd once, float64 (per-edge weights formed), {dt:.2f} s"}
+                               "sample": f"{len(e)} of {E} edges (the first receivers), harmonics + "
+                                         f"fwd + bwd once, float64 (per-edge weights formed), {dt:.2f} s"}
     print(json.dumps(res))
 
 

@@ -434,9 +434,9 @@ def fc_backward_workspace(plan, n_nodes, n_radial):
     return b.value
 
 
-def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "Theta"), ws=None):
+def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "Theta"), ws=None, outs=None):
     """(grad_x, grad_Y, grad_R, grad_Theta) of the fully connected convolution;
-    entries not in ``want`` are None (skipped on the device)."""
+    entries not in ``want`` (or None in ``outs``) are None (skipped on the device)."""
     torch = _torch()
     N, E = graph.n_nodes, graph.n_edges
     H = R.shape[1]
@@ -450,10 +450,12 @@ def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "The
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
     elif ws.numel() < nbytes:
         raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
-    gx = torch.empty_like(x) if "x" in want else None
-    gY = torch.empty_like(Y) if "Y" in want else None
-    gR = torch.empty_like(R) if "R" in want else None
-    gT = torch.empty_like(Theta) if "Theta" in want else None
+    if outs is None:
+        outs = (torch.empty_like(x) if "x" in want else None,
+                torch.empty_like(Y) if "Y" in want else None,
+                torch.empty_like(R) if "R" in want else None,
+                torch.empty_like(Theta) if "Theta" in want else None)
+    gx, gY, gR, gT = outs
     g = graph.cstruct()
     _check(lib().tp_conv_backward_fc(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(R), H, _ptr(Theta),
                                      _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gR), _ptr(gT), _ptr(ws),
