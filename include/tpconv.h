@@ -234,7 +234,7 @@ tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float*
  * (G_e: the CG adjoint terms of gout_i and Y_e), and grad_x = Theta^T Q_j; the
  * forward's state S is recomputed for grad_Theta = sum S^T gout.  No per-edge
  * weight matrix or message is formed.  ws: tp_conv_fc_backward_workspace
- * bytes, 16-byte aligned; grad_x needs the graph's sender grouping.  Errors as
+ * bytes; ws and Theta 16-byte aligned; grad_x needs the graph's sender grouping.  Errors as
  * tp_conv_forward_fc.  Deterministic. */
 tp_status tp_conv_fc_backward_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial, size_t* bytes);
 tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,

@@ -561,8 +561,8 @@ tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float
   if (E > 0 && (!x || !Y || !R)) return set_error(TP_ERR_ARG, "tp_conv_backward_fc: x/Y/R NULL");
   if (ws_bytes < need || (need > 0 && !ws))
     return set_error(TP_ERR_WORKSPACE, "tp_conv_backward_fc: workspace too small");
-  if (reinterpret_cast<uintptr_t>(ws) & 15)
-    return set_error(TP_ERR_ARG, "tp_conv_backward_fc: ws must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(ws) | reinterpret_cast<uintptr_t>(Theta)) & 15)
+    return set_error(TP_ERR_ARG, "tp_conv_backward_fc: ws and Theta must be 16-byte aligned");
   tpc::FcArgs a;
   a.n_nodes = N;
   a.n_edges = E;

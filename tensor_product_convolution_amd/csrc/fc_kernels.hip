@@ -302,24 +302,51 @@ __global__ void __launch_bounds__(256)
   const int ra = row0 + e16;
   const bool va = ra < rows;
   const int node = (va ? ra : rows - 1) / d3, c = (va ? ra : rows - 1) % d3;
-  // A[row e16][v = 4 ks + g]
+  // K order (free for a sum): step ks feeds lane group g the channel
+  // v = 16 (ks / 4) + 4 g + ks % 4, so each lane reads Theta as 16-byte rows
+  // A[row e16][v]
   float av[U / 4];
 #pragma unroll
-  for (int ks = 0; ks < U / 4; ++ks)
-    av[ks] = va ? gout[(size_t)node * outdim + (size_t)U * lay.ko[k] + (4 * ks + g) * d3 + c] : 0.f;
-  for (int ct = wv; ct < KK / 16; ct += 4) {
-    // columns K = 16 ct + e16 = (h npk + pl) U + uu; a 16-block shares (h, pl)
-    const int t = (16 * ct) / U, uu = (16 * ct) % U + e16;
-    const int pl = t % npk, h = t / npk;
-    const float* th = Theta + (((size_t)h * P + lay.pg[k][pl]) * U + uu) * U + g;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < U / 4; ++ks) {
+    const int v = 16 * (ks / 4) + 4 * g + ks % 4;
+    av[ks] = va ? gout[(size_t)node * outdim + (size_t)U * lay.ko[k] + v * d3 + c] : 0.f;
+  }
+  // this wave's column tiles ct = wv + 4 m, four at a time: their Theta
+  // operands are all loaded before the products (tiles past the end re-read
+  // the last one and are not stored)
+  constexpr int CB = 4;
+  const int nct = KK / 16;
+  for (int c0 = wv; c0 < nct; c0 += 4 * CB) {
+    float bv[CB][U / 4];
 #pragma unroll
-    for (int ks = 0; ks < U / 4; ++ks) acc = mfma_16x16x4(av[ks], th[4 * ks], acc);
-    // D[row 4g + r][column e16]
+    for (int q = 0; q < CB; ++q) {
+      // columns K = 16 ct + e16 = (h npk + pl) U + uu; a 16-block shares (h, pl)
+      const int ct = c0 + 4 * q < nct ? c0 + 4 * q : nct - 1;
+      const int t = (16 * ct) / U, uu = (16 * ct) % U + e16;
+      const int pl = t % npk, h = t / npk;
+      const float4* th = reinterpret_cast<const float4*>(Theta + (((size_t)h * P + lay.pg[k][pl]) * U + uu) * U);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 4 * g + r;
-      if (row < rows) gS[lay.base[k] + (size_t)row * KK + 16 * ct + e16] = acc[r];
+      for (int b4 = 0; b4 < U / 16; ++b4) {
+        const float4 t4 = th[4 * b4 + g];   // v = 16 b4 + 4 g .. + 3
+        bv[q][4 * b4] = t4.x;
+        bv[q][4 * b4 + 1] = t4.y;
+        bv[q][4 * b4 + 2] = t4.z;
+        bv[q][4 * b4 + 3] = t4.w;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
+      const int ct = c0 + 4 * q;
+      if (ct >= nct) break;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < U / 4; ++ks) acc = mfma_16x16x4(av[ks], bv[q][ks], acc);
+      // D[row 4g + r][column e16]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 4 * g + r;
+        if (row < rows) gS[lay.base[k] + (size_t)row * KK + 16 * ct + e16] = acc[r];
+      }
     }
   }
 }
@@ -356,15 +383,23 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int r_end = min(rows, (rb + 1) * kRowBlock);
+  // this lane's row r = (node, c), advanced by four rows per step without a division
+  int r = rb * kRowBlock + g;
+  int node = r / d3, c = r - node * d3;
+  const int q4 = 4 / d3, m4 = 4 - q4 * d3;
   for (int r0 = rb * kRowBlock; r0 < r_end; r0 += 4) {
-    const int r = r0 + g;
     const bool ok = r < r_end;
-    const int rr = ok ? r : r_end - 1;
-    const int node = rr / d3, c = rr % d3;
-    const float a = ok ? Sbuf[lay.base[k] + (size_t)rr * KK + K0 + e16] : 0.f;
-    const float* gr = gout + (size_t)node * outdim + (size_t)U * lay.ko[k] + c;
+    const float a = ok ? Sbuf[lay.base[k] + (size_t)r * KK + K0 + e16] : 0.f;
+    const float* gr = gout + (size_t)(ok ? node : 0) * outdim + (size_t)U * lay.ko[k] + (ok ? c : 0);
 #pragma unroll
     for (int n = 0; n < NV; ++n) acc[n] = mfma_16x16x4(a, ok ? gr[(16 * n + e16) * d3] : 0.f, acc[n]);
+    r += 4;
+    node += q4;
+    c += m4;
+    if (c >= d3) {
+      c -= d3;
+      ++node;
+    }
   }
   // D[K = K0 + 4g + r][v = 16 n + e16]
   float* pk = part + plan_part.base[k] + (size_t)rb * KK * U;
