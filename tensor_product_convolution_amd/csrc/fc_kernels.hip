@@ -189,8 +189,9 @@ __global__ void __launch_bounds__(256)
   });
 }
 
-// Phase 2.  One workgroup (4 waves) per tile of 16 rows (i, c) of one output
-// irrep; the waves split the contraction length K_k in four and meet in LDS.
+// Phase 2.  One workgroup (kCW waves) per tile of 16 rows (i, c) of one output
+// irrep; the waves split the contraction length K_k (wave = radial feature h)
+// and meet in LDS.
 // Within a wave, lane group l/16 takes four consecutive K per four MFMA steps
 // (the order of a sum over K is free), so each lane reads its row with one
 // 16-byte load per four steps.  Rows of all irreps are enumerated irrep by
@@ -198,12 +199,13 @@ __global__ void __launch_bounds__(256)
 // TRANS: the product with Theta transposed in its two channel indices (the
 // backward's grad_x, whose state rows carry output channels v and whose
 // columns are input channels u).
+constexpr int kCW = 8;   // waves per contraction workgroup (each a slice of K)
 template <int U, int H, bool TRANS>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * kCW)
     k_fc_contract(int n_nodes, const float* __restrict__ Sbuf, const float* __restrict__ Theta, int P,
                   int outdim, float* __restrict__ out, FcLayout lay) {
   constexpr int NV = U / 16;
-  __shared__ float red[3][NV][4][64];
+  __shared__ float red[kCW - 1][NV][4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e16 = lane & 15, g = lane >> 4;
   int k = 0, first = 0;
@@ -212,19 +214,20 @@ __global__ void __launch_bounds__(256)
     ++k;
   }
   const int d3 = lay.d3[k], npk = lay.npk[k];
-  const int KK = H * npk * U;                       // a multiple of 256
+  const int KK = H * npk * U;                       // a multiple of 8 U
   const int rows = n_nodes * d3;
   const int row0 = ((int)blockIdx.x - first) * 16;
   const int ra = row0 + e16;                         // this lane's A row
   const bool va = ra < rows;
   const float* arow = Sbuf + lay.base[k] + (size_t)(va ? ra : rows - 1) * KK;
-  const int kq = KK / 4;                             // this wave's share of K
+  const int kq = KK / kCW;                           // this wave's share of K
   const int K0 = wv * kq;
   f32x4 acc[NV];
 #pragma unroll
   for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   // K = (h * npk + pl) * U + uu; a 16-aligned block of K shares (h, pl), so
   // t = K / U is uniform over the wave and Theta's row block is a scalar base.
+  static_assert(H % kCW == 0, "whole (h, path) blocks per wave");
   for (int t = K0 / U; t < (K0 + kq) / U; ++t) {
     const int pl = t % npk, h = t / npk;
     // element (row uu, column col) of this (h, path) block of Theta
@@ -233,8 +236,8 @@ __global__ void __launch_bounds__(256)
     const float* ab = arow + (size_t)t * U + 4 * g;
 #pragma unroll
     for (int ub = 0; ub < U; ub += 16) {
-      const float4 a4 = va ? *reinterpret_cast<const float4*>(ab + ub) : float4{0.f, 0.f, 0.f, 0.f};
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float4 a4 = *reinterpret_cast<const float4*>(ab + ub);
+      const float av[4] = {va ? a4.x : 0.f, va ? a4.y : 0.f, va ? a4.z : 0.f, va ? a4.w : 0.f};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const float* th = thb + (size_t)(ub + 4 * g + st) * RS;
@@ -254,7 +257,12 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int n = 0; n < NV; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[n][r] += red[0][n][r][lane] + red[1][n][r][lane] + red[2][n][r][lane];
+      for (int r = 0; r < 4; ++r) {
+        float a = acc[n][r];
+#pragma unroll
+        for (int w2 = 0; w2 < kCW - 1; ++w2) a += red[w2][n][r][lane];
+        acc[n][r] = a;
+      }
     // D[row 4g + r][v = 16n + l%16]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -387,19 +395,38 @@ __global__ void __launch_bounds__(256)
   int r = rb * kRowBlock + g;
   int node = r / d3, c = r - node * d3;
   const int q4 = 4 / d3, m4 = 4 - q4 * d3;
-  for (int r0 = rb * kRowBlock; r0 < r_end; r0 += 4) {
-    const bool ok = r < r_end;
-    const float a = ok ? Sbuf[lay.base[k] + (size_t)r * KK + K0 + e16] : 0.f;
-    const float* gr = gout + (size_t)(ok ? node : 0) * outdim + (size_t)U * lay.ko[k] + (ok ? c : 0);
+  // kGtBatch steps per batch: every load of the batch is issued (rows past the
+  // block's end re-read a valid row and are replaced by zero) before its
+  // products, so the wave waits once per batch rather than once per step
+  constexpr int kGtBatch = 8;
+  const float* Sk = Sbuf + lay.base[k] + K0 + e16;
+  const float* gk = gout + (size_t)U * lay.ko[k] + (size_t)e16 * d3;
+  for (int r0 = rb * kRowBlock; r0 < r_end; r0 += 4 * kGtBatch) {
+    float a[kGtBatch], gv[kGtBatch][NV];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) acc[n] = mfma_16x16x4(a, ok ? gr[(16 * n + e16) * d3] : 0.f, acc[n]);
-    r += 4;
-    node += q4;
-    c += m4;
-    if (c >= d3) {
-      c -= d3;
-      ++node;
+    for (int s = 0; s < kGtBatch; ++s) {
+      const bool ok = r < r_end;
+      const float* gr = gk + (size_t)(ok ? node : 0) * outdim + (ok ? c : 0);
+      const float av = Sk[(size_t)(ok ? r : r_end - 1) * KK];
+      a[s] = ok ? av : 0.f;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        const float gvn = gr[16 * n * d3];
+        gv[s][n] = ok ? gvn : 0.f;
+      }
+      r += 4;
+      node += q4;
+      c += m4;
+      if (c >= d3) {
+        c -= d3;
+        ++node;
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < kGtBatch; ++s)
+#pragma unroll
+      for (int n = 0; n < NV; ++n) acc[n] = mfma_16x16x4(a[s], gv[s][n], acc[n]);
   }
   // D[K = K0 + 4g + r][v = 16 n + e16]
   float* pk = part + plan_part.base[k] + (size_t)rb * KK * U;
@@ -431,6 +458,31 @@ __global__ void __launch_bounds__(256)
   gTheta[idx] = a;
 }
 
+// Sums of N values over the lanes that differ in the bits below 2 OFF (the
+// channel lanes of one edge), by recursive halving: at the stage with lane
+// offset OFF a lane keeps one half of its list (the upper half if its OFF bit
+// is set), sends the other half to the partner lane and adds what the partner
+// sent, so a stage costs ceil(N / 2) exchanges instead of N.  After the last
+// stage a lane holds ls_final(N, 2 OFF) totals, the first of which is value
+// sum over stages of (bit ? ceil(n / 2) : 0), n the list length at that stage;
+// slots past the real values hold zeros.
+constexpr int ls_final(int n, int lanes) { return lanes <= 1 ? n : ls_final((n + 1) / 2, lanes / 2); }
+
+template <int N, int OFF, int CAP>
+__device__ __forceinline__ void lane_sum_halving(float (&v)[CAP], int lane) {
+  if constexpr (OFF >= 1) {
+    constexpr int H = (N + 1) / 2;
+    const bool bit = (lane & OFF) != 0;
+#pragma unroll
+    for (int q = 0; q < H; ++q) {
+      const float lo = v[q], hi = q + H < N ? v[q + H] : 0.f;
+      const float keep = bit ? hi : lo, send = bit ? lo : hi;
+      v[q] = keep + __shfl_xor(send, OFF, 64);
+    }
+    lane_sum_halving<H, OFF / 2>(v, lane);
+  }
+}
+
 // Receiver pass: grad_R and grad_Y.  One workgroup per receiver, one wave per
 // path group (as the state kernel); the receiver's gS for the group sits in
 // registers (8 features x the group's output components per lane).  Per edge
@@ -453,6 +505,18 @@ __global__ void __launch_bounds__(256)
   const int beg = row_ptr[i], end = row_ptr[i + 1];
   const int grp = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
   const int ec = lane / U, u = lane % U;
+  constexpr int NF = ls_final(NR, U);
+  int ls_first = 0, ls_len = NR;
+  for (int off = U / 2, n = NR; off >= 1; off >>= 1) {
+    const int h = (n + 1) / 2;
+    if (lane & off) {
+      ls_first += h;
+      ls_len = ls_len > h ? ls_len - h : 0;
+    } else {
+      ls_len = ls_len < h ? ls_len : h;
+    }
+    n = h;
+  }
   static_for<NG>([&](auto G) {
     if (grp != G) return;
     constexpr int P0 = PG.start[G], NPP = PG.start[G + 1] - P0;
@@ -512,14 +576,13 @@ __global__ void __launch_bounds__(256)
             for (int h = 0; h < H; ++h) acc[h] = fmaf(gs[OFF + C][h], tv[C], acc[h]);
           });
         });
-        // sum over the edge's U channel lanes
+        // sum over the edge's U channel lanes; lane u then holds the totals
+        // of values ls_first .. ls_first + ls_len - 1
+        lane_sum_halving<NR, U / 2>(acc, lane);
+        if (ok) {
 #pragma unroll
-        for (int q = 0; q < NR; ++q)
-#pragma unroll
-          for (int off = 1; off < U; off <<= 1) acc[q] += __shfl_xor(acc[q], off, 64);
-        if (ok && u == 0) {
-#pragma unroll
-          for (int q = 0; q < NR; ++q) red[G][e][q] = acc[q];
+          for (int j = 0; j < NF; ++j)
+            if (j < ls_len) red[G][e][ls_first + j] = acc[j];
         }
       }
       __syncthreads();
@@ -744,7 +807,7 @@ hipError_t launch_fc_fwd(const FcArgs& a) {
                      a.col, a.x, a.Y, a.R, Sbuf, L);
   int tiles = 0;
   for (int k = 0; k < L.n_out; ++k) tiles += (a.n_nodes * L.d3[k] + 15) / 16;
-  hipLaunchKernelGGL((k_fc_contract<U, kH, false>), dim3(tiles), dim3(256), 0, a.stream, a.n_nodes, Sbuf, a.Theta,
+  hipLaunchKernelGGL((k_fc_contract<U, kH, false>), dim3(tiles), dim3(64 * kCW), 0, a.stream, a.n_nodes, Sbuf, a.Theta,
                      SigF::NP, a.outdim, a.out, L);
   return hipGetLastError();
 }
@@ -793,7 +856,7 @@ hipError_t launch_fc_bwd(const FcArgs& a) {
                        a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.R, a.gout, Q, Li);
     int tin = 0;
     for (int b = 0; b < Li.n_out; ++b) tin += (a.n_nodes * Li.d3[b] + 15) / 16;
-    hipLaunchKernelGGL((k_fc_contract<U, kH, true>), dim3(tin), dim3(256), 0, a.stream, a.n_nodes, Q, a.Theta,
+    hipLaunchKernelGGL((k_fc_contract<U, kH, true>), dim3(tin), dim3(64 * kCW), 0, a.stream, a.n_nodes, Q, a.Theta,
                        SigF::NP, SigF::XC * U, a.grad_x, Li);
   }
   return hipGetLastError();
