@@ -15,8 +15,9 @@
 //     bitwise reproducible.
 // Backward:
 //   * receiver pass: with grad_out[i] in registers, each edge yields
-//     grad_w[e] (per lane) and grad_Y[e] (a butterfly sum over the edge's
-//     channel lanes), written once per edge -- these are requested outputs;
+//     grad_w[e] (per lane) and grad_Y[e] (a recursive-halving sum over the
+//     edge's channel lanes), written once per edge -- these are requested
+//     outputs;
 //   * sender pass: each workgroup owns a sender j and walks its edges in the
 //     sender grouping, gathering grad_out of each receiver, and stores
 //     grad_x[j] once.  Again no atomics.
@@ -34,6 +35,31 @@ struct LaneMap {
   static constexpr int EPW = 64 / LPE;           // edges per wave step
   static constexpr int CPL = U >= 64 ? U / 64 : 1;  // channels per lane
 };
+
+// Sums of N values over the lanes that differ in the bits below 2 OFF (for
+// example the channel lanes of one edge), by recursive halving: at the stage
+// with lane offset OFF a lane keeps one half of its list (the upper half if
+// its OFF bit is set), sends the other half to the partner lane and adds what
+// the partner sent, so a stage costs ceil(N / 2) exchanges instead of N.
+// After the last stage a lane holds ls_final(N, 2 OFF) totals, the first of
+// which is value sum over stages of (bit ? ceil(n / 2) : 0), n the list
+// length at that stage; slots past the real values hold zeros.
+constexpr int ls_final(int n, int lanes) { return lanes <= 1 ? n : ls_final((n + 1) / 2, lanes / 2); }
+
+template <int N, int OFF, int CAP>
+__device__ __forceinline__ void lane_sum_halving(float (&v)[CAP], int lane) {
+  if constexpr (OFF >= 1) {
+    constexpr int H = (N + 1) / 2;
+    const bool bit = (lane & OFF) != 0;
+#pragma unroll
+    for (int q = 0; q < H; ++q) {
+      const float lo = v[q], hi = q + H < N ? v[q + H] : 0.f;
+      const float keep = bit ? hi : lo, send = bit ? lo : hi;
+      v[q] = keep + __shfl_xor(send, OFF, 64);
+    }
+    lane_sum_halving<H, OFF / 2>(v, lane);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // per-edge arithmetic of one channel
@@ -442,9 +468,9 @@ struct Cfg {
   using R = RecvStage<S, U>;
   using Sd = SendStage<S, U>;
   // receiver pass stores per step and lane: one word per path and channel set
-  // (grad_w), one word per LPE harmonic components (grad_Y)
+  // (grad_w), the lane's share of grad_Y after the halving channel sum
   static constexpr int ST_W = S::NP * M::CPL;
-  static constexpr int ST_Y = (S::YC + M::LPE - 1) / M::LPE;
+  static constexpr int ST_Y = ls_final(S::YC, M::LPE);
   static constexpr int NST = ST_W + ST_Y;
   // Staging depth: double buffering (deeper pipelines measured slower on the
   // 1,536-atom workload), single buffering when a step has too many memory
@@ -589,7 +615,18 @@ __global__ void __launch_bounds__(WPB * 64)
   for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + (NBUF - 1) * SLOTS + r, last)];
   // Results of step k are stored during step k+1, after its wait, straight
   // from registers; the number of store instructions per step is fixed (NST).
-  float pgw[M::CPL][S::NP], pgy[(S::YC + M::LPE - 1) / M::LPE];
+  float pgw[M::CPL][S::NP], pgy[C::ST_Y];
+  int y_first = 0, y_len = S::YC;   // this lane's grad_Y components after the channel sum
+  for (int off = M::LPE / 2, n = S::YC; off >= 1; off >>= 1) {
+    const int h = (n + 1) / 2;
+    if (lane & off) {
+      y_first += h;
+      y_len = y_len > h ? y_len - h : 0;
+    } else {
+      y_len = y_len < h ? y_len : h;
+    }
+    n = h;
+  }
   size_t pq = 0;
   auto flush = [&]() {
     if constexpr (MODE & 1) {
@@ -601,10 +638,8 @@ __global__ void __launch_bounds__(WPB * 64)
     }
     if constexpr (MODE & 2) {
 #pragma unroll
-      for (int r = 0; r < (S::YC + M::LPE - 1) / M::LPE; ++r) {
-        const int b = uu + r * M::LPE;
-        if (b < S::YC) __builtin_nontemporal_store(pgy[r], grad_Y + pq * S::YC + b);
-      }
+      for (int r = 0; r < C::ST_Y; ++r)
+        if (r < y_len) __builtin_nontemporal_store(pgy[r], grad_Y + pq * S::YC + y_first + r);
     }
   };
   for (int k = 0; k < trips; ++k) {
@@ -632,19 +667,10 @@ __global__ void __launch_bounds__(WPB * 64)
     for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_recv<S>(xr[cc], yr, wr[cc], gr[cc], pgw[cc], gy);
     if constexpr (MODE & 2) {
       // sum over the edge's channel lanes (partners stay inside the slot);
-      // lane uu then keeps components uu, uu + LPE, ...
+      // the lane then holds components y_first .. y_first + y_len - 1
+      lane_sum_halving<S::YC, M::LPE / 2>(gy, lane);
 #pragma unroll
-      for (int b = 0; b < S::YC; ++b)
-#pragma unroll
-        for (int off = 1; off < M::LPE; off <<= 1) gy[b] += __shfl_xor(gy[b], off, 64);
-#pragma unroll
-      for (int r = 0; r < (S::YC + M::LPE - 1) / M::LPE; ++r) {
-        const int b = uu + r * M::LPE;
-        float v = 0.f;
-#pragma unroll
-        for (int bb = 0; bb < S::YC; ++bb) v = (bb == b) ? gy[bb] : v;
-        pgy[r] = v;
-      }
+      for (int r = 0; r < C::ST_Y; ++r) pgy[r] = gy[r];
     }
     pq = (size_t)min(q0 + slot, last);
   }

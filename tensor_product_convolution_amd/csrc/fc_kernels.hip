@@ -458,31 +458,6 @@ __global__ void __launch_bounds__(256)
   gTheta[idx] = a;
 }
 
-// Sums of N values over the lanes that differ in the bits below 2 OFF (the
-// channel lanes of one edge), by recursive halving: at the stage with lane
-// offset OFF a lane keeps one half of its list (the upper half if its OFF bit
-// is set), sends the other half to the partner lane and adds what the partner
-// sent, so a stage costs ceil(N / 2) exchanges instead of N.  After the last
-// stage a lane holds ls_final(N, 2 OFF) totals, the first of which is value
-// sum over stages of (bit ? ceil(n / 2) : 0), n the list length at that stage;
-// slots past the real values hold zeros.
-constexpr int ls_final(int n, int lanes) { return lanes <= 1 ? n : ls_final((n + 1) / 2, lanes / 2); }
-
-template <int N, int OFF, int CAP>
-__device__ __forceinline__ void lane_sum_halving(float (&v)[CAP], int lane) {
-  if constexpr (OFF >= 1) {
-    constexpr int H = (N + 1) / 2;
-    const bool bit = (lane & OFF) != 0;
-#pragma unroll
-    for (int q = 0; q < H; ++q) {
-      const float lo = v[q], hi = q + H < N ? v[q + H] : 0.f;
-      const float keep = bit ? hi : lo, send = bit ? lo : hi;
-      v[q] = keep + __shfl_xor(send, OFF, 64);
-    }
-    lane_sum_halving<H, OFF / 2>(v, lane);
-  }
-}
-
 // Receiver pass: grad_R and grad_Y.  One workgroup per receiver, one wave per
 // path group (as the state kernel); the receiver's gS for the group sits in
 // registers (8 features x the group's output components per lane).  Per edge
