@@ -61,6 +61,25 @@ __device__ __forceinline__ void lane_sum_halving(float (&v)[CAP], int lane) {
   }
 }
 
+// the values a lane holds after lane_sum_halving over LANES lanes of a list of N
+struct HalvingShare {
+  int first, len;
+};
+__device__ __forceinline__ HalvingShare halving_share(int n, int lanes, int lane) {
+  HalvingShare s{0, n};
+  for (int off = lanes / 2; off >= 1; off >>= 1) {
+    const int h = (n + 1) / 2;
+    if (lane & off) {
+      s.first += h;
+      s.len = s.len > h ? s.len - h : 0;
+    } else {
+      s.len = s.len < h ? s.len : h;
+    }
+    n = h;
+  }
+  return s;
+}
+
 // ---------------------------------------------------------------------------
 // per-edge arithmetic of one channel
 //
@@ -616,17 +635,7 @@ __global__ void __launch_bounds__(WPB * 64)
   // Results of step k are stored during step k+1, after its wait, straight
   // from registers; the number of store instructions per step is fixed (NST).
   float pgw[M::CPL][S::NP], pgy[C::ST_Y];
-  int y_first = 0, y_len = S::YC;   // this lane's grad_Y components after the channel sum
-  for (int off = M::LPE / 2, n = S::YC; off >= 1; off >>= 1) {
-    const int h = (n + 1) / 2;
-    if (lane & off) {
-      y_first += h;
-      y_len = y_len > h ? y_len - h : 0;
-    } else {
-      y_len = y_len < h ? y_len : h;
-    }
-    n = h;
-  }
+  const HalvingShare ysh = halving_share(S::YC, M::LPE, lane);   // this lane's grad_Y components
   size_t pq = 0;
   auto flush = [&]() {
     if constexpr (MODE & 1) {
@@ -639,7 +648,7 @@ __global__ void __launch_bounds__(WPB * 64)
     if constexpr (MODE & 2) {
 #pragma unroll
       for (int r = 0; r < C::ST_Y; ++r)
-        if (r < y_len) __builtin_nontemporal_store(pgy[r], grad_Y + pq * S::YC + y_first + r);
+        if (r < ysh.len) __builtin_nontemporal_store(pgy[r], grad_Y + pq * S::YC + ysh.first + r);
     }
   };
   for (int k = 0; k < trips; ++k) {
@@ -667,7 +676,7 @@ __global__ void __launch_bounds__(WPB * 64)
     for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_recv<S>(xr[cc], yr, wr[cc], gr[cc], pgw[cc], gy);
     if constexpr (MODE & 2) {
       // sum over the edge's channel lanes (partners stay inside the slot);
-      // the lane then holds components y_first .. y_first + y_len - 1
+      // the lane then holds components ysh.first .. ysh.first + ysh.len - 1
       lane_sum_halving<S::YC, M::LPE / 2>(gy, lane);
 #pragma unroll
       for (int r = 0; r < C::ST_Y; ++r) pgy[r] = gy[r];

@@ -18,15 +18,6 @@
 
 namespace tpc {
 
-// sum over the lanes of one edge slot (lane bits below LPE)
-template <int LPE, int N>
-__device__ __forceinline__ void slot_sum(float (&v)[N]) {
-#pragma unroll
-  for (int m = 1; m < LPE; m <<= 1)
-#pragma unroll
-    for (int t = 0; t < N; ++t) v[t] += __shfl_xor(v[t], m, 64);
-}
-
 // sum over the edge slots of the wave (lane bits at and above LPE)
 template <int LPE, int N>
 __device__ __forceinline__ void cross_slot_sum(float (&v)[N]) {
@@ -173,10 +164,12 @@ __global__ void __launch_bounds__(64)
         }
       }
       if (dY) {
-        slot_sum<M::LPE, S::YC>(dyv);
-        if (valid && uu == 0) {
+        lane_sum_halving<S::YC, M::LPE / 2>(dyv, lane);
+        if (valid) {
+          const HalvingShare sh = halving_share(S::YC, M::LPE, lane);
 #pragma unroll
-          for (int b = 0; b < S::YC; ++b) dY[(size_t)e * S::YC + b] = dyv[b];
+          for (int r = 0; r < ls_final(S::YC, M::LPE); ++r)
+            if (r < sh.len) dY[(size_t)e * S::YC + sh.first + r] = dyv[r];
         }
       }
     }

@@ -481,17 +481,7 @@ __global__ void __launch_bounds__(256)
   const int grp = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
   const int ec = lane / U, u = lane % U;
   constexpr int NF = ls_final(NR, U);
-  int ls_first = 0, ls_len = NR;
-  for (int off = U / 2, n = NR; off >= 1; off >>= 1) {
-    const int h = (n + 1) / 2;
-    if (lane & off) {
-      ls_first += h;
-      ls_len = ls_len > h ? ls_len - h : 0;
-    } else {
-      ls_len = ls_len < h ? ls_len : h;
-    }
-    n = h;
-  }
+  const HalvingShare share = halving_share(NR, U, lane);
   static_for<NG>([&](auto G) {
     if (grp != G) return;
     constexpr int P0 = PG.start[G], NPP = PG.start[G + 1] - P0;
@@ -551,13 +541,13 @@ __global__ void __launch_bounds__(256)
             for (int h = 0; h < H; ++h) acc[h] = fmaf(gs[OFF + C][h], tv[C], acc[h]);
           });
         });
-        // sum over the edge's U channel lanes; lane u then holds the totals
-        // of values ls_first .. ls_first + ls_len - 1
+        // sum over the edge's U channel lanes; the lane then holds the totals
+        // of values share.first .. share.first + share.len - 1
         lane_sum_halving<NR, U / 2>(acc, lane);
         if (ok) {
 #pragma unroll
           for (int j = 0; j < NF; ++j)
-            if (j < ls_len) red[G][e][ls_first + j] = acc[j];
+            if (j < share.len) red[G][e][share.first + j] = acc[j];
         }
       }
       __syncthreads();
