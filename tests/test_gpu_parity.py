@@ -171,6 +171,7 @@ def test_sph_harm_parity(tpc):
     ("stream", 300, None, True),
     ("mid", 200, 8, True),
     ("mid", 200, 16, True),
+    ("mid", 1100, 16, True),      # past the small-graph launch threshold
     ("mid", 200, 64, True),
     ("lmax3", 200, 32, True),
     ("lmax3", 120, 128, True),
