@@ -565,7 +565,7 @@ def fc_algorithmic(N, E, P, U, H, d3_paths, d1_paths, xdim, outdim, ysh):
     node = 4.0 * N * (xdim + outdim)
     return {
         "fwd": edge_in + node + theta + 2 * s_state,
-        "bwd_theta": edge_in + 4.0 * N * (xdim + outdim) + theta + 2 * s_state,
+        "bwd_theta": 4.0 * N * outdim + theta + s_state,   # the forward's saved S read once
         "bwd_RY": edge_in + 4.0 * N * (xdim + outdim) + theta + 2 * s_state + 4.0 * E * (ysh + H),
         "bwd_x": edge_in + 4.0 * E + 4.0 * N * (outdim + xdim) + theta + 2 * q_state,
         "compulsory": 4.0 * E * (1 + 2 * ysh + 2 * H) + 4.0 * N * 2 * (xdim + outdim) + 2 * theta,
@@ -587,18 +587,20 @@ def bench_fc(args, torch, tpc, make_workload, dev):
     Rs = tpc.gather_rows(T(R), g.perm)
     x, Tht, go = T(wl.x), T(Th), T(go_h)
     out = torch.empty(N, plan.outdim, device=dev)
-    ws = torch.empty(tpc.fc_workspace(plan, N, H), dtype=torch.uint8, device=dev)
-    wsb = torch.empty(tpc.fc_backward_workspace(plan, N, H), dtype=torch.uint8, device=dev)
+    # one workspace for both calls: the backward reads the state the forward left in it
+    ws = torch.empty(tpc.fc_backward_workspace(plan, N, H), dtype=torch.uint8, device=dev)
+    wsb = ws
     gx, gY, gR, gT = torch.empty_like(x), torch.empty_like(Y), torch.empty_like(Rs), torch.empty_like(Tht)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
     def step():
         tpc.forward_fc(plan, g, x, Y, Rs, Tht, out=out, ws=ws)
-        tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(gx, gY, gR, gT))
+        tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(gx, gY, gR, gT), state_saved=True)
 
     phases = {
         "fwd": lambda: tpc.forward_fc(plan, g, x, Y, Rs, Tht, out=out, ws=ws),
-        "bwd_theta": lambda: tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(None, None, None, gT)),
+        "bwd_theta": lambda: tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(None, None, None, gT),
+                                             state_saved=True),
         "bwd_RY": lambda: tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(None, gY, gR, None)),
         "bwd_x": lambda: tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(gx, None, None, None)),
     }
@@ -633,7 +635,9 @@ def bench_fc(args, torch, tpc, make_workload, dev):
         "phase_ms": kt,
         "fwd_edges_per_s": E / (kt["fwd"] * 1e-3),
         "compulsory_bytes": alg["compulsory"],
-        "state_bytes": ws.numel(),
+        "state_bytes": tpc.fc_workspace(plan, N, H),
+        "backward_note": "the backward reads the state S the forward left in the shared workspace "
+                         "(TP_FC_STATE_SAVED) instead of recomputing it",
         "wall_s_timed_region": wall,
         "roofline": {"bound": "hbm", "kernel": f"{dom} (one entry-point call)",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

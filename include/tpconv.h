@@ -232,15 +232,22 @@ tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float*
  * receiver pass forms grad_R = <gS_i, T_e> and the CG adjoint for grad_Y; a
  * sender pass accumulates the sender-side state Q_j = sum_e R_e (x) G_e
  * (G_e: the CG adjoint terms of gout_i and Y_e), and grad_x = Theta^T Q_j; the
- * forward's state S is recomputed for grad_Theta = sum S^T gout.  No per-edge
+ * forward's state S is needed for grad_Theta = sum S^T gout.  No per-edge
  * weight matrix or message is formed.  ws: tp_conv_fc_backward_workspace
- * bytes; ws and Theta 16-byte aligned; grad_x needs the graph's sender grouping.  Errors as
- * tp_conv_forward_fc.  Deterministic. */
+ * bytes; ws and Theta 16-byte aligned; grad_x needs the graph's sender
+ * grouping.  flags: 0, or TP_FC_STATE_SAVED when the first
+ * tp_conv_fc_workspace bytes of ws still hold the state that
+ * tp_conv_forward_fc wrote there for the same plan, graph, x, Y and R (the
+ * caller passed this ws to the forward and kept those bytes, as an autograd
+ * function keeps what it saved): S is then read, not recomputed.  Without the
+ * flag S is recomputed into ws.  Errors as tp_conv_forward_fc, and TP_ERR_ARG
+ * for other flags.  Deterministic; both ways give identical results. */
+#define TP_FC_STATE_SAVED 1
 tp_status tp_conv_fc_backward_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial, size_t* bytes);
 tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
                               const float* R, int32_t n_radial, const float* Theta, const float* grad_out,
-                              float* grad_x, float* grad_Y, float* grad_R, float* grad_Theta, void* ws,
-                              size_t ws_bytes, hipStream_t stream);
+                              float* grad_x, float* grad_Y, float* grad_R, float* grad_Theta, int32_t flags,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- Gaunt (spherical-grid) product: a different, cheaper operator ----------
  * The Gaunt tensor product is not the CG product: it lacks the couplings with

@@ -21,6 +21,7 @@ STATUS_NAMES = {-1: "TP_ERR_ARG", -2: "TP_ERR_IRREPS", -3: "TP_ERR_UNSUPPORTED",
                 -7: "TP_ERR_INDEX"}
 TP_GRAPH_CHECK = 1
 TP_MODE_UVU, TP_MODE_GAUNT = 0, 1
+TP_FC_STATE_SAVED = 1
 
 # every exported symbol of include/tpconv.h
 EXPORTS = (
@@ -93,8 +94,8 @@ def lib():
         "tp_conv_fc_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_forward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, SZ, VP]),
         "tp_conv_fc_backward_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
-        "tp_conv_backward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, VP, VP, VP, VP,
-                                      SZ, VP]),
+        "tp_conv_backward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, VP, VP, VP, I32,
+                                      VP, SZ, VP]),
         "tp_conv_gaunt_dims": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "tp_conv_forward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_backward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
@@ -434,9 +435,12 @@ def fc_backward_workspace(plan, n_nodes, n_radial):
     return b.value
 
 
-def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "Theta"), ws=None, outs=None):
+def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "Theta"), ws=None, outs=None,
+                state_saved=False):
     """(grad_x, grad_Y, grad_R, grad_Theta) of the fully connected convolution;
-    entries not in ``want`` (or None in ``outs``) are None (skipped on the device)."""
+    entries not in ``want`` (or None in ``outs``) are None (skipped on the device).
+    ``state_saved``: ``ws`` is the workspace ``forward_fc`` was given for the
+    same graph and inputs and still holds its state (read instead of recomputed)."""
     torch = _torch()
     N, E = graph.n_nodes, graph.n_edges
     H = R.shape[1]
@@ -447,6 +451,8 @@ def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "The
     _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
     nbytes = fc_backward_workspace(plan, N, H)
     if ws is None:
+        if state_saved:
+            raise ValueError("state_saved needs the workspace the forward wrote")
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
     elif ws.numel() < nbytes:
         raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
@@ -458,8 +464,9 @@ def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "The
     gx, gY, gR, gT = outs
     g = graph.cstruct()
     _check(lib().tp_conv_backward_fc(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(R), H, _ptr(Theta),
-                                     _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gR), _ptr(gT), _ptr(ws),
-                                     ws.numel(), _stream(x.device)))
+                                     _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gR), _ptr(gT),
+                                     TP_FC_STATE_SAVED if state_saved else 0, _ptr(ws), ws.numel(),
+                                     _stream(x.device)))
     return gx, gY, gR, gT
 
 

@@ -548,9 +548,10 @@ tp_status tp_conv_fc_backward_workspace(tp_plan_t plan, int32_t n_nodes, int32_t
 
 tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
                               const float* R, int32_t n_radial, const float* Theta, const float* grad_out,
-                              float* grad_x, float* grad_Y, float* grad_R, float* grad_Theta, void* ws,
-                              size_t ws_bytes, hipStream_t stream) {
+                              float* grad_x, float* grad_Y, float* grad_R, float* grad_Theta, int32_t flags,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward_fc: plan is NULL");
+  if (flags & ~TP_FC_STATE_SAVED) return set_error(TP_ERR_ARG, "tp_conv_backward_fc: unknown flags");
   size_t need = 0;
   tp_status s = tp_conv_fc_backward_workspace(plan, graph ? graph->n_nodes : 0, n_radial, &need);
   if (s != TP_OK) return s;
@@ -581,6 +582,7 @@ tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float
   a.grad_Y = grad_Y;
   a.grad_R = grad_R;
   a.grad_Theta = grad_Theta;
+  a.state_saved = (flags & TP_FC_STATE_SAVED) != 0;
   a.ws = ws;
   a.stream = stream;
   hipError_t e = find_fc(plan, n_radial)->bwd(a);

@@ -792,8 +792,9 @@ hipError_t launch_fc_bwd(const FcArgs& a) {
   int tiles = 0;
   for (int k = 0; k < L.n_out; ++k) tiles += (a.n_nodes * L.d3[k] + 15) / 16;
   if (a.grad_Theta) {
-    hipLaunchKernelGGL((k_fc_state<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes, a.row_ptr,
-                       a.col, a.x, a.Y, a.R, Sbuf, L);
+    if (!a.state_saved)   // else the forward's S is still in ws
+      hipLaunchKernelGGL((k_fc_state<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes,
+                         a.row_ptr, a.col, a.x, a.Y, a.R, Sbuf, L);
     int nb = 0;
     for (int k = 0; k < L.n_out; ++k)
       nb += ((a.n_nodes * L.d3[k] + kRowBlock - 1) / kRowBlock) * ((kH * L.npk[k] * U / 16 + 3) / 4);

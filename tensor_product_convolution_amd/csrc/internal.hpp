@@ -66,6 +66,7 @@ struct FcArgs {
   // backward: upstream gradient and outputs (NULL: skip)
   const float* gout = nullptr;
   float *grad_x = nullptr, *grad_Y = nullptr, *grad_R = nullptr, *grad_Theta = nullptr;
+  bool state_saved = false;   // backward: ws already holds the forward's state S
   void* ws = nullptr;
   hipStream_t stream = nullptr;
 };

@@ -220,3 +220,15 @@ def test_fc_and_gaunt_host_validation_without_launch():
                                 16, None) == -5
     assert L.tp_conv_forward_fc(cg.handle, ctypes.byref(g), fake, fake, fake, 8, fake, fake, odd,
                                 1 << 30, None) == -1
+    # fully connected backward: flags, workspace, alignment, the sender grouping for grad_x
+    assert L.tp_conv_fc_backward_workspace(cg.handle, 4, 8, ctypes.byref(sz)) == 0   # g has 4 nodes
+    need = sz.value
+    assert L.tp_conv_fc_workspace(cg.handle, 4, 8, ctypes.byref(sz)) == 0 and need > sz.value
+    args = (fake, fake, fake, 8, fake, fake, fake, fake, fake, fake)
+    assert L.tp_conv_backward_fc(cg.handle, ctypes.byref(g), *args, 2, fake, 1 << 30, None) == -1
+    assert "flags" in L.tp_conv_last_error().decode()
+    assert L.tp_conv_backward_fc(cg.handle, ctypes.byref(g), *args, tpc.TP_FC_STATE_SAVED, fake,
+                                 need - 1, None) == -5
+    assert L.tp_conv_backward_fc(cg.handle, ctypes.byref(g), *args, 0, odd, 1 << 30, None) == -1
+    assert L.tp_conv_backward_fc(cg.handle, ctypes.byref(gg), *args, 0, fake, 1 << 30, None) == -1
+    assert L.tp_conv_backward_fc(p.handle, ctypes.byref(g), *args, 0, fake, 1 << 30, None) == -3

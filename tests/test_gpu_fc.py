@@ -121,3 +121,23 @@ def test_fc_backward_subsets_isolated_empty(tpc):
     wl.src, wl.dst, wl.r = wl.src[:0], wl.dst[:0], wl.r[:0]
     empty, _ = _gpu_bwd(tpc, irr, wl, R[:0], Th, go)
     assert np.all(empty[0] == 0) and np.all(empty[3] == 0) and empty[1].size == 0 and empty[2].size == 0
+
+
+def test_fc_backward_reads_the_saved_state(tpc):
+    """With TP_FC_STATE_SAVED the backward reads the state the forward left in
+    the shared workspace instead of recomputing it: identical results."""
+    say("fc backward with the forward's saved state")
+    irr, op, wl, R, Th = _case(32, "mid", 300, seed=5)
+    go = T(np.random.default_rng(9).normal(size=(wl.n_nodes, op.outdim)).astype(np.float32))
+    plan = tpc.Plan(irr, 2, 2)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+    Rs, x, Tt = tpc.gather_rows(T(R), g.perm), T(wl.x), T(Th)
+    ws = torch.empty(tpc.fc_backward_workspace(plan, wl.n_nodes, H), dtype=torch.uint8, device=x.device)
+    ref = tpc.backward_fc(plan, g, x, Y, Rs, Tt, go)
+    tpc.forward_fc(plan, g, x, Y, Rs, Tt, ws=ws)
+    got = tpc.backward_fc(plan, g, x, Y, Rs, Tt, go, ws=ws, state_saved=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(got, ref))
+    with pytest.raises(ValueError):
+        tpc.backward_fc(plan, g, x, Y, Rs, Tt, go, state_saved=True)
