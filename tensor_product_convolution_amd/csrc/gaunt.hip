@@ -26,9 +26,9 @@
 // is small enough to stay in every XCD's L2, unlike x expanded onto the grid
 // (3.6 times larger), which would be gathered from beyond the L2.
 //
-// Workgroup = one receiver, 4 waves; U <= 32: the waves split the receiver's
-// edges; U = 64 / 128: two / four 32-channel tiles, the waves of a tile split
-// the edges.  The waves meet in LDS, the projection onto the output harmonics
+// Workgroup = one receiver; U <= 32: two waves split the receiver's edges;
+// U = 64 / 128: two / four 32-channel tiles, the two / one waves of a tile
+// split the edges.  The waves meet in LDS, the projection onto the output harmonics
 // runs on the vector units and each output row is written once: no per-edge
 // message, no atomics, a fixed summation order.
 #include <cmath>
@@ -109,16 +109,17 @@ __device__ __forceinline__ v16f mfma32(float a, float b, v16f c) {
 // v_mfma_f32_32x32x2f32 operand and result layouts (lane l, k = l / 32):
 //   A[i][k] from lane i + 32 k, B[k][j] from lane j + 32 k,
 //   D[i][j] in lane j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8).
-template <int U, int NL2>
-__global__ void __launch_bounds__(256)
+template <int U, int NL2, int WPT>
+__global__ void __launch_bounds__(64 * (U >= 32 ? U / 32 : 1) * WPT)
     k_gaunt_conv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                  const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ w,
                  float* __restrict__ out, GauntLayout L) {
   constexpr int NUT = U >= 32 ? U / 32 : 1;       // 32-channel tiles
-  constexpr int WPT = 4 / NUT;                    // waves per tile
+  constexpr int NW = NUT * WPT;                   // waves (WPT per tile)
+  constexpr int NTH = 64 * NW;
   constexpr int WD = NL2 * U;                     // weights per edge
   __shared__ __align__(16) float ps[9][kHS];
-  __shared__ __align__(16) float hs[4][32][kHS];
+  __shared__ __align__(16) float hs[NW][32][kHS];
   __shared__ int cs[kChunk];
   __shared__ float ysm[kChunk * 9];
   const int i = blockIdx.x, t = threadIdx.x;
@@ -129,7 +130,7 @@ __global__ void __launch_bounds__(256)
   float yv[9];
 #pragma unroll
   for (int c = 0; c < 9; ++c) yv[c] = c_grid.y[c][n];      // harmonics at this lane's point
-  for (int k = t; k < 9 * kQ; k += 256) ps[k / kQ][k % kQ] = c_grid.p[k / kQ][k % kQ];
+  for (int k = t; k < 9 * kQ; k += NTH) ps[k / kQ][k % kQ] = c_grid.p[k / kQ][k % kQ];
   // f = A_x B_Y with K index a = 2 ks + hk: B[a][q] = Yq[a][q], zero for the
   // padding a = 9 and for degrees the input lacks (their A entries are then
   // any finite in-row value); A[u][a] = x[j][block of degree l(a)][u][m(a)].
@@ -209,8 +210,8 @@ __global__ void __launch_bounds__(256)
   for (int c0 = beg; c0 < end; c0 += kChunk) {
     const int cn = end - c0 < kChunk ? end - c0 : kChunk;
     __syncthreads();   // previous chunk consumed
-    for (int k = t; k < cn; k += 256) cs[k] = col[c0 + k];
-    for (int k = t; k < cn * L.ysh; k += 256) ysm[k] = Y[(size_t)c0 * L.ysh + k];
+    for (int k = t; k < cn; k += NTH) cs[k] = col[c0 + k];
+    for (int k = t; k < cn * L.ysh; k += NTH) ysm[k] = Y[(size_t)c0 * L.ysh + k];
     __syncthreads();
     // batches of kBatch edges per wave: all gathers of a batch are issued
     // before its products, which then wait for their own loads only (loads
@@ -234,7 +235,7 @@ __global__ void __launch_bounds__(256)
   for (int r = 0; r < 16; ++r) hs[wave][8 * (r / 4) + 4 * hk + r % 4][n] = h[r];
   __syncthreads();
   if (WPT > 1) {   // the waves of a tile add up, once, into the tile's first copy
-    for (int k = t; k < NUT * 32 * 32; k += 256) {
+    for (int k = t; k < NUT * 32 * 32; k += NTH) {
       const int tw = (k / 1024) * WPT, row = (k / 32) % 32, q = k % 32;
       float a = hs[tw][row][q];
 #pragma unroll
@@ -245,7 +246,7 @@ __global__ void __launch_bounds__(256)
   }
   // projection onto the output harmonics; block l3 starts at column U l3^2,
   // channel uu's components at uu (2 l3 + 1)
-  for (int o = t; o < L.outdim; o += 256) {
+  for (int o = t; o < L.outdim; o += NTH) {
     const int l3 = o < U ? 0 : (o < 4 * U ? 1 : 2);
     const int d = 2 * l3 + 1, r = o - U * l3 * l3;
     const int uu = r / d, c = l3 * l3 + (r - uu * d);
@@ -293,8 +294,8 @@ __device__ __forceinline__ void out_operand(const GauntLayout& L, int U, int uc,
 // sum over channels for grad_Y is in-lane (the lane's 16 channels) plus one
 // cross-half exchange, then a butterfly over the 32 points; the sum over
 // points for grad_w goes through a per-wave LDS transpose of gg.
-template <int U, int NL2>
-__global__ void __launch_bounds__(256)
+template <int U, int NL2, int NW>
+__global__ void __launch_bounds__(64 * NW)
     k_gaunt_bwd_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                      const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ w,
                      const float* __restrict__ gout, float* __restrict__ grad_Y, float* __restrict__ grad_w,
@@ -307,9 +308,9 @@ __global__ void __launch_bounds__(256)
   __shared__ int cs[CR];
   __shared__ float ysm[CR * 9];
   __shared__ __align__(16) float wsm[CR * WD];
-  __shared__ __align__(16) float tr[4][32][kHS];     // per-wave transpose of gg
-  __shared__ __align__(16) float zt[4][3][kQ];       // per-wave Z at the 32 points
-  __shared__ __align__(16) float yr[4][9][kHS];      // per-wave grad_Y terms at the 32 points
+  __shared__ __align__(16) float tr[NW][32][kHS];     // per-wave transpose of gg
+  __shared__ __align__(16) float zt[NW][3][kQ];       // per-wave Z at the 32 points
+  __shared__ __align__(16) float yr[NW][9][kHS];      // per-wave grad_Y terms at the 32 points
   const int i = blockIdx.x, t = threadIdx.x;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
   const int wave = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
@@ -435,20 +436,20 @@ __global__ void __launch_bounds__(256)
   for (int c0 = beg; c0 < end; c0 += CR) {
     const int cn = end - c0 < CR ? end - c0 : CR;
     __syncthreads();   // previous chunk consumed
-    for (int k = t; k < cn; k += 256) cs[k] = col[c0 + k];
-    for (int k = t; k < cn * L.ysh; k += 256) ysm[k] = Y[(size_t)c0 * L.ysh + k];
+    for (int k = t; k < cn; k += 64 * NW) cs[k] = col[c0 + k];
+    for (int k = t; k < cn * L.ysh; k += 64 * NW) ysm[k] = Y[(size_t)c0 * L.ysh + k];
     {
       const float4* src = reinterpret_cast<const float4*>(w + (size_t)c0 * WD);
-      for (int k = t; k < cn * WD / 4; k += 256) reinterpret_cast<float4*>(wsm)[k] = src[k];
+      for (int k = t; k < cn * WD / 4; k += 64 * NW) reinterpret_cast<float4*>(wsm)[k] = src[k];
     }
     __syncthreads();
     // batches of NB edges per wave: the sender rows of a batch are gathered
     // before its products (slots past the chunk re-read its last edge, unused)
-    for (int k0 = wave; k0 < cn; k0 += 4 * NB) {
+    for (int k0 = wave; k0 < cn; k0 += NW * NB) {
       float xa[NB][NUT][5];
 #pragma unroll
       for (int r = 0; r < NB; ++r) {
-        const int k = k0 + 4 * r < cn ? k0 + 4 * r : cn - 1;
+        const int k = k0 + NW * r < cn ? k0 + NW * r : cn - 1;
         const float* xj = x + (size_t)cs[k] * L.xdim;
 #pragma unroll
         for (int ut = 0; ut < NUT; ++ut)
@@ -458,7 +459,7 @@ __global__ void __launch_bounds__(256)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < NB; ++r)
-        if (k0 + 4 * r < cn) edge(c0, k0 + 4 * r, xa[r]);
+        if (k0 + NW * r < cn) edge(c0, k0 + NW * r, xa[r]);
     }
   }
 }
@@ -469,17 +470,17 @@ __global__ void __launch_bounds__(256)
 // gradient row) times the filter g (two products), summed on the grid and
 // projected once onto the sender's harmonics (no quadrature weights: the
 // adjoint of evaluating x on the grid).
-template <int U, int NL2>
-__global__ void __launch_bounds__(256)
+template <int U, int NL2, int WPT>
+__global__ void __launch_bounds__(64 * (U >= 32 ? U / 32 : 1) * WPT)
     k_gaunt_bwd_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                      const int32_t* __restrict__ t_col, const float* __restrict__ Y,
                      const float* __restrict__ w, const float* __restrict__ gout, float* __restrict__ grad_x,
                      GauntLayout L) {
   constexpr int NUT = U >= 32 ? U / 32 : 1;
-  constexpr int WPT = 4 / NUT;
+  constexpr int NW = NUT * WPT, NTH = 64 * NW;
   constexpr int WD = NL2 * U;
   __shared__ __align__(16) float yt[10][kHS];
-  __shared__ __align__(16) float hs[4][32][kHS];
+  __shared__ __align__(16) float hs[NW][32][kHS];
   __shared__ int rs[kChunk], ps_[kChunk];
   __shared__ float ysm[kChunk * 9];
   const int j = blockIdx.x, t = threadIdx.x;
@@ -490,7 +491,7 @@ __global__ void __launch_bounds__(256)
   float yv[9];
 #pragma unroll
   for (int c = 0; c < 9; ++c) yv[c] = c_grid.y[c][n];
-  for (int k = t; k < 9 * kQ; k += 256) yt[k / kQ][k % kQ] = c_grid.y[k / kQ][k % kQ];
+  for (int k = t; k < 9 * kQ; k += NTH) yt[k / kQ][k % kQ] = c_grid.y[k / kQ][k % kQ];
   const int u = 32 * ut + n, uc = u < U ? u : U - 1;
   int oo[5];
   float bp[5];
@@ -507,12 +508,12 @@ __global__ void __launch_bounds__(256)
   for (int c0 = beg; c0 < end; c0 += kChunk) {
     const int cn = end - c0 < kChunk ? end - c0 : kChunk;
     __syncthreads();
-    for (int k = t; k < cn; k += 256) {
+    for (int k = t; k < cn; k += NTH) {
       rs[k] = t_col[c0 + k];
       ps_[k] = t_perm[c0 + k];
     }
     __syncthreads();
-    for (int k = t; k < cn * L.ysh; k += 256)
+    for (int k = t; k < cn * L.ysh; k += NTH)
       ysm[k] = Y[(size_t)ps_[k / L.ysh] * L.ysh + k % L.ysh];
     __syncthreads();
     for (int k = sub; k < cn; k += WPT) {
@@ -542,7 +543,7 @@ __global__ void __launch_bounds__(256)
   for (int r = 0; r < 16; ++r) hs[wave][8 * (r / 4) + 4 * hk + r % 4][n] = h[r];
   __syncthreads();
   if (WPT > 1) {
-    for (int k = t; k < NUT * 32 * 32; k += 256) {
+    for (int k = t; k < NUT * 32 * 32; k += NTH) {
       const int tw = (k / 1024) * WPT, row = (k / 32) % 32, q = k % 32;
       float a = hs[tw][row][q];
 #pragma unroll
@@ -552,7 +553,7 @@ __global__ void __launch_bounds__(256)
     __syncthreads();
   }
   // grad_x[j][block b][uu][m] = sum_q Yq[l_b^2 + m][q] H[uu][q]
-  for (int o = t; o < L.xdim; o += 256) {
+  for (int o = t; o < L.xdim; o += NTH) {
     int b = 0;
     while (b + 1 < L.n_in && o >= L.off[b + 1]) ++b;
     const int l = L.deg[b], d = 2 * l + 1, r = o - L.off[b];
@@ -572,35 +573,57 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// waves per 32-channel tile of the forward: two up to 32 channels (31 against
+// 33 us with four and 35 with one on the 1,536-atom graph), else four waves
+// per workgroup in all
+template <int U>
+constexpr int fwd_wpt() {
+  return U <= 32 ? 2 : 4 / (U / 32);
+}
+
 template <int U>
 hipError_t launch(const GauntArgs& a, const GauntLayout& L) {
-  const dim3 blocks(a.n_nodes), threads(256);
+  constexpr int WPT = fwd_wpt<U>();
+  const dim3 blocks(a.n_nodes), threads(64 * (U >= 32 ? U / 32 : 1) * WPT);
   switch (a.lmax_sh) {
     case 0:
-      hipLaunchKernelGGL((k_gaunt_conv<U, 1>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y, a.w,
-                         a.out, L);
+      hipLaunchKernelGGL((k_gaunt_conv<U, 1, WPT>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
+                         a.w, a.out, L);
       break;
     case 1:
-      hipLaunchKernelGGL((k_gaunt_conv<U, 2>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y, a.w,
-                         a.out, L);
+      hipLaunchKernelGGL((k_gaunt_conv<U, 2, WPT>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
+                         a.w, a.out, L);
       break;
     default:
-      hipLaunchKernelGGL((k_gaunt_conv<U, 3>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y, a.w,
-                         a.out, L);
+      hipLaunchKernelGGL((k_gaunt_conv<U, 3, WPT>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
+                         a.w, a.out, L);
       break;
   }
   return hipGetLastError();
 }
 
+// waves of the receiver pass (two up to 32 channels: 46 against 50 us with
+// four on the 1,536-atom graph), and per 32-channel tile of the sender pass
+// (four waves per workgroup in all; two per tile took 36.6 against 34.9 us)
+template <int U>
+constexpr int recv_waves() {
+  return U <= 32 ? 2 : 4;
+}
+template <int U>
+constexpr int send_wpt() {
+  return 4 / (U >= 32 ? U / 32 : 1);
+}
+
 template <int U, int NL2>
 hipError_t launch_bwd_nl(const GauntArgs& a, const GauntLayout& L) {
-  const dim3 blocks(a.n_nodes), threads(256);
+  constexpr int NW = recv_waves<U>(), WPT = send_wpt<U>();
+  const dim3 blocks(a.n_nodes);
   if (a.n_edges > 0 && (a.grad_w || a.grad_Y))
-    hipLaunchKernelGGL((k_gaunt_bwd_recv<U, NL2>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
-                       a.w, a.gout, a.grad_Y, a.grad_w, L);
+    hipLaunchKernelGGL((k_gaunt_bwd_recv<U, NL2, NW>), blocks, dim3(64 * NW), 0, a.stream, a.row_ptr, a.col,
+                       a.x, a.Y, a.w, a.gout, a.grad_Y, a.grad_w, L);
   if (a.grad_x)
-    hipLaunchKernelGGL((k_gaunt_bwd_send<U, NL2>), blocks, threads, 0, a.stream, a.t_row_ptr, a.t_perm,
-                       a.t_col, a.Y, a.w, a.gout, a.grad_x, L);
+    hipLaunchKernelGGL((k_gaunt_bwd_send<U, NL2, WPT>), blocks, dim3(64 * (U >= 32 ? U / 32 : 1) * WPT), 0,
+                       a.stream, a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.w, a.gout, a.grad_x, L);
   return hipGetLastError();
 }
 
