@@ -506,20 +506,25 @@ struct Cfg {
   // fill the chip (no cross-wave reduction; 23.3 against 24.2 us on the
   // 1,536-atom graph with two) and two on small graphs (WPB_F2), where the
   // latency of one workgroup is that of the launch
+  // (large signatures take four waves where their single buffers fit: 164
+  // against 172 us for the lmax-3 forward, 1.88 against 1.97 ms on the Zipf
+  // graph)
   static constexpr int WPB_F2 = 2 * R::BUF <= LDS ? 2 : 1;
-  static constexpr int WPB_F = U <= 32 ? 1 : WPB_F2;
+  static constexpr int WPB_F = kPhased<S> ? (fits(R::BUF, 1, 4) ? 4 : WPB_F2) : (U <= 32 ? 1 : WPB_F2);
   // the receiver pass takes four waves where their buffers fit (shorter
   // workgroups that the dispatcher refills as they finish: 39.8 against
   // 42.6 us on the 1,536-atom graph with two)
   static constexpr int WPB_R = fits(R::BUF, kPhased<S> ? 1 : 2, 4) ? 4 : (2 * R::BUF <= LDS ? 2 : 1);
-  static constexpr int WPB_S = (U <= 32 || 2 * Sd::BUF > LDS) ? 1 : 2;
+  // the sender pass one wave per workgroup up to 32 channels and for large
+  // signatures (1.73 against 1.86 ms on the Zipf graph with two)
+  static constexpr int WPB_S = (U <= 32 || kPhased<S> || 2 * Sd::BUF > LDS) ? 1 : 2;
   // large signatures are arithmetic-heavy: one buffer per wave doubles the
   // workgroups (waves) that fit in LDS, which hides more latency than a
   // second buffer would
   static constexpr int NBUF_F = kPhased<S> ? 1 : depth(R::NLOADS, R::BUF, WPB_F);
   static constexpr int NBUF_F2 = kPhased<S> ? 1 : depth(R::NLOADS, R::BUF, WPB_F2);
   static constexpr int NBUF_R = kPhased<S> ? 1 : depth(R::NLOADS + NST, R::BUF, WPB_R);
-  static constexpr int NBUF_S = depth(Sd::NLOADS, Sd::BUF, WPB_S);
+  static constexpr int NBUF_S = kPhased<S> ? 1 : depth(Sd::NLOADS, Sd::BUF, WPB_S);
   static_assert(fits(R::BUF, NBUF_F, WPB_F) && fits(R::BUF, NBUF_F2, WPB_F2) && fits(R::BUF, NBUF_R, WPB_R) &&
                     fits(Sd::BUF, NBUF_S, WPB_S), "staging exceeds 64 KB of LDS");
 };
