@@ -172,6 +172,8 @@ def test_sph_harm_parity(tpc):
     ("mid", 200, 8, True),
     ("mid", 200, 16, True),
     ("mid", 1100, 16, True),      # past the small-graph launch threshold
+    ("mid", 1030, 8, False),
+    ("lmax3", 1050, 32, False),
     ("mid", 200, 64, True),
     ("lmax3", 200, 32, True),
     ("lmax3", 120, 128, True),
