@@ -532,27 +532,48 @@ __global__ void __launch_bounds__(64 * (U >= 32 ? U / 32 : 1) * WPT)
     for (int k = t; k < cn * L.ysh; k += NTH)
       ysm[k] = Y[(size_t)ps_[k / L.ysh] * L.ysh + k % L.ysh];
     __syncthreads();
-    for (int k = sub; k < cn; k += WPT) {
-      const float* gi = gout + (size_t)rs[k] * L.outdim;
-      const float* we = w + (size_t)ps_[k] * WD;
+    // edges one at a time, software-pipelined: the next edge's gathers are in
+    // flight while this edge's products run (34.5 against 35.9 us)
+    struct EdgeOps {
       float ga[5], wa[2];
+    };
+    // one edge's gathers (the index clamped to the chunk)
+    auto fetch = [&](int k, EdgeOps& o) {
+      const int kc = k < cn ? k : cn - 1;
+      const float* gi = gout + (size_t)rs[kc] * L.outdim;
+      const float* we = w + (size_t)ps_[kc] * WD;
 #pragma unroll
-      for (int ks = 0; ks < 5; ++ks) ga[ks] = gi[oo[ks]];
+      for (int ks = 0; ks < 5; ++ks) o.ga[ks] = gi[oo[ks]];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) wa[ks] = __builtin_nontemporal_load(we + wo[ks]);
+      for (int ks = 0; ks < 2; ++ks) o.wa[ks] = __builtin_nontemporal_load(we + wo[ks]);
+    };
+    auto product = [&](int k, const EdgeOps& o) {
       float z[3] = {0.f, 0.f, 0.f};
 #pragma unroll
       for (int l2 = 0; l2 < NL2; ++l2)
 #pragma unroll
         for (int m = 0; m < 2 * l2 + 1; ++m) z[l2] = fmaf(ysm[k * L.ysh + l2 * l2 + m], yv[l2 * l2 + m], z[l2]);
       const float zb0 = hk ? z[1] : z[0], zb1 = hk ? 0.f : z[2];
-      v16f gh = mfma32(ga[0], bp[0], zero);
+      v16f gh = mfma32(o.ga[0], bp[0], zero);
 #pragma unroll
-      for (int ks = 1; ks < 5; ++ks) gh = mfma32(ga[ks], bp[ks], gh);
-      v16f g = mfma32(wa[0], zb0, zero);
-      g = mfma32(wa[1], zb1, g);
+      for (int ks = 1; ks < 5; ++ks) gh = mfma32(o.ga[ks], bp[ks], gh);
+      v16f g = mfma32(o.wa[0], zb0, zero);
+      g = mfma32(o.wa[1], zb1, g);
 #pragma unroll
       for (int r = 0; r < 16; ++r) h[r] = fmaf(gh[r], g[r], h[r]);
+    };
+    if (sub < cn) {
+      EdgeOps ea, eb;
+      fetch(sub, ea);
+      for (int k = sub; k < cn; k += 2 * WPT) {
+        fetch(k + WPT, eb);
+        __builtin_amdgcn_sched_barrier(0);
+        product(k, ea);
+        if (k + WPT >= cn) break;
+        fetch(k + 2 * WPT, ea);
+        __builtin_amdgcn_sched_barrier(0);
+        product(k + WPT, eb);
+      }
     }
   }
 #pragma unroll
