@@ -88,9 +88,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // the same edge.  So each instruction adds R_e[h] T_e[u] for 64 / U edges x
 // U channels x 4 features with no idle rows, and the edge classes are summed
 // across lanes once at the end.  The receiver's sender indices, Y rows and R
-// rows are staged in LDS; x channels are gathered per step (BATCH steps at a
-// time; one measured best, since the accumulators already take most of the
-// registers).
+// rows are staged in LDS; x channels are gathered per step, software-
+// pipelined (the next step's gathers in flight during this step's arithmetic:
+// 9 registers, where gathering two steps before computing them cost more
+// occupancy than it hid).
 template <class S, int U, int H>
 __global__ void __launch_bounds__(256)
     k_fc_state(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
@@ -99,7 +100,6 @@ __global__ void __launch_bounds__(256)
   constexpr int EPI = 64 / U;                      // edges per instruction (edge classes)
   constexpr int NG = 4;
   constexpr int CH = 128;                          // edges staged in LDS at a time
-  constexpr int BATCH = 1;                         // steps whose gathers are in flight together
   static_assert(H == 8 && (U == 16 || U == 32 || U == 64), "fc state tiling");
   constexpr PathGroups<S, NG> PG = make_groups<S, NG>();
   __shared__ int cs[CH];
@@ -123,40 +123,46 @@ __global__ void __launch_bounds__(256)
       for (int k = t; k < cn * S::YC; k += 256) ys[k] = Y[(size_t)c0 * S::YC + k];
       for (int k = t; k < cn * H; k += 256) rs[k] = R[(size_t)c0 * H + k];
       __syncthreads();
-      for (int s0 = 0; s0 * EPI < cn; s0 += BATCH) {
-        float xr[BATCH][S::XC];
+      auto xload = [&](int s0, float (&xr)[S::XC]) {
+        const int e = s0 * EPI + ec;
+        load_x_channel<S, U>(x, cs[e < cn ? e : cn - 1], u, xr);
+      };
+      auto step = [&](int s0, const float (&xr)[S::XC]) {
+        const int e = s0 * EPI + ec;
+        const bool ok = e < cn;
+        const int ee = ok ? e : cn - 1;
+        float yr[S::YC];
 #pragma unroll
-        for (int bb = 0; bb < BATCH; ++bb) {
-          const int e = (s0 + bb) * EPI + ec;
-          load_x_channel<S, U>(x, cs[e < cn ? e : cn - 1], u, xr[bb]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int bb = 0; bb < BATCH; ++bb) {
-          const int e = (s0 + bb) * EPI + ec;
-          const bool ok = e < cn;
-          const int ee = ok ? e : cn - 1;
-          float yr[S::YC];
-#pragma unroll
-          for (int b = 0; b < S::YC; ++b) yr[b] = ys[ee * S::YC + b];
-          const float a0 = ok ? rs[ee * H + p4] : 0.f, a1 = ok ? rs[ee * H + 4 + p4] : 0.f;
-          float tv[NT];
-          static_for<NPP>([&](auto PP) {
-            constexpr PathInfo pi = S::paths.p[P0 + PP];
-            using T = CgPath<pi.l1, pi.l2, pi.l3>;
-            constexpr int D3 = 2 * pi.l3 + 1, OFF = comp_off<S>(P0, P0 + PP);
-            static_for<D3>([&](auto C) { tv[OFF + C] = 0.f; });
-            static_for<T::nnz>([&](auto N) {
-              constexpr Nz z = T::table.e[N];
-              tv[OFF + z.c] = fmaf(z.v, xr[bb][pi.xo + z.a] * yr[pi.yo + z.b], tv[OFF + z.c]);
-            });
+        for (int b = 0; b < S::YC; ++b) yr[b] = ys[ee * S::YC + b];
+        const float a0 = ok ? rs[ee * H + p4] : 0.f, a1 = ok ? rs[ee * H + 4 + p4] : 0.f;
+        float tv[NT];
+        static_for<NPP>([&](auto PP) {
+          constexpr PathInfo pi = S::paths.p[P0 + PP];
+          using T = CgPath<pi.l1, pi.l2, pi.l3>;
+          constexpr int D3 = 2 * pi.l3 + 1, OFF = comp_off<S>(P0, P0 + PP);
+          static_for<D3>([&](auto C) { tv[OFF + C] = 0.f; });
+          static_for<T::nnz>([&](auto N) {
+            constexpr Nz z = T::table.e[N];
+            tv[OFF + z.c] = fmaf(z.v, xr[pi.xo + z.a] * yr[pi.yo + z.b], tv[OFF + z.c]);
           });
+        });
 #pragma unroll
-          for (int k = 0; k < NT; ++k) {
-            acc[k][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, tv[k], acc[k][0], 0, 0, 0);
-            acc[k][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, tv[k], acc[k][1], 0, 0, 0);
-          }
+        for (int k = 0; k < NT; ++k) {
+          acc[k][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, tv[k], acc[k][0], 0, 0, 0);
+          acc[k][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, tv[k], acc[k][1], 0, 0, 0);
         }
+      };
+      // the next step's gathers are issued before this step's arithmetic
+      float xa[S::XC], xb[S::XC];
+      xload(0, xa);
+      for (int s0 = 0; s0 * EPI < cn; s0 += 2) {
+        xload(s0 + 1, xb);
+        __builtin_amdgcn_sched_barrier(0);
+        step(s0, xa);
+        if ((s0 + 1) * EPI >= cn) break;
+        xload(s0 + 2, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        step(s0 + 1, xb);
       }
     }
     // sum the edge classes (lanes u, u + U, ...), then lanes of class 0 store
@@ -506,12 +512,11 @@ __global__ void __launch_bounds__(256)
       for (int k = t; k < cn * S::YC; k += 256) ys[k] = Y[(size_t)c0 * S::YC + k];
       for (int k = t; k < cn * H; k += 256) rs[k] = R[(size_t)c0 * H + k];
       __syncthreads();
-      for (int s0 = 0; s0 * EPI < cn; ++s0) {
+      auto body = [&](int s0, const float (&xr)[S::XC]) {
         const int e = s0 * EPI + ec;
         const bool ok = e < cn;
         const int ee = ok ? e : cn - 1;
-        float xr[S::XC], yr[S::YC], rr[H];
-        load_x_channel<S, U>(x, cs[ee], u, xr);
+        float yr[S::YC], rr[H];
 #pragma unroll
         for (int b = 0; b < S::YC; ++b) yr[b] = ys[ee * S::YC + b];
 #pragma unroll
@@ -549,6 +554,22 @@ __global__ void __launch_bounds__(256)
           for (int j = 0; j < NF; ++j)
             if (j < share.len) red[G][e][share.first + j] = acc[j];
         }
+      };
+      // the next step's gathers are issued before this step's arithmetic
+      auto pload = [&](int s0, float (&xv)[S::XC]) {
+        const int e = s0 * EPI + ec;
+        load_x_channel<S, U>(x, cs[e < cn ? e : cn - 1], u, xv);
+      };
+      float xa[S::XC], xb[S::XC];
+      pload(0, xa);
+      for (int s0 = 0; s0 * EPI < cn; s0 += 2) {
+        pload(s0 + 1, xb);
+        __builtin_amdgcn_sched_barrier(0);
+        body(s0, xa);
+        if ((s0 + 1) * EPI >= cn) break;
+        pload(s0 + 2, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        body(s0 + 1, xb);
       }
       __syncthreads();
       for (int k = t; k < cn * NR; k += 256) {
@@ -634,12 +655,11 @@ __global__ void __launch_bounds__(256)
         ys[k] = Y[(size_t)t_perm[c0 + k / S::YC] * S::YC + k % S::YC];
       for (int k = t; k < cn * H; k += 256) rs[k] = R[(size_t)t_perm[c0 + k / H] * H + k % H];
       __syncthreads();
-      for (int s0 = 0; s0 * EPI < cn; ++s0) {
+      auto body = [&](int s0, const float (&gr)[S::OC]) {
         const int e = s0 * EPI + ec;
         const bool ok = e < cn;
         const int ee = ok ? e : cn - 1;
-        float gr[S::OC], yr[S::YC];
-        load_o_channel<S, U>(gout, rc[ee], v, gr);
+        float yr[S::YC];
 #pragma unroll
         for (int b = 0; b < S::YC; ++b) yr[b] = ys[ee * S::YC + b];
         const float a0 = ok ? rs[ee * H + p4] : 0.f, a1 = ok ? rs[ee * H + 4 + p4] : 0.f;
@@ -660,6 +680,22 @@ __global__ void __launch_bounds__(256)
           acc[q][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, gt[q], acc[q][0], 0, 0, 0);
           acc[q][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, gt[q], acc[q][1], 0, 0, 0);
         }
+      };
+      // the next step's gathers are issued before this step's arithmetic
+      auto pload = [&](int s0, float (&xv)[S::OC]) {
+        const int e = s0 * EPI + ec;
+        load_o_channel<S, U>(gout, rc[e < cn ? e : cn - 1], v, xv);
+      };
+      float xa[S::OC], xb[S::OC];
+      pload(0, xa);
+      for (int s0 = 0; s0 * EPI < cn; s0 += 2) {
+        pload(s0 + 1, xb);
+        __builtin_amdgcn_sched_barrier(0);
+        body(s0, xa);
+        if ((s0 + 1) * EPI >= cn) break;
+        pload(s0 + 2, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        body(s0 + 1, xb);
       }
     }
 #pragma unroll
