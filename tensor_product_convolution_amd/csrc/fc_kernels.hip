@@ -459,8 +459,20 @@ __global__ void __launch_bounds__(256)
   const int KK = H * lay.npk[k] * U;
   const int nrb = (n_nodes * lay.d3[k] + kRowBlock - 1) / kRowBlock;
   const float* pk = part + plan_part.base[k] + (size_t)((h * lay.npk[k] + pl) * U + u) * U + v;
+  const size_t stride = (size_t)KK * U;
+  // eight independent loads in flight per step (partials of blocks rb, rb + 1,
+  // ... summed in block order, so the result does not depend on the grouping
+  // of the loads)
   float a = 0.f;
-  for (int rb = 0; rb < nrb; ++rb) a += pk[(size_t)rb * KK * U];
+  int rb = 0;
+  for (; rb + 8 <= nrb; rb += 8) {
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = pk[(rb + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a += q[j];
+  }
+  for (; rb < nrb; ++rb) a += pk[rb * stride];
   gTheta[idx] = a;
 }
 
