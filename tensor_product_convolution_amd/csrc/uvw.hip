@@ -219,8 +219,17 @@ __global__ void __launch_bounds__(256)
   const int k = blockIdx.y;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= UU) return;
+  // eight loads in flight at a time, added in block order
   float s = 0.f;
-  for (int b = sp.start[k]; b < sp.start[k + 1]; ++b) s += part[(size_t)b * UU + e];
+  int b = sp.start[k];
+  for (; b + 8 <= sp.start[k + 1]; b += 8) {
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = part[(size_t)(b + j) * UU + e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += q[j];
+  }
+  for (; b < sp.start[k + 1]; ++b) s += part[(size_t)b * UU + e];
   out[(size_t)k * UU + e] = s;
 }
 
