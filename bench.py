@@ -73,7 +73,8 @@ GAUNT_SOURCES = ("gaunt.hip",)
 FP32_MFMA_PEAK_TFLOPS = 157.3
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_{}.txt")
 KERNEL_SOURCES = ("conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
-RADIAL_SOURCES = ("radial_kernels.hpp", "conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
+RADIAL_SOURCES = ("radial_kernels.hpp", "radial_l012_s2.hip", "uvw.hip", "conv_kernels.hpp", "sig.hpp",
+                  "cg_table.hpp")
 FC_SOURCES = ("fc_kernels.hip", "radial_kernels.hpp", "conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
 
 
