@@ -172,7 +172,34 @@ __device__ __forceinline__ void edge_bwd_recv(const float (&xin)[S::XC], const f
   });
 }
 
-// grad_x_a += sum_p w_p sum_nz C Y_b g_c
+// grad_x_a += sum_p w_p sum_nz C Y_b g_c, grouped by (input irrep, l2): the
+// paths of a group share the x block and the Y block, so
+//   V[a][b] = sum_{p in group} w_p sum_c C_p[a,b,c] g[c]
+// is formed first and folded with Y once per group, grad_x_a += sum_b Y_b
+// V[a][b] (the adjoint of the forward's shared products x_a Y_b): per edge and
+// channel nnz + sum_p (2l3+1) + the coupled (a, b) pairs of each group
+// (1,023 operations at lmax 3) instead of 2 nnz + sum_p (2l3+1) (1,378).
+template <class S, int P>
+constexpr bool group_first() {
+  if constexpr (P > 0) {
+    constexpr PathInfo a = S::paths.p[P - 1], b = S::paths.p[P];
+    return a.in != b.in || a.l2 != b.l2;
+  }
+  return true;
+}
+
+// does some path of the group (l1, l2, l3 = |l1-l2| .. min(l1+l2, lout))
+// couple x component a with Y component b?
+constexpr bool group_couples(int l1, int l2, int lout, int a, int b) {
+  const int lo = l1 > l2 ? l1 - l2 : l2 - l1, hi = l1 + l2 < lout ? l1 + l2 : lout;
+  for (int l3 = lo; l3 <= hi; ++l3)
+    for (int c = 0; c <= 2 * l3; ++c) {
+      const double v = real_cg_raw(l1, l2, l3, a, b, c);
+      if (v > kZeroTol || v < -kZeroTol) return true;
+    }
+  return false;
+}
+
 template <class S>
 __device__ __forceinline__ void edge_bwd_send(const float (&yin)[S::YC], const float (&wr)[S::NP],
                                               const float (&gin)[S::OC], float (&gx)[S::XC]) {
@@ -181,20 +208,31 @@ __device__ __forceinline__ void edge_bwd_send(const float (&yin)[S::YC], const f
   for (int b = 0; b < S::YC; ++b) yr[b] = yin[b];
 #pragma unroll
   for (int c = 0; c < S::OC; ++c) gr[c] = gin[c];
+  float V[7 * 7];   // one group's (2l1+1) x (2l2+1), l <= 3
   static_for<S::NP>([&](auto P) {
     constexpr PathInfo pi = S::paths.p[P];
     using T = CgPath<pi.l1, pi.l2, pi.l3>;
-    constexpr int D3 = 2 * pi.l3 + 1;
+    constexpr int D1 = 2 * pi.l1 + 1, D2 = 2 * pi.l2 + 1, D3 = 2 * pi.l3 + 1;
+    static_assert(D1 * D2 <= 7 * 7, "degrees up to 3");
+    if constexpr (group_first<S, P>()) static_for<D1 * D2>([&](auto I) { V[I] = 0.f; });
     float wg[D3];
     static_for<D3>([&](auto C) { wg[C] = wr[P] * gr[pi.ko + C]; });
     static_for<T::nnz>([&](auto N) {
       constexpr Nz z = T::table.e[N];
-      gx[pi.xo + z.a] = fmaf(z.v, yr[pi.yo + z.b] * wg[z.c], gx[pi.xo + z.a]);
+      V[z.a * D2 + z.b] = fmaf(z.v, wg[z.c], V[z.a * D2 + z.b]);
     });
-    if constexpr (kPhased<S> && group_end<S, P>()) {
-      launder(gx);
-      launder(yr);
-      launder(gr);
+    if constexpr (P + 1 == S::NP || group_end<S, P>()) {
+      static_for<D1>([&](auto A) {
+        static_for<D2>([&](auto B) {
+          if constexpr (group_couples(pi.l1, pi.l2, S::lmax_out, A, B))
+            gx[pi.xo + A] = fmaf(yr[pi.yo + B], V[A * D2 + B], gx[pi.xo + A]);
+        });
+      });
+      if constexpr (kPhased<S>) {
+        launder(gx);
+        launder(yr);
+        launder(gr);
+      }
     }
   });
 }
