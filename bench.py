@@ -258,7 +258,7 @@ def main():
                     help="short run for rocprofv3 counter passes: a few steps plus a 512 MiB copy")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the receiver-range sharding is a design, not code). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
