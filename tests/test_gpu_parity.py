@@ -198,6 +198,29 @@ def test_conv_parity(tpc, name, n_nodes, mul, bwd):
         assert np.max(np.abs(res["gr"] - gr)) <= TOL * np.max(np.abs(gr))
 
 
+def test_conv_parity_hub_graph_small_signature(tpc):
+    """The 32-channel lmax-2 signature on a power-law graph past the small-graph
+    threshold: hubs of up to 256 edges walked by one forward wave, four
+    receiver-pass waves and one sender-pass wave per node."""
+    say("conv parity mid signature on a Zipf graph, 1100 nodes")
+    plan, op = plans("mid")
+    wl = make_workload("mid", dims_of(op), n_nodes=1100, seed=4)
+    gw = make_workload("zipf", dims_of(op), n_nodes=1100, seed=4, graph_only=True)
+    wl.src, wl.dst, wl.r = gw.src, gw.dst, gw.r
+    rng = np.random.default_rng(5)
+    wl.w = (rng.normal(size=(len(wl.src), op.n_paths, op.U)) / np.sqrt(op.n_paths)).astype(np.float32)
+    assert np.bincount(wl.dst, minlength=wl.n_nodes).max() >= 100
+    res = run_gpu(tpc, plan, wl, True)
+    Y = oracle.sh_real(op.lmax_sh, wl.r)
+    ref = oracle.tp_conv_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w)
+    assert block_err(res["out"], ref, out_blocks(op)) <= TOL
+    gx, gY, gw_ = oracle.tp_conv_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w, wl.g)
+    p = res["perm"]
+    assert block_err(res["gx"], gx, in_blocks(op)) <= TOL
+    assert block_err(res["gY"], gY[p], y_blocks(op)) <= TOL
+    assert w_err(res["gw"], gw_[p]) <= TOL
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled rows
 
