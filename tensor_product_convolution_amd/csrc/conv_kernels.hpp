@@ -535,14 +535,18 @@ struct Cfg {
   static constexpr int depth(int nl, int buf, int waves) {
     return (nl <= 63 && 2 * buf * waves <= 64 * 1024) ? 2 : 1;
   }
-  static constexpr bool fits(int buf, int nbuf, int waves) { return buf * nbuf * waves <= 64 * 1024; }
+  static constexpr bool fits(int buf, int nbuf, int waves) { return buf * nbuf * waves <= 64 * 1024;
+  }
+  // waves per workgroup of each pass (one if a single buffer per wave for two
+  // waves would not fit)
   static constexpr int LDS = 64 * 1024;
-  // Waves per workgroup of each pass (measured).  The forward takes one wave
-  // up to 32 channels on graphs that fill the chip (no cross-wave reduction;
-  // 23.3 against 24.2 us on the 1,536-atom graph with two) and two on small
-  // graphs (WPB_F2), where the latency of one workgroup is that of the launch;
-  // large signatures take four where their single buffers fit (164 against
-  // 172 us for the lmax-3 forward, 1.88 against 1.97 ms on the Zipf graph).
+  // the forward takes one wave per workgroup up to 32 channels on graphs that
+  // fill the chip (no cross-wave reduction; 23.3 against 24.2 us on the
+  // 1,536-atom graph with two) and two on small graphs (WPB_F2), where the
+  // latency of one workgroup is that of the launch
+  // (large signatures take four waves where their single buffers fit: 164
+  // against 172 us for the lmax-3 forward, 1.88 against 1.97 ms on the Zipf
+  // graph)
   static constexpr int WPB_F2 = 2 * R::BUF <= LDS ? 2 : 1;
   static constexpr int WPB_F = kPhased<S> ? (fits(R::BUF, 1, 4) ? 4 : WPB_F2) : (U <= 32 ? 1 : WPB_F2);
   // the receiver pass takes four waves where their buffers fit (shorter
