@@ -249,9 +249,12 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     const bool valid = has && q < end;
     const int qc = has ? (q < end ? q : end - 1) : 0;
     const int j = has ? col[qc] : 0;
-    float bq[NB / 4], hB[NH / 4], ds[NH / 4], yr[S::YC], gy[S::YC];
+    float hB[NH / 4], yr[S::YC], gy[S::YC];
     const float rl = has ? r_len[qc] : 1.f;
-    hidden_T<NB, NH>(rl, valid, rp, w1a, g, bq, hB, ds);
+    {
+      float bq0[NB / 4], ds0[NH / 4];               // recomputed after the chunks
+      hidden_T<NB, NH>(rl, valid, rp, w1a, g, bq0, hB, ds0);
+    }
 #pragma unroll
     for (int t = 0; t < S::YC; ++t) {
       yr[t] = has ? Y[(size_t)qc * S::YC + t] : 0.f;
@@ -335,6 +338,16 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     if (grad_Y && g == 0 && valid) {
 #pragma unroll
       for (int t = 0; t < S::YC; ++t) grad_Y[(size_t)q * S::YC + t] = gy[t];
+    }
+    // The basis values and SiLU derivatives are evaluated again here rather
+    // than kept through the chunk loop (their 18 registers would spill); the
+    // empty asm hides that the edge length is the same, so the two evaluations
+    // are not merged.
+    float bq[NB / 4], ds[NH / 4];
+    {
+      float rl2 = rl, hB2[NH / 4];
+      asm volatile("" : "+v"(rl2));
+      hidden_T<NB, NH>(rl2, valid, rp, w1a, g, bq, hB2, ds);
     }
     // grad_pre (zero for an invalid edge) in the K-slot order of the hidden values
     float gp[NH / 4];
