@@ -95,6 +95,10 @@ def algorithmic_bytes(N, E, P, U, ysh, xdim, outdim):
         "bwd_send": E * (4 * P * U + 4 * ysh + 8) + node,     # w, Y, t_perm, t_col in; grad_x out
         # compulsory bytes of the whole step: each array once
         "step": E * (8 * P * U + 8 * ysh + 4) + 4 * N * (2 * xdim + 2 * outdim + 1),
+        # second-order backward, each array once: w, gg_w, Y, gg_Y, col, t_perm,
+        # t_col in, d_w and d_Y out; x, gg_x, grad_out and both row pointers in,
+        # d_x and d_grad_out out
+        "double_bwd": E * (12 * P * U + 12 * ysh + 12) + 4 * N * (3 * xdim + 2 * outdim + 2),
     }
 
 
@@ -382,6 +386,8 @@ def main():
         "bwd_ms": extra_ms.get("bwd"),
         "bwd_note": "one backward call (receiver then sender pass), per call",
         "double_bwd_ms": extra_ms.get("double_bwd"),
+        "double_bwd_hbm_frac": (None if "double_bwd" not in extra_ms else
+                                ab["double_bwd"] / (extra_ms["double_bwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS),
         "double_bwd_note": "second-order backward (dx, dY, dw, d grad_out for cotangents of all "
                            "three first-order outputs), per call; not part of the step",
         "forces_ms": extra_ms.get("forces"),

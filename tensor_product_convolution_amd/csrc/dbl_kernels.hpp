@@ -12,8 +12,9 @@
 // operand replaced, so one receiver-grouped pass produces dg, dY and dw (the
 // Z-form of x against g serves both the ggY and the ggw term) and one
 // sender-grouped pass produces dx.  A missing cotangent counts as zero.
-// Lane map as in the first-order kernels (LaneMap): one wave per node, lanes
-// = (edge slot, channel); operands are read straight from global memory.
+// Lane map as in the first-order kernels (LaneMap): lanes = (edge slot,
+// channel), one or four waves per node; operands are read straight from
+// global memory.
 #pragma once
 
 namespace tpc {
@@ -52,21 +53,122 @@ __device__ __forceinline__ void load_wrow(const float* __restrict__ w, int e, in
   for (int p = 0; p < S::NP; ++p) wr[p] = w[((size_t)e * S::NP + p) * U + u];
 }
 
-// Receiver pass of the second-order backward: dg per receiver (first loop
-// over its edges), dY and dw per edge (second loop).  Each term's operands
-// are loaded just before it is computed so that large signatures do not hold
-// every operand of every term at once.
+// Whether one walk over a receiver's edges can hold every operand of every
+// term at once (one channel per lane, and the dg accumulator, the grad_out
+// row, both sender rows, the four edge rows and the dw/dY values of an edge
+// within about 160 registers); otherwise the receiver pass walks twice.
 template <class S, int U>
-__global__ void __launch_bounds__(64)
+constexpr bool dbl_one_walk() {
+  return LaneMap<U>::CPL == 1 && 2 * S::OC + 2 * S::XC + 3 * S::YC + 3 * S::NP <= 160;
+}
+
+// Waves per receiver in the receiver pass: with one walk, the waves of a
+// receiver take every NW-th step of its edges, which keeps several waves per
+// SIMD in flight on graphs of a few thousand nodes; the per-wave dg partials are
+// added in wave order through LDS.  The two-walk form keeps one wave.
+template <class S, int U>
+constexpr int dbl_recv_waves() { return dbl_one_walk<S, U>() ? 4 : 1; }
+
+// Receiver pass of the second-order backward: dg per receiver, dY and dw per
+// edge.  Where the signature allows it, one walk over the receiver's edges
+// reads each edge's rows once and produces all three; otherwise dg comes from
+// a first walk and dY, dw from a second, each term's operands loaded just
+// before it is computed so that large signatures do not hold every operand of
+// every term at once.  Per edge the terms are added in the same order either
+// way.
+template <class S, int U, int NW>
+__global__ void __launch_bounds__(64 * NW)
     k_dbl_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ w,
                const float* __restrict__ g, const float* __restrict__ ggx, const float* __restrict__ ggY,
                const float* __restrict__ ggw, float* __restrict__ dY, float* __restrict__ dw,
                float* __restrict__ dg) {
   using M = LaneMap<U>;
-  const int i = blockIdx.x, lane = threadIdx.x;
+  const int i = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
+  if constexpr (dbl_one_walk<S, U>()) {
+    __shared__ float red[NW > 1 ? NW - 1 : 1][M::LPE][S::OC];
+    const bool want_yw = dY || dw;
+    float acc[S::OC], gr[1][S::OC];
+#pragma unroll
+    for (int o = 0; o < S::OC; ++o) acc[o] = 0.f;
+    if (want_yw) load_orow<S, U>(g + (size_t)i * (U * S::OC), uu, gr);
+    for (int e0 = beg + wv * M::EPW; e0 < end; e0 += NW * M::EPW) {
+      const int e = e0 + slot;
+      const bool valid = e < end;
+      const int ec = valid ? e : end - 1;
+      const int j = col[ec];
+      float yr[S::YC], gyr[S::YC], wr[S::NP], gwr[S::NP], xr[1][S::XC], gxr[1][S::XC];
+#pragma unroll
+      for (int b = 0; b < S::YC; ++b) {
+        yr[b] = Y[(size_t)ec * S::YC + b];
+        gyr[b] = ggY ? ggY[(size_t)ec * S::YC + b] : 0.f;
+      }
+      load_wrow<S, U>(w, ec, uu, wr);
+      if (ggw) load_wrow<S, U>(ggw, ec, uu, gwr);
+      else {
+#pragma unroll
+        for (int p = 0; p < S::NP; ++p) gwr[p] = 0.f;
+      }
+      load_xrow<S, U>(x + (size_t)j * (U * S::XC), uu, xr);
+      if (ggx) load_xrow<S, U>(ggx + (size_t)j * (U * S::XC), uu, gxr);
+      if (dg && valid) {
+        if (ggx) edge_fwd<S>(gxr[0], yr, wr, acc);     // out(ggx, Y, w)
+        if (ggY) edge_fwd<S>(xr[0], gyr, wr, acc);     // out(x, ggY, w)
+        if (ggw) edge_fwd<S>(xr[0], yr, gwr, acc);     // out(x, Y, ggw)
+      }
+      if (want_yw) {
+        float tw[S::NP], dyv[S::YC];
+#pragma unroll
+        for (int p = 0; p < S::NP; ++p) tw[p] = 0.f;
+#pragma unroll
+        for (int b = 0; b < S::YC; ++b) dyv[b] = 0.f;
+        if (ggx) edge_bwd_recv_acc<S>(gxr[0], yr, wr, gr[0], tw, dyv);     // gw(ggx, Y, g), gY(ggx, w, g)
+        if (ggY || ggw) edge_bwd_recv_acc<S>(xr[0], gyr, gwr, gr[0], tw, dyv);  // gw(x, ggY, g), gY(x, ggw, g)
+        if (dw && valid) {
+#pragma unroll
+          for (int p = 0; p < S::NP; ++p) dw[((size_t)e * S::NP + p) * U + uu] = tw[p];
+        }
+        if (dY) {
+          lane_sum_halving<S::YC, M::LPE / 2>(dyv, lane);
+          if (valid) {
+            const HalvingShare sh = halving_share(S::YC, M::LPE, lane);
+#pragma unroll
+            for (int r = 0; r < ls_final(S::YC, M::LPE); ++r)
+              if (r < sh.len) dY[(size_t)e * S::YC + sh.first + r] = dyv[r];
+          }
+        }
+      }
+    }
+    if (dg) {
+      cross_slot_sum<M::LPE, S::OC>(acc);
+      if constexpr (NW > 1) {
+        if (wv > 0 && slot == 0) {
+#pragma unroll
+          for (int o = 0; o < S::OC; ++o) red[wv - 1][uu][o] = acc[o];
+        }
+        __syncthreads();
+        if (wv == 0) {
+#pragma unroll
+          for (int v = 0; v < NW - 1; ++v)
+#pragma unroll
+            for (int o = 0; o < S::OC; ++o) acc[o] += red[v][uu][o];
+        }
+      }
+      if (wv == 0 && slot == 0) {
+        float* row = dg + (size_t)i * (U * S::OC);
+        static_for<S::NO>([&](auto K) {
+          constexpr OutInfo oi = S::outs.o[K];
+          constexpr int d = 2 * oi.l + 1;
+          static_for<d>([&](auto C) { row[U * oi.ko + uu * d + C] = acc[oi.ko + C]; });
+        });
+      }
+    }
+    return;
+  } else {
+    static_assert(NW == 1, "the two-walk receiver pass runs one wave per receiver");
+  }
   if (dg) {
     float acc[M::CPL][S::OC];
 #pragma unroll
@@ -176,19 +278,24 @@ __global__ void __launch_bounds__(64)
   }
 }
 
+// Waves per sender in the sender pass (each takes every NW-th step of the
+// sender's edges; the dx partials are added in wave order through LDS).
 template <class S, int U>
-__global__ void __launch_bounds__(64)
+constexpr int dbl_send_waves() { return LaneMap<U>::CPL == 1 ? 4 : 1; }
+
+template <class S, int U, int NW>
+__global__ void __launch_bounds__(64 * NW)
     k_dbl_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                const int32_t* __restrict__ t_col, const float* __restrict__ Y, const float* __restrict__ w,
                const float* __restrict__ g, const float* __restrict__ ggY, const float* __restrict__ ggw,
                float* __restrict__ dx) {
   using M = LaneMap<U>;
-  const int j = blockIdx.x, lane = threadIdx.x;
+  const int j = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
   float acc[M::CPL][S::XC];
   zero_xrow<S, U>(acc);
-  for (int e0 = beg; e0 < end; e0 += M::EPW) {
+  for (int e0 = beg + wv * M::EPW; e0 < end; e0 += NW * M::EPW) {
     const int t = e0 + slot;
     if (t < end) {
       const int e = t_perm[t], i = t_col[t];
@@ -216,7 +323,22 @@ __global__ void __launch_bounds__(64)
   }
 #pragma unroll
   for (int cc = 0; cc < M::CPL; ++cc) cross_slot_sum<M::LPE, S::XC>(acc[cc]);
-  if (slot == 0) {
+  if constexpr (NW > 1) {
+    static_assert(M::CPL == 1, "several waves per sender only with one channel per lane");
+    __shared__ float red[NW - 1][M::LPE][S::XC];
+    if (wv > 0 && slot == 0) {
+#pragma unroll
+      for (int a = 0; a < S::XC; ++a) red[wv - 1][uu][a] = acc[0][a];
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int v = 0; v < NW - 1; ++v)
+#pragma unroll
+        for (int a = 0; a < S::XC; ++a) acc[0][a] += red[v][uu][a];
+    }
+  }
+  if (wv == 0 && slot == 0) {
     float* row = dx + (size_t)j * (U * S::XC);
     static_for<S::NIN>([&](auto I) {
       constexpr int d = 2 * S::ls.v[I] + 1;
@@ -231,7 +353,8 @@ __global__ void __launch_bounds__(64)
 template <class S, int U>
 hipError_t launch_dbl_recv(const ConvArgs& a) {
   if (a.n_nodes == 0 || (!a.d_Y && !a.d_w && !a.d_g)) return hipSuccess;
-  hipLaunchKernelGGL((k_dbl_recv<S, U>), dim3(a.n_nodes), dim3(64), 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
+  constexpr int NW = dbl_recv_waves<S, U>();
+  hipLaunchKernelGGL((k_dbl_recv<S, U, NW>), dim3(a.n_nodes), dim3(64 * NW), 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
                      a.w, a.grad_out, a.gg_x, a.gg_Y, a.gg_w, a.d_Y, a.d_w, a.d_g);
   return hipGetLastError();
 }
@@ -239,7 +362,8 @@ hipError_t launch_dbl_recv(const ConvArgs& a) {
 template <class S, int U>
 hipError_t launch_dbl_send(const ConvArgs& a) {
   if (a.n_nodes == 0 || !a.d_x) return hipSuccess;
-  hipLaunchKernelGGL((k_dbl_send<S, U>), dim3(a.n_nodes), dim3(64), 0, a.stream, a.t_row_ptr, a.t_perm,
+  constexpr int NW = dbl_send_waves<S, U>();
+  hipLaunchKernelGGL((k_dbl_send<S, U, NW>), dim3(a.n_nodes), dim3(64 * NW), 0, a.stream, a.t_row_ptr, a.t_perm,
                      a.t_col, a.Y, a.w, a.grad_out, a.gg_Y, a.gg_w, a.d_x);
   return hipGetLastError();
 }

@@ -29,6 +29,10 @@ def test_algorithmic_bytes_of_the_1536_atom_workload():
     assert ab["step"] == 46080 * (8 * 480 + 72 + 4) + 4 * 1536 * (2 * 288 + 2 * 544 + 1)
     assert round(ab["fwd"] / 1e6, 1) == 95.4 and round(ab["bwd_recv"] / 1e6, 1) == 185.6
     assert round(ab["step"] / 1e6, 1) == 190.7
+    # second-order backward: three edge streams in (w, gg_w; Y, gg_Y), one out
+    # (d_w; d_Y), three index arrays; x, gg_x, d_x, grad_out, d_grad_out, two row pointers
+    assert ab["double_bwd"] == 46080 * (12 * 480 + 108 + 12) + 4 * 1536 * (3 * 288 + 2 * 544 + 2)
+    assert round(ab["double_bwd"] / 1e6, 1) == 283.0
 
 
 def test_fc_and_gaunt_counts():

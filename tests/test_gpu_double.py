@@ -84,3 +84,27 @@ def test_double_backward_missing_cotangents(tpc, which):
     wl = make_workload("mid", dims_of(op), n_nodes=150)
     cot = _cotangents(op, wl, 8)
     _check(op, wl, cot, _run(tpc, plan, wl, cot, which), which)
+
+
+@pytest.mark.parametrize("want", [("g",), ("Y", "w"), ("x", "w"), ("Y",)])
+def test_double_backward_output_subsets(tpc, want):
+    """Requesting only some outputs gives those outputs bit for bit as the full
+    call does (the receiver pass branches on which of dg, dY and dw are asked
+    for); the full call is the one checked against the oracle above."""
+    say(f"double backward outputs {want}")
+    plan, op = plans("mid")
+    wl = make_workload("mid", dims_of(op), n_nodes=150)
+    cot = _cotangents(op, wl, 9)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(plan.lmax_sh, tpc.gather_rows(T(wl.r), g.perm))
+    w = tpc.gather_rows(T(wl.w), g.perm)
+    args = (plan, g, T(wl.x), Y, w, T(wl.g), T(cot["x"]), tpc.gather_rows(T(cot["Y"]), g.perm),
+            tpc.gather_rows(T(cot["w"]), g.perm))
+    full = tpc.double_backward(*args)
+    part = tpc.double_backward(*args, want=want)
+    torch.cuda.synchronize()
+    for k, a, b in zip("xYwg", full, part):
+        if k in want:
+            assert torch.equal(a, b), k
+        else:
+            assert b is None
