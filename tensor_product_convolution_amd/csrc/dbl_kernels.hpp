@@ -28,6 +28,27 @@ __device__ __forceinline__ void cross_slot_sum(float (&v)[N]) {
     for (int t = 0; t < N; ++t) v[t] += __shfl_xor(v[t], m, 64);
 }
 
+// Adds the partial sums of waves 1..NW-1 (held by the lanes of edge slot 0)
+// to those of wave 0, in wave order, through LDS; every thread of the
+// workgroup calls it.
+template <int NW, int LPE, int N>
+__device__ __forceinline__ void add_wave_partials(float (&acc)[N], float (&red)[NW > 1 ? NW - 1 : 1][LPE][N],
+                                                  int wv, int slot, int uu) {
+  if constexpr (NW > 1) {
+    if (wv > 0 && slot == 0) {
+#pragma unroll
+      for (int t = 0; t < N; ++t) red[wv - 1][uu][t] = acc[t];
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int v = 0; v < NW - 1; ++v)
+#pragma unroll
+        for (int t = 0; t < N; ++t) acc[t] += red[v][uu][t];
+    }
+  }
+}
+
 template <class S, int U>
 __device__ __forceinline__ void zero_xrow(float (&v)[LaneMap<U>::CPL][S::XC]) {
 #pragma unroll
@@ -62,12 +83,12 @@ constexpr bool dbl_one_walk() {
   return LaneMap<U>::CPL == 1 && 2 * S::OC + 2 * S::XC + 3 * S::YC + 3 * S::NP <= 160;
 }
 
-// Waves per receiver in the receiver pass: with one walk, the waves of a
-// receiver take every NW-th step of its edges, which keeps several waves per
-// SIMD in flight on graphs of a few thousand nodes; the per-wave dg partials are
-// added in wave order through LDS.  The two-walk form keeps one wave.
-template <class S, int U>
-constexpr int dbl_recv_waves() { return dbl_one_walk<S, U>() ? 4 : 1; }
+// Waves per node in both passes (one channel per lane): the waves of a node
+// take every NW-th step of its edges, which keeps several waves per SIMD in
+// flight on graphs of a few thousand nodes and splits a hub's edges four ways;
+// the per-wave partial sums are added in wave order through LDS.
+template <int U>
+constexpr int dbl_waves() { return LaneMap<U>::CPL == 1 ? 4 : 1; }
 
 // Receiver pass of the second-order backward: dg per receiver, dY and dw per
 // edge.  Where the signature allows it, one walk over the receiver's edges
@@ -143,19 +164,7 @@ __global__ void __launch_bounds__(64 * NW)
     }
     if (dg) {
       cross_slot_sum<M::LPE, S::OC>(acc);
-      if constexpr (NW > 1) {
-        if (wv > 0 && slot == 0) {
-#pragma unroll
-          for (int o = 0; o < S::OC; ++o) red[wv - 1][uu][o] = acc[o];
-        }
-        __syncthreads();
-        if (wv == 0) {
-#pragma unroll
-          for (int v = 0; v < NW - 1; ++v)
-#pragma unroll
-            for (int o = 0; o < S::OC; ++o) acc[o] += red[v][uu][o];
-        }
-      }
+      add_wave_partials<NW, M::LPE, S::OC>(acc, red, wv, slot, uu);
       if (wv == 0 && slot == 0) {
         float* row = dg + (size_t)i * (U * S::OC);
         static_for<S::NO>([&](auto K) {
@@ -166,16 +175,16 @@ __global__ void __launch_bounds__(64 * NW)
       }
     }
     return;
-  } else {
-    static_assert(NW == 1, "the two-walk receiver pass runs one wave per receiver");
   }
+  static_assert(NW == 1 || M::CPL == 1, "several waves per receiver only with one channel per lane");
   if (dg) {
+    __shared__ float red[NW > 1 ? NW - 1 : 1][M::LPE][S::OC];
     float acc[M::CPL][S::OC];
 #pragma unroll
     for (int cc = 0; cc < M::CPL; ++cc)
 #pragma unroll
       for (int o = 0; o < S::OC; ++o) acc[cc][o] = 0.f;
-    for (int e0 = beg; e0 < end; e0 += M::EPW) {
+    for (int e0 = beg + wv * M::EPW; e0 < end; e0 += NW * M::EPW) {
       const int e = e0 + slot;
       if (e < end) {
         const int j = col[e];
@@ -210,7 +219,8 @@ __global__ void __launch_bounds__(64 * NW)
     }
 #pragma unroll
     for (int cc = 0; cc < M::CPL; ++cc) cross_slot_sum<M::LPE, S::OC>(acc[cc]);
-    if (slot == 0) {
+    add_wave_partials<NW, M::LPE, S::OC>(acc[0], red, wv, slot, uu);
+    if (wv == 0 && slot == 0) {
       float* row = dg + (size_t)i * (U * S::OC);
       static_for<S::NO>([&](auto K) {
         constexpr OutInfo oi = S::outs.o[K];
@@ -224,7 +234,7 @@ __global__ void __launch_bounds__(64 * NW)
   if (dY || dw) {
     float gr[M::CPL][S::OC];
     load_orow<S, U>(g + (size_t)i * (U * S::OC), uu, gr);
-    for (int e0 = beg; e0 < end; e0 += M::EPW) {
+    for (int e0 = beg + wv * M::EPW; e0 < end; e0 += NW * M::EPW) {
       const int e = e0 + slot;
       const bool valid = e < end;
       const int ec = valid ? e : end - 1;
@@ -278,11 +288,6 @@ __global__ void __launch_bounds__(64 * NW)
   }
 }
 
-// Waves per sender in the sender pass (each takes every NW-th step of the
-// sender's edges; the dx partials are added in wave order through LDS).
-template <class S, int U>
-constexpr int dbl_send_waves() { return LaneMap<U>::CPL == 1 ? 4 : 1; }
-
 template <class S, int U, int NW>
 __global__ void __launch_bounds__(64 * NW)
     k_dbl_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
@@ -323,21 +328,9 @@ __global__ void __launch_bounds__(64 * NW)
   }
 #pragma unroll
   for (int cc = 0; cc < M::CPL; ++cc) cross_slot_sum<M::LPE, S::XC>(acc[cc]);
-  if constexpr (NW > 1) {
-    static_assert(M::CPL == 1, "several waves per sender only with one channel per lane");
-    __shared__ float red[NW - 1][M::LPE][S::XC];
-    if (wv > 0 && slot == 0) {
-#pragma unroll
-      for (int a = 0; a < S::XC; ++a) red[wv - 1][uu][a] = acc[0][a];
-    }
-    __syncthreads();
-    if (wv == 0) {
-#pragma unroll
-      for (int v = 0; v < NW - 1; ++v)
-#pragma unroll
-        for (int a = 0; a < S::XC; ++a) acc[0][a] += red[v][uu][a];
-    }
-  }
+  static_assert(NW == 1 || M::CPL == 1, "several waves per sender only with one channel per lane");
+  __shared__ float red[NW > 1 ? NW - 1 : 1][M::LPE][S::XC];
+  add_wave_partials<NW, M::LPE, S::XC>(acc[0], red, wv, slot, uu);
   if (wv == 0 && slot == 0) {
     float* row = dx + (size_t)j * (U * S::XC);
     static_for<S::NIN>([&](auto I) {
@@ -353,7 +346,7 @@ __global__ void __launch_bounds__(64 * NW)
 template <class S, int U>
 hipError_t launch_dbl_recv(const ConvArgs& a) {
   if (a.n_nodes == 0 || (!a.d_Y && !a.d_w && !a.d_g)) return hipSuccess;
-  constexpr int NW = dbl_recv_waves<S, U>();
+  constexpr int NW = dbl_waves<U>();
   hipLaunchKernelGGL((k_dbl_recv<S, U, NW>), dim3(a.n_nodes), dim3(64 * NW), 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
                      a.w, a.grad_out, a.gg_x, a.gg_Y, a.gg_w, a.d_Y, a.d_w, a.d_g);
   return hipGetLastError();
@@ -362,7 +355,7 @@ hipError_t launch_dbl_recv(const ConvArgs& a) {
 template <class S, int U>
 hipError_t launch_dbl_send(const ConvArgs& a) {
   if (a.n_nodes == 0 || !a.d_x) return hipSuccess;
-  constexpr int NW = dbl_send_waves<S, U>();
+  constexpr int NW = dbl_waves<U>();
   hipLaunchKernelGGL((k_dbl_send<S, U, NW>), dim3(a.n_nodes), dim3(64 * NW), 0, a.stream, a.t_row_ptr, a.t_perm,
                      a.t_col, a.Y, a.w, a.grad_out, a.gg_Y, a.gg_w, a.d_x);
   return hipGetLastError();
