@@ -108,3 +108,40 @@ def test_double_backward_output_subsets(tpc, want):
             assert torch.equal(a, b), k
         else:
             assert b is None
+
+
+def test_double_backward_hub_isolated_and_empty(tpc):
+    """One receiver with 3,000 edges (its walk split over the waves of its
+    workgroup), 49 receivers and one sender without edges, against the oracle;
+    then a graph with no edges, whose node outputs are zeros."""
+    say("double backward hub receiver, isolated nodes")
+    plan, op = plans("mid")
+    rng = np.random.default_rng(11)
+
+    class W:
+        pass
+    wl = W()
+    wl.n_nodes, wl.n_edges = 50, 3000
+    wl.src = rng.integers(1, 50, 3000).astype(np.int32)
+    wl.dst = np.zeros(3000, np.int32)
+    wl.r = rng.normal(size=(3000, 3)).astype(np.float32)
+    wl.x = rng.normal(size=(50, op.xdim)).astype(np.float32)
+    wl.w = (rng.normal(size=(3000, op.n_paths, op.U)) / 4).astype(np.float32)
+    wl.g = rng.normal(size=(50, op.outdim)).astype(np.float32)
+    cot = _cotangents(op, wl, 12)
+    res = _run(tpc, plan, wl, cot)
+    _check(op, wl, cot, res, ("x", "Y", "w"))
+    _, dx, _, _, dg = res
+    assert np.all(dg[1:] == 0) and np.all(dx[0] == 0)
+
+    say("double backward empty graph")
+    N = 7
+    g = tpc.graph_build(T(np.zeros(0, np.int32)), T(np.zeros(0, np.int32)), N)
+    Y = torch.zeros(0, op.ysh, device="cuda")
+    w = torch.zeros(0, op.n_paths, op.U, device="cuda")
+    x = torch.randn(N, op.xdim, device="cuda")
+    gout = torch.randn(N, op.outdim, device="cuda")
+    dx, dY, dw, dg = tpc.double_backward(plan, g, x, Y, w, gout, torch.randn_like(x), Y, w)
+    torch.cuda.synchronize()
+    assert float(dx.abs().max()) == 0.0 and float(dg.abs().max()) == 0.0
+    assert dY.shape == (0, op.ysh) and dw.shape == (0, op.n_paths, op.U)
