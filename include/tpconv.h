@@ -44,7 +44,13 @@
  * Launches are asynchronous on the given stream; device faults surface at
  * the caller's next synchronisation.  tp_conv_last_error() describes the
  * last failure on the calling thread.  Outputs are overwritten, never
- * accumulated.  Device pointers must be 4-byte aligned.
+ * accumulated.  Device pointers must be 4-byte aligned; where an entry point
+ * stages rows with 16-byte loads its comment says which pointers must be
+ * 16-byte aligned, and a misaligned one is rejected with TP_ERR_ARG.
+ *
+ * Helper entry points that no page passage defines (plan inspection, buffer
+ * sizes, the gather into receiver order, the error text) exist so that a
+ * caller can size and lay out its buffers; their comments say so.
  */
 #ifndef TPCONV_H
 #define TPCONV_H
@@ -118,27 +124,35 @@ tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lma
                               int32_t lmax_out, int32_t mode, const tp_plan_opts* opts);
 
 /* Sizes of a plan.  Any output pointer may be NULL.  out_irreps receives the
- * output irreps string (NUL-terminated; TP_ERR_ARG if cap is too small). */
+ * output irreps string (NUL-terminated; TP_ERR_ARG if cap is too small).
+ * Helper: the sizes a caller needs to allocate its arrays. */
 tp_status tp_conv_plan_info(tp_plan_t plan, int32_t* n_paths, int32_t* mul, int32_t* xdim,
                             int32_t* ysh, int32_t* outdim, int32_t* nnz, char* out_irreps,
                             size_t out_irreps_cap);
 
-/* Path list: for path p, l1l2l3k[4p..4p+3] = (l1, l2, l3, output irrep index). */
+/* Path list: for path p, l1l2l3k[4p..4p+3] = (l1, l2, l3, output irrep index).
+ * Helper for inspection and tests; the path order is the plan's reading of
+ * the "all paths" of the path-aggregated product ("FlashTP", Abstract). */
 tp_status tp_conv_plan_paths(tp_plan_t plan, int32_t* l1l2l3k);
 
 /* CG nonzeros of the plan, path by path, (a, b, c) lexicographic within a
- * path: pabc[4n..4n+3] = (p, a, b, c), val[n] = coefficient (float64). */
+ * path: pabc[4n..4n+3] = (p, a, b, c), val[n] = coefficient (float64).
+ * Helper for inspection and tests: the sparse table the kernels carry as
+ * immediates ("FlashTP", Abstract: only the nonzero coefficients are used). */
 tp_status tp_conv_plan_cg(tp_plan_t plan, int16_t* pabc, double* val);
 
+/* Frees a plan (NULL is ignored).  Helper: ownership of the plan's table. */
 void tp_conv_plan_destroy(tp_plan_t plan);
 
 /* Dense real CG tensor of one path, out[(a*(2l2+1) + b)*(2l3+1) + c], for
  * degrees up to 6 (host only).  TP_ERR_ARG if a degree is out of range; the
- * tensor is all zeros when the triangle rule fails. */
+ * tensor is all zeros when the triangle rule fails.  Helper: the coupling
+ * tensor of the product under the conventions above, for callers and tests. */
 tp_status tp_cg_real(int32_t l1, int32_t l2, int32_t l3, double* out);
 
 /* ---- graph (device) --------------------------------------------------------
- * Workspace bytes tp_conv_graph_build needs for (n_nodes, n_edges). */
+ * Workspace bytes tp_conv_graph_build needs for (n_nodes, n_edges).  Helper:
+ * sizes the caller-owned scratch of the sort. */
 tp_status tp_conv_graph_workspace(int32_t n_nodes, int32_t n_edges, size_t* bytes);
 
 #define TP_GRAPH_CHECK 1   /* verify every src/dst is in [0, N); synchronises */
@@ -151,14 +165,18 @@ tp_status tp_conv_graph_workspace(int32_t n_nodes, int32_t n_edges, size_t* byte
  * Workload That Rewrites Molecular Physics", section "What Makes MLFF
  * Workloads Structurally Different").  ws must hold
  * tp_conv_graph_workspace bytes.  Without TP_GRAPH_CHECK, indices outside
- * [0, N) give an unspecified grouping (never an out-of-bounds write). */
+ * [0, N) give an unspecified grouping: the build never writes out of
+ * bounds, and col and t_col are clamped into [0, N), so later calls on the
+ * graph never read out of bounds either (their results are meaningless). */
 tp_status tp_conv_graph_build(const int32_t* src, const int32_t* dst, int32_t n_edges,
                               int32_t n_nodes, int32_t* row_ptr, int32_t* col, int32_t* perm,
                               int32_t* t_row_ptr, int32_t* t_perm, int32_t* t_col, void* ws,
                               size_t ws_bytes, int32_t flags, hipStream_t stream);
 
 /* out[q, :] = in[perm[q], :] for q < n_rows, rows of row_words 32-bit words
- * (device pointers).  Puts edge-sized inputs into receiver-sorted order. */
+ * (device pointers).  Puts edge-sized inputs into receiver-sorted order.
+ * Helper: the layout every edge-sized argument uses (see above); perm must
+ * come from tp_conv_graph_build (its entries index rows of in). */
 tp_status tp_conv_gather_rows(const void* in, const int32_t* perm, int64_t n_rows,
                               int64_t row_words, void* out, hipStream_t stream);
 
@@ -175,14 +193,20 @@ tp_status tp_conv_sph_harm(int32_t lmax, const float* r, int32_t n_edges, float*
  * Forward: out = conv(x, Y, w) for the edges of `graph` (formula above).
  * One pass streams each receiver's edges, keeps the receiver's outputs in
  * registers and LDS and stores each output row once; no edge-sized
- * intermediate is written ("Sobek", Abstract; "FlashTP", Abstract). */
+ * intermediate is written ("Sobek", Abstract; "FlashTP", Abstract).
+ * x and w must be 16-byte aligned (TP_ERR_ARG). */
 tp_status tp_conv_forward(tp_plan_t plan, const tp_graph* graph, const float* x,
                           const float* Y, const float* w, float* out, hipStream_t stream);
 
 /* Backward: gradients of <grad_out, out> with respect to x, Y and w (exact
  * adjoint of the forward; "Sobek", Abstract, backward pass).  grad_x, grad_Y
  * or grad_w may be NULL to skip that output.  grad_x [N][xdim]; grad_Y
- * [E][ysh] and grad_w [E][P][U] in receiver-sorted order. */
+ * [E][ysh] and grad_w [E][P][U] in receiver-sorted order.  With grad_x and an
+ * edge gradient requested (lmax-2 signatures) one sender-grouped pass forms
+ * all of them, reading w and Y once; otherwise a receiver pass (grad_w,
+ * grad_Y) and a sender pass (grad_x).  grad_x needs the graph's sender
+ * grouping.  x, w and grad_out must be 16-byte aligned (TP_ERR_ARG).
+ * Deterministic: no atomics, fixed summation order. */
 tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x,
                            const float* Y, const float* w, const float* grad_out,
                            float* grad_x, float* grad_Y, float* grad_w, hipStream_t stream);
@@ -298,7 +322,8 @@ tp_status tp_conv_backward_gaunt(tp_plan_t plan, const tp_graph* graph, const fl
  *   out[i, k, v, c] = sum_u Wmix[k][u][v] in[i, k, u, c]       (in, out: [N][outdim])
  * The post-aggregation channel mixing of the radial-weight layer ("Sobek",
  * Abstract, on preserving multiplicity mixing).  in and out must not alias
- * and must be 16-byte aligned (whole node blocks move as 16-byte granules). */
+ * and must be 16-byte aligned (whole node blocks move as 16-byte granules;
+ * TP_ERR_ARG otherwise). */
 tp_status tp_conv_uvw_forward(tp_plan_t plan, int32_t n_nodes, const float* Wmix, const float* in,
                               float* out, hipStream_t stream);
 
@@ -306,7 +331,8 @@ tp_status tp_conv_uvw_forward(tp_plan_t plan, int32_t n_nodes, const float* Wmix
  *   grad_in[i, k, u, c] = sum_v Wmix[k][u][v] grad_out[i, k, v, c]   (NULL: skip)
  *   grad_Wmix[k][u][v]  = sum_{i,c} in[i, k, u, c] grad_out[i, k, v, c]  (NULL: skip)
  * grad_Wmix is reduced deterministically through ws (tp_conv_uvw_workspace
- * bytes). */
+ * bytes; helper that sizes it).  in, grad_out and grad_in must be 16-byte
+ * aligned (TP_ERR_ARG). */
 tp_status tp_conv_uvw_backward(tp_plan_t plan, int32_t n_nodes, const float* Wmix, const float* in,
                                const float* grad_out, float* grad_in, float* grad_Wmix, void* ws,
                                size_t ws_bytes, hipStream_t stream);
@@ -366,7 +392,8 @@ tp_status tp_conv_sph_harm_backward(int32_t lmax, const float* r, int32_t n_edge
                                     const float* grad_Y, const float* grad_rlen, float* grad_r,
                                     hipStream_t stream);
 
-/* Thread-local description of the last failure on this thread. */
+/* Thread-local description of the last failure on this thread (helper for
+ * error reporting; valid until the next failing call on the thread). */
 const char* tp_conv_last_error(void);
 
 #ifdef __cplusplus

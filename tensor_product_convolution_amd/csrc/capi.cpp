@@ -10,6 +10,7 @@
 #include <cctype>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -387,6 +388,15 @@ static tp_status check_graph(const tp_graph* g, bool need_sender) {
   return TP_OK;
 }
 
+// Rows of x, w and grad_out are staged with 16-byte global->LDS loads (and
+// node blocks of the channel mix are moved as 16-byte granules), so these
+// pointers must be 16-byte aligned.
+static bool misaligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return true;
+  return false;
+}
+
 tp_status tp_conv_forward(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
                           const float* w, float* out, hipStream_t stream) {
   if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward: plan is NULL");
@@ -394,6 +404,7 @@ tp_status tp_conv_forward(tp_plan_t plan, const tp_graph* graph, const float* x,
   if (s != TP_OK) return s;
   if (graph->n_nodes > 0 && (!x || !out)) return set_error(TP_ERR_ARG, "tp_conv_forward: x/out NULL");
   if (graph->n_edges > 0 && (!Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_forward: Y/w NULL");
+  if (misaligned16({x, w})) return set_error(TP_ERR_ARG, "tp_conv_forward: x and w must be 16-byte aligned");
   tpc::ConvArgs a;
   a.n_nodes = graph->n_nodes;
   a.n_edges = graph->n_edges;
@@ -420,6 +431,8 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   if (graph->n_edges > 0 && (!Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_backward: Y/w NULL");
   if (graph->n_edges > 0 && any_edge_grad && !x)
     return set_error(TP_ERR_ARG, "tp_conv_backward: x NULL");
+  if (misaligned16({x, w, grad_out}))
+    return set_error(TP_ERR_ARG, "tp_conv_backward: x, w and grad_out must be 16-byte aligned");
   tpc::ConvArgs a;
   a.n_nodes = graph->n_nodes;
   a.n_edges = graph->n_edges;
@@ -437,6 +450,12 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   a.grad_w = grad_w;
   a.stream = stream;
   if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_backward: not a channel-wise CG plan");
+  if (grad_x && any_edge_grad && graph->n_edges > 0 && plan->ks->bwd_fused) {
+    // every gradient from one sender-grouped pass: w and Y are read once
+    hipError_t e = plan->ks->bwd_fused(a);
+    if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward fused pass");
+    return TP_OK;
+  }
   hipError_t e = plan->ks->bwd_recv(a);
   if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward receiver pass");
   e = plan->ks->bwd_send(a);
@@ -712,6 +731,7 @@ tp_status tp_conv_uvw_forward(tp_plan_t plan, int32_t n_nodes, const float* Wmix
   if (n_nodes > 0 && (!Wmix || !in || !out))
     return set_error(TP_ERR_ARG, "tp_conv_uvw_forward: NULL pointer");
   if (in == out) return set_error(TP_ERR_ARG, "tp_conv_uvw_forward: in and out must differ");
+  if (misaligned16({in, out})) return set_error(TP_ERR_ARG, "tp_conv_uvw_forward: in and out must be 16-byte aligned");
   return tpc::uvw_forward(n_nodes, plan->mul, plan->outdim, plan->uvw, Wmix, in, out, false, stream);
 }
 
@@ -723,6 +743,8 @@ tp_status tp_conv_uvw_backward(tp_plan_t plan, int32_t n_nodes, const float* Wmi
   if (s != TP_OK) return s;
   if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_uvw_backward: negative size");
   if (n_nodes > 0 && (!Wmix || !grad_out)) return set_error(TP_ERR_ARG, "tp_conv_uvw_backward: NULL pointer");
+  if (misaligned16({in, grad_out, grad_in}))
+    return set_error(TP_ERR_ARG, "tp_conv_uvw_backward: in, grad_out and grad_in must be 16-byte aligned");
   if (grad_Wmix) {
     if (n_nodes > 0 && !in) return set_error(TP_ERR_ARG, "tp_conv_uvw_backward: in is NULL");
     if (!ws || ws_bytes < tpc::uvw_workspace_bytes(plan->uvw.n, plan->mul))

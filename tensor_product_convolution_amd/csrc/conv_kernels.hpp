@@ -14,13 +14,18 @@
 //     coalesced.  No atomics; the reduction order is fixed, so results are
 //     bitwise reproducible.
 // Backward:
-//   * receiver pass: with grad_out[i] in registers, each edge yields
-//     grad_w[e] (per lane) and grad_Y[e] (a recursive-halving sum over the
-//     edge's channel lanes), written once per edge -- these are requested
-//     outputs;
-//   * sender pass: each workgroup owns a sender j and walks its edges in the
-//     sender grouping, gathering grad_out of each receiver, and stores
-//     grad_x[j] once.  Again no atomics.
+//   * one pass (lmax-2 signatures, every gradient requested): each workgroup
+//     owns a sender j with x[j] in registers, walks its edges in the sender
+//     grouping, gathers grad_out of each receiver, writes grad_w[e] and
+//     grad_Y[e] at the edge's receiver-sorted position and stores grad_x[j]
+//     once, so w and Y are read once per backward;
+//   * otherwise a receiver pass: with grad_out[i] in registers, each edge
+//     yields grad_w[e] (per lane) and grad_Y[e] (a recursive-halving sum over
+//     the edge's channel lanes), written once per edge -- these are
+//     requested outputs;
+//   * and a sender pass: each workgroup owns a sender j and walks its edges
+//     in the sender grouping, gathering grad_out of each receiver, and stores
+//     grad_x[j] once.  No atomics anywhere.
 #pragma once
 #include "internal.hpp"
 #include "sig.hpp"
@@ -231,6 +236,122 @@ __device__ __forceinline__ void edge_bwd_send(const float (&yin)[S::YC], const f
       if constexpr (kPhased<S>) {
         launder(gx);
         launder(yr);
+        launder(gr);
+      }
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// All three backward terms of one edge and channel in one pass.
+//
+// Every CG nonzero C_p[a,b,c] of a path that lands on output component
+// o = ko(p) + c meets the upstream gradient only as the product C g_o, and its
+// magnitude |C| takes few distinct values per component.  So the distinct
+// scaled values gC = |C| g_o (|C| != 1) are formed once per edge and channel
+// and shared by every path on that output irrep; each nonzero is then one
+// fused multiply-add with a sign modifier for each of the two contractions:
+//   Z_p[b]  += sign(C) x_a gC     (grad_w_p = sum_b Y_b Z_p[b];
+//                                  grad_Y_b += w_p Z_p[b])
+//   V[a][b] += sign(C) w_p gC     (per (input irrep, l2) group;
+//                                  grad_x_a += sum_b Y_b V[a][b])
+// On the lmax-2 signature of three inputs this is 42 scalings + 2 x 137
+// nonzero FMAs + 102 + 81 folds, against 645 operations for the receiver-side
+// Z form and the sender-side grouped adjoint evaluated separately.
+template <class S>
+struct ScaledG {
+  struct Ent {
+    int o;
+    float v;
+  };
+  struct Table {
+    Ent e[512];
+    int n;
+  };
+  static constexpr Table build() {
+    Table t{};
+    t.n = 0;
+    for (int p = 0; p < S::NP; ++p) {
+      const PathInfo pi = S::paths.p[p];
+      const double sg = real_cg_sign(pi.l1, pi.l2, pi.l3);
+      for (int a = 0; a <= 2 * pi.l1; ++a)
+        for (int b = 0; b <= 2 * pi.l2; ++b)
+          for (int c = 0; c <= 2 * pi.l3; ++c) {
+            const float v = static_cast<float>(real_cg(pi.l1, pi.l2, pi.l3, a, b, c, sg));
+            const float m = v < 0.f ? -v : v;
+            if (m == 0.f || m == 1.f) continue;
+            const int o = pi.ko + c;
+            bool seen = false;
+            for (int q = 0; q < t.n; ++q)
+              if (t.e[q].o == o && t.e[q].v == m) seen = true;
+            if (!seen) t.e[t.n++] = Ent{o, m};
+          }
+    }
+    return t;
+  }
+  static constexpr Table table = build();
+  static constexpr int N = table.n;
+  static_assert(N <= 512, "scaled-gradient table");
+  // slot of (component o, magnitude m) in the table; -1 for m == 1
+  static constexpr int find(int o, float m) {
+    for (int q = 0; q < N; ++q)
+      if (table.e[q].o == o && table.e[q].v == m) return q;
+    return -1;
+  }
+};
+
+// ym: Y for the sender-side fold (zero on a slot whose grad_x share is
+// dropped); gw is assigned, gy and gx accumulate.
+template <class S>
+__host__ __device__ __forceinline__ void edge_bwd_all(const float (&xin)[S::XC], const float (&yr)[S::YC],
+                                                      const float (&ym)[S::YC], const float (&wr)[S::NP],
+                                                      const float (&gin)[S::OC], float (&gw)[S::NP],
+                                                      float (&gy)[S::YC], float (&gx)[S::XC]) {
+  using G = ScaledG<S>;
+  float xr[S::XC], gr[S::OC];
+#pragma unroll
+  for (int a = 0; a < S::XC; ++a) xr[a] = xin[a];
+#pragma unroll
+  for (int c = 0; c < S::OC; ++c) gr[c] = gin[c];
+  float gc[G::N > 0 ? G::N : 1];
+  static_for<G::N>([&](auto I) { gc[I] = G::table.e[I].v * gr[G::table.e[I].o]; });
+  float V[7 * 7];   // one group's (2l1+1) x (2l2+1), l <= 3
+  static_for<S::NP>([&](auto P) {
+    constexpr PathInfo pi = S::paths.p[P];
+    using T = CgPath<pi.l1, pi.l2, pi.l3>;
+    constexpr int D1 = 2 * pi.l1 + 1, D2 = 2 * pi.l2 + 1;
+    static_assert(D1 * D2 <= 7 * 7, "degrees up to 3");
+    if constexpr (group_first<S, P>()) static_for<D1 * D2>([&](auto I) { V[I] = 0.f; });
+    float z[D2];
+    static_for<D2>([&](auto B) { z[B] = 0.f; });
+    static_for<T::nnz>([&](auto Nn) {
+      constexpr Nz e = T::table.e[Nn];
+      constexpr int o = pi.ko + e.c;
+      constexpr float m = e.v < 0.f ? -e.v : e.v;
+      constexpr int gi = m == 1.f ? -1 : G::find(o, m);
+      static_assert(m == 1.f || gi >= 0, "scaled-gradient slot");
+      const float gv = gi >= 0 ? gc[gi >= 0 ? gi : 0] : gr[o];
+      const float xs = e.v < 0.f ? -xr[pi.xo + e.a] : xr[pi.xo + e.a];
+      const float ws = e.v < 0.f ? -wr[P] : wr[P];
+      z[e.b] = fmaf(xs, gv, z[e.b]);
+      V[e.a * D2 + e.b] = fmaf(ws, gv, V[e.a * D2 + e.b]);
+    });
+    float sw = 0.f;
+    static_for<D2>([&](auto B) { sw = fmaf(yr[pi.yo + B], z[B], sw); });
+    gw[P] = sw;
+    static_for<D2>([&](auto B) { gy[pi.yo + B] = fmaf(wr[P], z[B], gy[pi.yo + B]); });
+    if constexpr (P + 1 == S::NP || group_end<S, P>()) {
+      static_for<D1>([&](auto A) {
+        static_for<D2>([&](auto B) {
+          if constexpr (group_couples(pi.l1, pi.l2, S::lmax_out, A, B))
+            gx[pi.xo + A] = fmaf(ym[pi.yo + B], V[A * D2 + B], gx[pi.xo + A]);
+        });
+      });
+      if constexpr (kPhased<S>) {
+        launder(gx);
+        launder(gy);
+        launder(gw);
+        launder(xr);
         launder(gr);
       }
     }
@@ -506,6 +627,35 @@ __device__ __forceinline__ int wave_trips(int beg, int end, int wv) {
   return __builtin_amdgcn_readfirstlane(n);
 }
 
+// Per-wave window of an int32 index array (col, t_perm, t_col): lane t holds
+// the entry of the wave's position for step kbase + t / EPW, slot t % EPW
+// (clamped to the segment's last edge), so a step's indices are register
+// reads (v_readlane) instead of scalar loads.  A scalar load issued inside the
+// step loop shares its counter with the LDS reads, and the wait for those
+// would stall on every index line the scalar cache misses.  A window covers
+// 64 / EPW steps; longer walks reload it (a vector load, waited for once).
+template <int EPW, int SLOTS>
+struct IdxWindow {
+  static constexpr int STEPS = 64 / EPW;
+  int v = 0;
+  int kbase = 0;
+  __device__ __forceinline__ void load(const int32_t* __restrict__ a, int k00, int kb, int last, int lane) {
+    kbase = kb;
+    v = a[min(k00 + (kb + lane / EPW) * SLOTS + lane % EPW, last)];
+  }
+  // entry of slot r at wave step k; reloads first if k is past the window.
+  // The reload waits for itself on its own path, so that no load of v is
+  // pending where the paths meet (otherwise the code generator would wait
+  // for every vector-memory operation before each read of the window).
+  __device__ __forceinline__ int get(const int32_t* __restrict__ a, int k00, int k, int r, int last, int lane) {
+    if (k - kbase >= STEPS) {
+      load(a, k00, k, last, lane);
+      wait_vmcnt<0>();
+    }
+    return __builtin_amdgcn_readlane(v, (k - kbase) * EPW + r);
+  }
+};
+
 // wait for vmcnt <= ahead*NL + sg*NS with ahead, sg in [0, NA) x [0, NSG)
 template <int NA, int NSG, int NL, int NS>
 __device__ __forceinline__ void wait_steps(int ahead, int sg) {
@@ -596,21 +746,23 @@ __global__ void __launch_bounds__(WPB * 64)
     for (int o = 0; o < S::OC; ++o) acc[cc][o] = 0.f;
   const int trips = wave_trips<U, WPB>(beg, end, wv);
   char* mybuf = smem + wv * NBUF * T::BUF;
-  // first position of this wave (wave-uniform, so the index loads are scalar)
+  // first position of this wave (wave-uniform)
   const int q00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
   if (trips > 0) {
+    IdxWindow<EPW, SLOTS> wj;
+    wj.load(col, q00, 0, last, lane);
     int jn[EPW];
     // prologue: stage steps 0 .. NBUF-2
 #pragma unroll
     for (int b = 0; b < NBUF - 1; ++b) {
       if (b < trips) {
 #pragma unroll
-        for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + b * SLOTS + r, last)];
+        for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, b, r, last, lane);
         stage_recv<S, U>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
       }
     }
 #pragma unroll
-    for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + (NBUF - 1) * SLOTS + r, last)];
+    for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, NBUF - 1, r, last, lane);
     for (int k = 0; k < trips; ++k) {
       const int q0 = q00 + k * SLOTS;
       const char* cur = mybuf + (k % NBUF) * T::BUF;
@@ -624,9 +776,9 @@ __global__ void __launch_bounds__(WPB * 64)
       float xr[M::CPL][S::XC], yr[S::YC], wr[M::CPL][S::NP];
       read_recv<S, U>(cur, slot, uu, xr, yr, wr);
       __builtin_amdgcn_sched_barrier(0);
-      // senders of the next step to stage, loaded while this step computes
+      // senders of the next step to stage
 #pragma unroll
-      for (int r = 0; r < EPW; ++r) jn[r] = col[min(q0 + NBUF * SLOTS + r, last)];
+      for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, k + NBUF, r, last, lane);
       // only the receiver's last step can hold slots past its edges (they
       // re-read its last edge); their weights are zeroed there alone
       if (q0 + EPW > end) {
@@ -666,24 +818,27 @@ __global__ void __launch_bounds__(WPB * 64)
   const int last = end - 1;
   const int trips = wave_trips<U, WPB>(beg, end, wv);
   if (trips == 0) return;
+  const int q00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
+  IdxWindow<EPW, SLOTS> wj;
+  wj.load(col, q00, 0, last, lane);
   float gr[M::CPL][S::OC];
   load_orow<S, U>(g + (size_t)i * OD, uu, gr);
-  // grad_out must have landed before the pipelined loop starts: a wait for it
-  // inside the loop would also wait for the staging loads in flight
+  // grad_out (and the senders) must have landed before the pipelined loop
+  // starts: a wait for them inside the loop would also wait for the staging
+  // loads in flight
   wait_vmcnt<0>();
   char* mybuf = smem + wv * WAVE_LDS;
-  const int q00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
   int jn[EPW];
 #pragma unroll
   for (int b = 0; b < NBUF - 1; ++b) {
     if (b < trips) {
 #pragma unroll
-      for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + b * SLOTS + r, last)];
+      for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, b, r, last, lane);
       stage_recv<S, U>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
     }
   }
 #pragma unroll
-  for (int r = 0; r < EPW; ++r) jn[r] = col[min(q00 + (NBUF - 1) * SLOTS + r, last)];
+  for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, NBUF - 1, r, last, lane);
   // Results of step k are stored during step k+1, after its wait, straight
   // from registers; the number of store instructions per step is fixed (NST).
   float pgw[M::CPL][S::NP], pgy[C::ST_Y];
@@ -720,7 +875,7 @@ __global__ void __launch_bounds__(WPB * 64)
     read_recv<S, U>(cur, slot, uu, xr, yr, wr);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < EPW; ++r) jn[r] = col[min(q0 + NBUF * SLOTS + r, last)];
+    for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, k + NBUF, r, last, lane);
     float gy[S::YC];
 #pragma unroll
     for (int b = 0; b < S::YC; ++b) gy[b] = 0.f;
@@ -770,22 +925,25 @@ __global__ void __launch_bounds__(WPB * 64)
   char* mybuf = smem + wv * NBUF * T::BUF;
   const int k00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
   if (trips > 0) {
+    IdxWindow<EPW, SLOTS> wq, wi;
+    wq.load(t_perm, k00, 0, last, lane);
+    wi.load(t_col, k00, 0, last, lane);
     int qn[EPW], in[EPW];
 #pragma unroll
     for (int b = 0; b < NBUF - 1; ++b) {
       if (b < trips) {
 #pragma unroll
         for (int r = 0; r < EPW; ++r) {
-          qn[r] = t_perm[min(k00 + b * SLOTS + r, last)];
-          in[r] = t_col[min(k00 + b * SLOTS + r, last)];
+          qn[r] = wq.get(t_perm, k00, b, r, last, lane);
+          in[r] = wi.get(t_col, k00, b, r, last, lane);
         }
         stage_send<S, U>(mybuf + b * T::BUF, Y, w, g, qn, in, lane);
       }
     }
 #pragma unroll
     for (int r = 0; r < EPW; ++r) {
-      qn[r] = t_perm[min(k00 + (NBUF - 1) * SLOTS + r, last)];
-      in[r] = t_col[min(k00 + (NBUF - 1) * SLOTS + r, last)];
+      qn[r] = wq.get(t_perm, k00, NBUF - 1, r, last, lane);
+      in[r] = wi.get(t_col, k00, NBUF - 1, r, last, lane);
     }
     for (int k = 0; k < trips; ++k) {
       const int k0 = k00 + k * SLOTS;
@@ -816,8 +974,8 @@ __global__ void __launch_bounds__(WPB * 64)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < EPW; ++r) {
-        qn[r] = t_perm[min(k0 + NBUF * SLOTS + r, last)];
-        in[r] = t_col[min(k0 + NBUF * SLOTS + r, last)];
+        qn[r] = wq.get(t_perm, k00, k + NBUF, r, last, lane);
+        in[r] = wi.get(t_col, k00, k + NBUF, r, last, lane);
       }
       // only the sender's last step can hold slots past its edges
       if (k0 + EPW > end) {
@@ -830,6 +988,213 @@ __global__ void __launch_bounds__(WPB * 64)
 #pragma unroll
       for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_send<S>(yr, wr[cc], gr[cc], gx[cc]);
     }
+  }
+  __syncthreads();
+  block_reduce_store<U, WPB, S::XC, S::NIN>(gx, (float*)smem, grad_x + (size_t)j * XD, InBlocks<S>{});
+}
+
+// ---------------------------------------------------------------------------
+// Whole backward in one sender-grouped pass.
+//
+// A workgroup owns sender j with x[j] in registers and walks its edges in the
+// sender grouping; per edge e = (j -> i) it stages w[e], Y[e] and grad_out[i]
+// and forms all three gradients from them:
+//   grad_w[e] and grad_Y[e] exactly as the receiver pass (Z form), stored at
+//   the edge's receiver-sorted position q = t_perm[k] (rows of P*U weights
+//   stay whole, so the stores are full cache lines);
+//   grad_x[j] accumulated in registers as the sender pass does.
+// So w and Y are read once per backward and grad_out is the only gathered
+// operand ("Sobek", Abstract: the backward consumes edge-local products into
+// bounded node-side state; no edge-sized adjoint beyond the requested
+// grad_w / grad_Y).  A slot past the sender's edges works on its clamped
+// last edge: its grad_w / grad_Y equal the real slot's bit for bit (same
+// operands, same lane arithmetic), and its grad_x share is masked.
+// Results of step k are stored during step k+1, after its wait.
+// MODE bit 0: write grad_w; bit 1: write grad_Y.
+template <class S, int U>
+struct FusedCfg {
+  using Sd = SendStage<S, U>;
+  using C = Cfg<S, U>;
+  // four waves per sender, two staging buffers each (about 70 KB per
+  // workgroup at 32 channels: two workgroups share a compute unit's 160 KB);
+  // measured on the 1,536-atom graph against 1 to 4 waves and 1 to 3 buffers,
+  // which all land within 10 %: the pass moves about as many bytes per second
+  // as a plain device copy
+  static constexpr int NBUF = 2;
+  static constexpr int WPB = (4 * NBUF * Sd::BUF <= 80 * 1024) ? 4 : (2 * NBUF * Sd::BUF <= 80 * 1024 ? 2 : 1);
+};
+
+template <class S, int U, int WPB, int NBUF>
+struct FusedSmem {
+  static constexpr int XB = S::XC * U * 4;                      // the sender's x row, per wave
+  static constexpr int XR_OFF = NBUF * WPB * SendStage<S, U>::BUF;
+  static constexpr int STAGE = XR_OFF + WPB * ceil16(XB);
+  static constexpr int RED = WPB * LaneMap<U>::CPL * S::XC * 65 * 4;
+  static constexpr int BYTES = STAGE > RED ? STAGE : RED;
+};
+
+template <class S, int U, int WPB, int NBUF, int MODE>
+__global__ void __launch_bounds__(WPB * 64)
+    k_conv_bwd_fused(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
+                     const int32_t* __restrict__ t_col, const float* __restrict__ x,
+                     const float* __restrict__ Y, const float* __restrict__ w,
+                     const float* __restrict__ g, float* __restrict__ grad_x,
+                     float* __restrict__ grad_w, float* __restrict__ grad_Y) {
+  using M = LaneMap<U>;
+  using T = SendStage<S, U>;
+  using C = Cfg<S, U>;
+  using SM = FusedSmem<S, U, WPB, NBUF>;
+  constexpr int XD = U * S::XC, SLOTS = WPB * M::EPW, EPW = M::EPW;
+  constexpr int NST = ((MODE & 1) ? C::ST_W : 0) + ((MODE & 2) ? C::ST_Y : 0);
+  static_assert(NBUF >= 1 && NBUF <= 4, "one to four staging buffers");
+  static_assert((NBUF - 1) * (T::NLOADS + NST) < 64, "pipeline too deep for vmcnt");
+  __shared__ __attribute__((aligned(16))) char smem[SM::BYTES];
+  const int j = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slot = lane / M::LPE, uu = lane % M::LPE;
+  const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
+  const int last = end - 1;
+  float gx[M::CPL][S::XC];
+#pragma unroll
+  for (int cc = 0; cc < M::CPL; ++cc)
+#pragma unroll
+    for (int a = 0; a < S::XC; ++a) gx[cc][a] = 0.f;
+  const int trips = wave_trips<U, WPB>(beg, end, wv);
+  char* mybuf = smem + wv * NBUF * T::BUF;
+  char* myx = smem + SM::XR_OFF + wv * ceil16(SM::XB);
+  const int k00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
+  if (trips > 0) {
+    // the sender's x row goes to LDS ahead of the first step's operands, so
+    // the first step's wait covers it (loads complete in issue order)
+    dma_rows16<1, SM::XB>(myx, [&](int) { return (const char*)(x + (size_t)j * XD); }, lane);
+    // qh[t]: receiver-sorted positions of the steps staged but not yet
+    // computed (qh[0] is the next one computed); qn/in: the step staged next
+    IdxWindow<EPW, SLOTS> wq, wi;
+    wq.load(t_perm, k00, 0, last, lane);
+    wi.load(t_col, k00, 0, last, lane);
+    int qh[NBUF > 1 ? NBUF - 1 : 1][EPW], qn[EPW], in[EPW];
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b) {
+#pragma unroll
+      for (int r = 0; r < EPW; ++r) {
+        qn[r] = wq.get(t_perm, k00, b, r, last, lane);
+        in[r] = wi.get(t_col, k00, b, r, last, lane);
+        qh[b][r] = qn[r];
+      }
+      if (b < trips) stage_send<S, U>(mybuf + b * T::BUF, Y, w, g, qn, in, lane);
+    }
+#pragma unroll
+    for (int r = 0; r < EPW; ++r) {
+      qn[r] = wq.get(t_perm, k00, NBUF - 1, r, last, lane);
+      in[r] = wi.get(t_col, k00, NBUF - 1, r, last, lane);
+    }
+    float xr[M::CPL][S::XC];
+    float pgw[M::CPL][S::NP], pgy[C::ST_Y];
+    const HalvingShare ysh = halving_share(S::YC, M::LPE, lane);
+    size_t pq = 0;
+    auto flush = [&]() {
+      if constexpr (MODE & 1) {
+#pragma unroll
+        for (int cc = 0; cc < M::CPL; ++cc)
+#pragma unroll
+          for (int p = 0; p < S::NP; ++p)
+            __builtin_nontemporal_store(pgw[cc][p], grad_w + (pq * S::NP + p) * U + uu + 64 * cc);
+      }
+      if constexpr (MODE & 2) {
+#pragma unroll
+        for (int r = 0; r < C::ST_Y; ++r)
+          if (r < ysh.len) __builtin_nontemporal_store(pgy[r], grad_Y + pq * S::YC + ysh.first + r);
+      }
+    };
+    for (int k = 0; k < trips; ++k) {
+      const int k0 = k00 + k * SLOTS;
+      const char* cur = mybuf + (k % NBUF) * T::BUF;
+      // receiver-sorted position of this lane's edge
+      const int q = NBUF == 1 ? pick(qn, slot) : pick(qh[0], slot);
+      int ahead = trips - 1 - k;
+      if (ahead >= NBUF - 1) {
+        ahead = NBUF - 1;
+        stage_send<S, U>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, Y, w, g, qn, in, lane);
+      }
+      // store groups issued after this step's loads: steps max(1, k-NBUF+1) .. k-1
+      const int sg = k - 1 < NBUF - 1 ? (k - 1 > 0 ? k - 1 : 0) : NBUF - 1;
+      wait_steps<NBUF, NBUF, T::NLOADS, NST>(ahead, sg);
+      if (k > 0) flush();
+      if (k == 0) {
+#pragma unroll
+        for (int cc = 0; cc < M::CPL; ++cc)
+          static_for<S::NIN>([&](auto I) {
+            constexpr int d = 2 * S::ls.v[I] + 1;
+            constexpr int xo = S::xoff(I);
+            const float* px = (const float*)myx + U * xo + (uu + 64 * cc) * d;
+            static_for<d>([&](auto A) { xr[cc][xo + A] = px[A]; });
+          });
+      }
+      const float* W = (const float*)(cur + T::W_OFF) + slot * (S::NP * U);
+      const float* Yv = (const float*)(cur + T::Y_OFF) + slot * S::YC;
+      const float* G = (const float*)(cur + T::G_OFF) + slot * (S::OC * U);
+      float yr[S::YC], wr[M::CPL][S::NP], gr[M::CPL][S::OC];
+#pragma unroll
+      for (int b = 0; b < S::YC; ++b) yr[b] = Yv[b];
+#pragma unroll
+      for (int cc = 0; cc < M::CPL; ++cc) {
+#pragma unroll
+        for (int p = 0; p < S::NP; ++p) wr[cc][p] = W[p * U + uu + 64 * cc];
+        static_for<S::NO>([&](auto K) {
+          constexpr OutInfo oi = S::outs.o[K];
+          constexpr int d = 2 * oi.l + 1;
+          const float* pg = G + U * oi.ko + (uu + 64 * cc) * d;
+          static_for<d>([&](auto Cc) { gr[cc][oi.ko + Cc] = pg[Cc]; });
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // positions of the steps still in flight, and indices of the step
+      // after the staged one, loaded while this step computes
+      if constexpr (NBUF > 1) {
+#pragma unroll
+        for (int t = 0; t + 1 < NBUF - 1; ++t)
+#pragma unroll
+          for (int r = 0; r < EPW; ++r) qh[t][r] = qh[t + 1][r];
+#pragma unroll
+        for (int r = 0; r < EPW; ++r) qh[NBUF - 2][r] = qn[r];
+      }
+#pragma unroll
+      for (int r = 0; r < EPW; ++r) {
+        qn[r] = wq.get(t_perm, k00, k + NBUF, r, last, lane);
+        in[r] = wi.get(t_col, k00, k + NBUF, r, last, lane);
+      }
+      float gy[S::YC];
+#pragma unroll
+      for (int b = 0; b < S::YC; ++b) gy[b] = 0.f;
+      // only the sender's last step can hold slots past its edges; their
+      // grad_x share is dropped (their grad_w / grad_Y are the real slot's)
+      const bool live = k0 + slot < end;
+      if constexpr (!kPhased<S>) {
+        float ym[S::YC];
+#pragma unroll
+        for (int b = 0; b < S::YC; ++b) ym[b] = live ? yr[b] : 0.f;
+#pragma unroll
+        for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_all<S>(xr[cc], yr, ym, wr[cc], gr[cc], pgw[cc], gy, gx[cc]);
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_recv<S>(xr[cc], yr, wr[cc], gr[cc], pgw[cc], gy);
+        if (k0 + EPW > end) {
+#pragma unroll
+          for (int cc = 0; cc < M::CPL; ++cc)
+#pragma unroll
+            for (int c = 0; c < S::OC; ++c) gr[cc][c] = live ? gr[cc][c] : 0.f;
+        }
+#pragma unroll
+        for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_send<S>(yr, wr[cc], gr[cc], gx[cc]);
+      }
+      if constexpr (MODE & 2) {
+        lane_sum_halving<S::YC, M::LPE / 2>(gy, lane);
+#pragma unroll
+        for (int r = 0; r < C::ST_Y; ++r) pgy[r] = gy[r];
+      }
+      pq = (size_t)q;
+    }
+    flush();
   }
   __syncthreads();
   block_reduce_store<U, WPB, S::XC, S::NIN>(gx, (float*)smem, grad_x + (size_t)j * XD, InBlocks<S>{});
@@ -884,16 +1249,46 @@ hipError_t launch_bwd_send(const ConvArgs& a) {
   return hipGetLastError();
 }
 
+// whole backward (grad_x with grad_w and/or grad_Y) in one sender-grouped pass
+
+template <class S, int U>
+hipError_t launch_bwd_fused(const ConvArgs& a) {
+  using F = FusedCfg<S, U>;
+  if (a.n_nodes == 0) return hipSuccess;
+  const dim3 grid(a.n_nodes), block(F::WPB * 64);
+  if (a.grad_w && a.grad_Y)
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 3>), grid, block, 0, a.stream, a.t_row_ptr,
+                       a.t_perm, a.t_col, a.x, a.Y, a.w, a.grad_out, a.grad_x, a.grad_w, a.grad_Y);
+  else if (a.grad_w)
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 1>), grid, block, 0, a.stream, a.t_row_ptr,
+                       a.t_perm, a.t_col, a.x, a.Y, a.w, a.grad_out, a.grad_x, a.grad_w, a.grad_Y);
+  else
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 2>), grid, block, 0, a.stream, a.t_row_ptr,
+                       a.t_perm, a.t_col, a.x, a.Y, a.w, a.grad_out, a.grad_x, a.grad_w, a.grad_Y);
+  return hipGetLastError();
+}
+
 }  // namespace tpc
 
 #include "dbl_kernels.hpp"
 
 namespace tpc {
 
+// The one-pass backward where its per-edge arithmetic fits in registers
+// (lmax 2); the large signatures are bound by their CG arithmetic and keep the
+// two passes (Zipf backward 5.0 against 6.0 ms in one pass).
+template <class S, int U>
+constexpr LaunchFn fused_backward() {
+  if constexpr (kPhased<S>)
+    return nullptr;
+  else
+    return &launch_bwd_fused<S, U>;
+}
+
 template <class S, int U>
 const KernelSet* kernel_set() {
-  static const KernelSet k{&launch_fwd<S, U>, &launch_bwd_recv<S, U>, &launch_bwd_send<S, U>,
-                           &launch_dbl_recv<S, U>, &launch_dbl_send<S, U>};
+  static const KernelSet k{&launch_fwd<S, U>,      &launch_bwd_recv<S, U>, &launch_bwd_send<S, U>,
+                           &launch_dbl_recv<S, U>, &launch_dbl_send<S, U>, fused_backward<S, U>()};
   return &k;
 }
 

@@ -169,17 +169,19 @@ __global__ void __launch_bounds__(256)
 }
 
 __global__ void __launch_bounds__(256)
-    k_gather_i32(const int32_t* __restrict__ in, const int32_t* __restrict__ idx, int n,
+    k_gather_i32(const int32_t* __restrict__ in, const int32_t* __restrict__ idx, int n, int n_nodes,
                  int32_t* __restrict__ out) {
+  // node indices are clamped to [0, n_nodes): an unchecked build with bad
+  // indices then yields a wrong grouping but never a later out-of-bounds read
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
-  if (q < n) out[q] = in[idx[q]];
+  if (q < n) out[q] = min(max(in[idx[q]], 0), n_nodes - 1);
 }
 
 __global__ void __launch_bounds__(256)
     k_gather2_i32(const int32_t* __restrict__ in, const int32_t* __restrict__ idx1,
-                  const int32_t* __restrict__ idx2, int n, int32_t* __restrict__ out) {
+                  const int32_t* __restrict__ idx2, int n, int n_nodes, int32_t* __restrict__ out) {
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
-  if (q < n) out[q] = in[idx1[idx2[q]]];
+  if (q < n) out[q] = min(max(in[idx1[idx2[q]]], 0), n_nodes - 1);
 }
 
 __global__ void __launch_bounds__(256)
@@ -285,7 +287,7 @@ tp_status graph_build(const int32_t* src, const int32_t* dst, int n_edges, int n
   }
   hipLaunchKernelGGL(k_row_ptr, dim3(rb), dim3(256), 0, st, ws.sorted, n_edges, n_nodes, row_ptr);
   if (n_edges > 0) {
-    hipLaunchKernelGGL(k_gather_i32, dim3(eb), dim3(256), 0, st, src, perm, n_edges, col);
+    hipLaunchKernelGGL(k_gather_i32, dim3(eb), dim3(256), 0, st, src, perm, n_edges, n_nodes, col);
     // sender grouping of receiver-sorted positions: sort col (values = positions)
     if ((e = radix_sort(reinterpret_cast<const uint32_t*>(col), n_edges, n_nodes - 1, ws.sorted,
                         t_perm, ws, st)) != hipSuccess)
@@ -293,7 +295,7 @@ tp_status graph_build(const int32_t* src, const int32_t* dst, int n_edges, int n
   }
   hipLaunchKernelGGL(k_row_ptr, dim3(rb), dim3(256), 0, st, ws.sorted, n_edges, n_nodes, t_row_ptr);
   if (n_edges > 0)
-    hipLaunchKernelGGL(k_gather2_i32, dim3(eb), dim3(256), 0, st, dst, perm, t_perm, n_edges, t_col);
+    hipLaunchKernelGGL(k_gather2_i32, dim3(eb), dim3(256), 0, st, dst, perm, t_perm, n_edges, n_nodes, t_col);
   if ((e = hipGetLastError()) != hipSuccess) return hip_error(e, "graph build launch");
   return TP_OK;
 }

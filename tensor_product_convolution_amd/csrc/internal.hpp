@@ -35,6 +35,7 @@ struct KernelSet {
   LaunchFn bwd_send = nullptr;  // sender pass: grad_x
   LaunchFn dbl_recv = nullptr;  // second order, receiver pass: d_grad_out, d_Y, d_w
   LaunchFn dbl_send = nullptr;  // second order, sender pass: d_x
+  LaunchFn bwd_fused = nullptr; // sender-grouped pass: grad_x with grad_w and/or grad_Y
 };
 
 // radial-weight variant (edge weights from a radial network of the length)

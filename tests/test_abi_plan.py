@@ -111,6 +111,33 @@ def test_graph_and_conv_argument_errors_without_launch():
     assert "negative" in msg
 
 
+def test_conv_alignment_errors_without_launch():
+    """Rows of x, w and grad_out are staged with 16-byte loads: a pointer that is
+    only 4-byte aligned is rejected on the host (no launch), for the forward,
+    the backward and the channel mix."""
+    L = tpc.lib()
+    p = tpc.Plan("8x0e+8x1o", 2, 2)
+    mix = tpc.Plan("16x0e+16x1o+16x2e", 2, 2, uvw=True)
+    fake, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1004)
+    out = ctypes.c_void_p(0x3000)
+    g = tpc._Graph(4, 10, fake, fake, fake, fake, fake, fake)
+    assert L.tp_conv_forward(p.handle, ctypes.byref(g), odd, fake, fake, out, None) == -1
+    assert "16-byte" in L.tp_conv_last_error().decode()
+    assert L.tp_conv_forward(p.handle, ctypes.byref(g), fake, fake, odd, out, None) == -1
+    # x, Y, w, grad_out | grad_x, grad_Y, grad_w
+    for bad in range(4):
+        args = [fake] * 4
+        if bad != 1:                     # Y rows move as 4-byte granules
+            args[bad] = odd
+            assert L.tp_conv_backward(p.handle, ctypes.byref(g), *args, out, out, out, None) == -1
+            assert "16-byte" in L.tp_conv_last_error().decode()
+    assert L.tp_conv_uvw_forward(mix.handle, 4, fake, fake, odd, None) == -1
+    assert L.tp_conv_uvw_backward(mix.handle, 4, fake, odd, fake, out, None, fake, 1 << 30, None) == -1
+    assert L.tp_conv_uvw_backward(mix.handle, 4, fake, fake, odd, out, None, fake, 1 << 30, None) == -1
+    assert "16-byte" in L.tp_conv_last_error().decode()
+    L.tp_conv_plan_destroy(None)          # NULL is ignored
+
+
 def test_radial_uvw_forces_double_argument_errors_without_launch():
     """Host validation of the radial, mix, forces and second-order entry points:
     every case returns its status before any HIP call."""
