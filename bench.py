@@ -1,35 +1,40 @@
 """Throughput of the fused tensor-product convolution on one MI355X.
 
-A step is one pass of the hot path over one batch: the forward kernel, the
-backward receiver pass (grad_w, grad_Y) and the backward sender pass
-(grad_x), on the 1,536-atom / 46,080-edge workload (32x0e+32x1o+32x2e,
-harmonics to l = 2, every path with l3 <= 2, channel-wise weights) by
-default.  The graph grouping (CSR build) is timed separately: it runs once per
-neighbour list, not per layer.
+A step is one pass of the hot path over one batch: the forward kernel and the
+backward (gradients with respect to x, w and Y) of one layer.  The default
+run measures the 1,536-atom / 46,080-edge workload (32x0e+32x1o+32x2e,
+harmonics to l = 2, every path with l3 <= 2, channel-wise weights) as the
+headline ``value`` and, in ``configs``, the other four workloads: the 32-atom
+tiny graph, the 4,096-atom lmax-3 forward, the 32,768-atom power-law (Zipf)
+graph at lmax 3, and the 100,000-atom / 3,000,000-edge streaming layer with
+on-chip radial weights and the channel mix.  ``--config NAME`` measures one
+workload alone (used for profiler runs).  The graph grouping (CSR build) is
+timed separately: it runs once per neighbour list, not per layer.
 
-Timing: W untimed warm-up steps, then K timed steps, each bracketed by a pair
-of HIP events on the stream the kernels run on (torch's current stream).
-Before each step a 1 GiB buffer is read so that L2 and the 256 MB Infinity
-Cache hold none of the step's inputs: they come from HBM.  Per-kernel launch
-durations (for the roofline) are event-timed over 10 back-to-back launches of
-that kernel after a flush.  ``--warm`` also times steps without the flush.
+Timing, every figure cold (nothing of the step's edge-sized inputs in L2 or
+the 256 MB Infinity Cache):
+  * steps: W untimed warm-up steps, then K timed steps, each preceded by a
+    1 GiB read of an unrelated buffer and bracketed by a pair of HIP events
+    on the stream the kernels run on (torch's current stream);
+  * kernels: back-to-back launches that rotate through enough copies of the
+    edge-sized inputs and outputs that a copy is reused only after at least
+    1 GiB of other edge data has been touched (one copy where a single
+    launch already moves more than that); the per-launch duration is the
+    event-timed batch divided by the launch count.  ``--warm`` also times
+    steps without the flush.
 
-``--config stream`` times the 100,000-atom / 3,000,000-edge streaming layer
-instead: edge weights from the radial network (8 Bessel functions, 64 SiLU
-units, 15 x 128 weights per edge) recomputed on chip in every pass, then the
-128 x 128 channel mix per output irrep; a step is its forward (radial pass +
-mix) and backward (mix adjoint, receiver pass, grad_W2 pass, sender pass).
-Its kernels are bound by the fp32 MFMA work of the radial network, so its
-roofline is reported against the 157.3 TFLOP/s fp32 matrix peak.
-
-Output: one JSON line (rank 0, N = 1).  ``value`` is edges per second of
-forward + backward; ``roofline`` reports the slowest of the three kernels
-against the 8 TB/s HBM peak with its algorithmic bytes; ``cpu_baseline`` is
-the float64 oracle timed on this host's cores on the same workload.
+Output: one JSON line.  ``value`` is edges per second of forward + backward
+on the 1,536-atom workload; ``roofline`` reports its slowest kernel against
+the 8 TB/s HBM peak with that kernel's algorithmic bytes, ``step_roofline``
+the whole step against the bytes it must move (each array once per pass);
+``valu_flop_util`` the fp32 vector flops of the CG arithmetic per second
+against 78.6 TFLOP/s; ``cpu_baseline`` the float64 oracle on this host's
+cores (a process pool over edge chunks) on the same workload.
 """
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -41,14 +46,20 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TP-conv edges/sec (fwd, fwd+bwd) fp32 at 1 GPU; % of MI355X HBM roofline"
 HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+FP32_VALU_PEAK_TFLOPS = 78.6      # non-packed fp32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2 x 2.4 GHz
+COLD_BYTES = 1 << 30              # edge data touched between two uses of one copy
+HOST_POOL_CAP = 16                # host cores of one GPU's share on the box
 WORKLOADS = {
     "mid": ("32x0e+32x1o+32x2e", 2, 2,
             "1536 atoms, 46080 directed edges (30 distinct random senders each), "
             "32x0e+32x1o+32x2e, real SH lmax 2, all paths l3<=2 (15), uvu weights, fwd+bwd"),
-    "tiny": ("8x0e+8x1o", 2, 2, "32 atoms in an 8 A periodic cube, cutoff 4 A, 8x0e+8x1o"),
-    "lmax3": ("64x0e+64x1o+64x2e+64x3o", 3, 3, "4096 atoms, degree U{5..30}, lmax 3, 64 channels"),
+    "tiny": ("8x0e+8x1o", 2, 2, "32 atoms in an 8 A periodic cube, cutoff 4 A, 8x0e+8x1o, fwd+bwd"),
+    "lmax3": ("64x0e+64x1o+64x2e+64x3o", 3, 3,
+              "4096 atoms, degree U{5..30}, 64x(0e+1o+2e+3o), SH lmax 3, 34 paths, fwd"),
     "zipf": ("64x0e+64x1o+64x2e+64x3o", 3, 3,
-             "32768 atoms, Zipf(1.5) degrees capped at 256, lmax 3, 64 channels"),
+             "32768 atoms, Zipf(1.5) receiver degrees capped at 256, 64x(0e+1o+2e+3o), "
+             "SH lmax 3, 34 paths, fwd+bwd"),
 }
 RADIAL_WORKLOADS = {
     "stream": ("128x0e+128x1o+128x2e", 2, 2, (8, 64, 5.0),
@@ -69,8 +80,8 @@ GAUNT_WORKLOADS = {
               "Gaunt product (even couplings, outputs 0e+1o+2e) evaluated on a 32-point spherical "
               "grid, filter weights per edge, degree and channel, fwd+bwd"),
 }
+DEFAULT_CONFIGS = ("tiny", "lmax3", "zipf", "stream")
 GAUNT_SOURCES = ("gaunt.hip",)
-FP32_MFMA_PEAK_TFLOPS = 157.3
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_{}.txt")
 KERNEL_SOURCES = ("conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
 RADIAL_SOURCES = ("radial_kernels.hpp", "radial_l012_s2.hip", "uvw.hip", "conv_kernels.hpp", "sig.hpp",
@@ -86,6 +97,12 @@ def kernel_source_hash(sources=KERNEL_SOURCES):
     return h.hexdigest()[:16]
 
 
+def one_pass_backward(lmax_sh):
+    """tp_conv_backward forms every gradient in one sender-grouped launch for the
+    lmax-2 signatures, and in a receiver pass plus a sender pass otherwise."""
+    return lmax_sh <= 2
+
+
 def algorithmic_bytes(N, E, P, U, ysh, xdim, outdim):
     """Bytes each kernel must move at least once (node arrays once, edge streams once)."""
     node = 4 * N * (xdim + outdim + 1)        # x, out (or grad_out / grad_x), row pointers
@@ -93,6 +110,9 @@ def algorithmic_bytes(N, E, P, U, ysh, xdim, outdim):
         "fwd": E * (4 * P * U + 4 * ysh + 4) + node,          # w, Y, col in; out
         "bwd_recv": E * (8 * P * U + 8 * ysh + 4) + node,     # w, Y, col in; grad_w, grad_Y out
         "bwd_send": E * (4 * P * U + 4 * ysh + 8) + node,     # w, Y, t_perm, t_col in; grad_x out
+        # one-pass backward: w, Y, t_perm, t_col in, grad_w, grad_Y out; x, grad_out,
+        # t_row_ptr in, grad_x out
+        "bwd": E * (8 * P * U + 8 * ysh + 8) + 4 * N * (2 * xdim + outdim + 1),
         # compulsory bytes of the whole step: each array once
         "step": E * (8 * P * U + 8 * ysh + 4) + 4 * N * (2 * xdim + 2 * outdim + 1),
         # second-order backward, each array once: w, gg_w, Y, gg_Y, col, t_perm,
@@ -100,6 +120,44 @@ def algorithmic_bytes(N, E, P, U, ysh, xdim, outdim):
         # d_x and d_grad_out out
         "double_bwd": E * (12 * P * U + 12 * ysh + 12) + 4 * N * (3 * xdim + 2 * outdim + 2),
     }
+
+
+def step_bytes(ab, fwd_only):
+    """Bytes a forward (+ backward) pass must move, each pass touching its arrays
+    once: the forward's and the one-pass backward's algorithmic bytes."""
+    return ab["fwd"] if fwd_only else ab["fwd"] + ab["bwd"]
+
+
+def cg_counts(paths, pabc, val):
+    """Operation counts of the CG arithmetic per edge and channel, from the
+    plan's path list ((l1, l2, l3, k) per path) and nonzeros ((p, a, b, c), C):
+    nnz; the coupled (a, b) pairs of each (l1, l2) group (the shared products
+    x_a Y_b and the grad_x folds); sum over paths of 2l2+1 and of 2l3+1; and
+    the distinct nontrivial magnitudes |C| per output component (the one-pass
+    backward's scaled upstream-gradient values)."""
+    ab, gc = set(), set()
+    for (p, a, b, c), v in zip(pabc, val):
+        l1, l2, l3, k = paths[p]
+        ab.add((l1, l2, int(a), int(b)))
+        m = float(np.float32(abs(v)))
+        if m != 1.0:
+            gc.add((k, int(c), m))
+    return {"nnz": len(val), "ab": len(ab), "d2": sum(2 * q[1] + 1 for q in paths),
+            "d3": sum(2 * q[2] + 1 for q in paths), "gc": len(gc)}
+
+
+def cg_flops(cnt):
+    """fp32 vector flops per edge and channel (multiply 1, fused multiply-add 2)
+    of the CG arithmetic in the forms the kernels evaluate:
+      fwd       products x_a Y_b, one FMA per nonzero, one FMA per (path, c) with w;
+      bwd       (one pass) scaled gradients, two FMAs per nonzero (Z and V forms),
+                grad_w and grad_Y folds over (path, b), grad_x folds over (a, b);
+      bwd_recv  multiply + FMA per nonzero (Z form), grad_w and grad_Y folds;
+      bwd_send  w g products, one FMA per nonzero, grad_x folds."""
+    return {"fwd": cnt["ab"] + 2 * cnt["nnz"] + 2 * cnt["d3"],
+            "bwd": cnt["gc"] + 4 * cnt["nnz"] + 4 * cnt["d2"] + 2 * cnt["ab"],
+            "bwd_recv": 3 * cnt["nnz"] + 4 * cnt["d2"],
+            "bwd_send": cnt["d3"] + 2 * cnt["nnz"] + 2 * cnt["ab"]}
 
 
 def radial_flops(E, P, U, NH):
@@ -129,38 +187,183 @@ def read_traffic(config, sources=KERNEL_SOURCES):
     return out or None
 
 
-def cpu_baseline(op, wl, fwd_only=False, max_edges=60000):
-    """The float64 oracle on this host: harmonics + fwd (+ bwd) over the whole
-    workload, or over the edges into the first receivers when it has more than
-    max_edges edges (a bounded sample of the same graph)."""
-    import oracle
+def read_profile_value(config, key, sources):
+    """one value of the committed counter summary (None if absent or stale)"""
+    path = PROFILE_SUMMARY.format(config)
+    if not os.path.exists(path):
+        return None
+    vals = dict(l.split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
+    vals = {k.strip(): v.strip() for k, v in vals.items()}
+    if vals.get("kernel_source_hash") != kernel_source_hash(sources):
+        return None
+    return float(vals[key]) if key in vals else None
+
+
+def copies_for_cold(bytes_per_copy):
+    """Copies of the edge-sized arrays so that one is reused only after
+    COLD_BYTES of other edge data (at most 16)."""
+    return int(min(16, max(1, math.ceil(COLD_BYTES / max(bytes_per_copy, 1)))))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle over a process pool
+
+
+def host_workers():
+    return max(1, min(HOST_POOL_CAP, len(os.sched_getaffinity(0))))
+
+
+_POOL_STATE = {}
+
+
+def _pool_init(plan_args):
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        _POOL_STATE["limits"] = threadpool_limits(1)
     except Exception:
-        threads = 1
-    src, dst, r, n, x, g = wl.src, wl.dst, wl.r, wl.n_nodes, wl.x, wl.g
-    w = wl.w
-    what = f"whole workload ({wl.n_edges} edges)"
-    if wl.n_edges > max_edges:
-        order = np.argsort(dst, kind="stable")
-        e = np.sort(order[:max_edges])
-        e = e[np.isin(dst[e], np.unique(dst[order[:max_edges]])[:-1])]   # whole receivers only
-        nodes = np.unique(np.concatenate([src[e], dst[e]]))
-        src, dst = np.searchsorted(nodes, src[e]), np.searchsorted(nodes, dst[e])
-        r, w, x, n = r[e], w[e], x[nodes], len(nodes)
-        g = None if g is None else g[nodes]
-        what = (f"edges into the first receivers ({len(e)} of {wl.n_edges} edges, "
-                f"{n} nodes)")
-    t0 = time.perf_counter()
+        pass
+    import oracle
+    _POOL_STATE["op"] = oracle.build_plan(*plan_args)
+
+
+def _oracle_direct_chunk(task):
+    """harmonics + forward (+ backward) of one chunk of edges (whole receivers)"""
+    import oracle
+    op = _POOL_STATE["op"]
+    src, dst, n, x, r, w, g = task
     Y = oracle.sh_real(op.lmax_sh, r)
-    oracle.tp_conv_fwd(op, src, dst, n, x, Y, w)
-    if not fwd_only:
-        oracle.tp_conv_bwd(op, src, dst, n, x, Y, w, g)
-    dt = time.perf_counter() - t0
-    return {"value": len(src) / dt, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{what}, harmonics + fwd{'' if fwd_only else ' + bwd'} once, float64, "
-                      f"{dt:.2f} s; host affinity {len(os.sched_getaffinity(0))} cores"}
+    res = [oracle.tp_conv_fwd(op, src, dst, n, x, Y, w)]
+    if g is not None:
+        res.extend(oracle.tp_conv_bwd(op, src, dst, n, x, Y, w, g))
+    return res
+
+
+def _oracle_radial_chunk(task):
+    import oracle
+    op = _POOL_STATE["op"]
+    src, dst, n, x, r, rl, W1, W2, Wm, g, nb, rc = task
+    Y = oracle.sh_real(op.lmax_sh, r)
+    out = oracle.tp_conv_radial_fwd(op, src, dst, n, x, Y, rl, W1, W2, Wm, nb, rc)
+    return [out, oracle.tp_conv_radial_bwd(op, src, dst, n, x, Y, rl, W1, W2, Wm, g, nb, rc)]
+
+
+def _receiver_sample(src, dst, max_edges):
+    """Edges into the first receivers (whole receivers, at most max_edges)."""
+    order = np.argsort(dst, kind="stable")
+    if len(order) <= max_edges:
+        return np.arange(len(src)), f"the whole workload ({len(src)} edges)"
+    keep = order[:max_edges]
+    last = dst[keep[-1]]
+    keep = keep[dst[keep] != last]
+    return np.sort(keep), f"edges into the first receivers ({len(keep)} of {len(src)} edges)"
+
+
+def _chunks_by_receiver(dst, n_chunks):
+    """Split edge indices into chunks of whole receivers, balanced by edge count."""
+    order = np.argsort(dst, kind="stable")
+    bounds = np.linspace(0, len(order), n_chunks + 1).astype(np.int64)
+    cuts = [0]
+    for b in bounds[1:-1]:
+        while b < len(order) and b > 0 and dst[order[b]] == dst[order[b - 1]]:
+            b += 1
+        cuts.append(max(b, cuts[-1]))
+    cuts.append(len(order))
+    return [order[cuts[t]:cuts[t + 1]] for t in range(n_chunks) if cuts[t + 1] > cuts[t]]
+
+
+def _local(src, dst, chunk, *node_arrays):
+    """The chunk's edges renumbered over the nodes they touch, with those nodes' rows."""
+    nodes = np.unique(np.concatenate([src[chunk], dst[chunk]]))
+    ls, ld = np.searchsorted(nodes, src[chunk]), np.searchsorted(nodes, dst[chunk])
+    return nodes, ls, ld, [None if a is None else a[nodes] for a in node_arrays]
+
+
+def pooled_oracle_direct(plan_args, src, dst, n, x, r, w, g, workers):
+    """The oracle's harmonics + forward (+ backward when g is given) for the edges
+    (src, dst), split by receiver over a process pool (each task carries only
+    the rows of the nodes its edges touch); returns (out, grad_x, grad_Y,
+    grad_w) in the given edge order (grads None without g) and the wall time of
+    the pooled evaluation (preparing and distributing the tasks and collecting
+    the results included; the pool's start-up and plan building excluded)."""
+    import multiprocessing as mp
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_pool_init, initargs=(plan_args,)) as pool:
+        pool.map(_oracle_direct_chunk, [(src[:0], dst[:0], 1, x[:1], r[:0], w[:0],
+                                         None if g is None else g[:1])] * workers)   # warm
+        t0 = time.perf_counter()
+        chunks = _chunks_by_receiver(dst, workers)
+        tasks, maps = [], []
+        for c in chunks:
+            nodes, ls, ld, (xc, gc) = _local(src, dst, c, x, g)
+            tasks.append((ls, ld, len(nodes), xc, r[c], w[c], gc))
+            maps.append(nodes)
+        parts = pool.map(_oracle_direct_chunk, tasks)
+        out = np.zeros((n,) + parts[0][0].shape[1:])
+        for nodes, p in zip(maps, parts):
+            out[nodes] += p[0]
+        grads = (None, None, None)
+        if g is not None:
+            gx = np.zeros((n,) + parts[0][1].shape[1:])
+            gY = np.zeros((len(src),) + parts[0][2].shape[1:])
+            gw = np.zeros((len(src),) + parts[0][3].shape[1:])
+            for c, nodes, p in zip(chunks, maps, parts):
+                gx[nodes] += p[1]
+                gY[c], gw[c] = p[2], p[3]
+            grads = (gx, gY, gw)
+        dt = time.perf_counter() - t0
+    return (out,) + grads, dt
+
+
+def cpu_baseline_direct(irreps, lsh, lout, wl, fwd_only, max_edges):
+    """The float64 oracle (harmonics + forward, + backward unless fwd_only) on a
+    bounded sample of the workload, its edges split by receiver over a process
+    pool of host_workers() workers (one BLAS thread each); per-node partial
+    results are summed in the parent."""
+    e, what = _receiver_sample(wl.src, wl.dst, max_edges)
+    nodes = np.unique(np.concatenate([wl.src[e], wl.dst[e]]))
+    src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
+    g = None if fwd_only else wl.g[nodes]
+    n, W = len(nodes), host_workers()
+    _, dt = pooled_oracle_direct((irreps, lsh, lout), src, dst, n, wl.x[nodes], wl.r[e], wl.w[e], g, W)
+    return {"value": len(e) / dt, "unit": "edges/s", "cores": W, "kind": "oracle",
+            "sample": f"{what}, {n} nodes: harmonics + fwd{'' if fwd_only else ' + bwd'} once, "
+                      f"float64, split by receiver over {W} worker processes (1 thread each), "
+                      f"{dt:.2f} s wall"}
+
+
+def cpu_baseline_radial(irreps, lsh, lout, wl, radial, max_edges=30000):
+    """The float64 oracle of the radial layer (fwd + bwd with the mix) on the
+    edges into the first receivers, split by receiver over the process pool
+    (per-node and parameter gradients summed in the parent)."""
+    import multiprocessing as mp
+    nb, _, rc = radial
+    e, what = _receiver_sample(wl.src, wl.dst, max_edges)
+    nodes = np.unique(np.concatenate([wl.src[e], wl.dst[e]]))
+    src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
+    x, g, rl, r = wl.x[nodes], wl.g[nodes], wl.r_len[e], wl.r[e]
+    n, W = len(nodes), host_workers()
+    ctx = mp.get_context("fork")
+    with ctx.Pool(W, initializer=_pool_init, initargs=((irreps, lsh, lout),)) as pool:
+        pool.map(_oracle_radial_chunk, [(src[:0], dst[:0], 1, x[:1], r[:0], rl[:0], wl.W1, wl.W2, wl.Wmix,
+                                         g[:1], nb, rc)] * W)
+        t0 = time.perf_counter()
+        tasks, maps = [], []
+        for c in _chunks_by_receiver(dst, W):
+            nc, ls, ld, (xc, gc) = _local(src, dst, c, x, g)
+            tasks.append((ls, ld, len(nc), xc, r[c], rl[c], wl.W1, wl.W2, wl.Wmix, gc, nb, rc))
+            maps.append(nc)
+        parts = pool.map(_oracle_radial_chunk, tasks)
+        out = np.zeros((n,) + parts[0][0].shape[1:])
+        for nc, p in zip(maps, parts):
+            out[nc] += p[0]
+        dt = time.perf_counter() - t0
+    return {"value": len(e) / dt, "unit": "edges/s", "cores": W, "kind": "oracle",
+            "sample": f"{what}, {n} nodes: harmonics + radial fwd + bwd with the mix once, float64, "
+                      f"split by receiver over {W} worker processes (1 thread each), {dt:.2f} s wall"}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
 
 
 def make_timers(torch, flush):
@@ -183,16 +386,19 @@ def make_timers(torch, flush):
         torch.cuda.synchronize()
         return np.array([e0.elapsed_time(e1) for e0, e1 in ev])   # ms
 
-    def timed_kernel(fn, reps, rounds):
-        # launch duration amortised over back-to-back launches (an event pair
-        # around a single short launch mostly measures the event overhead)
+    def timed_kernel(fn, copies, reps, rounds):
+        # fn(c) launches on copy c of the edge-sized arrays; back-to-back
+        # launches rotate over the copies, so each reads data last touched
+        # `copies` launches earlier (cold when copies x bytes >= 1 GiB); the
+        # duration is amortised over the batch (an event pair around a single
+        # short launch mostly measures the event overhead)
         res = []
         for _ in range(rounds):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             do_flush()
             e0.record()
-            for _ in range(reps):
-                fn()
+            for i in range(reps):
+                fn(i % copies)
             e1.record()
             torch.cuda.synchronize()
             res.append(e0.elapsed_time(e1) / reps)
@@ -220,18 +426,6 @@ def copy_bandwidth(torch, dev, flush, nbytes=1 << 29):
     return 2 * nbytes / (best * 1e-3) / 1e9
 
 
-def read_profile_value(config, key, sources):
-    """one value of the committed counter summary (None if absent or stale)"""
-    path = PROFILE_SUMMARY.format(config)
-    if not os.path.exists(path):
-        return None
-    vals = dict(l.split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
-    vals = {k.strip(): v.strip() for k, v in vals.items()}
-    if vals.get("kernel_source_hash") != kernel_source_hash(sources):
-        return None
-    return float(vals[key]) if key in vals else None
-
-
 def counters_run(torch, dev, flush, step, config):
     """a few steps plus a plain 512 MiB copy (the calibration of the counters)"""
     flush.fill_(1.0)
@@ -247,45 +441,22 @@ def counters_run(torch, dev, flush, step, config):
     print(json.dumps({"counters_run": config, "copy_bytes": a.numel() * 4}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mid",
-                    choices=sorted(WORKLOADS) + sorted(RADIAL_WORKLOADS) + sorted(FC_WORKLOADS)
-                    + sorted(GAUNT_WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--warm", action="store_true",
-                    help="also time the steps back to back without the cache flush")
-    ap.add_argument("--counters", action="store_true",
-                    help="short run for rocprofv3 counter passes: a few steps plus a 512 MiB copy")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(the receiver-range sharding is a design, not code). Run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
+def hbm_roofline(kernel, nbytes, ms, traffic=None, note=None):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes, "ms": ms, "traffic": traffic}
+    if note:
+        r["note"] = note
+    return r
 
-    import torch
-    import tensor_product_convolution_amd as tpc
-    from workloads import make_workload
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    if args.config in RADIAL_WORKLOADS:
-        return bench_radial(args, torch, tpc, make_workload, dev)
-    if args.config in FC_WORKLOADS:
-        return bench_fc(args, torch, tpc, make_workload, dev)
-    if args.config in GAUNT_WORKLOADS:
-        return bench_gaunt(args, torch, tpc, make_workload, dev)
-    irreps, lsh, lout, desc = WORKLOADS[args.config]
-    from workloads import CONFIGS
-    fwd_only = "fwd+bwd" not in CONFIGS[args.config]["modes"]   # the lmax-3 layer is forward only
+def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
+    """One direct-weight workload: returns (result dict, step function)."""
+    from workloads import CONFIGS, make_workload
+    irreps, lsh, lout, desc = WORKLOADS[name]
+    fwd_only = "fwd+bwd" not in CONFIGS[name]["modes"]   # the lmax-3 layer is forward only
     plan = tpc.Plan(irreps, lsh, lout)
-    wl = make_workload(args.config, plan.dims(), seed=0)
+    wl = make_workload(name, plan.dims(), seed=0)
     N, E = wl.n_nodes, wl.n_edges
     P, U, ysh = plan.n_paths, plan.mul, plan.ysh
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -298,32 +469,41 @@ def main():
     go = None if fwd_only else T(wl.g)
     out = torch.empty(N, plan.outdim, device=dev)
     gx = torch.empty_like(x)
-    gY = torch.empty_like(Y)
-    gw = torch.empty_like(w)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    NC = copies_for_cold(4 * E * (P * U + ysh))
+    Ys, ws = [Y] + [Y.clone() for _ in range(NC - 1)], [w] + [w.clone() for _ in range(NC - 1)]
+    gYs = [torch.empty_like(Y) for _ in range(NC)] if not fwd_only else None
+    gws = [torch.empty_like(w) for _ in range(NC)] if not fwd_only else None
 
     def step():
         tpc.forward(plan, g, x, Y, w, out=out)
         if not fwd_only:
-            tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))   # receiver, then sender pass
+            tpc.backward(plan, g, x, Y, w, go, outs=(gx, gYs[0], gws[0]))
 
     if args.counters:
-        counters_run(torch, dev, flush, step, args.config)
-        return
+        counters_run(torch, dev, flush, step, name)
+        return None, step
     do_flush, timed_steps_of, timed_kernel = make_timers(torch, flush)
     timed_steps = lambda k, cold: timed_steps_of(step, k, cold)
 
-    kernels = {"fwd": lambda: tpc.forward(plan, g, x, Y, w, out=out)}
+    kernels = {"fwd": lambda c: tpc.forward(plan, g, x, Ys[c], ws[c], out=out)}
+    one_pass = one_pass_backward(lsh)
     extras = {}
     if not fwd_only:
-        kernels["bwd_recv"] = lambda: tpc.backward(plan, g, x, Y, w, go, outs=(None, gY, gw))
-        kernels["bwd_send"] = lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, None, None))
-        extras["bwd"] = lambda: tpc.backward(plan, g, x, Y, w, go, outs=(gx, gY, gw))
+        bwd_call = lambda c: tpc.backward(plan, g, x, Ys[c], ws[c], go, outs=(gx, gYs[c], gws[c]))
+        if one_pass:
+            kernels["bwd"] = bwd_call
+        else:
+            kernels["bwd_recv"] = lambda c: tpc.backward(plan, g, x, Ys[c], ws[c], go,
+                                                         outs=(None, gYs[c], gws[c]))
+            kernels["bwd_send"] = lambda c: tpc.backward(plan, g, x, Ys[c], ws[c], go,
+                                                         outs=(gx, None, None))
+            extras["bwd"] = bwd_call
         r_sorted = tpc.gather_rows(T(wl.r), g.perm)
         grad_r = torch.empty_like(r_sorted)
-        extras["forces"] = lambda: tpc.sph_harm_backward(lsh, r_sorted, gY, out=grad_r)
+        extras["forces"] = lambda c: tpc.sph_harm_backward(lsh, r_sorted, gYs[c], out=grad_r)
         # second-order backward with all three cotangents (here: the first backward's outputs)
-        extras["double_bwd"] = lambda: tpc.double_backward(plan, g, x, Y, w, go, gx, gY, gw)
+        extras["double_bwd"] = lambda c: tpc.double_backward(plan, g, x, Ys[c], ws[c], go, gx, gYs[c],
+                                                             gws[c])
 
     flush.fill_(1.0)
     # graph grouping, timed separately
@@ -344,110 +524,70 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
     warm = timed_steps(args.steps, False) if args.warm else None
-    reps, rounds = 10, max(2, args.steps // 5)
-    kt_all = {n: timed_kernel(fn, reps, rounds) for n, fn in kernels.items()}
-    extra_ms = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in extras.items()}
+    reps = max(2 * NC, 12)
+    rounds = max(2, args.steps // 5)
+    kt = {n: float(timed_kernel(fn, NC, reps, rounds).mean()) for n, fn in kernels.items()}
+    extra_ms = {n: float(timed_kernel(fn, NC, reps, rounds).mean()) for n, fn in extras.items()}
 
-    names = list(kernels)
-    kt = np.array([kt_all[n].mean() for n in names])     # ms per launch
-    copy_gbs = copy_bandwidth(torch, dev, flush)
-    wk = read_profile_value(args.config, "write_kib.fwd", KERNEL_SOURCES)
-    fwd_write_ratio = None if wk is None else wk * 1024 / (4.0 * N * plan.outdim)
     step_ms = float(t.mean())
-    fwd_ms = float(kt[0])
     ab = algorithmic_bytes(N, E, P, U, ysh, plan.xdim, plan.outdim)
-    dom = names[int(np.argmax(kt))]
-    dom_ms = float(kt[names.index(dom)])
-    achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.config)
+    dom = max(kt, key=kt.get)
+    traffic = read_traffic(name)
+    cnt = cg_counts(plan.paths(), *plan.cg())
+    fl = cg_flops(cnt)
+    sb = step_bytes(ab, fwd_only)
     res = {
-        "metric": METRIC,
-        "value": E / (step_ms * 1e-3),
-        "unit": "edges/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "workload": f"{name}: {desc}", "n_nodes": N, "n_edges": E, "irreps": irreps,
+        "lmax_sh": lsh, "lmax_out": lout, "paths": P, "mode": "fwd" if fwd_only else "fwd+bwd",
         "ms_per_step": step_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded; stands in for the pages' molecular graph)",
-        "config": {"workload": f"{args.config}: {desc}", "n_nodes": N, "n_edges": E,
-                   "irreps": irreps, "lmax_sh": lsh, "lmax_out": lout, "paths": P,
-                   "mode": "fwd" if fwd_only else "fwd+bwd",
-                   "cache": "L2+MALL flushed before each step"},
-        "fwd_edges_per_s": E / (fwd_ms * 1e-3),
-        "fwd_edges_per_s_note": "forward kernel alone (launch duration); value is the whole step",
+        "edges_per_s": E / (step_ms * 1e-3),
         "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
-        "kernel_ms": {n: float(v) for n, v in zip(names, kt)},
-        "kernel_ms_note": f"per launch, {reps} back-to-back launches after a cache flush, mean of {rounds}",
-        "kernel_hbm_frac": {n: ab[n] / (float(v) * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in zip(names, kt)},
-        "bwd_ms": extra_ms.get("bwd"),
-        "bwd_note": "one backward call (receiver then sender pass), per call",
-        "double_bwd_ms": extra_ms.get("double_bwd"),
-        "double_bwd_hbm_frac": (None if "double_bwd" not in extra_ms else
-                                ab["double_bwd"] / (extra_ms["double_bwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS),
-        "double_bwd_note": "second-order backward (dx, dY, dw, d grad_out for cotangents of all "
-                           "three first-order outputs), per call; not part of the step",
-        "forces_ms": extra_ms.get("forces"),
-        "forces_note": "edge-vector gradient from grad_Y (tp_conv_sph_harm_backward), per launch; "
-                       "not part of the step",
-        "step_hbm_frac": ab["fwd" if fwd_only else "step"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "copy_GBs": copy_gbs,
-        "copy_note": "plain device copy of 512 MiB (read + write) after a flush: the practical "
-                     "ceiling of a kernel that writes as much as it reads",
-        "fwd_write_ratio": fwd_write_ratio,
-        "fwd_write_note": "forward HBM writes (rocprofv3 WRITE_SIZE, committed summary) over "
-                          "N*outdim*4: 1.0 means nothing but the output is written",
-        "warm_edges_per_s": None if warm is None else E / (float(warm.mean()) * 1e-3),
+        "fwd_edges_per_s": E / (kt["fwd"] * 1e-3),
+        "kernel_ms": kt,
+        "kernel_ms_note": (f"cold: {reps} back-to-back launches rotating over {NC} copies of the "
+                           f"edge-sized arrays ({NC * 4 * E * (P * U + ysh) / 1e6:.0f} MB of inputs), "
+                           f"after a flush; mean of {rounds}"),
+        "kernel_hbm_frac": {n: ab[n] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in kt.items()},
+        "roofline": hbm_roofline(dom, ab[dom], kt[dom], (traffic or {}).get(dom)),
+        "step_roofline": {"bound": "hbm", "bytes": sb, "ms": step_ms,
+                          "achieved": sb / (step_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": sb / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "note": "forward + backward bytes, each array once per pass (the "
+                                  "backward's re-read of w in the two-pass form is not counted)"},
+        "valu_flop_util": {n: fl[n] * E * U / (v * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS
+                           for n, v in kt.items()},
+        "valu_flops_per_edge_channel": {n: fl[n] for n in kt},
         "graph_build_ms": float(np.median(gb)),
         "wall_s_timed_region": wall,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "algorithmic_bytes": ab[dom],
-                     "traffic": (traffic or {}).get(dom)},
     }
-    if not args.no_cpu_baseline:
-        import oracle
-        op = oracle.build_plan(irreps, lsh, lout)
-        # about 10-30 s of oracle work: the lmax-3 product costs ~10x the lmax-2 one per edge
-        res["cpu_baseline"] = cpu_baseline(op, wl, fwd_only, max_edges=60000 if lsh <= 2 else 12000)
+    if not fwd_only:
+        res["bwd_ms"] = extra_ms.get("bwd", kt.get("bwd"))
+        res["double_bwd_ms"] = extra_ms.get("double_bwd")
+        res["double_bwd_hbm_frac"] = ab["double_bwd"] / (extra_ms["double_bwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+        res["double_bwd_note"] = ("second-order backward (dx, dY, dw, d grad_out for cotangents of all "
+                                  "three first-order outputs), per call; not part of the step")
+        res["forces_ms"] = extra_ms.get("forces")
+        res["forces_note"] = ("edge-vector gradient from grad_Y (tp_conv_sph_harm_backward), per "
+                              "launch; not part of the step")
+    if warm is not None:
+        res["warm_edges_per_s"] = E / (float(warm.mean()) * 1e-3)
+    if cpu:
+        # about 2-10 s of wall time on 16 host cores; the lmax-3 product costs
+        # about 10x the lmax-2 one per edge
+        res["cpu_baseline"] = cpu_baseline_direct(irreps, lsh, lout, wl, fwd_only,
+                                                  max_edges=60000 if lsh <= 2 else 40000)
     else:
         res["cpu_baseline"] = None
-    print(json.dumps(res))
+    del Ys, ws, gYs, gws
+    return res, step
 
 
-def cpu_baseline_radial(op, wl, radial, n_recv=200):
-    """The float64 oracle on this host, fwd + bwd (with the mix) over the edges
-    into the first n_recv receivers (a bounded sample of the layer)."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    nb, _, rc = radial
-    recv = np.arange(n_recv)
-    e = np.nonzero(np.isin(wl.dst, recv))[0]
-    nodes = np.unique(np.concatenate([wl.src[e], recv]))
-    src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
-    x, g, rl = wl.x[nodes], wl.g[nodes], wl.r_len[e]
-    t0 = time.perf_counter()
-    Y = oracle.sh_real(op.lmax_sh, wl.r[e])
-    oracle.tp_conv_radial_fwd(op, src, dst, len(nodes), x, Y, rl, wl.W1, wl.W2, wl.Wmix, nb, rc)
-    oracle.tp_conv_radial_bwd(op, src, dst, len(nodes), x, Y, rl, wl.W1, wl.W2, wl.Wmix, g, nb, rc)
-    dt = time.perf_counter() - t0
-    return {"value": len(e) / dt, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"edges into receivers 0..{n_recv - 1} ({len(e)} of {wl.n_edges} edges, "
-                      f"{len(nodes)} nodes): harmonics + radial fwd + bwd with the mix once, "
-                      f"float64, {dt:.2f} s; host affinity {len(os.sched_getaffinity(0))} cores"}
-
-
-def bench_radial(args, torch, tpc, make_workload, dev):
-    irreps, lsh, lout, radial, desc = RADIAL_WORKLOADS[args.config]
+def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
+    """The streaming layer: returns (result dict, step function)."""
+    from workloads import make_workload
+    irreps, lsh, lout, radial, desc = RADIAL_WORKLOADS[name]
     plan = tpc.Plan(irreps, lsh, lout, radial=radial, uvw=True)
-    wl = make_workload(args.config, plan.dims(), seed=0)
+    wl = make_workload(name, plan.dims(), seed=0)
     N, E = wl.n_nodes, wl.n_edges
     P, U = plan.n_paths, plan.mul
     NH = radial[1]
@@ -462,25 +602,26 @@ def bench_radial(args, torch, tpc, make_workload, dev):
     outs = {"x": torch.empty_like(x), "Y": torch.empty_like(Y), "W1": torch.empty_like(W1),
             "W2": torch.empty_like(W2), "Wmix": torch.empty_like(Wm)}
     ws = torch.empty(tpc.radial_workspace(plan, N, True), dtype=torch.uint8, device=dev)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
 
     def step():
         tpc.forward_radial(plan, g, x, Y, rl, W1, W2, Wm, out=out, out_pre=pre)
         tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, Wmix=Wm, out_pre=pre, outs=outs, ws=ws)
 
     if args.counters:
-        counters_run(torch, dev, flush, step, args.config)
-        return
+        counters_run(torch, dev, flush, step, name)
+        return None, step
     do_flush, timed_steps, timed_kernel = make_timers(torch, flush)
-    bwd = lambda want: (lambda: tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, want=want,
-                                                    outs=outs, ws=ws))
+    bwd = lambda want: (lambda c: tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, want=want,
+                                                      outs=outs, ws=ws))
+    # every launch gathers x or grad_out rows for 3M edges (GBs), far more than
+    # the 256 MB Infinity Cache: one copy is cold
     kernels = {
-        "fwd": lambda: tpc.forward_radial(plan, g, x, Y, rl, W1, W2, None, out=pre),
+        "fwd": lambda c: tpc.forward_radial(plan, g, x, Y, rl, W1, W2, None, out=pre),
         "bwd_recv": bwd(("Y", "W1")),
         "bwd_w2": bwd(("W2",)),
         "bwd_send": bwd(("x",)),
-        "fwd_with_mix": lambda: tpc.forward_radial(plan, g, x, Y, rl, W1, W2, Wm, out=out,
-                                                   out_pre=pre),
+        "fwd_with_mix": lambda c: tpc.forward_radial(plan, g, x, Y, rl, W1, W2, Wm, out=out,
+                                                     out_pre=pre),
     }
     r_sorted = tpc.gather_rows(T(wl.r), g.perm)
     grl = torch.empty_like(rl)
@@ -489,10 +630,10 @@ def bench_radial(args, torch, tpc, make_workload, dev):
     extras = {
         # receiver pass that also returns the edge-length gradient, then the
         # edge-vector gradient
-        "bwd_recv_with_rlen": lambda: tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go,
-                                                          want=("Y", "W1", "rlen"), outs=outs_f,
-                                                          ws=ws),
-        "forces": lambda: tpc.sph_harm_backward(lsh, r_sorted, outs["Y"], grl, out=grad_r),
+        "bwd_recv_with_rlen": lambda c: tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go,
+                                                            want=("Y", "W1", "rlen"), outs=outs_f,
+                                                            ws=ws),
+        "forces": lambda c: tpc.sph_harm_backward(lsh, r_sorted, outs["Y"], grl, out=grad_r),
     }
     flush.fill_(1.0)
     timed_steps(step, args.warmup, True)
@@ -502,62 +643,131 @@ def bench_radial(args, torch, tpc, make_workload, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
     reps, rounds = 3, 2
-    kt = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in kernels.items()}
-    extra_ms = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in extras.items()}
+    kt = {n: float(timed_kernel(fn, 1, reps, rounds).mean()) for n, fn in kernels.items()}
+    extra_ms = {n: float(timed_kernel(fn, 1, reps, rounds).mean()) for n, fn in extras.items()}
     fl = radial_flops(E, P, U, NH)
-    copy_gbs = copy_bandwidth(torch, dev, flush)
-    wk = read_profile_value(args.config, "write_kib.fwd", RADIAL_SOURCES)
-    fwd_write_ratio = None if wk is None else wk * 1024 / (4.0 * N * plan.outdim)
+    mix_flops = 2.0 * N * plan.outdim * U            # one application of the channel mix
     names = ["fwd", "bwd_recv", "bwd_w2", "bwd_send"]
     dom = max(names, key=lambda n: kt[n])
     achieved = fl[dom] / (kt[dom] * 1e-3) / 1e12
     step_ms = float(t.mean())
-    traffic = read_traffic(args.config, RADIAL_SOURCES)
+    step_flops = sum(fl[n] for n in names) + 3 * mix_flops   # mix forward, grad_in, grad_Wmix
+    traffic = read_traffic(name, RADIAL_SOURCES)
     res = {
+        "workload": f"{name}: {desc}", "n_nodes": N, "n_edges": E, "irreps": irreps,
+        "lmax_sh": lsh, "lmax_out": lout, "paths": P,
+        "radial": {"basis": radial[0], "hidden": radial[1], "r_cut": radial[2]}, "mode": "fwd+bwd",
+        "ms_per_step": step_ms,
+        "edges_per_s": E / (step_ms * 1e-3),
+        "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
+        "fwd_edges_per_s": E / (kt["fwd_with_mix"] * 1e-3),
+        "kernel_ms": kt,
+        "kernel_ms_note": (f"per call, {reps} back-to-back calls after a cache flush, mean of {rounds} "
+                           "(every call gathers GBs of node rows: cold without rotation); bwd_recv "
+                           "and bwd_w2 include their partial-sum kernels"),
+        "kernel_mfma_frac": {n: fl[n] / (kt[n] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS for n in names},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": fl[dom],
+                     "ms": kt[dom], "traffic": (traffic or {}).get(dom)},
+        "step_roofline": {"bound": "mfma", "flops": step_flops, "ms": step_ms,
+                          "achieved": step_flops / (step_ms * 1e-3) / 1e12,
+                          "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": step_flops / (step_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+                          "note": "radial-network products of the four passes plus three applications "
+                                  "of the channel mix (forward, grad_in, grad_Wmix)"},
+        "forces_ms": extra_ms,
+        "forces_note": "receiver pass that also returns the edge-length gradient, and the "
+                       "edge-vector gradient kernel; not part of the step",
+        "wall_s_timed_region": wall,
+    }
+    res["cpu_baseline"] = cpu_baseline_radial(irreps, lsh, lout, wl, radial) if cpu else None
+    return res, step
+
+
+def headline(name, res, args):
+    """The one-line contract around a workload's result."""
+    line = {
         "metric": METRIC,
-        "value": E / (step_ms * 1e-3),
+        "value": res["edges_per_s"],
         "unit": "edges/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_ms,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded; random-init radial MLP and mix weights)",
-        "config": {"workload": f"{args.config}: {desc}", "n_nodes": N, "n_edges": E,
-                   "irreps": irreps, "lmax_sh": lsh, "lmax_out": lout, "paths": P,
-                   "radial": {"basis": radial[0], "hidden": radial[1], "r_cut": radial[2]},
-                   "mode": "fwd+bwd", "cache": "L2+MALL flushed before each step"},
-        "fwd_edges_per_s": E / (kt["fwd_with_mix"] * 1e-3),
-        "fwd_edges_per_s_note": "forward alone (radial pass + mix, launch durations)",
-        "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
-        "kernel_ms": kt,
-        "kernel_ms_note": f"per call, {reps} back-to-back calls after a cache flush, mean of "
-                          f"{rounds}; bwd_recv and bwd_w2 include their partial-sum kernels",
-        "kernel_mfma_frac": {n: fl[n] / (kt[n] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS
-                             for n in names},
-        "forces_ms": extra_ms,
-        "forces_note": "receiver pass that also returns the edge-length gradient, and the "
-                       "edge-vector gradient kernel; not part of the step",
-        "copy_GBs": copy_gbs,
-        "fwd_write_ratio": fwd_write_ratio,
-        "fwd_write_note": "radial pass HBM writes (WRITE_SIZE, committed summary) over "
-                          "N*outdim*4: no per-edge weight or message is written",
-        "wall_s_timed_region": wall,
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
-                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": fl[dom],
-                     "traffic": (traffic or {}).get(dom)},
+        "data": "synthetic (seeded; stands in for the pages' molecular graphs and random-init models)",
+        "config": {"workload": res["workload"], "n_nodes": res["n_nodes"], "n_edges": res["n_edges"],
+                   "irreps": res["irreps"], "lmax_sh": res["lmax_sh"], "lmax_out": res["lmax_out"],
+                   "paths": res["paths"], "mode": res["mode"],
+                   "cache": "L2+MALL flushed before each step; kernels cold by rotating copies"},
     }
-    if not args.no_cpu_baseline:
-        import oracle
-        op = oracle.build_plan(irreps, lsh, lout)
-        res["cpu_baseline"] = cpu_baseline_radial(op, wl, radial)
+    line.update({k: v for k, v in res.items() if k not in ("workload", "n_nodes", "n_edges", "irreps",
+                                                           "lmax_sh", "lmax_out", "paths", "mode",
+                                                           "ms_per_step", "edges_per_s")})
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="all",
+                    choices=["all"] + sorted(WORKLOADS) + sorted(RADIAL_WORKLOADS) + sorted(FC_WORKLOADS)
+                    + sorted(GAUNT_WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time the steps back to back without the cache flush")
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for rocprofv3 counter passes: a few steps plus a 512 MiB copy")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the receiver-range sharding is a design, not code). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tensor_product_convolution_amd as tpc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.config in FC_WORKLOADS:
+        return bench_fc(args, torch, tpc, dev)
+    if args.config in GAUNT_WORKLOADS:
+        return bench_gaunt(args, torch, tpc, dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    cpu = not args.no_cpu_baseline
+    name = "mid" if args.config == "all" else args.config
+    if name in RADIAL_WORKLOADS:
+        res, _ = bench_radial(name, args, torch, tpc, dev, flush, cpu)
     else:
-        res["cpu_baseline"] = None
-    print(json.dumps(res))
+        res, _ = bench_direct(name, args, torch, tpc, dev, flush, cpu)
+    if res is None:          # counters run
+        return
+    line = headline(name, res, args)
+    line["copy_GBs"] = copy_bandwidth(torch, dev, flush)
+    line["copy_note"] = ("plain device copy of 512 MiB (read + write) after a flush: the practical "
+                         "ceiling of a kernel that writes as much as it reads")
+    if args.config == "all":
+        configs = {}
+        for other in DEFAULT_CONFIGS:
+            torch.cuda.empty_cache()
+            if other in RADIAL_WORKLOADS:
+                r, _ = bench_radial(other, args, torch, tpc, dev, flush, cpu)
+            else:
+                r, _ = bench_direct(other, args, torch, tpc, dev, flush, cpu)
+            configs[other] = r
+            print(json.dumps({"progress": other, "ms_per_step": r["ms_per_step"]}), file=sys.stderr,
+                  flush=True)
+        line["configs"] = configs
+    print(json.dumps(line))
 
 
 def fc_algorithmic(N, E, P, U, H, d3_paths, d1_paths, xdim, outdim, ysh):
@@ -579,8 +789,8 @@ def fc_algorithmic(N, E, P, U, H, d3_paths, d1_paths, xdim, outdim, ysh):
     }
 
 
-def bench_fc(args, torch, tpc, make_workload, dev):
-    from workloads import make_fc_inputs
+def bench_fc(args, torch, tpc, dev):
+    from workloads import make_fc_inputs, make_workload
     irreps, lsh, lout, H, desc = FC_WORKLOADS[args.config]
     plan = tpc.Plan(irreps, lsh, lout)
     wl = make_workload("mid", plan.dims(), seed=0)
@@ -624,7 +834,7 @@ def bench_fc(args, torch, tpc, make_workload, dev):
     wall = time.perf_counter() - t_wall0
     step_ms = float(np.median(t))
     reps, rounds = 5, max(2, args.steps // 5)
-    kt = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in phases.items()}
+    kt = {n: float(timed_kernel(lambda c, f=fn: f(), 1, reps, rounds).mean()) for n, fn in phases.items()}
     d3s = [2 * l3 + 1 for (_, _, l3, _) in plan.paths()]
     d1s = [2 * l1 + 1 for (l1, _, _, _) in plan.paths()]
     alg = fc_algorithmic(N, E, P, U, H, d3s, d1s, plan.xdim, plan.outdim, plan.ysh)
@@ -656,25 +866,23 @@ def bench_fc(args, torch, tpc, make_workload, dev):
     if not args.no_cpu_baseline:
         import oracle
         op = oracle.build_plan(irreps, lsh, lout)
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            threads = 1
+        from threadpoolctl import threadpool_limits
         n_s = 12000
         order = np.argsort(wl.dst, kind="stable")[:n_s]
         e = np.sort(order)
         nodes = np.unique(np.concatenate([wl.src[e], wl.dst[e]]))
         src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
-        t0 = time.perf_counter()
-        Yo = oracle.sh_real(lsh, wl.r[e])
-        oracle.fc_conv_fwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th)
-        oracle.fc_conv_bwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th, go_h[nodes])
-        dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": len(e) / dt, "unit": "edges/s", "cores": int(threads),
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            Yo = oracle.sh_real(lsh, wl.r[e])
+            oracle.fc_conv_fwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th)
+            oracle.fc_conv_bwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th, go_h[nodes])
+            dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(e) / dt, "unit": "edges/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"{len(e)} of {E} edges (the first receivers), harmonics + "
-                                         f"fwd + bwd once, float64 (per-edge weights formed), {dt:.2f} s"}
+                                         f"fwd + bwd once, float64 (per-edge weights formed), one "
+                                         f"process with one BLAS thread, {dt:.2f} s"}
     print(json.dumps(res))
 
 
@@ -697,8 +905,8 @@ def gaunt_algorithmic(N, E, U, xdim, ysh, wdim, outdim):
     }
 
 
-def bench_gaunt(args, torch, tpc, make_workload, dev):
-    from workloads import make_gaunt_weights
+def bench_gaunt(args, torch, tpc, dev):
+    from workloads import make_gaunt_weights, make_workload
     irreps, lsh, lout, desc = GAUNT_WORKLOADS[args.config]
     plan = tpc.Plan(irreps, lsh, lout, mode=tpc.TP_MODE_GAUNT)
     outdim, wdim, Q = tpc.gaunt_dims(plan)
@@ -739,7 +947,7 @@ def bench_gaunt(args, torch, tpc, make_workload, dev):
     wall = time.perf_counter() - t_wall0
     step_ms = float(np.median(t))
     reps, rounds = 10, max(2, args.steps // 5)
-    kt = {n: float(timed_kernel(fn, reps, rounds).mean()) for n, fn in kernels.items()}
+    kt = {n: float(timed_kernel(lambda c, f=fn: f(), 1, reps, rounds).mean()) for n, fn in kernels.items()}
     alg = gaunt_algorithmic(N, E, U, plan.xdim, plan.ysh, wdim, outdim)
     dom = max(kt, key=kt.get)
     tfs = alg[dom]["flops"] / (kt[dom] * 1e-3) / 1e12
@@ -770,24 +978,22 @@ def bench_gaunt(args, torch, tpc, make_workload, dev):
     }
     if not args.no_cpu_baseline:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            threads = 1
+        from threadpoolctl import threadpool_limits
         gp = oracle.gaunt_plan(irreps, lsh, lout)
         dts = []
-        for _ in range(3):
-            t0 = time.perf_counter()
-            Yo = oracle.sh_real(lsh, wl.r)
-            oracle.gaunt_conv_fwd(gp, wl.src, wl.dst, N, wl.x, Yo, w)
-            oracle.gaunt_conv_bwd(gp, wl.src, wl.dst, N, wl.x, Yo, w, go_h)
-            dts.append(time.perf_counter() - t0)
+        with threadpool_limits(1):
+            for _ in range(3):
+                t0 = time.perf_counter()
+                Yo = oracle.sh_real(lsh, wl.r)
+                oracle.gaunt_conv_fwd(gp, wl.src, wl.dst, N, wl.x, Yo, w)
+                oracle.gaunt_conv_bwd(gp, wl.src, wl.dst, N, wl.x, Yo, w, go_h)
+                dts.append(time.perf_counter() - t0)
         dt = float(np.median(dts))
-        res["cpu_baseline"] = {"value": E / dt, "unit": "edges/s", "cores": int(threads),
+        res["cpu_baseline"] = {"value": E / dt, "unit": "edges/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"the whole workload ({E} edges), harmonics + Gaunt fwd + bwd, "
-                                         f"float64, median of 3 runs ({dt:.2f} s each)"}
+                                         f"float64, one process with one BLAS thread, median of 3 runs "
+                                         f"({dt:.2f} s each)"}
     print(json.dumps(res))
 
 
