@@ -173,6 +173,23 @@ tp_status tp_conv_graph_build(const int32_t* src, const int32_t* dst, int32_t n_
                               int32_t* t_row_ptr, int32_t* t_perm, int32_t* t_col, void* ws,
                               size_t ws_bytes, int32_t flags, hipStream_t stream);
 
+/* tp_conv_graph_build without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The sort's scratch is a static device
+ * array of TP_GRAPH_STATIC_SCRATCH_BYTES (24 MiB) inside the library, one per
+ * GPU, held until the process ends; no call allocates.  Arguments, results
+ * and errors as tp_conv_graph_build (bit-identical arrays), plus
+ * TP_ERR_WORKSPACE, before any HIP call, when tp_conv_graph_workspace(n_nodes,
+ * n_edges) exceeds TP_GRAPH_STATIC_SCRATCH_BYTES (graphs above about 1.2
+ * million edges).  Every call on one GPU uses that GPU's single array: calls
+ * that overlap on one GPU (other streams or threads) race, and the caller
+ * must serialise them. */
+#define TP_GRAPH_STATIC_SCRATCH_BYTES (24u << 20)
+tp_status tp_conv_graph_build_static(const int32_t* src, const int32_t* dst, int32_t n_edges,
+                                     int32_t n_nodes, int32_t* row_ptr, int32_t* col, int32_t* perm,
+                                     int32_t* t_row_ptr, int32_t* t_perm, int32_t* t_col, int32_t flags,
+                                     hipStream_t stream);
+
 /* out[q, :] = in[perm[q], :] for q < n_rows, rows of row_words 32-bit words
  * (device pointers).  Puts edge-sized inputs into receiver-sorted order.
  * Helper: the layout every edge-sized argument uses (see above); perm must

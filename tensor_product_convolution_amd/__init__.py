@@ -27,7 +27,7 @@ TP_FC_STATE_SAVED = 1
 EXPORTS = (
     "tp_conv_plan_create", "tp_conv_plan_info", "tp_conv_plan_paths", "tp_conv_plan_cg",
     "tp_conv_plan_destroy", "tp_cg_real", "tp_conv_graph_workspace", "tp_conv_graph_build",
-    "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
+    "tp_conv_graph_build_static", "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
     "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
@@ -79,6 +79,7 @@ def lib():
         "tp_cg_real": (I32, [I32, I32, I32, VP]),
         "tp_conv_graph_workspace": (I32, [I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_graph_build": (I32, [VP, VP, I32, I32, VP, VP, VP, VP, VP, VP, VP, SZ, I32, VP]),
+        "tp_conv_graph_build_static": (I32, [VP, VP, I32, I32, VP, VP, VP, VP, VP, VP, I32, VP]),
         "tp_conv_gather_rows": (I32, [VP, VP, I64, I64, VP, VP]),
         "tp_conv_sph_harm": (I32, [I32, VP, I32, VP, VP]),
         "tp_conv_forward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
@@ -241,6 +242,26 @@ def graph_build(src, dst, n_nodes, check=True):
                                      _ptr(g.t_perm), _ptr(g.t_col), _ptr(ws), need.value,
                                      TP_GRAPH_CHECK if check else 0, _stream(dev)))
     g._ws = ws
+    return g
+
+
+def graph_build_static(src, dst, n_nodes, check=True, out=None):
+    """graph_build through the entry point that allocates nothing (the
+    library's static scratch); ``out`` (a Graph of the right sizes) is
+    filled in place, else new arrays are made."""
+    torch = _torch()
+    _need(src, "src", torch.int32)
+    E = src.shape[0]
+    _need(dst, "dst", torch.int32, (E,))
+    dev = src.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    g = out or Graph(n_nodes, E, torch.empty(n_nodes + 1, **i32), torch.empty(E, **i32),
+                     torch.empty(E, **i32), torch.empty(n_nodes + 1, **i32),
+                     torch.empty(E, **i32), torch.empty(E, **i32))
+    _check(lib().tp_conv_graph_build_static(_ptr(src), _ptr(dst), E, n_nodes, _ptr(g.row_ptr),
+                                            _ptr(g.col), _ptr(g.perm), _ptr(g.t_row_ptr),
+                                            _ptr(g.t_perm), _ptr(g.t_col),
+                                            TP_GRAPH_CHECK if check else 0, _stream(dev)))
     return g
 
 

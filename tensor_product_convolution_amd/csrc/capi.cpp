@@ -352,6 +352,28 @@ tp_status tp_conv_graph_build(const int32_t* src, const int32_t* dst, int32_t n_
                           ws, flags, stream);
 }
 
+tp_status tp_conv_graph_build_static(const int32_t* src, const int32_t* dst, int32_t n_edges,
+                                     int32_t n_nodes, int32_t* row_ptr, int32_t* col, int32_t* perm,
+                                     int32_t* t_row_ptr, int32_t* t_perm, int32_t* t_col, int32_t flags,
+                                     hipStream_t stream) {
+  if (n_nodes < 0 || n_edges < 0)
+    return set_error(TP_ERR_ARG, "tp_conv_graph_build_static: negative size");
+  if (n_edges > 0 && n_nodes == 0)
+    return set_error(TP_ERR_ARG, "tp_conv_graph_build_static: edges need at least one node");
+  if (!row_ptr || !t_row_ptr) return set_error(TP_ERR_ARG, "tp_conv_graph_build_static: NULL row pointer");
+  if (n_edges > 0 && (!src || !dst || !col || !perm || !t_perm || !t_col))
+    return set_error(TP_ERR_ARG, "tp_conv_graph_build_static: NULL edge array");
+  const size_t need = tpc::graph_workspace_bytes(n_nodes, n_edges);
+  if (need > TP_GRAPH_STATIC_SCRATCH_BYTES)
+    return set_error(TP_ERR_WORKSPACE,
+                     "tp_conv_graph_build_static: " + std::to_string(n_edges) + " edges need " +
+                         std::to_string(need) + " bytes of scratch; the static scratch holds " +
+                         std::to_string((size_t)TP_GRAPH_STATIC_SCRATCH_BYTES) +
+                         " (use tp_conv_graph_build with a workspace)");
+  return tpc::graph_build_static(src, dst, n_edges, n_nodes, row_ptr, col, perm, t_row_ptr, t_perm, t_col,
+                                 flags, stream);
+}
+
 tp_status tp_conv_gather_rows(const void* in, const int32_t* perm, int64_t n_rows,
                               int64_t row_words, void* out, hipStream_t stream) {
   if (n_rows < 0 || row_words < 0) return set_error(TP_ERR_ARG, "tp_conv_gather_rows: negative size");

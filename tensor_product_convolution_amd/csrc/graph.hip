@@ -21,6 +21,8 @@
 // Row pointers come from boundaries of the sorted keys (no atomics).  The
 // sender grouping sorts the receiver-sorted sender column the same way, so
 // its ties keep receiver-sorted order.
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace tpc {
@@ -298,6 +300,47 @@ tp_status graph_build(const int32_t* src, const int32_t* dst, int n_edges, int n
     hipLaunchKernelGGL(k_gather2_i32, dim3(eb), dim3(256), 0, st, dst, perm, t_perm, n_edges, n_nodes, t_col);
   if ((e = hipGetLastError()) != hipSuccess) return hip_error(e, "graph build launch");
   return TP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Graph build without a workspace argument: the sort's scratch is a device
+// array of this translation unit, one per GPU (each GPU that loads the
+// library holds its own copy until the process ends).  Its host-side name is
+// only a stand-in; the device address comes from hipGetSymbolAddress on the
+// first call on each device (with that device current) and is kept per
+// device.  Nothing here allocates.  Every scratch word the build reads is
+// written by the same build first (tile histograms, scans, sort buffers; the
+// range-check flag is cleared by a fill kernel), so the contents a previous
+// call left need no clearing.
+static __device__ __align__(256) char scratch[TP_GRAPH_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+tp_status graph_build_static(const int32_t* src, const int32_t* dst, int n_edges, int n_nodes,
+                             int32_t* row_ptr, int32_t* col, int32_t* perm, int32_t* t_row_ptr,
+                             int32_t* t_perm, int32_t* t_col, int32_t flags, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_error(e, "tp_conv_graph_build_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(TP_ERR_ARG, "tp_conv_graph_build_static: device index beyond 64");
+  void* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_error(e, "tp_conv_graph_build_static: hipGetSymbolAddress");
+      g_scratch_ptr[dev] = p;
+    }
+    base = g_scratch_ptr[dev];
+  }
+  return graph_build(src, dst, n_edges, n_nodes, row_ptr, col, perm, t_row_ptr, t_perm, t_col, base,
+                     flags, st);
 }
 
 tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64_t words, void* out,

@@ -124,6 +124,9 @@ size_t graph_workspace_bytes(int n_nodes, int n_edges);
 tp_status graph_build(const int32_t* src, const int32_t* dst, int n_edges, int n_nodes,
                       int32_t* row_ptr, int32_t* col, int32_t* perm, int32_t* t_row_ptr,
                       int32_t* t_perm, int32_t* t_col, void* ws, int32_t flags, hipStream_t st);
+tp_status graph_build_static(const int32_t* src, const int32_t* dst, int n_edges, int n_nodes,
+                             int32_t* row_ptr, int32_t* col, int32_t* perm, int32_t* t_row_ptr,
+                             int32_t* t_perm, int32_t* t_col, int32_t flags, hipStream_t st);
 tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64_t words, void* out,
                       hipStream_t st);
 tp_status sph_harm(int lmax, const float* r, int n, float* Y, hipStream_t st);

@@ -104,6 +104,15 @@ def test_graph_and_conv_argument_errors_without_launch():
                                  need.value, 0, None) == -1
     assert L.tp_conv_graph_build(fake, fake, 10, 0, fake, fake, fake, fake, fake, fake, fake,
                                  need.value, 0, None) == -1
+    # the graph build without a workspace: argument errors and a graph beyond its
+    # static scratch are reported before any HIP call
+    assert L.tp_conv_graph_build_static(fake, fake, 10, 0, fake, fake, fake, fake, fake, fake, 0, None) == -1
+    assert L.tp_conv_graph_build_static(None, None, 10, 4, fake, fake, fake, fake, fake, fake, 0, None) == -1
+    big = 2_000_000
+    assert L.tp_conv_graph_workspace(100000, big, ctypes.byref(need)) == 0 and need.value > 24 << 20
+    assert L.tp_conv_graph_build_static(fake, fake, big, 100000, fake, fake, fake, fake, fake, fake, 0,
+                                        None) == -5
+    assert "static scratch" in L.tp_conv_last_error().decode()
     assert L.tp_conv_sph_harm(2, None, 5, None, None) == -1
     assert L.tp_conv_gather_rows(None, None, 5, 3, None, None) == -1
     assert L.tp_conv_gather_rows(fake, fake, -1, 3, fake, None) == -1
