@@ -5,6 +5,8 @@ max|ref| of that block, against the float64 oracle on identical seeded
 float32 inputs.  Each side computes its own harmonics and radial weights from
 the same edge vectors.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -170,43 +172,100 @@ def _subgraph(wl, e, recv):
     return nodes, src, dst, np.searchsorted(nodes, recv)
 
 
+def _oracle_radial_part(task):
+    """oracle forward (with the unmixed output) and backward of one chunk of whole
+    receivers on its own subgraph (a process-pool worker)"""
+    op, src, dst, n, x, Y, rl, W1, W2, Wm, g2 = task
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    out, pre = oracle.tp_conv_radial_fwd(op, src, dst, n, x, Y, rl, W1, W2, Wm, 8, RC, return_pre_mix=True)
+    return out, pre, oracle.tp_conv_radial_bwd(op, src, dst, n, x, Y, rl, W1, W2, Wm, g2, 8, RC,
+                                               with_grad_rlen=True)
+
+
+def _pooled_radial_oracle(op, wl, e, recv, g2, workers):
+    """The oracle on the edges e into the receivers recv, split by receiver over a
+    process pool; per-node rows and parameter gradients are summed (each
+    receiver's in-edges sit in one chunk, so its outputs are whole there)."""
+    import multiprocessing as mp
+    order = np.argsort(wl.dst[e], kind="stable")
+    bounds = np.linspace(0, len(order), workers + 1).astype(np.int64)
+    cuts = [0]
+    for c in bounds[1:-1]:
+        while 0 < c < len(order) and wl.dst[e[order[c]]] == wl.dst[e[order[c - 1]]]:
+            c += 1
+        cuts.append(max(c, cuts[-1]))
+    cuts.append(len(order))
+    tasks, parts = [], []
+    for t in range(workers):
+        ec = e[np.sort(order[cuts[t]:cuts[t + 1]])]
+        if len(ec) == 0:
+            continue
+        rc = np.unique(wl.dst[ec])
+        nodes, src, dst, _ = _subgraph(wl, ec, rc)
+        tasks.append((op, src, dst, len(nodes), wl.x[nodes], oracle.sh_real(2, wl.r[ec]), wl.r_len[ec],
+                      wl.W1, wl.W2, wl.Wmix, g2[nodes]))
+        parts.append((ec, nodes))
+    with mp.get_context("fork").Pool(workers) as pool:
+        res = pool.map(_oracle_radial_part, tasks)
+    N, E = wl.n_nodes, wl.n_edges
+    out = np.zeros((N, op.outdim))
+    pre = np.zeros((N, op.outdim))
+    gx = np.zeros((N, op.xdim))
+    gY = np.zeros((E, op.ysh))
+    grl = np.zeros(E)
+    gW1 = gW2 = gWm = 0.0
+    for (ec, nodes), (o, p, r) in zip(parts, res):
+        out[nodes] += o
+        pre[nodes] += p
+        gx[nodes] += r[0]
+        gY[ec], grl[ec] = r[1], r[5]
+        gW1, gW2, gWm = gW1 + r[2], gW2 + r[3], gWm + r[4]
+    return out, pre, (gx, gY, gW1, gW2, gWm, grl)
+
+
 def test_radial_full_size_sampled(tpc):
     """The 100,000-atom / 3,000,000-edge streaming layer with its mix, forward and
-    backward at full size in the launch configuration the benchmark times.  Forward:
-    sampled receivers.  Backward: the upstream gradient is zero outside the sampled
-    receivers, so every gradient (including the parameter sums over all edges) is
-    exactly that of the sampled receivers' edges, which the oracle computes."""
-    say("radial full-size sampled: stream 100000 nodes")
+    backward at full size in the launch configuration the benchmark times.  The
+    upstream gradient is zero outside 2,048 sampled receivers, so every gradient
+    (including the parameter sums over all edges) is exactly that of those
+    receivers' edges, which the oracle computes.  The receivers are i = k + 2048 (k
+    mod 48), k < 2048: one in every residue class mod 2048, so every per-wave
+    partial sum of the receiver pass (node i -> slot i mod 2048 at full size) and
+    every block of the grad_W2 pass (node i -> block (i mod 256) / 4) carries data,
+    and the fixed-order sums over all of them are checked element by element."""
+    say("radial full-size sampled: stream 100000 nodes, 2048 receivers")
     U = 128
     op = oracle.build_plan(_irreps(U), 2, 2)
     wl = make_workload("stream", dims_of(op))
     N = wl.n_nodes
-    rng = np.random.default_rng(11)
-    recv = np.sort(rng.choice(N, size=24, replace=False))
+    k = np.arange(2048)
+    recv = np.sort(k + 2048 * (k % 48))
+    assert len(np.unique(recv % 2048)) == 2048 and recv.max() < N
     g2 = np.zeros_like(wl.g)
     g2[recv] = wl.g[recv]
     plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
     res = _gpu_radial(tpc, plan, wl, True, g2)
     e = np.nonzero(np.isin(wl.dst, recv))[0]
-    nodes, src, dst, rpos = _subgraph(wl, e, recv)
-    n = len(nodes)
-    Yo = oracle.sh_real(2, wl.r[e])
-    rl = wl.r_len[e]
-    ref_out, ref_pre = oracle.tp_conv_radial_fwd(op, src, dst, n, wl.x[nodes], Yo, rl, wl.W1, wl.W2,
-                                                 wl.Wmix, 8, RC, return_pre_mix=True)
-    assert block_err(res["pre"][recv], ref_pre[rpos], out_blocks(op)) <= TOL
-    assert block_err(res["out"][recv], ref_out[rpos], out_blocks(op)) <= TOL
-    # backward on the subgraph: the upstream gradient is zero off the sampled receivers
-    ref = oracle.tp_conv_radial_bwd(op, src, dst, n, wl.x[nodes], Yo, rl, wl.W1, wl.W2, wl.Wmix,
-                                    g2[nodes], 8, RC, with_grad_rlen=True)
-    assert block_err(res["gx"][nodes], ref[0], in_blocks(op)) <= TOL
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    say(f"  oracle on {len(e)} edges over {workers} processes")
+    ref_out, ref_pre, ref = _pooled_radial_oracle(op, wl, e, recv, g2, workers)
+    assert block_err(res["pre"][recv], ref_pre[recv], out_blocks(op)) <= TOL
+    assert block_err(res["out"][recv], ref_out[recv], out_blocks(op)) <= TOL
+    # backward: the upstream gradient is zero off the sampled receivers
+    nodes = np.unique(np.concatenate([wl.src[e], recv]))
+    assert block_err(res["gx"][nodes], ref[0][nodes], in_blocks(op)) <= TOL
+    rng = np.random.default_rng(11)
     others = np.setdiff1d(rng.choice(N, size=200, replace=False), nodes)
     assert np.all(res["gx"][others] == 0)
     inv = np.empty(wl.n_edges, np.int64)
     inv[res["perm"]] = np.arange(wl.n_edges)
-    assert block_err(res["gY"][inv[e]], ref[1], y_blocks(op)) <= TOL
-    assert _vec_err(res["grl"][inv[e]], ref[5]) <= TOL
-    assert _vec_err(res["gr"][inv[e]], _forces_ref(wl.r[e], ref[1], ref[5])) <= TOL
+    assert block_err(res["gY"][inv[e]], ref[1][e], y_blocks(op)) <= TOL
+    assert _vec_err(res["grl"][inv[e]], ref[5][e]) <= TOL
+    assert _vec_err(res["gr"][inv[e]], _forces_ref(wl.r[e], ref[1][e], ref[5][e])) <= TOL
     mask = np.ones(wl.n_edges, bool)
     mask[inv[e]] = False
     assert np.all(res["gY"][mask][:100000] == 0)
