@@ -228,6 +228,31 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
                            const float* Y, const float* w, const float* grad_out,
                            float* grad_x, float* grad_Y, float* grad_w, hipStream_t stream);
 
+/* ---- edge-vector form: harmonics evaluated on chip -------------------------
+ * The layer as a function of the edge vectors r [E][3] (receiver-sorted,
+ * r_e = pos[src] - pos[dst]) instead of their harmonics: each edge's
+ * Y = Y(r_e / |r_e|) (component-normalised, lmax_sh of the plan; a zero vector
+ * gives the polynomials at the origin, as tp_conv_sph_harm) is formed in
+ * registers, so no Y array is read or written ("Sobek", Abstract: no
+ * edge-sized intermediate; the harmonics of the edge direction are the
+ * product's second operand, "The GPU Workload That Rewrites Molecular
+ * Physics", section "What Makes MLFF Workloads Structurally Different").
+ * tp_conv_forward_r(.., r, ..) equals tp_conv_forward(.., tp_conv_sph_harm(r), ..).
+ * x and w must be 16-byte aligned (TP_ERR_ARG). */
+tp_status tp_conv_forward_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
+                            const float* w, float* out, hipStream_t stream);
+
+/* Backward of tp_conv_forward_r: grad_x [N][xdim], grad_w [E][P][U] and
+ * grad_r [E][3] = sum_b grad_Y[b] dY_b/dr, the gradient with respect to the
+ * edge vectors through the harmonics (the forces of a force field: add
+ * -grad_r to each edge's sender and +grad_r to its receiver), formed per edge
+ * on chip from the same products as grad_Y without storing grad_Y.  Any
+ * output may be NULL.  Same passes, layouts and errors as tp_conv_backward;
+ * x, w and grad_out must be 16-byte aligned.  Deterministic. */
+tp_status tp_conv_backward_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
+                             const float* w, const float* grad_out, float* grad_x, float* grad_r,
+                             float* grad_w, hipStream_t stream);
+
 /* Second-order backward ("Sobek", Abstract: the streaming schedule extends
  * through forward, backward and double backward), e.g. for training on
  * forces.  Given the inputs of tp_conv_backward and cotangents gg_x [N][xdim],

@@ -28,6 +28,7 @@ EXPORTS = (
     "tp_conv_plan_create", "tp_conv_plan_info", "tp_conv_plan_paths", "tp_conv_plan_cg",
     "tp_conv_plan_destroy", "tp_cg_real", "tp_conv_graph_workspace", "tp_conv_graph_build",
     "tp_conv_graph_build_static", "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
+    "tp_conv_forward_r", "tp_conv_backward_r",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
     "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
@@ -84,6 +85,8 @@ def lib():
         "tp_conv_sph_harm": (I32, [I32, VP, I32, VP, VP]),
         "tp_conv_forward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
+        "tp_conv_forward_r": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
+        "tp_conv_backward_r": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
         "tp_conv_uvw_forward": (I32, [P, I32, VP, VP, VP, VP]),
         "tp_conv_uvw_backward": (I32, [P, I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
         "tp_conv_uvw_workspace": (I32, [P, ctypes.POINTER(SZ)]),
@@ -341,6 +344,43 @@ def backward(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=None):
                                   _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw),
                                   _stream(x.device)))
     return gx, gY, gw
+
+
+def forward_r(plan, graph, x, r, w, out=None):
+    """forward from the edge vectors r [E, 3] (receiver-sorted); harmonics on chip."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(r, "r", torch.float32, (E, 3))
+    _need(w, "w", torch.float32, (E, plan.n_paths, plan.mul))
+    if out is None:
+        out = torch.empty((N, plan.outdim), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (N, plan.outdim))
+    g = graph.cstruct()
+    _check(lib().tp_conv_forward_r(plan.handle, ctypes.byref(g), _ptr(x), _ptr(r), _ptr(w),
+                                   _ptr(out), _stream(x.device)))
+    return out
+
+
+def backward_r(plan, graph, x, r, w, grad_out, want=("x", "r", "w"), outs=None):
+    """(grad_x, grad_r, grad_w) of forward_r; entries not in ``want`` come back as None."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(r, "r", torch.float32, (E, 3))
+    _need(w, "w", torch.float32, (E, plan.n_paths, plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    f32 = dict(dtype=torch.float32, device=x.device)
+    if outs is None:
+        gx = torch.empty((N, plan.xdim), **f32) if "x" in want else None
+        gr = torch.empty((E, 3), **f32) if "r" in want else None
+        gw = torch.empty((E, plan.n_paths, plan.mul), **f32) if "w" in want else None
+    else:
+        gx, gr, gw = outs
+    g = graph.cstruct()
+    _check(lib().tp_conv_backward_r(plan.handle, ctypes.byref(g), _ptr(x), _ptr(r), _ptr(w),
+                                    _ptr(grad_out), _ptr(gx), _ptr(gr), _ptr(gw), _stream(x.device)))
+    return gx, gr, gw
 
 
 def double_backward(plan, graph, x, Y, w, grad_out, gg_x=None, gg_Y=None, gg_w=None,

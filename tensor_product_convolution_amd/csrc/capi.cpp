@@ -485,6 +485,62 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   return TP_OK;
 }
 
+tp_status tp_conv_forward_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
+                            const float* w, float* out, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward_r: plan is NULL");
+  tp_status s = check_graph(graph, false);
+  if (s != TP_OK) return s;
+  if (graph->n_nodes > 0 && (!x || !out)) return set_error(TP_ERR_ARG, "tp_conv_forward_r: x/out NULL");
+  if (graph->n_edges > 0 && (!r || !w)) return set_error(TP_ERR_ARG, "tp_conv_forward_r: r/w NULL");
+  if (misaligned16({x, w})) return set_error(TP_ERR_ARG, "tp_conv_forward_r: x and w must be 16-byte aligned");
+  if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_forward_r: not a channel-wise CG plan");
+  tpc::ConvArgs a;
+  a.n_nodes = graph->n_nodes;
+  a.n_edges = graph->n_edges;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.x = x;
+  a.r = r;
+  a.w = w;
+  a.out = out;
+  a.stream = stream;
+  hipError_t e = plan->ks->fwd_r(a);
+  return e == hipSuccess ? TP_OK : tpc::hip_error(e, "tp_conv_forward_r launch");
+}
+
+tp_status tp_conv_backward_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
+                             const float* w, const float* grad_out, float* grad_x, float* grad_r,
+                             float* grad_w, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward_r: plan is NULL");
+  tp_status s = check_graph(graph, grad_x != nullptr);
+  if (s != TP_OK) return s;
+  if (graph->n_nodes > 0 && !grad_out) return set_error(TP_ERR_ARG, "tp_conv_backward_r: grad_out NULL");
+  if (graph->n_edges > 0 && (!r || !w)) return set_error(TP_ERR_ARG, "tp_conv_backward_r: r/w NULL");
+  if (graph->n_edges > 0 && (grad_r || grad_w) && !x)
+    return set_error(TP_ERR_ARG, "tp_conv_backward_r: x NULL");
+  if (misaligned16({x, w, grad_out}))
+    return set_error(TP_ERR_ARG, "tp_conv_backward_r: x, w and grad_out must be 16-byte aligned");
+  if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_backward_r: not a channel-wise CG plan");
+  tpc::ConvArgs a;
+  a.n_nodes = graph->n_nodes;
+  a.n_edges = graph->n_edges;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_perm = graph->t_perm;
+  a.t_col = graph->t_col;
+  a.x = x;
+  a.r = r;
+  a.w = w;
+  a.grad_out = grad_out;
+  a.grad_x = grad_x;
+  a.grad_r = grad_r;
+  a.grad_w = grad_w;
+  a.stream = stream;
+  hipError_t e = plan->ks->bwd_r(a);
+  return e == hipSuccess ? TP_OK : tpc::hip_error(e, "tp_conv_backward_r launch");
+}
+
 tp_status tp_conv_double_backward(tp_plan_t plan, const tp_graph* graph, const float* x,
                                   const float* Y, const float* w, const float* grad_out,
                                   const float* gg_x, const float* gg_Y, const float* gg_w,

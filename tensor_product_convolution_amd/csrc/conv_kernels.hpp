@@ -28,6 +28,7 @@
 //     grad_x[j] once.  No atomics anywhere.
 #pragma once
 #include "internal.hpp"
+#include "sh_eval.hpp"
 #include "sig.hpp"
 
 namespace tpc {
@@ -515,11 +516,14 @@ __device__ __forceinline__ int pick(const int (&v)[N], int r) {
 }
 
 // Per-wave staging layout for receiver-grouped passes: [W | Y | X] per buffer.
-template <class S, int U>
+// GEOM: the edge rows staged are the edge vectors r (3 floats) instead of Y,
+// and the harmonics are evaluated on chip (read_y).
+template <class S, int U, bool GEOM = false>
 struct RecvStage {
   static constexpr int EPW = LaneMap<U>::EPW;
   static constexpr int WB = S::NP * U * 4;       // weight row bytes
-  static constexpr int YB = S::YC * 4;           // Y row bytes
+  static constexpr int YR = GEOM ? 3 : S::YC;    // floats of an edge's geometry row
+  static constexpr int YB = YR * 4;              // Y (or r) row bytes
   static constexpr int XB = S::XC * U * 4;       // x row bytes
   static constexpr int W_OFF = 0;
   static constexpr int Y_OFF = ceil16(EPW * WB);
@@ -529,34 +533,72 @@ struct RecvStage {
 };
 
 // issue the loads of the wave step starting at segment position q0
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 __device__ __forceinline__ void stage_recv(char* buf, const float* __restrict__ x,
                                            const float* __restrict__ Y, const float* __restrict__ w,
                                            const int (&j)[LaneMap<U>::EPW], int q0, int last,
                                            int lane) {
-  using T = RecvStage<S, U>;
+  using T = RecvStage<S, U, GEOM>;
   dma_rows16<T::EPW, T::WB, kStream>(buf + T::W_OFF, [&](int r) {
     return (const char*)(w + (size_t)min(q0 + r, last) * (S::NP * U));
   }, lane);
   dma_rows4<T::EPW, T::YB, kStream>(buf + T::Y_OFF, [&](int r) {
-    return (const char*)(Y + (size_t)min(q0 + r, last) * S::YC);
+    return (const char*)(Y + (size_t)min(q0 + r, last) * T::YR);
   }, lane);
   dma_rows16<T::EPW, T::XB>(buf + T::X_OFF, [&](int r) {
     return (const char*)(x + (size_t)pick(j, r) * (S::XC * U));
   }, lane);
 }
 
+// the edge's harmonics from its staged row: Y itself or, with GEOM, evaluated
+// from the staged edge vector (the unit direction and 1/|r| go to geo for the
+// backward's pullback to r)
+template <class S, bool GEOM>
+__device__ __forceinline__ void read_y(const float* Yv, float (&yr)[S::YC], float (&geo)[4]) {
+  if constexpr (GEOM) {
+    float x = Yv[0], y = Yv[1], z = Yv[2], inv;
+    unit_dir(x, y, z, inv);
+    sh_eval<S::lmax_sh>(x, y, z, yr);
+    geo[0] = x;
+    geo[1] = y;
+    geo[2] = z;
+    geo[3] = inv;
+  } else {
+#pragma unroll
+    for (int b = 0; b < S::YC; ++b) yr[b] = Yv[b];
+  }
+}
+
+// This lane's share of an edge's gradient after the sum over the edge's
+// channel lanes: grad_Y or, with GEOM, grad_r, the pullback of grad_Y to the
+// edge vector (linear, so the per-lane partials are pulled back first and 3
+// values summed instead of (lmax+1)^2).
+template <class S, bool GEOM, int LPE, int NOUT>
+__device__ __forceinline__ void edge_grad_share(float (&gy)[S::YC], const float (&geo)[4], int lane,
+                                                float (&out)[NOUT]) {
+  if constexpr (GEOM) {
+    float g3[3];
+    sh_pullback<S::lmax_sh>(geo[0], geo[1], geo[2], geo[3], gy, 0.f, g3);
+    lane_sum_halving<3, LPE / 2>(g3, lane);
+#pragma unroll
+    for (int r = 0; r < NOUT; ++r) out[r] = g3[r];
+  } else {
+    lane_sum_halving<S::YC, LPE / 2>(gy, lane);
+#pragma unroll
+    for (int r = 0; r < NOUT; ++r) out[r] = gy[r];
+  }
+}
+
 // read this lane's operands of its edge slot from a staged buffer
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 __device__ __forceinline__ void read_recv(const char* buf, int slot, int uu,
                                           float (&xr)[LaneMap<U>::CPL][S::XC], float (&yr)[S::YC],
-                                          float (&wr)[LaneMap<U>::CPL][S::NP]) {
-  using T = RecvStage<S, U>;
+                                          float (&wr)[LaneMap<U>::CPL][S::NP], float (&geo)[4]) {
+  using T = RecvStage<S, U, GEOM>;
   const float* W = (const float*)(buf + T::W_OFF) + slot * (S::NP * U);
-  const float* Yv = (const float*)(buf + T::Y_OFF) + slot * S::YC;
+  const float* Yv = (const float*)(buf + T::Y_OFF) + slot * T::YR;
   const float* X = (const float*)(buf + T::X_OFF) + slot * (S::XC * U);
-#pragma unroll
-  for (int b = 0; b < S::YC; ++b) yr[b] = Yv[b];
+  read_y<S, GEOM>(Yv, yr, geo);
 #pragma unroll
   for (int p = 0; p < S::NP; ++p)
 #pragma unroll
@@ -573,11 +615,12 @@ __device__ __forceinline__ void read_recv(const char* buf, int slot, int uu,
 }
 
 // sender-grouped pass: [W | Y | G] per buffer, all rows gathered
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 struct SendStage {
   static constexpr int EPW = LaneMap<U>::EPW;
   static constexpr int WB = S::NP * U * 4;
-  static constexpr int YB = S::YC * 4;
+  static constexpr int YR = GEOM ? 3 : S::YC;
+  static constexpr int YB = YR * 4;
   static constexpr int GB = S::OC * U * 4;
   static constexpr int W_OFF = 0;
   static constexpr int Y_OFF = ceil16(EPW * WB);
@@ -586,17 +629,17 @@ struct SendStage {
   static constexpr int NLOADS = dma16_count<EPW, WB>() + dma4_count<EPW, YB>() + dma16_count<EPW, GB>();
 };
 
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 __device__ __forceinline__ void stage_send(char* buf, const float* __restrict__ Y,
                                            const float* __restrict__ w, const float* __restrict__ g,
                                            const int (&q)[LaneMap<U>::EPW],
                                            const int (&i)[LaneMap<U>::EPW], int lane) {
-  using T = SendStage<S, U>;
+  using T = SendStage<S, U, GEOM>;
   dma_rows16<T::EPW, T::WB, kStream>(buf + T::W_OFF, [&](int r) {
     return (const char*)(w + (size_t)pick(q, r) * (S::NP * U));
   }, lane);
   dma_rows4<T::EPW, T::YB, kStream>(buf + T::Y_OFF, [&](int r) {
-    return (const char*)(Y + (size_t)pick(q, r) * S::YC);
+    return (const char*)(Y + (size_t)pick(q, r) * T::YR);
   }, lane);
   dma_rows16<T::EPW, T::GB>(buf + T::G_OFF, [&](int r) {
     return (const char*)(g + (size_t)pick(i, r) * (S::OC * U));
@@ -669,15 +712,15 @@ __device__ __forceinline__ void wait_steps(int ahead, int sg) {
 // Launch configuration of a signature / multiplicity: waves per block and
 // staging depth, bounded by the 63 outstanding vector-memory operations a wave
 // can count and by 64 KB of LDS per workgroup.
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 struct Cfg {
   using M = LaneMap<U>;
-  using R = RecvStage<S, U>;
-  using Sd = SendStage<S, U>;
+  using R = RecvStage<S, U, GEOM>;
+  using Sd = SendStage<S, U, GEOM>;
   // receiver pass stores per step and lane: one word per path and channel set
   // (grad_w), the lane's share of grad_Y after the halving channel sum
   static constexpr int ST_W = S::NP * M::CPL;
-  static constexpr int ST_Y = ls_final(S::YC, M::LPE);
+  static constexpr int ST_Y = ls_final(GEOM ? 3 : S::YC, M::LPE);   // grad_Y (or grad_r) share
   static constexpr int NST = ST_W + ST_Y;
   // Staging depth: double buffering (deeper pipelines measured slower on the
   // 1,536-atom workload), single buffering when a step has too many memory
@@ -717,23 +760,24 @@ struct Cfg {
                     fits(Sd::BUF, NBUF_S, WPB_S), "staging exceeds 64 KB of LDS");
 };
 
-template <class S, int U, int WPB, int NBUF>
+template <class S, int U, int WPB, int NBUF, bool GEOM = false>
 struct FwdSmem {
-  static constexpr int STAGE = NBUF * WPB * RecvStage<S, U>::BUF;
+  static constexpr int STAGE = NBUF * WPB * RecvStage<S, U, GEOM>::BUF;
   static constexpr int RED = WPB * LaneMap<U>::CPL * S::OC * 65 * 4;
   static constexpr int BYTES = STAGE > RED ? STAGE : RED;
 };
 
-template <class S, int U, int WPB, int NBUF>
+// GEOM: Y holds the edge vectors r [E][3] and the harmonics are evaluated on chip
+template <class S, int U, int WPB, int NBUF, bool GEOM = false>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                const float* __restrict__ x, const float* __restrict__ Y,
                const float* __restrict__ w, float* __restrict__ out) {
   using M = LaneMap<U>;
-  using T = RecvStage<S, U>;
+  using T = RecvStage<S, U, GEOM>;
   constexpr int OD = U * S::OC, SLOTS = WPB * M::EPW, EPW = M::EPW;
   static_assert((NBUF - 1) * T::NLOADS < 64, "pipeline too deep for vmcnt");
-  __shared__ __attribute__((aligned(16))) char smem[FwdSmem<S, U, WPB, NBUF>::BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[FwdSmem<S, U, WPB, NBUF, GEOM>::BYTES];
   const int i = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
@@ -758,7 +802,7 @@ __global__ void __launch_bounds__(WPB * 64)
       if (b < trips) {
 #pragma unroll
         for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, b, r, last, lane);
-        stage_recv<S, U>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
+        stage_recv<S, U, GEOM>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
       }
     }
 #pragma unroll
@@ -769,12 +813,12 @@ __global__ void __launch_bounds__(WPB * 64)
       int ahead = trips - 1 - k;
       if (ahead >= NBUF - 1) {
         ahead = NBUF - 1;
-        stage_recv<S, U>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, x, Y, w, jn,
-                         q0 + (NBUF - 1) * SLOTS, last, lane);
+        stage_recv<S, U, GEOM>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, x, Y, w, jn,
+                               q0 + (NBUF - 1) * SLOTS, last, lane);
       }
       wait_steps<NBUF, 1, T::NLOADS, 0>(ahead, 0);
-      float xr[M::CPL][S::XC], yr[S::YC], wr[M::CPL][S::NP];
-      read_recv<S, U>(cur, slot, uu, xr, yr, wr);
+      float xr[M::CPL][S::XC], yr[S::YC], wr[M::CPL][S::NP], geo[4];
+      read_recv<S, U, GEOM>(cur, slot, uu, xr, yr, wr, geo);
       __builtin_amdgcn_sched_barrier(0);
       // senders of the next step to stage
 #pragma unroll
@@ -796,16 +840,17 @@ __global__ void __launch_bounds__(WPB * 64)
   block_reduce_store<U, WPB, S::OC, S::NO>(acc, (float*)smem, out + (size_t)i * OD, OutBlocks<S>{});
 }
 
-// MODE bit 0: write grad_w; bit 1: write grad_Y
-template <class S, int U, int WPB, int NBUF, int MODE>
+// MODE bit 0: write grad_w; bit 1: write grad_Y (with GEOM: Y holds the edge
+// vectors r [E][3] and grad_Y receives grad_r [E][3])
+template <class S, int U, int WPB, int NBUF, int MODE, bool GEOM = false>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_bwd_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                     const float* __restrict__ x, const float* __restrict__ Y,
                     const float* __restrict__ w, const float* __restrict__ g,
                     float* __restrict__ grad_w, float* __restrict__ grad_Y) {
   using M = LaneMap<U>;
-  using T = RecvStage<S, U>;
-  using C = Cfg<S, U>;
+  using T = RecvStage<S, U, GEOM>;
+  using C = Cfg<S, U, GEOM>;
   constexpr int OD = U * S::OC, SLOTS = WPB * M::EPW, EPW = M::EPW;
   constexpr int NST = ((MODE & 1) ? C::ST_W : 0) + ((MODE & 2) ? C::ST_Y : 0);
   static_assert((NBUF - 1) * (T::NLOADS + NST) < 64, "pipeline too deep for vmcnt");
@@ -834,7 +879,7 @@ __global__ void __launch_bounds__(WPB * 64)
     if (b < trips) {
 #pragma unroll
       for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, b, r, last, lane);
-      stage_recv<S, U>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
+      stage_recv<S, U, GEOM>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
     }
   }
 #pragma unroll
@@ -842,7 +887,7 @@ __global__ void __launch_bounds__(WPB * 64)
   // Results of step k are stored during step k+1, after its wait, straight
   // from registers; the number of store instructions per step is fixed (NST).
   float pgw[M::CPL][S::NP], pgy[C::ST_Y];
-  const HalvingShare ysh = halving_share(S::YC, M::LPE, lane);   // this lane's grad_Y components
+  const HalvingShare ysh = halving_share(T::YR, M::LPE, lane);   // this lane's grad_Y (grad_r) components
   size_t pq = 0;
   auto flush = [&]() {
     if constexpr (MODE & 1) {
@@ -855,7 +900,7 @@ __global__ void __launch_bounds__(WPB * 64)
     if constexpr (MODE & 2) {
 #pragma unroll
       for (int r = 0; r < C::ST_Y; ++r)
-        if (r < ysh.len) __builtin_nontemporal_store(pgy[r], grad_Y + pq * S::YC + ysh.first + r);
+        if (r < ysh.len) __builtin_nontemporal_store(pgy[r], grad_Y + pq * T::YR + ysh.first + r);
     }
   };
   for (int k = 0; k < trips; ++k) {
@@ -864,15 +909,15 @@ __global__ void __launch_bounds__(WPB * 64)
     int ahead = trips - 1 - k;
     if (ahead >= NBUF - 1) {
       ahead = NBUF - 1;
-      stage_recv<S, U>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, x, Y, w, jn,
-                       q0 + (NBUF - 1) * SLOTS, last, lane);
+      stage_recv<S, U, GEOM>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, x, Y, w, jn,
+                             q0 + (NBUF - 1) * SLOTS, last, lane);
     }
     // store groups issued after this step's loads: steps max(1, k-NBUF+1) .. k-1
     const int sg = k - 1 < NBUF - 1 ? (k - 1 > 0 ? k - 1 : 0) : NBUF - 1;
     wait_steps<NBUF, NBUF, T::NLOADS, NST>(ahead, sg);
     if (k > 0) flush();
-    float xr[M::CPL][S::XC], yr[S::YC], wr[M::CPL][S::NP];
-    read_recv<S, U>(cur, slot, uu, xr, yr, wr);
+    float xr[M::CPL][S::XC], yr[S::YC], wr[M::CPL][S::NP], geo[4];
+    read_recv<S, U, GEOM>(cur, slot, uu, xr, yr, wr, geo);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, k + NBUF, r, last, lane);
@@ -881,36 +926,33 @@ __global__ void __launch_bounds__(WPB * 64)
     for (int b = 0; b < S::YC; ++b) gy[b] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_recv<S>(xr[cc], yr, wr[cc], gr[cc], pgw[cc], gy);
-    if constexpr (MODE & 2) {
-      // sum over the edge's channel lanes (partners stay inside the slot);
-      // the lane then holds components ysh.first .. ysh.first + ysh.len - 1
-      lane_sum_halving<S::YC, M::LPE / 2>(gy, lane);
-#pragma unroll
-      for (int r = 0; r < C::ST_Y; ++r) pgy[r] = gy[r];
-    }
+    // sum over the edge's channel lanes (partners stay inside the slot); the
+    // lane then holds components ysh.first .. ysh.first + ysh.len - 1
+    if constexpr (MODE & 2) edge_grad_share<S, GEOM, M::LPE>(gy, geo, lane, pgy);
     pq = (size_t)min(q0 + slot, last);
   }
   flush();
 }
 
-template <class S, int U, int WPB, int NBUF>
+template <class S, int U, int WPB, int NBUF, bool GEOM = false>
 struct SendSmem {
-  static constexpr int STAGE = NBUF * WPB * SendStage<S, U>::BUF;
+  static constexpr int STAGE = NBUF * WPB * SendStage<S, U, GEOM>::BUF;
   static constexpr int RED = WPB * LaneMap<U>::CPL * S::XC * 65 * 4;
   static constexpr int BYTES = STAGE > RED ? STAGE : RED;
 };
 
-template <class S, int U, int WPB, int NBUF>
+// GEOM: Y holds the edge vectors r [E][3] and the harmonics are evaluated on chip
+template <class S, int U, int WPB, int NBUF, bool GEOM = false>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_bwd_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                     const int32_t* __restrict__ t_col, const float* __restrict__ Y,
                     const float* __restrict__ w, const float* __restrict__ g,
                     float* __restrict__ grad_x) {
   using M = LaneMap<U>;
-  using T = SendStage<S, U>;
+  using T = SendStage<S, U, GEOM>;
   constexpr int XD = U * S::XC, SLOTS = WPB * M::EPW, EPW = M::EPW;
   static_assert((NBUF - 1) * T::NLOADS < 64, "pipeline too deep for vmcnt");
-  __shared__ __attribute__((aligned(16))) char smem[SendSmem<S, U, WPB, NBUF>::BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[SendSmem<S, U, WPB, NBUF, GEOM>::BYTES];
   const int j = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
@@ -937,7 +979,7 @@ __global__ void __launch_bounds__(WPB * 64)
           qn[r] = wq.get(t_perm, k00, b, r, last, lane);
           in[r] = wi.get(t_col, k00, b, r, last, lane);
         }
-        stage_send<S, U>(mybuf + b * T::BUF, Y, w, g, qn, in, lane);
+        stage_send<S, U, GEOM>(mybuf + b * T::BUF, Y, w, g, qn, in, lane);
       }
     }
 #pragma unroll
@@ -951,15 +993,14 @@ __global__ void __launch_bounds__(WPB * 64)
       int ahead = trips - 1 - k;
       if (ahead >= NBUF - 1) {
         ahead = NBUF - 1;
-        stage_send<S, U>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, Y, w, g, qn, in, lane);
+        stage_send<S, U, GEOM>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, Y, w, g, qn, in, lane);
       }
       wait_steps<NBUF, 1, T::NLOADS, 0>(ahead, 0);
       const float* W = (const float*)(cur + T::W_OFF) + slot * (S::NP * U);
-      const float* Yv = (const float*)(cur + T::Y_OFF) + slot * S::YC;
+      const float* Yv = (const float*)(cur + T::Y_OFF) + slot * T::YR;
       const float* G = (const float*)(cur + T::G_OFF) + slot * (S::OC * U);
-      float yr[S::YC], wr[M::CPL][S::NP], gr[M::CPL][S::OC];
-#pragma unroll
-      for (int b = 0; b < S::YC; ++b) yr[b] = Yv[b];
+      float yr[S::YC], wr[M::CPL][S::NP], gr[M::CPL][S::OC], geo[4];
+      read_y<S, GEOM>(Yv, yr, geo);
 #pragma unroll
       for (int cc = 0; cc < M::CPL; ++cc) {
 #pragma unroll
@@ -1011,10 +1052,10 @@ __global__ void __launch_bounds__(WPB * 64)
 // operands, same lane arithmetic), and its grad_x share is masked.
 // Results of step k are stored during step k+1, after its wait.
 // MODE bit 0: write grad_w; bit 1: write grad_Y.
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 struct FusedCfg {
-  using Sd = SendStage<S, U>;
-  using C = Cfg<S, U>;
+  using Sd = SendStage<S, U, GEOM>;
+  using C = Cfg<S, U, GEOM>;
   // four waves per sender, two staging buffers each (about 70 KB per
   // workgroup at 32 channels: two workgroups share a compute unit's 160 KB);
   // measured on the 1,536-atom graph against 1 to 4 waves and 1 to 3 buffers,
@@ -1024,16 +1065,17 @@ struct FusedCfg {
   static constexpr int WPB = (4 * NBUF * Sd::BUF <= 80 * 1024) ? 4 : (2 * NBUF * Sd::BUF <= 80 * 1024 ? 2 : 1);
 };
 
-template <class S, int U, int WPB, int NBUF>
+template <class S, int U, int WPB, int NBUF, bool GEOM = false>
 struct FusedSmem {
   static constexpr int XB = S::XC * U * 4;                      // the sender's x row, per wave
-  static constexpr int XR_OFF = NBUF * WPB * SendStage<S, U>::BUF;
+  static constexpr int XR_OFF = NBUF * WPB * SendStage<S, U, GEOM>::BUF;
   static constexpr int STAGE = XR_OFF + WPB * ceil16(XB);
   static constexpr int RED = WPB * LaneMap<U>::CPL * S::XC * 65 * 4;
   static constexpr int BYTES = STAGE > RED ? STAGE : RED;
 };
 
-template <class S, int U, int WPB, int NBUF, int MODE>
+// GEOM: Y holds the edge vectors r [E][3] and grad_Y receives grad_r [E][3]
+template <class S, int U, int WPB, int NBUF, int MODE, bool GEOM = false>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_bwd_fused(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                      const int32_t* __restrict__ t_col, const float* __restrict__ x,
@@ -1041,9 +1083,9 @@ __global__ void __launch_bounds__(WPB * 64)
                      const float* __restrict__ g, float* __restrict__ grad_x,
                      float* __restrict__ grad_w, float* __restrict__ grad_Y) {
   using M = LaneMap<U>;
-  using T = SendStage<S, U>;
-  using C = Cfg<S, U>;
-  using SM = FusedSmem<S, U, WPB, NBUF>;
+  using T = SendStage<S, U, GEOM>;
+  using C = Cfg<S, U, GEOM>;
+  using SM = FusedSmem<S, U, WPB, NBUF, GEOM>;
   constexpr int XD = U * S::XC, SLOTS = WPB * M::EPW, EPW = M::EPW;
   constexpr int NST = ((MODE & 1) ? C::ST_W : 0) + ((MODE & 2) ? C::ST_Y : 0);
   static_assert(NBUF >= 1 && NBUF <= 4, "one to four staging buffers");
@@ -1081,7 +1123,7 @@ __global__ void __launch_bounds__(WPB * 64)
         in[r] = wi.get(t_col, k00, b, r, last, lane);
         qh[b][r] = qn[r];
       }
-      if (b < trips) stage_send<S, U>(mybuf + b * T::BUF, Y, w, g, qn, in, lane);
+      if (b < trips) stage_send<S, U, GEOM>(mybuf + b * T::BUF, Y, w, g, qn, in, lane);
     }
 #pragma unroll
     for (int r = 0; r < EPW; ++r) {
@@ -1090,7 +1132,7 @@ __global__ void __launch_bounds__(WPB * 64)
     }
     float xr[M::CPL][S::XC];
     float pgw[M::CPL][S::NP], pgy[C::ST_Y];
-    const HalvingShare ysh = halving_share(S::YC, M::LPE, lane);
+    const HalvingShare ysh = halving_share(T::YR, M::LPE, lane);
     size_t pq = 0;
     auto flush = [&]() {
       if constexpr (MODE & 1) {
@@ -1103,7 +1145,7 @@ __global__ void __launch_bounds__(WPB * 64)
       if constexpr (MODE & 2) {
 #pragma unroll
         for (int r = 0; r < C::ST_Y; ++r)
-          if (r < ysh.len) __builtin_nontemporal_store(pgy[r], grad_Y + pq * S::YC + ysh.first + r);
+          if (r < ysh.len) __builtin_nontemporal_store(pgy[r], grad_Y + pq * T::YR + ysh.first + r);
       }
     };
     for (int k = 0; k < trips; ++k) {
@@ -1114,7 +1156,7 @@ __global__ void __launch_bounds__(WPB * 64)
       int ahead = trips - 1 - k;
       if (ahead >= NBUF - 1) {
         ahead = NBUF - 1;
-        stage_send<S, U>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, Y, w, g, qn, in, lane);
+        stage_send<S, U, GEOM>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, Y, w, g, qn, in, lane);
       }
       // store groups issued after this step's loads: steps max(1, k-NBUF+1) .. k-1
       const int sg = k - 1 < NBUF - 1 ? (k - 1 > 0 ? k - 1 : 0) : NBUF - 1;
@@ -1131,11 +1173,10 @@ __global__ void __launch_bounds__(WPB * 64)
           });
       }
       const float* W = (const float*)(cur + T::W_OFF) + slot * (S::NP * U);
-      const float* Yv = (const float*)(cur + T::Y_OFF) + slot * S::YC;
+      const float* Yv = (const float*)(cur + T::Y_OFF) + slot * T::YR;
       const float* G = (const float*)(cur + T::G_OFF) + slot * (S::OC * U);
-      float yr[S::YC], wr[M::CPL][S::NP], gr[M::CPL][S::OC];
-#pragma unroll
-      for (int b = 0; b < S::YC; ++b) yr[b] = Yv[b];
+      float yr[S::YC], wr[M::CPL][S::NP], gr[M::CPL][S::OC], geo[4];
+      read_y<S, GEOM>(Yv, yr, geo);
 #pragma unroll
       for (int cc = 0; cc < M::CPL; ++cc) {
 #pragma unroll
@@ -1187,11 +1228,7 @@ __global__ void __launch_bounds__(WPB * 64)
 #pragma unroll
         for (int cc = 0; cc < M::CPL; ++cc) edge_bwd_send<S>(yr, wr[cc], gr[cc], gx[cc]);
       }
-      if constexpr (MODE & 2) {
-        lane_sum_halving<S::YC, M::LPE / 2>(gy, lane);
-#pragma unroll
-        for (int r = 0; r < C::ST_Y; ++r) pgy[r] = gy[r];
-      }
+      if constexpr (MODE & 2) edge_grad_share<S, GEOM, M::LPE>(gy, geo, lane, pgy);
       pq = (size_t)q;
     }
     flush();
@@ -1207,65 +1244,96 @@ __global__ void __launch_bounds__(WPB * 64)
 // chip and the forward takes more waves per receiver
 constexpr int kSmallGraph = 1024;
 
-template <class S, int U>
+// GEOM: the edge operand is r (a.r) instead of Y, and the edge gradient grad_r
+// (a.grad_r) instead of grad_Y
+template <bool GEOM>
+const float* edge_geom(const ConvArgs& a) {
+  return GEOM ? a.r : a.Y;
+}
+template <bool GEOM>
+float* edge_geom_grad(const ConvArgs& a) {
+  return GEOM ? a.grad_r : a.grad_Y;
+}
+
+template <class S, int U, bool GEOM = false>
 hipError_t launch_fwd(const ConvArgs& a) {
-  using C = Cfg<S, U>;
+  using C = Cfg<S, U, GEOM>;
   if (a.n_nodes == 0) return hipSuccess;
+  const float* Y = edge_geom<GEOM>(a);
   if constexpr (C::WPB_F != C::WPB_F2) {
     if (a.n_nodes < kSmallGraph) {
-      hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F2, C::NBUF_F2>), dim3(a.n_nodes), dim3(C::WPB_F2 * 64), 0,
-                         a.stream, a.row_ptr, a.col, a.x, a.Y, a.w, a.out);
+      hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F2, C::NBUF_F2, GEOM>), dim3(a.n_nodes), dim3(C::WPB_F2 * 64),
+                         0, a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F, C::NBUF_F>), dim3(a.n_nodes), dim3(C::WPB_F * 64), 0,
-                     a.stream, a.row_ptr, a.col, a.x, a.Y, a.w, a.out);
+  hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F, C::NBUF_F, GEOM>), dim3(a.n_nodes), dim3(C::WPB_F * 64), 0,
+                     a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out);
   return hipGetLastError();
 }
 
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 hipError_t launch_bwd_recv(const ConvArgs& a) {
-  using C = Cfg<S, U>;
-  if (a.n_nodes == 0 || a.n_edges == 0 || (!a.grad_w && !a.grad_Y)) return hipSuccess;
+  using C = Cfg<S, U, GEOM>;
+  const float* Y = edge_geom<GEOM>(a);
+  float* gY = edge_geom_grad<GEOM>(a);
+  if (a.n_nodes == 0 || a.n_edges == 0 || (!a.grad_w && !gY)) return hipSuccess;
   const dim3 grid(a.n_nodes), block(C::WPB_R * 64);
-  if (a.grad_w && a.grad_Y)
-    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 3>), grid, block, 0, a.stream,
-                       a.row_ptr, a.col, a.x, a.Y, a.w, a.grad_out, a.grad_w, a.grad_Y);
+  if (a.grad_w && gY)
+    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 3, GEOM>), grid, block, 0, a.stream,
+                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY);
   else if (a.grad_w)
-    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 1>), grid, block, 0, a.stream,
-                       a.row_ptr, a.col, a.x, a.Y, a.w, a.grad_out, a.grad_w, a.grad_Y);
+    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 1, GEOM>), grid, block, 0, a.stream,
+                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY);
   else
-    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 2>), grid, block, 0, a.stream,
-                       a.row_ptr, a.col, a.x, a.Y, a.w, a.grad_out, a.grad_w, a.grad_Y);
+    hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 2, GEOM>), grid, block, 0, a.stream,
+                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY);
   return hipGetLastError();
 }
 
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 hipError_t launch_bwd_send(const ConvArgs& a) {
-  using C = Cfg<S, U>;
+  using C = Cfg<S, U, GEOM>;
   if (a.n_nodes == 0 || !a.grad_x) return hipSuccess;
-  hipLaunchKernelGGL((k_conv_bwd_send<S, U, C::WPB_S, C::NBUF_S>), dim3(a.n_nodes), dim3(C::WPB_S * 64), 0,
-                     a.stream, a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.w, a.grad_out, a.grad_x);
+  hipLaunchKernelGGL((k_conv_bwd_send<S, U, C::WPB_S, C::NBUF_S, GEOM>), dim3(a.n_nodes), dim3(C::WPB_S * 64),
+                     0, a.stream, a.t_row_ptr, a.t_perm, a.t_col, edge_geom<GEOM>(a), a.w, a.grad_out,
+                     a.grad_x);
   return hipGetLastError();
 }
 
 // whole backward (grad_x with grad_w and/or grad_Y) in one sender-grouped pass
 
-template <class S, int U>
+template <class S, int U, bool GEOM = false>
 hipError_t launch_bwd_fused(const ConvArgs& a) {
-  using F = FusedCfg<S, U>;
+  using F = FusedCfg<S, U, GEOM>;
   if (a.n_nodes == 0) return hipSuccess;
+  const float* Y = edge_geom<GEOM>(a);
+  float* gY = edge_geom_grad<GEOM>(a);
   const dim3 grid(a.n_nodes), block(F::WPB * 64);
-  if (a.grad_w && a.grad_Y)
-    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 3>), grid, block, 0, a.stream, a.t_row_ptr,
-                       a.t_perm, a.t_col, a.x, a.Y, a.w, a.grad_out, a.grad_x, a.grad_w, a.grad_Y);
+  if (a.grad_w && gY)
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 3, GEOM>), grid, block, 0, a.stream, a.t_row_ptr,
+                       a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
   else if (a.grad_w)
-    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 1>), grid, block, 0, a.stream, a.t_row_ptr,
-                       a.t_perm, a.t_col, a.x, a.Y, a.w, a.grad_out, a.grad_x, a.grad_w, a.grad_Y);
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 1, GEOM>), grid, block, 0, a.stream, a.t_row_ptr,
+                       a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
   else
-    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 2>), grid, block, 0, a.stream, a.t_row_ptr,
-                       a.t_perm, a.t_col, a.x, a.Y, a.w, a.grad_out, a.grad_x, a.grad_w, a.grad_Y);
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 2, GEOM>), grid, block, 0, a.stream, a.t_row_ptr,
+                       a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
   return hipGetLastError();
+}
+
+// Backward of the edge-vector form: grad_x, grad_w and grad_r (a.r, a.grad_r),
+// one sender-grouped pass where the signature has it and both kinds of
+// gradient are asked for, else a receiver pass and a sender pass.
+template <class S, int U>
+hipError_t launch_bwd_geom(const ConvArgs& a) {
+  const bool edge = a.grad_w || a.grad_r;
+  if constexpr (!kPhased<S>) {
+    if (a.grad_x && edge && a.n_edges > 0) return launch_bwd_fused<S, U, true>(a);
+  }
+  hipError_t e = launch_bwd_recv<S, U, true>(a);
+  if (e != hipSuccess) return e;
+  return launch_bwd_send<S, U, true>(a);
 }
 
 }  // namespace tpc
@@ -1288,7 +1356,8 @@ constexpr LaunchFn fused_backward() {
 template <class S, int U>
 const KernelSet* kernel_set() {
   static const KernelSet k{&launch_fwd<S, U>,      &launch_bwd_recv<S, U>, &launch_bwd_send<S, U>,
-                           &launch_dbl_recv<S, U>, &launch_dbl_send<S, U>, fused_backward<S, U>()};
+                           &launch_dbl_recv<S, U>, &launch_dbl_send<S, U>, fused_backward<S, U>(),
+                           &launch_fwd<S, U, true>, &launch_bwd_geom<S, U>};
   return &k;
 }
 

@@ -24,6 +24,9 @@ struct ConvArgs {
   // second-order backward: cotangents of (grad_x, grad_Y, grad_w), outputs
   const float *gg_x = nullptr, *gg_Y = nullptr, *gg_w = nullptr;
   float *d_x = nullptr, *d_Y = nullptr, *d_w = nullptr, *d_g = nullptr;
+  // edge-vector form: r [E][3] in place of Y, grad_r [E][3] in place of grad_Y
+  const float* r = nullptr;
+  float* grad_r = nullptr;
   hipStream_t stream = nullptr;
 };
 
@@ -36,6 +39,8 @@ struct KernelSet {
   LaunchFn dbl_recv = nullptr;  // second order, receiver pass: d_grad_out, d_Y, d_w
   LaunchFn dbl_send = nullptr;  // second order, sender pass: d_x
   LaunchFn bwd_fused = nullptr; // sender-grouped pass: grad_x with grad_w and/or grad_Y
+  LaunchFn fwd_r = nullptr;     // forward from edge vectors (harmonics on chip)
+  LaunchFn bwd_r = nullptr;     // backward from edge vectors: grad_x, grad_w, grad_r
 };
 
 // radial-weight variant (edge weights from a radial network of the length)
