@@ -419,6 +419,23 @@ tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const f
  * a channel mix is differentiated too). */
 tp_status tp_conv_radial_workspace(tp_plan_t plan, int32_t n_nodes, int32_t with_mix, size_t* bytes);
 
+/* Edge-vector form of the radial layer: r [E][3] (receiver-sorted) replaces Y
+ * and r_len; each edge's harmonics and length |r| are evaluated on chip
+ * (tp_conv_forward_r) for the radial network and the product.  The backward
+ * returns grad_r [E][3], the gradient with respect to the edge vectors through
+ * both the harmonics and the lengths (the forces of the layer), in place of
+ * grad_Y and grad_rlen; neither is stored.  Otherwise as
+ * tp_conv_forward_radial / tp_conv_backward_radial (same workspace, alignment,
+ * outputs that may be NULL, fixed-order parameter sums). */
+tp_status tp_conv_forward_radial_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
+                                   const float* W1, const float* W2, const float* Wmix, float* out_pre,
+                                   float* out, hipStream_t stream);
+tp_status tp_conv_backward_radial_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
+                                    const float* W1, const float* W2, const float* Wmix,
+                                    const float* out_pre, const float* grad_out, float* grad_x,
+                                    float* grad_r, float* grad_W1, float* grad_W2, float* grad_Wmix,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Gradient with respect to the edge vectors r[E][3] of a loss that depends on
  * them through Y = tp_conv_sph_harm(lmax, r) (upstream grad_Y[E][(lmax+1)^2])
  * and, optionally, through the edge lengths |r| (upstream grad_rlen[E], NULL:

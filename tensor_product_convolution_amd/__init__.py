@@ -31,6 +31,7 @@ EXPORTS = (
     "tp_conv_forward_r", "tp_conv_backward_r",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
+    "tp_conv_forward_radial_r", "tp_conv_backward_radial_r",
     "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
     "tp_conv_forward_fc", "tp_conv_fc_backward_workspace", "tp_conv_backward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_backward_gaunt",
     "tp_conv_last_error",
@@ -95,6 +96,9 @@ def lib():
         "tp_conv_backward_radial": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP,
                                           VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
         "tp_conv_sph_harm_backward": (I32, [I32, VP, I32, VP, VP, VP, VP]),
+        "tp_conv_forward_radial_r": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
+        "tp_conv_backward_radial_r": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
+                                            VP, VP, VP, VP, VP, SZ, VP]),
         "tp_conv_fc_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_forward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, SZ, VP]),
         "tp_conv_fc_backward_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
@@ -636,6 +640,74 @@ def backward_radial(plan, graph, x, Y, r_len, W1, W2, grad_out, Wmix=None, out_p
                                          _ptr(gx), _ptr(gY), _ptr(grl), _ptr(gW1), _ptr(gW2),
                                          _ptr(gWm), _ptr(ws), ws.numel(), _stream(x.device)))
     return gx, gY, gW1, gW2, gWm, grl
+
+
+def forward_radial_r(plan, graph, x, r, W1, W2, Wmix=None, out=None, out_pre=None):
+    """forward_radial from the edge vectors r [E, 3] (receiver-sorted): harmonics
+    and lengths evaluated on chip."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    nb, nh, _ = plan.radial
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(r, "r", torch.float32, (E, 3))
+    _need(W1, "W1", torch.float32, (nb, nh))
+    _need(W2, "W2", torch.float32, (nh, plan.n_paths * plan.mul))
+    f32 = dict(dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((N, plan.outdim), **f32)
+    if Wmix is not None and out_pre is None:
+        out_pre = torch.empty((N, plan.outdim), **f32)
+    g = graph.cstruct()
+    _check(lib().tp_conv_forward_radial_r(plan.handle, ctypes.byref(g), _ptr(x), _ptr(r), _ptr(W1),
+                                          _ptr(W2), _ptr(Wmix),
+                                          _ptr(out_pre) if Wmix is not None else None, _ptr(out),
+                                          _stream(x.device)))
+    return out, (out_pre if Wmix is not None else None)
+
+
+def backward_radial_r(plan, graph, x, r, W1, W2, grad_out, Wmix=None, out_pre=None,
+                      want=("x", "r", "W1", "W2", "Wmix"), outs=None, ws=None):
+    """(grad_x, grad_r, grad_W1, grad_W2, grad_Wmix) of forward_radial_r; grad_r [E, 3]
+    (receiver-sorted) is the gradient with respect to the edge vectors through the
+    harmonics and the lengths.  Entries not in ``want`` and grad_Wmix without a mix
+    are None."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    nb, nh, _ = plan.radial
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(r, "r", torch.float32, (E, 3))
+    _need(W1, "W1", torch.float32, (nb, nh))
+    _need(W2, "W2", torch.float32, (nh, plan.n_paths * plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    if Wmix is not None:
+        K = len(plan.out_irreps.split("+"))
+        _need(Wmix, "Wmix", torch.float32, (K, plan.mul, plan.mul))
+        if "Wmix" in want:
+            _need(out_pre, "out_pre", torch.float32, (N, plan.outdim))
+    outs = outs or {}
+
+    def buf(name, like):
+        if name not in want or like is None:
+            return None
+        t = outs.get(name)
+        if t is None:
+            return torch.empty_like(like)
+        _need(t, "grad_" + name, torch.float32, tuple(like.shape))
+        return t
+    gx, gr, gW1, gW2 = buf("x", x), buf("r", r), buf("W1", W1), buf("W2", W2)
+    gWm = buf("Wmix", Wmix)
+    nbytes = radial_workspace(plan, N, Wmix is not None)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    elif ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
+    g = graph.cstruct()
+    _check(lib().tp_conv_backward_radial_r(plan.handle, ctypes.byref(g), _ptr(x), _ptr(r), _ptr(W1),
+                                           _ptr(W2), _ptr(Wmix),
+                                           _ptr(out_pre) if gWm is not None else None, _ptr(grad_out),
+                                           _ptr(gx), _ptr(gr), _ptr(gW1), _ptr(gW2), _ptr(gWm), _ptr(ws),
+                                           ws.numel(), _stream(x.device)))
+    return gx, gr, gW1, gW2, gWm
 
 
 def radial_workspace(plan, n_nodes, with_mix):

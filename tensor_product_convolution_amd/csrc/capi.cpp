@@ -838,18 +838,18 @@ tp_status tp_conv_uvw_backward(tp_plan_t plan, int32_t n_nodes, const float* Wmi
   return TP_OK;
 }
 
-tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
-                                 const float* Y, const float* r_len, const float* W1,
-                                 const float* W2, const float* Wmix, float* out_pre, float* out,
-                                 hipStream_t stream) {
+// geom: Y holds the edge vectors r [E][3] and r_len is unused
+static tp_status forward_radial_impl(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                     const float* r_len, const float* W1, const float* W2, const float* Wmix,
+                                     float* out_pre, float* out, hipStream_t stream, bool geom) {
   if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward_radial: plan is NULL");
   if (!plan->rs) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
   tp_status s = check_graph(graph, false);
   if (s != TP_OK) return s;
   const int N = graph->n_nodes, E = graph->n_edges;
   if (N > 0 && (!x || !out)) return set_error(TP_ERR_ARG, "tp_conv_forward_radial: x/out NULL");
-  if (E > 0 && (!Y || !r_len || !W1 || !W2))
-    return set_error(TP_ERR_ARG, "tp_conv_forward_radial: Y/r_len/W1/W2 NULL");
+  if (E > 0 && (!Y || (!geom && !r_len) || !W1 || !W2))
+    return set_error(TP_ERR_ARG, "tp_conv_forward_radial: Y (r) / r_len / W1 / W2 NULL");
   if (Wmix && N > 0 && (!out_pre || out_pre == out))
     return set_error(TP_ERR_ARG, "tp_conv_forward_radial: a mix needs a separate out_pre buffer");
   tpc::RadialArgs a;
@@ -864,6 +864,7 @@ tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const fl
   a.W2 = W2;
   a.r_cut = plan->opts.r_cut;
   a.out = Wmix ? out_pre : out;
+  a.geom = geom;
   a.stream = stream;
   hipError_t e = plan->rs->fwd(a);
   if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_forward_radial launch");
@@ -873,6 +874,19 @@ tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const fl
     return tpc::uvw_forward(N, plan->mul, plan->outdim, plan->uvw, Wmix, out_pre, out, false, stream);
   }
   return TP_OK;
+}
+
+tp_status tp_conv_forward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                 const float* Y, const float* r_len, const float* W1,
+                                 const float* W2, const float* Wmix, float* out_pre, float* out,
+                                 hipStream_t stream) {
+  return forward_radial_impl(plan, graph, x, Y, r_len, W1, W2, Wmix, out_pre, out, stream, false);
+}
+
+tp_status tp_conv_forward_radial_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
+                                   const float* W1, const float* W2, const float* Wmix, float* out_pre,
+                                   float* out, hipStream_t stream) {
+  return forward_radial_impl(plan, graph, x, r, nullptr, W1, W2, Wmix, out_pre, out, stream, true);
 }
 
 static size_t align_up(size_t b) { return (b + 255) & ~size_t(255); }
@@ -893,12 +907,14 @@ tp_status tp_conv_radial_workspace(tp_plan_t plan, int32_t n_nodes, int32_t with
   return TP_OK;
 }
 
-tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
-                                  const float* Y, const float* r_len, const float* W1,
-                                  const float* W2, const float* Wmix, const float* out_pre,
-                                  const float* grad_out, float* grad_x, float* grad_Y,
-                                  float* grad_rlen, float* grad_W1, float* grad_W2,
-                                  float* grad_Wmix, void* ws, size_t ws_bytes, hipStream_t stream) {
+// geom: Y holds the edge vectors r [E][3] (r_len unused) and grad_Y receives
+// grad_r [E][3] (grad_rlen unused)
+static tp_status backward_radial_impl(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                      const float* r_len, const float* W1, const float* W2,
+                                      const float* Wmix, const float* out_pre, const float* grad_out,
+                                      float* grad_x, float* grad_Y, float* grad_rlen, float* grad_W1,
+                                      float* grad_W2, float* grad_Wmix, void* ws, size_t ws_bytes,
+                                      hipStream_t stream, bool geom) {
   if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: plan is NULL");
   if (!plan->rs || !plan->rs->bwd) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
   tp_status s = check_graph(graph, grad_x != nullptr);
@@ -906,7 +922,8 @@ tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const f
   const int N = graph->n_nodes, E = graph->n_edges;
   if (N > 0 && !grad_out) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: grad_out NULL");
   if (!W1 || !W2) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: W1/W2 NULL");
-  if (E > 0 && (!x || !Y || !r_len)) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: x/Y/r_len NULL");
+  if (E > 0 && (!x || !Y || (!geom && !r_len)))
+    return set_error(TP_ERR_ARG, "tp_conv_backward_radial: x / Y (r) / r_len NULL");
   if (grad_Wmix && !Wmix) return set_error(TP_ERR_ARG, "tp_conv_backward_radial: grad_Wmix without Wmix");
   if (Wmix && grad_Wmix && N > 0 && !out_pre)
     return set_error(TP_ERR_ARG, "tp_conv_backward_radial: grad_Wmix needs out_pre");
@@ -953,11 +970,31 @@ tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const f
   a.grad_W1 = grad_W1;
   a.grad_W2 = grad_W2;
   a.r_cut = plan->opts.r_cut;
+  a.geom = geom;
   a.ws = w;
   a.stream = stream;
   hipError_t e = plan->rs->bwd(a);
   if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_backward_radial launch");
   return TP_OK;
+}
+
+tp_status tp_conv_backward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                  const float* Y, const float* r_len, const float* W1,
+                                  const float* W2, const float* Wmix, const float* out_pre,
+                                  const float* grad_out, float* grad_x, float* grad_Y,
+                                  float* grad_rlen, float* grad_W1, float* grad_W2,
+                                  float* grad_Wmix, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return backward_radial_impl(plan, graph, x, Y, r_len, W1, W2, Wmix, out_pre, grad_out, grad_x, grad_Y,
+                              grad_rlen, grad_W1, grad_W2, grad_Wmix, ws, ws_bytes, stream, false);
+}
+
+tp_status tp_conv_backward_radial_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
+                                    const float* W1, const float* W2, const float* Wmix,
+                                    const float* out_pre, const float* grad_out, float* grad_x,
+                                    float* grad_r, float* grad_W1, float* grad_W2, float* grad_Wmix,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  return backward_radial_impl(plan, graph, x, r, nullptr, W1, W2, Wmix, out_pre, grad_out, grad_x, grad_r,
+                              nullptr, grad_W1, grad_W2, grad_Wmix, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

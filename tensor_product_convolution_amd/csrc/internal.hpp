@@ -53,6 +53,9 @@ struct RadialArgs {
   float *out = nullptr, *grad_x = nullptr, *grad_Y = nullptr, *grad_W1 = nullptr, *grad_W2 = nullptr;
   float* grad_rlen = nullptr;        // gradient w.r.t. the edge lengths (through the basis)
   float r_cut = 0.f;
+  // edge-vector form: Y holds r [E][3] (r_len unused), grad_Y receives grad_r
+  // [E][3] (grad_rlen unused)
+  bool geom = false;
   void* ws = nullptr;
   hipStream_t stream = nullptr;
 };

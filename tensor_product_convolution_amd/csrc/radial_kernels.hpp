@@ -21,6 +21,31 @@
 
 namespace tpc {
 
+// An edge's harmonics and length: read from Y [E][(lmax+1)^2] and r_len [E],
+// or, with GEOM, evaluated from the edge vector r [E][3] (passed as Y).
+template <class S, bool GEOM>
+__device__ __forceinline__ void radial_edge_y(const float* __restrict__ Y, size_t e, float (&yr)[S::YC]) {
+  if constexpr (GEOM) {
+    float x = Y[3 * e], y = Y[3 * e + 1], z = Y[3 * e + 2], inv;
+    unit_dir(x, y, z, inv);
+    sh_eval<S::lmax_sh>(x, y, z, yr);
+  } else {
+#pragma unroll
+    for (int t = 0; t < S::YC; ++t) yr[t] = Y[e * S::YC + t];
+  }
+}
+template <bool GEOM>
+__device__ __forceinline__ float radial_edge_len(const float* __restrict__ Y, const float* __restrict__ r_len,
+                                                 size_t e) {
+  if constexpr (GEOM) {
+    float x = Y[3 * e], y = Y[3 * e + 1], z = Y[3 * e + 2], inv;
+    return unit_dir(x, y, z, inv);
+  } else {
+    return r_len[e];
+  }
+}
+
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
@@ -209,7 +234,9 @@ __device__ __forceinline__ void stage_g(float* gs, const float* __restrict__ g, 
 // chunks: grad_Y is summed over the edge's channel lanes and stored, and
 // grad_W1 = B^T (grad_h * SiLU') is reduced through LDS into one partial per
 // wave (part[wave][n][hid]), summed later in a fixed order.
-template <class S, int U, int NB, int NH, int NW>
+// GEOM: Y holds the edge vectors r [E][3] (r_len unused) and grad_Y receives
+// grad_r [E][3] = the pullback of grad_Y and grad_rlen to r (grad_rlen unused)
+template <class S, int U, int NB, int NH, int NW, bool GEOM = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
     k_radial_bwd_recv(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                       const float* __restrict__ x, const float* __restrict__ Y,
@@ -250,14 +277,15 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     const int qc = has ? (q < end ? q : end - 1) : 0;
     const int j = has ? col[qc] : 0;
     float hB[NH / 4], yr[S::YC], gy[S::YC];
-    const float rl = has ? r_len[qc] : 1.f;
+    const float rl = has ? radial_edge_len<GEOM>(Y, r_len, qc) : 1.f;
     {
       float bq0[NB / 4], ds0[NH / 4];               // recomputed after the chunks
       hidden_T<NB, NH>(rl, valid, rp, w1a, g, bq0, hB, ds0);
     }
+    radial_edge_y<S, GEOM>(Y, qc, yr);              // qc is a valid edge even without a receiver
 #pragma unroll
     for (int t = 0; t < S::YC; ++t) {
-      yr[t] = has ? Y[(size_t)qc * S::YC + t] : 0.f;
+      yr[t] = has ? yr[t] : 0.f;
       gy[t] = 0.f;
     }
     f32x4 gh[NH / 16];
@@ -335,7 +363,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
       gy[t] += __shfl_xor(gy[t], 16, 64);
       gy[t] += __shfl_xor(gy[t], 32, 64);
     }
-    if (grad_Y && g == 0 && valid) {
+    if (!GEOM && grad_Y && g == 0 && valid) {
 #pragma unroll
       for (int t = 0; t < S::YC; ++t) grad_Y[(size_t)q * S::YC + t] = gy[t];
     }
@@ -353,7 +381,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     float gp[NH / 4];
 #pragma unroll
     for (int k = 0; k < NH / 4; ++k) gp[k] = gh[k >> 2][k & 3] * ds[k];
-    if (grad_rlen && has) {
+    if ((GEOM ? grad_Y != nullptr : grad_rlen != nullptr) && has) {
       // grad_B[n][edge] = sum_h W1[n][h] grad_pre[h][edge] on the MFMA (rows
       // n >= NB zero); lane l gets n = 4(l/16) + i of edge l%16, then
       // grad_rlen = sum_n grad_B[n] dB_n/dr, summed over the lane groups
@@ -373,7 +401,19 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
       }
       acc += __shfl_xor(acc, 16, 64);
       acc += __shfl_xor(acc, 32, 64);
-      if (g == 0 && valid) grad_rlen[q] = acc;
+      if constexpr (GEOM) {
+        // grad_r = pullback of (grad_Y, grad_rlen) to the edge vector
+        if (g == 0 && valid) {
+          float ux = Y[3 * (size_t)q], uy = Y[3 * (size_t)q + 1], uz = Y[3 * (size_t)q + 2], inv, o[3];
+          unit_dir(ux, uy, uz, inv);
+          sh_pullback<S::lmax_sh>(ux, uy, uz, inv, gy, acc, o);
+          grad_Y[3 * (size_t)q + 0] = o[0];
+          grad_Y[3 * (size_t)q + 1] = o[1];
+          grad_Y[3 * (size_t)q + 2] = o[2];
+        }
+      } else {
+        if (g == 0 && valid) grad_rlen[q] = acc;
+      }
     }
     // grad_W1[n][hid] += sum over the tile's edges of B_n * grad_pre[hid]
     __syncthreads();                                // W2 slice no longer read
@@ -420,7 +460,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
 // needed here, so each wave computes only its own 16 hidden units.  The
 // accumulators (one 16x16 tile per path) stay in registers; one partial per
 // workgroup is written and summed later in a fixed order.
-template <class S, int U, int NB, int NH>
+// GEOM: Y holds the edge vectors r [E][3]; r_len unused
+template <class S, int U, int NB, int NH, bool GEOM = false>
 __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_per_eu(2)))
     k_radial_bwd_w2(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                     const float* __restrict__ x, const float* __restrict__ Y,
@@ -464,7 +505,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
     if (i < n_nodes) {
       if (g == 0) {
         const int q = t0 + e16;
-        s_r[wv * 16 + e16] = q < end ? r_len[q] : -1.f;
+        s_r[wv * 16 + e16] = q < end ? radial_edge_len<GEOM>(Y, r_len, q) : -1.f;
       }
       float gr[S::OC];
       load_o_channel<S, U>(gout, i, u, gr);
@@ -475,8 +516,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
         const int qc = q < end ? q : end - 1;       // its hidden values are zero
         float xr[S::XC], yr[S::YC];
         load_x_channel<S, U>(x, col[qc], u, xr);
-#pragma unroll
-        for (int t = 0; t < S::YC; ++t) yr[t] = Y[(size_t)qc * S::YC + t];
+        radial_edge_y<S, GEOM>(Y, qc, yr);
         static_for<S::NP>([&](auto P) {
           constexpr PathInfo pi = S::paths.p[P];
           using T = CgPath<pi.l1, pi.l2, pi.l3>;
@@ -557,7 +597,8 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
 // grouped by receiver, x of each sender gathered).  Sender pass: grad_x[j] of
 // sender j (edges grouped by sender through t_perm, grad_out of each receiver
 // gathered).  Each output row chunk is written once; no atomics.
-template <class S, int U, int NB, int NH, int NW, bool SEND>
+// GEOM: Y holds the edge vectors r [E][3]; r_len unused
+template <class S, int U, int NB, int NH, int NW, bool SEND, bool GEOM = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
     k_radial_node(int n_nodes, const int32_t* __restrict__ ptr, const int32_t* __restrict__ perm,
                   const int32_t* __restrict__ other, const float* __restrict__ feat,
@@ -591,8 +632,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
         const int q = t0 + 4 * g + r;
         const int qc = q < end ? q : end - 1;       // weights of a padded edge are zero
         const int e = SEND ? perm[qc] : qc;
-#pragma unroll
-        for (int b = 0; b < S::YC; ++b) yr[r][b] = Y[(size_t)e * S::YC + b];
+        radial_edge_y<S, GEOM>(Y, e, yr[r]);
         if constexpr (SEND) load_o_channel<S, U>(feat, other[qc], u, fr[r]);
         else load_x_channel<S, U>(feat, other[qc], u, fr[r]);
       }
@@ -601,7 +641,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
       const bool va = qa < end;
       const int qac = va ? qa : end - 1;
       float bq[NB / 4], hB[NH / 4], ds[NH / 4];
-      hidden_T<NB, NH>(r_len[SEND ? perm[qac] : qac], va, rp, w1a, g, bq, hB, ds);
+      hidden_T<NB, NH>(radial_edge_len<GEOM>(Y, r_len, SEND ? perm[qac] : qac), va, rp, w1a, g, bq, hB, ds);
       f32x4 C[S::NP];
 #pragma unroll
       for (int p = 0; p < S::NP; ++p) {

@@ -66,14 +66,19 @@ dim3 node_grid(int n_nodes) {
   return dim3(want < cap ? (want > 0 ? want : 1) : cap, U / 16);
 }
 
-template <int U>
-static hipError_t launch_radial_fwd(const RadialArgs& a) {
+// a.geom: a.Y holds the edge vectors r [E][3] and a.grad_Y receives grad_r
+template <int U, bool GEOM>
+static hipError_t launch_radial_fwd_as(const RadialArgs& a) {
   if (a.n_nodes == 0) return hipSuccess;
   RadialParams rp{a.r_cut, a.W1, a.W2};
-  hipLaunchKernelGGL((k_radial_node<SigR, U, kNB, kNH, kNodeWaves, false>), node_grid<U>(a.n_nodes),
+  hipLaunchKernelGGL((k_radial_node<SigR, U, kNB, kNH, kNodeWaves, false, GEOM>), node_grid<U>(a.n_nodes),
                      dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.row_ptr, nullptr, a.col, a.x, a.Y,
                      a.r_len, rp, a.out);
   return hipGetLastError();
+}
+template <int U>
+static hipError_t launch_radial_fwd(const RadialArgs& a) {
+  return a.geom ? launch_radial_fwd_as<U, true>(a) : launch_radial_fwd_as<U, false>(a);
 }
 
 template <int U>
@@ -84,15 +89,15 @@ static size_t radial_bwd_ws(int n_nodes, int /*n_edges*/) {
 
 // grad_Y and grad_W1 (receiver pass), grad_W2, grad_x (sender pass); a.ws holds
 // radial_bwd_ws bytes.  grad_W1/grad_W2/grad_x may be null (skipped).
-template <int U>
-static hipError_t launch_radial_bwd(const RadialArgs& a) {
+template <int U, bool GEOM>
+static hipError_t launch_radial_bwd_as(const RadialArgs& a) {
   RadialParams rp{a.r_cut, a.W1, a.W2};
   const int nb1 = recv_parts(a.n_nodes), nb2 = w2_blocks<U>(a.n_nodes);
   float* part1 = static_cast<float*>(a.ws);
   float* part2 = reinterpret_cast<float*>(static_cast<char*>(a.ws) +
                                           align256((size_t)nb1 * kNB * kNH * sizeof(float)));
   if (a.grad_Y || a.grad_W1 || a.grad_rlen) {
-    hipLaunchKernelGGL((k_radial_bwd_recv<SigR, U, kNB, kNH, kRecvWaves>), dim3(recv_blocks(a.n_nodes)),
+    hipLaunchKernelGGL((k_radial_bwd_recv<SigR, U, kNB, kNH, kRecvWaves, GEOM>), dim3(recv_blocks(a.n_nodes)),
                        dim3(64 * kRecvWaves), 0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len,
                        rp, a.grad_out, a.grad_Y, a.grad_rlen, part1);
     if (a.grad_W1) {
@@ -102,17 +107,22 @@ static hipError_t launch_radial_bwd(const RadialArgs& a) {
     }
   }
   if (a.grad_W2) {
-    hipLaunchKernelGGL((k_radial_bwd_w2<SigR, U, kNB, kNH>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)), 0,
+    hipLaunchKernelGGL((k_radial_bwd_w2<SigR, U, kNB, kNH, GEOM>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)), 0,
                        a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.grad_out, part2);
     const long long n = (long long)kNH * SigR::NP * U;
     hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, a.stream,
                        part2, nb2, n, a.grad_W2);
   }
   if (a.grad_x && a.n_nodes > 0)
-    hipLaunchKernelGGL((k_radial_node<SigR, U, kNB, kNH, kNodeWaves, true>), node_grid<U>(a.n_nodes),
+    hipLaunchKernelGGL((k_radial_node<SigR, U, kNB, kNH, kNodeWaves, true, GEOM>), node_grid<U>(a.n_nodes),
                        dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.t_row_ptr, a.t_perm, a.t_col,
                        a.grad_out, a.Y, a.r_len, rp, a.grad_x);
   return hipGetLastError();
+}
+
+template <int U>
+static hipError_t launch_radial_bwd(const RadialArgs& a) {
+  return a.geom ? launch_radial_bwd_as<U, true>(a) : launch_radial_bwd_as<U, false>(a);
 }
 
 template <int U>

@@ -154,3 +154,71 @@ def test_geom_zero_vectors_and_empty_graph(tpc):
     torch.cuda.synchronize()
     assert float(out.abs().max()) == 0.0 and float(gx.abs().max()) == 0.0
     assert gr.shape == (0, 3) and gw.shape[0] == 0
+
+
+# ---------------------------------------------------------------------------
+# the streaming radial layer from edge vectors
+
+
+def _radial_geom(tpc, plan, wl, mix, g2, with_y_form=False):
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    r = tpc.gather_rows(T(wl.r), g.perm)
+    x, W1, W2 = T(wl.x), T(wl.W1), T(wl.W2)
+    Wm = T(wl.Wmix) if mix else None
+    out, pre = tpc.forward_radial_r(plan, g, x, r, W1, W2, Wm)
+    gx, gr, gW1, gW2, gWm = tpc.backward_radial_r(plan, g, x, r, W1, W2, T(g2), Wmix=Wm, out_pre=pre)
+    res = dict(out=out, pre=pre, gx=gx, gr=gr, gW1=gW1, gW2=gW2, gWm=gWm)
+    if with_y_form:
+        Y = tpc.sph_harm(2, r)
+        rl = tpc.gather_rows(T(wl.r_len), g.perm)
+        o, p = tpc.forward_radial(plan, g, x, Y, rl, W1, W2, Wm)
+        b = tpc.backward_radial(plan, g, x, Y, rl, W1, W2, T(g2), Wmix=Wm, out_pre=p,
+                                want=("x", "Y", "W1", "W2", "Wmix", "rlen"))
+        res.update(out_y=o, gx_y=b[0], gW1_y=b[2], gW2_y=b[3], gWm_y=b[4],
+                   gr_y=tpc.sph_harm_backward(2, r, b[1], b[5]))
+    torch.cuda.synchronize()
+    res = {k: (None if v is None else v.cpu().numpy()) for k, v in res.items()}
+    res["perm"] = g.perm.cpu().numpy()[:wl.n_edges]
+    return res
+
+
+@pytest.mark.parametrize("U,name,n,mix", [(16, "stream", 300, True), (128, "stream", 120, True),
+                                          (16, "zipf", 400, False), (128, "lmax3", 100, True)])
+def test_radial_geom_parity(tpc, U, name, n, mix):
+    """forward and backward of the radial layer from r against the oracle: out,
+    grad_x, the parameter gradients and grad_r through the harmonics and the
+    lengths (the oracle's Jacobian of its harmonics and of |r|)"""
+    from tests.test_gpu_radial import RC, _check_params, _forces_ref, _irreps, _radial_inputs
+    say(f"radial edge-vector form U={U} graph={name} n={n} mix={mix}")
+    op, wl = _radial_inputs(U, name, n)
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    res = _radial_geom(tpc, plan, wl, mix, wl.g)
+    Yo = oracle.sh_real(2, wl.r)
+    out = oracle.tp_conv_radial_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Yo, wl.r_len, wl.W1, wl.W2,
+                                    wl.Wmix if mix else None, 8, RC)
+    assert block_err(res["out"], out, out_blocks(op)) <= TOL
+    ref = oracle.tp_conv_radial_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Yo, wl.r_len, wl.W1, wl.W2,
+                                    wl.Wmix if mix else None, wl.g, 8, RC, with_grad_rlen=True)
+    assert block_err(res["gx"], ref[0], in_blocks(op)) <= TOL
+    p = res["perm"]
+    assert _vec_err(res["gr"], _forces_ref(wl.r, ref[1], ref[5])[p]) <= TOL
+    _check_params(op, res, ref, U)
+
+
+def test_radial_geom_full_size_against_y_form(tpc):
+    """The 100,000-atom / 3,000,000-edge layer from r against the Y form (the
+    harmonics and tp_conv_sph_harm_backward of grad_Y and grad_rlen): the same
+    float32 harmonics, lengths from a float32 square root on chip against the
+    given float32 lengths, so the results agree to float32 rounding."""
+    from tests.test_gpu_radial import RC, _irreps
+    say("radial edge-vector form full size")
+    U = 128
+    op = oracle.build_plan(_irreps(U), 2, 2)
+    wl = make_workload("stream", dims_of(op))
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    res = _radial_geom(tpc, plan, wl, True, wl.g, with_y_form=True)
+    assert block_err(res["out"], res["out_y"], out_blocks(op)) <= 1e-5
+    assert block_err(res["gx"], res["gx_y"], in_blocks(op)) <= 1e-5
+    for k in ("gW1", "gW2", "gWm"):
+        assert _vec_err(res[k], res[k + "_y"]) <= 1e-5, k
+    assert _vec_err(res["gr"], res["gr_y"]) <= 1e-5
