@@ -122,6 +122,16 @@ def algorithmic_bytes(N, E, P, U, ysh, xdim, outdim):
     }
 
 
+def algorithmic_bytes_geom(N, E, P, U, xdim, outdim):
+    """The same counts for the edge-vector form: r [E, 3] (12 B) in place of Y,
+    grad_r (12 B) in place of grad_Y."""
+    return {
+        "fwd_r": E * (4 * P * U + 12 + 4) + 4 * N * (xdim + outdim + 1),     # w, r, col; x, out
+        # w, r, t_perm, t_col in, grad_w, grad_r out; x, grad_out, t_row_ptr in, grad_x out
+        "bwd_r": E * (8 * P * U + 24 + 8) + 4 * N * (2 * xdim + outdim + 1),
+    }
+
+
 def step_bytes(ab, fwd_only):
     """Bytes a forward (+ backward) pass must move, each pass touching its arrays
     once: the forward's and the one-pass backward's algorithmic bytes."""
@@ -504,6 +514,11 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
         # second-order backward with all three cotangents (here: the first backward's outputs)
         extras["double_bwd"] = lambda c: tpc.double_backward(plan, g, x, Ys[c], ws[c], go, gx, gYs[c],
                                                              gws[c])
+        # the same step from the edge vectors: harmonics on chip, grad_r in place of grad_Y
+        rs = [r_sorted] + [r_sorted.clone() for _ in range(NC - 1)]
+        grs = [torch.empty_like(r_sorted) for _ in range(NC)]
+        geom = {"fwd_r": lambda c: tpc.forward_r(plan, g, x, rs[c], ws[c], out=out),
+                "bwd_r": lambda c: tpc.backward_r(plan, g, x, rs[c], ws[c], go, outs=(gx, grs[c], gws[c]))}
 
     flush.fill_(1.0)
     # graph grouping, timed separately
@@ -528,6 +543,13 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
     rounds = max(2, args.steps // 5)
     kt = {n: float(timed_kernel(fn, NC, reps, rounds).mean()) for n, fn in kernels.items()}
     extra_ms = {n: float(timed_kernel(fn, NC, reps, rounds).mean()) for n, fn in extras.items()}
+    if not fwd_only:
+        def step_r():
+            tpc.forward_r(plan, g, x, rs[0], ws[0], out=out)
+            tpc.backward_r(plan, g, x, rs[0], ws[0], go, outs=(gx, grs[0], gws[0]))
+        timed_steps_of(step_r, max(args.warmup, 1), True)
+        t_r = timed_steps_of(step_r, args.steps, True)
+        kt_r = {n: float(timed_kernel(fn, NC, reps, rounds).mean()) for n, fn in geom.items()}
 
     step_ms = float(t.mean())
     ab = algorithmic_bytes(N, E, P, U, ysh, plan.xdim, plan.outdim)
@@ -569,6 +591,16 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
         res["forces_ms"] = extra_ms.get("forces")
         res["forces_note"] = ("edge-vector gradient from grad_Y (tp_conv_sph_harm_backward), per "
                               "launch; not part of the step")
+        ab_r = algorithmic_bytes_geom(N, E, P, U, plan.xdim, plan.outdim)
+        ms_r = float(t_r.mean())
+        res["edge_vector_step"] = {
+            "ms_per_step": ms_r, "edges_per_s": E / (ms_r * 1e-3), "kernel_ms": kt_r,
+            "kernel_hbm_frac": {n: ab_r[n] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in kt_r.items()},
+            "step_hbm_frac": (ab_r["fwd_r"] + ab_r["bwd_r"]) / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": ab_r,
+            "note": ("forward and one-pass backward from r [E, 3]: harmonics evaluated per edge on chip, "
+                     "grad_r (the forces' edge term) in place of grad_Y; timed as the step above"),
+        }
     if warm is not None:
         res["warm_edges_per_s"] = E / (float(warm.mean()) * 1e-3)
     if cpu:
@@ -645,6 +677,17 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     reps, rounds = 3, 2
     kt = {n: float(timed_kernel(fn, 1, reps, rounds).mean()) for n, fn in kernels.items()}
     extra_ms = {n: float(timed_kernel(fn, 1, reps, rounds).mean()) for n, fn in extras.items()}
+    # the same step from the edge vectors: harmonics and lengths on chip, grad_r out
+    outs_r = dict(outs, r=grad_r)
+
+    def step_r():
+        tpc.forward_radial_r(plan, g, x, r_sorted, W1, W2, Wm, out=out, out_pre=pre)
+        tpc.backward_radial_r(plan, g, x, r_sorted, W1, W2, go, Wmix=Wm, out_pre=pre,
+                              want=("x", "r", "W1", "W2", "Wmix"), outs=outs_r, ws=ws)
+    timed_steps(step_r, 1, True)
+    t_r = timed_steps(step_r, args.steps, True)
+    kt_r = {"fwd_r": float(timed_kernel(lambda c: tpc.forward_radial_r(plan, g, x, r_sorted, W1, W2, None,
+                                                                       out=pre), 1, reps, rounds).mean())}
     fl = radial_flops(E, P, U, NH)
     mix_flops = 2.0 * N * plan.outdim * U            # one application of the channel mix
     names = ["fwd", "bwd_recv", "bwd_w2", "bwd_send"]
@@ -680,6 +723,14 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
         "forces_note": "receiver pass that also returns the edge-length gradient, and the "
                        "edge-vector gradient kernel; not part of the step",
         "wall_s_timed_region": wall,
+    }
+    ms_r = float(t_r.mean())
+    res["edge_vector_step"] = {
+        "ms_per_step": ms_r, "edges_per_s": E / (ms_r * 1e-3), "kernel_ms": kt_r,
+        "step_mfma_frac": step_flops / (ms_r * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+        "note": ("forward and backward from r [E, 3] with the channel mix: harmonics and lengths "
+                 "evaluated per edge on chip, grad_r (forces' edge term) in place of grad_Y; timed "
+                 "as the step above"),
     }
     res["cpu_baseline"] = cpu_baseline_radial(irreps, lsh, lout, wl, radial) if cpu else None
     return res, step

@@ -41,6 +41,15 @@ def test_algorithmic_bytes_of_the_1536_atom_workload():
     assert round(ab["double_bwd"] / 1e6, 1) == 283.0
 
 
+def test_algorithmic_bytes_of_the_edge_vector_form():
+    # r (12 B) replaces Y (36 B) in, grad_r (12 B) replaces grad_Y (36 B) out
+    ab = bench.algorithmic_bytes_geom(1536, 46080, 15, 32, 288, 544)
+    assert ab["fwd_r"] == 46080 * (4 * 480 + 12 + 4) + 4 * 1536 * (288 + 544 + 1)
+    assert ab["bwd_r"] == 46080 * (8 * 480 + 24 + 8) + 4 * 1536 * (2 * 288 + 544 + 1)
+    y = bench.algorithmic_bytes(1536, 46080, 15, 32, 9, 288, 544)
+    assert y["fwd"] - ab["fwd_r"] == 46080 * 24 and y["bwd"] - ab["bwd_r"] == 46080 * 48
+
+
 def _oracle_counts(irreps, lsh):
     """the same counts taken from the oracle's dense tables (independent of the
     library's plan and of bench.cg_counts)"""
