@@ -39,7 +39,8 @@ from .wigner import wigner_D_real
 from .csr import csr_build
 from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, bessel_basis_deriv, radial_mlp_fwd,
                    radial_mlp_bwd, uvw_mix_fwd, uvw_mix_bwd,
-                   tp_conv_radial_fwd, tp_conv_radial_bwd, tp_conv_double_bwd)
+                   tp_conv_radial_fwd, tp_conv_radial_bwd, tp_conv_double_bwd,
+                   bessel_basis_deriv2, silu_derivs, tp_conv_radial_double_bwd)
 from .fc import fc_conv_fwd, fc_conv_bwd
 from .gaunt import (sphere_quadrature, gaunt_coefficients, gaunt_plan, gaunt_conv_fwd,
                     gaunt_conv_bwd)
@@ -50,7 +51,8 @@ __all__ = [
     "sh_real_vjp", "wigner_D_real", "csr_build", "tp_conv_fwd", "tp_conv_bwd",
     "bessel_basis", "bessel_basis_deriv",
     "radial_mlp_fwd", "radial_mlp_bwd", "uvw_mix_fwd", "uvw_mix_bwd",
-    "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd", "fc_conv_fwd",
+    "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd", "bessel_basis_deriv2",
+    "silu_derivs", "tp_conv_radial_double_bwd", "fc_conv_fwd",
     "fc_conv_bwd", "sphere_quadrature", "gaunt_coefficients", "gaunt_plan", "gaunt_conv_fwd",
     "gaunt_conv_bwd",
 ]

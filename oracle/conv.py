@@ -278,3 +278,101 @@ def tp_conv_radial_bwd(plan, src, dst, n_nodes, x, Y, r_len, W1, W2, Wmix, g2,
     if with_grad_rlen:
         return grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix, grad_rlen
     return grad_x, grad_Y, grad_W1, grad_W2, grad_Wmix
+
+
+# ---------------------------------------------------------------------------
+# Second-order backward of the radial-weight convolution ("Sobek", Abstract:
+# forward, backward and double backward, with the radial projection streamed
+# so that edge weights never exist in memory).
+#
+# Reading: the cotangents are those a loss on forces produces -- on the first
+# backward's node gradient grad_x, its harmonic gradient grad_Y and its length
+# gradient grad_rlen (the edge-vector gradient is built from the last two).
+# Cotangents of the parameter gradients (grad_W1, grad_W2, grad_Wmix) are not
+# taken: training differentiates a loss on forces, never one on parameter
+# gradients.
+# ---------------------------------------------------------------------------
+
+def bessel_basis_deriv2(r_len, n_basis, r_cut):
+    """d^2 B_n / dr^2 = sqrt(2/r_c) (-k^2 sin(kr)/r - 2k cos(kr)/r^2 + 2 sin(kr)/r^3)."""
+    r = np.asarray(r_len, dtype=np.float64).reshape(-1, 1)
+    k = np.arange(1, n_basis + 1, dtype=np.float64).reshape(1, -1) * np.pi / r_cut
+    s, c = np.sin(k * r), np.cos(k * r)
+    return np.sqrt(2.0 / r_cut) * (-k * k * s / r - 2.0 * k * c / r ** 2 + 2.0 * s / r ** 3)
+
+
+def silu_derivs(z):
+    """(SiLU(z), SiLU'(z), SiLU''(z)) with SiLU(z) = z sigma(z):
+    SiLU' = sigma (1 + z (1 - sigma)), SiLU'' = sigma (1 - sigma) (2 + z (1 - 2 sigma))."""
+    z = np.asarray(z, dtype=np.float64)
+    s = _sigmoid(z)
+    return z * s, s * (1.0 + z * (1.0 - s)), s * (1.0 - s) * (2.0 + z * (1.0 - 2.0 * s))
+
+
+def tp_conv_radial_double_bwd(plan, src, dst, n_nodes, x, Y, r_len, W1, W2, Wmix, g2,
+                              n_basis, r_cut, ggx=None, ggY=None, ggr=None):
+    """Gradients of L = <ggx, grad_x> + <ggY, grad_Y> + <ggr, grad_rlen>, the
+    first backward's outputs (``tp_conv_radial_bwd`` with ``with_grad_rlen``),
+    with respect to x, Y, r_len, W1, W2, Wmix and the upstream gradient g2.
+    Missing cotangents (None) are zero.
+
+    With g = mix^T(g2) the unmixed upstream gradient and F(g, x, Y, w) =
+    <g, out(x, Y, w)> (linear in each argument), grad_rlen[e] =
+    <dw_e/dr_e, grad_w_e>, so
+        L = F(g, ggx, Y, w) + F(g, x, ggY, w) + F(g, x, Y, v),
+        v[e] = ggr[e] dw_e/dr_e     (the tangent of the weights along ggr).
+    Hence, with out_dot = out(ggx, Y, w) + out(x, ggY, w) + out(x, Y, v):
+        d_g2 = mix(out_dot), d_Wmix = grad_Wmix of <g2, mix(out_dot)>,
+        dx = gx(ggY, w, g) + gx(Y, v, g),  dY = gY(ggx, w, g) + gY(x, v, g),
+    and the weights' cotangent dw = gw(ggx, Y, g) + gw(x, ggY, g) and the
+    tangent's cotangent dv = gw(x, Y, g) flow back through the network
+    pre = B W1, h = SiLU(pre), w = h W2, a = B' W1, t = SiLU'(pre) a,
+    v = ggr t W2 by the chain rule, which is where SiLU'' and B'' enter.
+    Returns (dx, dY, d_rlen, dW1, dW2, dWmix, d_g2); dWmix is None without a
+    mix."""
+    src, dst, x, Y = _check(plan, src, dst, n_nodes, x, Y)
+    E = len(src)
+    r_len = np.asarray(r_len, dtype=np.float64)
+    W1 = np.asarray(W1, dtype=np.float64)
+    W2 = np.asarray(W2, dtype=np.float64)
+    g2 = np.asarray(g2, dtype=np.float64)
+    z = lambda a, like: np.zeros_like(like) if a is None else np.asarray(a, dtype=np.float64)
+    ggx, ggY, ggr = z(ggx, x), z(ggY, Y), z(ggr, r_len)
+    if Wmix is not None:
+        g, _ = uvw_mix_bwd(plan, np.zeros_like(g2), Wmix, g2)
+    else:
+        g = g2
+    # the network, its derivative in r and the weight tangent
+    B = bessel_basis(r_len, n_basis, r_cut)
+    dB = bessel_basis_deriv(r_len, n_basis, r_cut)
+    d2B = bessel_basis_deriv2(r_len, n_basis, r_cut)
+    pre = B @ W1
+    h, s1, s2 = silu_derivs(pre)
+    a = dB @ W1                                   # d pre / dr
+    t = s1 * a                                    # d h / dr
+    w = (h @ W2).reshape(E, plan.n_paths, plan.U)
+    v = ((ggr[:, None] * t) @ W2).reshape(E, plan.n_paths, plan.U)
+    args = (plan, src, dst, n_nodes)
+    out_dot = (tp_conv_fwd(*args, ggx, Y, w) + tp_conv_fwd(*args, x, ggY, w)
+               + tp_conv_fwd(*args, x, Y, v))
+    if Wmix is not None:
+        d_g2 = uvw_mix_fwd(plan, out_dot, Wmix)
+        _, dWmix = uvw_mix_bwd(plan, out_dot, Wmix, g2)
+    else:
+        d_g2, dWmix = out_dot, None
+    _, gY_a, gw_a = tp_conv_bwd(*args, ggx, Y, w, g)      # x -> ggx
+    gx_b, _, gw_b = tp_conv_bwd(*args, x, ggY, w, g)      # Y -> ggY
+    gx_c, gY_c, gw_c = tp_conv_bwd(*args, x, Y, v, g)     # w -> v
+    dx = gx_b + gx_c
+    dY = gY_a + gY_c
+    dw = (gw_a + gw_b).reshape(E, -1)
+    dv = gw_c.reshape(E, -1)
+    # back through the network
+    dW2 = h.T @ dw + (ggr[:, None] * t).T @ dv
+    dh = dw @ W2.T
+    dt = ggr[:, None] * (dv @ W2.T)
+    dpre = s1 * dh + s2 * a * dt
+    da = s1 * dt
+    dW1 = B.T @ dpre + dB.T @ da
+    d_rlen = np.sum(dB * (dpre @ W1.T), axis=1) + np.sum(d2B * (da @ W1.T), axis=1)
+    return dx, dY, d_rlen, dW1, dW2, dWmix, d_g2

@@ -404,3 +404,121 @@ def test_double_backward_by_differences_and_multilinearity():
     b = oracle.tp_conv_double_bwd(*args, x, Y, w, g, ggx, np.zeros_like(Y), np.zeros_like(w))
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+def test_bessel_second_derivative_against_the_spherical_bessel_equation():
+    # B_n(r) = sqrt(2/r_c) k j0(k r): B_n'' = sqrt(2/r_c) k^3 j0''(k r), and j0
+    # solves x^2 y'' + 2 x y' + x^2 y = 0, so j0'' = -j0 - 2 j0' / x
+    r = np.linspace(0.8, 5.0, 50)
+    d2B = oracle.bessel_basis_deriv2(r, 8, 5.0)
+    for n in range(1, 9):
+        k = n * np.pi / 5.0
+        xx = k * r
+        j0dd = -spherical_jn(0, xx) - 2.0 * spherical_jn(0, xx, derivative=True) / xx
+        want = np.sqrt(2.0 / 5.0) * k ** 3 * j0dd
+        assert np.max(np.abs(d2B[:, n - 1] - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+
+def test_silu_derivatives_against_sympy():
+    import sympy
+    zs = sympy.Symbol("z")
+    f = zs / (1 + sympy.exp(-zs))
+    f1, f2 = sympy.diff(f, zs), sympy.diff(f, zs, 2)
+    pts = np.array([-30.0, -4.5, -1.0, -0.3, 0.0, 0.7, 2.0, 6.0, 25.0])
+    s0, s1, s2 = oracle.silu_derivs(pts)
+    for i, p in enumerate(pts):
+        for got, expr in ((s0[i], f), (s1[i], f1), (s2[i], f2)):
+            want = float(expr.subs(zs, sympy.Float(p, 30)).evalf(30))
+            assert abs(got - want) <= 1e-14 * max(1.0, abs(want))
+
+
+def _radial_small(seed, n_nodes=10):
+    plan = oracle.build_plan("4x0e+4x1o+4x2e", 2, 2)
+    wl = make_workload("stream", dims_of(plan), seed=seed, n_nodes=n_nodes)
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+    ins = dict(x=f64(wl.x), Y=oracle.sh_real(2, f64(wl.r)), r_len=f64(wl.r_len), W1=f64(wl.W1),
+               W2=f64(wl.W2), Wmix=f64(wl.Wmix), g2=f64(wl.g))
+    return plan, wl, ins
+
+
+@pytest.mark.parametrize("with_mix", [True, False])
+def test_radial_double_backward_by_differences(with_mix):
+    """Central differences of the first backward's loss in every input:
+    L = <ggx, grad_x> + <ggY, grad_Y> + <ggr, grad_rlen> (the first backward
+    is itself pinned by differences of the forward)."""
+    plan, wl, ins = _radial_small(4)
+    if not with_mix:
+        ins["Wmix"] = None
+    rng = np.random.default_rng(12)
+    ggx = rng.normal(size=ins["x"].shape)
+    ggY = rng.normal(size=ins["Y"].shape)
+    ggr = rng.normal(size=ins["r_len"].shape)
+    args = (plan, wl.src, wl.dst, wl.n_nodes)
+    kw = dict(n_basis=wl.n_basis, r_cut=wl.r_cut)
+
+    def L(v):
+        o = oracle.tp_conv_radial_bwd(*args, v["x"], v["Y"], v["r_len"], v["W1"], v["W2"], v["Wmix"],
+                                      v["g2"], with_grad_rlen=True, **kw)
+        return float(np.sum(ggx * o[0]) + np.sum(ggY * o[1]) + np.sum(ggr * o[5]))
+
+    dx, dY, drl, dW1, dW2, dWm, dg2 = oracle.tp_conv_radial_double_bwd(
+        *args, ins["x"], ins["Y"], ins["r_len"], ins["W1"], ins["W2"], ins["Wmix"], ins["g2"],
+        ggx=ggx, ggY=ggY, ggr=ggr, **kw)
+    grads = dict(x=dx, Y=dY, r_len=drl, W1=dW1, W2=dW2, Wmix=dWm, g2=dg2)
+    h = 1e-5
+    for name, grad in grads.items():
+        if ins[name] is None:
+            assert grad is None
+            continue
+        for _ in range(2):
+            d = rng.normal(size=ins[name].shape)
+            if name == "r_len":
+                d *= 0.1                        # stay inside the basis' range
+            up, dn = dict(ins), dict(ins)
+            up[name] = ins[name] + h * d
+            dn[name] = ins[name] - h * d
+            fd = (L(up) - L(dn)) / (2 * h)
+            an = float(np.sum(grad * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_radial_double_backward_without_length_cotangent_is_the_direct_one():
+    """With no cotangent on grad_rlen the weight tangent vanishes: dx, dY and
+    the (unmixed) d_g2 are the direct-weight second-order backward at
+    w = network(r_len), and dW1, dW2 are the network's first backward of that
+    pass's d_w."""
+    plan, wl, ins = _radial_small(7)
+    rng = np.random.default_rng(3)
+    ggx, ggY = rng.normal(size=ins["x"].shape), rng.normal(size=ins["Y"].shape)
+    args = (plan, wl.src, wl.dst, wl.n_nodes)
+    kw = dict(n_basis=wl.n_basis, r_cut=wl.r_cut)
+    dx, dY, drl, dW1, dW2, dWm, dg2 = oracle.tp_conv_radial_double_bwd(
+        *args, ins["x"], ins["Y"], ins["r_len"], ins["W1"], ins["W2"], None, ins["g2"],
+        ggx=ggx, ggY=ggY, **kw)
+    w, cache = oracle.radial_mlp_fwd(ins["r_len"], ins["W1"], ins["W2"], wl.n_basis, wl.r_cut)
+    w = w.reshape(wl.n_edges, plan.n_paths, plan.U)
+    ex, eY, ew, eg = oracle.tp_conv_double_bwd(*args, ins["x"], ins["Y"], w, ins["g2"], ggx, ggY, None)
+    gW1, gW2, gB = oracle.radial_mlp_bwd(ew.reshape(wl.n_edges, -1), cache, ins["W2"], ins["W1"])
+    grl = np.sum(gB * oracle.bessel_basis_deriv(ins["r_len"], wl.n_basis, wl.r_cut), axis=1)
+    for got, want in ((dx, ex), (dY, eY), (dg2, eg), (dW1, gW1), (dW2, gW2), (drl, grl)):
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert dWm is None
+
+
+def test_radial_double_backward_is_linear_in_the_cotangents():
+    plan, wl, ins = _radial_small(8)
+    rng = np.random.default_rng(5)
+    cot = dict(ggx=rng.normal(size=ins["x"].shape), ggY=rng.normal(size=ins["Y"].shape),
+               ggr=rng.normal(size=ins["r_len"].shape))
+    args = (plan, wl.src, wl.dst, wl.n_nodes, ins["x"], ins["Y"], ins["r_len"], ins["W1"], ins["W2"],
+            ins["Wmix"], ins["g2"])
+    kw = dict(n_basis=wl.n_basis, r_cut=wl.r_cut)
+    both = oracle.tp_conv_radial_double_bwd(*args, **cot, **kw)
+    parts = [oracle.tp_conv_radial_double_bwd(*args, **{k: v}, **kw) for k, v in cot.items()]
+    twice = oracle.tp_conv_radial_double_bwd(*args, **{k: 2 * v for k, v in cot.items()}, **kw)
+    for i in range(7):
+        s = sum(p[i] for p in parts)
+        assert np.allclose(both[i], s, rtol=1e-10, atol=1e-12)
+        assert np.allclose(twice[i], 2 * both[i], rtol=1e-12, atol=1e-12)
+    none = oracle.tp_conv_radial_double_bwd(*args, **kw)
+    assert all(np.max(np.abs(a)) == 0 for a in none)
