@@ -436,6 +436,37 @@ tp_status tp_conv_backward_radial_r(tp_plan_t plan, const tp_graph* graph, const
                                     float* grad_r, float* grad_W1, float* grad_W2, float* grad_Wmix,
                                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Second-order backward of the radial layer ("Sobek", Abstract: forward,
+ * backward and double backward, the radial projection streamed).  Given the
+ * inputs of tp_conv_backward_radial and cotangents gg_x [N][xdim], gg_Y
+ * [E][ysh] and gg_rlen [E] of its outputs grad_x, grad_Y and grad_rlen (what a
+ * loss on forces produces; any may be NULL: zero), returns the gradients of
+ *   L = <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_rlen, grad_rlen>
+ * with respect to x (d_x [N][xdim]), Y (d_Y [E][ysh]), r_len (d_rlen [E]),
+ * W1, W2 (d_W1, d_W2, their shapes), Wmix (d_Wmix, with a mix) and grad_out
+ * (d_grad_out [N][outdim]).  With v = gg_rlen dw/dr the weights' tangent and
+ * out_dot = out(gg_x, Y, w) + out(x, gg_Y, w) + out(x, Y, v) (unmixed):
+ * d_grad_out = mix(out_dot), d_Wmix = grad_Wmix of <grad_out, mix(out_dot)>,
+ * d_x and d_Y are first-order adjoints with one operand replaced, and d_W1,
+ * d_W2, d_rlen follow by the chain rule through the network (second
+ * derivatives of SiLU and of the basis enter there).  Outputs may be NULL to
+ * skip them; d_Wmix needs Wmix.  The weights and their tangent are recomputed
+ * on chip, never stored; parameter gradients are fixed-order sums through ws
+ * (tp_conv_radial_double_workspace bytes), so results are bitwise
+ * reproducible.  x, gg_x, grad_out and W2 must be 16-byte aligned
+ * (TP_ERR_ARG); edge arrays receiver-sorted. */
+tp_status tp_conv_double_backward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                         const float* Y, const float* r_len, const float* W1,
+                                         const float* W2, const float* Wmix, const float* grad_out,
+                                         const float* gg_x, const float* gg_Y, const float* gg_rlen,
+                                         float* d_x, float* d_Y, float* d_rlen, float* d_W1, float* d_W2,
+                                         float* d_Wmix, float* d_grad_out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream);
+/* Workspace bytes of tp_conv_double_backward_radial for n_nodes nodes
+ * (with_mix != 0: a channel mix).  Helper that sizes ws. */
+tp_status tp_conv_radial_double_workspace(tp_plan_t plan, int32_t n_nodes, int32_t with_mix,
+                                          size_t* bytes);
+
 /* Gradient with respect to the edge vectors r[E][3] of a loss that depends on
  * them through Y = tp_conv_sph_harm(lmax, r) (upstream grad_Y[E][(lmax+1)^2])
  * and, optionally, through the edge lengths |r| (upstream grad_rlen[E], NULL:

@@ -31,8 +31,8 @@ EXPORTS = (
     "tp_conv_forward_r", "tp_conv_backward_r",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
-    "tp_conv_forward_radial_r", "tp_conv_backward_radial_r",
-    "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
+    "tp_conv_forward_radial_r", "tp_conv_backward_radial_r", "tp_conv_double_backward_radial",
+    "tp_conv_radial_double_workspace", "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
     "tp_conv_forward_fc", "tp_conv_fc_backward_workspace", "tp_conv_backward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_backward_gaunt",
     "tp_conv_last_error",
 )
@@ -110,6 +110,8 @@ def lib():
         "tp_conv_double_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP,
                                           VP, VP, VP, VP]),
         "tp_conv_radial_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
+        "tp_conv_double_backward_radial": (I32, [P, ctypes.POINTER(_Graph)] + [VP] * 18 + [SZ, VP]),
+        "tp_conv_radial_double_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -708,6 +710,62 @@ def backward_radial_r(plan, graph, x, r, W1, W2, grad_out, Wmix=None, out_pre=No
                                            _ptr(gx), _ptr(gr), _ptr(gW1), _ptr(gW2), _ptr(gWm), _ptr(ws),
                                            ws.numel(), _stream(x.device)))
     return gx, gr, gW1, gW2, gWm
+
+
+def double_backward_radial(plan, graph, x, Y, r_len, W1, W2, grad_out, Wmix=None, gg_x=None, gg_Y=None,
+                           gg_rlen=None, want=("x", "Y", "rlen", "W1", "W2", "Wmix", "g"), outs=None,
+                           ws=None):
+    """(d_x, d_Y, d_rlen, d_W1, d_W2, d_Wmix, d_grad_out): gradients of
+    <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_rlen, grad_rlen> (the outputs of
+    backward_radial) with respect to its inputs; missing cotangents are zero,
+    outputs not in ``want`` (and d_Wmix without a mix) are None.  ``outs`` (a
+    dict name -> tensor) and ``ws`` supply preallocated buffers."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    nb, nh, _ = plan.radial
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(r_len, "r_len", torch.float32, (E,))
+    _need(W1, "W1", torch.float32, (nb, nh))
+    _need(W2, "W2", torch.float32, (nh, plan.n_paths * plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    if Wmix is not None:
+        K = len(plan.out_irreps.split("+"))
+        _need(Wmix, "Wmix", torch.float32, (K, plan.mul, plan.mul))
+    for t, name, shape in ((gg_x, "gg_x", (N, plan.xdim)), (gg_Y, "gg_Y", (E, plan.ysh)),
+                           (gg_rlen, "gg_rlen", (E,))):
+        if t is not None:
+            _need(t, name, torch.float32, shape)
+    outs = outs or {}
+
+    def buf(name, like):
+        if name not in want or like is None:
+            return None
+        t = outs.get(name)
+        if t is None:
+            return torch.empty_like(like)
+        _need(t, "d_" + name, torch.float32, tuple(like.shape))
+        return t
+    dx, dY, drl = buf("x", x), buf("Y", Y), buf("rlen", r_len)
+    dW1, dW2, dWm, dg = buf("W1", W1), buf("W2", W2), buf("Wmix", Wmix), buf("g", grad_out)
+    nbytes = radial_double_workspace(plan, N, Wmix is not None)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    elif ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
+    g = graph.cstruct()
+    _check(lib().tp_conv_double_backward_radial(
+        plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(r_len), _ptr(W1), _ptr(W2), _ptr(Wmix),
+        _ptr(grad_out), _ptr(gg_x), _ptr(gg_Y), _ptr(gg_rlen), _ptr(dx), _ptr(dY), _ptr(drl), _ptr(dW1),
+        _ptr(dW2), _ptr(dWm), _ptr(dg), _ptr(ws), ws.numel(), _stream(x.device)))
+    return dx, dY, drl, dW1, dW2, dWm, dg
+
+
+def radial_double_workspace(plan, n_nodes, with_mix):
+    """bytes of workspace double_backward_radial needs"""
+    b = ctypes.c_size_t()
+    _check(lib().tp_conv_radial_double_workspace(plan.handle, n_nodes, int(bool(with_mix)), ctypes.byref(b)))
+    return b.value
 
 
 def radial_workspace(plan, n_nodes, with_mix):

@@ -997,4 +997,103 @@ tp_status tp_conv_backward_radial_r(tp_plan_t plan, const tp_graph* graph, const
                               nullptr, grad_W1, grad_W2, grad_Wmix, ws, ws_bytes, stream, true);
 }
 
+tp_status tp_conv_radial_double_workspace(tp_plan_t plan, int32_t n_nodes, int32_t with_mix, size_t* bytes) {
+  if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_radial_double_workspace: NULL argument");
+  if (!plan->rs || !plan->rs->dbl_workspace)
+    return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_radial_double_workspace: negative size");
+  size_t b = plan->rs->dbl_workspace(n_nodes, 0);
+  if (with_mix) {
+    tp_status s = need_uvw(plan);
+    if (s != TP_OK) return s;
+    // unmixed upstream gradient and out_dot, then the kernels' or the mix's scratch
+    const size_t u = tpc::uvw_workspace_bytes(plan->uvw.n, plan->mul);
+    b = 2 * align_up((size_t)n_nodes * plan->outdim * sizeof(float)) + (u > b ? u : b);
+  }
+  *bytes = b;
+  return TP_OK;
+}
+
+tp_status tp_conv_double_backward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
+                                         const float* Y, const float* r_len, const float* W1,
+                                         const float* W2, const float* Wmix, const float* grad_out,
+                                         const float* gg_x, const float* gg_Y, const float* gg_rlen,
+                                         float* d_x, float* d_Y, float* d_rlen, float* d_W1, float* d_W2,
+                                         float* d_Wmix, float* d_grad_out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  const char* fn = "tp_conv_double_backward_radial";
+  if (!plan) return set_error(TP_ERR_ARG, std::string(fn) + ": plan is NULL");
+  if (!plan->rs || !plan->rs->dbl) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  tp_status s = check_graph(graph, d_x != nullptr);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && (!x || !grad_out)) return set_error(TP_ERR_ARG, std::string(fn) + ": x / grad_out NULL");
+  if (!W1 || !W2) return set_error(TP_ERR_ARG, std::string(fn) + ": W1/W2 NULL");
+  if (E > 0 && (!Y || !r_len)) return set_error(TP_ERR_ARG, std::string(fn) + ": Y / r_len NULL");
+  if (d_Wmix && !Wmix) return set_error(TP_ERR_ARG, std::string(fn) + ": d_Wmix without Wmix");
+  if (misaligned16({x, gg_x, grad_out, W2}))
+    return set_error(TP_ERR_ARG, std::string(fn) + ": x, gg_x, grad_out and W2 must be 16-byte aligned");
+  size_t need = 0;
+  s = tp_conv_radial_double_workspace(plan, N, Wmix != nullptr, &need);
+  if (s != TP_OK) return s;
+  if (ws_bytes < need || (need > 0 && !ws))
+    return set_error(TP_ERR_WORKSPACE, std::string(fn) + ": workspace too small");
+  char* w = static_cast<char*>(ws);
+  const float* g = grad_out;
+  float* out_dot = d_grad_out;                   // without a mix, out_dot is d_grad_out itself
+  if (Wmix) {
+    s = need_uvw(plan);
+    if (s != TP_OK) return s;
+    float* gmix = reinterpret_cast<float*>(w);
+    w += align_up((size_t)N * plan->outdim * sizeof(float));
+    out_dot = (d_grad_out || d_Wmix) ? reinterpret_cast<float*>(w) : nullptr;
+    w += align_up((size_t)N * plan->outdim * sizeof(float));
+    if (N > 0) {
+      s = tpc::uvw_forward(N, plan->mul, plan->outdim, plan->uvw, Wmix, grad_out, gmix, true, stream);
+      if (s != TP_OK) return s;
+    }
+    g = gmix;
+  }
+  tpc::RadialArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_perm = graph->t_perm;
+  a.t_col = graph->t_col;
+  a.x = x;
+  a.Y = Y;
+  a.r_len = r_len;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.grad_out = g;
+  a.gg_x = gg_x;
+  a.gg_Y = gg_Y;
+  a.gg_rlen = gg_rlen;
+  a.out = out_dot;
+  a.d_x = d_x;
+  a.d_Y = d_Y;
+  a.d_rlen = d_rlen;
+  a.d_W1 = d_W1;
+  a.d_W2 = d_W2;
+  a.r_cut = plan->opts.r_cut;
+  a.ws = w;
+  a.stream = stream;
+  hipError_t e = plan->rs->dbl(a);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_double_backward_radial launch");
+  if (Wmix && N > 0) {
+    if (d_grad_out) {
+      s = tpc::uvw_forward(N, plan->mul, plan->outdim, plan->uvw, Wmix, out_dot, d_grad_out, false, stream);
+      if (s != TP_OK) return s;
+    }
+    if (d_Wmix) {
+      // the kernels' partial sums are consumed; their scratch is free again
+      s = tpc::uvw_grad_w(N, plan->mul, plan->outdim, plan->uvw, out_dot, grad_out, d_Wmix, w, stream);
+      if (s != TP_OK) return s;
+    }
+  }
+  return TP_OK;
+}
+
 }  // extern "C"

@@ -56,6 +56,10 @@ struct RadialArgs {
   // edge-vector form: Y holds r [E][3] (r_len unused), grad_Y receives grad_r
   // [E][3] (grad_rlen unused)
   bool geom = false;
+  // second-order backward: cotangents of (grad_x, grad_Y, grad_rlen) and
+  // outputs (out receives d_grad_out before the mix)
+  const float *gg_x = nullptr, *gg_Y = nullptr, *gg_rlen = nullptr;
+  float *d_x = nullptr, *d_Y = nullptr, *d_rlen = nullptr, *d_W1 = nullptr, *d_W2 = nullptr;
   void* ws = nullptr;
   hipStream_t stream = nullptr;
 };
@@ -64,6 +68,8 @@ struct RadialSet {
   RadialFn fwd = nullptr;
   RadialFn bwd = nullptr;                        // grad_x, grad_Y, grad_rlen, grad_W1, grad_W2
   size_t (*bwd_workspace)(int n_nodes, int n_edges) = nullptr;
+  RadialFn dbl = nullptr;                        // d_grad_out (unmixed), d_x, d_Y, d_rlen, d_W1, d_W2
+  size_t (*dbl_workspace)(int n_nodes, int n_edges) = nullptr;
 };
 // fully connected per-edge weights (W_e = sum_h R_e[h] Theta[h]), reassociated
 struct FcArgs {

@@ -1,5 +1,5 @@
 // Radial-weight kernel specialisations for the 0e+1o+2e / lmax 2 signature.
-#include "radial_kernels.hpp"
+#include "radial_dbl_kernels.hpp"
 
 namespace tpc {
 
@@ -48,6 +48,12 @@ int recv_blocks(int n_nodes) {
   return b < 512 ? (b > 0 ? b : 1) : 512;                 // two workgroups per CU
 }
 int recv_parts(int n_nodes) { return recv_blocks(n_nodes) * kRecvWaves; }
+// the second-order receiver pass runs one wave per SIMD: one workgroup per CU
+int dbl_recv_blocks(int n_nodes) {
+  const int b = (n_nodes + kRecvWaves - 1) / kRecvWaves;
+  return b < 256 ? (b > 0 ? b : 1) : 256;
+}
+int dbl_recv_parts(int n_nodes) { return dbl_recv_blocks(n_nodes) * kRecvWaves; }
 template <int U>
 int w2_blocks(int n_nodes) {
   const int want = (n_nodes + kNH / 16 - 1) / (kNH / 16), cap = 512 / (U / 16);
@@ -125,9 +131,60 @@ static hipError_t launch_radial_bwd(const RadialArgs& a) {
   return a.geom ? launch_radial_bwd_as<U, true>(a) : launch_radial_bwd_as<U, false>(a);
 }
 
+// second-order backward: d_W1 partials (receiver pass), then the two d_W2
+// terms' partials, back to back so that one fixed-order sum adds them
+template <int U>
+static size_t radial_dbl_ws(int n_nodes, int /*n_edges*/) {
+  return align256((size_t)dbl_recv_parts(n_nodes) * kNB * kNH * sizeof(float)) +
+         (size_t)2 * w2_blocks<U>(n_nodes) * kNH * SigR::NP * U * sizeof(float);
+}
+
+// a.grad_out is the unmixed upstream gradient g; a.out receives out_dot (d_g
+// before the mix); cotangents a.gg_* may be null (zeros); outputs may be null
+template <int U>
+static hipError_t launch_radial_dbl(const RadialArgs& a) {
+  RadialParams rp{a.r_cut, a.W1, a.W2};
+  const int nb1 = dbl_recv_parts(a.n_nodes), nb2 = w2_blocks<U>(a.n_nodes);
+  float* part1 = static_cast<float*>(a.ws);
+  float* part2 = reinterpret_cast<float*>(static_cast<char*>(a.ws) +
+                                          align256((size_t)nb1 * kNB * kNH * sizeof(float)));
+  if (a.out && a.n_nodes > 0)
+    hipLaunchKernelGGL((k_radial_node_dbl<SigR, U, kNB, kNH, kNodeWaves, false>), node_grid<U>(a.n_nodes),
+                       dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.row_ptr, nullptr, a.col, a.x, a.gg_x,
+                       a.Y, a.gg_Y, a.r_len, a.gg_rlen, rp, a.out);
+  if (a.d_Y || a.d_rlen || a.d_W1) {
+    hipLaunchKernelGGL((k_radial_dbl_recv<SigR, U, kNB, kNH, kRecvWaves>), dim3(dbl_recv_blocks(a.n_nodes)),
+                       dim3(64 * kRecvWaves), 0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.gg_x, a.Y,
+                       a.gg_Y, a.r_len, a.gg_rlen, rp, a.grad_out, a.d_Y, a.d_rlen, part1);
+    if (a.d_W1) {
+      const long long n = (long long)kNB * kNH;
+      hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, a.stream,
+                         part1, nb1, n, a.d_W1);
+    }
+  }
+  if (a.d_W2) {
+    const size_t half = (size_t)nb2 * kNH * SigR::NP * U;
+    hipLaunchKernelGGL((k_radial_dbl_w2<SigR, U, kNB, kNH, 0>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)), 0,
+                       a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.gg_x, a.Y, a.gg_Y, a.r_len, a.gg_rlen,
+                       rp, a.grad_out, part2);
+    hipLaunchKernelGGL((k_radial_dbl_w2<SigR, U, kNB, kNH, 1>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)), 0,
+                       a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.gg_x, a.Y, a.gg_Y, a.r_len, a.gg_rlen,
+                       rp, a.grad_out, part2 + half);
+    const long long n = (long long)kNH * SigR::NP * U;
+    hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, a.stream,
+                       part2, 2 * nb2, n, a.d_W2);
+  }
+  if (a.d_x && a.n_nodes > 0)
+    hipLaunchKernelGGL((k_radial_node_dbl<SigR, U, kNB, kNH, kNodeWaves, true>), node_grid<U>(a.n_nodes),
+                       dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.t_row_ptr, a.t_perm, a.t_col,
+                       a.grad_out, nullptr, a.Y, a.gg_Y, a.r_len, a.gg_rlen, rp, a.d_x);
+  return hipGetLastError();
+}
+
 template <int U>
 static const RadialSet* radial_set() {
-  static const RadialSet s{&launch_radial_fwd<U>, &launch_radial_bwd<U>, &radial_bwd_ws<U>};
+  static const RadialSet s{&launch_radial_fwd<U>, &launch_radial_bwd<U>, &radial_bwd_ws<U>,
+                           &launch_radial_dbl<U>, &radial_dbl_ws<U>};
   return &s;
 }
 

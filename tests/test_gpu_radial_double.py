@@ -1,0 +1,259 @@
+"""GPU parity of the second-order backward of the radial-weight convolution
+(tp_conv_double_backward_radial) against the float64 oracle on identical
+seeded float32 inputs: every output block within 1e-4 of max|ref| of that
+block, parameter gradients per path block and per irrep.  Cotangents on
+grad_x, grad_Y and grad_rlen; the weights, their tangent and the network's
+derivatives are recomputed on chip."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests._common import dims_of
+from tests.test_gpu_parity import T, block_err, in_blocks, out_blocks, say, y_blocks
+from tests.test_gpu_radial import RC, _irreps, _param_err, _radial_inputs, _subgraph, _vec_err
+from workloads import make_workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+ALL = ("x", "Y", "rlen", "W1", "W2", "Wmix", "g")
+
+
+@pytest.fixture(scope="module")
+def tpc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_product_convolution_amd as m
+    m.lib()
+    return m
+
+
+def _cotangents(op, n_nodes, n_edges, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.normal(size=(n_nodes, op.xdim)).astype(np.float32),
+            rng.normal(size=(n_edges, op.ysh)).astype(np.float32),
+            rng.normal(size=n_edges).astype(np.float32))
+
+
+def _gpu_dbl(tpc, plan, wl, mix, g2, ggx, ggY, ggr, want=ALL):
+    """second-order backward on the GPU (cotangents in original edge order,
+    gathered to receiver order); outputs as numpy, edge arrays receiver-sorted"""
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+    rl = tpc.gather_rows(T(wl.r_len), g.perm)
+    opt = lambda a, gather: None if a is None else (tpc.gather_rows(T(a), g.perm) if gather else T(a))
+    res = tpc.double_backward_radial(plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), T(g2),
+                                     Wmix=T(wl.Wmix) if mix else None, gg_x=opt(ggx, False),
+                                     gg_Y=opt(ggY, True), gg_rlen=opt(ggr, True), want=want)
+    torch.cuda.synchronize()
+    cpu = lambda t: None if t is None else t.cpu().numpy()
+    names = ("dx", "dY", "drl", "dW1", "dW2", "dWm", "dg")
+    out = {k: cpu(v) for k, v in zip(names, res)}
+    out["perm"] = cpu(g.perm)[:wl.n_edges]
+    return out
+
+
+def _ref(op, wl, mix, g2, ggx, ggY, ggr):
+    Yo = oracle.sh_real(2, wl.r)
+    return oracle.tp_conv_radial_double_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Yo, wl.r_len, wl.W1,
+                                            wl.W2, wl.Wmix if mix else None, g2, 8, RC, ggx=ggx, ggY=ggY,
+                                            ggr=ggr)
+
+
+def _check(op, res, ref, U, p, edges=None, nodes=None, recv=None):
+    """res (GPU, receiver-sorted edges) against ref (oracle, original order);
+    p maps receiver-sorted positions to original edges.  edges / nodes / recv
+    restrict the comparison (full-size sampled case)."""
+    dx, dY, drl, dW1, dW2, dWm, dg = ref
+    if res["dx"] is not None:
+        n = slice(None) if nodes is None else nodes
+        assert block_err(res["dx"][n], dx[n], in_blocks(op)) <= TOL, "d_x"
+    if edges is None:
+        sel_gpu, sel_ref = slice(None), p
+    else:
+        inv = np.empty(len(p), np.int64)
+        inv[p] = np.arange(len(p))
+        sel_gpu, sel_ref = inv[edges], edges
+    if res["dY"] is not None:
+        assert block_err(res["dY"][sel_gpu], dY[sel_ref], y_blocks(op)) <= TOL, "d_Y"
+    if res["drl"] is not None:
+        assert _vec_err(res["drl"][sel_gpu], drl[sel_ref]) <= TOL, "d_rlen"
+    if res["dW1"] is not None:
+        assert _param_err(res["dW1"], dW1) <= TOL, "d_W1"
+    if res["dW2"] is not None:
+        P = op.n_paths
+        a, b = res["dW2"].reshape(-1, P, U), dW2.reshape(-1, P, U)
+        for q in range(P):
+            assert _param_err(a[:, q], b[:, q]) <= TOL, f"d_W2 path {q}"
+    if res["dWm"] is not None:
+        for k in range(dWm.shape[0]):
+            assert _param_err(res["dWm"][k], dWm[k]) <= TOL, f"d_Wmix irrep {k}"
+    if res["dg"] is not None:
+        r = slice(None) if recv is None else recv
+        assert block_err(res["dg"][r], dg[r], out_blocks(op)) <= TOL, "d_grad_out"
+
+
+@pytest.mark.parametrize("U,name,n,mix", [(16, "stream", 300, True), (128, "stream", 120, True),
+                                          (16, "zipf", 400, False), (128, "uniform", 100, True)])
+def test_radial_double_backward_parity(tpc, U, name, n, mix):
+    say(f"radial double bwd U={U} graph={name} n={n} mix={mix}")
+    gname = "lmax3" if name == "uniform" else name
+    op, wl = _radial_inputs(U, gname, n)
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    ggx, ggY, ggr = _cotangents(op, wl.n_nodes, wl.n_edges, U + n)
+    res = _gpu_dbl(tpc, plan, wl, mix, wl.g, ggx, ggY, ggr)
+    ref = _ref(op, wl, mix, wl.g, ggx, ggY, ggr)
+    _check(op, res, ref, U, res["perm"])
+    if not mix:
+        assert res["dWm"] is None
+
+
+@pytest.mark.parametrize("which", ["x", "Y", "r", "none"])
+def test_radial_double_backward_missing_cotangents(tpc, which):
+    """A missing cotangent is a zero one; with none every output is zero."""
+    say(f"radial double bwd, only gg_{which}")
+    U = 16
+    op, wl = _radial_inputs(U, "stream", 200, seed=5)
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    ggx, ggY, ggr = _cotangents(op, wl.n_nodes, wl.n_edges, 17)
+    ggx, ggY, ggr = (ggx if which == "x" else None, ggY if which == "Y" else None,
+                     ggr if which == "r" else None)
+    res = _gpu_dbl(tpc, plan, wl, True, wl.g, ggx, ggY, ggr)
+    if which == "none":
+        for k in ("dx", "dY", "drl", "dW1", "dW2", "dWm", "dg"):
+            assert np.all(res[k] == 0), k
+        return
+    _check(op, res, _ref(op, wl, True, wl.g, ggx, ggY, ggr), U, res["perm"])
+
+
+def test_radial_double_backward_output_subsets(tpc):
+    """Outputs left out are not computed and the others do not change."""
+    say("radial double bwd output subsets")
+    U = 16
+    op, wl = _radial_inputs(U, "zipf", 300, seed=2)
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    cot = _cotangents(op, wl.n_nodes, wl.n_edges, 23)
+    full = _gpu_dbl(tpc, plan, wl, True, wl.g, *cot)
+    for want in (("x",), ("Y", "rlen"), ("W1",), ("W2",), ("Wmix",), ("g",), ("W1", "W2", "Wmix")):
+        part = _gpu_dbl(tpc, plan, wl, True, wl.g, *cot, want=want)
+        names = dict(x="dx", Y="dY", rlen="drl", W1="dW1", W2="dW2", Wmix="dWm", g="dg")
+        for k, v in names.items():
+            if k in want:
+                assert np.array_equal(part[v], full[v]), (want, k)
+            else:
+                assert part[v] is None, (want, k)
+
+
+def test_radial_double_backward_degenerate_graphs_and_determinism(tpc):
+    """Nodes without edges, a graph without edges, and bitwise-identical repeats."""
+    say("radial double bwd degenerate graphs and determinism")
+    U = 16
+    op = oracle.build_plan(_irreps(U), 2, 2)
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    wl = make_workload("stream", dims_of(op), seed=3, n_nodes=60)
+    keep = (wl.src >= 10) & (wl.dst >= 10)          # nodes 0..9 lose every edge
+    wl.src, wl.dst, wl.r = wl.src[keep], wl.dst[keep], wl.r[keep]
+    cot = _cotangents(op, wl.n_nodes, wl.n_edges, 29)
+    a = _gpu_dbl(tpc, plan, wl, True, wl.g, *cot)
+    b = _gpu_dbl(tpc, plan, wl, True, wl.g, *cot)
+    for k, v in a.items():
+        assert np.array_equal(v, b[k]), k
+    _check(op, a, _ref(op, wl, True, wl.g, *cot), U, a["perm"])
+    assert np.all(a["dx"][:10] == 0) and np.all(a["dg"][:10] == 0)
+    wl.src, wl.dst, wl.r = wl.src[:0], wl.dst[:0], wl.r[:0]
+    cot = _cotangents(op, wl.n_nodes, 0, 31)
+    c = _gpu_dbl(tpc, plan, wl, True, wl.g, *cot)
+    for k in ("dx", "dW1", "dW2", "dWm", "dg"):
+        assert np.all(c[k] == 0), k
+    assert c["dY"].shape == (0, 9) and c["drl"].shape == (0,)
+
+
+def _oracle_dbl_part(task):
+    """the oracle's second-order backward on one chunk of whole receivers (a
+    process-pool worker)"""
+    op, src, dst, n, x, Y, rl, W1, W2, Wm, g2, ggx, ggY, ggr = task
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    return oracle.tp_conv_radial_double_bwd(op, src, dst, n, x, Y, rl, W1, W2, Wm, g2, 8, RC,
+                                            ggx=ggx, ggY=ggY, ggr=ggr)
+
+
+def _pooled_dbl_oracle(op, wl, e, g2, ggx, ggY, ggr, workers):
+    """The oracle on the edges e, split by receiver over a process pool: per-node
+    rows and parameter gradients are sums over the chunks (each receiver's
+    in-edges sit in one chunk)."""
+    import multiprocessing as mp
+    order = np.argsort(wl.dst[e], kind="stable")
+    bounds = np.linspace(0, len(order), workers + 1).astype(np.int64)
+    cuts = [0]
+    for c in bounds[1:-1]:
+        while 0 < c < len(order) and wl.dst[e[order[c]]] == wl.dst[e[order[c - 1]]]:
+            c += 1
+        cuts.append(max(c, cuts[-1]))
+    cuts.append(len(order))
+    tasks, parts = [], []
+    for t in range(workers):
+        ec = e[np.sort(order[cuts[t]:cuts[t + 1]])]
+        if len(ec) == 0:
+            continue
+        rc = np.unique(wl.dst[ec])
+        nodes, src, dst, _ = _subgraph(wl, ec, rc)
+        tasks.append((op, src, dst, len(nodes), wl.x[nodes], oracle.sh_real(2, wl.r[ec]), wl.r_len[ec],
+                      wl.W1, wl.W2, wl.Wmix, g2[nodes], ggx[nodes], ggY[ec], ggr[ec]))
+        parts.append((ec, nodes))
+    with mp.get_context("fork").Pool(workers) as pool:
+        res = pool.map(_oracle_dbl_part, tasks)
+    N, E = wl.n_nodes, wl.n_edges
+    dx = np.zeros((N, op.xdim))
+    dY = np.zeros((E, op.ysh))
+    drl = np.zeros(E)
+    dg = np.zeros((N, op.outdim))
+    dW1 = dW2 = dWm = 0.0
+    for (ec, nodes), r in zip(parts, res):
+        dx[nodes] += r[0]
+        dY[ec], drl[ec] = r[1], r[2]
+        dW1, dW2, dWm = dW1 + r[3], dW2 + r[4], dWm + r[5]
+        dg[nodes] += r[6]
+    return dx, dY, drl, dW1, dW2, dWm, dg
+
+
+def test_radial_double_backward_full_size_sampled(tpc):
+    """The 100,000-atom / 3,000,000-edge streaming layer with its mix at full
+    size, in the launch configuration the benchmark times.  The upstream
+    gradient is zero outside 2,048 sampled receivers (one in each residue class
+    mod 2,048), so every output except d_grad_out is exactly that of those
+    receivers' in-edges, which the oracle computes, and d_grad_out (which does
+    not depend on the upstream gradient) is compared on the sampled rows.
+    Cotangents are dense over all nodes and edges."""
+    say("radial double bwd full-size sampled: stream 100000 nodes, 2048 receivers")
+    U = 128
+    op = oracle.build_plan(_irreps(U), 2, 2)
+    wl = make_workload("stream", dims_of(op))
+    N = wl.n_nodes
+    k = np.arange(2048)
+    recv = np.sort(k + 2048 * (k % 48))
+    g2 = np.zeros_like(wl.g)
+    g2[recv] = wl.g[recv]
+    ggx, ggY, ggr = _cotangents(op, N, wl.n_edges, 37)
+    plan = tpc.Plan(_irreps(U), 2, 2, radial=(8, 64, RC), uvw=True)
+    res = _gpu_dbl(tpc, plan, wl, True, g2, ggx, ggY, ggr)
+    e = np.nonzero(np.isin(wl.dst, recv))[0]
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    say(f"  oracle on {len(e)} edges over {workers} processes")
+    ref = _pooled_dbl_oracle(op, wl, e, g2, ggx, ggY, ggr, workers)
+    nodes = np.unique(np.concatenate([wl.src[e], recv]))
+    _check(op, res, ref, U, res["perm"], edges=e, nodes=nodes, recv=recv)
+    rng = np.random.default_rng(13)
+    others = np.setdiff1d(rng.choice(N, size=200, replace=False), nodes)
+    assert np.all(res["dx"][others] == 0)
+    inv = np.empty(wl.n_edges, np.int64)
+    inv[res["perm"]] = np.arange(wl.n_edges)
+    mask = np.ones(wl.n_edges, bool)
+    mask[inv[e]] = False
+    assert np.all(res["dY"][mask][:100000] == 0) and np.all(res["drl"][mask][:100000] == 0)
