@@ -82,6 +82,14 @@ def test_cg_operation_counts(irreps, lsh):
         assert fl["fwd"] == 81 + 2 * 137 + 2 * 51 and fl["bwd"] == 42 + 4 * 137 + 4 * 51 + 2 * 81
 
 
+def test_radial_flops():
+    # 3,000,000 edges, 15 paths x 128 channels, 64 hidden units: one [E x 64] x
+    # [64 x 1920] product is 0.737 TFLOP; the second-order backward forms ten
+    fl = bench.radial_flops(3_000_000, 15, 128, 64)
+    assert round(fl["fwd"] / 1e12, 3) == 0.737
+    assert fl["bwd_recv"] == 2 * fl["fwd"] and fl["double_bwd"] == 10 * fl["fwd"]
+
+
 def test_cold_copy_count():
     assert bench.copies_for_cold(90e6) == 12            # 1,536-atom w + Y: 12 x 90 MB >= 1 GiB
     assert bench.copies_for_cold(7e9) == 1              # the Zipf weight stream alone is cold
