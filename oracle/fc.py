@@ -88,3 +88,29 @@ def fc_conv_bwd(plan, src, dst, n_nodes, x, Y, R, Theta, g):
         grad_R[e] = np.einsum("epuv,hpuv->eh", gW, Th)
         grad_Th += np.einsum("eh,epuv->hpuv", R[e], gW)
     return grad_x, grad_Y, grad_R, grad_Th
+
+
+def fc_conv_double_bwd(plan, src, dst, n_nodes, x, Y, R, Theta, g, ggx=None, ggY=None, ggR=None,
+                       ggTheta=None):
+    """Second-order backward of the fully connected family ("Sobek", Abstract:
+    both operator families through forward, backward and double backward).
+    F(g, x, Y, R, Theta) = <g, out> is linear in each argument, so for
+    cotangents (ggx, ggY, ggR, ggTheta) of the first backward's outputs (None:
+    zero) the loss L = <ggx, gx> + <ggY, gY> + <ggR, gR> + <ggTheta, gTheta>
+    equals F(g, ggx, Y, R, Theta) + F(g, x, ggY, R, Theta) + F(g, x, Y, ggR, Theta)
+    + F(g, x, Y, R, ggTheta); each gradient of L is a sum of first-order
+    results with one operand replaced.  Returns (dx, dY, dR, dTheta, dg)."""
+    src, dst, x, Y = _check(plan, src, dst, n_nodes, x, Y)
+    R = np.asarray(R, dtype=np.float64)
+    Th = np.asarray(Theta, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    z = lambda a, like: np.zeros_like(like) if a is None else np.asarray(a, dtype=np.float64)
+    ggx, ggY, ggR, ggTh = z(ggx, x), z(ggY, Y), z(ggR, R), z(ggTheta, Th)
+    args = (plan, src, dst, n_nodes)
+    dg = (fc_conv_fwd(*args, ggx, Y, R, Th) + fc_conv_fwd(*args, x, ggY, R, Th)
+          + fc_conv_fwd(*args, x, Y, ggR, Th) + fc_conv_fwd(*args, x, Y, R, ggTh))
+    _, gY_x, gR_x, gT_x = fc_conv_bwd(*args, ggx, Y, R, Th, g)      # x -> ggx
+    gx_Y, _, gR_Y, gT_Y = fc_conv_bwd(*args, x, ggY, R, Th, g)      # Y -> ggY
+    gx_R, gY_R, _, gT_R = fc_conv_bwd(*args, x, Y, ggR, Th, g)      # R -> ggR
+    gx_T, gY_T, gR_T, _ = fc_conv_bwd(*args, x, Y, R, ggTh, g)      # Theta -> ggTheta
+    return (gx_Y + gx_R + gx_T, gY_x + gY_R + gY_T, gR_x + gR_Y + gR_T, gT_x + gT_Y + gT_R, dg)

@@ -73,3 +73,38 @@ def test_backward_multilinearity_and_differences():
         fd = (np.sum(g * fc_conv_fwd(*args, *up)) - np.sum(g * fc_conv_fwd(*args, *dn))) / (2 * h)
         an = float(np.sum([gx, gY, gR, gTh][which] * d))
         assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+def test_double_backward_by_differences_and_multilinearity():
+    """The second-order backward: central differences of the first backward's
+    loss L = <ggx, gx> + <ggY, gY> + <ggR, gR> + <ggTheta, gTheta> in each of
+    x, Y, R, Theta and g (exact up to rounding: every term is multilinear), the
+    identity <dg, g> = L (L is linear in g), and missing cotangents as zeros."""
+    from oracle.fc import fc_conv_double_bwd
+    plan, wl, Y, R, Th, rng = _case(seed=4)
+    x = wl.x.astype(np.float64)
+    g = rng.normal(size=(wl.n_nodes, plan.outdim))
+    args = (plan, wl.src, wl.dst, wl.n_nodes)
+    cot = [rng.normal(size=a.shape) for a in (x, Y, R, Th)]
+
+    def L(x_, Y_, R_, Th_, g_):
+        return float(sum(np.sum(c * v) for c, v in zip(cot, fc_conv_bwd(*args, x_, Y_, R_, Th_, g_))))
+
+    dx, dY, dR, dTh, dg = fc_conv_double_bwd(*args, x, Y, R, Th, g, *cot)
+    h = 1e-3
+    base = [x, Y, R, Th, g]
+    for which, grad in enumerate((dx, dY, dR, dTh, dg)):
+        d = rng.normal(size=base[which].shape)
+        up, dn = list(base), list(base)
+        up[which] = base[which] + h * d
+        dn[which] = base[which] - h * d
+        fd = (L(*up) - L(*dn)) / (2 * h)
+        an = float(np.sum(grad * d))
+        assert abs(fd - an) <= 1e-9 * max(1.0, abs(an)), which
+    Lv = L(x, Y, R, Th, g)
+    assert abs(float(np.sum(dg * g)) - Lv) <= 1e-10 * max(1.0, abs(Lv))
+    a = fc_conv_double_bwd(*args, x, Y, R, Th, g, cot[0], None, None, None)
+    b = fc_conv_double_bwd(*args, x, Y, R, Th, g, cot[0], np.zeros_like(Y), np.zeros_like(R),
+                           np.zeros_like(Th))
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
