@@ -315,6 +315,31 @@ tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float
                               float* grad_x, float* grad_Y, float* grad_R, float* grad_Theta, int32_t flags,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Second-order backward of the fully connected family ("Sobek", Abstract:
+ * both operator families through forward, backward and double backward).
+ * Given the inputs of tp_conv_backward_fc and cotangents gg_x [N][xdim], gg_Y
+ * [E][ysh], gg_R [E][n_radial], gg_Theta [n_radial][P][U][U] of its outputs
+ * (any may be NULL: zero), returns the gradients of
+ *   L = <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_R, grad_R> + <gg_Theta, grad_Theta>:
+ * the product is linear in each of x, Y, R and Theta, so
+ *   d_grad_out = out(gg_x, ..) + out(.., gg_Y, ..) + out(.., gg_R, ..) + out(.., gg_Theta)
+ * and d_x, d_Y, d_R, d_Theta are each the sum of the first backward's result
+ * with one of the other operands replaced by its cotangent.  Each present
+ * cotangent costs one reassociated forward and one backward (no per-edge
+ * weight or message is formed); outputs may be NULL to skip them and get
+ * zeros when no cotangent reaches them.  ws: tp_conv_fc_double_workspace
+ * bytes (the first-order workspace plus one scratch row per output); ws,
+ * Theta and gg_Theta 16-byte aligned; d_x needs the graph's sender grouping.
+ * Deterministic. */
+tp_status tp_conv_fc_double_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_edges, int32_t n_radial,
+                                      size_t* bytes);
+tp_status tp_conv_double_backward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                     const float* R, int32_t n_radial, const float* Theta,
+                                     const float* grad_out, const float* gg_x, const float* gg_Y,
+                                     const float* gg_R, const float* gg_Theta, float* d_x, float* d_Y,
+                                     float* d_R, float* d_Theta, float* d_grad_out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
 /* ---- Gaunt (spherical-grid) product: a different, cheaper operator ----------
  * The Gaunt tensor product is not the CG product: it lacks the couplings with
  * l1 + l2 + l3 odd (such as the cross product) and so is less expressive, and

@@ -33,7 +33,8 @@ EXPORTS = (
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
     "tp_conv_forward_radial_r", "tp_conv_backward_radial_r", "tp_conv_double_backward_radial",
     "tp_conv_radial_double_workspace", "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
-    "tp_conv_forward_fc", "tp_conv_fc_backward_workspace", "tp_conv_backward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_backward_gaunt",
+    "tp_conv_forward_fc", "tp_conv_fc_backward_workspace", "tp_conv_backward_fc", "tp_conv_fc_double_workspace",
+    "tp_conv_double_backward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_backward_gaunt",
     "tp_conv_last_error",
 )
 
@@ -104,6 +105,9 @@ def lib():
         "tp_conv_fc_backward_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_backward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32, VP, VP, VP, VP, VP, VP, I32,
                                       VP, SZ, VP]),
+        "tp_conv_fc_double_workspace": (I32, [P, I32, I32, I32, ctypes.POINTER(SZ)]),
+        "tp_conv_double_backward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32] + [VP] * 11
+                                       + [VP, SZ, VP]),
         "tp_conv_gaunt_dims": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "tp_conv_forward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_backward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
@@ -500,6 +504,44 @@ def fc_backward_workspace(plan, n_nodes, n_radial):
     b = ctypes.c_size_t()
     _check(lib().tp_conv_fc_backward_workspace(plan.handle, n_nodes, n_radial, ctypes.byref(b)))
     return b.value
+
+
+def fc_double_workspace(plan, n_nodes, n_edges, n_radial):
+    """bytes of workspace double_backward_fc needs"""
+    b = ctypes.c_size_t()
+    _check(lib().tp_conv_fc_double_workspace(plan.handle, n_nodes, n_edges, n_radial, ctypes.byref(b)))
+    return b.value
+
+
+def double_backward_fc(plan, graph, x, Y, R, Theta, grad_out, gg_x=None, gg_Y=None, gg_R=None, gg_Theta=None,
+                       want=("x", "Y", "R", "Theta", "g"), ws=None):
+    """(d_x, d_Y, d_R, d_Theta, d_grad_out): gradients of <gg_x, grad_x> + <gg_Y, grad_Y>
+    + <gg_R, grad_R> + <gg_Theta, grad_Theta> (the outputs of backward_fc) with respect
+    to its inputs; missing cotangents are zero, outputs not in ``want`` are None."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    H = R.shape[1]
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(R, "R", torch.float32, (E, H))
+    _need(Theta, "Theta", torch.float32, (H, plan.n_paths, plan.mul, plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    for t, like, name in ((gg_x, x, "gg_x"), (gg_Y, Y, "gg_Y"), (gg_R, R, "gg_R"), (gg_Theta, Theta, "gg_Theta")):
+        if t is not None:
+            _need(t, name, torch.float32, tuple(like.shape))
+    nbytes = fc_double_workspace(plan, N, E, H)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    elif ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
+    mk = lambda name, like: torch.empty_like(like) if name in want else None
+    dx, dY, dR, dT, dg = mk("x", x), mk("Y", Y), mk("R", R), mk("Theta", Theta), mk("g", grad_out)
+    g = graph.cstruct()
+    _check(lib().tp_conv_double_backward_fc(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(R), H,
+                                            _ptr(Theta), _ptr(grad_out), _ptr(gg_x), _ptr(gg_Y), _ptr(gg_R),
+                                            _ptr(gg_Theta), _ptr(dx), _ptr(dY), _ptr(dR), _ptr(dT), _ptr(dg),
+                                            _ptr(ws), ws.numel(), _stream(x.device)))
+    return dx, dY, dR, dT, dg
 
 
 def backward_fc(plan, graph, x, Y, R, Theta, grad_out, want=("x", "Y", "R", "Theta"), ws=None, outs=None,

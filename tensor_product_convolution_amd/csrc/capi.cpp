@@ -687,6 +687,70 @@ tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float
   return TP_OK;
 }
 
+tp_status tp_conv_fc_double_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_edges, int32_t n_radial,
+                                      size_t* bytes) {
+  if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_fc_double_workspace: NULL argument");
+  if (n_nodes < 0 || n_edges < 0) return set_error(TP_ERR_ARG, "tp_conv_fc_double_workspace: negative size");
+  const tpc::FcSet* fs = find_fc(plan, n_radial);
+  if (!fs || !fs->dbl_workspace)
+    return set_error(TP_ERR_UNSUPPORTED, "no compiled fully connected kernel (supported: 0e+1o+2e / "
+                                         "lmax 2 with 16 or 32 channels and 8 radial features)");
+  *bytes = fs->dbl_workspace(n_nodes, n_edges);
+  return TP_OK;
+}
+
+tp_status tp_conv_double_backward_fc(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                     const float* R, int32_t n_radial, const float* Theta,
+                                     const float* grad_out, const float* gg_x, const float* gg_Y,
+                                     const float* gg_R, const float* gg_Theta, float* d_x, float* d_Y,
+                                     float* d_R, float* d_Theta, float* d_grad_out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  const char* fn = "tp_conv_double_backward_fc";
+  if (!plan) return set_error(TP_ERR_ARG, std::string(fn) + ": plan is NULL");
+  size_t need = 0;
+  tp_status s = tp_conv_fc_double_workspace(plan, graph ? graph->n_nodes : 0, graph ? graph->n_edges : 0,
+                                            n_radial, &need);
+  if (s != TP_OK) return s;
+  s = check_graph(graph, d_x != nullptr);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && (!grad_out || !Theta)) return set_error(TP_ERR_ARG, std::string(fn) + ": grad_out/Theta NULL");
+  if (E > 0 && (!x || !Y || !R)) return set_error(TP_ERR_ARG, std::string(fn) + ": x/Y/R NULL");
+  if (ws_bytes < need || (need > 0 && !ws))
+    return set_error(TP_ERR_WORKSPACE, std::string(fn) + ": workspace too small");
+  if (misaligned16({ws, Theta, gg_Theta}))
+    return set_error(TP_ERR_ARG, std::string(fn) + ": ws, Theta and gg_Theta must be 16-byte aligned");
+  tpc::FcArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.outdim = plan->outdim;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_perm = graph->t_perm;
+  a.t_col = graph->t_col;
+  a.x = x;
+  a.Y = Y;
+  a.R = R;
+  a.Theta = Theta;
+  a.gout = grad_out;
+  a.ws = ws;
+  a.stream = stream;
+  tpc::FcDbl d;
+  d.gg_x = gg_x;
+  d.gg_Y = gg_Y;
+  d.gg_R = gg_R;
+  d.gg_Theta = gg_Theta;
+  d.d_x = d_x;
+  d.d_Y = d_Y;
+  d.d_R = d_R;
+  d.d_Theta = d_Theta;
+  d.d_g = d_grad_out;
+  hipError_t e = find_fc(plan, n_radial)->dbl(a, d);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_double_backward_fc launch");
+  return TP_OK;
+}
+
 // ---- Gaunt (spherical-grid) product -----------------------------------------
 static tp_status gaunt_supported(tp_plan_t plan, const char* who) {
   const int m = plan->mul;

@@ -900,9 +900,108 @@ hipError_t launch_fc_bwd(const FcArgs& a) {
   return hipGetLastError();
 }
 
+// ---- second-order backward --------------------------------------------------
+// out is linear in each of x, Y, R and Theta, so the gradients of
+// L = <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_R, grad_R> + <gg_Theta, grad_Theta>
+// are sums of first-order results with one operand replaced by its cotangent:
+// per present cotangent one forward (its term of d_grad_out) and one backward
+// (its terms of the other three gradients).  The first term of each output is
+// written in place, later ones go through a scratch row and are added.
+
+__global__ void __launch_bounds__(256) k_fc_acc(float* __restrict__ y, const float* __restrict__ x, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) y[i] += x[i];
+}
+__global__ void __launch_bounds__(256) k_fc_zero(float* __restrict__ y, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) y[i] = 0.f;
+}
+unsigned fc_elem_grid(long long n) {
+  const long long b = (n + 255) / 256;
+  return (unsigned)(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+
+size_t fc_align(size_t b) { return (b + 255) & ~size_t(255); }
+
+// scratch rows after the first-order workspace: d_grad_out, d_x, d_Y, d_R, d_Theta
+template <int U>
+size_t fc_dbl_ws(int n_nodes, int n_edges) {
+  return fc_align(fc_bwd_ws<U>(n_nodes)) + fc_align((size_t)n_nodes * SigF::OC * U * 4) +
+         fc_align((size_t)n_nodes * SigF::XC * U * 4) + fc_align((size_t)n_edges * SigF::YC * 4) +
+         fc_align((size_t)n_edges * kH * 4) + fc_align((size_t)kH * SigF::NP * U * U * 4);
+}
+
+struct FcAcc {
+  float* out;
+  float* tmp;
+  long long n;
+  bool first;
+  float* dest() const { return out ? (first ? out : tmp) : nullptr; }
+};
+
+template <int U>
+hipError_t launch_fc_dbl(const FcArgs& a, const FcDbl& d) {
+  const long long N = a.n_nodes, E = a.n_edges;
+  char* w = static_cast<char*>(a.ws) + fc_align(fc_bwd_ws<U>(a.n_nodes));
+  auto take = [&](size_t bytes) {
+    float* p = reinterpret_cast<float*>(w);
+    w += fc_align(bytes);
+    return p;
+  };
+  FcAcc ag{d.d_g, take((size_t)N * SigF::OC * U * 4), N * SigF::OC * U, true};
+  FcAcc ax{d.d_x, take((size_t)N * SigF::XC * U * 4), N * SigF::XC * U, true};
+  FcAcc aY{d.d_Y, take((size_t)E * SigF::YC * 4), E * SigF::YC, true};
+  FcAcc aR{d.d_R, take((size_t)E * kH * 4), E * kH, true};
+  FcAcc aT{d.d_Theta, take((size_t)kH * SigF::NP * U * U * 4), (long long)kH * SigF::NP * U * U, true};
+  auto done = [&](FcAcc& c) {
+    if (!c.out) return;
+    if (c.first) {
+      c.first = false;
+    } else {
+      hipLaunchKernelGGL(k_fc_acc, dim3(fc_elem_grid(c.n)), dim3(256), 0, a.stream, c.out, c.tmp, c.n);
+    }
+  };
+  if (N > 0 && E > 0) {
+    for (int which = 0; which < 4; ++which) {
+      const float* cot = which == 0 ? d.gg_x : which == 1 ? d.gg_Y : which == 2 ? d.gg_R : d.gg_Theta;
+      if (!cot) continue;
+      FcArgs f = a;
+      if (which == 0) f.x = cot;
+      if (which == 1) f.Y = cot;
+      if (which == 2) f.R = cot;
+      if (which == 3) f.Theta = cot;
+      if (ag.out) {
+        f.out = ag.dest();
+        hipError_t e = launch_fc_fwd<U>(f);
+        if (e != hipSuccess) return e;
+        done(ag);
+      }
+      FcArgs b = f;
+      b.out = nullptr;
+      b.state_saved = false;
+      b.grad_x = which == 0 ? nullptr : ax.dest();
+      b.grad_Y = which == 1 ? nullptr : aY.dest();
+      b.grad_R = which == 2 ? nullptr : aR.dest();
+      b.grad_Theta = which == 3 ? nullptr : aT.dest();
+      if (b.grad_x || b.grad_Y || b.grad_R || b.grad_Theta) {
+        hipError_t e = launch_fc_bwd<U>(b);
+        if (e != hipSuccess) return e;
+        if (which != 0) done(ax);
+        if (which != 1) done(aY);
+        if (which != 2) done(aR);
+        if (which != 3) done(aT);
+      }
+    }
+  }
+  // outputs that received no term are zero
+  for (FcAcc* c : {&ag, &ax, &aY, &aR, &aT})
+    if (c->out && c->first && c->n > 0)
+      hipLaunchKernelGGL(k_fc_zero, dim3(fc_elem_grid(c->n)), dim3(256), 0, a.stream, c->out, c->n);
+  return hipGetLastError();
+}
+
 template <int U>
 const FcSet* fc_set() {
-  static const FcSet s{&launch_fc_fwd<U>, &fc_ws<U>, kH, &launch_fc_bwd<U>, &fc_bwd_ws<U>};
+  static const FcSet s{&launch_fc_fwd<U>, &fc_ws<U>, kH, &launch_fc_bwd<U>, &fc_bwd_ws<U>,
+                       &launch_fc_dbl<U>, &fc_dbl_ws<U>};
   return &s;
 }
 

@@ -85,12 +85,20 @@ struct FcArgs {
   void* ws = nullptr;
   hipStream_t stream = nullptr;
 };
+// second-order backward: cotangents of (grad_x, grad_Y, grad_R, grad_Theta)
+// (NULL: zero) and outputs (NULL: skip); the FcArgs carry the first-order inputs
+struct FcDbl {
+  const float *gg_x = nullptr, *gg_Y = nullptr, *gg_R = nullptr, *gg_Theta = nullptr;
+  float *d_x = nullptr, *d_Y = nullptr, *d_R = nullptr, *d_Theta = nullptr, *d_g = nullptr;
+};
 struct FcSet {
   hipError_t (*fwd)(const FcArgs&) = nullptr;
   size_t (*workspace)(int n_nodes) = nullptr;
   int n_radial = 0;
   hipError_t (*bwd)(const FcArgs&) = nullptr;
   size_t (*bwd_workspace)(int n_nodes) = nullptr;
+  hipError_t (*dbl)(const FcArgs&, const FcDbl&) = nullptr;
+  size_t (*dbl_workspace)(int n_nodes, int n_edges) = nullptr;
 };
 const FcSet* fc_l012_s2(int mul, int n_radial);
 
