@@ -908,6 +908,13 @@ def bench_fc(args, torch, tpc, dev):
     step_ms = float(np.median(t))
     reps, rounds = 5, max(2, args.steps // 5)
     kt = {n: float(timed_kernel(lambda c, f=fn: f(), 1, reps, rounds).mean()) for n, fn in phases.items()}
+    # second-order backward, all four cotangents (here the first backward's outputs)
+    tpc.backward_fc(plan, g, x, Y, Rs, Tht, go, ws=wsb, outs=(gx, gY, gR, gT))
+    wsd = torch.empty(tpc.fc_double_workspace(plan, N, E, H), dtype=torch.uint8, device=dev)
+    dbl = lambda c: tpc.double_backward_fc(plan, g, x, Y, Rs, Tht, go, gg_x=gx, gg_Y=gY, gg_R=gR, gg_Theta=gT,
+                                           ws=wsd)
+    dbl(0)
+    dbl_ms = float(timed_kernel(dbl, 1, 3, rounds).mean())
     d3s = [2 * l3 + 1 for (_, _, l3, _) in plan.paths()]
     d1s = [2 * l1 + 1 for (l1, _, _, _) in plan.paths()]
     alg = fc_algorithmic(N, E, P, U, H, d3s, d1s, plan.xdim, plan.outdim, plan.ysh)
@@ -928,6 +935,10 @@ def bench_fc(args, torch, tpc, dev):
         "state_bytes": tpc.fc_workspace(plan, N, H),
         "backward_note": "the backward reads the state S the forward left in the shared workspace "
                          "(TP_FC_STATE_SAVED) instead of recomputing it",
+        "double_bwd_ms": dbl_ms,
+        "double_bwd_note": "second-order backward with cotangents on all four first-order outputs "
+                           "(four reassociated forwards and four backwards, one operand replaced in each); "
+                           "per call after a flush, not part of the step",
         "wall_s_timed_region": wall,
         "roofline": {"bound": "hbm", "kernel": f"{dom} (one entry-point call)",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

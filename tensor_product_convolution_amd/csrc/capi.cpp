@@ -275,7 +275,7 @@ tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lma
       delete p;
       return set_error(TP_ERR_UNSUPPORTED,
                        "no compiled radial-weight kernel for this signature (supported: 0e+1o+2e / "
-                       "lmax 2, multiplicity 16 or 128, 8 basis functions, 64 hidden units)");
+                       "lmax 2, multiplicity 16, 32, 64 or 128, 8 basis functions, 64 hidden units)");
     }
   }
   p->ks = tpc::find_kernels(ls, lmax_sh, lmax_out, p->mul);

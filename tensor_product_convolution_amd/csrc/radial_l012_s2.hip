@@ -192,6 +192,8 @@ const RadialSet* radial_l012_s2(int mul, int nb, int nh) {
   if (nb != kNB || nh != kNH) return nullptr;
   switch (mul) {
     case 16: return radial_set<16>();
+    case 32: return radial_set<32>();
+    case 64: return radial_set<64>();
     case 128: return radial_set<128>();
     default: return nullptr;
   }

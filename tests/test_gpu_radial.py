@@ -78,7 +78,8 @@ def _gpu_radial_fwd(tpc, plan, wl, mix=True):
 
 
 @pytest.mark.parametrize("U,name,n", [(16, "stream", 300), (128, "stream", 200),
-                                      (16, "zipf", 400), (128, "uniform", 150)])
+                                      (16, "zipf", 400), (128, "uniform", 150),
+                                      (32, "stream", 250), (64, "zipf", 300)])
 def test_radial_forward_parity(tpc, U, name, n):
     say(f"radial fwd U={U} graph={name} n={n}")
     gname = "lmax3" if name == "uniform" else name   # lmax3's graph: degree U{5..30}
@@ -142,7 +143,8 @@ def _check_params(op, res, ref, U):
 
 
 @pytest.mark.parametrize("U,name,n,mix", [(16, "stream", 300, True), (128, "stream", 120, True),
-                                          (16, "zipf", 400, False), (128, "uniform", 100, True)])
+                                          (16, "zipf", 400, False), (128, "uniform", 100, True),
+                                          (32, "stream", 200, True), (64, "uniform", 150, False)])
 def test_radial_backward_parity(tpc, U, name, n, mix):
     say(f"radial bwd U={U} graph={name} n={n} mix={mix}")
     gname = "lmax3" if name == "uniform" else name

@@ -97,7 +97,8 @@ def _check(op, res, ref, U, p, edges=None, nodes=None, recv=None):
 
 
 @pytest.mark.parametrize("U,name,n,mix", [(16, "stream", 300, True), (128, "stream", 120, True),
-                                          (16, "zipf", 400, False), (128, "uniform", 100, True)])
+                                          (16, "zipf", 400, False), (128, "uniform", 100, True),
+                                          (32, "zipf", 300, True), (64, "stream", 150, True)])
 def test_radial_double_backward_parity(tpc, U, name, n, mix):
     say(f"radial double bwd U={U} graph={name} n={n} mix={mix}")
     gname = "lmax3" if name == "uniform" else name
