@@ -114,7 +114,9 @@ typedef struct {
  * Builds the path list, output irreps and real CG tables of a channel-wise
  * ("uvu") tensor product of `irreps_in` (e.g. "32x0e+32x1o+32x2e": one shared
  * multiplicity, natural parity) with harmonics up to lmax_sh, keeping output
- * degrees up to lmax_out, and selects the compiled kernel specialisation.
+ * degrees up to lmax_out, and selects the compiled kernel specialisation
+ * (compiled: 0e+1o with lmax_sh = lmax_out = 1, 2 or 3; 0e+1o+2e with 2;
+ * 0e+1o+2e+3o with 3; multiplicity 8, 16, 32, 64 or 128).
  * Source: path-aggregated sparse CG product ("FlashTP", Abstract).
  * mode TP_MODE_GAUNT builds the plan of the Gaunt product instead (see
  * tp_conv_forward_gaunt: even couplings only, no CG table, nnz = 0).
@@ -219,7 +221,8 @@ tp_status tp_conv_forward(tp_plan_t plan, const tp_graph* graph, const float* x,
  * adjoint of the forward; "Sobek", Abstract, backward pass).  grad_x, grad_Y
  * or grad_w may be NULL to skip that output.  grad_x [N][xdim]; grad_Y
  * [E][ysh] and grad_w [E][P][U] in receiver-sorted order.  With grad_x and an
- * edge gradient requested (lmax-2 signatures) one sender-grouped pass forms
+ * edge gradient requested (signatures of at most 256 CG nonzeros: all but
+ * 0e+1o+2e+3o / lmax 3) one sender-grouped pass forms
  * all of them, reading w and Y once; otherwise a receiver pass (grad_w,
  * grad_Y) and a sender pass (grad_x).  grad_x needs the graph's sender
  * grouping.  x, w and grad_out must be 16-byte aligned (TP_ERR_ARG).

@@ -60,7 +60,9 @@ const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_o
 }
 
 const KernelSet* find_kernels(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul) {
+  if (ls == std::vector<int>{0, 1} && lmax_sh == 1 && lmax_out == 1) return kernels_l01_s1(mul);
   if (ls == std::vector<int>{0, 1} && lmax_sh == 2 && lmax_out == 2) return kernels_l01_s2(mul);
+  if (ls == std::vector<int>{0, 1} && lmax_sh == 3 && lmax_out == 3) return kernels_l01_s3(mul);
   if (ls == std::vector<int>{0, 1, 2} && lmax_sh == 2 && lmax_out == 2) return kernels_l012_s2(mul);
   if (ls == std::vector<int>{0, 1, 2, 3} && lmax_sh == 3 && lmax_out == 3)
     return kernels_l0123_s3(mul);
@@ -282,7 +284,7 @@ tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lma
   if (!p->ks) {
     delete p;
     return set_error(TP_ERR_UNSUPPORTED,
-                     "no compiled kernel for this signature (supported: 0e+1o / lmax 2, "
+                     "no compiled kernel for this signature (supported: 0e+1o / lmax 1, 2 or 3, "
                      "0e+1o+2e / lmax 2, 0e+1o+2e+3o / lmax 3; multiplicity 8, 16, 32, 64 or 128)");
   }
   *out = p;

@@ -129,7 +129,9 @@ const RadialSet* radial_l012_s2(int mul, int nb, int nh);
 const KernelSet* find_kernels(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul);
 
 // Per-signature registries (one translation unit each).
+const KernelSet* kernels_l01_s1(int mul);
 const KernelSet* kernels_l01_s2(int mul);
+const KernelSet* kernels_l01_s3(int mul);
 const KernelSet* kernels_l012_s2(int mul);
 const KernelSet* kernels_l0123_s3(int mul);
 

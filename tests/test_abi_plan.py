@@ -31,7 +31,8 @@ def test_library_exports_every_declared_symbol():
 
 CONFIGS = [("8x0e+8x1o", 2, 2), ("32x0e+32x1o+32x2e", 2, 2),
            ("64x0e+64x1o+64x2e+64x3o", 3, 3), ("128x0e+128x1o+128x2e", 2, 2),
-           ("16x0e+16x1o", 2, 2), ("64x0e+64x1o+64x2e", 2, 2)]
+           ("16x0e+16x1o", 2, 2), ("64x0e+64x1o+64x2e", 2, 2),
+           ("32x0e+32x1o", 1, 1), ("64x0e+64x1o", 3, 3)]
 
 
 @pytest.mark.parametrize("irreps,lsh,lout", CONFIGS)
