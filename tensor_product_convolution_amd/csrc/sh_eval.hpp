@@ -19,21 +19,24 @@
 
 namespace tpc {
 
-// (x, y, z) <- r / |r|, inv <- 1 / |r| (both 0 for r = 0); returns |r|
-__host__ __device__ __forceinline__ float unit_dir(float& x, float& y, float& z, float& inv) {
+// (x, y, z) <- r / |r|, inv <- 1 / |r|; returns |r|.  1/|r| is the hardware
+// reciprocal square root (about 1 ulp), |r| = |r|^2 / |r|; a vector whose
+// squared length is below the smallest normal float counts as zero (all three
+// results 0).
+__device__ __forceinline__ float unit_dir(float& x, float& y, float& z, float& inv) {
 #pragma clang fp contract(off)
   const float n2 = x * x + y * y + z * z;
-  const float len = sqrtf(n2);
-  inv = n2 > 0.f ? 1.0f / len : 0.f;
+  const bool nz = n2 >= 1.17549435e-38f;
+  inv = nz ? __builtin_amdgcn_rsqf(n2) : 0.f;
   x *= inv;
   y *= inv;
   z *= inv;
-  return len;
+  return n2 * inv;
 }
 
 // harmonics of the unit direction (x, y, z), (LMAX+1)^2 values
 template <int LMAX, int N>
-__host__ __device__ __forceinline__ void sh_eval(float x, float y, float z, float (&v)[N]) {
+__device__ __forceinline__ void sh_eval(float x, float y, float z, float (&v)[N]) {
 #pragma clang fp contract(off)
   static_assert(N >= (LMAX + 1) * (LMAX + 1), "room for every component");
   v[0] = 1.0f;
@@ -75,7 +78,7 @@ __host__ __device__ __forceinline__ void sh_eval(float x, float y, float z, floa
 // unit direction, 1/|r| and g = dL/dY, returns dL/dr = sum_b g_b dY_b/dr,
 // plus gl u for a gradient gl with respect to the length |r|.
 template <int LMAX, int N>
-__host__ __device__ __forceinline__ void sh_pullback(float x, float y, float z, float inv, const float (&g)[N],
+__device__ __forceinline__ void sh_pullback(float x, float y, float z, float inv, const float (&g)[N],
                                                      float gl, float (&gr)[3]) {
 #pragma clang fp contract(off)
   static_assert(N >= (LMAX + 1) * (LMAX + 1), "room for every component");

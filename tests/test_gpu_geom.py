@@ -131,9 +131,9 @@ def test_geom_full_size_against_y_form_and_oracle(tpc, name):
 
 
 def test_geom_zero_vectors_and_empty_graph(tpc):
-    """A zero edge vector has no direction: both forms use the harmonics'
-    polynomials at the origin (Y_0 = 1, the rest 0) and a zero gradient; an
-    empty graph gives zero outputs."""
+    """A zero edge vector has no direction: both forms evaluate the harmonics'
+    formulas at the zero direction (x = y = z = 0) and give it a zero gradient;
+    an empty graph gives zero outputs."""
     say("edge-vector form degenerate cases")
     plan, op = plans("mid")
     wl = make_workload("mid", dims_of(op), n_nodes=200)
