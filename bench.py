@@ -492,7 +492,18 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
             tpc.backward(plan, g, x, Y, w, go, outs=(gx, gYs[0], gws[0]))
 
     if args.counters:
-        counters_run(torch, dev, flush, step, name)
+        if fwd_only:
+            counters_run(torch, dev, flush, step, name)
+        else:
+            # the edge-vector step too, so the counters cover both forms
+            r_c = tpc.gather_rows(T(wl.r), g.perm)
+            gr_c = torch.empty_like(r_c)
+
+            def both():
+                step()
+                tpc.forward_r(plan, g, x, r_c, w, out=out)
+                tpc.backward_r(plan, g, x, r_c, w, go, outs=(gx, gr_c, gws[0]))
+            counters_run(torch, dev, flush, both, name)
         return None, step
     do_flush, timed_steps_of, timed_kernel = make_timers(torch, flush)
     timed_steps = lambda k, cold: timed_steps_of(step, k, cold)
@@ -597,6 +608,7 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
         ms_r = float(t_r.mean())
         res["edge_vector_step"] = {
             "ms_per_step": ms_r, "edges_per_s": E / (ms_r * 1e-3), "kernel_ms": kt_r,
+            "traffic": {n: (traffic or {}).get(n) for n in kt_r},
             "kernel_hbm_frac": {n: ab_r[n] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS for n, v in kt_r.items()},
             "step_hbm_frac": (ab_r["fwd_r"] + ab_r["bwd_r"]) / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": ab_r,
