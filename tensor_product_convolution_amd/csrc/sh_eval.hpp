@@ -10,10 +10,11 @@
 // (x, y, z): Y_0 = 1 and Y_1 = sqrt3 (y, z, x).  The polynomials are the
 // standard real harmonics of degree <= 3 scaled by sqrt(4 pi).
 //
-// Contraction of a * b + c into fused multiply-adds is switched off in these
-// functions: every operation rounds as written, so the harmonics (and their
-// pullback) are the same float32 values wherever they are inlined, whatever
-// the surrounding code lets the compiler share.
+// Contraction of a * b + c into fused multiply-adds is switched off in the
+// direction and the harmonics: every operation rounds as written, so the
+// harmonics are the same float32 values wherever they are inlined, whatever
+// the surrounding code lets the compiler share.  The pullback (a gradient,
+// compared to a tolerance, not bit for bit) may contract.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -80,7 +81,6 @@ __device__ __forceinline__ void sh_eval(float x, float y, float z, float (&v)[N]
 template <int LMAX, int N>
 __device__ __forceinline__ void sh_pullback(float x, float y, float z, float inv, const float (&g)[N],
                                                      float gl, float (&gr)[3]) {
-#pragma clang fp contract(off)
   static_assert(N >= (LMAX + 1) * (LMAX + 1), "room for every component");
   float gx = 0.f, gy = 0.f, gz = 0.f, lp = 0.f;   // sum g grad P, sum g l P
   if constexpr (LMAX >= 1) {
