@@ -269,3 +269,62 @@ def test_fc_and_gaunt_host_validation_without_launch():
     assert L.tp_conv_backward_fc(cg.handle, ctypes.byref(g), *args, 0, odd, 1 << 30, None) == -1
     assert L.tp_conv_backward_fc(cg.handle, ctypes.byref(gg), *args, 0, fake, 1 << 30, None) == -1
     assert L.tp_conv_backward_fc(p.handle, ctypes.byref(g), *args, 0, fake, 1 << 30, None) == -3
+
+
+def test_second_order_and_edge_vector_argument_errors_without_launch():
+    """Host validation of the radial and fully connected second-order backward
+    and of the edge-vector entry points: each case returns its status before
+    any HIP call."""
+    L = tpc.lib()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)                  # not 16-byte aligned
+    plain = tpc.Plan("16x0e+16x1o+16x2e", 2, 2)
+    rad = tpc.Plan("16x0e+16x1o+16x2e", 2, 2, radial=(8, 64, 5.0), uvw=True)
+    g = tpc._Graph(4, 10, fake, fake, fake, fake, fake, fake)
+    sz = ctypes.c_size_t()
+    # radial second order: workspace, then the entry point
+    assert L.tp_conv_radial_double_workspace(plain.handle, 4, 0, ctypes.byref(sz)) == -3
+    assert L.tp_conv_radial_double_workspace(rad.handle, -1, 0, ctypes.byref(sz)) == -1
+    assert L.tp_conv_radial_double_workspace(rad.handle, 4, 0, ctypes.byref(sz)) == 0 and sz.value > 0
+    base = sz.value
+    assert L.tp_conv_radial_double_workspace(rad.handle, 4, 1, ctypes.byref(sz)) == 0 and sz.value > base
+    # x, Y, r_len, W1, W2 | Wmix | grad_out | gg_x, gg_Y, gg_rlen | d_x, d_Y, d_rlen, d_W1, d_W2 | d_Wmix | d_g
+    args = [fake] * 5 + [None] + [fake] + [fake] * 3 + [fake] * 5 + [None] + [fake]
+    f = L.tp_conv_double_backward_radial
+    assert f(None, ctypes.byref(g), *args, fake, 1 << 30, None) == -1
+    assert f(plain.handle, ctypes.byref(g), *args, fake, 1 << 30, None) == -3
+    assert f(rad.handle, ctypes.byref(g), *args, fake, 16, None) == -5
+    bad = list(args)
+    bad[7] = odd                                   # gg_x
+    assert f(rad.handle, ctypes.byref(g), *bad, fake, 1 << 30, None) == -1
+    assert "aligned" in L.tp_conv_last_error().decode()
+    nomix = list(args)
+    nomix[15] = fake                               # d_Wmix without Wmix
+    assert f(rad.handle, ctypes.byref(g), *nomix, fake, 1 << 30, None) == -1
+    noy = list(args)
+    noy[1] = None                                  # Y with edges
+    assert f(rad.handle, ctypes.byref(g), *noy, fake, 1 << 30, None) == -1
+    # fully connected second order
+    assert L.tp_conv_fc_double_workspace(plain.handle, 4, 10, 3, ctypes.byref(sz)) == -3
+    assert L.tp_conv_fc_double_workspace(plain.handle, -1, 10, 8, ctypes.byref(sz)) == -1
+    assert L.tp_conv_fc_double_workspace(plain.handle, 4, 10, 8, ctypes.byref(sz)) == 0 and sz.value > 0
+    # x, Y, R | H | Theta, grad_out | gg_x, gg_Y, gg_R, gg_Theta | d_x, d_Y, d_R, d_Theta, d_g
+    fd = L.tp_conv_double_backward_fc
+    fargs = [fake] * 3 + [8] + [fake] * 2 + [fake] * 4 + [fake] * 5
+    assert fd(plain.handle, ctypes.byref(g), *fargs, fake, 16, None) == -5
+    bad = list(fargs)
+    bad[9] = odd                                   # gg_Theta
+    assert fd(plain.handle, ctypes.byref(g), *bad, fake, 1 << 30, None) == -1
+    bad = list(fargs)
+    bad[5] = None                                  # grad_out
+    assert fd(plain.handle, ctypes.byref(g), *bad, fake, 1 << 30, None) == -1
+    bad = list(fargs)
+    bad[3] = 3                                     # radial features not compiled
+    assert fd(plain.handle, ctypes.byref(g), *bad, fake, 1 << 30, None) == -3
+    # edge-vector forms
+    assert L.tp_conv_forward_r(plain.handle, ctypes.byref(g), odd, fake, fake, fake, None) == -1
+    assert L.tp_conv_forward_r(plain.handle, ctypes.byref(g), fake, None, fake, fake, None) == -1
+    assert L.tp_conv_backward_r(plain.handle, ctypes.byref(g), fake, fake, fake, odd, fake, fake, fake,
+                                None) == -1
+    assert L.tp_conv_forward_radial_r(plain.handle, ctypes.byref(g), fake, fake, fake, fake, None, None,
+                                      fake, None) == -3
