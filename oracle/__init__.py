@@ -43,7 +43,7 @@ from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, bessel_basis_deriv, r
                    bessel_basis_deriv2, silu_derivs, tp_conv_radial_double_bwd)
 from .fc import fc_conv_fwd, fc_conv_bwd, fc_conv_double_bwd
 from .gaunt import (sphere_quadrature, gaunt_coefficients, gaunt_plan, gaunt_conv_fwd,
-                    gaunt_conv_bwd)
+                    gaunt_conv_bwd, gaunt_conv_double_bwd)
 
 __all__ = [
     "parse_irreps", "build_plan", "OraclePlan", "cg_complex",
@@ -54,5 +54,5 @@ __all__ = [
     "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd", "bessel_basis_deriv2",
     "silu_derivs", "tp_conv_radial_double_bwd", "fc_conv_fwd",
     "fc_conv_bwd", "fc_conv_double_bwd", "sphere_quadrature", "gaunt_coefficients", "gaunt_plan", "gaunt_conv_fwd",
-    "gaunt_conv_bwd",
+    "gaunt_conv_bwd", "gaunt_conv_double_bwd",
 ]

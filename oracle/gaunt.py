@@ -192,3 +192,25 @@ def gaunt_conv_bwd(gp, src, dst, n_nodes, x, Y, w, g):
             gxe[:, xs] += np.einsum("abc,eb,euc,eu->eua", G, yb, gc, wl, optimize=True).reshape(n, -1)
         np.add.at(gx, src[e], gxe)
     return gx, gY, gw
+
+
+def gaunt_conv_double_bwd(gp, src, dst, n_nodes, x, Y, w, g, ggx=None, ggY=None, ggw=None):
+    """Second-order backward of the Gaunt convolution.  F(g, x, Y, w) =
+    <g, out> is linear in each argument, so for cotangents (ggx, ggY, ggw) of
+    the first backward's outputs (None: zero) the loss
+    L = <ggx, gx> + <ggY, gY> + <ggw, gw> equals
+    F(g, ggx, Y, w) + F(g, x, ggY, w) + F(g, x, Y, ggw), and each of its
+    gradients is a sum of first-order results with one operand replaced.
+    Returns (dx, dY, dw, dg)."""
+    x = np.asarray(x, dtype=np.float64)
+    Y = np.asarray(Y, dtype=np.float64)
+    E = len(src)
+    w = np.asarray(w, dtype=np.float64).reshape(E, gp.lmax_sh + 1, gp.U)
+    z = lambda a, like: np.zeros_like(like) if a is None else np.asarray(a, dtype=np.float64).reshape(like.shape)
+    ggx, ggY, ggw = z(ggx, x), z(ggY, Y), z(ggw, w)
+    args = (gp, src, dst, n_nodes)
+    dg = gaunt_conv_fwd(*args, ggx, Y, w) + gaunt_conv_fwd(*args, x, ggY, w) + gaunt_conv_fwd(*args, x, Y, ggw)
+    _, gY_x, gw_x = gaunt_conv_bwd(*args, ggx, Y, w, g)      # x -> ggx
+    gx_Y, _, gw_Y = gaunt_conv_bwd(*args, x, ggY, w, g)      # Y -> ggY
+    gx_w, gY_w, _ = gaunt_conv_bwd(*args, x, Y, ggw, g)      # w -> ggw
+    return gx_Y + gx_w, gY_x + gY_w, gw_x + gw_Y, dg

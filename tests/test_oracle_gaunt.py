@@ -245,3 +245,39 @@ def test_backward_central_differences():
             fm = f(args["x"], args["Y"], args["w"])
             num = (fp - fm) / (2 * h)
             assert abs(num - grad.reshape(-1)[k]) <= 1e-7 * max(1.0, abs(num)), (name, k)
+
+
+def test_double_backward_by_differences_and_multilinearity():
+    """The second-order backward: central differences of the first backward's
+    loss L = <ggx, gx> + <ggY, gY> + <ggw, gw> in each of x, Y, w and g (exact
+    up to rounding: every term is multilinear), <dg, g> = L, and missing
+    cotangents as zeros."""
+    from oracle.gaunt import gaunt_conv_double_bwd
+    gp, wl, Y, w = _case(n=10, U=3, seed=5)
+    w = np.asarray(w, dtype=np.float64).reshape(wl.n_edges, gp.lmax_sh + 1, gp.U)
+    rng = np.random.default_rng(6)
+    x = wl.x.astype(np.float64)
+    g = rng.normal(size=(wl.n_nodes, gp.outdim))
+    args = (gp, wl.src, wl.dst, wl.n_nodes)
+    cot = [rng.normal(size=a.shape) for a in (x, Y, w)]
+
+    def L(x_, Y_, w_, g_):
+        return float(sum(np.sum(c * v) for c, v in zip(cot, gaunt_conv_bwd(*args, x_, Y_, w_, g_))))
+
+    dx, dY, dw, dg = gaunt_conv_double_bwd(*args, x, Y, w, g, *cot)
+    h = 1e-3
+    base = [x, Y, w, g]
+    for which, grad in enumerate((dx, dY, dw, dg)):
+        d = rng.normal(size=base[which].shape)
+        up, dn = list(base), list(base)
+        up[which] = base[which] + h * d
+        dn[which] = base[which] - h * d
+        fd = (L(*up) - L(*dn)) / (2 * h)
+        an = float(np.sum(grad * d))
+        assert abs(fd - an) <= 1e-9 * max(1.0, abs(an)), which
+    Lv = L(x, Y, w, g)
+    assert abs(float(np.sum(dg * g)) - Lv) <= 1e-10 * max(1.0, abs(Lv))
+    a = gaunt_conv_double_bwd(*args, x, Y, w, g, cot[0], None, None)
+    b = gaunt_conv_double_bwd(*args, x, Y, w, g, cot[0], np.zeros_like(Y), np.zeros_like(w))
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
