@@ -1044,6 +1044,12 @@ def bench_gaunt(args, torch, tpc, dev):
     step_ms = float(np.median(t))
     reps, rounds = 10, max(2, args.steps // 5)
     kt = {n: float(timed_kernel(lambda c, f=fn: f(), 1, reps, rounds).mean()) for n, fn in kernels.items()}
+    # second-order backward, all three cotangents (here the first backward's outputs)
+    tpc.backward_gaunt(plan, g, x, Y, ws_, go, outs=(gx, gY, gw))
+    wsd = torch.empty(tpc.gaunt_double_workspace(plan, N, E), dtype=torch.uint8, device=dev)
+    dbl = lambda c: tpc.double_backward_gaunt(plan, g, x, Y, ws_, go, gg_x=gx, gg_Y=gY, gg_w=gw, ws=wsd)
+    dbl(0)
+    dbl_ms = float(timed_kernel(dbl, 1, 3, rounds).mean())
     alg = gaunt_algorithmic(N, E, U, plan.xdim, plan.ysh, wdim, outdim)
     dom = max(kt, key=kt.get)
     tfs = alg[dom]["flops"] / (kt[dom] * 1e-3) / 1e12
@@ -1060,6 +1066,10 @@ def bench_gaunt(args, torch, tpc, dev):
         "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
         "kernel_ms": kt,
         "fwd_edges_per_s": E / (kt["fwd"] * 1e-3),
+        "double_bwd_ms": dbl_ms,
+        "double_bwd_note": "second-order backward with cotangents on all three first-order outputs "
+                           "(three grid forwards and three grid backwards, one operand replaced in each); "
+                           "per call after a flush, not part of the step",
         "compulsory_bytes": alg["step_bytes"],
         "hbm_frac_step": alg["step_bytes"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "hbm_frac_per_kernel": {n: alg[n]["bytes"] / (kt[n] * 1e-3) / 1e9 / HBM_PEAK_GBS for n in kt},

@@ -386,6 +386,25 @@ tp_status tp_conv_backward_gaunt(tp_plan_t plan, const tp_graph* graph, const fl
                                  const float* w, const float* grad_out, float* grad_x, float* grad_Y,
                                  float* grad_w, hipStream_t stream);
 
+/* Second-order backward of the Gaunt product ("Sobek", Abstract: forward,
+ * backward and double backward).  Given the inputs of tp_conv_backward_gaunt
+ * and cotangents gg_x [N][xdim], gg_Y [E][ysh], gg_w [E][wdim] of its outputs
+ * (any may be NULL: zero), returns the gradients of
+ *   L = <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_w, grad_w>:
+ * the product is linear in each of x, Y and w, so
+ *   d_grad_out = out(gg_x, Y, w) + out(x, gg_Y, w) + out(x, Y, gg_w)
+ * and d_x, d_Y, d_w are each the sum of the first backward's result with one
+ * of the other operands replaced by its cotangent (one grid forward and one
+ * grid backward per present cotangent).  Outputs may be NULL to skip them
+ * and get zeros when no cotangent reaches them; ws:
+ * tp_conv_gaunt_double_workspace bytes (one scratch row per output); w and
+ * gg_w 16-byte aligned; d_x needs the graph's sender grouping.  Deterministic. */
+tp_status tp_conv_gaunt_double_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_edges, size_t* bytes);
+tp_status tp_conv_double_backward_gaunt(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                        const float* w, const float* grad_out, const float* gg_x,
+                                        const float* gg_Y, const float* gg_w, float* d_x, float* d_Y, float* d_w,
+                                        float* d_grad_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- channel mix ("uvw", dense; fp32 MFMA) ----------------------------------
  * One U x U matrix per output irrep k (Wmix [K][U][U], K = number of output
  * irreps, U = 16, 32, 64 or 128; 1e and 1o never mix):

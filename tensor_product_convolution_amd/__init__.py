@@ -35,6 +35,7 @@ EXPORTS = (
     "tp_conv_radial_double_workspace", "tp_conv_sph_harm_backward", "tp_conv_double_backward", "tp_conv_fc_workspace",
     "tp_conv_forward_fc", "tp_conv_fc_backward_workspace", "tp_conv_backward_fc", "tp_conv_fc_double_workspace",
     "tp_conv_double_backward_fc", "tp_conv_gaunt_dims", "tp_conv_forward_gaunt", "tp_conv_backward_gaunt",
+    "tp_conv_gaunt_double_workspace", "tp_conv_double_backward_gaunt",
     "tp_conv_last_error",
 )
 
@@ -108,6 +109,8 @@ def lib():
         "tp_conv_fc_double_workspace": (I32, [P, I32, I32, I32, ctypes.POINTER(SZ)]),
         "tp_conv_double_backward_fc": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, I32] + [VP] * 11
                                        + [VP, SZ, VP]),
+        "tp_conv_gaunt_double_workspace": (I32, [P, I32, I32, ctypes.POINTER(SZ)]),
+        "tp_conv_double_backward_gaunt": (I32, [P, ctypes.POINTER(_Graph)] + [VP] * 11 + [VP, SZ, VP]),
         "tp_conv_gaunt_dims": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "tp_conv_forward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_backward_gaunt": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
@@ -497,6 +500,45 @@ def backward_gaunt(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=No
     _check(lib().tp_conv_backward_gaunt(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
                                         _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw), _stream(x.device)))
     return gx, gY, gw
+
+
+def gaunt_double_workspace(plan, n_nodes, n_edges):
+    """bytes of workspace double_backward_gaunt needs"""
+    b = ctypes.c_size_t()
+    _check(lib().tp_conv_gaunt_double_workspace(plan.handle, n_nodes, n_edges, ctypes.byref(b)))
+    return b.value
+
+
+def double_backward_gaunt(plan, graph, x, Y, w, grad_out, gg_x=None, gg_Y=None, gg_w=None,
+                          want=("x", "Y", "w", "g"), ws=None):
+    """(d_x, d_Y, d_w, d_grad_out): gradients of <gg_x, grad_x> + <gg_Y, grad_Y> +
+    <gg_w, grad_w> (the outputs of backward_gaunt) with respect to its inputs;
+    missing cotangents are zero, outputs not in ``want`` are None."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    outdim, wdim, _ = gaunt_dims(plan)
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(w, "w", torch.float32, tuple(w.shape))
+    if w.numel() != E * wdim:
+        raise ValueError(f"w has {w.numel()} elements, expected {E * wdim}")
+    _need(grad_out, "grad_out", torch.float32, (N, outdim))
+    for t, like, name in ((gg_x, x, "gg_x"), (gg_Y, Y, "gg_Y"), (gg_w, w, "gg_w")):
+        if t is not None:
+            _need(t, name, torch.float32, tuple(like.shape))
+    nbytes = gaunt_double_workspace(plan, N, E)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    elif ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
+    mk = lambda name, like: torch.empty_like(like) if name in want else None
+    dx, dY, dw, dg = mk("x", x), mk("Y", Y), mk("w", w), mk("g", grad_out)
+    g = graph.cstruct()
+    _check(lib().tp_conv_double_backward_gaunt(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
+                                               _ptr(grad_out), _ptr(gg_x), _ptr(gg_Y), _ptr(gg_w), _ptr(dx),
+                                               _ptr(dY), _ptr(dw), _ptr(dg), _ptr(ws), ws.numel(),
+                                               _stream(x.device)))
+    return dx, dY, dw, dg
 
 
 def fc_backward_workspace(plan, n_nodes, n_radial):

@@ -851,6 +851,71 @@ tp_status tp_conv_backward_gaunt(tp_plan_t plan, const tp_graph* graph, const fl
   return TP_OK;
 }
 
+static tpc::GauntArgs gaunt_args(tp_plan_t plan, const tp_graph* graph, int N, int E) {
+  tpc::GauntArgs a;
+  a.n_nodes = N;
+  a.n_edges = E;
+  a.U = plan->mul;
+  a.n_in = (int)plan->ls.size();
+  for (int b = 0; b < a.n_in; ++b) a.deg[b] = plan->ls[b];
+  a.lmax_sh = plan->lmax_sh;
+  a.lmax_out = plan->lmax_out;
+  if (graph) {
+    a.row_ptr = graph->row_ptr;
+    a.col = graph->col;
+    a.t_row_ptr = graph->t_row_ptr;
+    a.t_perm = graph->t_perm;
+    a.t_col = graph->t_col;
+  }
+  return a;
+}
+
+tp_status tp_conv_gaunt_double_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_edges, size_t* bytes) {
+  if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_gaunt_double_workspace: NULL argument");
+  tp_status s = gaunt_supported(plan, "tp_conv_gaunt_double_workspace");
+  if (s != TP_OK) return s;
+  if (n_nodes < 0 || n_edges < 0) return set_error(TP_ERR_ARG, "tp_conv_gaunt_double_workspace: negative size");
+  *bytes = tpc::gaunt_double_workspace(gaunt_args(plan, nullptr, n_nodes, n_edges));
+  return TP_OK;
+}
+
+tp_status tp_conv_double_backward_gaunt(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                                        const float* w, const float* grad_out, const float* gg_x,
+                                        const float* gg_Y, const float* gg_w, float* d_x, float* d_Y, float* d_w,
+                                        float* d_grad_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "tp_conv_double_backward_gaunt";
+  if (!plan) return set_error(TP_ERR_ARG, std::string(fn) + ": plan is NULL");
+  tp_status s = gaunt_supported(plan, fn);
+  if (s != TP_OK) return s;
+  s = check_graph(graph, d_x != nullptr);
+  if (s != TP_OK) return s;
+  const int N = graph->n_nodes, E = graph->n_edges;
+  if (N > 0 && !grad_out) return set_error(TP_ERR_ARG, std::string(fn) + ": grad_out NULL");
+  if (E > 0 && (!x || !Y || !w)) return set_error(TP_ERR_ARG, std::string(fn) + ": x/Y/w NULL");
+  if (misaligned16({w, gg_w})) return set_error(TP_ERR_ARG, std::string(fn) + ": w and gg_w must be 16-byte aligned");
+  tpc::GauntArgs a = gaunt_args(plan, graph, N, E);
+  const size_t need = tpc::gaunt_double_workspace(a);
+  if (ws_bytes < need || (need > 0 && !ws))
+    return set_error(TP_ERR_WORKSPACE, std::string(fn) + ": workspace too small");
+  a.x = x;
+  a.Y = Y;
+  a.w = w;
+  a.gout = grad_out;
+  a.stream = stream;
+  tpc::GauntDbl d;
+  d.gg_x = gg_x;
+  d.gg_Y = gg_Y;
+  d.gg_w = gg_w;
+  d.d_x = d_x;
+  d.d_Y = d_Y;
+  d.d_w = d_w;
+  d.d_g = d_grad_out;
+  d.ws = ws;
+  hipError_t e = tpc::gaunt_double_backward(a, d);
+  if (e != hipSuccess) return tpc::hip_error(e, "tp_conv_double_backward_gaunt launch");
+  return TP_OK;
+}
+
 static tp_status need_uvw(tp_plan_t plan) {
   const int m = plan->mul;
   if (m > 128 || (m & (m - 1)) || m < 16 || plan->outs.size() > 8)

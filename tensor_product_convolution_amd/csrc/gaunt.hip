@@ -734,4 +734,102 @@ hipError_t gaunt_backward(const GauntArgs& a) {
   }
 }
 
+// ---- second-order backward ---------------------------------------------------
+// out is linear in each of x, Y and w, so the gradients of
+// L = <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_w, grad_w> are sums of first-order
+// results with one operand replaced by its cotangent: per present cotangent
+// one forward (its term of d_grad_out) and one backward (its terms of the
+// other two gradients).  The first term of each output is written in place,
+// later ones go through a scratch row and are added.
+
+namespace {
+__global__ void __launch_bounds__(256) k_gaunt_acc(float* __restrict__ y, const float* __restrict__ x,
+                                                   long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) y[i] += x[i];
+}
+__global__ void __launch_bounds__(256) k_gaunt_zero(float* __restrict__ y, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) y[i] = 0.f;
+}
+unsigned gaunt_elem_grid(long long n) {
+  const long long b = (n + 255) / 256;
+  return (unsigned)(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+long long align64(long long n) { return (n + 63) & ~63LL; }   // floats: 256-byte steps
+
+struct GauntAcc {
+  float* out;
+  float* tmp;
+  long long n;
+  bool first;
+  float* dest() const { return out ? (first ? out : tmp) : nullptr; }
+};
+
+// element counts of d_grad_out, d_x, d_Y and d_w
+void gaunt_dbl_sizes(const GauntArgs& a, long long (&n)[4]) {
+  int xc = 0;
+  for (int b = 0; b < a.n_in; ++b) xc += 2 * a.deg[b] + 1;
+  n[0] = (long long)a.n_nodes * a.U * (a.lmax_out + 1) * (a.lmax_out + 1);
+  n[1] = (long long)a.n_nodes * a.U * xc;
+  n[2] = (long long)a.n_edges * (a.lmax_sh + 1) * (a.lmax_sh + 1);
+  n[3] = (long long)a.n_edges * (a.lmax_sh + 1) * a.U;
+}
+}  // namespace
+
+size_t gaunt_double_workspace(const GauntArgs& a) {
+  long long n[4];
+  gaunt_dbl_sizes(a, n);
+  return (size_t)(align64(n[0]) + align64(n[1]) + align64(n[2]) + align64(n[3])) * sizeof(float);
+}
+
+hipError_t gaunt_double_backward(const GauntArgs& a, const GauntDbl& d) {
+  long long n[4];
+  gaunt_dbl_sizes(a, n);
+  float* t = static_cast<float*>(d.ws);
+  GauntAcc acc[4] = {{d.d_g, t, n[0], true}, {d.d_x, t + align64(n[0]), n[1], true},
+                     {d.d_Y, t + align64(n[0]) + align64(n[1]), n[2], true},
+                     {d.d_w, t + align64(n[0]) + align64(n[1]) + align64(n[2]), n[3], true}};
+  GauntAcc &ag = acc[0], &ax = acc[1], &aY = acc[2], &aw = acc[3];
+  auto done = [&](GauntAcc& c) {
+    if (!c.out) return;
+    if (c.first) {
+      c.first = false;
+    } else {
+      hipLaunchKernelGGL(k_gaunt_acc, dim3(gaunt_elem_grid(c.n)), dim3(256), 0, a.stream, c.out, c.tmp, c.n);
+    }
+  };
+  if (a.n_nodes > 0 && a.n_edges > 0) {
+    for (int which = 0; which < 3; ++which) {
+      const float* cot = which == 0 ? d.gg_x : which == 1 ? d.gg_Y : d.gg_w;
+      if (!cot) continue;
+      GauntArgs f = a;
+      if (which == 0) f.x = cot;
+      if (which == 1) f.Y = cot;
+      if (which == 2) f.w = cot;
+      if (ag.out) {
+        f.out = ag.dest();
+        hipError_t e = gaunt_forward(f);
+        if (e != hipSuccess) return e;
+        done(ag);
+      }
+      GauntArgs b = f;
+      b.out = nullptr;
+      b.grad_x = which == 0 ? nullptr : ax.dest();
+      b.grad_Y = which == 1 ? nullptr : aY.dest();
+      b.grad_w = which == 2 ? nullptr : aw.dest();
+      if (b.grad_x || b.grad_Y || b.grad_w) {
+        hipError_t e = gaunt_backward(b);
+        if (e != hipSuccess) return e;
+        if (which != 0) done(ax);
+        if (which != 1) done(aY);
+        if (which != 2) done(aw);
+      }
+    }
+  }
+  // outputs that received no term are zero
+  for (GauntAcc& c : acc)
+    if (c.out && c.first && c.n > 0)
+      hipLaunchKernelGGL(k_gaunt_zero, dim3(gaunt_elem_grid(c.n)), dim3(256), 0, a.stream, c.out, c.n);
+  return hipGetLastError();
+}
+
 }  // namespace tpc

@@ -118,6 +118,15 @@ struct GauntArgs {
 };
 hipError_t gaunt_forward(const GauntArgs& a);
 hipError_t gaunt_backward(const GauntArgs& a);
+// second-order backward: cotangents of (grad_x, grad_Y, grad_w) (NULL: zero),
+// outputs (NULL: skip) and scratch of gaunt_double_workspace bytes
+struct GauntDbl {
+  const float *gg_x = nullptr, *gg_Y = nullptr, *gg_w = nullptr;
+  float *d_x = nullptr, *d_Y = nullptr, *d_w = nullptr, *d_g = nullptr;
+  void* ws = nullptr;
+};
+hipError_t gaunt_double_backward(const GauntArgs& a, const GauntDbl& d);
+size_t gaunt_double_workspace(const GauntArgs& a);
 int gaunt_grid_points();
 
 const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul, int nb,

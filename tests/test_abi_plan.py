@@ -328,3 +328,30 @@ def test_second_order_and_edge_vector_argument_errors_without_launch():
                                 None) == -1
     assert L.tp_conv_forward_radial_r(plain.handle, ctypes.byref(g), fake, fake, fake, fake, None, None,
                                       fake, None) == -3
+
+
+def test_gaunt_second_order_argument_errors_without_launch():
+    L = tpc.lib()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    plain = tpc.Plan("16x0e+16x1o+16x2e", 2, 2)
+    gaunt = tpc.Plan("16x0e+16x1o+16x2e", 2, 2, mode=tpc.TP_MODE_GAUNT)
+    g = tpc._Graph(4, 10, fake, fake, fake, fake, fake, fake)
+    sz = ctypes.c_size_t()
+    assert L.tp_conv_gaunt_double_workspace(plain.handle, 4, 10, ctypes.byref(sz)) == -3
+    assert L.tp_conv_gaunt_double_workspace(gaunt.handle, 4, -1, ctypes.byref(sz)) == -1
+    assert L.tp_conv_gaunt_double_workspace(gaunt.handle, 4, 10, ctypes.byref(sz)) == 0
+    # d_grad_out, d_x, d_Y, d_w rows: 4 x 144, 4 x 144, 10 x 9, 10 x 48 floats, each 256-byte aligned
+    assert sz.value == 4 * (576 + 576 + 128 + 512)
+    # x, Y, w, grad_out | gg_x, gg_Y, gg_w | d_x, d_Y, d_w, d_g
+    args = [fake] * 4 + [fake] * 3 + [fake] * 4
+    f = L.tp_conv_double_backward_gaunt
+    assert f(None, ctypes.byref(g), *args, fake, 1 << 30, None) == -1
+    assert f(plain.handle, ctypes.byref(g), *args, fake, 1 << 30, None) == -3
+    assert f(gaunt.handle, ctypes.byref(g), *args, fake, 16, None) == -5
+    bad = list(args)
+    bad[6] = odd                                   # gg_w
+    assert f(gaunt.handle, ctypes.byref(g), *bad, fake, 1 << 30, None) == -1
+    bad = list(args)
+    bad[3] = None                                  # grad_out
+    assert f(gaunt.handle, ctypes.byref(g), *bad, fake, 1 << 30, None) == -1
