@@ -86,6 +86,67 @@ __device__ __forceinline__ void load_o_channel(const float* __restrict__ g, int 
   });
 }
 
+// The distinct nontrivial coefficient magnitudes (|C| != 1) of one path per
+// output component, and for each nonzero the slot of its (c, |C|) (-1 for
+// |C| = 1).
+template <int L1, int L2, int L3>
+struct CgScaled {
+  using T = CgPath<L1, L2, L3>;
+  struct Tab {
+    int c[T::nnz > 0 ? T::nnz : 1];
+    float m[T::nnz > 0 ? T::nnz : 1];
+    int slot[T::nnz > 0 ? T::nnz : 1];
+    int n;
+  };
+  static constexpr Tab build() {
+    Tab t{};
+    t.n = 0;
+    for (int k = 0; k < T::nnz; ++k) {
+      const Nz e = T::table.e[k];
+      const float m = e.v < 0.f ? -e.v : e.v;
+      if (m == 1.f) {
+        t.slot[k] = -1;
+        continue;
+      }
+      int s = -1;
+      for (int q = 0; q < t.n; ++q)
+        if (t.c[q] == e.c && t.m[q] == m) s = q;
+      if (s < 0) {
+        s = t.n;
+        t.c[t.n] = e.c;
+        t.m[t.n] = m;
+        ++t.n;
+      }
+      t.slot[k] = s;
+    }
+    return t;
+  }
+  static constexpr Tab tab = build();
+};
+
+// z[b] = sum_{a,c} C[a,b,c] x[XO + a] g[GO + c] for one path and one channel,
+// the Z-form of the adjoint: g scaled by each distinct nontrivial |C| of the
+// path once, then one signed multiply-add per nonzero (instead of forming
+// t[b][c] = sum_a C x_a and then z[b] = sum_c t[b][c] g_c)
+template <int L1, int L2, int L3, int XO, int GO, int NX, int NG>
+__device__ __forceinline__ void zform_scaled(const float (&x)[NX], const float (&g)[NG], float (&z)[2 * L2 + 1]) {
+  using T = CgPath<L1, L2, L3>;
+  using CS = CgScaled<L1, L2, L3>;
+  constexpr int NS = CS::tab.n;
+  float gs[NS > 0 ? NS : 1];
+  static_for<NS>([&](auto Q) { gs[Q] = CS::tab.m[Q] * g[GO + CS::tab.c[Q]]; });
+  static_for<2 * L2 + 1>([&](auto B) { z[B] = 0.f; });
+  static_for<T::nnz>([&](auto N) {
+    constexpr Nz e = T::table.e[N];
+    constexpr int sl = CS::tab.slot[N];
+    float gv;
+    if constexpr (sl < 0) gv = g[GO + e.c];
+    else gv = gs[sl];
+    if constexpr (e.v < 0.f) z[e.b] = fmaf(-x[XO + e.a], gv, z[e.b]);
+    else z[e.b] = fmaf(x[XO + e.a], gv, z[e.b]);
+  });
+}
+
 // sum over the four lanes that share l%16 (lanes l, l^16, l^32, l^48)
 template <int N>
 __device__ __forceinline__ void reduce_quads(float (&v)[N]) {
@@ -320,26 +381,12 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
           });
           float gw[4];
           static_for<4>([&](auto R) {
-            // z[b] = sum_c g_c sum_a C_abc x_a (contracting x first keeps the
-            // temporaries local to the path)
-            float t[D2][D3];
-            static_for<D2>([&](auto B2) {
-              static_for<D3>([&](auto C3) {
-                if constexpr (T::has_bc(B2, C3)) t[B2][C3] = 0.f;
-              });
-            });
-            static_for<T::nnz>([&](auto N) {
-              constexpr Nz e = T::table.e[N];
-              t[e.b][e.c] = fmaf(e.v, xr[R][pi.xo + e.a], t[e.b][e.c]);
-            });
+            float z[D2];
+            zform_scaled<pi.l1, pi.l2, pi.l3, pi.xo, R * D3>(xr[R], gb, z);
             float s = 0.f;
             static_for<D2>([&](auto B2) {
-              float z = 0.f;
-              static_for<D3>([&](auto C3) {
-                if constexpr (T::has_bc(B2, C3)) z = fmaf(t[B2][C3], gb[R * D3 + C3], z);
-              });
-              s = fmaf(yr[pi.yo + B2], z, s);
-              gy[pi.yo + B2] = fmaf(w[int(R)], z, gy[pi.yo + B2]);
+              s = fmaf(yr[pi.yo + B2], z[B2], s);
+              gy[pi.yo + B2] = fmaf(w[int(R)], z[B2], gy[pi.yo + B2]);
             });
             gw[R] = s;
           });
@@ -519,26 +566,11 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
         radial_edge_y<S, GEOM>(Y, qc, yr);
         static_for<S::NP>([&](auto P) {
           constexpr PathInfo pi = S::paths.p[P];
-          using T = CgPath<pi.l1, pi.l2, pi.l3>;
-          constexpr int D2 = 2 * pi.l2 + 1, D3 = 2 * pi.l3 + 1;
-          float tt[D2][D3];
-          static_for<D2>([&](auto B2) {
-            static_for<D3>([&](auto C3) {
-              if constexpr (T::has_bc(B2, C3)) tt[B2][C3] = 0.f;
-            });
-          });
-          static_for<T::nnz>([&](auto N) {
-            constexpr Nz e = T::table.e[N];
-            tt[e.b][e.c] = fmaf(e.v, xr[pi.xo + e.a], tt[e.b][e.c]);
-          });
+          constexpr int D2 = 2 * pi.l2 + 1;
+          float z[D2];
+          zform_scaled<pi.l1, pi.l2, pi.l3, pi.xo, pi.ko>(xr, gr, z);
           float s = 0.f;
-          static_for<D2>([&](auto B2) {
-            float z = 0.f;
-            static_for<D3>([&](auto C3) {
-              if constexpr (T::has_bc(B2, C3)) z = fmaf(tt[B2][C3], gr[pi.ko + C3], z);
-            });
-            s = fmaf(yr[pi.yo + B2], z, s);
-          });
+          static_for<D2>([&](auto B2) { s = fmaf(yr[pi.yo + B2], z[B2], s); });
           gw_own[P * PS + (4 * g + r) * RS + e16] = s;
         });
         __builtin_amdgcn_sched_barrier(0);
