@@ -326,25 +326,13 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1,
           });
           float dw[4], dv[4];
           static_for<4>([&](auto R) {
-            float tx[D2][D3];
-            static_for<D2>([&](auto B2) {
-              static_for<D3>([&](auto C3) {
-                if constexpr (T::has_bc(B2, C3)) tx[B2][C3] = 0.f;
-              });
-            });
-            static_for<T::nnz>([&](auto N) {
-              constexpr Nz e = T::table.e[N];
-              tx[e.b][e.c] = fmaf(e.v, xr[R][pi.xo + e.a], tx[e.b][e.c]);
-            });
+            float zx[D2];
+            zform_scaled<pi.l1, pi.l2, pi.l3, pi.xo, R * D3>(xr[R], gb, zx);
             float sw = 0.f, sv = 0.f;
             static_for<D2>([&](auto B2) {
-              float zx = 0.f;
-              static_for<D3>([&](auto C3) {
-                if constexpr (T::has_bc(B2, C3)) zx = fmaf(tx[B2][C3], gb[R * D3 + C3], zx);
-              });
-              sw = fmaf(gyr[pi.yo + B2], zx, sw);
-              sv = fmaf(yr[pi.yo + B2], zx, sv);
-              dy[pi.yo + B2] = fmaf(v[int(R)], zx, dy[pi.yo + B2]);
+              sw = fmaf(gyr[pi.yo + B2], zx[B2], sw);
+              sv = fmaf(yr[pi.yo + B2], zx[B2], sv);
+              dy[pi.yo + B2] = fmaf(v[int(R)], zx[B2], dy[pi.yo + B2]);
             });
             dw[R] = sw;
             dv[R] = sv;
@@ -386,24 +374,12 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1,
             });
             float dw[4];
             static_for<4>([&](auto R) {
-              float tg[D2][D3];
-              static_for<D2>([&](auto B2) {
-                static_for<D3>([&](auto C3) {
-                  if constexpr (T::has_bc(B2, C3)) tg[B2][C3] = 0.f;
-                });
-              });
-              static_for<T::nnz>([&](auto N) {
-                constexpr Nz e = T::table.e[N];
-                tg[e.b][e.c] = fmaf(e.v, xr[R][pi.xo + e.a], tg[e.b][e.c]);
-              });
+              float zg[D2];
+              zform_scaled<pi.l1, pi.l2, pi.l3, pi.xo, R * D3>(xr[R], gb, zg);
               float sw = 0.f;
               static_for<D2>([&](auto B2) {
-                float zg = 0.f;
-                static_for<D3>([&](auto C3) {
-                  if constexpr (T::has_bc(B2, C3)) zg = fmaf(tg[B2][C3], gb[R * D3 + C3], zg);
-                });
-                sw = fmaf(yr[pi.yo + B2], zg, sw);
-                dy[pi.yo + B2] = fmaf(w[int(R)], zg, dy[pi.yo + B2]);
+                sw = fmaf(yr[pi.yo + B2], zg[B2], sw);
+                dy[pi.yo + B2] = fmaf(w[int(R)], zg[B2], dy[pi.yo + B2]);
               });
               dw[R] = sw;
             });
@@ -590,38 +566,20 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
         }
         static_for<S::NP>([&](auto P) {
           constexpr PathInfo pi = S::paths.p[P];
-          using T = CgPath<pi.l1, pi.l2, pi.l3>;
-          constexpr int D2 = 2 * pi.l2 + 1, D3 = 2 * pi.l3 + 1;
-          float tx[D2][D3], tg[D2][D3];
-          static_for<D2>([&](auto B2) {
-            static_for<D3>([&](auto C3) {
-              if constexpr (T::has_bc(B2, C3)) {
-                tx[B2][C3] = 0.f;
-                tg[B2][C3] = 0.f;
-              }
-            });
-          });
-          static_for<T::nnz>([&](auto N) {
-            constexpr Nz e = T::table.e[N];
-            tx[e.b][e.c] = fmaf(e.v, xr[pi.xo + e.a], tx[e.b][e.c]);
-            if constexpr (KIND == 0) tg[e.b][e.c] = fmaf(e.v, gxr[pi.xo + e.a], tg[e.b][e.c]);
-          });
+          constexpr int D2 = 2 * pi.l2 + 1;
+          float zx[D2];
+          zform_scaled<pi.l1, pi.l2, pi.l3, pi.xo, pi.ko>(xr, gr, zx);
           float s = 0.f;
-          static_for<D2>([&](auto B2) {
-            float zx = 0.f, zg = 0.f;
-            static_for<D3>([&](auto C3) {
-              if constexpr (T::has_bc(B2, C3)) {
-                zx = fmaf(tx[B2][C3], gr[pi.ko + C3], zx);
-                if constexpr (KIND == 0) zg = fmaf(tg[B2][C3], gr[pi.ko + C3], zg);
-              }
+          if constexpr (KIND == 0) {
+            float zg[D2];
+            zform_scaled<pi.l1, pi.l2, pi.l3, pi.xo, pi.ko>(gxr, gr, zg);
+            static_for<D2>([&](auto B2) {
+              s = fmaf(yr[pi.yo + B2], zg[B2], s);
+              s = fmaf(gyr[pi.yo + B2], zx[B2], s);
             });
-            if constexpr (KIND == 0) {
-              s = fmaf(yr[pi.yo + B2], zg, s);
-              s = fmaf(gyr[pi.yo + B2], zx, s);
-            } else {
-              s = fmaf(yr[pi.yo + B2], zx, s);
-            }
-          });
+          } else {
+            static_for<D2>([&](auto B2) { s = fmaf(yr[pi.yo + B2], zx[B2], s); });
+          }
           gw_own[P * PS + (4 * g + r) * RS + e16] = s;
         });
         __builtin_amdgcn_sched_barrier(0);
