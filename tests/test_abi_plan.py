@@ -119,6 +119,8 @@ def test_graph_and_conv_argument_errors_without_launch():
     assert L.tp_conv_gather_rows(fake, fake, -1, 3, fake, None) == -1
     msg = L.tp_conv_last_error().decode()
     assert "negative" in msg
+    # more rows than the int32 edge indices can address
+    assert L.tp_conv_gather_rows(fake, fake, 1 << 31, 3, fake, None) == -4
 
 
 def test_conv_alignment_errors_without_launch():
