@@ -595,7 +595,7 @@ tp_status tp_conv_fc_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n_radial
   const tpc::FcSet* fs = find_fc(plan, n_radial);
   if (!fs)
     return set_error(TP_ERR_UNSUPPORTED, "no compiled fully connected kernel (supported: 0e+1o+2e / "
-                                         "lmax 2 with 16 or 32 channels and 8 radial features)");
+                                         "lmax 2 with 16, 32 or 64 channels and 8 radial features)");
   *bytes = fs->workspace(n_nodes);
   return TP_OK;
 }
@@ -640,7 +640,7 @@ tp_status tp_conv_fc_backward_workspace(tp_plan_t plan, int32_t n_nodes, int32_t
   const tpc::FcSet* fs = find_fc(plan, n_radial);
   if (!fs || !fs->bwd_workspace)
     return set_error(TP_ERR_UNSUPPORTED, "no compiled fully connected kernel (supported: 0e+1o+2e / "
-                                         "lmax 2 with 16 or 32 channels and 8 radial features)");
+                                         "lmax 2 with 16, 32 or 64 channels and 8 radial features)");
   *bytes = fs->bwd_workspace(n_nodes);
   return TP_OK;
 }
@@ -696,7 +696,7 @@ tp_status tp_conv_fc_double_workspace(tp_plan_t plan, int32_t n_nodes, int32_t n
   const tpc::FcSet* fs = find_fc(plan, n_radial);
   if (!fs || !fs->dbl_workspace)
     return set_error(TP_ERR_UNSUPPORTED, "no compiled fully connected kernel (supported: 0e+1o+2e / "
-                                         "lmax 2 with 16 or 32 channels and 8 radial features)");
+                                         "lmax 2 with 16, 32 or 64 channels and 8 radial features)");
   *bytes = fs->dbl_workspace(n_nodes, n_edges);
   return TP_OK;
 }

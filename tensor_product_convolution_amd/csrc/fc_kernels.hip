@@ -1012,6 +1012,7 @@ const FcSet* fc_l012_s2(int mul, int n_radial) {
   switch (mul) {
     case 16: return fc_set<16>();
     case 32: return fc_set<32>();
+    case 64: return fc_set<64>();
     default: return nullptr;
   }
 }

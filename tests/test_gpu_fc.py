@@ -48,7 +48,8 @@ def _gpu(tpc, irr, wl, R, Th):
 
 
 @pytest.mark.parametrize("U,graph,n", [(16, "mid", 200), (32, "mid", 300), (32, "zipf", 400),
-                                       (16, "lmax3", 250), (32, "mid", 1536)])
+                                       (16, "lmax3", 250), (32, "mid", 1536), (64, "mid", 300),
+                                       (64, "zipf", 500)])
 def test_fc_forward_parity(tpc, U, graph, n):
     say(f"fc forward U={U} graph={graph} n={n}")
     irr, op, wl, R, Th = _case(U, graph, n)
@@ -95,7 +96,8 @@ def _check_bwd(op, wl, R, Th, go, got, perm):
 
 
 @pytest.mark.parametrize("U,graph,n", [(16, "mid", 200), (32, "mid", 300), (32, "zipf", 400),
-                                       (16, "lmax3", 250), (32, "mid", 1536)])
+                                       (16, "lmax3", 250), (32, "mid", 1536), (64, "mid", 300),
+                                       (64, "lmax3", 200)])
 def test_fc_backward_parity(tpc, U, graph, n):
     say(f"fc backward U={U} graph={graph} n={n}")
     irr, op, wl, R, Th = _case(U, graph, n)
@@ -184,7 +186,8 @@ def _fc_cotangents(op, wl, R, Th, seed):
     return [f(wl.x.shape), f((wl.n_edges, op.ysh)), f(R.shape), (f(Th.shape) / op.U).astype(np.float32)]
 
 
-@pytest.mark.parametrize("U,graph,n", [(16, "mid", 200), (32, "zipf", 400), (32, "lmax3", 600)])
+@pytest.mark.parametrize("U,graph,n", [(16, "mid", 200), (32, "zipf", 400), (32, "lmax3", 600),
+                                       (64, "mid", 200)])
 def test_fc_double_backward_parity(tpc, U, graph, n):
     say(f"fc double backward U={U} graph={graph} n={n}")
     irr, op, wl, R, Th = _case(U, graph, n)
