@@ -101,7 +101,10 @@ typedef struct {
 /* Options of a plan.  Zero-initialised means "none".
  *   radial_basis, radial_hidden, r_cut: edge weights come from a radial
  *     network of the edge length (Bessel basis -> SiLU hidden layer ->
- *     P*U weights), used by the *_radial entry points;
+ *     P*U weights), used by the *_radial entry points (compiled for 8 basis
+ *     functions and 64 hidden units, with 0e+1o+2e / lmax 2 at multiplicity
+ *     16, 32, 64 or 128 and 0e+1o+2e+3o / lmax 3 at 16, 32 or 64; other
+ *     plans: TP_ERR_UNSUPPORTED at plan creation);
  *   uvw: a U x U channel mix per output irrep follows the aggregation. */
 typedef struct {
   int32_t radial_basis;
@@ -501,7 +504,9 @@ tp_status tp_conv_backward_radial_r(tp_plan_t plan, const tp_graph* graph, const
  * on chip, never stored; parameter gradients are fixed-order sums through ws
  * (tp_conv_radial_double_workspace bytes), so results are bitwise
  * reproducible.  x, gg_x, grad_out and W2 must be 16-byte aligned
- * (TP_ERR_ARG); edge arrays receiver-sorted. */
+ * (TP_ERR_ARG); edge arrays receiver-sorted.  Built for the lmax-2 radial
+ * plans; the lmax-3 ones return TP_ERR_UNSUPPORTED (here and from the
+ * workspace query). */
 tp_status tp_conv_double_backward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
                                          const float* Y, const float* r_len, const float* W1,
                                          const float* W2, const float* Wmix, const float* grad_out,

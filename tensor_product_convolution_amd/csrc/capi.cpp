@@ -56,6 +56,8 @@ const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_o
                              int nh) {
   if (ls == std::vector<int>{0, 1, 2} && lmax_sh == 2 && lmax_out == 2)
     return radial_l012_s2(mul, nb, nh);
+  if (ls == std::vector<int>{0, 1, 2, 3} && lmax_sh == 3 && lmax_out == 3)
+    return radial_l0123_s3(mul, nb, nh);
   return nullptr;
 }
 
@@ -277,7 +279,8 @@ tp_status tp_conv_plan_create(tp_plan_t* out, const char* irreps_in, int32_t lma
       delete p;
       return set_error(TP_ERR_UNSUPPORTED,
                        "no compiled radial-weight kernel for this signature (supported: 0e+1o+2e / "
-                       "lmax 2, multiplicity 16, 32, 64 or 128, 8 basis functions, 64 hidden units)");
+                       "lmax 2 with multiplicity 16, 32, 64 or 128 and 0e+1o+2e+3o / lmax 3 with 16, "
+                       "32 or 64; 8 basis functions, 64 hidden units)");
     }
   }
   p->ks = tpc::find_kernels(ls, lmax_sh, lmax_out, p->mul);
@@ -1130,8 +1133,9 @@ tp_status tp_conv_backward_radial_r(tp_plan_t plan, const tp_graph* graph, const
 
 tp_status tp_conv_radial_double_workspace(tp_plan_t plan, int32_t n_nodes, int32_t with_mix, size_t* bytes) {
   if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_radial_double_workspace: NULL argument");
-  if (!plan->rs || !plan->rs->dbl_workspace)
-    return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  if (!plan->rs) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  if (!plan->rs->dbl_workspace)
+    return set_error(TP_ERR_UNSUPPORTED, "no second-order radial kernels for this signature (lmax 2 only)");
   if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_radial_double_workspace: negative size");
   size_t b = plan->rs->dbl_workspace(n_nodes, 0);
   if (with_mix) {
@@ -1154,7 +1158,9 @@ tp_status tp_conv_double_backward_radial(tp_plan_t plan, const tp_graph* graph, 
                                          hipStream_t stream) {
   const char* fn = "tp_conv_double_backward_radial";
   if (!plan) return set_error(TP_ERR_ARG, std::string(fn) + ": plan is NULL");
-  if (!plan->rs || !plan->rs->dbl) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  if (!plan->rs) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
+  if (!plan->rs->dbl)
+    return set_error(TP_ERR_UNSUPPORTED, "no second-order radial kernels for this signature (lmax 2 only)");
   tp_status s = check_graph(graph, d_x != nullptr);
   if (s != TP_OK) return s;
   const int N = graph->n_nodes, E = graph->n_edges;

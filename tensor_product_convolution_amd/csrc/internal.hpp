@@ -132,6 +132,7 @@ int gaunt_grid_points();
 const RadialSet* find_radial(const std::vector<int>& ls, int lmax_sh, int lmax_out, int mul, int nb,
                              int nh);
 const RadialSet* radial_l012_s2(int mul, int nb, int nh);
+const RadialSet* radial_l0123_s3(int mul, int nb, int nh);
 
 // Lookup of the compiled specialisation for (input degrees, lmax_sh,
 // lmax_out, multiplicity); nullptr if none.

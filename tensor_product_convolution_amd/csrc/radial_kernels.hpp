@@ -507,29 +507,33 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
 // needed here, so each wave computes only its own 16 hidden units.  The
 // accumulators (one 16x16 tile per path) stay in registers; one partial per
 // workgroup is written and summed later in a fixed order.
-// GEOM: Y holds the edge vectors r [E][3]; r_len unused
-template <class S, int U, int NB, int NH, bool GEOM = false>
+// GEOM: Y holds the edge vectors r [E][3]; r_len unused.  One launch covers
+// the NPG paths P0 .. P0 + NPG - 1 (all paths by default; wider signatures are
+// split into groups whose grad_w tiles fit in LDS, one launch per group, each
+// writing its own columns of the partials).
+template <class S, int U, int NB, int NH, bool GEOM = false, int P0 = 0, int NPG = S::NP>
 __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_per_eu(2)))
     k_radial_bwd_w2(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                     const float* __restrict__ x, const float* __restrict__ Y,
                     const float* __restrict__ r_len, RadialParams rp, const float* __restrict__ gout,
                     float* __restrict__ part) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NB % 4 == 0, "radial tiling");
+  static_assert(P0 >= 0 && NPG > 0 && P0 + NPG <= S::NP, "path group");
   constexpr int NW = NH / 16;
   constexpr int LD = S::NP * U;
   // grad_w of one tile in LDS: [p][edge 16][ch 16 + 4 pad]; the edge-row stride
   // of 20 floats puts the four lane groups (edges 4g + k) on distinct banks
   constexpr int RS = 20, PS = 16 * RS;
-  constexpr int TILE = S::NP * PS;
+  constexpr int TILE = NPG * PS;
   __shared__ __attribute__((aligned(16))) float s_gw[NW * TILE];
   __shared__ float s_r[NW * 16];                    // edge lengths of the tiles (-1: no edge)
   const int c = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e16 = lane & 15, g = lane >> 4;
   const int u = 16 * c + e16;
-  f32x4 acc[S::NP];
+  f32x4 acc[NPG];
 #pragma unroll
-  for (int p = 0; p < S::NP; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < NPG; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
   // W1 operands of this wave's hidden units (B[n][hid 16w + e16], n = 4s + g)
   float w1b[NB / 4];
 #pragma unroll
@@ -564,14 +568,14 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
         float xr[S::XC], yr[S::YC];
         load_x_channel<S, U>(x, col[qc], u, xr);
         radial_edge_y<S, GEOM>(Y, qc, yr);
-        static_for<S::NP>([&](auto P) {
-          constexpr PathInfo pi = S::paths.p[P];
+        static_for<NPG>([&](auto G) {
+          constexpr PathInfo pi = S::paths.p[P0 + G];
           constexpr int D2 = 2 * pi.l2 + 1;
           float z[D2];
           zform_scaled<pi.l1, pi.l2, pi.l3, pi.xo, pi.ko>(xr, gr, z);
           float s = 0.f;
           static_for<D2>([&](auto B2) { s = fmaf(yr[pi.yo + B2], z[B2], s); });
-          gw_own[P * PS + (4 * g + r) * RS + e16] = s;
+          gw_own[G * PS + (4 * g + r) * RS + e16] = s;
         });
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -605,7 +609,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
       for (int t = 0; t < 4; ++t) hA[t] = silu(z[t]);
       const float* gt = s_gw + tw * TILE + 4 * g * RS + e16;
 #pragma unroll
-      for (int p = 0; p < S::NP; ++p)
+      for (int p = 0; p < NPG; ++p)
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[p] = mfma_16x16x4(hA[k], gt[p * PS + k * RS], acc[p]);
     }
@@ -614,9 +618,9 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
   // part[block][hid][p*U + u]; each chunk writes its own columns
   float* pb = part + (size_t)blockIdx.x * NH * LD;
 #pragma unroll
-  for (int p = 0; p < S::NP; ++p)
+  for (int p = 0; p < NPG; ++p)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pb[(size_t)(16 * wv + 4 * g + t) * LD + p * U + u] = acc[p][t];
+    for (int t = 0; t < 4; ++t) pb[(size_t)(16 * wv + 4 * g + t) * LD + (P0 + p) * U + u] = acc[p][t];
 }
 
 // Forward (SEND = false) and sender pass (SEND = true), chunk-major: workgroup

@@ -1,0 +1,23 @@
+// Radial-weight kernel specialisations for the 0e+1o+2e+3o / lmax 3 signature
+// (34 paths).  The chunk's W2 slice takes 140 KB of LDS, so the forward, the
+// receiver pass and the sender pass run one workgroup (one wave per SIMD) per
+// CU; grad_W2 runs in three launches of at most 12 paths each.  The
+// second-order kernels are not built for this signature: their register state
+// at 34 paths does not fit a wave.
+#include "radial_launch.hpp"
+
+namespace tpc {
+
+using RadialL0123 = RadialSig<Sig<3, 3, 0, 1, 2, 3>, 12, false>;
+
+const RadialSet* radial_l0123_s3(int mul, int nb, int nh) {
+  if (nb != kNB || nh != kNH) return nullptr;
+  switch (mul) {
+    case 16: return radial_set<RadialL0123, 16>();
+    case 32: return radial_set<RadialL0123, 32>();
+    case 64: return radial_set<RadialL0123, 64>();
+    default: return nullptr;
+  }
+}
+
+}  // namespace tpc
