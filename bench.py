@@ -67,6 +67,10 @@ RADIAL_WORKLOADS = {
                "U[0.8,5] A), 128x0e+128x1o+128x2e, real SH lmax 2, all paths l3<=2 (15), edge "
                "weights from a radial MLP (8 Bessel -> 64 SiLU -> 15x128) computed on chip, "
                "128x128 uvw mix per output irrep, fwd+bwd"),
+    "lmax3_radial": ("64x0e+64x1o+64x2e+64x3o", 3, 3, (8, 64, 5.0),
+                     "4096 atoms, degree U{5..30} (length U[0.8,5] A), 64x(0e+1o+2e+3o), SH lmax 3, 34 "
+                     "paths, edge weights from a radial MLP (8 Bessel -> 64 SiLU -> 34x64) computed on "
+                     "chip, 64x64 uvw mix per output irrep, fwd+bwd"),
 }
 FC_WORKLOADS = {
     "fc": ("32x0e+32x1o+32x2e", 2, 2, 8,
@@ -80,12 +84,16 @@ GAUNT_WORKLOADS = {
               "Gaunt product (even couplings, outputs 0e+1o+2e) evaluated on a 32-point spherical "
               "grid, filter weights per edge, degree and channel, fwd+bwd"),
 }
-DEFAULT_CONFIGS = ("tiny", "lmax3", "zipf", "stream")
+DEFAULT_CONFIGS = ("tiny", "lmax3", "zipf", "stream", "lmax3_radial")
 GAUNT_SOURCES = ("gaunt.hip",)
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_{}.txt")
 KERNEL_SOURCES = ("conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
-RADIAL_SOURCES = ("radial_kernels.hpp", "radial_l012_s2.hip", "uvw.hip", "conv_kernels.hpp", "sig.hpp",
-                  "cg_table.hpp")
+RADIAL_SOURCES = {      # per radial workload: the sources its kernels are built from
+    "stream": ("radial_kernels.hpp", "radial_dbl_kernels.hpp", "radial_launch.hpp", "radial_l012_s2.hip",
+               "uvw.hip", "conv_kernels.hpp", "sig.hpp", "cg_table.hpp"),
+    "lmax3_radial": ("radial_kernels.hpp", "radial_launch.hpp", "radial_l0123_s3.hip", "uvw.hip",
+                     "conv_kernels.hpp", "sig.hpp", "cg_table.hpp"),
+}
 FC_SOURCES = ("fc_kernels.hip", "radial_kernels.hpp", "conv_kernels.hpp", "sig.hpp", "cg_table.hpp")
 
 
@@ -688,7 +696,10 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     t = timed_steps(step, args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    reps, rounds = 3, 2
+    # the stream layer gathers GBs per call (cold without rotation); the lmax-3
+    # layer's arrays fit in the Infinity Cache, so each call follows a flush
+    big = E * U * 4 > (1 << 30)
+    reps, rounds = (3, 2) if big else (1, 5)
     kt = {n: float(timed_kernel(fn, 1, reps, rounds).mean()) for n, fn in kernels.items()}
     extra_ms = {n: float(timed_kernel(fn, 1, reps, rounds).mean()) for n, fn in extras.items()}
     # the same step from the edge vectors: harmonics and lengths on chip, grad_r out
@@ -703,18 +714,21 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     kt_r = {"fwd_r": float(timed_kernel(lambda c: tpc.forward_radial_r(plan, g, x, r_sorted, W1, W2, None,
                                                                        out=pre), 1, reps, rounds).mean())}
     # second-order backward with cotangents on grad_x, grad_Y and grad_rlen (here
-    # the first backward's outputs, as in a loss on forces), all outputs
-    grl_c = outs_f["rlen"]
-    tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, want=("x", "Y", "rlen"), outs=outs_f, ws=ws)
-    d_outs = {"x": torch.empty_like(x), "Y": torch.empty_like(Y), "rlen": torch.empty_like(rl),
-              "W1": torch.empty_like(W1), "W2": torch.empty_like(W2), "Wmix": torch.empty_like(Wm),
-              "g": torch.empty_like(go)}
-    ws2 = torch.empty(tpc.radial_double_workspace(plan, N, True), dtype=torch.uint8, device=dev)
-    dbl = lambda c: tpc.double_backward_radial(plan, g, x, Y, rl, W1, W2, go, Wmix=Wm, gg_x=outs["x"],
-                                               gg_Y=outs["Y"], gg_rlen=grl_c, outs=d_outs, ws=ws2)
-    dbl(0)
-    dbl_ms = float(timed_kernel(dbl, 1, 2, rounds).mean())
-    del ws2, d_outs
+    # the first backward's outputs, as in a loss on forces), all outputs; built
+    # for the lmax-2 layer only
+    dbl_ms = None
+    if lsh == 2:
+        grl_c = outs_f["rlen"]
+        tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, want=("x", "Y", "rlen"), outs=outs_f, ws=ws)
+        d_outs = {"x": torch.empty_like(x), "Y": torch.empty_like(Y), "rlen": torch.empty_like(rl),
+                  "W1": torch.empty_like(W1), "W2": torch.empty_like(W2), "Wmix": torch.empty_like(Wm),
+                  "g": torch.empty_like(go)}
+        ws2 = torch.empty(tpc.radial_double_workspace(plan, N, True), dtype=torch.uint8, device=dev)
+        dbl = lambda c: tpc.double_backward_radial(plan, g, x, Y, rl, W1, W2, go, Wmix=Wm, gg_x=outs["x"],
+                                                   gg_Y=outs["Y"], gg_rlen=grl_c, outs=d_outs, ws=ws2)
+        dbl(0)
+        dbl_ms = float(timed_kernel(dbl, 1, 2, rounds).mean())
+        del ws2, d_outs
     fl = radial_flops(E, P, U, NH)
     mix_flops = 2.0 * N * plan.outdim * U            # one application of the channel mix
     names = ["fwd", "bwd_recv", "bwd_w2", "bwd_send"]
@@ -722,7 +736,7 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     achieved = fl[dom] / (kt[dom] * 1e-3) / 1e12
     step_ms = float(t.mean())
     step_flops = sum(fl[n] for n in names) + 3 * mix_flops   # mix forward, grad_in, grad_Wmix
-    traffic = read_traffic(name, RADIAL_SOURCES)
+    traffic = read_traffic(name, RADIAL_SOURCES[name])
     res = {
         "workload": f"{name}: {desc}", "n_nodes": N, "n_edges": E, "irreps": irreps,
         "lmax_sh": lsh, "lmax_out": lout, "paths": P,
@@ -732,9 +746,10 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
         "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
         "fwd_edges_per_s": E / (kt["fwd_with_mix"] * 1e-3),
         "kernel_ms": kt,
-        "kernel_ms_note": (f"per call, {reps} back-to-back calls after a cache flush, mean of {rounds} "
-                           "(every call gathers GBs of node rows: cold without rotation); bwd_recv "
-                           "and bwd_w2 include their partial-sum kernels"),
+        "kernel_ms_note": ((f"per call, {reps} back-to-back calls after a cache flush, mean of {rounds} "
+                            "(every call gathers GBs of node rows: cold without rotation)" if big else
+                            f"one call after a cache flush, mean of {rounds}")
+                           + "; bwd_recv and bwd_w2 include their partial-sum kernels"),
         "kernel_mfma_frac": {n: fl[n] / (kt[n] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS for n in names},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -753,8 +768,10 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     }
     dbl_flops = fl["double_bwd"] + 3 * mix_flops                  # mix: g, out_dot, d_Wmix
     res["double_bwd_ms"] = dbl_ms
-    res["double_bwd_mfma_frac"] = dbl_flops / (dbl_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS
-    res["double_bwd_note"] = ("second-order backward (d_x, d_Y, d_rlen, d_W1, d_W2, d_Wmix, d_grad_out "
+    res["double_bwd_mfma_frac"] = (dbl_flops / (dbl_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS
+                                   if dbl_ms else None)
+    res["double_bwd_note"] = "not built for this signature" if dbl_ms is None else (
+                              "second-order backward (d_x, d_Y, d_rlen, d_W1, d_W2, d_Wmix, d_grad_out "
                               "for cotangents on grad_x, grad_Y and grad_rlen), per call after a flush; "
                               "not part of the step; MFMA fraction on its ten network products per edge "
                               "and three applications of the mix")

@@ -1,14 +1,18 @@
 // Radial-weight kernel specialisations for the 0e+1o+2e+3o / lmax 3 signature
-// (34 paths).  The chunk's W2 slice takes 140 KB of LDS, so the forward, the
-// receiver pass and the sender pass run one workgroup (one wave per SIMD) per
-// CU; grad_W2 runs in three launches of at most 12 paths each.  The
-// second-order kernels are not built for this signature: their register state
-// at 34 paths does not fit a wave.
+// (34 paths).  The chunk's W2 slice takes 140 KB of LDS, so one workgroup fits
+// a CU: the forward and the sender pass run four waves (one per SIMD, 256
+// registers and up to 220 accumulation registers each), the receiver pass
+// eight waves that share the slice (two per SIMD at 256 registers, with a few
+// spilled: 1.03 against 1.37 ms with four waves on 4,096 atoms at 64
+// channels, the latency of each path's LDS -> MFMA -> VALU -> MFMA chain
+// hidden by the second wave).  grad_W2 runs in three launches of at most 12
+// paths each.  The second-order kernels are not built for this signature:
+// their register state at 34 paths does not fit a wave.
 #include "radial_launch.hpp"
 
 namespace tpc {
 
-using RadialL0123 = RadialSig<Sig<3, 3, 0, 1, 2, 3>, 12, false>;
+using RadialL0123 = RadialSig<Sig<3, 3, 0, 1, 2, 3>, 12, 8, false>;
 
 const RadialSet* radial_l0123_s3(int mul, int nb, int nh) {
   if (nb != kNB || nh != kNH) return nullptr;

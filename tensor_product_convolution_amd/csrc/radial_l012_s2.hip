@@ -3,8 +3,9 @@
 
 namespace tpc {
 
-// all 15 paths' grad_w tiles fit in one grad_W2 launch; second order built
-using RadialL012 = RadialSig<Sig<2, 2, 0, 1, 2>, 15, true>;
+// all 15 paths' grad_w tiles fit in one grad_W2 launch; receiver pass of four
+// waves (two workgroups per CU); second order built
+using RadialL012 = RadialSig<Sig<2, 2, 0, 1, 2>, 15, 4, true>;
 
 const RadialSet* radial_l012_s2(int mul, int nb, int nh) {
   if (nb != kNB || nh != kNH) return nullptr;

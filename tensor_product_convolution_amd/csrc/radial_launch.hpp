@@ -43,13 +43,16 @@ __global__ void __launch_bounds__(64 * kSumWaves)
 
 // persistent grid sizes (fixed functions of the node count, so the partial
 // sums and hence the results do not depend on the device)
-constexpr int kRecvWaves = 4;                             // waves per receiver-pass workgroup
+template <int NW>                                         // NW waves per receiver-pass workgroup
 int recv_blocks(int n_nodes) {
-  const int b = (n_nodes + kRecvWaves - 1) / kRecvWaves;
-  return b < 512 ? (b > 0 ? b : 1) : 512;                 // two workgroups per CU
+  const int b = (n_nodes + NW - 1) / NW;
+  return b < 512 ? (b > 0 ? b : 1) : 512;
 }
-int recv_parts(int n_nodes) { return recv_blocks(n_nodes) * kRecvWaves; }
-// the second-order receiver pass runs one wave per SIMD: one workgroup per CU
+template <int NW>
+int recv_parts(int n_nodes) { return recv_blocks<NW>(n_nodes) * NW; }
+// the second-order receiver pass runs one wave per SIMD: one workgroup of
+// kRecvWaves per CU
+constexpr int kRecvWaves = 4;
 int dbl_recv_blocks(int n_nodes) {
   const int b = (n_nodes + kRecvWaves - 1) / kRecvWaves;
   return b < 256 ? (b > 0 ? b : 1) : 256;
@@ -72,12 +75,14 @@ dim3 node_grid(int n_nodes) {
 }
 
 // A signature's radial kernels: S the CG signature, NPG the paths per grad_W2
-// launch (the grad_w tile of NPG paths must fit in LDS), DBL whether the
-// second-order kernels are built for it.
-template <class S, int NPG, bool DBL>
+// launch (the grad_w tile of NPG paths must fit in LDS), RW the waves of a
+// receiver-pass workgroup, DBL whether the second-order kernels are built for
+// it.
+template <class S, int NPG, int RW, bool DBL>
 struct RadialSig {
   using Sig = S;
   static constexpr int npg = NPG;
+  static constexpr int recv_waves = RW;
   static constexpr bool dbl = DBL;
 };
 
@@ -99,7 +104,7 @@ hipError_t launch_radial_fwd(const RadialArgs& a) {
 
 template <class R, int U>
 size_t radial_bwd_ws(int n_nodes, int /*n_edges*/) {
-  return align256((size_t)recv_parts(n_nodes) * kNB * kNH * sizeof(float)) +
+  return align256((size_t)recv_parts<R::recv_waves>(n_nodes) * kNB * kNH * sizeof(float)) +
          (size_t)w2_blocks<U>(n_nodes) * kNH * R::Sig::NP * U * sizeof(float);
 }
 
@@ -121,14 +126,15 @@ void launch_w2_groups(const RadialArgs& a, const RadialParams& rp, int nb2, floa
 template <class R, int U, bool GEOM>
 hipError_t launch_radial_bwd_as(const RadialArgs& a) {
   using S = typename R::Sig;
+  constexpr int RW = R::recv_waves;
   RadialParams rp{a.r_cut, a.W1, a.W2};
-  const int nb1 = recv_parts(a.n_nodes), nb2 = w2_blocks<U>(a.n_nodes);
+  const int nb1 = recv_parts<RW>(a.n_nodes), nb2 = w2_blocks<U>(a.n_nodes);
   float* part1 = static_cast<float*>(a.ws);
   float* part2 = reinterpret_cast<float*>(static_cast<char*>(a.ws) +
                                           align256((size_t)nb1 * kNB * kNH * sizeof(float)));
   if (a.grad_Y || a.grad_W1 || a.grad_rlen) {
-    hipLaunchKernelGGL((k_radial_bwd_recv<S, U, kNB, kNH, kRecvWaves, GEOM>), dim3(recv_blocks(a.n_nodes)),
-                       dim3(64 * kRecvWaves), 0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len,
+    hipLaunchKernelGGL((k_radial_bwd_recv<S, U, kNB, kNH, RW, GEOM>), dim3(recv_blocks<RW>(a.n_nodes)),
+                       dim3(64 * RW), 0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len,
                        rp, a.grad_out, a.grad_Y, a.grad_rlen, part1);
     if (a.grad_W1) {
       const long long n = (long long)kNB * kNH;

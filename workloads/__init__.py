@@ -36,6 +36,11 @@ CONFIGS = {
     "stream": dict(irreps="128x0e+128x1o+128x2e", lmax_sh=2, lmax_out=2, n_nodes=100000,
                    graph="fixed30", w_std="radial", modes=("fwd", "fwd+bwd"),
                    n_basis=8, hidden=64, r_cut=5.0),
+    # the lmax-3 graph and features with radial-network weights (the streaming
+    # layer at the lmax-3 width; the pages give no such configuration)
+    "lmax3_radial": dict(irreps="64x0e+64x1o+64x2e+64x3o", lmax_sh=3, lmax_out=3, n_nodes=4096,
+                         graph="uniform5_30", w_std="radial", modes=("fwd", "fwd+bwd"),
+                         n_basis=8, hidden=64, r_cut=5.0),
 }
 
 BOX = 8.0          # periodic cube edge (Angstrom) of the tiny workload
