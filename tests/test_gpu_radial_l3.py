@@ -126,3 +126,24 @@ def test_radial_l3_empty_and_isolated(tpc):
         _check_params(op, dict(gW1=gW1.cpu().numpy(), gW2=gW2.cpu().numpy(), gWm=None),
                       (None, None, rb[2], rb[3], None), U)
 
+
+
+def test_radial_l3_determinism(tpc):
+    """two backward calls give bitwise equal gradients (fixed-order sums of the
+    per-wave and per-workgroup partials)"""
+    say("radial lmax 3 determinism")
+    U = 32
+    op, wl = _inputs(U, "zipf", 600, seed=11)
+    plan = tpc.Plan(_irreps(U), 3, 3, radial=(8, 64, RC), uvw=True)
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    rs = tpc.gather_rows(T(wl.r), g.perm)
+    Y = tpc.sph_harm(3, rs)
+    rl = tpc.gather_rows(T(wl.r_len), g.perm)
+    args = (plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), T(wl.g))
+    want = ("x", "Y", "W1", "W2", "Wmix", "rlen")
+    _, pre = tpc.forward_radial(plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), T(wl.Wmix))
+    a = tpc.backward_radial(*args, Wmix=T(wl.Wmix), out_pre=pre, want=want)
+    b = tpc.backward_radial(*args, Wmix=T(wl.Wmix), out_pre=pre, want=want)
+    torch.cuda.synchronize()
+    for s, t in zip(a, b):
+        assert torch.equal(s, t)
