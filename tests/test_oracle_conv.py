@@ -238,18 +238,19 @@ def test_uvw_mix_against_kronecker_route_and_adjoint():
     assert abs(np.sum(gW * W) - f) <= 1e-12 * max(1, abs(f))
 
 
-def test_radial_conv_equivariance_and_gradients():
+@pytest.mark.parametrize("irreps,lmax", [("4x0e+4x1o+4x2e", 2), ("3x0e+3x1o+3x2e+3x3o", 3)])
+def test_radial_conv_equivariance_and_gradients(irreps, lmax):
     # the stream workload's structure with a narrow plan, for speed
-    plan = oracle.build_plan("4x0e+4x1o+4x2e", 2, 2)
+    plan = oracle.build_plan(irreps, lmax, lmax)
     wl = make_workload("stream", dims_of(plan), seed=1, n_nodes=12)
     x = wl.x.astype(np.float64)
-    Y = oracle.sh_real(2, wl.r)
+    Y = oracle.sh_real(lmax, wl.r)
     rl = wl.r_len.astype(np.float64)
     args = (plan, wl.src, wl.dst, wl.n_nodes)
     kw = dict(n_basis=wl.n_basis, r_cut=wl.r_cut)
     out = oracle.tp_conv_radial_fwd(*args, x, Y, rl, wl.W1, wl.W2, wl.Wmix, **kw)
     R = haar(np.random.default_rng(5))
-    Yr = oracle.sh_real(2, wl.r.astype(np.float64) @ R.T)
+    Yr = oracle.sh_real(lmax, wl.r.astype(np.float64) @ R.T)
     got = oracle.tp_conv_radial_fwd(*args, _rotate_x(plan, x, R), Yr, rl, wl.W1, wl.W2,
                                     wl.Wmix, **kw)
     assert np.max(np.abs(got - _rotate_out(plan, out, R))) <= 1e-10 * max(1, np.max(np.abs(out)))
