@@ -298,6 +298,43 @@ def _local(src, dst, chunk, *node_arrays):
     return nodes, ls, ld, [None if a is None else a[nodes] for a in node_arrays]
 
 
+def _block_err(got, ref, blocks):
+    """max over column blocks of max|got - ref| / max|ref| of the block"""
+    worst = 0.0
+    for sl in blocks:
+        r, g = ref[:, sl], got[:, sl]
+        if r.size == 0:
+            continue
+        scale = float(np.max(np.abs(r)))
+        err = float(np.max(np.abs(g - r)))
+        worst = max(worst, err / scale if scale > 0 else err)
+    return worst
+
+
+def _parity(plan_args, e, recv_rows, checks, what):
+    """Parity of the timed run against the oracle on the CPU-baseline sample:
+    checks is a list of (name, got, ref, kind) with kind 'out', 'x', 'Y' or 'w'
+    (rows already aligned); the block-relative error of each and their max."""
+    import oracle
+    op = oracle.build_plan(*plan_args)
+    U = op.U
+    blocks = {
+        "out": [slice(o, o + U * (2 * l + 1)) for (l, _), o in zip(op.out_irreps, op.out_offsets)],
+        "x": [slice(o, o + U * (2 * l + 1)) for (_, l, _), o in zip(op.irreps_in, op.in_offsets)],
+        "Y": [slice(l * l, (l + 1) ** 2) for l in range(op.lmax_sh + 1)],
+        "w": [slice(p * U, (p + 1) * U) for p in range(op.n_paths)],
+    }
+    errs = {}
+    for name, got, ref, kind in checks:
+        got = np.asarray(got, dtype=np.float64).reshape(len(got), -1)
+        ref = np.asarray(ref, dtype=np.float64).reshape(len(ref), -1)
+        errs[name] = _block_err(got, ref, blocks[kind])
+    return {"max_rel_err": max(errs.values()), "per_output": errs, "tol": 1e-4,
+            "sample": f"{what}: rows of {recv_rows} receivers with all their edges, and those edges",
+            "note": "largest max|gpu - oracle| / max|oracle| over the irrep, path and degree blocks; "
+                    "the GPU values are those of the timed step"}
+
+
 def pooled_oracle_direct(plan_args, src, dst, n, x, r, w, g, workers):
     """The oracle's harmonics + forward (+ backward when g is given) for the edges
     (src, dst), split by receiver over a process pool (each task carries only
@@ -334,27 +371,42 @@ def pooled_oracle_direct(plan_args, src, dst, n, x, r, w, g, workers):
     return (out,) + grads, dt
 
 
-def cpu_baseline_direct(irreps, lsh, lout, wl, fwd_only, max_edges):
+def cpu_baseline_direct(irreps, lsh, lout, wl, fwd_only, max_edges, snap=None):
     """The float64 oracle (harmonics + forward, + backward unless fwd_only) on a
     bounded sample of the workload, its edges split by receiver over a process
     pool of host_workers() workers (one BLAS thread each); per-node partial
-    results are summed in the parent."""
+    results are summed in the parent.  With snap (the timed step's outputs:
+    out, receiver-sorted grad_Y / grad_w, grad_x, and the permutation) the
+    oracle's results also give the parity of the timed run on the sample."""
     e, what = _receiver_sample(wl.src, wl.dst, max_edges)
     nodes = np.unique(np.concatenate([wl.src[e], wl.dst[e]]))
     src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
     g = None if fwd_only else wl.g[nodes]
     n, W = len(nodes), host_workers()
-    _, dt = pooled_oracle_direct((irreps, lsh, lout), src, dst, n, wl.x[nodes], wl.r[e], wl.w[e], g, W)
+    res, dt = pooled_oracle_direct((irreps, lsh, lout), src, dst, n, wl.x[nodes], wl.r[e], wl.w[e], g, W)
+    if snap is not None:
+        recv = np.unique(wl.dst[e])
+        li = np.searchsorted(nodes, recv)
+        checks = [("out", snap["out"][recv], res[0][li], "out")]
+        if not fwd_only:
+            pos = np.empty(len(snap["perm"]), dtype=np.int64)
+            pos[snap["perm"]] = np.arange(len(snap["perm"]))
+            checks += [("grad_Y", snap["gY"][pos[e]], res[2], "Y"), ("grad_w", snap["gw"][pos[e]], res[3], "w")]
+            if len(e) == len(wl.src):        # every edge in the sample: grad_x is complete
+                checks.append(("grad_x", snap["gx"][nodes], res[1], "x"))
+        snap["parity"] = _parity((irreps, lsh, lout), e, len(recv), checks, what)
     return {"value": len(e) / dt, "unit": "edges/s", "cores": W, "kind": "oracle",
             "sample": f"{what}, {n} nodes: harmonics + fwd{'' if fwd_only else ' + bwd'} once, "
                       f"float64, split by receiver over {W} worker processes (1 thread each), "
                       f"{dt:.2f} s wall"}
 
 
-def cpu_baseline_radial(irreps, lsh, lout, wl, radial, max_edges=30000):
+def cpu_baseline_radial(irreps, lsh, lout, wl, radial, max_edges=30000, snap=None):
     """The float64 oracle of the radial layer (fwd + bwd with the mix) on the
     edges into the first receivers, split by receiver over the process pool
-    (per-node and parameter gradients summed in the parent)."""
+    (per-node and parameter gradients summed in the parent).  With snap (the
+    timed step's mixed output, receiver-sorted grad_Y and the permutation) also
+    the parity of the timed run on the sample's receivers and edges."""
     import multiprocessing as mp
     nb, _, rc = radial
     e, what = _receiver_sample(wl.src, wl.dst, max_edges)
@@ -377,6 +429,16 @@ def cpu_baseline_radial(irreps, lsh, lout, wl, radial, max_edges=30000):
         for nc, p in zip(maps, parts):
             out[nc] += p[0]
         dt = time.perf_counter() - t0
+    if snap is not None:
+        gY = np.zeros((len(e), parts[0][1][1].shape[1]))
+        for c, p in zip(_chunks_by_receiver(dst, W), parts):
+            gY[c] = p[1][1]
+        recv = np.unique(wl.dst[e])
+        pos = np.empty(len(snap["perm"]), dtype=np.int64)
+        pos[snap["perm"]] = np.arange(len(snap["perm"]))
+        checks = [("out", snap["out"][recv], out[np.searchsorted(nodes, recv)], "out"),
+                  ("grad_Y", snap["gY"][pos[e]], gY, "Y")]
+        snap["parity"] = _parity((irreps, lsh, lout), e, len(recv), checks, what)
     return {"value": len(e) / dt, "unit": "edges/s", "cores": W, "kind": "oracle",
             "sample": f"{what}, {n} nodes: harmonics + radial fwd + bwd with the mix once, float64, "
                       f"split by receiver over {W} worker processes (1 thread each), {dt:.2f} s wall"}
@@ -558,6 +620,10 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
     t_wall0 = time.perf_counter()
     t = timed_steps(args.steps, True)
     torch.cuda.synchronize()
+    # the timed step's results, for the parity check on the CPU-baseline sample
+    snap = {"out": out.cpu().numpy(), "perm": g.perm.cpu().numpy()[:E]} if cpu else None
+    if cpu and not fwd_only:
+        snap.update(gx=gx.cpu().numpy(), gY=gYs[0].cpu().numpy(), gw=gws[0].cpu().numpy())
     wall = time.perf_counter() - t_wall0
     warm = timed_steps(args.steps, False) if args.warm else None
     reps = max(2 * NC, 12)
@@ -629,9 +695,11 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
         # about 2-10 s of wall time on 16 host cores; the lmax-3 product costs
         # about 10x the lmax-2 one per edge
         res["cpu_baseline"] = cpu_baseline_direct(irreps, lsh, lout, wl, fwd_only,
-                                                  max_edges=60000 if lsh <= 2 else 40000)
+                                                  max_edges=60000 if lsh <= 2 else 40000, snap=snap)
+        res["parity"] = snap["parity"]
     else:
         res["cpu_baseline"] = None
+        res["parity"] = None
     del Ys, ws, gYs, gws
     return res, step
 
@@ -696,6 +764,9 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     t = timed_steps(step, args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
+    # the timed step's results, for the parity check on the CPU-baseline sample
+    snap = ({"out": out.cpu().numpy(), "gY": outs["Y"].cpu().numpy(), "perm": g.perm.cpu().numpy()[:E]}
+            if cpu else None)
     # the stream layer gathers GBs per call (cold without rotation); the lmax-3
     # layer's arrays fit in the Infinity Cache, so each call follows a flush
     big = E * U * 4 > (1 << 30)
@@ -783,7 +854,8 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
                  "evaluated per edge on chip, grad_r (forces' edge term) in place of grad_Y; timed "
                  "as the step above"),
     }
-    res["cpu_baseline"] = cpu_baseline_radial(irreps, lsh, lout, wl, radial) if cpu else None
+    res["cpu_baseline"] = cpu_baseline_radial(irreps, lsh, lout, wl, radial, snap=snap) if cpu else None
+    res["parity"] = snap["parity"] if cpu else None
     return res, step
 
 

@@ -138,9 +138,72 @@ def test_fc_and_gaunt_counts():
 
 
 @pytest.mark.parametrize("config,sources", [("mid", bench.KERNEL_SOURCES), ("fc", bench.FC_SOURCES),
-                                            ("gaunt", bench.GAUNT_SOURCES)])
+                                            ("gaunt", bench.GAUNT_SOURCES),
+                                            ("stream", bench.RADIAL_SOURCES["stream"]),
+                                            ("lmax3_radial", bench.RADIAL_SOURCES["lmax3_radial"])])
 def test_counter_summaries_parse(config, sources):
     # null once the kernel sources change after the counters were taken, else
     # one positive byte count per kernel of the step
     t = bench.read_traffic(config, sources)
     assert t is None or (len(t) >= 2 and all(v > 0 for v in t.values()))
+
+
+def _direct_snapshot(op, wl):
+    """what the timed step leaves on the GPU, here from the oracle in float32:
+    out, grad_x, and receiver-sorted grad_Y / grad_w with the permutation"""
+    import oracle
+    Y = oracle.sh_real(op.lmax_sh, wl.r)
+    ref = oracle.tp_conv_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w)
+    rx, rY, rw = oracle.tp_conv_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w, wl.g)
+    perm = oracle.csr_build(wl.src, wl.dst, wl.n_nodes)["perm"]
+    f = lambda a: a.astype(np.float32)
+    return dict(out=f(ref), gx=f(rx), gY=f(rY[perm]), gw=f(rw[perm]), perm=perm)
+
+
+@pytest.mark.parametrize("max_edges", [100000, 300])
+def test_parity_on_the_cpu_baseline_sample(max_edges):
+    """The bench line's parity entry: the timed step's outputs against the
+    oracle on the CPU-baseline sample (whole workload, or the edges into the
+    first receivers); float32 copies of the oracle's own results pass, and an
+    error planted in one path block of one sampled edge is reported."""
+    import oracle
+    from workloads import make_workload
+    irr = "8x0e+8x1o+8x2e"
+    op = oracle.build_plan(irr, 2, 2)
+    dims = dict(xdim=op.xdim, n_paths=op.n_paths, U=op.U, outdim=op.outdim, n_out_irreps=5)
+    wl = make_workload("mid", dims, seed=2, n_nodes=40)
+    snap = _direct_snapshot(op, wl)
+    bench.cpu_baseline_direct(irr, 2, 2, wl, False, max_edges, snap=snap)
+    par = snap["parity"]
+    assert par["max_rel_err"] < 1e-6
+    assert set(par["per_output"]) == ({"out", "grad_Y", "grad_w", "grad_x"} if max_edges > wl.n_edges
+                                      else {"out", "grad_Y", "grad_w"})
+    # plant: the first sampled edge (the first receiver's first edge) at its sorted position 0
+    bad = _direct_snapshot(op, wl)
+    bad["gw"][0, 3, :] += 0.01 * np.max(np.abs(bad["gw"][:, 3, :]))
+    bench.cpu_baseline_direct(irr, 2, 2, wl, False, max_edges, snap=bad)
+    assert bad["parity"]["per_output"]["grad_w"] > 1e-3
+    assert bad["parity"]["per_output"]["out"] < 1e-6
+
+
+def test_parity_of_the_radial_sample():
+    """The same for the radial layer: the mixed output of the sampled
+    receivers and grad_Y of their edges."""
+    import oracle
+    from workloads import make_workload
+    irr = "4x0e+4x1o+4x2e"
+    op = oracle.build_plan(irr, 2, 2)
+    dims = dict(xdim=op.xdim, n_paths=op.n_paths, U=op.U, outdim=op.outdim, n_out_irreps=5)
+    wl = make_workload("stream", dims, seed=3, n_nodes=50)
+    Y = oracle.sh_real(2, wl.r)
+    out = oracle.tp_conv_radial_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.r_len, wl.W1, wl.W2,
+                                    wl.Wmix, 8, 5.0)
+    gY = oracle.tp_conv_radial_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.r_len, wl.W1, wl.W2,
+                                   wl.Wmix, wl.g, 8, 5.0)[1]
+    perm = oracle.csr_build(wl.src, wl.dst, wl.n_nodes)["perm"]
+    snap = dict(out=out.astype(np.float32), gY=gY[perm].astype(np.float32), perm=perm)
+    bench.cpu_baseline_radial(irr, 2, 2, wl, (8, 64, 5.0), max_edges=400, snap=snap)
+    assert snap["parity"]["max_rel_err"] < 1e-6
+    snap["gY"][0, 5] += 0.01 * np.max(np.abs(snap["gY"][:, 4:9]))
+    bench.cpu_baseline_radial(irr, 2, 2, wl, (8, 64, 5.0), max_edges=400, snap=snap)
+    assert snap["parity"]["per_output"]["grad_Y"] > 1e-3
