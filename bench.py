@@ -311,19 +311,27 @@ def _block_err(got, ref, blocks):
     return worst
 
 
-def _parity(plan_args, e, recv_rows, checks, what):
-    """Parity of the timed run against the oracle on the CPU-baseline sample:
-    checks is a list of (name, got, ref, kind) with kind 'out', 'x', 'Y' or 'w'
-    (rows already aligned); the block-relative error of each and their max."""
+def _cg_blocks(plan_args):
+    """column blocks of a CG plan's arrays: output and input irreps, harmonic
+    degrees, weight paths"""
     import oracle
     op = oracle.build_plan(*plan_args)
     U = op.U
-    blocks = {
+    return {
         "out": [slice(o, o + U * (2 * l + 1)) for (l, _), o in zip(op.out_irreps, op.out_offsets)],
         "x": [slice(o, o + U * (2 * l + 1)) for (_, l, _), o in zip(op.irreps_in, op.in_offsets)],
         "Y": [slice(l * l, (l + 1) ** 2) for l in range(op.lmax_sh + 1)],
         "w": [slice(p * U, (p + 1) * U) for p in range(op.n_paths)],
+        "all": [slice(None)],
     }
+
+
+def _parity(plan_args, e, recv_rows, checks, what, blocks=None):
+    """Parity of the timed run against the oracle on the CPU-baseline sample:
+    checks is a list of (name, got, ref, kind), kind a key of the column blocks
+    (those of the CG plan unless given; rows already aligned); the
+    block-relative error of each and their max."""
+    blocks = blocks or _cg_blocks(plan_args)
     errs = {}
     for name, got, ref, kind in checks:
         got = np.asarray(got, dtype=np.float64).reshape(len(got), -1)
@@ -1007,6 +1015,9 @@ def bench_fc(args, torch, tpc, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
     step_ms = float(np.median(t))
+    # the timed step's results (forward output, receiver-sorted grad_Y and grad_R)
+    snap = (dict(out=out.cpu().numpy(), gY=gY.cpu().numpy(), gR=gR.cpu().numpy(), perm=g.perm.cpu().numpy()[:E])
+            if not args.no_cpu_baseline else None)
     reps, rounds = 5, max(2, args.steps // 5)
     kt = {n: float(timed_kernel(lambda c, f=fn: f(), 1, reps, rounds).mean()) for n, fn in phases.items()}
     # second-order backward, all four cotangents (here the first backward's outputs)
@@ -1047,27 +1058,32 @@ def bench_fc(args, torch, tpc, dev):
                      "note": "inputs and outputs once plus one write and one read of each "
                              "node-sized state the phase uses", "traffic": None},
         "cpu_baseline": None,
+        "parity": None,
     }
     if not args.no_cpu_baseline:
         import oracle
         op = oracle.build_plan(irreps, lsh, lout)
         from threadpoolctl import threadpool_limits
-        n_s = 12000
-        order = np.argsort(wl.dst, kind="stable")[:n_s]
-        e = np.sort(order)
+        e, what = _receiver_sample(wl.src, wl.dst, 12000)
         nodes = np.unique(np.concatenate([wl.src[e], wl.dst[e]]))
         src, dst = np.searchsorted(nodes, wl.src[e]), np.searchsorted(nodes, wl.dst[e])
         with threadpool_limits(1):
             t0 = time.perf_counter()
             Yo = oracle.sh_real(lsh, wl.r[e])
-            oracle.fc_conv_fwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th)
-            oracle.fc_conv_bwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th, go_h[nodes])
+            ro = oracle.fc_conv_fwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th)
+            rb = oracle.fc_conv_bwd(op, src, dst, len(nodes), wl.x[nodes], Yo, R[e], Th, go_h[nodes])
             dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": len(e) / dt, "unit": "edges/s", "cores": 1,
                                "kind": "oracle",
-                               "sample": f"{len(e)} of {E} edges (the first receivers), harmonics + "
-                                         f"fwd + bwd once, float64 (per-edge weights formed), one "
-                                         f"process with one BLAS thread, {dt:.2f} s"}
+                               "sample": f"{what}, harmonics + fwd + bwd once, float64 (per-edge "
+                                         f"weights formed), one process with one BLAS thread, {dt:.2f} s"}
+        recv = np.unique(wl.dst[e])
+        pos = np.empty(E, dtype=np.int64)
+        pos[snap["perm"]] = np.arange(E)
+        res["parity"] = _parity((irreps, lsh, lout), e, len(recv), [
+            ("out", snap["out"][recv], ro[np.searchsorted(nodes, recv)], "out"),
+            ("grad_Y", snap["gY"][pos[e]], rb[1], "Y"),
+            ("grad_R", snap["gR"][pos[e]], rb[2], "all")], what)
     print(json.dumps(res))
 
 
@@ -1131,6 +1147,9 @@ def bench_gaunt(args, torch, tpc, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
     step_ms = float(np.median(t))
+    # the timed step's results (receiver-sorted grad_Y and grad_w)
+    snap = (dict(out=out.cpu().numpy(), gx=gx.cpu().numpy(), gY=gY.cpu().numpy(), gw=gw.cpu().numpy(),
+                 perm=g.perm.cpu().numpy()[:E]) if not args.no_cpu_baseline else None)
     reps, rounds = 10, max(2, args.steps // 5)
     kt = {n: float(timed_kernel(lambda c, f=fn: f(), 1, reps, rounds).mean()) for n, fn in kernels.items()}
     # second-order backward, all three cotangents (here the first backward's outputs)
@@ -1170,6 +1189,7 @@ def bench_gaunt(args, torch, tpc, dev):
                              "compulsory bytes are in hbm_frac_per_kernel",
                      "traffic": traffic},
         "cpu_baseline": None,
+        "parity": None,
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -1180,10 +1200,21 @@ def bench_gaunt(args, torch, tpc, dev):
             for _ in range(3):
                 t0 = time.perf_counter()
                 Yo = oracle.sh_real(lsh, wl.r)
-                oracle.gaunt_conv_fwd(gp, wl.src, wl.dst, N, wl.x, Yo, w)
-                oracle.gaunt_conv_bwd(gp, wl.src, wl.dst, N, wl.x, Yo, w, go_h)
+                ro = oracle.gaunt_conv_fwd(gp, wl.src, wl.dst, N, wl.x, Yo, w)
+                rb = oracle.gaunt_conv_bwd(gp, wl.src, wl.dst, N, wl.x, Yo, w, go_h)
                 dts.append(time.perf_counter() - t0)
         dt = float(np.median(dts))
+        pos = np.empty(E, dtype=np.int64)
+        pos[snap["perm"]] = np.arange(E)
+        Ug = gp.U
+        blocks = {"out": [slice(Ug * l * l, Ug * (l + 1) ** 2) for l in range(lout + 1)],
+                  "x": [slice(o, o + Ug * (2 * l + 1)) for l, o in zip(gp.degrees, gp.in_offsets)],
+                  "Y": [slice(l * l, (l + 1) ** 2) for l in range(lsh + 1)],
+                  "w": [slice(l * Ug, (l + 1) * Ug) for l in range(lsh + 1)]}
+        res["parity"] = _parity(None, None, N, [
+            ("out", snap["out"], ro, "out"), ("grad_x", snap["gx"], rb[0], "x"),
+            ("grad_Y", snap["gY"][pos], rb[1], "Y"), ("grad_w", snap["gw"][pos], rb[2], "w")],
+            f"the whole workload ({E} edges)", blocks=blocks)
         res["cpu_baseline"] = {"value": E / dt, "unit": "edges/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"the whole workload ({E} edges), harmonics + Gaunt fwd + bwd, "
