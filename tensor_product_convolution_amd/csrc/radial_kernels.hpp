@@ -624,15 +624,20 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
 }
 
 // Forward (SEND = false) and sender pass (SEND = true), chunk-major: workgroup
-// (block, chunk c) keeps chunk c's W2 slice in LDS for its whole life and its
-// NW waves walk nodes i = block*NW + wave, + gridDim.x*NW, ...  Per 16-edge
-// tile the hidden values come from the small MFMA, the weights of every path
-// from the w-MFMA (A = hidden rows of the tile's edges, B = the slice), so lane
-// l holds w[edge 4(l/16) + r][channel 16c + l%16]; the per-lane products then
-// run over the lane's four edges.  Forward: out[i] of receiver i (edges
-// grouped by receiver, x of each sender gathered).  Sender pass: grad_x[j] of
-// sender j (edges grouped by sender through t_perm, grad_out of each receiver
-// gathered).  Each output row chunk is written once; no atomics.
+// (block, chunk c) keeps chunk c's W2 slice in LDS for its whole life.  Each
+// lane group g (16 lanes, the chunk's 16 channels) of each wave walks its own
+// nodes: n = (block*NW + wave)*4 + g, + gridDim.x*NW*4, ..., four edges of its
+// node per step.  A step is one 16-edge tile whose rows 4g .. 4g+3 are group
+// g's edges: the hidden values come from the small MFMA, the weights of every
+// path from the w-MFMA (A = hidden rows of the tile's edges, B = the slice),
+// so lane l holds w[edge 4(l/16) + r][channel 16c + l%16], exactly the
+// weights of its own group's four edges, and accumulates its node's whole sum
+// in registers (a node's edges pad only to a multiple of four, not of 16, and
+// no reduction across groups is needed).  Forward: out[i] of receiver i
+// (edges grouped by receiver, x of each sender gathered).  Sender pass:
+// grad_x[j] of sender j (edges grouped by sender through t_perm, grad_out of
+// each receiver gathered).  Each output row chunk is written once (zeros for
+// a node without edges); no atomics.
 // GEOM: Y holds the edge vectors r [E][3]; r_len unused
 template <class S, int U, int NB, int NH, int NW, bool SEND, bool GEOM = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
@@ -653,64 +658,89 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   stage_w2<S, U, NH, NW>(w2s, rp.W2, c, wv, lane);
   wait_vmcnt<0>();
   __syncthreads();
-  for (int i = blockIdx.x * NW + wv; i < n_nodes; i += gridDim.x * NW) {
-    const int beg = ptr[i], end = ptr[i + 1];
-    float acc[NA];
+  float acc[NA];
 #pragma unroll
-    for (int o = 0; o < NA; ++o) acc[o] = 0.f;
-    for (int t0 = beg; t0 < end; t0 += 16) {
-      // gathered operands of the lane's four edges, requested first so that
-      // they arrive while the hidden layer and the weights are computed
-      constexpr int NF = SEND ? S::OC : S::XC;
-      float fr[4][NF], yr[4][S::YC];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int q = t0 + 4 * g + r;
-        const int qc = q < end ? q : end - 1;       // weights of a padded edge are zero
-        const int e = SEND ? perm[qc] : qc;
-        radial_edge_y<S, GEOM>(Y, e, yr[r]);
-        if constexpr (SEND) load_o_channel<S, U>(feat, other[qc], u, fr[r]);
-        else load_x_channel<S, U>(feat, other[qc], u, fr[r]);
-      }
-      __builtin_amdgcn_sched_barrier(0);            // keep the loads ahead of the MFMAs
-      const int qa = t0 + e16;
-      const bool va = qa < end;
-      const int qac = va ? qa : end - 1;
-      float bq[NB / 4], hB[NH / 4], ds[NH / 4];
-      hidden_T<NB, NH>(radial_edge_len<GEOM>(Y, r_len, SEND ? perm[qac] : qac), va, rp, w1a, g, bq, hB, ds);
-      f32x4 C[S::NP];
-#pragma unroll
-      for (int p = 0; p < S::NP; ++p) {
-        C[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const float* wb = w2s + p * 16 + e16;
-#pragma unroll
-        for (int k = 0; k < NH / 4; ++k) C[p] = mfma_16x16x4(hB[k], wb[hid_T(k, g) * L::WS], C[p]);
-      }
-      static_for<4>([&](auto R) {
-        float wr[S::NP];
-#pragma unroll
-        for (int p = 0; p < S::NP; ++p) wr[p] = C[p][int(R)];
-        if constexpr (SEND) edge_bwd_send<S>(yr[R], wr, fr[R], acc);
-        else edge_fwd<S>(fr[R], yr[R], wr, acc);
-        __builtin_amdgcn_sched_barrier(0);          // one edge's products live at a time
+  for (int o = 0; o < NA; ++o) acc[o] = 0.f;
+  // this lane group's cursor: node, next edge, end of the node's edges
+  const int gstride = gridDim.x * NW * 4;
+  int node = (blockIdx.x * NW + wv) * 4 + g, q = 0, qend = 0;
+  auto store = [&]() {                              // the group's node row, this channel
+    if constexpr (SEND) {
+      float* row = outp + (size_t)node * (U * S::XC);
+      static_for<S::NIN>([&](auto I) {
+        constexpr int d = 2 * S::ls.v[I] + 1;
+        constexpr int xo = S::xoff(I);
+        static_for<d>([&](auto A) { row[U * xo + u * d + A] = acc[xo + A]; });
+      });
+    } else {
+      float* row = outp + (size_t)node * (U * S::OC);
+      static_for<S::NO>([&](auto K) {
+        constexpr OutInfo oi = S::outs.o[K];
+        constexpr int d = 2 * oi.l + 1;
+        static_for<d>([&](auto C2) { row[U * oi.ko + u * d + C2] = acc[oi.ko + C2]; });
       });
     }
-    reduce_quads<NA>(acc);
-    if (lane < 16) {
-      if constexpr (SEND) {
-        float* row = outp + (size_t)i * (U * S::XC);
-        static_for<S::NIN>([&](auto I) {
-          constexpr int d = 2 * S::ls.v[I] + 1;
-          constexpr int xo = S::xoff(I);
-          static_for<d>([&](auto A) { row[U * xo + u * d + A] = acc[xo + A]; });
-        });
-      } else {
-        float* row = outp + (size_t)i * (U * S::OC);
-        static_for<S::NO>([&](auto K) {
-          constexpr OutInfo oi = S::outs.o[K];
-          constexpr int d = 2 * oi.l + 1;
-          static_for<d>([&](auto C2) { row[U * oi.ko + u * d + C2] = acc[oi.ko + C2]; });
-        });
+  };
+  auto seek = [&]() {                               // next node with edges; zero rows on the way
+    while (node < n_nodes) {
+      q = ptr[node];
+      qend = ptr[node + 1];
+      if (q < qend) break;
+      store();                                      // acc is zero here
+      node += gstride;
+    }
+  };
+  seek();
+  // all groups of the wave step together until every one has run out of nodes
+  while (__ballot(node < n_nodes) != 0ull) {
+    const bool act = node < n_nodes;
+    // gathered operands of the lane's four edges, requested first so that
+    // they arrive while the hidden layer and the weights are computed; a slot
+    // past the node's edges (or of a group without a node) reads a valid edge
+    // and gets zero weights
+    constexpr int NF = SEND ? S::OC : S::XC;
+    float fr[4][NF], yr[4][S::YC];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qq = q + r;
+      const int qc = act ? (qq < qend ? qq : qend - 1) : 0;
+      const int e = SEND ? perm[qc] : qc;
+      radial_edge_y<S, GEOM>(Y, e, yr[r]);
+      if constexpr (SEND) load_o_channel<S, U>(feat, other[qc], u, fr[r]);
+      else load_x_channel<S, U>(feat, other[qc], u, fr[r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);              // keep the loads ahead of the MFMAs
+    // hidden values of tile row e16: edge e16 % 4 of group e16 / 4's node
+    const int owner = 16 * (e16 >> 2);
+    const int qa = __shfl(q, owner, 64) + (e16 & 3);
+    const bool va = __shfl(act ? qend : 0, owner, 64) > qa;
+    const int qac = va ? qa : 0;
+    float bq[NB / 4], hB[NH / 4], ds[NH / 4];
+    hidden_T<NB, NH>(radial_edge_len<GEOM>(Y, r_len, SEND ? perm[qac] : qac), va, rp, w1a, g, bq, hB, ds);
+    f32x4 C[S::NP];
+#pragma unroll
+    for (int p = 0; p < S::NP; ++p) {
+      C[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* wb = w2s + p * 16 + e16;
+#pragma unroll
+      for (int k = 0; k < NH / 4; ++k) C[p] = mfma_16x16x4(hB[k], wb[hid_T(k, g) * L::WS], C[p]);
+    }
+    static_for<4>([&](auto R) {
+      float wr[S::NP];
+#pragma unroll
+      for (int p = 0; p < S::NP; ++p) wr[p] = C[p][int(R)];
+      if constexpr (SEND) edge_bwd_send<S>(yr[R], wr, fr[R], acc);
+      else edge_fwd<S>(fr[R], yr[R], wr, acc);
+      __builtin_amdgcn_sched_barrier(0);          // one edge's products live at a time
+    });
+    if (act) {
+      q += 4;
+      if (q >= qend) {                              // the node is done: its row, then the next node
+        store();
+#pragma unroll
+        for (int o = 0; o < NA; ++o) acc[o] = 0.f;
+        node += gstride;
+        seek();
       }
     }
   }

@@ -67,10 +67,17 @@ int w2_blocks(int n_nodes) {
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 constexpr int kNodeWaves = 4;                             // waves per forward / sender workgroup
-// chunk-major grid: (node blocks, chunks); about two workgroups per CU in all
+// chunk-major grid: (node blocks, chunks); about two workgroups per CU in all.
+// node_grid: a node per wave at a time (second-order passes); group_grid: a
+// node per 16-lane group (k_radial_node), four per wave
 template <int U>
 dim3 node_grid(int n_nodes) {
   const int want = (n_nodes + kNodeWaves - 1) / kNodeWaves, cap = 512 / (U / 16);
+  return dim3(want < cap ? (want > 0 ? want : 1) : cap, U / 16);
+}
+template <int U>
+dim3 group_grid(int n_nodes) {
+  const int want = (n_nodes + 4 * kNodeWaves - 1) / (4 * kNodeWaves), cap = 512 / (U / 16);
   return dim3(want < cap ? (want > 0 ? want : 1) : cap, U / 16);
 }
 
@@ -92,7 +99,7 @@ hipError_t launch_radial_fwd_as(const RadialArgs& a) {
   using S = typename R::Sig;
   if (a.n_nodes == 0) return hipSuccess;
   RadialParams rp{a.r_cut, a.W1, a.W2};
-  hipLaunchKernelGGL((k_radial_node<S, U, kNB, kNH, kNodeWaves, false, GEOM>), node_grid<U>(a.n_nodes),
+  hipLaunchKernelGGL((k_radial_node<S, U, kNB, kNH, kNodeWaves, false, GEOM>), group_grid<U>(a.n_nodes),
                      dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.row_ptr, nullptr, a.col, a.x, a.Y,
                      a.r_len, rp, a.out);
   return hipGetLastError();
@@ -149,7 +156,7 @@ hipError_t launch_radial_bwd_as(const RadialArgs& a) {
                        part2, nb2, n, a.grad_W2);
   }
   if (a.grad_x && a.n_nodes > 0)
-    hipLaunchKernelGGL((k_radial_node<S, U, kNB, kNH, kNodeWaves, true, GEOM>), node_grid<U>(a.n_nodes),
+    hipLaunchKernelGGL((k_radial_node<S, U, kNB, kNH, kNodeWaves, true, GEOM>), group_grid<U>(a.n_nodes),
                        dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.t_row_ptr, a.t_perm, a.t_col,
                        a.grad_out, a.Y, a.r_len, rp, a.grad_x);
   return hipGetLastError();
