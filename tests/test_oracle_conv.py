@@ -433,21 +433,22 @@ def test_silu_derivatives_against_sympy():
             assert abs(got - want) <= 1e-14 * max(1.0, abs(want))
 
 
-def _radial_small(seed, n_nodes=10):
-    plan = oracle.build_plan("4x0e+4x1o+4x2e", 2, 2)
+def _radial_small(seed, n_nodes=10, lmax=2):
+    irr = "4x0e+4x1o+4x2e" if lmax == 2 else "3x0e+3x1o+3x2e+3x3o"
+    plan = oracle.build_plan(irr, lmax, lmax)
     wl = make_workload("stream", dims_of(plan), seed=seed, n_nodes=n_nodes)
     f64 = lambda a: np.asarray(a, dtype=np.float64)
-    ins = dict(x=f64(wl.x), Y=oracle.sh_real(2, f64(wl.r)), r_len=f64(wl.r_len), W1=f64(wl.W1),
+    ins = dict(x=f64(wl.x), Y=oracle.sh_real(lmax, f64(wl.r)), r_len=f64(wl.r_len), W1=f64(wl.W1),
                W2=f64(wl.W2), Wmix=f64(wl.Wmix), g2=f64(wl.g))
     return plan, wl, ins
 
 
-@pytest.mark.parametrize("with_mix", [True, False])
-def test_radial_double_backward_by_differences(with_mix):
+@pytest.mark.parametrize("with_mix,lmax", [(True, 2), (False, 2), (True, 3)])
+def test_radial_double_backward_by_differences(with_mix, lmax):
     """Central differences of the first backward's loss in every input:
     L = <ggx, grad_x> + <ggY, grad_Y> + <ggr, grad_rlen> (the first backward
     is itself pinned by differences of the forward)."""
-    plan, wl, ins = _radial_small(4)
+    plan, wl, ins = _radial_small(4, lmax=lmax)
     if not with_mix:
         ins["Wmix"] = None
     rng = np.random.default_rng(12)
