@@ -793,21 +793,18 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     kt_r = {"fwd_r": float(timed_kernel(lambda c: tpc.forward_radial_r(plan, g, x, r_sorted, W1, W2, None,
                                                                        out=pre), 1, reps, rounds).mean())}
     # second-order backward with cotangents on grad_x, grad_Y and grad_rlen (here
-    # the first backward's outputs, as in a loss on forces), all outputs; built
-    # for the lmax-2 layer only
-    dbl_ms = None
-    if lsh == 2:
-        grl_c = outs_f["rlen"]
-        tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, want=("x", "Y", "rlen"), outs=outs_f, ws=ws)
-        d_outs = {"x": torch.empty_like(x), "Y": torch.empty_like(Y), "rlen": torch.empty_like(rl),
-                  "W1": torch.empty_like(W1), "W2": torch.empty_like(W2), "Wmix": torch.empty_like(Wm),
-                  "g": torch.empty_like(go)}
-        ws2 = torch.empty(tpc.radial_double_workspace(plan, N, True), dtype=torch.uint8, device=dev)
-        dbl = lambda c: tpc.double_backward_radial(plan, g, x, Y, rl, W1, W2, go, Wmix=Wm, gg_x=outs["x"],
-                                                   gg_Y=outs["Y"], gg_rlen=grl_c, outs=d_outs, ws=ws2)
-        dbl(0)
-        dbl_ms = float(timed_kernel(dbl, 1, 2, rounds).mean())
-        del ws2, d_outs
+    # the first backward's outputs, as in a loss on forces), all outputs
+    grl_c = outs_f["rlen"]
+    tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, want=("x", "Y", "rlen"), outs=outs_f, ws=ws)
+    d_outs = {"x": torch.empty_like(x), "Y": torch.empty_like(Y), "rlen": torch.empty_like(rl),
+              "W1": torch.empty_like(W1), "W2": torch.empty_like(W2), "Wmix": torch.empty_like(Wm),
+              "g": torch.empty_like(go)}
+    ws2 = torch.empty(tpc.radial_double_workspace(plan, N, True), dtype=torch.uint8, device=dev)
+    dbl = lambda c: tpc.double_backward_radial(plan, g, x, Y, rl, W1, W2, go, Wmix=Wm, gg_x=outs["x"],
+                                               gg_Y=outs["Y"], gg_rlen=grl_c, outs=d_outs, ws=ws2)
+    dbl(0)
+    dbl_ms = float(timed_kernel(dbl, 1, 2, rounds).mean())
+    del ws2, d_outs
     fl = radial_flops(E, P, U, NH)
     mix_flops = 2.0 * N * plan.outdim * U            # one application of the channel mix
     names = ["fwd", "bwd_recv", "bwd_w2", "bwd_send"]
@@ -847,10 +844,8 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     }
     dbl_flops = fl["double_bwd"] + 3 * mix_flops                  # mix: g, out_dot, d_Wmix
     res["double_bwd_ms"] = dbl_ms
-    res["double_bwd_mfma_frac"] = (dbl_flops / (dbl_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS
-                                   if dbl_ms else None)
-    res["double_bwd_note"] = "not built for this signature" if dbl_ms is None else (
-                              "second-order backward (d_x, d_Y, d_rlen, d_W1, d_W2, d_Wmix, d_grad_out "
+    res["double_bwd_mfma_frac"] = dbl_flops / (dbl_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS
+    res["double_bwd_note"] = ("second-order backward (d_x, d_Y, d_rlen, d_W1, d_W2, d_Wmix, d_grad_out "
                               "for cotangents on grad_x, grad_Y and grad_rlen), per call after a flush; "
                               "not part of the step; MFMA fraction on its ten network products per edge "
                               "and three applications of the mix")

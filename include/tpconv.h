@@ -504,9 +504,7 @@ tp_status tp_conv_backward_radial_r(tp_plan_t plan, const tp_graph* graph, const
  * on chip, never stored; parameter gradients are fixed-order sums through ws
  * (tp_conv_radial_double_workspace bytes), so results are bitwise
  * reproducible.  x, gg_x, grad_out and W2 must be 16-byte aligned
- * (TP_ERR_ARG); edge arrays receiver-sorted.  Built for the lmax-2 radial
- * plans; the lmax-3 ones return TP_ERR_UNSUPPORTED (here and from the
- * workspace query). */
+ * (TP_ERR_ARG); edge arrays receiver-sorted. */
 tp_status tp_conv_double_backward_radial(tp_plan_t plan, const tp_graph* graph, const float* x,
                                          const float* Y, const float* r_len, const float* W1,
                                          const float* W2, const float* Wmix, const float* grad_out,

@@ -1135,7 +1135,7 @@ tp_status tp_conv_radial_double_workspace(tp_plan_t plan, int32_t n_nodes, int32
   if (!plan || !bytes) return set_error(TP_ERR_ARG, "tp_conv_radial_double_workspace: NULL argument");
   if (!plan->rs) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
   if (!plan->rs->dbl_workspace)
-    return set_error(TP_ERR_UNSUPPORTED, "no second-order radial kernels for this signature (lmax 2 only)");
+    return set_error(TP_ERR_UNSUPPORTED, "no second-order radial kernels for this signature");
   if (n_nodes < 0) return set_error(TP_ERR_ARG, "tp_conv_radial_double_workspace: negative size");
   size_t b = plan->rs->dbl_workspace(n_nodes, 0);
   if (with_mix) {
@@ -1160,7 +1160,7 @@ tp_status tp_conv_double_backward_radial(tp_plan_t plan, const tp_graph* graph, 
   if (!plan) return set_error(TP_ERR_ARG, std::string(fn) + ": plan is NULL");
   if (!plan->rs) return set_error(TP_ERR_UNSUPPORTED, "plan has no radial network");
   if (!plan->rs->dbl)
-    return set_error(TP_ERR_UNSUPPORTED, "no second-order radial kernels for this signature (lmax 2 only)");
+    return set_error(TP_ERR_UNSUPPORTED, "no second-order radial kernels for this signature");
   tp_status s = check_graph(graph, d_x != nullptr);
   if (s != TP_OK) return s;
   const int N = graph->n_nodes, E = graph->n_edges;

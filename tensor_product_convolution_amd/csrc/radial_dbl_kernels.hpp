@@ -496,8 +496,10 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1,
 //           contracted with the hidden values h;
 //   KIND 1: the tangent's cotangent dv = gw(x, Y, g), contracted with the
 //           hidden tangent gg_r SiLU'(pre) a.
-// Each launch writes its own per-workgroup partials.
-template <class S, int U, int NB, int NH, int KIND>
+// Each launch writes its own per-workgroup partials; like k_radial_bwd_w2 a
+// launch covers the paths P0 .. P0 + NPG - 1 (wide signatures run one launch
+// per path group, each writing its own columns).
+template <class S, int U, int NB, int NH, int KIND, int P0 = 0, int NPG = S::NP>
 __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_per_eu(2)))
     k_radial_dbl_w2(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                     const float* __restrict__ x, const float* __restrict__ ggx, const float* __restrict__ Y,
@@ -505,10 +507,11 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
                     const float* __restrict__ ggr, RadialParams rp, const float* __restrict__ gout,
                     float* __restrict__ part) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NB % 4 == 0, "radial tiling");
+  static_assert(P0 >= 0 && NPG > 0 && P0 + NPG <= S::NP, "path group");
   constexpr int NW = NH / 16;
   constexpr int LD = S::NP * U;
   constexpr int RS = 20, PS = 16 * RS;
-  constexpr int TILE = S::NP * PS;
+  constexpr int TILE = NPG * PS;
   __shared__ __attribute__((aligned(16))) float s_gw[NW * TILE];
   __shared__ float s_r[NW * 16];                    // edge lengths of the tiles (-1: no edge)
   __shared__ float s_g[NW * 16];                    // their length cotangents (tangent term)
@@ -516,9 +519,9 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e16 = lane & 15, g = lane >> 4;
   const int u = 16 * c + e16;
-  f32x4 acc[S::NP];
+  f32x4 acc[NPG];
 #pragma unroll
-  for (int p = 0; p < S::NP; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < NPG; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
   float w1b[NB / 4];
 #pragma unroll
   for (int s = 0; s < NB / 4; ++s) w1b[s] = rp.W1[(4 * s + g) * NH + 16 * wv + e16];
@@ -564,8 +567,8 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
 #pragma unroll
           for (int b = 0; b < S::YC; ++b) gyr[b] = ggY ? ggY[(size_t)qc * S::YC + b] : 0.f;
         }
-        static_for<S::NP>([&](auto P) {
-          constexpr PathInfo pi = S::paths.p[P];
+        static_for<NPG>([&](auto G) {
+          constexpr PathInfo pi = S::paths.p[P0 + G];
           constexpr int D2 = 2 * pi.l2 + 1;
           float zx[D2];
           zform_scaled<pi.l1, pi.l2, pi.l3, pi.xo, pi.ko>(xr, gr, zx);
@@ -580,7 +583,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
           } else {
             static_for<D2>([&](auto B2) { s = fmaf(yr[pi.yo + B2], zx[B2], s); });
           }
-          gw_own[P * PS + (4 * g + r) * RS + e16] = s;
+          gw_own[G * PS + (4 * g + r) * RS + e16] = s;
         });
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -625,7 +628,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
       }
       const float* gtl = s_gw + tw * TILE + 4 * g * RS + e16;
 #pragma unroll
-      for (int p = 0; p < S::NP; ++p)
+      for (int p = 0; p < NPG; ++p)
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[p] = mfma_16x16x4(hA[k], gtl[p * PS + k * RS], acc[p]);
     }
@@ -633,9 +636,9 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
   }
   float* pb = part + (size_t)blockIdx.x * NH * LD;
 #pragma unroll
-  for (int p = 0; p < S::NP; ++p)
+  for (int p = 0; p < NPG; ++p)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pb[(size_t)(16 * wv + 4 * g + t) * LD + p * U + u] = acc[p][t];
+    for (int t = 0; t < 4; ++t) pb[(size_t)(16 * wv + 4 * g + t) * LD + (P0 + p) * U + u] = acc[p][t];
 }
 
 }  // namespace tpc

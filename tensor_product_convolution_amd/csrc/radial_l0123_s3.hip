@@ -5,14 +5,15 @@
 // eight waves that share the slice (two per SIMD at 256 registers, with a few
 // spilled: 1.03 against 1.37 ms with four waves on 4,096 atoms at 64
 // channels, the latency of each path's LDS -> MFMA -> VALU -> MFMA chain
-// hidden by the second wave).  grad_W2 runs in three launches of at most 12
-// paths each.  The second-order kernels are not built for this signature:
-// their register state at 34 paths does not fit a wave.
+// hidden by the second wave).  grad_W2 and the two d_W2 terms of the
+// second-order pass run in three launches of at most 12 paths each.  The
+// second-order node and receiver passes hold more state than a wave's 512
+// registers at 34 paths and spill (one wave per SIMD).
 #include "radial_launch.hpp"
 
 namespace tpc {
 
-using RadialL0123 = RadialSig<Sig<3, 3, 0, 1, 2, 3>, 12, 8, false>;
+using RadialL0123 = RadialSig<Sig<3, 3, 0, 1, 2, 3>, 12, 8, true>;
 
 const RadialSet* radial_l0123_s3(int mul, int nb, int nh) {
   if (nb != kNB || nh != kNH) return nullptr;

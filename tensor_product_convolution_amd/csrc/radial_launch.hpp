@@ -175,6 +175,20 @@ size_t radial_dbl_ws(int n_nodes, int /*n_edges*/) {
          (size_t)2 * w2_blocks<U>(n_nodes) * kNH * R::Sig::NP * U * sizeof(float);
 }
 
+// the two d_W2 terms' partials, one launch per term and path group
+template <class R, int U, int KIND, int G = 0>
+void launch_dbl_w2_groups(const RadialArgs& a, const RadialParams& rp, int nb2, float* part2) {
+  using S = typename R::Sig;
+  constexpr int P0 = G * R::npg;
+  if constexpr (P0 < S::NP) {
+    constexpr int N = S::NP - P0 < R::npg ? S::NP - P0 : R::npg;
+    hipLaunchKernelGGL((k_radial_dbl_w2<S, U, kNB, kNH, KIND, P0, N>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)),
+                       0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.gg_x, a.Y, a.gg_Y, a.r_len, a.gg_rlen,
+                       rp, a.grad_out, part2);
+    launch_dbl_w2_groups<R, U, KIND, G + 1>(a, rp, nb2, part2);
+  }
+}
+
 // a.grad_out is the unmixed upstream gradient g; a.out receives out_dot (d_g
 // before the mix); cotangents a.gg_* may be null (zeros); outputs may be null
 template <class R, int U>
@@ -201,12 +215,8 @@ hipError_t launch_radial_dbl(const RadialArgs& a) {
   }
   if (a.d_W2) {
     const size_t half = (size_t)nb2 * kNH * S::NP * U;
-    hipLaunchKernelGGL((k_radial_dbl_w2<S, U, kNB, kNH, 0>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)), 0,
-                       a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.gg_x, a.Y, a.gg_Y, a.r_len, a.gg_rlen,
-                       rp, a.grad_out, part2);
-    hipLaunchKernelGGL((k_radial_dbl_w2<S, U, kNB, kNH, 1>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)), 0,
-                       a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.gg_x, a.Y, a.gg_Y, a.r_len, a.gg_rlen,
-                       rp, a.grad_out, part2 + half);
+    launch_dbl_w2_groups<R, U, 0>(a, rp, nb2, part2);
+    launch_dbl_w2_groups<R, U, 1>(a, rp, nb2, part2 + half);
     const long long n = (long long)kNH * S::NP * U;
     hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, a.stream,
                        part2, 2 * nb2, n, a.d_W2);

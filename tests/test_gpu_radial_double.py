@@ -38,11 +38,11 @@ def _cotangents(op, n_nodes, n_edges, seed):
             rng.normal(size=n_edges).astype(np.float32))
 
 
-def _gpu_dbl(tpc, plan, wl, mix, g2, ggx, ggY, ggr, want=ALL):
+def _gpu_dbl(tpc, plan, wl, mix, g2, ggx, ggY, ggr, want=ALL, lmax=2):
     """second-order backward on the GPU (cotangents in original edge order,
     gathered to receiver order); outputs as numpy, edge arrays receiver-sorted"""
     g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
-    Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+    Y = tpc.sph_harm(lmax, tpc.gather_rows(T(wl.r), g.perm))
     rl = tpc.gather_rows(T(wl.r_len), g.perm)
     opt = lambda a, gather: None if a is None else (tpc.gather_rows(T(a), g.perm) if gather else T(a))
     res = tpc.double_backward_radial(plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), T(g2),
@@ -56,8 +56,8 @@ def _gpu_dbl(tpc, plan, wl, mix, g2, ggx, ggY, ggr, want=ALL):
     return out
 
 
-def _ref(op, wl, mix, g2, ggx, ggY, ggr):
-    Yo = oracle.sh_real(2, wl.r)
+def _ref(op, wl, mix, g2, ggx, ggY, ggr, lmax=2):
+    Yo = oracle.sh_real(lmax, wl.r)
     return oracle.tp_conv_radial_double_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Yo, wl.r_len, wl.W1,
                                             wl.W2, wl.Wmix if mix else None, g2, 8, RC, ggx=ggx, ggY=ggY,
                                             ggr=ggr)

@@ -4,7 +4,9 @@ float64 oracle: forward with and without the channel mix, the backward
 (grad_x, grad_Y, grad_r_len, grad_W1, grad_W2 per path, grad_Wmix, forces) and
 the edge-vector forms, on graphs with uniform degrees 5..30, a hub-heavy
 power law, and a 4,200-atom graph that fills the persistent grids of the
-receiver pass (512 workgroups of eight waves) and of the grad_W2 pass.  Same bar as the
+receiver pass (512 workgroups of eight waves) and of the grad_W2 pass; and
+the second-order backward (cotangents on grad_x, grad_Y and grad_r_len), incl.
+a 1,100-atom graph that fills its receiver pass's grid.  Same bar as the
 other signatures: every block within 1e-4 of max|ref| of that block."""
 import numpy as np
 import pytest
@@ -147,3 +149,20 @@ def test_radial_l3_determinism(tpc):
     torch.cuda.synchronize()
     for s, t in zip(a, b):
         assert torch.equal(s, t)
+
+
+@pytest.mark.parametrize("U,graph,n,mix,only", [(16, "zipf", 300, False, None), (64, "lmax3", 120, True, None),
+                                                (32, "stream", 150, True, "r"), (16, "lmax3", 1100, True, None)])
+def test_radial_l3_double_backward_parity(tpc, U, graph, n, mix, only):
+    from tests.test_gpu_radial_double import _check, _cotangents, _gpu_dbl, _ref
+    say(f"radial lmax 3 double bwd U={U} graph={graph} n={n} mix={mix} only={only}")
+    op, wl = _inputs(U, graph, n, seed=U + 3 * n)
+    plan = tpc.Plan(_irreps(U), 3, 3, radial=(8, 64, RC), uvw=True)
+    ggx, ggY, ggr = _cotangents(op, wl.n_nodes, wl.n_edges, U + n)
+    if only == "r":                                  # the weights' tangent alone
+        ggx, ggY = None, None
+    res = _gpu_dbl(tpc, plan, wl, mix, wl.g, ggx, ggY, ggr, lmax=3)
+    ref = _ref(op, wl, mix, wl.g, ggx, ggY, ggr, lmax=3)
+    _check(op, res, ref, U, res["perm"])
+    if not mix:
+        assert res["dWm"] is None
