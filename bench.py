@@ -13,9 +13,16 @@ timed separately: it runs once per neighbour list, not per layer.
 
 Timing, every figure cold (nothing of the step's edge-sized inputs in L2 or
 the 256 MB Infinity Cache):
-  * steps: W untimed warm-up steps, then K timed steps, each preceded by a
-    1 GiB read of an unrelated buffer and bracketed by a pair of HIP events
-    on the stream the kernels run on (torch's current stream);
+  * steps: W untimed warm-up steps, then K timed steps back to back in one
+    bracket of HIP events on the stream the kernels run on (torch's current
+    stream), after a 1 GiB read of an unrelated buffer; the steps rotate
+    over enough full copies of everything a step touches (graph, features,
+    weights, harmonics, gradients, outputs) that a copy is reused only after
+    at least 1 GiB of other data, so no step finds its inputs in L2 or the
+    Infinity Cache.  Where that many copies would not reach 1 GiB (the
+    32-atom graph) and for the radial, fully connected and Gaunt lines, each
+    step follows the flush in its own event bracket; the direct-weight lines
+    report that isolated step beside the stream (ms_per_step_isolated);
   * kernels: back-to-back launches that rotate through enough copies of the
     edge-sized inputs and outputs that a copy is reused only after at least
     1 GiB of other edge data has been touched (one copy where a single
@@ -121,6 +128,9 @@ def algorithmic_bytes(N, E, P, U, ysh, xdim, outdim):
         # one-pass backward: w, Y, t_perm, t_col in, grad_w, grad_Y out; x, grad_out,
         # t_row_ptr in, grad_x out
         "bwd": E * (8 * P * U + 8 * ysh + 8) + 4 * N * (2 * xdim + outdim + 1),
+        # sender-grouped layout: the forward also reads e_pos, the backward no t_perm
+        "fwd_sg": E * (4 * P * U + 4 * ysh + 8) + node,
+        "bwd_sg": E * (8 * P * U + 8 * ysh + 4) + 4 * N * (2 * xdim + outdim + 1),
         # compulsory bytes of the whole step: each array once
         "step": E * (8 * P * U + 8 * ysh + 4) + 4 * N * (2 * xdim + 2 * outdim + 1),
         # second-order backward, each array once: w, gg_w, Y, gg_Y, col, t_perm,
@@ -172,10 +182,12 @@ def cg_flops(cnt):
                 grad_w and grad_Y folds over (path, b), grad_x folds over (a, b);
       bwd_recv  multiply + FMA per nonzero (Z form), grad_w and grad_Y folds;
       bwd_send  w g products, one FMA per nonzero, grad_x folds."""
-    return {"fwd": cnt["ab"] + 2 * cnt["nnz"] + 2 * cnt["d3"],
-            "bwd": cnt["gc"] + 4 * cnt["nnz"] + 4 * cnt["d2"] + 2 * cnt["ab"],
-            "bwd_recv": 3 * cnt["nnz"] + 4 * cnt["d2"],
-            "bwd_send": cnt["d3"] + 2 * cnt["nnz"] + 2 * cnt["ab"]}
+    fl = {"fwd": cnt["ab"] + 2 * cnt["nnz"] + 2 * cnt["d3"],
+          "bwd": cnt["gc"] + 4 * cnt["nnz"] + 4 * cnt["d2"] + 2 * cnt["ab"],
+          "bwd_recv": 3 * cnt["nnz"] + 4 * cnt["d2"],
+          "bwd_send": cnt["d3"] + 2 * cnt["nnz"] + 2 * cnt["ab"]}
+    fl["fwd_sg"], fl["bwd_sg"] = fl["fwd"], fl["bwd"]     # same arithmetic in the sender layout
+    return fl
 
 
 def radial_flops(E, P, U, NH):
@@ -497,6 +509,25 @@ def make_timers(torch, flush):
     return do_flush, timed_steps, timed_kernel
 
 
+def timed_stream(torch, flush, step_c, copies, k, rounds):
+    # k steps back to back in one event bracket (what a training loop
+    # issues), step s on copy s % copies of every array the step touches;
+    # copies are chosen so that one is reused only after at least 1 GiB of
+    # other data, so each step starts as cold as after a flush.  Returns
+    # the per-step time of each of `rounds` brackets.
+    res = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        flush.sum()   # 1 GiB read: L2 and the Infinity Cache hold unrelated clean lines
+        e0.record()
+        for s in range(k):
+            step_c(s % copies)
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / k)
+    return np.array(res)
+
+
 def copy_bandwidth(torch, dev, flush, nbytes=1 << 29):
     """GB/s of a plain device copy (read + write of nbytes each) after a flush: the
     practical ceiling of a kernel that writes as much as it reads."""
@@ -564,6 +595,15 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
     gYs = [torch.empty_like(Y) for _ in range(NC)] if not fwd_only else None
     gws = [torch.empty_like(w) for _ in range(NC)] if not fwd_only else None
 
+    # fwd+bwd signatures with a one-pass backward are also timed with their edge
+    # rows in the sender grouping (tp_conv_forward_sg / tp_conv_backward_sg),
+    # reported beside the step (which uses the receiver-sorted layout)
+    sg = one_pass_backward(lsh) and not fwd_only
+    if sg:
+        e_pos = tpc.graph_sender_positions(g)
+        Ygs = [tpc.gather_rows(Yc, g.t_perm) for Yc in Ys]
+        wgs = [tpc.gather_rows(wc, g.t_perm) for wc in ws]
+
     def step():
         tpc.forward(plan, g, x, Y, w, out=out)
         if not fwd_only:
@@ -579,6 +619,9 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
 
             def both():
                 step()
+                if sg:      # the sender-grouped layout's kernels as well
+                    tpc.forward_sg(plan, g, e_pos, x, Ygs[0], wgs[0], out=out)
+                    tpc.backward_sg(plan, g, x, Ygs[0], wgs[0], go, outs=(gx, gYs[0], gws[0]))
                 tpc.forward_r(plan, g, x, r_c, w, out=out)
                 tpc.backward_r(plan, g, x, r_c, w, go, outs=(gx, gr_c, gws[0]))
             counters_run(torch, dev, flush, both, name)
@@ -606,6 +649,11 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
         extras["double_bwd"] = lambda c: tpc.double_backward(plan, g, x, Ys[c], ws[c], go, gx, gYs[c],
                                                              gws[c])
         # the same step from the edge vectors: harmonics on chip, grad_r in place of grad_Y
+        if sg:
+            # the step's kernels with the edge rows in the sender grouping
+            kernels["fwd_sg"] = lambda c: tpc.forward_sg(plan, g, e_pos, x, Ygs[c], wgs[c], out=out)
+            kernels["bwd_sg"] = lambda c: tpc.backward_sg(plan, g, x, Ygs[c], wgs[c], go,
+                                                          outs=(gx, gYs[c], gws[c]))
         rs = [r_sorted] + [r_sorted.clone() for _ in range(NC - 1)]
         grs = [torch.empty_like(r_sorted) for _ in range(NC)]
         geom = {"fwd_r": lambda c: tpc.forward_r(plan, g, x, rs[c], ws[c], out=out),
@@ -623,16 +671,80 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
         torch.cuda.synchronize()
         gb.append(e0.elapsed_time(e1))
 
+    # Timed steps.  Where the workload is large enough that STEP_COPIES full
+    # copies of everything a step touches (graph, x, Y, w, grad_out and the
+    # outputs) hold at least 1 GiB, the K steps run back to back in one event
+    # bracket over rotating copies (cold without a flush between steps);
+    # otherwise (the 32-atom graph) each step follows a flush in its own
+    # bracket.  The isolated flushed step is reported beside it either way.
+    per_copy = 4 * (E * (P * U + ysh) * (1 if fwd_only else 2) + 3 * E + 2 * N
+                    + N * (plan.xdim + plan.outdim) * (1 if fwd_only else 2))
+    SC = 1 if per_copy >= COLD_BYTES else min(16, math.ceil(COLD_BYTES / per_copy) + 1)
+    stream = max(SC - 1, 1) * per_copy >= COLD_BYTES
+    stream_rounds = 3
+    if stream:
+        gcs = [g] + [tpc.graph_build(src, dst, N, check=False) for _ in range(SC - 1)]
+        sets = [(gcs[0], x, go, out, gx)] + [
+            (gcs[c], x.clone(), None if fwd_only else go.clone(), torch.empty_like(out), torch.empty_like(gx))
+            for c in range(1, SC)]
+        Ys_s = Ys[:SC] + [Y.clone() for _ in range(SC - len(Ys[:SC]))]
+        ws_s = ws[:SC] + [w.clone() for _ in range(SC - len(ws[:SC]))]
+        gYs_s = None if fwd_only else gYs[:SC] + [torch.empty_like(Y) for _ in range(SC - len(gYs[:SC]))]
+        gws_s = None if fwd_only else gws[:SC] + [torch.empty_like(w) for _ in range(SC - len(gws[:SC]))]
+        if sg:
+            eps = [tpc.graph_sender_positions(gc) for gc in gcs]
+            Ygs_s = [tpc.gather_rows(Yc, g.t_perm) for Yc in Ys_s]
+            wgs_s = [tpc.gather_rows(wc, g.t_perm) for wc in ws_s]
+
+        def step_recv(c):
+            gc, xc, goc, outc, gxc = sets[c]
+            tpc.forward(plan, gc, xc, Ys_s[c], ws_s[c], out=outc)
+            if not fwd_only:
+                tpc.backward(plan, gc, xc, Ys_s[c], ws_s[c], goc, outs=(gxc, gYs_s[c], gws_s[c]))
+
+        def step_sg(c):
+            gc, xc, goc, outc, gxc = sets[c]
+            tpc.forward_sg(plan, gc, eps[c], xc, Ygs_s[c], wgs_s[c], out=outc)
+            tpc.backward_sg(plan, gc, xc, Ygs_s[c], wgs_s[c], goc, outs=(gxc, gYs_s[c], gws_s[c]))
+
     timed_steps(args.warmup, True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    t = timed_steps(args.steps, True)
+    t_sg = None
+    if stream:
+        timed_stream(torch, flush, step_recv, SC, max(args.warmup, 1), 1)
+        if sg:
+            # brackets of the two layouts alternate, so neither gains from its
+            # place in the run; the step's own bracket comes last in each round,
+            # so the outputs read back below are its (receiver-sorted) ones
+            timed_stream(torch, flush, step_sg, SC, max(args.warmup, 1), 1)
+            t, t_sg = [], []
+            for _ in range(stream_rounds):
+                t_sg.append(timed_stream(torch, flush, step_sg, SC, args.steps, 1)[0])
+                t.append(timed_stream(torch, flush, step_recv, SC, args.steps, 1)[0])
+            t, t_sg = np.array(t), np.array(t_sg)
+        else:
+            t = timed_stream(torch, flush, step_recv, SC, args.steps, stream_rounds)
+        c_last = (args.steps - 1) % SC      # the copy the last timed step wrote
+        res_out, res_gx = sets[c_last][3], sets[c_last][4]
+        res_gY = None if fwd_only else gYs_s[c_last]
+        res_gw = None if fwd_only else gws_s[c_last]
+    else:
+        t = timed_steps(args.steps, True)
+        res_out, res_gx = out, gx
+        res_gY = None if fwd_only else gYs[0]
+        res_gw = None if fwd_only else gws[0]
     torch.cuda.synchronize()
     # the timed step's results, for the parity check on the CPU-baseline sample
-    snap = {"out": out.cpu().numpy(), "perm": g.perm.cpu().numpy()[:E]} if cpu else None
+    snap = {"out": res_out.cpu().numpy(), "perm": g.perm.cpu().numpy()[:E]} if cpu else None
     if cpu and not fwd_only:
-        snap.update(gx=gx.cpu().numpy(), gY=gYs[0].cpu().numpy(), gw=gws[0].cpu().numpy())
+        snap.update(gx=res_gx.cpu().numpy(), gY=res_gY.cpu().numpy(), gw=res_gw.cpu().numpy())
     wall = time.perf_counter() - t_wall0
+    t_iso = timed_steps(args.steps, True) if stream else t
+    if stream:
+        del sets, Ys_s, ws_s, gYs_s, gws_s
+        if sg:
+            del Ygs_s, wgs_s
     warm = timed_steps(args.steps, False) if args.warm else None
     reps = max(2 * NC, 12)
     rounds = max(2, args.steps // 5)
@@ -648,7 +760,8 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
 
     step_ms = float(t.mean())
     ab = algorithmic_bytes(N, E, P, U, ysh, plan.xdim, plan.outdim)
-    dom = max(kt, key=kt.get)
+    # the dominant kernel among those of the timed step
+    dom = max((n for n in kt if not n.endswith("_sg")), key=kt.get)
     traffic = read_traffic(name)
     cnt = cg_counts(plan.paths(), *plan.cg())
     fl = cg_flops(cnt)
@@ -659,6 +772,14 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
         "ms_per_step": step_ms,
         "edges_per_s": E / (step_ms * 1e-3),
         "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
+        "step_timing": (f"{args.steps} steps back to back in one event bracket, rotating over {SC} "
+                        f"copies of every array a step touches ({SC * per_copy / 1e6:.0f} MB: a copy is "
+                        f"reused after >= 1 GiB of other data), after a flush; mean of {stream_rounds} "
+                        f"brackets" if stream else
+                        f"each of {args.steps} steps after a 1 GiB flush in its own event bracket"),
+        "ms_per_step_isolated": float(t_iso.mean()),
+        "ms_per_step_isolated_note": ("one step after a 1 GiB flush in its own event bracket (adds the "
+                                      "latency from the event to the first kernel)"),
         "fwd_edges_per_s": E / (kt["fwd"] * 1e-3),
         "kernel_ms": kt,
         "kernel_ms_note": (f"cold: {reps} back-to-back launches rotating over {NC} copies of the "
@@ -696,6 +817,19 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
             "algorithmic_bytes": ab_r,
             "note": ("forward and one-pass backward from r [E, 3]: harmonics evaluated per edge on chip, "
                      "grad_r (the forces' edge term) in place of grad_Y; timed as the step above"),
+        }
+    if sg:
+        ms_sg = float(t_sg.mean()) if t_sg is not None else None
+        res["sender_layout_step"] = {
+            "ms_per_step": ms_sg, "edges_per_s": None if ms_sg is None else E / (ms_sg * 1e-3),
+            "kernel_ms": {n: kt[n] for n in ("fwd_sg", "bwd_sg")},
+            "kernel_hbm_frac": {n: ab[n] / (kt[n] * 1e-3) / 1e9 / HBM_PEAK_GBS for n in ("fwd_sg", "bwd_sg")},
+            "traffic": {n: (traffic or {}).get(n) for n in ("fwd_sg", "bwd_sg")},
+            "note": ("the step with Y, w and their gradients stored in the sender grouping: "
+                     "tp_conv_forward_sg gathers the edge rows through e_pos, tp_conv_backward_sg "
+                     "reads and writes them in order (results bit for bit those of the step); "
+                     "timed like the step, its brackets alternating with the step's"
+                     if ms_sg is not None else "kernels only (the step is timed in isolation here)"),
         }
     if warm is not None:
         res["warm_edges_per_s"] = E / (float(warm.mean()) * 1e-3)
@@ -880,7 +1014,8 @@ def headline(name, res, args):
         "config": {"workload": res["workload"], "n_nodes": res["n_nodes"], "n_edges": res["n_edges"],
                    "irreps": res["irreps"], "lmax_sh": res["lmax_sh"], "lmax_out": res["lmax_out"],
                    "paths": res["paths"], "mode": res["mode"],
-                   "cache": "L2+MALL flushed before each step; kernels cold by rotating copies"},
+                   "cache": res.get("step_timing", "L2+MALL flushed before each step") +
+                            "; kernels cold by rotating copies"},
     }
     line.update({k: v for k, v in res.items() if k not in ("workload", "n_nodes", "n_edges", "irreps",
                                                            "lmax_sh", "lmax_out", "paths", "mode",

@@ -234,6 +234,42 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
                            const float* Y, const float* w, const float* grad_out,
                            float* grad_x, float* grad_Y, float* grad_w, hipStream_t stream);
 
+/* ---- sender-grouped edge layout ---------------------------------------------
+ * The same forward and backward with the edge-sized arrays (Y, w, grad_Y,
+ * grad_w) stored in the sender grouping: row k belongs to the edge at position
+ * k of t_perm, i.e. to receiver-sorted edge t_perm[k].  A caller that forms the
+ * per-edge weights and harmonics itself (a radial network and the harmonics of
+ * the edge vectors) can form them in this order just as well; then the
+ * backward, which walks the edges by sender, reads and writes its edge rows
+ * contiguously, and the forward, which walks them by receiver, gathers them
+ * (read only) through e_pos.  Streaming edge-local products into bounded node
+ * state in whichever grouping keeps the larger edge streams sequential is the
+ * schedule of "Sobek", Abstract; the gather-versus-stream trade-off is that of
+ * "The GPU Workload That Rewrites Molecular Physics", section "The Compute vs.
+ * Memory Bottleneck Shift".  Results equal those of tp_conv_forward /
+ * tp_conv_backward on the same edges (summation order unchanged). */
+
+/* e_pos[q] = the sender-grouped position of receiver-sorted edge q (the
+ * inverse of graph->t_perm), E int32 on the device, caller-owned.  Helper: the
+ * index the forward of this layout reads.  Needs the sender grouping. */
+tp_status tp_conv_graph_sender_positions(const tp_graph* graph, int32_t* e_pos, hipStream_t stream);
+
+/* tp_conv_forward with Y [E][ysh] and w [E][P][U] in the sender grouping;
+ * e_pos from tp_conv_graph_sender_positions.  x and w must be 16-byte aligned
+ * (TP_ERR_ARG); e_pos must be the graph's (entries index rows of Y and w). */
+tp_status tp_conv_forward_sg(tp_plan_t plan, const tp_graph* graph, const int32_t* e_pos, const float* x,
+                             const float* Y, const float* w, float* out, hipStream_t stream);
+
+/* tp_conv_backward with Y, w, grad_Y and grad_w in the sender grouping: one
+ * sender-grouped pass for any subset of grad_x, grad_Y, grad_w (each may be
+ * NULL), reading and writing the edge rows in order.  Signatures with a
+ * one-pass backward only (at most 256 CG nonzeros; 0e+1o+2e+3o / lmax 3 gets
+ * TP_ERR_UNSUPPORTED).  x, w and grad_out must be 16-byte aligned.
+ * Deterministic. */
+tp_status tp_conv_backward_sg(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                              const float* w, const float* grad_out, float* grad_x, float* grad_Y,
+                              float* grad_w, hipStream_t stream);
+
 /* ---- edge-vector form: harmonics evaluated on chip -------------------------
  * The layer as a function of the edge vectors r [E][3] (receiver-sorted,
  * r_e = pos[src] - pos[dst]) instead of their harmonics: each edge's

@@ -29,6 +29,7 @@ EXPORTS = (
     "tp_conv_plan_destroy", "tp_cg_real", "tp_conv_graph_workspace", "tp_conv_graph_build",
     "tp_conv_graph_build_static", "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
     "tp_conv_forward_r", "tp_conv_backward_r",
+    "tp_conv_graph_sender_positions", "tp_conv_forward_sg", "tp_conv_backward_sg",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
     "tp_conv_forward_radial_r", "tp_conv_backward_radial_r", "tp_conv_double_backward_radial",
@@ -90,6 +91,9 @@ def lib():
         "tp_conv_backward": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
         "tp_conv_forward_r": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_backward_r": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
+        "tp_conv_graph_sender_positions": (I32, [ctypes.POINTER(_Graph), VP, VP]),
+        "tp_conv_forward_sg": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP]),
+        "tp_conv_backward_sg": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
         "tp_conv_uvw_forward": (I32, [P, I32, VP, VP, VP, VP]),
         "tp_conv_uvw_backward": (I32, [P, I32, VP, VP, VP, VP, VP, VP, SZ, VP]),
         "tp_conv_uvw_workspace": (I32, [P, ctypes.POINTER(SZ)]),
@@ -356,6 +360,58 @@ def backward(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=None):
     _check(lib().tp_conv_backward(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
                                   _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw),
                                   _stream(x.device)))
+    return gx, gY, gw
+
+
+def graph_sender_positions(graph, out=None):
+    """e_pos [E] int32: the sender-grouped position of each receiver-sorted edge."""
+    torch = _torch()
+    E = graph.n_edges
+    dev = graph.row_ptr.device
+    if out is None:
+        out = torch.empty(E, dtype=torch.int32, device=dev)
+    _need(out, "e_pos", torch.int32, (E,))
+    g = graph.cstruct()
+    _check(lib().tp_conv_graph_sender_positions(ctypes.byref(g), _ptr(out), _stream(dev)))
+    return out
+
+
+def forward_sg(plan, graph, e_pos, x, Y, w, out=None):
+    """forward with Y and w in the sender grouping (row k = sender-grouped position k)."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    _need(e_pos, "e_pos", torch.int32, (E,))
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(w, "w", torch.float32, (E, plan.n_paths, plan.mul))
+    if out is None:
+        out = torch.empty((N, plan.outdim), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, (N, plan.outdim))
+    g = graph.cstruct()
+    _check(lib().tp_conv_forward_sg(plan.handle, ctypes.byref(g), _ptr(e_pos), _ptr(x), _ptr(Y),
+                                    _ptr(w), _ptr(out), _stream(x.device)))
+    return out
+
+
+def backward_sg(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=None):
+    """(grad_x, grad_Y, grad_w) with every edge array in the sender grouping."""
+    torch = _torch()
+    N, E = graph.n_nodes, graph.n_edges
+    _need(x, "x", torch.float32, (N, plan.xdim))
+    _need(Y, "Y", torch.float32, (E, plan.ysh))
+    _need(w, "w", torch.float32, (E, plan.n_paths, plan.mul))
+    _need(grad_out, "grad_out", torch.float32, (N, plan.outdim))
+    f32 = dict(dtype=torch.float32, device=x.device)
+    if outs is None:
+        gx = torch.empty((N, plan.xdim), **f32) if "x" in want else None
+        gY = torch.empty((E, plan.ysh), **f32) if "Y" in want else None
+        gw = torch.empty((E, plan.n_paths, plan.mul), **f32) if "w" in want else None
+    else:
+        gx, gY, gw = outs
+    g = graph.cstruct()
+    _check(lib().tp_conv_backward_sg(plan.handle, ctypes.byref(g), _ptr(x), _ptr(Y), _ptr(w),
+                                     _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw),
+                                     _stream(x.device)))
     return gx, gY, gw
 
 

@@ -490,6 +490,71 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   return TP_OK;
 }
 
+tp_status tp_conv_graph_sender_positions(const tp_graph* graph, int32_t* e_pos, hipStream_t stream) {
+  tp_status s = check_graph(graph, true);
+  if (s != TP_OK) return s;
+  if (graph->n_edges > 0 && !e_pos) return set_error(TP_ERR_ARG, "tp_conv_graph_sender_positions: e_pos NULL");
+  return tpc::sender_positions(graph->t_perm, graph->n_edges, e_pos, stream);
+}
+
+tp_status tp_conv_forward_sg(tp_plan_t plan, const tp_graph* graph, const int32_t* e_pos, const float* x,
+                             const float* Y, const float* w, float* out, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward_sg: plan is NULL");
+  tp_status s = check_graph(graph, false);
+  if (s != TP_OK) return s;
+  if (graph->n_nodes > 0 && (!x || !out)) return set_error(TP_ERR_ARG, "tp_conv_forward_sg: x/out NULL");
+  if (graph->n_edges > 0 && (!Y || !w || !e_pos))
+    return set_error(TP_ERR_ARG, "tp_conv_forward_sg: Y/w/e_pos NULL");
+  if (misaligned16({x, w})) return set_error(TP_ERR_ARG, "tp_conv_forward_sg: x and w must be 16-byte aligned");
+  if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_forward_sg: not a channel-wise CG plan");
+  tpc::ConvArgs a;
+  a.n_nodes = graph->n_nodes;
+  a.n_edges = graph->n_edges;
+  a.row_ptr = graph->row_ptr;
+  a.col = graph->col;
+  a.sender_rows = true;
+  a.e_pos = e_pos;
+  a.x = x;
+  a.Y = Y;
+  a.w = w;
+  a.out = out;
+  a.stream = stream;
+  hipError_t e = plan->ks->fwd(a);
+  return e == hipSuccess ? TP_OK : tpc::hip_error(e, "tp_conv_forward_sg launch");
+}
+
+tp_status tp_conv_backward_sg(tp_plan_t plan, const tp_graph* graph, const float* x, const float* Y,
+                              const float* w, const float* grad_out, float* grad_x, float* grad_Y,
+                              float* grad_w, hipStream_t stream) {
+  if (!plan) return set_error(TP_ERR_ARG, "tp_conv_backward_sg: plan is NULL");
+  tp_status s = check_graph(graph, true);
+  if (s != TP_OK) return s;
+  if (graph->n_nodes > 0 && !grad_out) return set_error(TP_ERR_ARG, "tp_conv_backward_sg: grad_out NULL");
+  if (graph->n_edges > 0 && (!Y || !w || !x)) return set_error(TP_ERR_ARG, "tp_conv_backward_sg: x/Y/w NULL");
+  if (misaligned16({x, w, grad_out}))
+    return set_error(TP_ERR_ARG, "tp_conv_backward_sg: x, w and grad_out must be 16-byte aligned");
+  if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_backward_sg: not a channel-wise CG plan");
+  if (!plan->ks->bwd_fused)
+    return set_error(TP_ERR_UNSUPPORTED, "tp_conv_backward_sg: this signature has no one-pass backward");
+  if (!grad_x && !grad_Y && !grad_w) return TP_OK;
+  tpc::ConvArgs a;
+  a.n_nodes = graph->n_nodes;
+  a.n_edges = graph->n_edges;
+  a.t_row_ptr = graph->t_row_ptr;
+  a.t_col = graph->t_col;
+  a.sender_rows = true;
+  a.x = x;
+  a.Y = Y;
+  a.w = w;
+  a.grad_out = grad_out;
+  a.grad_x = grad_x;
+  a.grad_Y = grad_Y;
+  a.grad_w = grad_w;
+  a.stream = stream;
+  hipError_t e = plan->ks->bwd_fused(a);
+  return e == hipSuccess ? TP_OK : tpc::hip_error(e, "tp_conv_backward_sg launch");
+}
+
 tp_status tp_conv_forward_r(tp_plan_t plan, const tp_graph* graph, const float* x, const float* r,
                             const float* w, float* out, hipStream_t stream) {
   if (!plan) return set_error(TP_ERR_ARG, "tp_conv_forward_r: plan is NULL");

@@ -550,6 +550,25 @@ __device__ __forceinline__ void stage_recv(char* buf, const float* __restrict__ 
   }, lane);
 }
 
+// the same step when the edge rows are stored in the sender grouping: the
+// weight and Y rows of the step's edges are gathered at rows e[r]
+template <class S, int U, bool GEOM = false>
+__device__ __forceinline__ void stage_recv_at(char* buf, const float* __restrict__ x,
+                                              const float* __restrict__ Y, const float* __restrict__ w,
+                                              const int (&j)[LaneMap<U>::EPW],
+                                              const int (&e)[LaneMap<U>::EPW], int lane) {
+  using T = RecvStage<S, U, GEOM>;
+  dma_rows16<T::EPW, T::WB, kStream>(buf + T::W_OFF, [&](int r) {
+    return (const char*)(w + (size_t)pick(e, r) * (S::NP * U));
+  }, lane);
+  dma_rows4<T::EPW, T::YB, kStream>(buf + T::Y_OFF, [&](int r) {
+    return (const char*)(Y + (size_t)pick(e, r) * T::YR);
+  }, lane);
+  dma_rows16<T::EPW, T::XB>(buf + T::X_OFF, [&](int r) {
+    return (const char*)(x + (size_t)pick(j, r) * (S::XC * U));
+  }, lane);
+}
+
 // the edge's harmonics from its staged row: Y itself or, with GEOM, evaluated
 // from the staged edge vector (the unit direction and 1/|r| go to geo for the
 // backward's pullback to r)
@@ -767,12 +786,15 @@ struct FwdSmem {
   static constexpr int BYTES = STAGE > RED ? STAGE : RED;
 };
 
-// GEOM: Y holds the edge vectors r [E][3] and the harmonics are evaluated on chip
-template <class S, int U, int WPB, int NBUF, bool GEOM = false>
+// GEOM: Y holds the edge vectors r [E][3] and the harmonics are evaluated on chip.
+// EPOS: the edge rows of w and Y are stored in the sender grouping and epos[q]
+// is the row of receiver-sorted edge q (otherwise row q itself).
+template <class S, int U, int WPB, int NBUF, bool GEOM = false, bool EPOS = false>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                const float* __restrict__ x, const float* __restrict__ Y,
-               const float* __restrict__ w, float* __restrict__ out) {
+               const float* __restrict__ w, float* __restrict__ out,
+               const int32_t* __restrict__ epos) {
   using M = LaneMap<U>;
   using T = RecvStage<S, U, GEOM>;
   constexpr int OD = U * S::OC, SLOTS = WPB * M::EPW, EPW = M::EPW;
@@ -793,36 +815,46 @@ __global__ void __launch_bounds__(WPB * 64)
   // first position of this wave (wave-uniform)
   const int q00 = __builtin_amdgcn_readfirstlane(beg + wv * EPW);
   if (trips > 0) {
-    IdxWindow<EPW, SLOTS> wj;
+    IdxWindow<EPW, SLOTS> wj, we;
     wj.load(col, q00, 0, last, lane);
-    int jn[EPW];
+    if constexpr (EPOS) we.load(epos, q00, 0, last, lane);
+    int jn[EPW], en[EPW];
+    auto stage = [&](char* buf, int q0) {
+      if constexpr (EPOS)
+        stage_recv_at<S, U, GEOM>(buf, x, Y, w, jn, en, lane);
+      else
+        stage_recv<S, U, GEOM>(buf, x, Y, w, jn, q0, last, lane);
+    };
+    auto next = [&](int k) {
+#pragma unroll
+      for (int r = 0; r < EPW; ++r) {
+        jn[r] = wj.get(col, q00, k, r, last, lane);
+        if constexpr (EPOS) en[r] = we.get(epos, q00, k, r, last, lane);
+      }
+    };
     // prologue: stage steps 0 .. NBUF-2
 #pragma unroll
     for (int b = 0; b < NBUF - 1; ++b) {
       if (b < trips) {
-#pragma unroll
-        for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, b, r, last, lane);
-        stage_recv<S, U, GEOM>(mybuf + b * T::BUF, x, Y, w, jn, q00 + b * SLOTS, last, lane);
+        next(b);
+        stage(mybuf + b * T::BUF, q00 + b * SLOTS);
       }
     }
-#pragma unroll
-    for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, NBUF - 1, r, last, lane);
+    next(NBUF - 1);
     for (int k = 0; k < trips; ++k) {
       const int q0 = q00 + k * SLOTS;
       const char* cur = mybuf + (k % NBUF) * T::BUF;
       int ahead = trips - 1 - k;
       if (ahead >= NBUF - 1) {
         ahead = NBUF - 1;
-        stage_recv<S, U, GEOM>(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, x, Y, w, jn,
-                               q0 + (NBUF - 1) * SLOTS, last, lane);
+        stage(mybuf + ((k + NBUF - 1) % NBUF) * T::BUF, q0 + (NBUF - 1) * SLOTS);
       }
       wait_steps<NBUF, 1, T::NLOADS, 0>(ahead, 0);
       float xr[M::CPL][S::XC], yr[S::YC], wr[M::CPL][S::NP], geo[4];
       read_recv<S, U, GEOM>(cur, slot, uu, xr, yr, wr, geo);
       __builtin_amdgcn_sched_barrier(0);
-      // senders of the next step to stage
-#pragma unroll
-      for (int r = 0; r < EPW; ++r) jn[r] = wj.get(col, q00, k + NBUF, r, last, lane);
+      // senders (and edge rows) of the next step to stage
+      next(k + NBUF);
       // only the receiver's last step can hold slots past its edges (they
       // re-read its last edge); their weights are zeroed there alone
       if (q0 + EPW > end) {
@@ -1074,8 +1106,11 @@ struct FusedSmem {
   static constexpr int BYTES = STAGE > RED ? STAGE : RED;
 };
 
-// GEOM: Y holds the edge vectors r [E][3] and grad_Y receives grad_r [E][3]
-template <class S, int U, int WPB, int NBUF, int MODE, bool GEOM = false>
+// GEOM: Y holds the edge vectors r [E][3] and grad_Y receives grad_r [E][3].
+// IDQ: the edge rows (w, Y, grad_w, grad_Y) are stored in the sender grouping,
+// so the row of sender-grouped position k is k itself and t_perm is not read.
+// grad_x may be null (not stored).
+template <class S, int U, int WPB, int NBUF, int MODE, bool GEOM = false, bool IDQ = false>
 __global__ void __launch_bounds__(WPB * 64)
     k_conv_bwd_fused(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                      const int32_t* __restrict__ t_col, const float* __restrict__ x,
@@ -1112,14 +1147,21 @@ __global__ void __launch_bounds__(WPB * 64)
     // qh[t]: receiver-sorted positions of the steps staged but not yet
     // computed (qh[0] is the next one computed); qn/in: the step staged next
     IdxWindow<EPW, SLOTS> wq, wi;
-    wq.load(t_perm, k00, 0, last, lane);
+    if constexpr (!IDQ) wq.load(t_perm, k00, 0, last, lane);
     wi.load(t_col, k00, 0, last, lane);
+    // row of the edge in slot r at wave step t
+    auto row_at = [&](int t, int r) {
+      if constexpr (IDQ)
+        return min(k00 + t * SLOTS + r, last);
+      else
+        return wq.get(t_perm, k00, t, r, last, lane);
+    };
     int qh[NBUF > 1 ? NBUF - 1 : 1][EPW], qn[EPW], in[EPW];
 #pragma unroll
     for (int b = 0; b < NBUF - 1; ++b) {
 #pragma unroll
       for (int r = 0; r < EPW; ++r) {
-        qn[r] = wq.get(t_perm, k00, b, r, last, lane);
+        qn[r] = row_at(b, r);
         in[r] = wi.get(t_col, k00, b, r, last, lane);
         qh[b][r] = qn[r];
       }
@@ -1127,7 +1169,7 @@ __global__ void __launch_bounds__(WPB * 64)
     }
 #pragma unroll
     for (int r = 0; r < EPW; ++r) {
-      qn[r] = wq.get(t_perm, k00, NBUF - 1, r, last, lane);
+      qn[r] = row_at(NBUF - 1, r);
       in[r] = wi.get(t_col, k00, NBUF - 1, r, last, lane);
     }
     float xr[M::CPL][S::XC];
@@ -1201,7 +1243,7 @@ __global__ void __launch_bounds__(WPB * 64)
       }
 #pragma unroll
       for (int r = 0; r < EPW; ++r) {
-        qn[r] = wq.get(t_perm, k00, k + NBUF, r, last, lane);
+        qn[r] = row_at(k + NBUF, r);
         in[r] = wi.get(t_col, k00, k + NBUF, r, last, lane);
       }
       float gy[S::YC];
@@ -1233,6 +1275,7 @@ __global__ void __launch_bounds__(WPB * 64)
     }
     flush();
   }
+  if (!grad_x) return;
   __syncthreads();
   block_reduce_store<U, WPB, S::XC, S::NIN>(gx, (float*)smem, grad_x + (size_t)j * XD, InBlocks<S>{});
 }
@@ -1255,21 +1298,31 @@ float* edge_geom_grad(const ConvArgs& a) {
   return GEOM ? a.grad_r : a.grad_Y;
 }
 
-template <class S, int U, bool GEOM = false>
-hipError_t launch_fwd(const ConvArgs& a) {
+template <class S, int U, bool GEOM = false, bool EPOS = false>
+hipError_t launch_fwd_as(const ConvArgs& a) {
   using C = Cfg<S, U, GEOM>;
-  if (a.n_nodes == 0) return hipSuccess;
   const float* Y = edge_geom<GEOM>(a);
   if constexpr (C::WPB_F != C::WPB_F2) {
     if (a.n_nodes < kSmallGraph) {
-      hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F2, C::NBUF_F2, GEOM>), dim3(a.n_nodes), dim3(C::WPB_F2 * 64),
-                         0, a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out);
+      hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F2, C::NBUF_F2, GEOM, EPOS>), dim3(a.n_nodes),
+                         dim3(C::WPB_F2 * 64), 0, a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out, a.e_pos);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F, C::NBUF_F, GEOM>), dim3(a.n_nodes), dim3(C::WPB_F * 64), 0,
-                     a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out);
+  hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F, C::NBUF_F, GEOM, EPOS>), dim3(a.n_nodes), dim3(C::WPB_F * 64), 0,
+                     a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out, a.e_pos);
   return hipGetLastError();
+}
+
+// edge rows in receiver-sorted order, or (a.sender_rows, direct-weight form
+// only) in the sender grouping, read through a.e_pos
+template <class S, int U, bool GEOM = false>
+hipError_t launch_fwd(const ConvArgs& a) {
+  if (a.n_nodes == 0) return hipSuccess;
+  if constexpr (!GEOM) {
+    if (a.sender_rows) return launch_fwd_as<S, U, false, true>(a);
+  }
+  return launch_fwd_as<S, U, GEOM, false>(a);
 }
 
 template <class S, int U, bool GEOM = false>
@@ -1303,23 +1356,37 @@ hipError_t launch_bwd_send(const ConvArgs& a) {
 
 // whole backward (grad_x with grad_w and/or grad_Y) in one sender-grouped pass
 
-template <class S, int U, bool GEOM = false>
-hipError_t launch_bwd_fused(const ConvArgs& a) {
+template <class S, int U, bool GEOM = false, bool IDQ = false>
+hipError_t launch_bwd_fused_as(const ConvArgs& a) {
   using F = FusedCfg<S, U, GEOM>;
-  if (a.n_nodes == 0) return hipSuccess;
   const float* Y = edge_geom<GEOM>(a);
   float* gY = edge_geom_grad<GEOM>(a);
   const dim3 grid(a.n_nodes), block(F::WPB * 64);
   if (a.grad_w && gY)
-    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 3, GEOM>), grid, block, 0, a.stream, a.t_row_ptr,
-                       a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 3, GEOM, IDQ>), grid, block, 0, a.stream,
+                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
   else if (a.grad_w)
-    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 1, GEOM>), grid, block, 0, a.stream, a.t_row_ptr,
-                       a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
-  else
-    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 2, GEOM>), grid, block, 0, a.stream, a.t_row_ptr,
-                       a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 1, GEOM, IDQ>), grid, block, 0, a.stream,
+                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
+  else if (gY)
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 2, GEOM, IDQ>), grid, block, 0, a.stream,
+                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
+  else if constexpr (IDQ)
+    hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 0, GEOM, IDQ>), grid, block, 0, a.stream,
+                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
   return hipGetLastError();
+}
+
+// edge rows in receiver-sorted order (gathered through t_perm), or
+// (a.sender_rows, direct-weight form only) already in the sender grouping; in
+// that layout this pass serves any subset of grad_x, grad_w and grad_Y
+template <class S, int U, bool GEOM = false>
+hipError_t launch_bwd_fused(const ConvArgs& a) {
+  if (a.n_nodes == 0) return hipSuccess;
+  if constexpr (!GEOM) {
+    if (a.sender_rows) return launch_bwd_fused_as<S, U, false, true>(a);
+  }
+  return launch_bwd_fused_as<S, U, GEOM, false>(a);
 }
 
 // Backward of the edge-vector form: grad_x, grad_w and grad_r (a.r, a.grad_r),

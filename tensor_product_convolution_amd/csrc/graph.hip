@@ -355,4 +355,23 @@ tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64
   return e == hipSuccess ? TP_OK : hip_error(e, "gather_rows launch");
 }
 
+// e_pos[t_perm[k]] = k: for each receiver-sorted edge, its sender-grouped
+// position (the inverse permutation of t_perm).  Entries outside [0, E) (a
+// grouping that did not come from the build) are skipped, never written.
+__global__ void __launch_bounds__(256)
+    k_invert_perm(const int32_t* __restrict__ t_perm, int n, int32_t* __restrict__ e_pos) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < n) {
+    const int q = t_perm[k];
+    if (q >= 0 && q < n) e_pos[q] = k;
+  }
+}
+
+tp_status sender_positions(const int32_t* t_perm, int n_edges, int32_t* e_pos, hipStream_t st) {
+  if (n_edges == 0) return TP_OK;
+  hipLaunchKernelGGL(k_invert_perm, dim3((n_edges + 255) / 256), dim3(256), 0, st, t_perm, n_edges, e_pos);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TP_OK : hip_error(e, "sender_positions launch");
+}
+
 }  // namespace tpc

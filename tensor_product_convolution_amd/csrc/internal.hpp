@@ -19,6 +19,11 @@ struct ConvArgs {
   int32_t n_nodes = 0, n_edges = 0;
   const int32_t *row_ptr = nullptr, *col = nullptr;
   const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
+  // sender_rows: the edge rows (w, Y and their gradients) are stored in the
+  // sender grouping (row k = sender-grouped position k); e_pos[q] is then the
+  // row of receiver-sorted edge q, which the forward reads
+  bool sender_rows = false;
+  const int32_t* e_pos = nullptr;
   const float *x = nullptr, *Y = nullptr, *w = nullptr, *grad_out = nullptr;
   float *out = nullptr, *grad_x = nullptr, *grad_Y = nullptr, *grad_w = nullptr;
   // second-order backward: cotangents of (grad_x, grad_Y, grad_w), outputs
@@ -163,6 +168,7 @@ tp_status graph_build_static(const int32_t* src, const int32_t* dst, int n_edges
                              int32_t* t_perm, int32_t* t_col, int32_t flags, hipStream_t st);
 tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64_t words, void* out,
                       hipStream_t st);
+tp_status sender_positions(const int32_t* t_perm, int n_edges, int32_t* e_pos, hipStream_t st);
 tp_status sph_harm(int lmax, const float* r, int n, float* Y, hipStream_t st);
 tp_status sph_harm_bwd(int lmax, const float* r, int n, const float* gY, const float* grl, float* gr,
                        hipStream_t st);

@@ -378,3 +378,38 @@ def test_radial_lmax3_plans_without_launch():
         tpc.Plan("128x0e+128x1o+128x2e+128x3o", 3, 3, radial=(8, 64, 5.0))
     with pytest.raises(Exception, match="radial"):
         tpc.Plan("16x0e+16x1o+16x2e+16x3o", 3, 3, radial=(8, 32, 5.0))
+
+
+def test_sender_layout_argument_errors_without_launch():
+    """The sender-grouped layout's entry points reject bad arguments on the
+    host: missing e_pos or sender grouping, misaligned rows, and a signature
+    without a one-pass backward (0e+1o+2e+3o / lmax 3)."""
+    L = tpc.lib()
+    p = tpc.Plan("8x0e+8x1o", 2, 2)
+    p3 = tpc.Plan("16x0e+16x1o+16x2e+16x3o", 3, 3)
+    fake, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1004)
+    g = tpc._Graph(4, 10, fake, fake, fake, fake, fake, fake)
+    no_sender = tpc._Graph(4, 10, fake, fake, fake, None, None, None)
+    assert L.tp_conv_graph_sender_positions(ctypes.byref(g), None, None) == -1
+    assert L.tp_conv_graph_sender_positions(ctypes.byref(no_sender), fake, None) == -1
+    assert L.tp_conv_graph_sender_positions(None, fake, None) == -1
+    # forward: e_pos is required when there are edges
+    assert L.tp_conv_forward_sg(p.handle, ctypes.byref(g), None, fake, fake, fake, fake, None) == -1
+    assert "e_pos" in L.tp_conv_last_error().decode()
+    assert L.tp_conv_forward_sg(p.handle, ctypes.byref(g), fake, odd, fake, fake, fake, None) == -1
+    assert "16-byte" in L.tp_conv_last_error().decode()
+    assert L.tp_conv_forward_sg(None, ctypes.byref(g), fake, fake, fake, fake, fake, None) == -1
+    # backward: needs the sender grouping and aligned x, w, grad_out
+    assert L.tp_conv_backward_sg(p.handle, ctypes.byref(no_sender), fake, fake, fake, fake, fake, fake,
+                                 fake, None) == -1
+    for bad in (0, 2, 3):
+        args = [fake] * 4
+        args[bad] = odd
+        assert L.tp_conv_backward_sg(p.handle, ctypes.byref(g), *args, fake, fake, fake, None) == -1
+        assert "16-byte" in L.tp_conv_last_error().decode()
+    assert L.tp_conv_backward_sg(p3.handle, ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake,
+                                 None) == -3
+    assert "one-pass" in L.tp_conv_last_error().decode()
+    # nothing requested: returns before any launch
+    assert L.tp_conv_backward_sg(p.handle, ctypes.byref(g), fake, fake, fake, fake, None, None, None,
+                                 None) == 0
