@@ -36,7 +36,7 @@ from .irreps import parse_irreps, build_plan, OraclePlan
 from .cg import cg_complex, real_basis_matrix, cg_real
 from .sh import sh_complex, sh_real, sh_real_jacobian, sh_real_vjp
 from .wigner import wigner_D_real
-from .csr import csr_build
+from .csr import csr_build, launch_order
 from .conv import (tp_conv_fwd, tp_conv_bwd, bessel_basis, bessel_basis_deriv, radial_mlp_fwd,
                    radial_mlp_bwd, uvw_mix_fwd, uvw_mix_bwd,
                    tp_conv_radial_fwd, tp_conv_radial_bwd, tp_conv_double_bwd,
@@ -48,7 +48,7 @@ from .gaunt import (sphere_quadrature, gaunt_coefficients, gaunt_plan, gaunt_con
 __all__ = [
     "parse_irreps", "build_plan", "OraclePlan", "cg_complex",
     "real_basis_matrix", "cg_real", "sh_complex", "sh_real", "sh_real_jacobian",
-    "sh_real_vjp", "wigner_D_real", "csr_build", "tp_conv_fwd", "tp_conv_bwd",
+    "sh_real_vjp", "wigner_D_real", "csr_build", "launch_order", "tp_conv_fwd", "tp_conv_bwd",
     "bessel_basis", "bessel_basis_deriv",
     "radial_mlp_fwd", "radial_mlp_bwd", "uvw_mix_fwd", "uvw_mix_bwd",
     "tp_conv_radial_fwd", "tp_conv_radial_bwd", "tp_conv_double_bwd", "bessel_basis_deriv2",

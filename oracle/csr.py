@@ -16,6 +16,12 @@ Returned arrays (all int64 here; the GPU keeps int32):
 * ``t_perm``    -- receiver-sorted positions regrouped by sender, stable;
 * ``t_row_ptr`` -- [N+1] sender offsets into ``t_perm``;
 * ``t_col``     -- receiver of each sender-grouped edge.
+
+``launch_order`` orders the nodes of a grouping by descending degree, ties
+by ascending node id: the pages name variable degree and hub atoms as what
+sets these workloads apart ("The GPU Workload That Rewrites Molecular
+Physics", section "What Makes MLFF Workloads Structurally Different"); the
+order is a schedule (the largest node first), and the pages fix no tie-break.
 """
 import numpy as np
 
@@ -31,3 +37,9 @@ def csr_build(src, dst, n_nodes):
     t_col = dst[perm][t_perm]
     return dict(perm=perm, row_ptr=row_ptr, col=col, t_perm=t_perm,
                 t_row_ptr=t_row_ptr, t_col=t_col)
+
+
+def launch_order(ptr):
+    """Nodes by descending degree (ptr[i+1] - ptr[i]), ties by node id."""
+    deg = np.diff(np.asarray(ptr, dtype=np.int64))
+    return np.argsort(-deg, kind="stable")

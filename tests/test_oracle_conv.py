@@ -290,6 +290,26 @@ def test_csr_against_loops():
     assert list(c["t_col"]) == [int(dst[perm[q]]) for q in tp]
 
 
+def test_launch_order_against_loops_and_its_defining_properties():
+    """Nodes by descending degree, ties by node id: built by a plain loop over
+    degrees from the largest down, and checked as a permutation whose degrees
+    never rise and whose ties keep node order (empty and isolated nodes too)."""
+    rng = np.random.default_rng(13)
+    for n, e in ((23, 400), (50, 60), (7, 0), (1, 5), (300, 3000)):
+        src = rng.integers(0, n, e)
+        dst = rng.integers(0, max(1, n // 3), e)         # many nodes without in-edges
+        c = oracle.csr_build(src, dst, n)
+        for ptr in (c["row_ptr"], c["t_row_ptr"]):
+            deg = [int(ptr[i + 1] - ptr[i]) for i in range(n)]
+            want = [i for d in range(max(deg), -1, -1) for i in range(n) if deg[i] == d]
+            got = oracle.launch_order(ptr)
+            assert list(got) == want
+            assert sorted(got) == list(range(n))
+            for k in range(n - 1):
+                a, b = got[k], got[k + 1]
+                assert deg[a] > deg[b] or (deg[a] == deg[b] and a < b)
+
+
 def test_workload_shapes():
     plan, wl = _wl("mid")
     assert wl.n_edges == 46080 and wl.n_nodes == 1536
