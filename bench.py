@@ -571,6 +571,14 @@ def hbm_roofline(kernel, nbytes, ms, traffic=None, note=None):
     return r
 
 
+def node_order(g):
+    """The same graph arrays without a launch order (passes walk node ids)."""
+    import copy
+    h = copy.copy(g)
+    h.order = h.t_order = None
+    return h
+
+
 def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
     """One direct-weight workload: returns (result dict, step function)."""
     from workloads import CONFIGS, make_workload
@@ -583,7 +591,9 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     src, dst = T(wl.src), T(wl.dst)
-    g = tpc.graph_build(src, dst, N)
+    # the graph preparation, once per neighbour list: grouping, then the
+    # launch order (nodes by descending degree) every pass below walks
+    g = tpc.graph_launch_order(tpc.graph_build(src, dst, N))
     Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
     w = tpc.gather_rows(T(wl.w), g.perm)
     x = T(wl.x)
@@ -670,6 +680,15 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
         e1.record()
         torch.cuda.synchronize()
         gb.append(e0.elapsed_time(e1))
+    go_ms = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        do_flush()
+        e0.record()
+        tpc.graph_launch_order(g)
+        e1.record()
+        torch.cuda.synchronize()
+        go_ms.append(e0.elapsed_time(e1))
 
     # Timed steps.  Where the workload is large enough that STEP_COPIES full
     # copies of everything a step touches (graph, x, Y, w, grad_out and the
@@ -683,7 +702,9 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
     stream = max(SC - 1, 1) * per_copy >= COLD_BYTES
     stream_rounds = 3
     if stream:
-        gcs = [g] + [tpc.graph_build(src, dst, N, check=False) for _ in range(SC - 1)]
+        gcs = [g] + [tpc.graph_launch_order(tpc.graph_build(src, dst, N, check=False)) for _ in range(SC - 1)]
+        # the same graphs walked in node order (no launch order)
+        gcs_n = [node_order(gc) for gc in gcs]
         sets = [(gcs[0], x, go, out, gx)] + [
             (gcs[c], x.clone(), None if fwd_only else go.clone(), torch.empty_like(out), torch.empty_like(gx))
             for c in range(1, SC)]
@@ -702,6 +723,12 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
             if not fwd_only:
                 tpc.backward(plan, gc, xc, Ys_s[c], ws_s[c], goc, outs=(gxc, gYs_s[c], gws_s[c]))
 
+        def step_node_order(c):
+            _, xc, goc, outc, gxc = sets[c]
+            tpc.forward(plan, gcs_n[c], xc, Ys_s[c], ws_s[c], out=outc)
+            if not fwd_only:
+                tpc.backward(plan, gcs_n[c], xc, Ys_s[c], ws_s[c], goc, outs=(gxc, gYs_s[c], gws_s[c]))
+
         def step_sg(c):
             gc, xc, goc, outc, gxc = sets[c]
             tpc.forward_sg(plan, gc, eps[c], xc, Ygs_s[c], wgs_s[c], out=outc)
@@ -710,21 +737,24 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
     timed_steps(args.warmup, True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    t_sg = None
+    t_sg = t_no = None
     if stream:
-        timed_stream(torch, flush, step_recv, SC, max(args.warmup, 1), 1)
-        if sg:
-            # brackets of the two layouts alternate, so neither gains from its
-            # place in the run; the step's own bracket comes last in each round,
-            # so the outputs read back below are its (receiver-sorted) ones
-            timed_stream(torch, flush, step_sg, SC, max(args.warmup, 1), 1)
-            t, t_sg = [], []
-            for _ in range(stream_rounds):
-                t_sg.append(timed_stream(torch, flush, step_sg, SC, args.steps, 1)[0])
-                t.append(timed_stream(torch, flush, step_recv, SC, args.steps, 1)[0])
-            t, t_sg = np.array(t), np.array(t_sg)
-        else:
-            t = timed_stream(torch, flush, step_recv, SC, args.steps, stream_rounds)
+        # brackets of the variants (node order, sender-grouped layout) and of
+        # the step alternate, so none gains from its place in the run; the
+        # step's own bracket comes last in each round, so the outputs read
+        # back below are its (receiver-sorted) ones
+        variants = [step_node_order] + ([step_sg] if sg else [])
+        for f in variants + [step_recv]:
+            timed_stream(torch, flush, f, SC, max(args.warmup, 1), 1)
+        tv = [[] for _ in variants]
+        t = []
+        for _ in range(stream_rounds):
+            for v, f in enumerate(variants):
+                tv[v].append(timed_stream(torch, flush, f, SC, args.steps, 1)[0])
+            t.append(timed_stream(torch, flush, step_recv, SC, args.steps, 1)[0])
+        t = np.array(t)
+        t_no = np.array(tv[0])
+        t_sg = np.array(tv[1]) if sg else None
         c_last = (args.steps - 1) % SC      # the copy the last timed step wrote
         res_out, res_gx = sets[c_last][3], sets[c_last][4]
         res_gY = None if fwd_only else gYs_s[c_last]
@@ -796,6 +826,11 @@ def bench_direct(name, args, torch, tpc, dev, flush, cpu=True):
                            for n, v in kt.items()},
         "valu_flops_per_edge_channel": {n: fl[n] for n in kt},
         "graph_build_ms": float(np.median(gb)),
+        "launch_order_ms": float(np.median(go_ms)),
+        "launch_order": ("every pass launches its nodes by descending degree (tp_conv_graph_launch_order, "
+                         "computed with the grouping, outside the step)"),
+        "node_order_ms_per_step": None if t_no is None else float(t_no.mean()),
+        "node_order_note": "the same step with the nodes launched in node order; brackets alternating",
         "wall_s_timed_region": wall,
     }
     if not fwd_only:

@@ -86,7 +86,12 @@ typedef struct tp_plan_s* tp_plan_t;
  *   perm[E]        original edge id of each receiver-sorted position
  *   t_row_ptr[N+1] sender offsets into t_perm
  *   t_perm[E]      receiver-sorted positions grouped by sender (ascending)
- *   t_col[E]       receiver of each sender-grouped edge */
+ *   t_col[E]       receiver of each sender-grouped edge
+ * and, optionally (NULL: node order), filled by tp_conv_graph_launch_order:
+ *   order[N]       receivers in the order the receiver-grouped passes launch
+ *                  their workgroups
+ *   t_order[N]     senders in the order the sender-grouped passes launch theirs
+ * Zero-initialise the struct so that unused optional fields are NULL. */
 typedef struct {
   int32_t n_nodes;
   int32_t n_edges;
@@ -96,6 +101,8 @@ typedef struct {
   const int32_t* t_row_ptr;
   const int32_t* t_perm;
   const int32_t* t_col;
+  const int32_t* order;
+  const int32_t* t_order;
 } tp_graph;
 
 /* Options of a plan.  Zero-initialised means "none".
@@ -234,6 +241,30 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
                            const float* Y, const float* w, const float* grad_out,
                            float* grad_x, float* grad_Y, float* grad_w, hipStream_t stream);
 
+/* ---- launch order -------------------------------------------------------------
+ * Degrees vary from node to node (hub atoms; "The GPU Workload That Rewrites
+ * Molecular Physics", section "What Makes MLFF Workloads Structurally
+ * Different"), and the forward, the receiver pass, the sender pass and the
+ * one-pass backward give each node one workgroup, so a high-degree node whose
+ * workgroup starts late leaves the chip idle at the end of the launch.  With
+ * graph->order / t_order set, the grid walks the nodes largest degree first
+ * (longest first), which shortens that tail; every result is bit for bit the
+ * same as in node order.  Helper: a schedule, not an operation of the pages.
+ *
+ * Workspace bytes tp_conv_graph_launch_order needs for n_nodes. */
+tp_status tp_conv_graph_order_workspace(int32_t n_nodes, size_t* bytes);
+
+/* order[k] = the receiver of k-th largest in-degree, t_order[k] = the sender
+ * of k-th largest out-degree (ties in ascending node id), from the graph's
+ * row_ptr and t_row_ptr; either output may be NULL (not both when N > 0).
+ * N int32 each, device, caller-owned; ws must hold
+ * tp_conv_graph_order_workspace bytes (TP_ERR_WORKSPACE otherwise).  Store
+ * them in the graph's order / t_order fields for the convolution calls;
+ * entries are clamped into [0, N), but an array that is not a permutation of
+ * the nodes skips some nodes and repeats others. */
+tp_status tp_conv_graph_launch_order(const tp_graph* graph, int32_t* order, int32_t* t_order, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
 /* ---- sender-grouped edge layout ---------------------------------------------
  * The same forward and backward with the edge-sized arrays (Y, w, grad_Y,
  * grad_w) stored in the sender grouping: row k belongs to the edge at position
@@ -255,8 +286,11 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
 tp_status tp_conv_graph_sender_positions(const tp_graph* graph, int32_t* e_pos, hipStream_t stream);
 
 /* tp_conv_forward with Y [E][ysh] and w [E][P][U] in the sender grouping;
- * e_pos from tp_conv_graph_sender_positions.  x and w must be 16-byte aligned
- * (TP_ERR_ARG); e_pos must be the graph's (entries index rows of Y and w). */
+ * e_pos from tp_conv_graph_sender_positions on the same graph.  x and w must
+ * be 16-byte aligned (TP_ERR_ARG).  e_pos is not checked: an array that did
+ * not come from that call (entries outside [0, E)) makes the forward read
+ * outside Y and w.  The sender grouping of any graph from tp_conv_graph_build
+ * is a permutation, so the e_pos made from it is always valid. */
 tp_status tp_conv_forward_sg(tp_plan_t plan, const tp_graph* graph, const int32_t* e_pos, const float* x,
                              const float* Y, const float* w, float* out, hipStream_t stream);
 

@@ -30,6 +30,7 @@ EXPORTS = (
     "tp_conv_graph_build_static", "tp_conv_gather_rows", "tp_conv_sph_harm", "tp_conv_forward", "tp_conv_backward",
     "tp_conv_forward_r", "tp_conv_backward_r",
     "tp_conv_graph_sender_positions", "tp_conv_forward_sg", "tp_conv_backward_sg",
+    "tp_conv_graph_order_workspace", "tp_conv_graph_launch_order",
     "tp_conv_uvw_forward", "tp_conv_uvw_backward", "tp_conv_uvw_workspace",
     "tp_conv_forward_radial", "tp_conv_backward_radial", "tp_conv_radial_workspace",
     "tp_conv_forward_radial_r", "tp_conv_backward_radial_r", "tp_conv_double_backward_radial",
@@ -51,7 +52,8 @@ class _Graph(ctypes.Structure):
     _fields_ = [("n_nodes", ctypes.c_int32), ("n_edges", ctypes.c_int32),
                 ("row_ptr", ctypes.c_void_p), ("col", ctypes.c_void_p),
                 ("perm", ctypes.c_void_p), ("t_row_ptr", ctypes.c_void_p),
-                ("t_perm", ctypes.c_void_p), ("t_col", ctypes.c_void_p)]
+                ("t_perm", ctypes.c_void_p), ("t_col", ctypes.c_void_p),
+                ("order", ctypes.c_void_p), ("t_order", ctypes.c_void_p)]
 
 
 class _Opts(ctypes.Structure):
@@ -92,6 +94,8 @@ def lib():
         "tp_conv_forward_r": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP]),
         "tp_conv_backward_r": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
         "tp_conv_graph_sender_positions": (I32, [ctypes.POINTER(_Graph), VP, VP]),
+        "tp_conv_graph_order_workspace": (I32, [I32, ctypes.POINTER(SZ)]),
+        "tp_conv_graph_launch_order": (I32, [ctypes.POINTER(_Graph), VP, VP, VP, SZ, VP]),
         "tp_conv_forward_sg": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP]),
         "tp_conv_backward_sg": (I32, [P, ctypes.POINTER(_Graph), VP, VP, VP, VP, VP, VP, VP, VP]),
         "tp_conv_uvw_forward": (I32, [P, I32, VP, VP, VP, VP]),
@@ -236,11 +240,14 @@ class Graph:
         self.n_nodes, self.n_edges = n_nodes, n_edges
         self.row_ptr, self.col, self.perm = row_ptr, col, perm
         self.t_row_ptr, self.t_perm, self.t_col = t_row_ptr, t_perm, t_col
+        self.order = self.t_order = None        # launch orders (graph_launch_order)
 
     def cstruct(self):
+        ptr = lambda t: None if t is None else t.data_ptr()
         return _Graph(self.n_nodes, self.n_edges, self.row_ptr.data_ptr(),
                       self.col.data_ptr(), self.perm.data_ptr(), self.t_row_ptr.data_ptr(),
-                      self.t_perm.data_ptr(), self.t_col.data_ptr())
+                      self.t_perm.data_ptr(), self.t_col.data_ptr(), ptr(self.order),
+                      ptr(self.t_order))
 
 
 def graph_build(src, dst, n_nodes, check=True):
@@ -361,6 +368,25 @@ def backward(plan, graph, x, Y, w, grad_out, want=("x", "Y", "w"), outs=None):
                                   _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gw),
                                   _stream(x.device)))
     return gx, gY, gw
+
+
+def graph_launch_order(graph, receivers=True, senders=True):
+    """Fill graph.order / graph.t_order (int32 [N]): nodes by descending in- /
+    out-degree, ties by node id; the convolution calls on this graph then
+    launch their workgroups in that order (results unchanged)."""
+    torch = _torch()
+    N = graph.n_nodes
+    dev = graph.row_ptr.device
+    need = ctypes.c_size_t()
+    _check(lib().tp_conv_graph_order_workspace(N, ctypes.byref(need)))
+    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+    order = torch.empty(N, dtype=torch.int32, device=dev) if receivers else None
+    t_order = torch.empty(N, dtype=torch.int32, device=dev) if senders else None
+    g = graph.cstruct()
+    _check(lib().tp_conv_graph_launch_order(ctypes.byref(g), _ptr(order), _ptr(t_order), _ptr(ws),
+                                            need.value, _stream(dev)))
+    graph.order, graph.t_order = order, t_order
+    return graph
 
 
 def graph_sender_positions(graph, out=None):

@@ -433,6 +433,8 @@ tp_status tp_conv_forward(tp_plan_t plan, const tp_graph* graph, const float* x,
   if (graph->n_edges > 0 && (!Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_forward: Y/w NULL");
   if (misaligned16({x, w})) return set_error(TP_ERR_ARG, "tp_conv_forward: x and w must be 16-byte aligned");
   tpc::ConvArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = graph->n_nodes;
   a.n_edges = graph->n_edges;
   a.row_ptr = graph->row_ptr;
@@ -461,6 +463,8 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   if (misaligned16({x, w, grad_out}))
     return set_error(TP_ERR_ARG, "tp_conv_backward: x, w and grad_out must be 16-byte aligned");
   tpc::ConvArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = graph->n_nodes;
   a.n_edges = graph->n_edges;
   a.row_ptr = graph->row_ptr;
@@ -490,6 +494,24 @@ tp_status tp_conv_backward(tp_plan_t plan, const tp_graph* graph, const float* x
   return TP_OK;
 }
 
+tp_status tp_conv_graph_order_workspace(int32_t n_nodes, size_t* bytes) {
+  if (n_nodes < 0 || !bytes) return set_error(TP_ERR_ARG, "tp_conv_graph_order_workspace: bad argument");
+  *bytes = tpc::order_workspace_bytes(n_nodes);
+  return TP_OK;
+}
+
+tp_status tp_conv_graph_launch_order(const tp_graph* graph, int32_t* order, int32_t* t_order, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  tp_status s = check_graph(graph, t_order != nullptr);
+  if (s != TP_OK) return s;
+  if (graph->n_nodes > 0 && !order && !t_order)
+    return set_error(TP_ERR_ARG, "tp_conv_graph_launch_order: order and t_order both NULL");
+  if (graph->n_nodes > 0 && (!ws || ws_bytes < tpc::order_workspace_bytes(graph->n_nodes)))
+    return set_error(TP_ERR_WORKSPACE, "tp_conv_graph_launch_order: workspace missing or too small");
+  return tpc::launch_order(graph->row_ptr, graph->t_row_ptr, graph->n_nodes, graph->n_edges, order, t_order, ws,
+                           stream);
+}
+
 tp_status tp_conv_graph_sender_positions(const tp_graph* graph, int32_t* e_pos, hipStream_t stream) {
   tp_status s = check_graph(graph, true);
   if (s != TP_OK) return s;
@@ -508,6 +530,8 @@ tp_status tp_conv_forward_sg(tp_plan_t plan, const tp_graph* graph, const int32_
   if (misaligned16({x, w})) return set_error(TP_ERR_ARG, "tp_conv_forward_sg: x and w must be 16-byte aligned");
   if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_forward_sg: not a channel-wise CG plan");
   tpc::ConvArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = graph->n_nodes;
   a.n_edges = graph->n_edges;
   a.row_ptr = graph->row_ptr;
@@ -538,6 +562,8 @@ tp_status tp_conv_backward_sg(tp_plan_t plan, const tp_graph* graph, const float
     return set_error(TP_ERR_UNSUPPORTED, "tp_conv_backward_sg: this signature has no one-pass backward");
   if (!grad_x && !grad_Y && !grad_w) return TP_OK;
   tpc::ConvArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = graph->n_nodes;
   a.n_edges = graph->n_edges;
   a.t_row_ptr = graph->t_row_ptr;
@@ -565,6 +591,8 @@ tp_status tp_conv_forward_r(tp_plan_t plan, const tp_graph* graph, const float* 
   if (misaligned16({x, w})) return set_error(TP_ERR_ARG, "tp_conv_forward_r: x and w must be 16-byte aligned");
   if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_forward_r: not a channel-wise CG plan");
   tpc::ConvArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = graph->n_nodes;
   a.n_edges = graph->n_edges;
   a.row_ptr = graph->row_ptr;
@@ -592,6 +620,8 @@ tp_status tp_conv_backward_r(tp_plan_t plan, const tp_graph* graph, const float*
     return set_error(TP_ERR_ARG, "tp_conv_backward_r: x, w and grad_out must be 16-byte aligned");
   if (!plan->ks) return set_error(TP_ERR_UNSUPPORTED, "tp_conv_backward_r: not a channel-wise CG plan");
   tpc::ConvArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = graph->n_nodes;
   a.n_edges = graph->n_edges;
   a.row_ptr = graph->row_ptr;
@@ -625,6 +655,8 @@ tp_status tp_conv_double_backward(tp_plan_t plan, const tp_graph* graph, const f
     return set_error(TP_ERR_ARG, "tp_conv_double_backward: grad_out NULL");
   if (E > 0 && (!x || !Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_double_backward: x/Y/w NULL");
   tpc::ConvArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.row_ptr = graph->row_ptr;

@@ -665,6 +665,14 @@ __device__ __forceinline__ void stage_send(char* buf, const float* __restrict__ 
   }, lane);
 }
 
+// Node of this workgroup: the grid walks the nodes in the given launch order
+// (largest degree first, so the longest workgroups do not start last), or in
+// node order without one.  Entries are clamped into [0, n).
+__device__ __forceinline__ int launch_node(const int32_t* __restrict__ order, int n) {
+  const int b = blockIdx.x;
+  return order ? min(max(order[b], 0), n - 1) : b;
+}
+
 // ---------------------------------------------------------------------------
 // kernels
 //
@@ -794,13 +802,13 @@ __global__ void __launch_bounds__(WPB * 64)
     k_conv_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                const float* __restrict__ x, const float* __restrict__ Y,
                const float* __restrict__ w, float* __restrict__ out,
-               const int32_t* __restrict__ epos) {
+               const int32_t* __restrict__ epos, const int32_t* __restrict__ order) {
   using M = LaneMap<U>;
   using T = RecvStage<S, U, GEOM>;
   constexpr int OD = U * S::OC, SLOTS = WPB * M::EPW, EPW = M::EPW;
   static_assert((NBUF - 1) * T::NLOADS < 64, "pipeline too deep for vmcnt");
   __shared__ __attribute__((aligned(16))) char smem[FwdSmem<S, U, WPB, NBUF, GEOM>::BYTES];
-  const int i = blockIdx.x;
+  const int i = launch_node(order, gridDim.x);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
@@ -879,7 +887,8 @@ __global__ void __launch_bounds__(WPB * 64)
     k_conv_bwd_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                     const float* __restrict__ x, const float* __restrict__ Y,
                     const float* __restrict__ w, const float* __restrict__ g,
-                    float* __restrict__ grad_w, float* __restrict__ grad_Y) {
+                    float* __restrict__ grad_w, float* __restrict__ grad_Y,
+                    const int32_t* __restrict__ order) {
   using M = LaneMap<U>;
   using T = RecvStage<S, U, GEOM>;
   using C = Cfg<S, U, GEOM>;
@@ -888,7 +897,7 @@ __global__ void __launch_bounds__(WPB * 64)
   static_assert((NBUF - 1) * (T::NLOADS + NST) < 64, "pipeline too deep for vmcnt");
   constexpr int WAVE_LDS = NBUF * T::BUF;
   __shared__ __attribute__((aligned(16))) char smem[WPB * WAVE_LDS];
-  const int i = blockIdx.x;
+  const int i = launch_node(order, gridDim.x);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
@@ -979,13 +988,13 @@ __global__ void __launch_bounds__(WPB * 64)
     k_conv_bwd_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                     const int32_t* __restrict__ t_col, const float* __restrict__ Y,
                     const float* __restrict__ w, const float* __restrict__ g,
-                    float* __restrict__ grad_x) {
+                    float* __restrict__ grad_x, const int32_t* __restrict__ order) {
   using M = LaneMap<U>;
   using T = SendStage<S, U, GEOM>;
   constexpr int XD = U * S::XC, SLOTS = WPB * M::EPW, EPW = M::EPW;
   static_assert((NBUF - 1) * T::NLOADS < 64, "pipeline too deep for vmcnt");
   __shared__ __attribute__((aligned(16))) char smem[SendSmem<S, U, WPB, NBUF, GEOM>::BYTES];
-  const int j = blockIdx.x;
+  const int j = launch_node(order, gridDim.x);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
@@ -1116,7 +1125,8 @@ __global__ void __launch_bounds__(WPB * 64)
                      const int32_t* __restrict__ t_col, const float* __restrict__ x,
                      const float* __restrict__ Y, const float* __restrict__ w,
                      const float* __restrict__ g, float* __restrict__ grad_x,
-                     float* __restrict__ grad_w, float* __restrict__ grad_Y) {
+                     float* __restrict__ grad_w, float* __restrict__ grad_Y,
+                     const int32_t* __restrict__ order) {
   using M = LaneMap<U>;
   using T = SendStage<S, U, GEOM>;
   using C = Cfg<S, U, GEOM>;
@@ -1126,7 +1136,7 @@ __global__ void __launch_bounds__(WPB * 64)
   static_assert(NBUF >= 1 && NBUF <= 4, "one to four staging buffers");
   static_assert((NBUF - 1) * (T::NLOADS + NST) < 64, "pipeline too deep for vmcnt");
   __shared__ __attribute__((aligned(16))) char smem[SM::BYTES];
-  const int j = blockIdx.x;
+  const int j = launch_node(order, gridDim.x);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
@@ -1305,12 +1315,12 @@ hipError_t launch_fwd_as(const ConvArgs& a) {
   if constexpr (C::WPB_F != C::WPB_F2) {
     if (a.n_nodes < kSmallGraph) {
       hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F2, C::NBUF_F2, GEOM, EPOS>), dim3(a.n_nodes),
-                         dim3(C::WPB_F2 * 64), 0, a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out, a.e_pos);
+                         dim3(C::WPB_F2 * 64), 0, a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out, a.e_pos, a.r_order);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((k_conv_fwd<S, U, C::WPB_F, C::NBUF_F, GEOM, EPOS>), dim3(a.n_nodes), dim3(C::WPB_F * 64), 0,
-                     a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out, a.e_pos);
+                     a.stream, a.row_ptr, a.col, a.x, Y, a.w, a.out, a.e_pos, a.r_order);
   return hipGetLastError();
 }
 
@@ -1334,13 +1344,13 @@ hipError_t launch_bwd_recv(const ConvArgs& a) {
   const dim3 grid(a.n_nodes), block(C::WPB_R * 64);
   if (a.grad_w && gY)
     hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 3, GEOM>), grid, block, 0, a.stream,
-                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY);
+                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY, a.r_order);
   else if (a.grad_w)
     hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 1, GEOM>), grid, block, 0, a.stream,
-                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY);
+                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY, a.r_order);
   else
     hipLaunchKernelGGL((k_conv_bwd_recv<S, U, C::WPB_R, C::NBUF_R, 2, GEOM>), grid, block, 0, a.stream,
-                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY);
+                       a.row_ptr, a.col, a.x, Y, a.w, a.grad_out, a.grad_w, gY, a.r_order);
   return hipGetLastError();
 }
 
@@ -1350,7 +1360,7 @@ hipError_t launch_bwd_send(const ConvArgs& a) {
   if (a.n_nodes == 0 || !a.grad_x) return hipSuccess;
   hipLaunchKernelGGL((k_conv_bwd_send<S, U, C::WPB_S, C::NBUF_S, GEOM>), dim3(a.n_nodes), dim3(C::WPB_S * 64),
                      0, a.stream, a.t_row_ptr, a.t_perm, a.t_col, edge_geom<GEOM>(a), a.w, a.grad_out,
-                     a.grad_x);
+                     a.grad_x, a.s_order);
   return hipGetLastError();
 }
 
@@ -1364,16 +1374,16 @@ hipError_t launch_bwd_fused_as(const ConvArgs& a) {
   const dim3 grid(a.n_nodes), block(F::WPB * 64);
   if (a.grad_w && gY)
     hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 3, GEOM, IDQ>), grid, block, 0, a.stream,
-                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
+                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY, a.s_order);
   else if (a.grad_w)
     hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 1, GEOM, IDQ>), grid, block, 0, a.stream,
-                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
+                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY, a.s_order);
   else if (gY)
     hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 2, GEOM, IDQ>), grid, block, 0, a.stream,
-                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
+                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY, a.s_order);
   else if constexpr (IDQ)
     hipLaunchKernelGGL((k_conv_bwd_fused<S, U, F::WPB, F::NBUF, 0, GEOM, IDQ>), grid, block, 0, a.stream,
-                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY);
+                       a.t_row_ptr, a.t_perm, a.t_col, a.x, Y, a.w, a.grad_out, a.grad_x, a.grad_w, gY, a.s_order);
   return hipGetLastError();
 }
 

@@ -355,6 +355,41 @@ tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64
   return e == hipSuccess ? TP_OK : hip_error(e, "gather_rows launch");
 }
 
+// Launch order of the receiver- or sender-grouped kernels: nodes by
+// descending degree, ties in ascending node id, as the stable sort of
+// keys[i] = E - deg_i.  Degrees are clamped into [0, E].
+__global__ void __launch_bounds__(256)
+    k_degree_keys(const int32_t* __restrict__ ptr, int n, int n_edges, uint32_t* __restrict__ keys) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const int d = min(max(ptr[i + 1] - ptr[i], 0), n_edges);
+    keys[i] = (uint32_t)(n_edges - d);
+  }
+}
+
+size_t order_workspace_bytes(int n_nodes) {
+  return ws_layout(0, n_nodes, nullptr, nullptr) + align256((size_t)(n_nodes > 0 ? n_nodes : 1) * 4);
+}
+
+tp_status launch_order(const int32_t* row_ptr, const int32_t* t_row_ptr, int n_nodes, int n_edges,
+                       int32_t* order, int32_t* t_order, void* ws_ptr, hipStream_t st) {
+  if (n_nodes == 0) return TP_OK;
+  GraphWs ws;
+  const size_t base = ws_layout(0, n_nodes, static_cast<char*>(ws_ptr), &ws);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws_ptr) + base);
+  const int nb = cdiv(n_nodes, 256);
+  const int32_t* ptrs[2] = {row_ptr, t_row_ptr};
+  int32_t* outs[2] = {order, t_order};
+  for (int s = 0; s < 2; ++s) {
+    if (!outs[s]) continue;
+    hipLaunchKernelGGL(k_degree_keys, dim3(nb), dim3(256), 0, st, ptrs[s], n_nodes, n_edges, keys);
+    hipError_t e = radix_sort(keys, n_nodes, n_edges, ws.sorted, outs[s], ws, st);
+    if (e != hipSuccess) return hip_error(e, "launch order sort");
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TP_OK : hip_error(e, "launch order launch");
+}
+
 // e_pos[t_perm[k]] = k: for each receiver-sorted edge, its sender-grouped
 // position (the inverse permutation of t_perm).  Entries outside [0, E) (a
 // grouping that did not come from the build) are skipped, never written.

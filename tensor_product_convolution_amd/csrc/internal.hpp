@@ -24,6 +24,8 @@ struct ConvArgs {
   // row of receiver-sorted edge q, which the forward reads
   bool sender_rows = false;
   const int32_t* e_pos = nullptr;
+  // launch order of the receiver- and sender-grouped kernels (null: node id)
+  const int32_t *r_order = nullptr, *s_order = nullptr;
   const float *x = nullptr, *Y = nullptr, *w = nullptr, *grad_out = nullptr;
   float *out = nullptr, *grad_x = nullptr, *grad_Y = nullptr, *grad_w = nullptr;
   // second-order backward: cotangents of (grad_x, grad_Y, grad_w), outputs
@@ -169,6 +171,9 @@ tp_status graph_build_static(const int32_t* src, const int32_t* dst, int n_edges
 tp_status gather_rows(const void* in, const int32_t* perm, int64_t n_rows, int64_t words, void* out,
                       hipStream_t st);
 tp_status sender_positions(const int32_t* t_perm, int n_edges, int32_t* e_pos, hipStream_t st);
+size_t order_workspace_bytes(int n_nodes);
+tp_status launch_order(const int32_t* row_ptr, const int32_t* t_row_ptr, int n_nodes, int n_edges,
+                       int32_t* order, int32_t* t_order, void* ws, hipStream_t st);
 tp_status sph_harm(int lmax, const float* r, int n, float* Y, hipStream_t st);
 tp_status sph_harm_bwd(int lmax, const float* r, int n, const float* gY, const float* grl, float* gr,
                        hipStream_t st);

@@ -413,3 +413,21 @@ def test_sender_layout_argument_errors_without_launch():
     # nothing requested: returns before any launch
     assert L.tp_conv_backward_sg(p.handle, ctypes.byref(g), fake, fake, fake, fake, None, None, None,
                                  None) == 0
+
+
+def test_launch_order_argument_errors_without_launch():
+    """tp_conv_graph_launch_order checks its graph, outputs and workspace on the
+    host; the graph struct carries the optional order fields at its end."""
+    L = tpc.lib()
+    assert [f[0] for f in tpc._Graph._fields_][-2:] == ["order", "t_order"]
+    fake = ctypes.c_void_p(0x1000)
+    need = ctypes.c_size_t()
+    assert L.tp_conv_graph_order_workspace(1000, ctypes.byref(need)) == 0 and need.value >= 4000
+    assert L.tp_conv_graph_order_workspace(-1, ctypes.byref(need)) == -1
+    g = tpc._Graph(4, 10, fake, fake, fake, fake, fake, fake)
+    no_sender = tpc._Graph(4, 10, fake, fake, fake, None, None, None)
+    assert L.tp_conv_graph_launch_order(ctypes.byref(g), None, None, fake, 1 << 20, None) == -1
+    assert L.tp_conv_graph_launch_order(ctypes.byref(g), fake, fake, fake, 16, None) == -5
+    assert L.tp_conv_graph_launch_order(ctypes.byref(g), fake, fake, None, 1 << 20, None) == -5
+    assert L.tp_conv_graph_launch_order(ctypes.byref(no_sender), fake, fake, fake, 1 << 20, None) == -1
+    assert L.tp_conv_graph_launch_order(None, fake, fake, fake, 1 << 20, None) == -1

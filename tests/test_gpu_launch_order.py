@@ -1,0 +1,121 @@
+"""GPU: launch orders (tp_conv_graph_launch_order) and the convolution with
+them, through the C ABI.
+
+Bar: order / t_order bit for bit those of the oracle (nodes by descending
+degree, ties by node id) on every workload's graph and on edge cases; the
+forward, the backward (one-pass, two-pass, edge-vector and sender-grouped
+forms) bit for bit the same with and without a launch order, and within 1e-4
+* max|ref| per irrep block of the float64 oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests._common import dims_of
+from tests.test_gpu_parity import (T, block_err, in_blocks, out_blocks, plans, say, w_err, y_blocks)
+from workloads import make_workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def tpc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tensor_product_convolution_amd as m
+    m.lib()
+    return m
+
+
+def check_orders(tpc, src, dst, n):
+    g = tpc.graph_launch_order(tpc.graph_build(T(np.asarray(src, np.int32)), T(np.asarray(dst, np.int32)), n))
+    torch.cuda.synchronize()
+    ref = oracle.csr_build(src, dst, n)
+    assert np.array_equal(g.order.cpu().numpy(), oracle.launch_order(ref["row_ptr"]))
+    assert np.array_equal(g.t_order.cpu().numpy(), oracle.launch_order(ref["t_row_ptr"]))
+    return g
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "lmax3", "zipf", "stream"])
+def test_launch_order_bit_exact_full_size(tpc, name):
+    say(f"launch order {name}")
+    wl = make_workload(name, dict(xdim=0, n_paths=0, U=0, outdim=0, n_out_irreps=0), graph_only=True)
+    check_orders(tpc, wl.src, wl.dst, wl.n_nodes)
+
+
+def test_launch_order_edge_cases(tpc):
+    rng = np.random.default_rng(0)
+    say("launch order edge cases")
+    check_orders(tpc, np.zeros(0, np.int32), np.zeros(0, np.int32), 5)            # no edges: node order
+    check_orders(tpc, [0, 0, 0], [0, 0, 0], 1)                                    # one node
+    check_orders(tpc, rng.integers(0, 50, 7000), np.zeros(7000, np.int64), 50)    # one hub
+    check_orders(tpc, rng.integers(0, 300000, 5000), rng.integers(0, 300000, 5000), 300000)  # 3 passes
+    # one grouping only
+    g = tpc.graph_build(T(np.array([1, 2, 2], np.int32)), T(np.array([0, 0, 1], np.int32)), 3)
+    tpc.graph_launch_order(g, senders=False)
+    torch.cuda.synchronize()
+    assert g.t_order is None and g.order.cpu().tolist() == [0, 1, 2]
+    tpc.graph_launch_order(g, receivers=False)
+    torch.cuda.synchronize()
+    assert g.order is None and g.t_order.cpu().tolist() == [2, 1, 0]
+
+
+def run(tpc, plan, wl, ordered, forms=("y", "r", "sg")):
+    g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+    if ordered:
+        tpc.graph_launch_order(g)
+    r = tpc.gather_rows(T(wl.r), g.perm)
+    Y = tpc.sph_harm(plan.lmax_sh, r)
+    w = tpc.gather_rows(T(wl.w), g.perm)
+    x, go = T(wl.x), T(wl.g)
+    res = {"out": tpc.forward(plan, g, x, Y, w)}
+    res["gx"], res["gY"], res["gw"] = tpc.backward(plan, g, x, Y, w, go)
+    # each pass alone (the two-pass form's receiver and sender passes)
+    res["gx_only"] = tpc.backward(plan, g, x, Y, w, go, want=("x",))[0]
+    res["gw_only"] = tpc.backward(plan, g, x, Y, w, go, want=("w",))[2]
+    if "r" in forms:
+        res["out_r"] = tpc.forward_r(plan, g, x, r, w)
+        res["gx_r"], res["gr_r"], res["gw_r"] = tpc.backward_r(plan, g, x, r, w, go)
+    if "sg" in forms:
+        e_pos = tpc.graph_sender_positions(g)
+        Ys, ws = tpc.gather_rows(Y, g.t_perm), tpc.gather_rows(w, g.t_perm)
+        res["out_sg"] = tpc.forward_sg(plan, g, e_pos, x, Ys, ws)
+        res["gx_sg"], res["gY_sg"], res["gw_sg"] = tpc.backward_sg(plan, g, x, Ys, ws, go)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in res.items()}
+    out["perm"] = g.perm.cpu().numpy()[:wl.n_edges]
+    return out
+
+
+@pytest.mark.parametrize("name,n_nodes,mul,zipf_graph", [
+    ("mid", None, None, False),        # the full 1,536-atom graph
+    ("mid", 1100, None, True),         # hubs past the small-graph threshold
+    ("mid", 300, 128, False),
+    ("tiny", None, None, False),       # small-graph launch shape
+    ("lmax3", 600, 16, True),          # two-pass backward on a power-law graph
+])
+def test_conv_with_launch_order(tpc, name, n_nodes, mul, zipf_graph):
+    say(f"conv with launch order {name} n={n_nodes} mul={mul} zipf={zipf_graph}")
+    plan, op = plans(name, mul)
+    wl = make_workload(name, dims_of(op), n_nodes=n_nodes, seed=4)
+    if zipf_graph:
+        gz = make_workload("zipf", dims_of(op), n_nodes=wl.n_nodes, seed=4, graph_only=True)
+        wl.src, wl.dst, wl.r = gz.src, gz.dst, gz.r
+        rng = np.random.default_rng(5)
+        wl.w = (rng.normal(size=(len(wl.src), op.n_paths, op.U)) / np.sqrt(op.n_paths)).astype(np.float32)
+    forms = ("y", "r") if op.lmax_sh == 3 else ("y", "r", "sg")
+    a = run(tpc, plan, wl, False, forms)
+    b = run(tpc, plan, wl, True, forms)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    Y = oracle.sh_real(op.lmax_sh, wl.r)
+    ref = oracle.tp_conv_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w)
+    assert block_err(b["out"], ref, out_blocks(op)) <= TOL
+    gx, gY, gw = oracle.tp_conv_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Y, wl.w, wl.g)
+    p = b["perm"]
+    assert block_err(b["gx"], gx, in_blocks(op)) <= TOL
+    assert block_err(b["gY"], gY[p], y_blocks(op)) <= TOL
+    assert w_err(b["gw"], gw[p]) <= TOL
