@@ -103,9 +103,9 @@ __global__ void __launch_bounds__(64 * NW)
                const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ w,
                const float* __restrict__ g, const float* __restrict__ ggx, const float* __restrict__ ggY,
                const float* __restrict__ ggw, float* __restrict__ dY, float* __restrict__ dw,
-               float* __restrict__ dg) {
+               float* __restrict__ dg, const int32_t* __restrict__ order) {
   using M = LaneMap<U>;
-  const int i = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int i = launch_node(order, gridDim.x), lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
   if constexpr (dbl_one_walk<S, U>()) {
@@ -293,9 +293,9 @@ __global__ void __launch_bounds__(64 * NW)
     k_dbl_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                const int32_t* __restrict__ t_col, const float* __restrict__ Y, const float* __restrict__ w,
                const float* __restrict__ g, const float* __restrict__ ggY, const float* __restrict__ ggw,
-               float* __restrict__ dx) {
+               float* __restrict__ dx, const int32_t* __restrict__ order) {
   using M = LaneMap<U>;
-  const int j = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int j = launch_node(order, gridDim.x), lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / M::LPE, uu = lane % M::LPE;
   const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
   float acc[M::CPL][S::XC];
@@ -348,7 +348,7 @@ hipError_t launch_dbl_recv(const ConvArgs& a) {
   if (a.n_nodes == 0 || (!a.d_Y && !a.d_w && !a.d_g)) return hipSuccess;
   constexpr int NW = dbl_waves<U>();
   hipLaunchKernelGGL((k_dbl_recv<S, U, NW>), dim3(a.n_nodes), dim3(64 * NW), 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
-                     a.w, a.grad_out, a.gg_x, a.gg_Y, a.gg_w, a.d_Y, a.d_w, a.d_g);
+                     a.w, a.grad_out, a.gg_x, a.gg_Y, a.gg_w, a.d_Y, a.d_w, a.d_g, a.r_order);
   return hipGetLastError();
 }
 
@@ -357,7 +357,7 @@ hipError_t launch_dbl_send(const ConvArgs& a) {
   if (a.n_nodes == 0 || !a.d_x) return hipSuccess;
   constexpr int NW = dbl_waves<U>();
   hipLaunchKernelGGL((k_dbl_send<S, U, NW>), dim3(a.n_nodes), dim3(64 * NW), 0, a.stream, a.t_row_ptr, a.t_perm,
-                     a.t_col, a.Y, a.w, a.grad_out, a.gg_Y, a.gg_w, a.d_x);
+                     a.t_col, a.Y, a.w, a.grad_out, a.gg_Y, a.gg_w, a.d_x, a.s_order);
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@ Bar: order / t_order bit for bit those of the oracle (nodes by descending
 degree, ties by node id) on every workload's graph and on edge cases; the
 forward, the backward (one-pass, two-pass, edge-vector and sender-grouped
 forms) bit for bit the same with and without a launch order, and within 1e-4
-* max|ref| per irrep block of the float64 oracle.
+* max|ref| per irrep block of the float64 oracle; the second-order backward
+bit for bit the same with and without a launch order.
 """
 import numpy as np
 import pytest
@@ -76,6 +77,9 @@ def run(tpc, plan, wl, ordered, forms=("y", "r", "sg")):
     # each pass alone (the two-pass form's receiver and sender passes)
     res["gx_only"] = tpc.backward(plan, g, x, Y, w, go, want=("x",))[0]
     res["gw_only"] = tpc.backward(plan, g, x, Y, w, go, want=("w",))[2]
+    # second order, the first-order outputs as cotangents
+    res["dx"], res["dY"], res["dw"], res["dg"] = tpc.double_backward(plan, g, x, Y, w, go, res["gx"],
+                                                                     res["gY"], res["gw"])
     if "r" in forms:
         res["out_r"] = tpc.forward_r(plan, g, x, r, w)
         res["gx_r"], res["gr_r"], res["gw_r"] = tpc.backward_r(plan, g, x, r, w, go)
