@@ -892,7 +892,7 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     NH = radial[1]
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     src, dst = T(wl.src), T(wl.dst)
-    g = tpc.graph_build(src, dst, N)
+    g = tpc.graph_launch_order(tpc.graph_build(src, dst, N))    # grouping and launch order
     Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
     rl = tpc.gather_rows(T(wl.r_len), g.perm)
     x, W1, W2, Wm, go = T(wl.x), T(wl.W1), T(wl.W2), T(wl.Wmix), T(wl.g)
@@ -941,6 +941,16 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
     t = timed_steps(step, args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
+    # the same step with the nodes walked in node order (no launch order)
+    gn = node_order(g)
+
+    def step_node_order():
+        tpc.forward_radial(plan, gn, x, Y, rl, W1, W2, Wm, out=out, out_pre=pre)
+        tpc.backward_radial(plan, gn, x, Y, rl, W1, W2, go, Wmix=Wm, out_pre=pre, outs=outs, ws=ws)
+
+    t_no = timed_steps(step_node_order, args.steps, True)
+    step()          # the outputs read back below are the timed step's
+    torch.cuda.synchronize()
     # the timed step's results, for the parity check on the CPU-baseline sample
     snap = ({"out": out.cpu().numpy(), "gY": outs["Y"].cpu().numpy(), "perm": g.perm.cpu().numpy()[:E]}
             if cpu else None)
@@ -989,6 +999,9 @@ def bench_radial(name, args, torch, tpc, dev, flush, cpu=True):
         "ms_per_step": step_ms,
         "edges_per_s": E / (step_ms * 1e-3),
         "ms_per_step_p10_p90": [float(np.percentile(t, 10)), float(np.percentile(t, 90))],
+        "launch_order": "every pass walks its nodes by descending degree (tp_conv_graph_launch_order)",
+        "node_order_ms_per_step": float(t_no.mean()),
+        "node_order_note": "the same step with the nodes walked in node order, one step per flush",
         "fwd_edges_per_s": E / (kt["fwd_with_mix"] * 1e-3),
         "kernel_ms": kt,
         "kernel_ms_note": ((f"per call, {reps} back-to-back calls after a cache flush, mean of {rounds} "

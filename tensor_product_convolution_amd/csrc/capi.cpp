@@ -1084,6 +1084,8 @@ static tp_status forward_radial_impl(tp_plan_t plan, const tp_graph* graph, cons
   if (Wmix && N > 0 && (!out_pre || out_pre == out))
     return set_error(TP_ERR_ARG, "tp_conv_forward_radial: a mix needs a separate out_pre buffer");
   tpc::RadialArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.row_ptr = graph->row_ptr;
@@ -1182,6 +1184,8 @@ static tp_status backward_radial_impl(tp_plan_t plan, const tp_graph* graph, con
     g = gmix;
   }
   tpc::RadialArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.row_ptr = graph->row_ptr;
@@ -1289,6 +1293,8 @@ tp_status tp_conv_double_backward_radial(tp_plan_t plan, const tp_graph* graph, 
     g = gmix;
   }
   tpc::RadialArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.row_ptr = graph->row_ptr;

@@ -55,6 +55,8 @@ struct RadialArgs {
   int32_t n_nodes = 0, n_edges = 0;
   const int32_t *row_ptr = nullptr, *col = nullptr;
   const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
+  // launch order of the receiver- and sender-grouped passes (null: node id)
+  const int32_t *r_order = nullptr, *s_order = nullptr;
   const float *x = nullptr, *Y = nullptr, *r_len = nullptr, *W1 = nullptr, *W2 = nullptr;
   const float* grad_out = nullptr;   // gradient w.r.t. the unmixed output
   float *out = nullptr, *grad_x = nullptr, *grad_Y = nullptr, *grad_W1 = nullptr, *grad_W2 = nullptr;

@@ -302,7 +302,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     k_radial_bwd_recv(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                       const float* __restrict__ x, const float* __restrict__ Y,
                       const float* __restrict__ r_len, RadialParams rp, const float* __restrict__ gout,
-                      float* __restrict__ grad_Y, float* __restrict__ grad_rlen, float* __restrict__ part) {
+                      float* __restrict__ grad_Y, float* __restrict__ grad_rlen, float* __restrict__ part,
+                      const int32_t* __restrict__ order) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NH <= 64 && NB <= 16, "radial tiling");
   using L = W2Slice<S, NH>;
   constexpr int GF = 16 * S::OC;                    // staged grad_out floats per wave
@@ -319,20 +320,21 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   float w1[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) w1[n] = 0.f;
-  // tile cursor of this wave: receiver i, first edge t0
+  // tile cursor of this wave: position pos of the launch order, its receiver i, first edge t0
   const int stride = gridDim.x * NW;
-  int i = blockIdx.x * NW + wv, t0 = 0, end = 0;
-  auto seek = [&]() {   // first receiver >= i with edges
-    while (i < n_nodes) {
+  int pos = blockIdx.x * NW + wv, i = 0, t0 = 0, end = 0;
+  auto seek = [&]() {   // first position >= pos whose receiver has edges
+    while (pos < n_nodes) {
+      i = order ? min(max(order[pos], 0), n_nodes - 1) : pos;
       t0 = row_ptr[i];
       end = row_ptr[i + 1];
       if (t0 < end) break;
-      i += stride;
+      pos += stride;
     }
   };
   seek();
-  while (__syncthreads_or(i < n_nodes)) {
-    const bool has = i < n_nodes;
+  while (__syncthreads_or(pos < n_nodes)) {
+    const bool has = pos < n_nodes;
     const int q = t0 + e16;
     const bool valid = has && q < end;
     const int qc = has ? (q < end ? q : end - 1) : 0;
@@ -484,7 +486,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
       // advance the cursor
       t0 += 16;
       if (t0 >= end) {
-        i += stride;
+        pos += stride;
         seek();
       }
     }
@@ -516,7 +518,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
     k_radial_bwd_w2(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                     const float* __restrict__ x, const float* __restrict__ Y,
                     const float* __restrict__ r_len, RadialParams rp, const float* __restrict__ gout,
-                    float* __restrict__ part) {
+                    float* __restrict__ part, const int32_t* __restrict__ order) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NB % 4 == 0, "radial tiling");
   static_assert(P0 >= 0 && NPG > 0 && P0 + NPG <= S::NP, "path group");
   constexpr int NW = NH / 16;
@@ -541,19 +543,20 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
   const float pre_b = sqrtf(2.0f / rp.r_cut);
   const float kk = 3.14159265358979323846f / rp.r_cut;
   const int stride = gridDim.x * NW;
-  int i = blockIdx.x * NW + wv, t0 = 0, end = 0;
+  int pos = blockIdx.x * NW + wv, i = 0, t0 = 0, end = 0;
   auto seek = [&]() {
-    while (i < n_nodes) {
+    while (pos < n_nodes) {
+      i = order ? min(max(order[pos], 0), n_nodes - 1) : pos;
       t0 = row_ptr[i];
       end = row_ptr[i + 1];
       if (t0 < end) break;
-      i += stride;
+      pos += stride;
     }
   };
   seek();
   float* gw_own = s_gw + wv * TILE;
-  while (__syncthreads_or(i < n_nodes)) {
-    if (i < n_nodes) {
+  while (__syncthreads_or(pos < n_nodes)) {
+    if (pos < n_nodes) {
       if (g == 0) {
         const int q = t0 + e16;
         s_r[wv * 16 + e16] = q < end ? radial_edge_len<GEOM>(Y, r_len, q) : -1.f;
@@ -581,7 +584,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
       }
       t0 += 16;
       if (t0 >= end) {
-        i += stride;
+        pos += stride;
         seek();
       }
     } else {
@@ -644,7 +647,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     k_radial_node(int n_nodes, const int32_t* __restrict__ ptr, const int32_t* __restrict__ perm,
                   const int32_t* __restrict__ other, const float* __restrict__ feat,
                   const float* __restrict__ Y, const float* __restrict__ r_len, RadialParams rp,
-                  float* __restrict__ outp) {
+                  float* __restrict__ outp, const int32_t* __restrict__ order) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NH <= 64, "radial tiling");
   using L = W2Slice<S, NH>;
   constexpr int NA = SEND ? S::XC : S::OC;          // accumulated components per channel
@@ -661,9 +664,10 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   float acc[NA];
 #pragma unroll
   for (int o = 0; o < NA; ++o) acc[o] = 0.f;
-  // this lane group's cursor: node, next edge, end of the node's edges
+  // this lane group's cursor: position pos of the launch order, its node,
+  // next edge, end of the node's edges
   const int gstride = gridDim.x * NW * 4;
-  int node = (blockIdx.x * NW + wv) * 4 + g, q = 0, qend = 0;
+  int pos = (blockIdx.x * NW + wv) * 4 + g, node = 0, q = 0, qend = 0;
   auto store = [&]() {                              // the group's node row, this channel
     if constexpr (SEND) {
       float* row = outp + (size_t)node * (U * S::XC);
@@ -682,18 +686,19 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
     }
   };
   auto seek = [&]() {                               // next node with edges; zero rows on the way
-    while (node < n_nodes) {
+    while (pos < n_nodes) {
+      node = order ? min(max(order[pos], 0), n_nodes - 1) : pos;
       q = ptr[node];
       qend = ptr[node + 1];
       if (q < qend) break;
       store();                                      // acc is zero here
-      node += gstride;
+      pos += gstride;
     }
   };
   seek();
   // all groups of the wave step together until every one has run out of nodes
-  while (__ballot(node < n_nodes) != 0ull) {
-    const bool act = node < n_nodes;
+  while (__ballot(pos < n_nodes) != 0ull) {
+    const bool act = pos < n_nodes;
     // gathered operands of the lane's four edges, requested first so that
     // they arrive while the hidden layer and the weights are computed; a slot
     // past the node's edges (or of a group without a node) reads a valid edge
@@ -739,7 +744,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
         store();
 #pragma unroll
         for (int o = 0; o < NA; ++o) acc[o] = 0.f;
-        node += gstride;
+        pos += gstride;
         seek();
       }
     }

@@ -101,7 +101,7 @@ hipError_t launch_radial_fwd_as(const RadialArgs& a) {
   RadialParams rp{a.r_cut, a.W1, a.W2};
   hipLaunchKernelGGL((k_radial_node<S, U, kNB, kNH, kNodeWaves, false, GEOM>), group_grid<U>(a.n_nodes),
                      dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.row_ptr, nullptr, a.col, a.x, a.Y,
-                     a.r_len, rp, a.out);
+                     a.r_len, rp, a.out, a.r_order);
   return hipGetLastError();
 }
 template <class R, int U>
@@ -123,7 +123,8 @@ void launch_w2_groups(const RadialArgs& a, const RadialParams& rp, int nb2, floa
   if constexpr (P0 < S::NP) {
     constexpr int N = S::NP - P0 < R::npg ? S::NP - P0 : R::npg;
     hipLaunchKernelGGL((k_radial_bwd_w2<S, U, kNB, kNH, GEOM, P0, N>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)),
-                       0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.grad_out, part2);
+                       0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len, rp, a.grad_out, part2,
+                       a.r_order);
     launch_w2_groups<R, U, GEOM, G + 1>(a, rp, nb2, part2);
   }
 }
@@ -142,7 +143,7 @@ hipError_t launch_radial_bwd_as(const RadialArgs& a) {
   if (a.grad_Y || a.grad_W1 || a.grad_rlen) {
     hipLaunchKernelGGL((k_radial_bwd_recv<S, U, kNB, kNH, RW, GEOM>), dim3(recv_blocks<RW>(a.n_nodes)),
                        dim3(64 * RW), 0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.Y, a.r_len,
-                       rp, a.grad_out, a.grad_Y, a.grad_rlen, part1);
+                       rp, a.grad_out, a.grad_Y, a.grad_rlen, part1, a.r_order);
     if (a.grad_W1) {
       const long long n = (long long)kNB * kNH;
       hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, a.stream,
@@ -158,7 +159,7 @@ hipError_t launch_radial_bwd_as(const RadialArgs& a) {
   if (a.grad_x && a.n_nodes > 0)
     hipLaunchKernelGGL((k_radial_node<S, U, kNB, kNH, kNodeWaves, true, GEOM>), group_grid<U>(a.n_nodes),
                        dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.t_row_ptr, a.t_perm, a.t_col,
-                       a.grad_out, a.Y, a.r_len, rp, a.grad_x);
+                       a.grad_out, a.Y, a.r_len, rp, a.grad_x, a.s_order);
   return hipGetLastError();
 }
 

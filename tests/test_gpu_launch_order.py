@@ -123,3 +123,45 @@ def test_conv_with_launch_order(tpc, name, n_nodes, mul, zipf_graph):
     assert block_err(b["gx"], gx, in_blocks(op)) <= TOL
     assert block_err(b["gY"], gY[p], y_blocks(op)) <= TOL
     assert w_err(b["gw"], gw[p]) <= TOL
+
+
+@pytest.mark.parametrize("U,lsh,graph,n", [(16, 3, "zipf", 400), (16, 3, "lmax3", 1100),
+                                           (128, 2, "lmax3", 150)])
+def test_radial_layer_with_launch_order(tpc, U, lsh, graph, n):
+    """The radial-weight layer with a launch order: per-node and per-edge
+    outputs bit for bit those in node order (each node is still formed by one
+    lane group or wave), the parameter gradients, whose per-wave partial sums
+    now collect other nodes, within the bar of the oracle."""
+    from tests.test_gpu_radial import _check_params, _vec_err
+    say(f"radial layer with launch order U={U} lmax={lsh} graph={graph} n={n}")
+    irr = "+".join(f"{U}x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(lsh + 1))
+    op = oracle.build_plan(irr, lsh, lsh)
+    wl = make_workload("stream", dims_of(op), seed=U + n, n_nodes=n)
+    gw = make_workload(graph, dims_of(op), seed=U + n, n_nodes=n, graph_only=True)
+    wl.src, wl.dst, wl.r = gw.src, gw.dst, gw.r
+    plan = tpc.Plan(irr, lsh, lsh, radial=(8, 64, 5.0), uvw=True)
+    res = []
+    for ordered in (False, True):
+        g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+        if ordered:
+            tpc.graph_launch_order(g)
+        Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
+        rl = tpc.gather_rows(T(wl.r_len), g.perm)
+        x, W1, W2, Wm, go = T(wl.x), T(wl.W1), T(wl.W2), T(wl.Wmix), T(wl.g)
+        out, pre = tpc.forward_radial(plan, g, x, Y, rl, W1, W2, Wm)
+        b = tpc.backward_radial(plan, g, x, Y, rl, W1, W2, go, Wmix=Wm, out_pre=pre,
+                                want=("x", "Y", "W1", "W2", "Wmix", "rlen"))
+        torch.cuda.synchronize()
+        res.append([t.cpu().numpy() for t in (out, pre) + tuple(b)] + [g.perm.cpu().numpy()[:wl.n_edges]])
+    a, o = res
+    for k, name in enumerate(("out", "out_pre", "grad_x", "grad_Y")):
+        assert np.array_equal(a[k], o[k]), name
+    assert np.array_equal(a[7], o[7])                                   # grad_rlen
+    Yo = oracle.sh_real(lsh, wl.r)
+    rb = oracle.tp_conv_radial_bwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, Yo, wl.r_len, wl.W1, wl.W2, wl.Wmix,
+                                   wl.g, 8, 5.0, with_grad_rlen=True)
+    p = o[8]
+    assert block_err(o[2], rb[0], in_blocks(op)) <= TOL
+    assert block_err(o[3], rb[1][p], y_blocks(op)) <= TOL
+    assert _vec_err(o[7], rb[5][p]) <= TOL
+    _check_params(op, dict(gW1=o[4], gW2=o[5], gWm=o[6]), rb, U)
