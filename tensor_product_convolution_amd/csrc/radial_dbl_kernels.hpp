@@ -102,7 +102,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
                       const int32_t* __restrict__ other, const float* __restrict__ feat,
                       const float* __restrict__ gfeat, const float* __restrict__ Y,
                       const float* __restrict__ ggY, const float* __restrict__ r_len,
-                      const float* __restrict__ ggr, RadialParams rp, float* __restrict__ outp) {
+                      const float* __restrict__ ggr, RadialParams rp, float* __restrict__ outp,
+                      const int32_t* __restrict__ order) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NH <= 64, "radial tiling");
   using L = W2Slice<S, NH>;
   constexpr int NA = SEND ? S::XC : S::OC;          // accumulated components per channel
@@ -117,7 +118,9 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)
   stage_w2<S, U, NH, NW>(w2s, rp.W2, c, wv, lane);
   wait_vmcnt<0>();
   __syncthreads();
-  for (int i = blockIdx.x * NW + wv; i < n_nodes; i += gridDim.x * NW) {
+  // positions of the launch order, their nodes i
+  for (int pos = blockIdx.x * NW + wv; pos < n_nodes; pos += gridDim.x * NW) {
+    const int i = order ? min(max(order[pos], 0), n_nodes - 1) : pos;
     const int beg = ptr[i], end = ptr[i + 1];
     float acc[NA];
 #pragma unroll
@@ -241,7 +244,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1,
                       const float* __restrict__ x, const float* __restrict__ ggx, const float* __restrict__ Y,
                       const float* __restrict__ ggY, const float* __restrict__ r_len,
                       const float* __restrict__ ggr, RadialParams rp, const float* __restrict__ gout,
-                      float* __restrict__ d_Y, float* __restrict__ d_rlen, float* __restrict__ part) {
+                      float* __restrict__ d_Y, float* __restrict__ d_rlen, float* __restrict__ part,
+                      const int32_t* __restrict__ order) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NH <= 64 && NB <= 16, "radial tiling");
   using L = W2Slice<S, NH>;
   constexpr int GF = 16 * S::OC;                    // staged upstream-gradient floats per wave
@@ -260,18 +264,19 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1,
 #pragma unroll
   for (int n = 0; n < NB; ++n) w1[n] = 0.f;
   const int stride = gridDim.x * NW;
-  int i = blockIdx.x * NW + wv, t0 = 0, end = 0;
+  int pos = blockIdx.x * NW + wv, i = 0, t0 = 0, end = 0;   // position of the launch order, its node
   auto seek = [&]() {
-    while (i < n_nodes) {
+    while (pos < n_nodes) {
+      i = order ? min(max(order[pos], 0), n_nodes - 1) : pos;
       t0 = row_ptr[i];
       end = row_ptr[i + 1];
       if (t0 < end) break;
-      i += stride;
+      pos += stride;
     }
   };
   seek();
-  while (__syncthreads_or(i < n_nodes)) {
-    const bool has = i < n_nodes;
+  while (__syncthreads_or(pos < n_nodes)) {
+    const bool has = pos < n_nodes;
     const int q = t0 + e16;
     const bool valid = has && q < end;
     const int qc = has ? (q < end ? q : end - 1) : 0;
@@ -479,7 +484,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1,
       }
       t0 += 16;
       if (t0 >= end) {
-        i += stride;
+        pos += stride;
         seek();
       }
     }
@@ -505,7 +510,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
                     const float* __restrict__ x, const float* __restrict__ ggx, const float* __restrict__ Y,
                     const float* __restrict__ ggY, const float* __restrict__ r_len,
                     const float* __restrict__ ggr, RadialParams rp, const float* __restrict__ gout,
-                    float* __restrict__ part) {
+                    float* __restrict__ part, const int32_t* __restrict__ order) {
   static_assert(U % 16 == 0 && NH % 16 == 0 && NB % 4 == 0, "radial tiling");
   static_assert(P0 >= 0 && NPG > 0 && P0 + NPG <= S::NP, "path group");
   constexpr int NW = NH / 16;
@@ -528,19 +533,20 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
   const float cb = sqrtf(2.0f / rp.r_cut);
   const float kk = 3.14159265358979323846f / rp.r_cut;
   const int stride = gridDim.x * NW;
-  int i = blockIdx.x * NW + wv, t0 = 0, end = 0;
+  int pos = blockIdx.x * NW + wv, i = 0, t0 = 0, end = 0;   // position of the launch order, its node
   auto seek = [&]() {
-    while (i < n_nodes) {
+    while (pos < n_nodes) {
+      i = order ? min(max(order[pos], 0), n_nodes - 1) : pos;
       t0 = row_ptr[i];
       end = row_ptr[i + 1];
       if (t0 < end) break;
-      i += stride;
+      pos += stride;
     }
   };
   seek();
   float* gw_own = s_gw + wv * TILE;
-  while (__syncthreads_or(i < n_nodes)) {
-    if (i < n_nodes) {
+  while (__syncthreads_or(pos < n_nodes)) {
+    if (pos < n_nodes) {
       if (g == 0) {
         const int q = t0 + e16;
         s_r[wv * 16 + e16] = q < end ? r_len[q] : -1.f;
@@ -589,7 +595,7 @@ __global__ void __launch_bounds__(64 * (NH / 16)) __attribute__((amdgpu_waves_pe
       }
       t0 += 16;
       if (t0 >= end) {
-        i += stride;
+        pos += stride;
         seek();
       }
     } else {

@@ -185,7 +185,7 @@ void launch_dbl_w2_groups(const RadialArgs& a, const RadialParams& rp, int nb2, 
     constexpr int N = S::NP - P0 < R::npg ? S::NP - P0 : R::npg;
     hipLaunchKernelGGL((k_radial_dbl_w2<S, U, kNB, kNH, KIND, P0, N>), dim3(nb2, U / 16), dim3(64 * (kNH / 16)),
                        0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.gg_x, a.Y, a.gg_Y, a.r_len, a.gg_rlen,
-                       rp, a.grad_out, part2);
+                       rp, a.grad_out, part2, a.r_order);
     launch_dbl_w2_groups<R, U, KIND, G + 1>(a, rp, nb2, part2);
   }
 }
@@ -203,11 +203,11 @@ hipError_t launch_radial_dbl(const RadialArgs& a) {
   if (a.out && a.n_nodes > 0)
     hipLaunchKernelGGL((k_radial_node_dbl<S, U, kNB, kNH, kNodeWaves, false>), node_grid<U>(a.n_nodes),
                        dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.row_ptr, nullptr, a.col, a.x, a.gg_x,
-                       a.Y, a.gg_Y, a.r_len, a.gg_rlen, rp, a.out);
+                       a.Y, a.gg_Y, a.r_len, a.gg_rlen, rp, a.out, a.r_order);
   if (a.d_Y || a.d_rlen || a.d_W1) {
     hipLaunchKernelGGL((k_radial_dbl_recv<S, U, kNB, kNH, kRecvWaves>), dim3(dbl_recv_blocks(a.n_nodes)),
                        dim3(64 * kRecvWaves), 0, a.stream, a.n_nodes, a.row_ptr, a.col, a.x, a.gg_x, a.Y,
-                       a.gg_Y, a.r_len, a.gg_rlen, rp, a.grad_out, a.d_Y, a.d_rlen, part1);
+                       a.gg_Y, a.r_len, a.gg_rlen, rp, a.grad_out, a.d_Y, a.d_rlen, part1, a.r_order);
     if (a.d_W1) {
       const long long n = (long long)kNB * kNH;
       hipLaunchKernelGGL(k_radial_sum, dim3((unsigned)((n + 63) / 64)), dim3(64 * kSumWaves), 0, a.stream,
@@ -225,7 +225,7 @@ hipError_t launch_radial_dbl(const RadialArgs& a) {
   if (a.d_x && a.n_nodes > 0)
     hipLaunchKernelGGL((k_radial_node_dbl<S, U, kNB, kNH, kNodeWaves, true>), node_grid<U>(a.n_nodes),
                        dim3(64 * kNodeWaves), 0, a.stream, a.n_nodes, a.t_row_ptr, a.t_perm, a.t_col,
-                       a.grad_out, nullptr, a.Y, a.gg_Y, a.r_len, a.gg_rlen, rp, a.d_x);
+                       a.grad_out, nullptr, a.Y, a.gg_Y, a.r_len, a.gg_rlen, rp, a.d_x, a.s_order);
   return hipGetLastError();
 }
 

@@ -165,3 +165,38 @@ def test_radial_layer_with_launch_order(tpc, U, lsh, graph, n):
     assert block_err(o[3], rb[1][p], y_blocks(op)) <= TOL
     assert _vec_err(o[7], rb[5][p]) <= TOL
     _check_params(op, dict(gW1=o[4], gW2=o[5], gWm=o[6]), rb, U)
+
+
+@pytest.mark.parametrize("U,lsh,graph,n", [(16, 2, "zipf", 400), (16, 3, "lmax3", 300)])
+def test_radial_double_backward_with_launch_order(tpc, U, lsh, graph, n):
+    """Second-order backward of the radial layer with a launch order: per-node
+    and per-edge outputs bit for bit those in node order, all outputs within
+    the bar of the oracle."""
+    from tests.test_gpu_radial_double import _check, _cotangents, _ref
+    say(f"radial double backward with launch order U={U} lmax={lsh} graph={graph} n={n}")
+    irr = "+".join(f"{U}x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(lsh + 1))
+    op = oracle.build_plan(irr, lsh, lsh)
+    wl = make_workload("stream", dims_of(op), seed=U + n, n_nodes=n)
+    gw = make_workload(graph, dims_of(op), seed=U + n, n_nodes=n, graph_only=True)
+    wl.src, wl.dst, wl.r = gw.src, gw.dst, gw.r
+    plan = tpc.Plan(irr, lsh, lsh, radial=(8, 64, 5.0), uvw=True)
+    ggx, ggY, ggr = _cotangents(op, wl.n_nodes, wl.n_edges, U + n)
+    names = ("dx", "dY", "drl", "dW1", "dW2", "dWm", "dg")
+    res = []
+    for ordered in (False, True):
+        g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+        if ordered:
+            tpc.graph_launch_order(g)
+        Y = tpc.sph_harm(lsh, tpc.gather_rows(T(wl.r), g.perm))
+        rl = tpc.gather_rows(T(wl.r_len), g.perm)
+        out = tpc.double_backward_radial(plan, g, T(wl.x), Y, rl, T(wl.W1), T(wl.W2), T(wl.g), Wmix=T(wl.Wmix),
+                                         gg_x=T(ggx), gg_Y=tpc.gather_rows(T(ggY), g.perm),
+                                         gg_rlen=tpc.gather_rows(T(ggr), g.perm))
+        torch.cuda.synchronize()
+        r = {k: v.cpu().numpy() for k, v in zip(names, out)}
+        r["perm"] = g.perm.cpu().numpy()[:wl.n_edges]
+        res.append(r)
+    a, o = res
+    for k in ("dx", "dY", "drl", "dg"):
+        assert np.array_equal(a[k], o[k]), k
+    _check(op, o, _ref(op, wl, True, wl.g, ggx, ggY, ggr, lmax=lsh), U, o["perm"])
