@@ -717,6 +717,8 @@ tp_status tp_conv_forward_fc(tp_plan_t plan, const tp_graph* graph, const float*
   if (reinterpret_cast<uintptr_t>(ws) & 15)
     return set_error(TP_ERR_ARG, "tp_conv_forward_fc: ws must be 16-byte aligned");
   tpc::FcArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.outdim = plan->outdim;
@@ -764,6 +766,8 @@ tp_status tp_conv_backward_fc(tp_plan_t plan, const tp_graph* graph, const float
   if ((reinterpret_cast<uintptr_t>(ws) | reinterpret_cast<uintptr_t>(Theta)) & 15)
     return set_error(TP_ERR_ARG, "tp_conv_backward_fc: ws and Theta must be 16-byte aligned");
   tpc::FcArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.outdim = plan->outdim;
@@ -823,6 +827,8 @@ tp_status tp_conv_double_backward_fc(tp_plan_t plan, const tp_graph* graph, cons
   if (misaligned16({ws, Theta, gg_Theta}))
     return set_error(TP_ERR_ARG, std::string(fn) + ": ws, Theta and gg_Theta must be 16-byte aligned");
   tpc::FcArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.outdim = plan->outdim;
@@ -893,6 +899,8 @@ tp_status tp_conv_forward_gaunt(tp_plan_t plan, const tp_graph* graph, const flo
   if (N > 0 && !out) return set_error(TP_ERR_ARG, "tp_conv_forward_gaunt: out NULL");
   if (E > 0 && (!x || !Y || !w)) return set_error(TP_ERR_ARG, "tp_conv_forward_gaunt: x/Y/w NULL");
   tpc::GauntArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.U = plan->mul;
@@ -926,6 +934,8 @@ tp_status tp_conv_backward_gaunt(tp_plan_t plan, const tp_graph* graph, const fl
   if (reinterpret_cast<uintptr_t>(w) & 15)
     return set_error(TP_ERR_ARG, "tp_conv_backward_gaunt: w must be 16-byte aligned");
   tpc::GauntArgs a;
+  a.r_order = graph->order;
+  a.s_order = graph->t_order;
   a.n_nodes = N;
   a.n_edges = E;
   a.U = plan->mul;
@@ -961,6 +971,8 @@ static tpc::GauntArgs gaunt_args(tp_plan_t plan, const tp_graph* graph, int N, i
   a.lmax_sh = plan->lmax_sh;
   a.lmax_out = plan->lmax_out;
   if (graph) {
+    a.r_order = graph->order;
+    a.s_order = graph->t_order;
     a.row_ptr = graph->row_ptr;
     a.col = graph->col;
     a.t_row_ptr = graph->t_row_ptr;

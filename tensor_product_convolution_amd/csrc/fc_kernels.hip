@@ -96,7 +96,7 @@ template <class S, int U, int H>
 __global__ void __launch_bounds__(256)
     k_fc_state(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ R,
-               float* __restrict__ Sbuf, FcLayout lay) {
+               float* __restrict__ Sbuf, FcLayout lay, const int32_t* __restrict__ order) {
   constexpr int EPI = 64 / U;                      // edges per instruction (edge classes)
   constexpr int NG = 4;
   constexpr int CH = 128;                          // edges staged in LDS at a time
@@ -105,7 +105,8 @@ __global__ void __launch_bounds__(256)
   __shared__ int cs[CH];
   __shared__ float ys[CH * S::YC];
   __shared__ float rs[CH * H];
-  const int i = blockIdx.x, t = threadIdx.x;
+  // node of this workgroup in the launch order (largest degree first), or node order
+  const int i = order ? min(max(order[blockIdx.x], 0), n_nodes - 1) : (int)blockIdx.x, t = threadIdx.x;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
   const int grp = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
   const int ec = lane / U, u = lane % U, p4 = lane % 4;
@@ -511,14 +512,15 @@ __global__ void __launch_bounds__(256)
     k_fc_bwd_recv(int n_nodes, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                   const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ R,
                   const float* __restrict__ gS, float* __restrict__ grad_Y, float* __restrict__ grad_R,
-                  FcLayout lay) {
+                  FcLayout lay, const int32_t* __restrict__ order) {
   constexpr int EPI = 64 / U, NG = 4, CH = 64, NR = H + S::YC;
   constexpr PathGroups<S, NG> PG = make_groups<S, NG>();
   __shared__ int cs[CH];
   __shared__ float ys[CH * S::YC];
   __shared__ float rs[CH * H];
   __shared__ float red[NG][CH][NR];
-  const int i = blockIdx.x, t = threadIdx.x;
+  // node of this workgroup in the launch order (largest degree first), or node order
+  const int i = order ? min(max(order[blockIdx.x], 0), n_nodes - 1) : (int)blockIdx.x, t = threadIdx.x;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
   const int grp = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
   const int ec = lane / U, u = lane % U;
@@ -666,13 +668,14 @@ template <class S, int U, int H>
 __global__ void __launch_bounds__(256)
     k_fc_bwd_send(int n_nodes, const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                   const int32_t* __restrict__ t_col, const float* __restrict__ Y, const float* __restrict__ R,
-                  const float* __restrict__ gout, float* __restrict__ Qbuf, FcLayout lin) {
+                  const float* __restrict__ gout, float* __restrict__ Qbuf, FcLayout lin,
+                  const int32_t* __restrict__ order) {
   constexpr int EPI = 64 / U, NG = 4, CH = 128;
   constexpr PathGroups<S, NG> PG = make_groups_in<S, NG>();
   __shared__ int rc[CH];
   __shared__ float ys[CH * S::YC];
   __shared__ float rs[CH * H];
-  const int j = blockIdx.x, t = threadIdx.x;
+  const int j = order ? min(max(order[blockIdx.x], 0), n_nodes - 1) : (int)blockIdx.x, t = threadIdx.x;
   const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
   const int grp = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
   const int ec = lane / U, v = lane % U, p4 = lane % 4;
@@ -841,7 +844,7 @@ hipError_t launch_fc_fwd(const FcArgs& a) {
   const FcLayout L = make_layout<U>(a.n_nodes);
   float* Sbuf = static_cast<float*>(a.ws);
   hipLaunchKernelGGL((k_fc_state<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes, a.row_ptr,
-                     a.col, a.x, a.Y, a.R, Sbuf, L);
+                     a.col, a.x, a.Y, a.R, Sbuf, L, a.r_order);
   int tiles = 0;
   for (int k = 0; k < L.n_out; ++k) tiles += (a.n_nodes * L.d3[k] + 16 * kRT - 1) / (16 * kRT);
   hipLaunchKernelGGL((k_fc_contract<U, kH, false>), dim3(tiles), dim3(64 * kCW), 0, a.stream, a.n_nodes, Sbuf, a.Theta,
@@ -866,7 +869,7 @@ hipError_t launch_fc_bwd(const FcArgs& a) {
   if (a.grad_Theta) {
     if (!a.state_saved)   // else the forward's S is still in ws
       hipLaunchKernelGGL((k_fc_state<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes,
-                         a.row_ptr, a.col, a.x, a.Y, a.R, Sbuf, L);
+                         a.row_ptr, a.col, a.x, a.Y, a.R, Sbuf, L, a.r_order);
     int nb = 0;
     for (int k = 0; k < L.n_out; ++k)
       nb += ((a.n_nodes * L.d3[k] + kRowBlock - 1) / kRowBlock) * ((kH * L.npk[k] * U / 16 + 3) / 4);
@@ -887,11 +890,11 @@ hipError_t launch_fc_bwd(const FcArgs& a) {
     hipLaunchKernelGGL((k_fc_expand<U, kH>), dim3(tiles), dim3(256), 0, a.stream, a.n_nodes, a.gout, a.Theta,
                        SigF::NP, a.outdim, gS, L);
     hipLaunchKernelGGL((k_fc_bwd_recv<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes,
-                       a.row_ptr, a.col, a.x, a.Y, a.R, gS, a.grad_Y, a.grad_R, L);
+                       a.row_ptr, a.col, a.x, a.Y, a.R, gS, a.grad_Y, a.grad_R, L, a.r_order);
   }
   if (a.grad_x) {
     hipLaunchKernelGGL((k_fc_bwd_send<SigF, U, kH>), dim3(a.n_nodes), dim3(256), 0, a.stream, a.n_nodes,
-                       a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.R, a.gout, Q, Li);
+                       a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.R, a.gout, Q, Li, a.s_order);
     int tin = 0;
     for (int b = 0; b < Li.n_out; ++b) tin += (a.n_nodes * Li.d3[b] + 16 * kRT - 1) / (16 * kRT);
     hipLaunchKernelGGL((k_fc_contract<U, kH, true>), dim3(tin), dim3(64 * kCW), 0, a.stream, a.n_nodes, Q, a.Theta,

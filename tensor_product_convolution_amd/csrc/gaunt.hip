@@ -113,7 +113,8 @@ template <int U, int NL2, int WPT>
 __global__ void __launch_bounds__(64 * (U >= 32 ? U / 32 : 1) * WPT)
     k_gaunt_conv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                  const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ w,
-                 float* __restrict__ out, GauntLayout L) {
+                 float* __restrict__ out, GauntLayout L,
+                 const int32_t* __restrict__ order) {
   constexpr int NUT = U >= 32 ? U / 32 : 1;       // 32-channel tiles
   constexpr int NW = NUT * WPT;                   // waves (WPT per tile)
   constexpr int NTH = 64 * NW;
@@ -122,7 +123,8 @@ __global__ void __launch_bounds__(64 * (U >= 32 ? U / 32 : 1) * WPT)
   __shared__ __align__(16) float hs[NW][32][kHS];
   __shared__ int cs[kChunk];
   __shared__ float ysm[kChunk * 9];
-  const int i = blockIdx.x, t = threadIdx.x;
+  // node of this workgroup in the launch order (largest degree first), or node order
+  const int i = order ? min(max(order[blockIdx.x], 0), (int)gridDim.x - 1) : (int)blockIdx.x, t = threadIdx.x;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
   const int wave = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
   const int ut = wave / WPT, sub = wave % WPT;
@@ -315,7 +317,7 @@ __global__ void __launch_bounds__(64 * NW)
     k_gaunt_bwd_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                      const float* __restrict__ x, const float* __restrict__ Y, const float* __restrict__ w,
                      const float* __restrict__ gout, float* __restrict__ grad_Y, float* __restrict__ grad_w,
-                     GauntLayout L) {
+                     GauntLayout L, const int32_t* __restrict__ order) {
   constexpr int NUT = U >= 32 ? U / 32 : 1;
   constexpr int WD = NL2 * U;
   constexpr int YS = NL2 * NL2;
@@ -326,7 +328,8 @@ __global__ void __launch_bounds__(64 * NW)
   __shared__ __align__(16) float tr[NW][32][kHS];     // per-wave transpose of gg
   __shared__ __align__(16) float zt[NW][3][kQ];       // per-wave Z at the 32 points
   __shared__ __align__(16) float yr[NW][9][kHS];      // per-wave grad_Y terms at the 32 points
-  const int i = blockIdx.x, t = threadIdx.x;
+  // node of this workgroup in the launch order (largest degree first), or node order
+  const int i = order ? min(max(order[blockIdx.x], 0), (int)gridDim.x - 1) : (int)blockIdx.x, t = threadIdx.x;
   const int beg = row_ptr[i], end = row_ptr[i + 1];
   const int wave = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
   const int n = lane % 32, hk = lane / 32;
@@ -506,7 +509,7 @@ __global__ void __launch_bounds__(64 * (U >= 32 ? U / 32 : 1) * WPT)
     k_gaunt_bwd_send(const int32_t* __restrict__ t_row_ptr, const int32_t* __restrict__ t_perm,
                      const int32_t* __restrict__ t_col, const float* __restrict__ Y,
                      const float* __restrict__ w, const float* __restrict__ gout, float* __restrict__ grad_x,
-                     GauntLayout L) {
+                     GauntLayout L, const int32_t* __restrict__ order) {
   constexpr int NUT = U >= 32 ? U / 32 : 1;
   constexpr int NW = NUT * WPT, NTH = 64 * NW;
   constexpr int WD = NL2 * U;
@@ -514,7 +517,7 @@ __global__ void __launch_bounds__(64 * (U >= 32 ? U / 32 : 1) * WPT)
   __shared__ __align__(16) float hs[NW][32][kHS];
   __shared__ int rs[kChunk], ps_[kChunk];
   __shared__ float ysm[kChunk * 9];
-  const int j = blockIdx.x, t = threadIdx.x;
+  const int j = order ? min(max(order[blockIdx.x], 0), (int)gridDim.x - 1) : (int)blockIdx.x, t = threadIdx.x;
   const int beg = t_row_ptr[j], end = t_row_ptr[j + 1];
   const int wave = __builtin_amdgcn_readfirstlane(t / 64), lane = t % 64;
   const int ut = wave / WPT, sub = wave % WPT;
@@ -640,15 +643,15 @@ hipError_t launch(const GauntArgs& a, const GauntLayout& L) {
   switch (a.lmax_sh) {
     case 0:
       hipLaunchKernelGGL((k_gaunt_conv<U, 1, WPT>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
-                         a.w, a.out, L);
+                         a.w, a.out, L, a.r_order);
       break;
     case 1:
       hipLaunchKernelGGL((k_gaunt_conv<U, 2, WPT>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
-                         a.w, a.out, L);
+                         a.w, a.out, L, a.r_order);
       break;
     default:
       hipLaunchKernelGGL((k_gaunt_conv<U, 3, WPT>), blocks, threads, 0, a.stream, a.row_ptr, a.col, a.x, a.Y,
-                         a.w, a.out, L);
+                         a.w, a.out, L, a.r_order);
       break;
   }
   return hipGetLastError();
@@ -672,10 +675,10 @@ hipError_t launch_bwd_nl(const GauntArgs& a, const GauntLayout& L) {
   const dim3 blocks(a.n_nodes);
   if (a.n_edges > 0 && (a.grad_w || a.grad_Y))
     hipLaunchKernelGGL((k_gaunt_bwd_recv<U, NL2, NW>), blocks, dim3(64 * NW), 0, a.stream, a.row_ptr, a.col,
-                       a.x, a.Y, a.w, a.gout, a.grad_Y, a.grad_w, L);
+                       a.x, a.Y, a.w, a.gout, a.grad_Y, a.grad_w, L, a.r_order);
   if (a.grad_x)
     hipLaunchKernelGGL((k_gaunt_bwd_send<U, NL2, WPT>), blocks, dim3(64 * (U >= 32 ? U / 32 : 1) * WPT), 0,
-                       a.stream, a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.w, a.gout, a.grad_x, L);
+                       a.stream, a.t_row_ptr, a.t_perm, a.t_col, a.Y, a.w, a.gout, a.grad_x, L, a.s_order);
   return hipGetLastError();
 }
 

@@ -85,6 +85,7 @@ struct FcArgs {
   int32_t n_nodes = 0, n_edges = 0, outdim = 0;
   const int32_t *row_ptr = nullptr, *col = nullptr;
   const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
+  const int32_t *r_order = nullptr, *s_order = nullptr;   // launch orders (null: node id)
   const float *x = nullptr, *Y = nullptr, *R = nullptr, *Theta = nullptr;
   float* out = nullptr;
   // backward: upstream gradient and outputs (NULL: skip)
@@ -123,6 +124,7 @@ struct GauntArgs {
   const float* gout = nullptr;
   const int32_t *t_row_ptr = nullptr, *t_perm = nullptr, *t_col = nullptr;
   float *grad_x = nullptr, *grad_Y = nullptr, *grad_w = nullptr;
+  const int32_t *r_order = nullptr, *s_order = nullptr;   // launch orders (null: node id)
   hipStream_t stream = nullptr;
 };
 hipError_t gaunt_forward(const GauntArgs& a);

@@ -200,3 +200,59 @@ def test_radial_double_backward_with_launch_order(tpc, U, lsh, graph, n):
     for k in ("dx", "dY", "drl", "dg"):
         assert np.array_equal(a[k], o[k]), k
     _check(op, o, _ref(op, wl, True, wl.g, ggx, ggY, ggr, lmax=lsh), U, o["perm"])
+
+
+def test_fc_and_gaunt_with_launch_order(tpc):
+    """The fully connected family and the Gaunt product on a power-law graph
+    with a launch order: forward and backward bit for bit those in node order,
+    and within the bar of the oracle."""
+    from tests.test_gpu_fc import _case as fc_case, _check_bwd as fc_check
+    from tests.test_gpu_gaunt import _bwd_blocks, _blocks, _case as gaunt_case
+    say("fc with launch order, U=32 zipf 400")
+    irr, op, wl, R, Th = fc_case(32, "zipf", 400)
+    go = np.random.default_rng(7).normal(size=(wl.n_nodes, op.outdim)).astype(np.float32)
+    res = []
+    for ordered in (False, True):
+        plan = tpc.Plan(irr, 2, 2)
+        g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+        if ordered:
+            tpc.graph_launch_order(g)
+        Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+        Rs = tpc.gather_rows(T(R), g.perm)
+        out = tpc.forward_fc(plan, g, T(wl.x), Y, Rs, T(Th))
+        b = tpc.backward_fc(plan, g, T(wl.x), Y, Rs, T(Th), T(go))
+        torch.cuda.synchronize()
+        res.append([out.cpu().numpy()] + [t.cpu().numpy() for t in b] + [g.perm.cpu().numpy()])
+    for k in range(5):
+        assert np.array_equal(res[0][k], res[1][k]), k
+    ref = oracle.fc_conv_fwd(op, wl.src, wl.dst, wl.n_nodes, wl.x, oracle.sh_real(2, wl.r), R, Th)
+    assert block_err(res[1][0], ref, out_blocks(op)) <= TOL
+    fc_check(op, wl, R, Th, go, res[1][1:5], res[1][5])
+
+    say("gaunt with launch order, U=32 zipf 400")
+    irr = "32x0e+32x1o+32x2e"
+    gp, wl, w = gaunt_case(irr, 2, 2, "zipf", 400)
+    go = np.random.default_rng(11).normal(size=(wl.n_nodes, gp.outdim)).astype(np.float32)
+    res = []
+    for ordered in (False, True):
+        plan = tpc.Plan(irr, 2, 2, mode=tpc.TP_MODE_GAUNT)
+        g = tpc.graph_build(T(wl.src), T(wl.dst), wl.n_nodes)
+        if ordered:
+            tpc.graph_launch_order(g)
+        Y = tpc.sph_harm(2, tpc.gather_rows(T(wl.r), g.perm))
+        ws = tpc.gather_rows(T(w.reshape(w.shape[0], w.shape[1] * w.shape[2])), g.perm)
+        out = tpc.forward_gaunt(plan, g, T(wl.x), Y, ws)
+        b = tpc.backward_gaunt(plan, g, T(wl.x), Y, ws, T(go))
+        torch.cuda.synchronize()
+        res.append([out.cpu().numpy()] + [t.cpu().numpy() for t in b] + [g.perm.cpu().numpy()])
+    for k in range(4):
+        assert np.array_equal(res[0][k], res[1][k]), k
+    o = res[1]
+    ref = oracle.gaunt_conv_fwd(gp, wl.src, wl.dst, wl.n_nodes, wl.x, oracle.sh_real(2, wl.r), w)
+    assert block_err(o[0], ref, _blocks(gp)) <= TOL
+    rx, rY, rw = oracle.gaunt_conv_bwd(gp, wl.src, wl.dst, wl.n_nodes, wl.x, oracle.sh_real(2, wl.r), w, go)
+    xb, yb, wb = _bwd_blocks(gp, wl.n_edges)
+    perm = o[4][:wl.n_edges]
+    assert block_err(o[1], rx, xb) <= TOL
+    assert block_err(o[2], rY[perm], yb) <= TOL
+    assert block_err(o[3], rw.reshape(len(rw), -1)[perm], wb) <= TOL
