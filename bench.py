@@ -8,8 +8,12 @@ headline ``value`` and, in ``configs``, the other four workloads: the 32-atom
 tiny graph, the 4,096-atom lmax-3 forward, the 32,768-atom power-law (Zipf)
 graph at lmax 3, and the 100,000-atom / 3,000,000-edge streaming layer with
 on-chip radial weights and the channel mix.  ``--config NAME`` measures one
-workload alone (used for profiler runs).  The graph grouping (CSR build) is
-timed separately: it runs once per neighbour list, not per layer.
+workload alone (used for profiler runs).  The graph preparation (CSR build
+and launch order) is timed separately: it runs once per neighbour list, not
+per layer.  Every pass walks its nodes in the launch order (largest degree
+first); the direct-weight and radial lines also time the same step in node
+order, and the lmax-2 direct-weight lines the step with the edge rows in
+the sender grouping.
 
 Timing, every figure cold (nothing of the step's edge-sized inputs in L2 or
 the 256 MB Infinity Cache):
