@@ -207,3 +207,21 @@ def test_parity_of_the_radial_sample():
     snap["gY"][0, 5] += 0.01 * np.max(np.abs(snap["gY"][:, 4:9]))
     bench.cpu_baseline_radial(irr, 2, 2, wl, (8, 64, 5.0), max_edges=400, snap=snap)
     assert snap["parity"]["per_output"]["grad_Y"] > 1e-3
+
+
+def test_sender_layout_bytes_and_node_order_copy():
+    """The sender-grouped layout moves the same bytes over a step (the forward
+    reads e_pos, the backward no t_perm), and the node-order copy of a graph
+    drops only the launch orders."""
+    ab = bench.algorithmic_bytes(1536, 46080, 15, 32, 9, 288, 544)
+    assert ab["fwd_sg"] == ab["fwd"] + 4 * 46080
+    assert ab["bwd_sg"] == ab["bwd"] - 4 * 46080
+    assert ab["fwd_sg"] + ab["bwd_sg"] == ab["fwd"] + ab["bwd"]
+
+    class G:
+        pass
+    g = G()
+    g.row_ptr, g.order, g.t_order = object(), object(), object()
+    h = bench.node_order(g)
+    assert h.order is None and h.t_order is None and h.row_ptr is g.row_ptr
+    assert g.order is not None and g.t_order is not None
