@@ -766,13 +766,19 @@ struct Cfg {
   // latency of one workgroup is that of the launch
   // (large signatures take four waves where their single buffers fit: 164
   // against 172 us for the lmax-3 forward, 1.88 against 1.97 ms on the Zipf
-  // graph)
+  // graph, in node order; at 64 channels and with the nodes in launch order,
+  // two: 1.49 against 1.55 ms on the Zipf graph)
   static constexpr int WPB_F2 = 2 * R::BUF <= LDS ? 2 : 1;
-  static constexpr int WPB_F = kPhased<S> ? (fits(R::BUF, 1, 4) ? 4 : WPB_F2) : (U <= 32 ? 1 : WPB_F2);
+  static constexpr int WPB_F = kPhased<S> ? (U == 64 ? 2 : (fits(R::BUF, 1, 4) ? 4 : WPB_F2))
+                                          : (U <= 32 ? 1 : WPB_F2);
   // the receiver pass takes four waves where their buffers fit (shorter
   // workgroups that the dispatcher refills as they finish: 39.8 against
-  // 42.6 us on the 1,536-atom graph with two)
-  static constexpr int WPB_R = fits(R::BUF, kPhased<S> ? 1 : 2, 4) ? 4 : (2 * R::BUF <= LDS ? 2 : 1);
+  // 42.6 us on the 1,536-atom graph with two); the large signature at 64
+  // channels two once the nodes run in launch order (2.79 against 2.89 ms on
+  // the Zipf graph)
+  static constexpr int WPB_R = (kPhased<S> && U == 64)
+                                   ? 2
+                                   : (fits(R::BUF, kPhased<S> ? 1 : 2, 4) ? 4 : (2 * R::BUF <= LDS ? 2 : 1));
   // the sender pass one wave per workgroup up to 32 channels and for large
   // signatures (1.73 against 1.86 ms on the Zipf graph with two)
   static constexpr int WPB_S = (U <= 32 || kPhased<S> || 2 * Sd::BUF > LDS) ? 1 : 2;
