@@ -85,10 +85,13 @@ constexpr bool dbl_one_walk() {
 
 // Waves per node in both passes (one channel per lane): the waves of a node
 // take every NW-th step of its edges, which keeps several waves per SIMD in
-// flight on graphs of a few thousand nodes and splits a hub's edges four ways;
-// the per-wave partial sums are added in wave order through LDS.
+// flight on graphs of a few thousand nodes and splits a hub's edges; the
+// per-wave partial sums are added in wave order through LDS.  Two waves
+// (measured with the nodes in launch order: Zipf graph 12.4 against 12.9 ms
+// with four, 1,536 atoms 107 against 108 us; four had paid in node order,
+// where hubs starting late set the end of the launch).
 template <int U>
-constexpr int dbl_waves() { return LaneMap<U>::CPL == 1 ? 4 : 1; }
+constexpr int dbl_waves() { return LaneMap<U>::CPL == 1 ? 2 : 1; }
 
 // Receiver pass of the second-order backward: dg per receiver, dY and dw per
 // edge.  Where the signature allows it, one walk over the receiver's edges
